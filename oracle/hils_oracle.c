@@ -1,0 +1,337 @@
+/*
+ * hils_oracle.c -- plain fp64 CPU reference of the HiLS-Attention forward path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the GPU library.
+ *
+ * Source: "Hierarchical Sparse Attention Done Right: Toward Infinite Context
+ * Modeling" (HiLS-Attention).  Citations name the page and its section:
+ *   [p1 BSA]   paper-body page, section "Block Sparse Attention" preliminaries
+ *              (chunk partition, aligned window, candidate set, token logits,
+ *              chunk masses, top-k selection).
+ *   [p1 RQ1]   paper-body page, RQ1 (LogSumExp linearization, landmark query,
+ *              "each query routes over all chunk summaries, keeps the top-k").
+ *   [p1 RQ2]   paper-body page, RQ2 (hierarchical factorisation of weights).
+ *   [p1 GQA]   paper-body page, implementation: GQA-aware chunk selection.
+ *   [p1 Q-Cal] paper-body page, implementation: the partition estimate combines
+ *              chunk-level surrogates with token-level attention mass.
+ *   [p2 Eq.7], [p2 Eq.8], [p2 Eq.10]  summary page, Methodology 1 and 2.
+ *
+ * Everything is computed in double precision from the stored input bytes
+ * (fp32 or bf16 values widen exactly).  The only roundings are the two storage
+ * points of the path's outputs that later stages read back: the chunk summary
+ * key k' (to the summary dtype) and the entropy bias b' (to fp32).
+ *
+ * Readings where the pages are silent (stated once here, used below):
+ *   - token i lies in chunk floor(i/S); only complete chunks are summarised;
+ *   - window left edge l_i = max(0, S*floor((i-W+1)/S)) (floor toward -inf);
+ *     window = [l_i, i]; candidates C_i = {c : (c+1)*S <= l_i};
+ *   - logit scale is the caller's `scale` (1/sqrt(d) by default) everywhere;
+ *   - token logits use q, retrieval scores use q_hat;
+ *   - GQA rank key r_c = max_h (s_hat_{h,c} - LSE_{c' in C_i} s_hat_{h,c'}),
+ *     for a group of one head r_c = s_hat_c; ties go to the lower chunk index;
+ *   - |C_i| <= k selects every candidate;
+ *   - the window enters the normaliser at its true token-level log-mass.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_F64 = 2 };
+enum { ORND_NONE = 0, ORND_F32 = 1, ORND_BF16 = 2 };
+
+/* Read element i of an array of dtype dt, widened exactly to double. */
+static double ld(const void* p, int dt, int64_t i) {
+    if (dt == ODT_F32) return (double)((const float*)p)[i];
+    if (dt == ODT_BF16) {
+        uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return ((const double*)p)[i];
+}
+
+/* Round a double once, to nearest with ties to even, onto the bf16 grid
+ * (8 significant bits). */
+static double round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    (void)frexp(fabs(x), &e);            /* |x| in [2^(e-1), 2^e) */
+    int qe = e - 8;                      /* spacing of the bf16 grid there */
+    if (qe < -133) qe = -133;            /* subnormal spacing */
+    double r = nearbyint(ldexp(fabs(x), -qe));
+    double y = ldexp(r, qe);
+    if (y > 3.3895313892515355e38) y = INFINITY;
+    return copysign(y, x);
+}
+
+static double round_to(double x, int mode) {
+    if (mode == ORND_F32) return (double)(float)x;
+    if (mode == ORND_BF16) return round_bf16(x);
+    return x;
+}
+
+/* log(sum_j exp(x_j)) for n >= 1 values, max-shifted. */
+static double lse(const double* x, int64_t n) {
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) if (x[j] > m) m = x[j];
+    if (m == -INFINITY) return -INFINITY;
+    double z = 0.0;
+    for (int64_t j = 0; j < n; ++j) z += exp(x[j] - m);
+    return m + log(z);
+}
+
+static int64_t floor_div(int64_t a, int64_t b) {
+    int64_t q = a / b;
+    if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+    return q;
+}
+
+/* [p1 BSA]: aligned window left edge and candidate count for position i. */
+int64_t orc_window_left(int64_t i, int S, int W) {
+    int64_t l = (int64_t)S * floor_div(i - (int64_t)W + 1, S);
+    return l < 0 ? 0 : l;
+}
+
+int64_t orc_num_candidates(int64_t i, int S, int W) {
+    return orc_window_left(i, S, W) / S;
+}
+
+/*
+ * Landmark summaries, [p2 Eq.8] with [p1 RQ1] (landmark query gives q'_c).
+ * For every (b, h, c) with c in [c0, c0+nc), g = h / (Hq/Hkv):
+ *   s_j = scale * q'_{h,c} . k_{g,cS+j},  j = 0..S-1
+ *   p = softmax(s);  k'_{h,c} = sum_j p_j k_{g,cS+j};  b'_{h,c} = -sum_j p_j log p_j
+ * b' is evaluated as LSE(s) - sum_j p_j s_j, the same quantity without log(0).
+ *
+ * k      [B, Hkv, k_T, d]  dtype k_dt
+ * ql     [B, Hq, ql_NC, d] dtype ql_dt
+ * ksum   [B, Hq, ks_NC, d] doubles (rounded per ks_round)
+ * bsum   [B, Hq, ks_NC]    doubles (rounded to fp32)
+ */
+int orc_summarize(int B, int Hq, int Hkv, int d, int S, double scale,
+                  const void* k, int k_dt, int64_t k_T,
+                  const void* ql, int ql_dt, int64_t ql_NC,
+                  int64_t c0, int64_t nc, int ks_round,
+                  double* ksum, double* bsum, int64_t ks_NC) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || S <= 0 || d <= 0) return -1;
+    if ((c0 + nc) * S > k_T || c0 + nc > ql_NC || c0 + nc > ks_NC) return -2;
+    const int G = Hq / Hkv;
+    const int64_t total = (int64_t)B * Hq * nc;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < total; ++t) {
+        const int64_t c = c0 + t % nc;
+        const int h = (int)((t / nc) % Hq);
+        const int b = (int)(t / (nc * Hq));
+        const int g = h / G;
+        double* s = (double*)malloc(sizeof(double) * (size_t)S);
+        double* p = (double*)malloc(sizeof(double) * (size_t)S);
+        const int64_t qoff = (((int64_t)b * Hq + h) * ql_NC + c) * d;
+        const int64_t koff = (((int64_t)b * Hkv + g) * k_T + c * S) * d;
+        for (int j = 0; j < S; ++j) {
+            double acc = 0.0;
+            for (int e = 0; e < d; ++e) acc += ld(ql, ql_dt, qoff + e) * ld(k, k_dt, koff + (int64_t)j * d + e);
+            s[j] = scale * acc;
+        }
+        const double L = lse(s, S);
+        double ps = 0.0;
+        for (int j = 0; j < S; ++j) {
+            p[j] = exp(s[j] - L);
+            ps += p[j] * s[j];
+        }
+        double* kout = ksum + (((int64_t)b * Hq + h) * ks_NC + c) * d;
+        for (int e = 0; e < d; ++e) {
+            double acc = 0.0;
+            for (int j = 0; j < S; ++j) acc += p[j] * ld(k, k_dt, koff + (int64_t)j * d + e);
+            kout[e] = round_to(acc, ks_round);
+        }
+        bsum[((int64_t)b * Hq + h) * ks_NC + c] = round_to(L - ps, ORND_F32);
+        free(s);
+        free(p);
+    }
+    return 0;
+}
+
+typedef struct { double r; int64_t c; } rank_entry;
+
+/* Order: larger rank key first; equal keys -> lower chunk index first. */
+static int rank_cmp(const void* a, const void* b) {
+    const rank_entry* x = (const rank_entry*)a;
+    const rank_entry* y = (const rank_entry*)b;
+    if (x->r > y->r) return -1;
+    if (x->r < y->r) return 1;
+    return (x->c < y->c) ? -1 : (x->c > y->c);
+}
+
+static int cmp_i64(const void* a, const void* b) {
+    int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+    return (x < y) ? -1 : (x > y);
+}
+
+/* Intra-group attention ([p1 BSA] token logits, [p2 Eq.10] first factor):
+ * for keys/values rows [j0, j1) of KV head (b, g) and query vector qv:
+ *   log Z = LSE_j (scale q.k_j);  o = sum_j exp(s_j - log Z) v_j. */
+static double group_attend(const double* qv, int d, double scale,
+                           const void* k, const void* v, int kv_dt, int64_t base,
+                           int64_t j0, int64_t j1, double* s, double* o) {
+    const int64_t n = j1 - j0;
+    for (int64_t j = 0; j < n; ++j) {
+        double acc = 0.0;
+        const int64_t off = base + (j0 + j) * d;
+        for (int e = 0; e < d; ++e) acc += qv[e] * ld(k, kv_dt, off + e);
+        s[j] = scale * acc;
+    }
+    const double logZ = lse(s, n);
+    for (int e = 0; e < d; ++e) o[e] = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        const double w = exp(s[j] - logZ);
+        const int64_t off = base + (j0 + j) * d;
+        for (int e = 0; e < d; ++e) o[e] += w * ld(v, kv_dt, off + e);
+    }
+    return logZ;
+}
+
+/*
+ * One query row per entry: (b, g, position i, row iq of the query arrays).
+ * For each row and each head h of group g:
+ *   s_hat_{h,c} = scale * q_hat_{h,i} . k'_{h,c} + b'_{h,c},  c in C_i     [p2 Eq.10 / p1 RQ1]
+ *   Sel = top-k of the rank key over C_i (all of C_i if |C_i| <= k)      [p1 BSA, p1 GQA]
+ *   per group gamma in Sel + {window}: log Z_gamma, o_gamma              [p2 Eq.10]
+ *   log Zhat = LSE({s_hat_c : c in Sel} + {log Z_win})                    [p1 Q-Cal, p2 Eq.10]
+ *   out = sum_c exp(s_hat_c - log Zhat) o_c + exp(log Z_win - log Zhat) o_win;  lse = log Zhat
+ *
+ * q, qh      [B, Hq, q_T, d]   dtype q_dt (row iq is the query of position i)
+ * k, v       [B, Hkv, kv_T, d] dtype kv_dt (rows 0..i are read, nothing beyond)
+ * ksum, bsum [B, Hq, ks_NC(, d)] doubles
+ * forced_idx [nrows, topk] or NULL: use this selection instead of computing one
+ * idx_out    [nrows, topk]       ascending chunk ids, -1 padded
+ * ssel_out   [nrows, G, topk]    each head's s_hat on the selection, -inf padded
+ * gap_out    [nrows]             r_(k) - r_(k+1); +inf when |C_i| <= k
+ * ncand_out  [nrows]             |C_i|
+ * out        [nrows, G, d], lse [nrows, G]
+ * r_out      NULL or [nrows, r_stride]: the rank key of every candidate
+ */
+int orc_rows(int B, int Hq, int Hkv, int d, int S, int W, int topk, double scale,
+             int64_t nrows, const int32_t* rb, const int32_t* rg, const int64_t* ri,
+             const int64_t* rq,
+             const void* q, const void* qh, int q_dt, int64_t q_T,
+             const void* k, const void* v, int kv_dt, int64_t kv_T,
+             const double* ksum, const double* bsum, int64_t ks_NC,
+             const int32_t* forced_idx,
+             int32_t* idx_out, double* ssel_out, double* gap_out, int64_t* ncand_out,
+             double* out, double* lse_out, double* r_out, int64_t r_stride) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || topk < 0) return -1;
+    const int G = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int b = rb[t], g = rg[t];
+        const int64_t i = ri[t], iq = rq[t];
+        if (b < 0 || b >= B || g < 0 || g >= Hkv || i < 0 || i >= kv_T || iq < 0 || iq >= q_T) {
+#pragma omp atomic write
+            err = -2;
+            continue;
+        }
+        const int64_t lw = orc_window_left(i, S, W);
+        const int64_t nc = lw / S;
+        if (nc > ks_NC) {
+#pragma omp atomic write
+            err = -3;
+            continue;
+        }
+        ncand_out[t] = nc;
+        const int64_t nsel = nc < topk ? nc : topk;
+        double* sh = (double*)malloc(sizeof(double) * (size_t)(G * (nc > 0 ? nc : 1)));
+        double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+        int64_t* sel = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1));
+        /* retrieval scores of every candidate, per head */
+        for (int hh = 0; hh < G; ++hh) {
+            const int h = g * G + hh;
+            const int64_t qo = (((int64_t)b * Hq + h) * q_T + iq) * d;
+            for (int e = 0; e < d; ++e) qv[e] = ld(qh, q_dt, qo + e);
+            for (int64_t c = 0; c < nc; ++c) {
+                const double* kk = ksum + (((int64_t)b * Hq + h) * ks_NC + c) * d;
+                double acc = 0.0;
+                for (int e = 0; e < d; ++e) acc += qv[e] * kk[e];
+                sh[hh * nc + c] = scale * acc + bsum[((int64_t)b * Hq + h) * ks_NC + c];
+            }
+        }
+        /* rank keys and selection */
+        double gap = INFINITY;
+        if (forced_idx) {
+            for (int64_t s = 0; s < nsel; ++s) {
+                sel[s] = forced_idx[t * topk + s];
+                if (sel[s] < 0 || sel[s] >= nc) {
+#pragma omp atomic write
+                    err = -4;
+                    sel[s] = 0;
+                }
+            }
+        } else if (nc > 0) {
+            rank_entry* re = (rank_entry*)malloc(sizeof(rank_entry) * (size_t)nc);
+            double* L = (double*)malloc(sizeof(double) * (size_t)G);
+            for (int hh = 0; hh < G; ++hh) L[hh] = lse(sh + hh * nc, nc);
+            for (int64_t c = 0; c < nc; ++c) {
+                double r;
+                if (G == 1) {
+                    r = sh[c];
+                } else {
+                    r = -INFINITY;
+                    for (int hh = 0; hh < G; ++hh) {
+                        const double x = sh[hh * nc + c] - L[hh];
+                        if (x > r) r = x;
+                    }
+                }
+                re[c].r = r;
+                re[c].c = c;
+                if (r_out) r_out[t * r_stride + c] = r;
+            }
+            qsort(re, (size_t)nc, sizeof(rank_entry), rank_cmp);
+            for (int64_t s = 0; s < nsel; ++s) sel[s] = re[s].c;
+            if (nc > topk && topk > 0) gap = re[topk - 1].r - re[topk].r;
+            free(re);
+            free(L);
+        }
+        qsort(sel, (size_t)nsel, sizeof(int64_t), cmp_i64);
+        gap_out[t] = gap;
+        for (int s = 0; s < topk; ++s) idx_out[t * topk + s] = s < nsel ? (int32_t)sel[s] : -1;
+
+        /* attention per head: window and selected chunks, then the fusion */
+        const int64_t wlen = i - lw + 1;
+        const int64_t smax = wlen > S ? wlen : S;
+        double* s = (double*)malloc(sizeof(double) * (size_t)smax);
+        double* o = (double*)malloc(sizeof(double) * (size_t)d);
+        double* ow = (double*)malloc(sizeof(double) * (size_t)d);
+        double* ws = (double*)malloc(sizeof(double) * (size_t)(nsel + 1));
+        double* oc = (double*)malloc(sizeof(double) * (size_t)((nsel > 0 ? nsel : 1) * d));
+        const int64_t kvb = ((int64_t)b * Hkv + g) * kv_T * d;
+        for (int hh = 0; hh < G; ++hh) {
+            const int h = g * G + hh;
+            const int64_t qo = (((int64_t)b * Hq + h) * q_T + iq) * d;
+            for (int e = 0; e < d; ++e) qv[e] = ld(q, q_dt, qo + e);
+            const double logZw = group_attend(qv, d, scale, k, v, kv_dt, kvb, lw, i + 1, s, ow);
+            for (int64_t sidx = 0; sidx < nsel; ++sidx) {
+                const int64_t c = sel[sidx];
+                (void)group_attend(qv, d, scale, k, v, kv_dt, kvb, c * S, c * S + S, s, oc + sidx * d);
+                ws[sidx] = sh[hh * (nc > 0 ? nc : 1) + c];
+                ssel_out[(t * G + hh) * topk + sidx] = ws[sidx];
+            }
+            for (int64_t sidx = nsel; sidx < topk; ++sidx) ssel_out[(t * G + hh) * topk + sidx] = -INFINITY;
+            ws[nsel] = logZw;
+            const double Lhat = lse(ws, nsel + 1);
+            for (int e = 0; e < d; ++e) o[e] = exp(logZw - Lhat) * ow[e];
+            for (int64_t sidx = 0; sidx < nsel; ++sidx) {
+                const double w = exp(ws[sidx] - Lhat);
+                for (int e = 0; e < d; ++e) o[e] += w * oc[sidx * d + e];
+            }
+            for (int e = 0; e < d; ++e) out[(t * G + hh) * d + e] = o[e];
+            lse_out[t * G + hh] = Lhat;
+        }
+        free(s); free(o); free(ow); free(ws); free(oc);
+        free(sh); free(qv); free(sel);
+    }
+    return err;
+}

@@ -1,0 +1,80 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Every mutant is a one-line textual change to a copy of `oracle/hils_oracle.c`,
+built on the host; the pins of `test_oracle_pins.py` then run against it.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "hils_oracle.c")
+
+# (name, original text, mutated text)
+MUTANTS = [
+    ("drop entropy bias in score", "scale * acc + bsum[((int64_t)b * Hq + h) * ks_NC + c]",
+     "scale * acc + 0.0 * bsum[((int64_t)b * Hq + h) * ks_NC + c]"),
+    ("entropy sign", "round_to(L - ps, ORND_F32)", "round_to(ps - L, ORND_F32)"),
+    ("mean key instead of weighted", "acc += p[j] * ld(k, k_dt, koff + (int64_t)j * d + e);",
+     "acc += ld(k, k_dt, koff + (int64_t)j * d + e) / S;"),
+    ("tie to higher index", "return (x->c < y->c) ? -1 : (x->c > y->c);",
+     "return (x->c > y->c) ? -1 : (x->c < y->c);"),
+    ("window off by one", "(int64_t)S * floor_div(i - (int64_t)W + 1, S)",
+     "(int64_t)S * floor_div(i - (int64_t)W, S)"),
+    ("q_hat in token logits", "for (int e = 0; e < d; ++e) qv[e] = ld(q, q_dt, qo + e);",
+     "for (int e = 0; e < d; ++e) qv[e] = ld(qh, q_dt, qo + e);"),
+    ("window left out of normaliser", "const double Lhat = lse(ws, nsel + 1);",
+     "const double Lhat = nsel ? lse(ws, nsel) : logZw;"),
+    ("GQA without per-head normalisation", "const double x = sh[hh * nc + c] - L[hh];",
+     "const double x = sh[hh * nc + c];"),
+    ("GQA sum instead of max", "if (x > r) r = x;", "r = (r == -INFINITY ? 0.0 : r) + x;"),
+    ("scale missing in summary", "            s[j] = scale * acc;\n        }\n        const double L",
+     "            s[j] = acc;\n        }\n        const double L"),
+    ("scale missing in token logits", "        s[j] = scale * acc;\n    }\n    const double logZ",
+     "        s[j] = acc;\n    }\n    const double logZ"),
+    ("fused weight uses window mass for chunks", "const double w = exp(ws[sidx] - Lhat);",
+     "const double w = exp(logZw - Lhat);"),
+]
+
+PIN_TESTS = [
+    lambda g: pins.test_golden_hand_example(g),
+    lambda g: pins.test_golden_gqa_rule(g),
+    lambda g: pins.test_window_and_candidates(),
+    lambda g: pins.test_p1_taylor_exact_at_landmark(),
+    lambda g: pins.test_p1_through_rows(),
+    lambda g: pins.test_p7_mean_pool_special_case(),
+    lambda g: pins.test_p8_entropy_regimes(),
+    lambda g: pins.test_p3_fused_weights_sum_to_one(),
+    lambda g: pins.test_p4_chunk_size_one_is_dense(3),
+    lambda g: pins.test_p5_single_query_exact_any_chunk_size(),
+    lambda g: pins.test_p6_short_prefix_and_window_only(),
+    lambda g: pins.test_p9_brute_force_matrix_form(dict(B=1, Hq=4, Hkv=2, T=28, d=6, S=4, W=6, k=1)),
+    lambda g: pins.test_p9_brute_force_matrix_form(dict(B=1, Hq=1, Hkv=1, T=32, d=4, S=2, W=4, k=3)),
+    lambda g: pins.test_psel_exact_ties_lower_index_wins(1, 1),
+    lambda g: pins.test_p11_gqa_identical_heads_equals_mha(),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, orig, mut, tmp_path, golden):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, "mutation anchor not found: " + name
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(orig, mut))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O1", "-fopenmp", "-std=c11", "-shared", "-fPIC", str(mpath),
+                           "-o", str(so), "-lm"])
+    oracle.use_library(str(so))
+    caught = []
+    try:
+        for k, t in enumerate(PIN_TESTS):
+            try:
+                t(golden)
+            except (AssertionError, RuntimeError):
+                caught.append(k)
+    finally:
+        oracle.use_library(None)
+    assert caught, "planted mistake '%s' passed every pin" % name
