@@ -1,0 +1,617 @@
+// attend.hip -- per-group attention and the hierarchical fusion (prefill).
+//
+// Summary page, Methodology 2, Eq. 10: w_ij = exp(s_ij)/Z_{i,c(j)} * Zhat_{i,c(j)}/Zhat_i
+// with Zhat_{i,c} = exp(s_hat_{i,c}) for a selected chunk and, for the window, its
+// true token-level mass Z_{i,win} (paper-body page, implementation: the partition
+// estimate combines chunk-level surrogates with token-level attention mass).  So
+//   out_i = sum_{c in Sel} exp(s_hat_c - L) o_c + exp(log Z_win - L) o_win,
+//   L = LSE({s_hat_c} + {log Z_win}),
+// where o_gamma is ordinary softmax attention of q_i over the group's tokens.
+//
+// The pages batch adjacent queries over the union of their selected chunks
+// (paper-body page, implementation, kernel design).  That reuse depends on
+// adjacent queries picking overlapping chunks; when they do not, every
+// (query, chunk) visit re-reads 32 KiB of K/V.  This file instead runs the
+// selected part chunk-major: each selected chunk's K/V is staged once in LDS and
+// attended by every query that selected it, in MFMA tiles of 16 (query, head)
+// rows; each visit writes its weighted output exp(s_hat_c - L_sel) o_c
+// (L_sel = LSE over the selected chunks only) to a partial slot.  The window
+// part is dense and runs query-major, flash-style, and its epilogue fuses:
+//   out_i = exp(log Z_win - L) o_win + exp(L_sel - L) * sum_slots partial,
+//   L = LSE(L_sel, log Z_win).
+// The (query, slot) lists per chunk are built deterministically: per 64-query
+// tile an LDS bitmap of which queries chose each chunk, a column scan over
+// tiles and a scan over chunks give every entry a fixed position.
+//
+// Score tiles are computed transposed, S^T = K Q^T (tokens x rows), so each lane
+// holds one row's scores for 16 tokens; the same registers, cast to the operand
+// type, are the B operand of O^T = V^T P^T with the reduction order of the
+// token axis permuted to match (V is staged transposed in LDS).
+#include "hils_internal.h"
+
+namespace hils {
+
+namespace {
+
+constexpr int kS = 64;  // chunk size
+
+template <typename T> struct Pad;
+template <> struct Pad<bf16_t> { static constexpr int K = 8, V = 4; };
+template <> struct Pad<float> { static constexpr int K = 4, V = 4; };
+
+struct IdxArgs {
+  const int32_t* idx;
+  const float* ssel;
+  int32_t* tile_cnt;   // [B, Hkv, ntiles, NCs]: counts, then exclusive offsets
+  int32_t* bcount;     // [B, Hkv, NCs]
+  int64_t* bbase;      // [B, Hkv, NCs]
+  uint32_t* entries;   // i * 64 + slot
+  float* lsel;         // [B, Hq, T]
+  int B, Hq, Hkv, topk;
+  int64_t T, NCs, ntiles;
+};
+
+// Bitmap of the tile's queries that selected each chunk.
+__device__ void build_bitmap(const IdxArgs& a, uint64_t* bm, int b, int g, int64_t t) {
+  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) bm[c] = 0ull;
+  __syncthreads();
+  const int64_t i0 = t * 64;
+  const int n = 64 * a.topk;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int ql = e / a.topk, s = e % a.topk;
+    const int64_t i = i0 + ql;
+    if (i >= a.T) continue;
+    const int32_t c = a.idx[(((int64_t)b * a.Hkv + g) * a.T + i) * a.topk + s];
+    if (c >= 0 && c < a.NCs) atomicOr((unsigned long long*)&bm[c], 1ull << ql);
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void idx_count_kernel(IdxArgs a) {
+  extern __shared__ uint64_t bm[];
+  const int64_t t = blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  build_bitmap(a, bm, b, g, t);
+  int32_t* out = a.tile_cnt + (((int64_t)b * a.Hkv + g) * a.ntiles + t) * a.NCs;
+  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) out[c] = __popcll(bm[c]);
+}
+
+// Column scan over tiles: exclusive offsets in place, totals to bcount.  A block
+// owns 32 chunk columns of one (b, g); its 32 thread rows split the tiles into
+// segments (segment sums, a scan across segments, then the in-place rewrite).
+__global__ __launch_bounds__(1024) void idx_scan_tiles_kernel(IdxArgs a) {
+  __shared__ int32_t part[32][33];
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;
+  const int64_t c = (int64_t)blockIdx.x * 32 + tx;
+  const int64_t bg = blockIdx.y;
+  const int64_t seg = (a.ntiles + 31) / 32;
+  const int64_t t0 = ty * seg, t1 = min(t0 + seg, a.ntiles);
+  int32_t* col = a.tile_cnt + bg * a.ntiles * a.NCs + c;
+  int32_t s = 0;
+  if (c < a.NCs)
+    for (int64_t t = t0; t < t1; ++t) s += col[t * a.NCs];
+  part[ty][tx] = s;
+  __syncthreads();
+  int32_t run = 0;
+  for (int k = 0; k < ty; ++k) run += part[k][tx];
+  if (c < a.NCs) {
+    for (int64_t t = t0; t < t1; ++t) {
+      const int32_t v = col[t * a.NCs];
+      col[t * a.NCs] = run;
+      run += v;
+    }
+    if (ty == 31) a.bcount[bg * a.NCs + c] = run;
+  }
+}
+
+// Exclusive scan of all bucket counts (one block).
+__global__ __launch_bounds__(1024) void idx_scan_buckets_kernel(IdxArgs a) {
+  __shared__ int64_t part[1024];
+  const int64_t nb = (int64_t)a.B * a.Hkv * a.NCs;
+  const int64_t per = (nb + 1023) / 1024;
+  const int64_t lo = threadIdx.x * per, hi = min(lo + per, nb);
+  int64_t s = 0;
+  for (int64_t j = lo; j < hi; ++j) s += a.bcount[j];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int64_t v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int64_t run = part[threadIdx.x] - s;
+  for (int64_t j = lo; j < hi; ++j) {
+    a.bbase[j] = run;
+    run += a.bcount[j];
+  }
+}
+
+// Entries at their final positions, and L_sel = LSE of each head's selected s_hat.
+__global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
+  extern __shared__ uint64_t bm[];
+  const int64_t t = blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  build_bitmap(a, bm, b, g, t);
+  const int64_t i0 = t * 64;
+  const int32_t* toff = a.tile_cnt + (((int64_t)b * a.Hkv + g) * a.ntiles + t) * a.NCs;
+  const int64_t* bbase = a.bbase + ((int64_t)b * a.Hkv + g) * a.NCs;
+  const int n = 64 * a.topk;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const int ql = e / a.topk, s = e % a.topk;
+    const int64_t i = i0 + ql;
+    if (i >= a.T) continue;
+    const int32_t c = a.idx[(((int64_t)b * a.Hkv + g) * a.T + i) * a.topk + s];
+    if (c < 0 || c >= a.NCs) continue;
+    const int rank = __popcll(bm[c] & ((1ull << ql) - 1ull));
+    a.entries[bbase[c] + toff[c] + rank] = (uint32_t)(i * 64 + s);
+  }
+}
+
+// L_sel = LSE of each head's s_hat over its selected chunks (-inf if none).
+__global__ __launch_bounds__(256) void lsel_kernel(IdxArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)a.B * a.Hq * a.T) return;
+  const int64_t i = gid % a.T;
+  const int h = (int)((gid / a.T) % a.Hq);
+  const int b = (int)(gid / (a.T * a.Hq));
+  const int g = h / (a.Hq / a.Hkv);
+  const float* sr = a.ssel + gid * a.topk;
+  const int32_t* ir = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * a.topk;
+  float m = kNegInf;
+  for (int s = 0; s < a.topk; ++s)
+    if (ir[s] >= 0) m = fmaxf(m, sr[s]);
+  float z = 0.f;
+  if (m != kNegInf)
+    for (int s = 0; s < a.topk; ++s)
+      if (ir[s] >= 0) z += __expf(sr[s] - m);
+  a.lsel[gid] = m == kNegInf ? kNegInf : m + __logf(z);
+}
+
+// Stage one chunk of K (row-major) and V (transposed) into LDS.
+template <typename T, int D>
+__device__ __forceinline__ void stage_chunk(const T* kc, const T* vc, T* ks, T* vt) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
+#pragma unroll
+  for (int base = 0; base < kS * D; base += 256 * EPV) {
+    const int e = base + threadIdx.x * EPV;
+    const int row = e / D, col = e % D;
+    const uint4 uk = *reinterpret_cast<const uint4*>(kc + e);
+    *reinterpret_cast<uint4*>(ks + row * KP + col) = uk;
+    const uint4 uv = *reinterpret_cast<const uint4*>(vc + e);
+    const T* tv = reinterpret_cast<const T*>(&uv);
+#pragma unroll
+    for (int t = 0; t < EPV; ++t) vt[(col + t) * VP + row] = tv[t];
+  }
+}
+
+// S^T tile (64 tokens x 16 rows) for one row-fragment set bq[KS]; acc[mt][i] is the
+// logit of token 16*mt + 4*grp + i for row lane%16.
+template <typename T, int D>
+__device__ __forceinline__ void score_tile(const T* ks, const Frag<T> (&bq)[D / 32], f32x4_t (&acc)[4],
+                                           int r16, int grp) {
+  constexpr int KP = D + Pad<T>::K;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kq = 0; kq < D / 32; ++kq) {
+      Frag<T> af;
+      load_frag(af, ks + (16 * mt + r16) * KP + 8 * grp + 32 * kq);
+      mma(acc[mt], af, bq[kq]);
+    }
+  }
+}
+
+// O^T += V^T P^T: o[md] (dims 16*md + 4*grp + i, row lane%16), p[mt][i] as from score_tile.
+template <typename T, int D>
+__device__ __forceinline__ void pv_tile(const T* vt, const float (&p)[4][4], f32x4_t (&o)[D / 16],
+                                        int r16, int grp) {
+  constexpr int VP = kS + Pad<T>::V;
+  Frag<T> pf[2];
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = p[2 * k2][i];
+      x[4 + i] = p[2 * k2 + 1][i];
+    }
+    set_frag(pf[k2], x);
+  }
+#pragma unroll
+  for (int md = 0; md < D / 16; ++md) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const T* row = vt + (16 * md + r16) * VP + 32 * k2 + 4 * grp;
+      Frag<T> af;
+      load_frag2x4(af, row, row + 16);
+      mma(o[md], af, pf[k2]);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const f32x4_t& v, float w);
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const f32x4_t& v, float w) {
+  const uint32_t lo = (uint32_t)f2bf(v[0] * w) | ((uint32_t)f2bf(v[1] * w) << 16);
+  const uint32_t hi = (uint32_t)f2bf(v[2] * w) | ((uint32_t)f2bf(v[3] * w) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const f32x4_t& v, float w) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0] * w, v[1] * w, v[2] * w, v[3] * w);
+}
+template <typename T>
+__device__ __forceinline__ void load4_add(f32x4_t& acc, const T* p);
+template <>
+__device__ __forceinline__ void load4_add<bf16_t>(f32x4_t& acc, const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  acc[0] += __uint_as_float(u.x << 16);
+  acc[1] += __uint_as_float(u.x & 0xffff0000u);
+  acc[2] += __uint_as_float(u.y << 16);
+  acc[3] += __uint_as_float(u.y & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void load4_add<float>(f32x4_t& acc, const float* p) {
+  const float4 u = *reinterpret_cast<const float4*>(p);
+  acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
+}
+
+struct ChunkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* ssel;
+  const float* lsel;
+  const int32_t* bcount;
+  const int64_t* bbase;
+  const uint32_t* entries;
+  void* part;   // [B, Hkv_pass, G, T, topk, D]
+  int B, Hq, Hkv, topk, g0, gpass;
+  int64_t T, NCs;
+  float scale;
+};
+
+// Selected chunks, chunk-major: one workgroup per (b, g, c).
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int NE = 16 / G;  // entries per 16-row tile
+  constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
+  __shared__ __align__(16) T ks[kS * KP];
+  __shared__ __align__(16) T vt[D * VP];
+  const int64_t c = blockIdx.x;
+  const int g = a.g0 + blockIdx.y, b = blockIdx.z;
+  const int64_t bucket = ((int64_t)b * a.Hkv + g) * a.NCs + c;
+  const int n = a.bcount[bucket];
+  if (n == 0) return;
+  const int64_t base = a.bbase[bucket];
+  const T* kc = static_cast<const T*>(a.k) + (((int64_t)b * a.Hkv + g) * a.T + c * kS) * D;
+  const T* vc = static_cast<const T*>(a.v) + (((int64_t)b * a.Hkv + g) * a.T + c * kS) * D;
+  stage_chunk<T, D>(kc, vc, ks, vt);
+  __syncthreads();
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int r16 = lane % 16, grp = lane / 16;
+  const float sl2 = a.scale * kLog2e;
+  const T* qbase = static_cast<const T*>(a.q);
+  T* part = static_cast<T*>(a.part);
+  const int ntile = (n + NE - 1) / NE;
+  for (int nt = wave; nt < ntile; nt += 4) {
+    const int e = nt * NE + r16 / G, hh = r16 % G;
+    const bool valid = e < n;
+    const uint32_t word = valid ? a.entries[base + e] : 0u;
+    const int64_t i = word >> 6;
+    const int slot = word & 63;
+    const int h = g * G + hh;
+    Frag<T> bq[KS];
+    if (valid) {
+      const T* qrow = qbase + (((int64_t)b * a.Hq + h) * a.T + i) * D + 8 * grp;
+#pragma unroll
+      for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
+    } else {
+#pragma unroll
+      for (int kq = 0; kq < KS; ++kq) zero_frag(bq[kq]);
+    }
+    f32x4_t acc[4];
+    score_tile<T, D>(ks, bq, acc, r16, grp);
+    float mx = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) mx = fmaxf(mx, acc[mt][q4] * sl2);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float p[4][4], ls = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        p[mt][q4] = exp2f(acc[mt][q4] * sl2 - mx);
+        ls += p[mt][q4];
+      }
+    ls += __shfl_xor(ls, 16, kWave);
+    ls += __shfl_xor(ls, 32, kWave);
+    f32x4_t o[D / 16];
+#pragma unroll
+    for (int md = 0; md < D / 16; ++md) o[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    pv_tile<T, D>(vt, p, o, r16, grp);
+    if (valid) {
+      const int64_t rowq = ((int64_t)b * a.Hq + h) * a.T + i;
+      const float w = __expf(a.ssel[rowq * a.topk + slot] - a.lsel[rowq]) / ls;
+      T* prow = part + (((((int64_t)b * a.gpass + (g - a.g0)) * G + hh) * a.T + i) * a.topk + slot) * D;
+#pragma unroll
+      for (int md = 0; md < D / 16; ++md) store4<T>(prow + 16 * md + 4 * grp, o[md], w);
+    }
+  }
+}
+
+struct WinArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  const float* lsel;
+  const void* part;
+  void* out;
+  float* lse;
+  int B, Hq, Hkv, topk, g0, gpass, S, W;
+  int64_t T;
+  float scale;
+};
+
+// Window attention (query-major, dense) and the fusion with the selected partials.
+// A wave owns 64 rows = (64/G queries) x G heads as four 16-row tiles.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void window_fuse_kernel(WinArgs a) {
+  constexpr int KS = D / 32, MD = D / 16;
+  constexpr int QW = 64 / G;        // queries per wave
+  constexpr int QB = 4 * QW;        // queries per block
+  constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
+  __shared__ __align__(16) T ks[kS * KP];
+  __shared__ __align__(16) T vt[D * VP];
+  const int g = a.g0 + blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int r16 = lane % 16, grp = lane / 16;
+  const int64_t T_ = a.T;
+  // Consecutive query tiles share most window chunks: give each XCD (blocks are
+  // dealt round-robin over the 8 XCDs) a contiguous run of tiles so they meet in
+  // one L2.
+  int64_t bx = blockIdx.x;
+  if (gridDim.x % 8 == 0) bx = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+  const int64_t qb0 = bx * QB;
+  const int64_t qlast = min(qb0 + QB - 1, T_ - 1);
+  const float sl2 = a.scale * kLog2e;
+  const T* qbase = static_cast<const T*>(a.q);
+
+  // rows of tile nt: R = 16*nt + r16 -> query wave*QW + R/G, head R%G
+  int64_t ir[4], lw[4];
+  Frag<T> bq[4][KS];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int R = 16 * nt + r16;
+    const int64_t i = qb0 + wave * QW + R / G;
+    ir[nt] = i;
+    lw[nt] = window_left(i, a.S, a.W);
+    const int h = g * G + R % G;
+    const int64_t ia = i < T_ ? i : T_ - 1;
+    const T* qrow = qbase + (((int64_t)b * a.Hq + h) * T_ + ia) * D + 8 * grp;
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) load_frag(bq[nt][kq], qrow + 32 * kq);
+  }
+  float m[4], ls[4];
+  f32x4_t o[4][MD];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    m[nt] = kNegInf;
+    ls[nt] = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[nt][md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int64_t c_lo = window_left(qb0, a.S, a.W) / kS;
+  const int64_t c_hi = qlast / kS;
+  const T* kbase = static_cast<const T*>(a.k) + ((int64_t)b * a.Hkv + g) * T_ * D;
+  const T* vbase = static_cast<const T*>(a.v) + ((int64_t)b * a.Hkv + g) * T_ * D;
+  for (int64_t c = c_lo; c <= c_hi; ++c) {
+    __syncthreads();
+    if ((c + 1) * kS <= T_) {
+      stage_chunk<T, D>(kbase + c * kS * D, vbase + c * kS * D, ks, vt);
+    } else {
+      // trailing partial chunk: stage the valid rows, zero the rest
+      constexpr int EPV = 16 / sizeof(T);
+      for (int e = threadIdx.x * EPV; e < kS * D; e += 256 * EPV) {
+        const int row = e / D, col = e % D;
+        const bool ok = c * kS + row < T_;
+        uint4 uk = make_uint4(0, 0, 0, 0), uv = make_uint4(0, 0, 0, 0);
+        if (ok) {
+          uk = *reinterpret_cast<const uint4*>(kbase + c * kS * D + e);
+          uv = *reinterpret_cast<const uint4*>(vbase + c * kS * D + e);
+        }
+        *reinterpret_cast<uint4*>(ks + row * KP + col) = uk;
+        const T* tv = reinterpret_cast<const T*>(&uv);
+        for (int t = 0; t < EPV; ++t) vt[(col + t) * VP + row] = tv[t];
+      }
+    }
+    __syncthreads();
+    const int64_t j0 = c * kS;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      // skip tiles with no row whose window meets this chunk (uniform per wave)
+      f32x4_t acc[4];
+      score_tile<T, D>(ks, bq[nt], acc, r16, grp);
+      float x[4][4], mx = kNegInf;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int64_t j = j0 + 16 * mt + 4 * grp + q4;
+          const bool ok = j >= lw[nt] && j <= ir[nt] && ir[nt] < T_;
+          x[mt][q4] = ok ? acc[mt][q4] * sl2 : kNegInf;
+          mx = fmaxf(mx, x[mt][q4]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mn = fmaxf(m[nt], mx);
+      const float alpha = (m[nt] == mn) ? 1.f : exp2f(m[nt] - mn);
+      float p[4][4], psum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          p[mt][q4] = x[mt][q4] == kNegInf ? 0.f : exp2f(x[mt][q4] - mn);
+          psum += p[mt][q4];
+        }
+      ls[nt] = ls[nt] * alpha + psum;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[nt][md] *= alpha;
+      m[nt] = mn;
+      pv_tile<T, D>(vt, p, o[nt], r16, grp);
+    }
+  }
+
+  // epilogue: window log-mass, fusion with the selected partials
+  const int gl = g - a.g0;
+  const T* part = static_cast<const T*>(a.part);
+  T* outp = static_cast<T*>(a.out);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int R = 16 * nt + r16;
+    const int hh = R % G, h = g * G + hh;
+    const int64_t i = ir[nt];
+    float lsum = ls[nt];
+    lsum += __shfl_xor(lsum, 16, kWave);
+    lsum += __shfl_xor(lsum, 32, kWave);
+    if (i >= T_) continue;
+    const float logzw = (m[nt] + __log2f(lsum)) * kLn2;
+    const int64_t rowq = ((int64_t)b * a.Hq + h) * T_ + i;
+    const float lsel = a.lsel ? a.lsel[rowq] : kNegInf;
+    const float L = lsel == kNegInf ? logzw
+                                    : fmaxf(lsel, logzw) + __logf(1.f + __expf(-fabsf(lsel - logzw)));
+    const float ww = __expf(logzw - L) / lsum;
+    const float wsel = lsel == kNegInf ? 0.f : __expf(lsel - L);
+    f32x4_t sacc[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) sacc[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * T_ + i) * a.topk;
+    const T* prow = part + ((((int64_t)b * a.gpass + gl) * G + hh) * T_ + i) * a.topk * D;
+    for (int s = 0; s < a.topk; ++s) {
+      if (irow[s] < 0) continue;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) load4_add<T>(sacc[md], prow + s * D + 16 * md + 4 * grp);
+    }
+    T* orow = outp + rowq * D;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      f32x4_t r;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) r[q4] = o[nt][md][q4] * ww + sacc[md][q4] * wsel;
+      store4<T>(orow + 16 * md + 4 * grp, r, 1.f);
+    }
+    if (a.lse && grp == 0) a.lse[rowq] = L;
+  }
+}
+
+template <typename T, int D, int G>
+hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, int gpp,
+                            hipStream_t st) {
+  for (int g0 = 0; g0 < a.Hkv; g0 += gpp) {
+    const int gp = min(gpp, a.Hkv - g0);
+    ChunkArgs ca{a.q, a.k, a.v, a.ssel, ia.lsel, ia.bcount, ia.bbase, ia.entries, part,
+                 a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, a.scale};
+    if (ia.NCs > 0 && a.topk > 0) {
+      hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)ia.NCs, gp, a.B), dim3(256),
+                         0, st, ca);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    WinArgs wa{a.q, a.k, a.v, a.idx, ia.lsel, part, a.out, a.lse, a.B, a.Hq, a.Hkv, a.topk,
+               g0, gpp, a.S, a.W, a.T, a.scale};
+    const int QB = 4 * (64 / G);
+    hipLaunchKernelGGL((window_fuse_kernel<T, D, G>), dim3((unsigned)((a.T + QB - 1) / QB), gp, a.B),
+                       dim3(256), 0, st, wa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T, int D>
+hipError_t launch_attend_t(const AttArgs& a, const IdxArgs& ia, void* part, int gpp, hipStream_t st) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, gpp, st);
+    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, gpp, st);
+    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, gpp, st);
+    default: return launch_attend_tg<T, D, 8>(a, ia, part, gpp, st);
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, bool bf16,
+                      size_t* fixed, size_t* per_kv_head) {
+  const int64_t NCs = T / S;
+  const int64_t ntiles = (T + 63) / 64;
+  size_t f = 0;
+  f += align256((size_t)B * Hkv * ntiles * NCs * sizeof(int32_t));  // tile_cnt
+  f += align256((size_t)B * Hkv * NCs * sizeof(int32_t));           // bcount
+  f += align256((size_t)B * Hkv * NCs * sizeof(int64_t));           // bbase
+  f += align256((size_t)B * Hkv * T * topk * sizeof(uint32_t));     // entries
+  f += align256((size_t)B * Hq * T * sizeof(float));                // lsel
+  *fixed = f + 256;
+  *per_kv_head = align256((size_t)B * (Hq / Hkv) * T * topk * D * (bf16 ? 2 : 4));
+}
+
+hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
+  size_t fixed, per;
+  attend_workspace(a.B, a.Hq, a.Hkv, a.T, a.S, a.D, a.topk, a.bf16, &fixed, &per);
+  const int64_t NCs = a.T / a.S;
+  const int64_t ntiles = (a.T + 63) / 64;
+  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(a.ws) + 255) & ~(uintptr_t)255);
+  IdxArgs ia{};
+  ia.idx = a.idx;
+  ia.ssel = a.ssel;
+  ia.tile_cnt = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)a.B * a.Hkv * ntiles * NCs * sizeof(int32_t));
+  ia.bcount = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)a.B * a.Hkv * NCs * sizeof(int32_t));
+  ia.bbase = reinterpret_cast<int64_t*>(w);
+  w += align256((size_t)a.B * a.Hkv * NCs * sizeof(int64_t));
+  ia.entries = reinterpret_cast<uint32_t*>(w);
+  w += align256((size_t)a.B * a.Hkv * a.T * a.topk * sizeof(uint32_t));
+  ia.lsel = reinterpret_cast<float*>(w);
+  w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
+  ia.B = a.B; ia.Hq = a.Hq; ia.Hkv = a.Hkv; ia.topk = a.topk;
+  ia.T = a.T; ia.NCs = NCs; ia.ntiles = ntiles;
+  void* part = w;
+  const size_t avail = a.ws_bytes - fixed;
+  int gpp = per > 0 ? (int)(avail / per) : a.Hkv;  // k = 0 needs no partial outputs
+  if (gpp > a.Hkv) gpp = a.Hkv;
+  if (gpp < 1) gpp = 1;  // the host checked the minimum size
+
+  if (a.topk > 0 && NCs > 0) {
+    const size_t lds = (size_t)NCs * sizeof(uint64_t);
+    hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
+    hipLaunchKernelGGL(idx_scan_tiles_kernel, dim3((unsigned)((NCs + 31) / 32), a.B * a.Hkv),
+                       dim3(1024), 0, st, ia);
+    hipLaunchKernelGGL(idx_scan_buckets_kernel, dim3(1), dim3(1024), 0, st, ia);
+    hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
+  }
+  if (a.topk > 0) {
+    const int64_t nrow = (int64_t)a.B * a.Hq * a.T;
+    hipLaunchKernelGGL(lsel_kernel, dim3((unsigned)((nrow + 255) / 256)), dim3(256), 0, st, ia);
+  } else {
+    ia.lsel = nullptr;  // no selection: the window is the whole normaliser
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, gpp, st);
+  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, gpp, st) : launch_attend_t<float, 64>(a, ia, part, gpp, st);
+}
+
+}  // namespace hils

@@ -1,0 +1,210 @@
+// hils.cpp -- the C ABI of include/hils.h: validation, workspace sizing, dispatch.
+//
+// Every check happens here, on the host, before any work is enqueued; a nonzero
+// status therefore means nothing was launched and nothing was written.
+#include "hils.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "hils_internal.h"
+
+namespace {
+
+using hils::kDecSelBlock;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+enum Mode { kSummarize, kPrefill, kDecode };
+
+hils_status check_shape(const hils_shape* s, Mode mode) {
+  if (!s) return HILS_E_NULL;
+  if (s->io_dtype != HILS_F32 && s->io_dtype != HILS_BF16) return HILS_E_DTYPE;
+  if (s->summary_dtype != HILS_F32 && s->summary_dtype != HILS_BF16) return HILS_E_DTYPE;
+  if (s->batch < 1 || s->heads_q < 1 || s->heads_kv < 1 || s->head_dim < 1 || s->chunk < 1 ||
+      s->window < 1 || s->top_k < 0 || s->seq_len < 1)
+    return HILS_E_SHAPE;
+  if (s->heads_q % s->heads_kv != 0) return HILS_E_SHAPE;
+  if (!(s->scale >= 0.f) || std::isinf(s->scale)) return HILS_E_SHAPE;
+  const int G = s->heads_q / s->heads_kv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return HILS_E_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return HILS_E_UNSUPPORTED;
+  if (s->chunk != 64) return HILS_E_UNSUPPORTED;
+  if (s->top_k > 64) return HILS_E_UNSUPPORTED;
+  if (s->summary_dtype != s->io_dtype) return HILS_E_UNSUPPORTED;
+  if (mode == kDecode) {
+    if (s->batch > 64) return HILS_E_UNSUPPORTED;
+    if (s->seq_len % s->chunk != 0) return HILS_E_SHAPE;
+    const int64_t nc = s->seq_len / s->chunk;
+    const int64_t nb = (nc + kDecSelBlock - 1) / kDecSelBlock;
+    if (nb * 4 * s->top_k > 2048) return HILS_E_UNSUPPORTED;
+    if (s->seq_len > (int64_t(1) << 31)) return HILS_E_UNSUPPORTED;
+  } else if (mode == kPrefill) {
+    if (s->seq_len / s->chunk > 4096) return HILS_E_UNSUPPORTED;  // <= 4096 chunks per sequence
+  }
+  return HILS_OK;
+}
+
+float eff_scale(const hils_shape* s) {
+  return s->scale > 0.f ? s->scale : 1.0f / std::sqrt((float)s->head_dim);
+}
+
+hils_status from_hip(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_E_LAUNCH; }
+
+size_t attend_min_ws(const hils_shape* s, size_t* full) {
+  size_t fixed, per;
+  hils::attend_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk, s->head_dim,
+                         s->top_k, s->io_dtype == HILS_BF16, &fixed, &per);
+  if (full) *full = fixed + per * (size_t)s->heads_kv;
+  return fixed + per;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hils_abi_version(void) { return HILS_ABI_VERSION; }
+
+const char* hils_status_string(hils_status st) {
+  switch (st) {
+    case HILS_OK: return "ok";
+    case HILS_E_NULL: return "a required pointer is NULL";
+    case HILS_E_SHAPE: return "inconsistent or out-of-range sizes";
+    case HILS_E_DTYPE: return "unknown dtype code";
+    case HILS_E_ALIGN: return "tensor pointer not 16-byte aligned";
+    case HILS_E_WORKSPACE: return "workspace missing or too small";
+    case HILS_E_POS: return "decode position outside the cache";
+    case HILS_E_NEED_QLAND: return "a chunk completes but no landmark query was given";
+    case HILS_E_UNSUPPORTED: return "configuration not supported by this build";
+    case HILS_E_LAUNCH: return "the HIP runtime refused a launch";
+  }
+  return "unknown status";
+}
+
+size_t hils_workspace_bytes(const hils_shape* s, hils_op op) {
+  const Mode m = op == HILS_OP_DECODE ? kDecode : op == HILS_OP_SUMMARIZE ? kSummarize : kPrefill;
+  if (check_shape(s, m) != HILS_OK) return 0;
+  switch (op) {
+    case HILS_OP_SUMMARIZE: return 0;
+    case HILS_OP_SELECT:
+      return hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
+                                    nullptr, nullptr);
+    case HILS_OP_ATTEND_FUSE: {
+      size_t full = 0;
+      attend_min_ws(s, &full);
+      return full;
+    }
+    case HILS_OP_DECODE:
+      return hils::decode_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
+                                    s->window, s->head_dim, s->top_k);
+  }
+  return 0;
+}
+
+hils_status hils_summarize(const hils_shape* s, const void* k, const void* q_land,
+                           int64_t chunk_begin, int64_t n_chunks, void* k_sum, float* b_sum,
+                           hipStream_t stream) {
+  const hils_status st = check_shape(s, kSummarize);
+  if (st != HILS_OK) return st;
+  if (!k || !q_land || !k_sum || !b_sum) return HILS_E_NULL;
+  if (!aligned16(k) || !aligned16(q_land) || !aligned16(k_sum) || !aligned16(b_sum)) return HILS_E_ALIGN;
+  const int64_t NC = s->seq_len / s->chunk;
+  if (chunk_begin < 0 || n_chunks < 0 || chunk_begin + n_chunks > NC) return HILS_E_SHAPE;
+  if (n_chunks > 0x7fffffff) return HILS_E_UNSUPPORTED;
+  if (n_chunks == 0) return HILS_OK;
+  hils::SumArgs a{};
+  a.k = k; a.ql = q_land; a.ksum = k_sum; a.bsum = b_sum;
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim;
+  a.bf16 = s->io_dtype == HILS_BF16;
+  a.kT = s->seq_len; a.NCs = NC;
+  a.ql_sb = (int64_t)s->heads_q * NC * s->head_dim;
+  a.ql_sh = NC * s->head_dim;
+  a.ql_sc = s->head_dim;
+  a.c0 = chunk_begin; a.n_chunks = n_chunks;
+  a.scale = eff_scale(s);
+  a.list.n = 0;
+  return from_hip(hils::launch_summarize(a, stream));
+}
+
+hils_status hils_select(const hils_shape* s, const void* q_hat, const void* k_sum,
+                        const float* b_sum, int32_t* sel_idx, float* sel_score, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  const hils_status st = check_shape(s, kPrefill);
+  if (st != HILS_OK) return st;
+  const bool has_chunks = s->seq_len / s->chunk > 0;  // no complete chunk: no summaries to read
+  if (!q_hat || (has_chunks && (!k_sum || !b_sum)) || (s->top_k > 0 && (!sel_idx || !sel_score)))
+    return HILS_E_NULL;
+  if (!aligned16(q_hat) || !aligned16(k_sum) || !aligned16(b_sum) || !aligned16(sel_idx) ||
+      !aligned16(sel_score))
+    return HILS_E_ALIGN;
+  if (s->top_k == 0) return HILS_OK;  // nothing to select
+  int n_slots = 0;
+  int64_t stride = 0;
+  const size_t need = hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len,
+                                             s->chunk, &n_slots, &stride);
+  if (!ws || ws_bytes < need) return HILS_E_WORKSPACE;
+  hils::SelArgs a{};
+  a.qh = q_hat; a.ksum = k_sum; a.bsum = b_sum; a.idx = sel_idx; a.ssel = sel_score;
+  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+  a.scratch = reinterpret_cast<float*>(w);
+  a.L = reinterpret_cast<float*>(w + (size_t)n_slots * stride * sizeof(float));
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
+  a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
+  a.T = s->seq_len; a.NCs = s->seq_len / s->chunk; a.scale = eff_scale(s);
+  a.n_slots = n_slots; a.slot_stride = stride;
+  return from_hip(hils::launch_select(a, stream));
+}
+
+hils_status hils_attend_fuse(const hils_shape* s, const void* q, const void* k, const void* v,
+                             const int32_t* sel_idx, const float* sel_score, void* out, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  const hils_status st = check_shape(s, kPrefill);
+  if (st != HILS_OK) return st;
+  if (!q || !k || !v || !out || (s->top_k > 0 && (!sel_idx || !sel_score))) return HILS_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse) ||
+      !aligned16(sel_idx) || !aligned16(sel_score))
+    return HILS_E_ALIGN;
+  if (s->seq_len > (int64_t(1) << 25)) return HILS_E_UNSUPPORTED;
+  const size_t need = attend_min_ws(s, nullptr);
+  if (!ws || ws_bytes < need) return HILS_E_WORKSPACE;
+  hils::AttArgs a{};
+  a.q = q; a.k = k; a.v = v; a.idx = sel_idx; a.ssel = sel_score; a.out = out; a.lse = lse;
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
+  a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
+  a.T = s->seq_len; a.scale = eff_scale(s); a.ws = ws; a.ws_bytes = ws_bytes;
+  return from_hip(hils::launch_attend(a, stream));
+}
+
+hils_status hils_decode_step(const hils_shape* s, const int64_t* pos, const void* q,
+                             const void* q_hat, const void* k_new, const void* v_new,
+                             const void* q_land_new, void* k_cache, void* v_cache, void* k_sum,
+                             float* b_sum, void* out, float* lse, int32_t* sel_idx, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  const hils_status st = check_shape(s, kDecode);
+  if (st != HILS_OK) return st;
+  if (!pos || !q || !q_hat || !k_new || !v_new || !k_cache || !v_cache || !k_sum || !b_sum || !out)
+    return HILS_E_NULL;
+  if (!aligned16(q) || !aligned16(q_hat) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned16(q_land_new) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_sum) ||
+      !aligned16(b_sum) || !aligned16(out) || !aligned16(lse) || !aligned16(sel_idx))
+    return HILS_E_ALIGN;
+  bool completes = false;
+  for (int b = 0; b < s->batch; ++b) {
+    if (pos[b] < 0 || pos[b] >= s->seq_len) return HILS_E_POS;
+    if ((pos[b] + 1) % s->chunk == 0) completes = true;
+  }
+  if (completes && !q_land_new) return HILS_E_NEED_QLAND;
+  const size_t need = hils::decode_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len,
+                                             s->chunk, s->window, s->head_dim, s->top_k);
+  if (!ws || ws_bytes < need) return HILS_E_WORKSPACE;
+  hils::DecArgs a{};
+  a.pos = pos; a.q = q; a.qh = q_hat; a.k_new = k_new; a.v_new = v_new; a.ql_new = q_land_new;
+  a.kc = k_cache; a.vc = v_cache; a.ksum = k_sum; a.bsum = b_sum; a.out = out; a.lse = lse;
+  a.idx = sel_idx;
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
+  a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
+  a.Lcap = s->seq_len; a.scale = eff_scale(s); a.ws = ws; a.ws_bytes = ws_bytes;
+  return from_hip(hils::launch_decode(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// hils_internal.h -- launch interfaces between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hils_common.h"
+
+namespace hils {
+
+// Landmark summaries for a contiguous chunk range of every (b, head), or (decode)
+// for a list of (b, chunk) pairs whose landmark queries come from a [B, Hq, d] array.
+struct SumList {
+  int32_t n;
+  int32_t b[64];
+  int64_t c[64];
+};
+
+struct SumArgs {
+  const void* k;
+  const void* ql;
+  void* ksum;
+  float* bsum;
+  int B, Hq, Hkv, D;
+  bool bf16;
+  int64_t kT;      // key rows per KV head
+  int64_t NCs;     // chunks per head in ksum / bsum
+  int64_t ql_sb, ql_sh, ql_sc;  // landmark query strides (elements) per b, head, chunk
+  int64_t c0, n_chunks;         // range mode
+  float scale;
+  SumList list;                 // list mode when list.n > 0
+};
+hipError_t launch_summarize(const SumArgs& a, hipStream_t st);
+
+struct SelArgs {
+  const void* qh;
+  const void* ksum;
+  const float* bsum;
+  int32_t* idx;
+  float* ssel;
+  float* L;          // [B, Hq, T] scratch (G > 1)
+  float* scratch;    // rank keys, per persistent slot
+  int B, Hq, Hkv, D, S, W, topk;
+  bool bf16;
+  int64_t T, NCs;
+  float scale;
+  int n_slots;
+  int64_t slot_stride;  // floats per slot
+};
+hipError_t launch_select(const SelArgs& a, hipStream_t st);
+size_t select_workspace(int B, int Hq, int Hkv, int64_t T, int S, int* n_slots, int64_t* slot_stride);
+
+struct AttArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* idx;
+  const float* ssel;
+  void* out;
+  float* lse;
+  int B, Hq, Hkv, D, S, W, topk;
+  bool bf16;
+  int64_t T;
+  float scale;
+  void* ws;
+  size_t ws_bytes;
+};
+hipError_t launch_attend(const AttArgs& a, hipStream_t st);
+// Bytes for the index structures (fixed part) and for partial outputs of one KV head.
+void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, bool bf16,
+                      size_t* fixed, size_t* per_kv_head);
+
+struct DecArgs {
+  const int64_t* pos;  // host
+  const void* q;
+  const void* qh;
+  const void* k_new;
+  const void* v_new;
+  const void* ql_new;
+  void* kc;
+  void* vc;
+  void* ksum;
+  float* bsum;
+  void* out;
+  float* lse;
+  int32_t* idx;
+  int B, Hq, Hkv, D, S, W, topk;
+  bool bf16;
+  int64_t Lcap;
+  float scale;
+  void* ws;
+  size_t ws_bytes;
+};
+hipError_t launch_decode(const DecArgs& a, hipStream_t st);
+size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk);
+// Candidates per decode selection block and per-wave list capacity limit.
+constexpr int64_t kDecSelBlock = 4 * 64 * 32;
+
+}  // namespace hils

@@ -1,0 +1,208 @@
+/*
+ * hils.h -- C ABI of the HiLS-Attention forward path on AMD Instinct MI355X (gfx950).
+ *
+ * HiLS-Attention ("Hierarchical Sparse Attention Done Right: Toward Infinite
+ * Context Modeling") factorises causal attention hierarchically: every query
+ * attends, independently, to each retrieved chunk and to a chunk-aligned
+ * sliding window, and the per-group results are fused with weights given by
+ * learned chunk retrieval scores.  This library computes the forward pass in
+ * four calls:
+ *
+ *   hils_summarize    landmark chunk summaries (k', b')
+ *   hils_select       retrieval scores and top-k chunk selection
+ *   hils_attend_fuse  per-group attention and the fusion
+ *   hils_decode_step  all of the above for one new token per sequence
+ *
+ * Notation: B batch, Hq query heads, Hkv key/value heads, G = Hq/Hkv heads per
+ * group, d head dimension, S chunk size, W window, k top-k, T tokens,
+ * NC = floor(T/S) complete chunks, scale = 1/sqrt(d) unless given.  Token i
+ * lies in chunk floor(i/S).  The window of position i is [l_i, i] with
+ * l_i = max(0, S*floor((i-W+1)/S)) (its left edge rounded down to a chunk
+ * boundary); the candidate chunks of i are C_i = {c : (c+1)*S <= l_i}, the
+ * complete chunks left of the window (paper-body page, Block Sparse Attention
+ * preliminaries).
+ *
+ * Conventions for every call:
+ *  - Tensors are caller-owned device memory, contiguous and row-major,
+ *    head-major ([B, H, T, d]), 16-byte aligned.  The library allocates no
+ *    memory, keeps no pointer after returning and holds no mutable global
+ *    state, so calls on different streams may run concurrently as long as
+ *    their buffers are disjoint.  Scratch memory is the caller's workspace,
+ *    sized by hils_workspace_bytes().
+ *  - Every check runs on the host before anything is enqueued.  A nonzero
+ *    status means nothing was enqueued and nothing was written.  Work is
+ *    asynchronous on `stream` (NULL = the default stream); a fault inside a
+ *    kernel surfaces at the caller's next synchronisation with that stream.
+ *  - Outputs are overwritten completely (index pads -1, score pads -inf).
+ *  - Supported: d in {64, 128}; S = 64; Hq % Hkv == 0 with G in {1, 2, 4, 8};
+ *    0 <= k <= 64; W >= 1; io_dtype in {F32, BF16} and
+ *    summary_dtype == io_dtype.  Anything else returns HILS_E_UNSUPPORTED.
+ *  - Results are deterministic: the same inputs give bitwise identical
+ *    outputs on every run.
+ */
+#ifndef HILS_H_
+#define HILS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HILS_ABI_VERSION 1
+
+typedef enum {
+    HILS_OK = 0,
+    HILS_E_NULL = -1,          /* a required pointer is NULL */
+    HILS_E_SHAPE = -2,         /* inconsistent or out-of-range sizes */
+    HILS_E_DTYPE = -3,         /* unknown dtype code */
+    HILS_E_ALIGN = -4,         /* a tensor pointer is not 16-byte aligned */
+    HILS_E_WORKSPACE = -5,     /* workspace missing or smaller than required */
+    HILS_E_POS = -6,           /* decode position outside the cache */
+    HILS_E_NEED_QLAND = -7,    /* a chunk completes but no landmark query was given */
+    HILS_E_UNSUPPORTED = -8,   /* valid, but outside what this build implements */
+    HILS_E_LAUNCH = -9         /* the HIP runtime refused a launch */
+} hils_status;
+
+typedef enum { HILS_F32 = 0, HILS_BF16 = 1 } hils_dtype;
+
+typedef enum {
+    HILS_OP_SUMMARIZE = 0,
+    HILS_OP_SELECT = 1,
+    HILS_OP_ATTEND_FUSE = 2,
+    HILS_OP_DECODE = 3
+} hils_op;
+
+typedef struct {
+    int32_t batch;          /* B */
+    int32_t heads_q;        /* Hq */
+    int32_t heads_kv;       /* Hkv */
+    int32_t head_dim;       /* d */
+    int32_t chunk;          /* S */
+    int32_t window;         /* W */
+    int32_t top_k;          /* k */
+    int64_t seq_len;        /* prefill: T; decode: cache capacity Lcap (a multiple of S) */
+    float scale;            /* logit scale; 0 selects 1/sqrt(d) */
+    hils_dtype io_dtype;    /* q, q_hat, q_land, k, v, out */
+    hils_dtype summary_dtype; /* k' (b' is always fp32) */
+} hils_shape;
+
+/*
+ * Landmark chunk summaries (summary page, Methodology 1, Eq. 8; paper-body
+ * page, RQ1: the landmark token appended to a chunk supplies q'_c, and the
+ * pair (k', b') is the chunk's entropy-calibrated compressed key).
+ * For every b, query head h (KV head g = h/G) and chunk c in
+ * [chunk_begin, chunk_begin + n_chunks):
+ *     s_j = scale * q'_{h,c} . k_{g, cS+j},  j = 0..S-1,   p = softmax(s)
+ *     k'_{h,c} = sum_j p_j k_{g,cS+j}      (rounded once to summary_dtype)
+ *     b'_{h,c} = -sum_j p_j log p_j        (fp32)
+ *
+ * k       [B, Hkv, seq_len, d]      io_dtype (rows of chunks in range are read)
+ * q_land  [B, Hq,  seq_len/S, d]    io_dtype
+ * k_sum   [B, Hq,  seq_len/S, d]    summary_dtype; only the chunks in range are written
+ * b_sum   [B, Hq,  seq_len/S]       fp32; likewise
+ * Requires 0 <= chunk_begin, chunk_begin + n_chunks <= seq_len/S.  n_chunks == 0
+ * is a no-op.  Needs no workspace.
+ */
+hils_status hils_summarize(const hils_shape* shape, const void* k, const void* q_land,
+                           int64_t chunk_begin, int64_t n_chunks,
+                           void* k_sum, float* b_sum, hipStream_t stream);
+
+/*
+ * Retrieval scores and top-k selection (paper-body page, RQ1: each query scores
+ * every chunk summary by the linear surrogate of Eq. 7 and keeps the top-k;
+ * summary page, Eq. 10: s_hat = q_hat . k' / sqrt(d) + b'; paper-body page,
+ * GQA-aware chunk selection).  For every b, position i < T and group g:
+ *     s_hat_{h,i,c} = scale * q_hat_{h,i} . k'_{h,c} + b'_{h,c},   c in C_i
+ *     rank key r_c  = s_hat_{h,i,c}                              (G == 1)
+ *                   = max_{h in g} (s_hat_{h,i,c} - LSE_{c' in C_i} s_hat_{h,i,c'})   (G > 1)
+ *     Sel = the k candidates with the largest r (equal r: lower c first);
+ *           all of C_i when |C_i| <= k.
+ * The max over heads of log-normalised scores ranks chunks exactly as the max
+ * over heads of each head's softmax weights over C_i.
+ *
+ * q_hat     [B, Hq, T, d]        io_dtype (the calibrated query; pass q when none)
+ * k_sum     [B, Hq, T/S, d]      summary_dtype
+ * b_sum     [B, Hq, T/S]         fp32
+ * sel_idx   [B, Hkv, T, k]       int32 out: chunk ids ascending, -1 padded
+ * sel_score [B, Hq, T, k]        fp32 out: each head's s_hat at sel_idx, -inf padded
+ * Requires T <= 64 * 4096 (at most 4096 chunks) for this build.
+ */
+hils_status hils_select(const hils_shape* shape, const void* q_hat, const void* k_sum,
+                        const float* b_sum, int32_t* sel_idx, float* sel_score,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-group attention and fusion (summary page, Methodology 2, Eq. 10, the
+ * hierarchical softmax; paper-body page, implementation: the partition
+ * estimate combines chunk-level mass surrogates with token-level attention
+ * mass).  For every b, query head h (group g), position i:
+ *     for each selected chunk c and for the window Win_i = [l_i, i]:
+ *         s_ij = scale * q_{h,i} . k_{g,j}
+ *         log Z_gamma = LSE_j s_ij,   o_gamma = sum_j exp(s_ij - log Z_gamma) v_{g,j}
+ *     log Zhat_i = LSE({s_hat_c : c in Sel} + {log Z_win})   (the window enters
+ *                  at its true token-level log-mass)
+ *     out_i = sum_c exp(s_hat_c - log Zhat_i) o_c + exp(log Z_win - log Zhat_i) o_win
+ *     lse_i = log Zhat_i
+ * Token logits use q (not q_hat).
+ *
+ * q [B,Hq,T,d], k and v [B,Hkv,T,d]: io_dtype
+ * sel_idx [B,Hkv,T,k] and sel_score [B,Hq,T,k]: as written by hils_select
+ * (each row's valid ids ascending and < |C_i|, pads -1 at the end)
+ * out [B,Hq,T,d] io_dtype; lse [B,Hq,T] fp32 or NULL.
+ * The workspace holds per-(query, head, selected chunk) partial outputs; a
+ * workspace smaller than hils_workspace_bytes() but at least the size for one
+ * KV head runs the same computation in several passes.
+ */
+hils_status hils_attend_fuse(const hils_shape* shape, const void* q, const void* k, const void* v,
+                             const int32_t* sel_idx, const float* sel_score,
+                             void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step for every sequence of the batch (summary page, Summary:
+ * constant per-token decoding; the step is the prefill row i = pos[b] of the
+ * definitions above).  For each b with position i = pos[b]:
+ *   1. write k_new, v_new into row i of the caches;
+ *   2. select over C_i using the cached summaries and q_hat (as hils_select);
+ *   3. attend and fuse for query q over the selection and the window [l_i, i]
+ *      (which includes the new token) (as hils_attend_fuse);
+ *   4. if (i+1) % S == 0, summarise the chunk that token i completes with
+ *      q_land_new[b] into row i/S of k_sum, b_sum (as hils_summarize).  That chunk
+ *      is never a candidate of its own completing step, since W >= 1.
+ * The caller owns and advances pos.
+ *
+ * pos        host array [B]: 0 <= pos[b] < seq_len (seq_len = cache capacity)
+ * q, q_hat   [B, Hq, d]      io_dtype
+ * k_new, v_new [B, Hkv, d]   io_dtype
+ * q_land_new [B, Hq, d] io_dtype, or NULL when no sequence completes a chunk
+ *            (HILS_E_NEED_QLAND otherwise)
+ * k_cache, v_cache [B, Hkv, seq_len, d] io_dtype (rows <= pos[b] valid after step 1)
+ * k_sum [B, Hq, seq_len/S, d] summary_dtype, b_sum [B, Hq, seq_len/S] fp32:
+ *            rows of every complete chunk before pos[b] must be valid
+ * out [B, Hq, d] io_dtype; lse [B, Hq] fp32 or NULL; sel_idx [B, Hkv, k] int32 or NULL
+ */
+hils_status hils_decode_step(const hils_shape* shape, const int64_t* pos,
+                             const void* q, const void* q_hat,
+                             const void* k_new, const void* v_new, const void* q_land_new,
+                             void* k_cache, void* v_cache, void* k_sum, float* b_sum,
+                             void* out, float* lse, int32_t* sel_idx,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes `op` needs for `shape` (0 for HILS_OP_SUMMARIZE); 0 as well
+ * for an invalid shape. */
+size_t hils_workspace_bytes(const hils_shape* shape, hils_op op);
+
+/* Static, human-readable name of a status code. */
+const char* hils_status_string(hils_status status);
+
+/* HILS_ABI_VERSION of the built library. */
+int hils_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HILS_H_ */

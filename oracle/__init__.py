@@ -227,4 +227,5 @@ def to_dense(res: dict, B: int, Hq: int, Hkv: int, T: int, topk: int):
     ssel = res["ssel"].reshape(B, Hkv, T, G, topk).transpose(0, 1, 3, 2, 4).reshape(B, Hq, T, topk)
     out = res["out"].reshape(B, Hkv, T, G, d).transpose(0, 1, 3, 2, 4).reshape(B, Hq, T, d)
     lse = res["lse"].reshape(B, Hkv, T, G).transpose(0, 1, 3, 2).reshape(B, Hq, T)
-    return {"idx": idx, "gap": gap, "ncand": ncand, "ssel": ssel, "out": out, "lse": lse}
+    res = {"idx": idx, "gap": gap, "ncand": ncand, "ssel": ssel, "out": out, "lse": lse}
+    return {k: np.ascontiguousarray(v) for k, v in res.items()}

@@ -1,0 +1,112 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunk_wise_sparse_summary_amd as hils
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hils.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hils_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(hils.EXPORTS)
+    L = hils.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    L = hils.lib()
+    assert L.hils_abi_version() == 1
+    for code in hils.STATUS:
+        assert L.hils_status_string(code)
+    assert L.hils_status_string(-99) == b"unknown status"
+
+
+def _shape(**kw):
+    base = dict(B=1, Hq=32, Hkv=8, d=128, S=64, W=1024, k=32, T=131072, dtype="bf16")
+    base.update(kw)
+    return hils.Shape.make(base["B"], base["Hq"], base["Hkv"], base["d"], base["S"], base["W"],
+                           base["k"], base["T"], base["dtype"])
+
+
+def test_workspace_sizes():
+    s = _shape()
+    assert hils.hils_workspace_bytes(s, hils.OP_SUMMARIZE) == 0
+    sel = hils.hils_workspace_bytes(s, hils.OP_SELECT)
+    att = hils.hils_workspace_bytes(s, hils.OP_ATTEND_FUSE)
+    # partial outputs: B*Hq*T*k*d bf16 dominate the attend workspace
+    assert att >= 32 * 131072 * 32 * 128 * 2
+    assert 0 < sel < att
+    d = _shape(B=4, T=524544, k=32)
+    assert hils.hils_workspace_bytes(d, hils.OP_DECODE) > 4 * 32 * (524544 // 64) * 4
+    assert hils.hils_workspace_bytes(_shape(S=32), hils.OP_SELECT) == 0     # unsupported
+    assert hils.hils_workspace_bytes(_shape(Hq=12, Hkv=8), hils.OP_SELECT) == 0
+
+
+def _call_select(shape, q=16, ks=16, bs=16, idx=16, sc=16, ws=16, nws=1 << 40):
+    L = hils.lib()
+    P = ctypes.c_void_p
+    return L.hils_select(ctypes.byref(shape), P(q), P(ks), P(bs), P(idx), P(sc), P(ws), nws, None)
+
+
+def test_validation_before_launch():
+    L = hils.lib()
+    P = ctypes.c_void_p
+    assert _call_select(_shape(), q=0) == -1                       # NULL
+    assert _call_select(_shape(), q=8) == -4                       # alignment
+    assert _call_select(_shape(Hq=30)) == -2                       # Hq % Hkv
+    assert _call_select(_shape(d=96)) == -8                        # unsupported head dim
+    assert _call_select(_shape(k=65)) == -8
+    assert _call_select(_shape(T=64 * 4097)) == -8                 # > 4096 chunks
+    assert _call_select(_shape(), nws=10) == -5                    # workspace
+    bad = _shape()
+    bad.io_dtype = 7
+    assert _call_select(bad) == -3
+    neg = _shape()
+    neg.scale = -1.0
+    assert _call_select(neg) == -2
+    assert L.hils_select(None, P(16), P(16), P(16), P(16), P(16), P(16), 1 << 40, None) == -1
+    # summarize: chunk range beyond the sequence
+    s = _shape()
+    assert L.hils_summarize(ctypes.byref(s), P(16), P(16), 2047, 2, P(16), P(16), None) == -2
+    assert L.hils_summarize(ctypes.byref(s), P(16), P(16), -1, 1, P(16), P(16), None) == -2
+    assert L.hils_summarize(ctypes.byref(s), P(16), P(16), 0, 0, P(16), P(16), None) == 0  # no-op
+    # attend: workspace below one KV head's share
+    assert L.hils_attend_fuse(ctypes.byref(s), P(16), P(16), P(16), P(16), P(16), P(16), P(16),
+                              P(16), 1024, None) == -5
+
+
+def test_decode_validation():
+    L = hils.lib()
+    P = ctypes.c_void_p
+    s = _shape(B=2, T=4096, k=8, W=128)
+    ws = hils.hils_workspace_bytes(s, hils.OP_DECODE)
+    assert ws > 0
+
+    def call(pos, qland=16, nws=ws):
+        arr = (ctypes.c_int64 * 2)(*pos)
+        a = [P(16)] * 4
+        return L.hils_decode_step(ctypes.byref(s), arr, *a, P(qland), P(16), P(16), P(16), P(16),
+                                  P(16), P(16), P(16), P(16), nws, None)
+
+    assert call([0, 4096]) == -6          # position beyond the cache
+    assert call([-1, 3]) == -6
+    assert call([62, 63], qland=0) == -7  # sequence 1 completes chunk 0 and no q_land
+    assert call([5, 6], nws=ws - 1) == -5
+    s2 = _shape(B=2, T=4000, k=8, W=128)  # capacity not a multiple of S
+    arr = (ctypes.c_int64 * 2)(1, 2)
+    assert L.hils_decode_step(ctypes.byref(s2), arr, *[P(16)] * 13, 1 << 30, None) == -2
+    s3 = _shape(B=65, T=4096, k=8)
+    arr3 = (ctypes.c_int64 * 65)(*([1] * 65))
+    assert L.hils_decode_step(ctypes.byref(s3), arr3, *[P(16)] * 13, 1 << 30, None) == -8

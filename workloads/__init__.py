@@ -308,7 +308,7 @@ def make_dyadic_select(B=1, Hq=4, Hkv=1, T=512, d=64, S=16, k=8, W=32, seed=0,
     NC = T // S
     qh = rng.integers(-3, 4, size=(B, Hq, T, d)).astype(np.float32) * 2.0 ** -4
     ks = rng.integers(-3, 4, size=(B, Hq, NC, d)).astype(np.float32) * 2.0 ** -3
-    bs = rng.integers(0, 64, size=(B, Hq, NC)).astype(np.float32) * 2.0 ** -6
+    bs = rng.integers(0, 8, size=(B, Hq, NC)).astype(np.float32) * 2.0 ** -6
     if identical_heads:
         for g in range(Hkv):
             for h in range(g * G + 1, (g + 1) * G):
