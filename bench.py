@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the HiLS-Attention forward hot path on one MI355X.
+
+One step = one pass of the whole path over synthetic inputs already resident in
+HBM: a 128K-token prefill forward (hils_summarize + hils_select +
+hils_attend_fuse; B=1, 32 query / 8 KV heads, d=128, S=64, k=32, W=1024,
+per-head scales U[0.5, 2]) followed by 64 decode steps over the 512K-token
+caches of 4 sequences (hils_decode_step; k=32, W=1024).  Every call is timed
+with HIP events on the stream the library launches on (torch's current
+stream).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HiLS fwd prefill tokens/s @128K + decode µs/token @512K; % HBM/MFMA roof"
+PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # HBM3E, B/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def window_stats(T, S, W):
+    i = np.arange(T, dtype=np.int64)
+    a = i - W + 1
+    lw = np.where(a > 0, (a // S) * S, 0)
+    return lw // S, i - lw + 1       # |C_i|, |Win_i|
+
+
+def attended_flops(B, Hq, T, d, S, W, k):
+    nc, win = window_stats(T, S, W)
+    return float(B * Hq * np.sum(4.0 * d * (np.minimum(k, nc) * S + win)))
+
+
+def score_flops(B, Hq, T, d, S, W):
+    nc, _ = window_stats(T, S, W)
+    return float(B * Hq * np.sum(nc) * 2.0 * d)
+
+
+def summary_bytes(B, Hq, Hkv, T, d, S, esz=2):
+    NC = T // S
+    return float(B * Hkv * NC * S * d * esz + 2 * B * Hq * NC * d * esz + B * Hq * NC * 4)
+
+
+def decode_bytes(B, Hq, Hkv, d, S, W, k, positions, esz=2):
+    tot = 0.0
+    for i in positions:
+        a = i - W + 1
+        lw = (a // S) * S if a > 0 else 0
+        nc = lw // S
+        win = i - lw + 1
+        tot += Hq * nc * (d * esz + 4)                   # k', b' of every candidate
+        tot += Hkv * min(k, nc) * S * d * esz * 2        # selected chunks' K and V
+        tot += Hkv * win * d * esz * 2                   # window K and V
+        tot += Hq * d * esz * 3 + Hkv * d * esz * 2      # q, q_hat, out; k_new, v_new
+    return tot
+
+
+def cpu_baseline(x, wl, seconds=10.0):
+    """The fp64 oracle on the host: summaries of every chunk plus a sample of query rows."""
+    import torch
+    import oracle
+    L = oracle.lib()
+    threads = int(L.orc_max_threads())
+    k_h = x["k"].cpu()
+    ql_h = x["q_land"].cpu()
+    t0 = time.perf_counter()
+    ks, bs = oracle.summarize(k_h, ql_h, wl.S, wl.Hq, ks_round=oracle.ORND_BF16)
+    t_sum = time.perf_counter() - t0
+    v_h = x["v"].cpu()
+    T = wl.T
+    n = 8
+    while True:
+        pos = np.linspace(T // 2, T - 1, n).astype(np.int64)
+        q_rows = x["q"][:, :, pos].cpu()
+        qh_rows = x["q_hat"][:, :, pos].cpu()
+        rb, rg, rq = np.meshgrid(np.arange(wl.B), np.arange(wl.Hkv), np.arange(n), indexing="ij")
+        rb, rg, rq = rb.ravel(), rg.ravel(), rq.ravel()
+        ri = pos[rq]
+        t0 = time.perf_counter()
+        oracle.rows(rb, rg, ri, rq, q_rows, qh_rows, k_h, v_h, ks, bs, S=wl.S, W=wl.W, topk=wl.k)
+        t_rows = time.perf_counter() - t0
+        if t_rows + t_sum > seconds * 0.4 or n >= 512:
+            break
+        n *= 2
+    per_token = t_sum / T + t_rows / n
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "128K prefill: fp64 summaries of all %d chunks x %d heads (%.1f s) plus all "
+                      "%d KV groups of %d query positions from the second half of the sequence "
+                      "(%.1f s); tokens/s = 1/(t_summaries/T + t_rows/positions)"
+                      % (T // wl.S, wl.Hq, t_sum, wl.Hkv, n, t_rows)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=64,
+                    help="decode steps per bench step (64: one chunk completion per step)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the HiLS path here runs on a single device and has "
+              "no multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunk_wise_sparse_summary_amd as hils
+    import workloads as wk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = wk.CONFIGS["128k"]
+    dl = wk.CONFIGS["512k_decode"]
+    log("generating 128K prefill inputs on device")
+    x = wk.make_prefill(wl, seed=0, device=dev)
+    B, Hq, Hkv, d, S, W, k, T = wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, wl.W, wl.k, wl.T
+    NC = T // S
+    shape = hils.Shape.make(B, Hq, Hkv, d, S, W, k, T, torch.bfloat16)
+    k_sum = torch.empty((B, Hq, NC, d), dtype=torch.bfloat16, device=dev)
+    b_sum = torch.empty((B, Hq, NC), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, Hkv, T, k), dtype=torch.int32, device=dev)
+    ssel = torch.empty((B, Hq, T, k), dtype=torch.float32, device=dev)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws_sel = hils.workspace(shape, hils.OP_SELECT, dev)
+    ws_att = hils.workspace(shape, hils.OP_ATTEND_FUSE, dev)
+    log("workspaces: select %.2f GiB, attend %.2f GiB" % (ws_sel.numel() / 2**30, ws_att.numel() / 2**30))
+
+    log("generating 512K decode caches on device")
+    cache = wk.make_decode_cache(dl, seed=1, device=dev)
+    cap = cache["capacity"]
+    dshape = hils.Shape.make(dl.B, dl.Hq, dl.Hkv, dl.d, dl.S, dl.W, dl.k, cap, torch.bfloat16)
+    dks = torch.empty((dl.B, dl.Hq, cap // dl.S, dl.d), dtype=torch.bfloat16, device=dev)
+    dbs = torch.empty((dl.B, dl.Hq, cap // dl.S), dtype=torch.float32, device=dev)
+    ws_dec = hils.workspace(dshape, hils.OP_DECODE, dev)
+    L0 = cache["length"]
+    # summaries of the initial cache (also the summary-bandwidth measurement)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    sum_ms = []
+    for rep in range(3):
+        ev[0].record()
+        hils.hils_summarize(cache["k_cache"], cache["q_land"], dks, dbs, dshape, 0, L0 // dl.S)
+        ev[1].record()
+        torch.cuda.synchronize()
+        sum_ms.append(ev[0].elapsed_time(ev[1]))
+    sum_dec_bytes = summary_bytes(dl.B, dl.Hq, dl.Hkv, L0, dl.d, dl.S)
+    nsteps_total = (args.warmup + args.steps) * args.decode_steps
+    nsteps_total = min(nsteps_total, cap - L0)
+    dsteps = [wk.make_decode_step(dl, s, seed=1, device=dev) for s in range(nsteps_total)]
+    dout = torch.empty((dl.B, dl.Hq, dl.d), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((dl.B, dl.Hq), dtype=torch.float32, device=dev)
+    didx = torch.empty((dl.B, dl.Hkv, dl.k), dtype=torch.int32, device=dev)
+    dpos = [0]
+
+    names = ["summarize", "select", "attend_fuse", "decode"]
+    times = {n_: [] for n_ in names}
+
+    def step(record: bool):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        e[0].record()
+        hils.hils_summarize(x["k"], x["q_land"], k_sum, b_sum, shape)
+        e[1].record()
+        hils.hils_select(x["q_hat"], k_sum, b_sum, idx, ssel, shape, ws_sel)
+        e[2].record()
+        hils.hils_attend_fuse(x["q"], x["k"], x["v"], idx, ssel, out, lse, shape, ws_att)
+        e[3].record()
+        de = []
+        for _ in range(args.decode_steps):
+            s = dpos[0] % nsteps_total
+            dpos[0] += 1
+            st = dsteps[s]
+            p = L0 + s
+            a = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a.record()
+            hils.hils_decode_step([p] * dl.B, st["q"], st["q_hat"], st["k_new"], st["v_new"],
+                                  st["q_land_new"], cache["k_cache"], cache["v_cache"], dks, dbs,
+                                  dout, dlse, didx, dshape, ws_dec)
+            b_.record()
+            de.append((a, b_))
+        e[4].record()
+        return e, de
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    dpos[0] = 0  # decode positions restart: every timed step sees the same cache lengths
+    log("timed steps")
+    recs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        recs.append(step(True))
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = g0.elapsed_time(g1)
+    for e, de in recs:
+        times["summarize"].append(e[0].elapsed_time(e[1]))
+        times["select"].append(e[1].elapsed_time(e[2]))
+        times["attend_fuse"].append(e[2].elapsed_time(e[3]))
+        for a, b_ in de:
+            times["decode"].append(a.elapsed_time(b_))
+    avg = {n_: float(np.mean(v)) for n_, v in times.items()}
+    med = {n_: float(np.median(v)) for n_, v in times.items()}
+    ms_per_step = total_ms / args.steps
+    prefill_ms = avg["summarize"] + avg["select"] + avg["attend_fuse"]
+
+    af = attended_flops(B, Hq, T, d, S, W, k)
+    sf = score_flops(B, Hq, T, d, S, W)
+    sb = summary_bytes(B, Hq, Hkv, T, d, S)
+    dpositions = [L0 + s for s in range(args.decode_steps)]
+    db = decode_bytes(dl.B, dl.Hq, dl.Hkv, dl.d, dl.S, dl.W, dl.k, dpositions) / len(dpositions)
+    parts = {
+        "summarize": {"bound": "hbm", "work": sb, "unit": "GB/s", "peak": PEAK_HBM},
+        "select": {"bound": "mfma", "work": sf, "unit": "TFLOP/s", "peak": PEAK_BF16},
+        "attend_fuse": {"bound": "mfma", "work": af, "unit": "TFLOP/s", "peak": PEAK_BF16},
+        "decode": {"bound": "hbm", "work": db, "unit": "GB/s", "peak": PEAK_HBM},
+    }
+    per_step_ms = {"summarize": avg["summarize"], "select": avg["select"],
+                   "attend_fuse": avg["attend_fuse"],
+                   "decode": avg["decode"] * args.decode_steps}
+    dom = max(per_step_ms, key=per_step_ms.get)
+    p = parts[dom]
+    ach = p["work"] / (avg[dom] * 1e-3)
+    scale = 1e9 if p["unit"] == "GB/s" else 1e12
+    roof = {"bound": p["bound"], "kernel": "hils_" + dom, "achieved": ach / scale,
+            "peak": p["peak"] / scale, "unit": p["unit"], "frac": ach / p["peak"],
+            "traffic": None,
+            "work_per_launch": p["work"],
+            "avg_launch_ms": avg[dom]}
+    breakdown = {}
+    for n_, pp in parts.items():
+        a_ = pp["work"] / (avg[n_] * 1e-3)
+        breakdown[n_] = {"avg_ms": avg[n_], "median_ms": med[n_], "bound": pp["bound"],
+                         "achieved": a_ / (1e9 if pp["unit"] == "GB/s" else 1e12),
+                         "unit": pp["unit"], "frac": a_ / pp["peak"]}
+    tokens = B * T + dl.B * args.decode_steps
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "128K prefill (B=1, 32q/8kv, d=128, S=64, k=32, W=1024) + %d decode "
+                               "steps over 512K caches (B=4, k=32, W=1024)" % args.decode_steps,
+                   "prefill_tokens": B * T, "decode_batch": dl.B, "decode_cache_len": L0},
+        "prefill_tokens_per_s": B * T / (prefill_ms * 1e-3),
+        "prefill_ms": prefill_ms,
+        "decode_us_per_step": avg["decode"] * 1e3,
+        "decode_us_per_step_median": med["decode"] * 1e3,
+        "decode_us_per_token": avg["decode"] * 1e3 / dl.B,
+        "summary_512k_cache_GBps": sum_dec_bytes / (min(sum_ms) * 1e-3) / 1e9,
+        "roofline": roof,
+        "breakdown": breakdown,
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(x, wl)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

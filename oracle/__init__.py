@@ -67,6 +67,7 @@ def lib():
         L.orc_window_left.restype = I64
         L.orc_num_candidates.argtypes = [I64, I, I]
         L.orc_num_candidates.restype = I64
+        L.orc_max_threads.restype = I
         _lib = L
     return _lib
 

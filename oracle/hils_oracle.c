@@ -38,6 +38,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_F64 = 2 };
 enum { ORND_NONE = 0, ORND_F32 = 1, ORND_BF16 = 2 };
@@ -88,6 +91,15 @@ static int64_t floor_div(int64_t a, int64_t b) {
     int64_t q = a / b;
     if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
     return q;
+}
+
+/* Threads an OpenMP region of the oracle uses (1 without OpenMP). */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* [p1 BSA]: aligned window left edge and candidate count for position i. */
