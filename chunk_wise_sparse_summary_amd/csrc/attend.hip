@@ -16,7 +16,8 @@
 // attended by every query that selected it, in MFMA tiles of 16 (query, head)
 // rows; each visit writes its weighted output exp(s_hat_c - L_sel) o_c
 // (L_sel = LSE over the selected chunks only) to a partial slot.  The window
-// part is dense and runs query-major, flash-style, and its epilogue fuses:
+// part is dense and runs query-major, flash-style, writing o_win and log Z_win;
+// a last, fully coalesced pass fuses:
 //   out_i = exp(log Z_win - L) o_win + exp(L_sel - L) * sum_slots partial,
 //   L = LSE(L_sel, log Z_win).
 // The (query, slot) lists per chunk are built deterministically: per 64-query
@@ -28,6 +29,7 @@
 // type, are the B operand of O^T = V^T P^T with the reduction order of the
 // token axis permuted to match (V is staged transposed in LDS).
 #include "hils_internal.h"
+#include "topk.h"
 
 namespace hils {
 
@@ -148,44 +150,52 @@ __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
   }
 }
 
+
 // L_sel = LSE of each head's s_hat over its selected chunks (-inf if none).
-__global__ __launch_bounds__(256) void lsel_kernel(IdxArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)a.B * a.Hq * a.T) return;
-  const int64_t i = gid % a.T;
-  const int h = (int)((gid / a.T) % a.Hq);
-  const int b = (int)(gid / (a.T * a.Hq));
+// L lanes per row (L = smallest power of two >= k), rows of 64/L per wave.
+__global__ __launch_bounds__(256) void lsel_kernel(IdxArgs a, int L) {
+  const int64_t lane_g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = lane_g / L;
+  const int l = (int)(lane_g % L);
+  const int64_t nrows = (int64_t)a.B * a.Hq * a.T;
+  const bool live = row < nrows;
+  const int64_t rr = live ? row : nrows - 1;
+  const int64_t i = rr % a.T;
+  const int h = (int)((rr / a.T) % a.Hq);
+  const int b = (int)(rr / (a.T * a.Hq));
   const int g = h / (a.Hq / a.Hkv);
-  const float* sr = a.ssel + gid * a.topk;
-  const int32_t* ir = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * a.topk;
-  float m = kNegInf;
-  for (int s = 0; s < a.topk; ++s)
-    if (ir[s] >= 0) m = fmaxf(m, sr[s]);
-  float z = 0.f;
-  if (m != kNegInf)
-    for (int s = 0; s < a.topk; ++s)
-      if (ir[s] >= 0) z += __expf(sr[s] - m);
-  a.lsel[gid] = m == kNegInf ? kNegInf : m + __logf(z);
+  float x = kNegInf;
+  if (l < a.topk) {
+    const int32_t c = a.idx[(((int64_t)b * a.Hkv + g) * a.T + i) * a.topk + l];
+    if (c >= 0) x = a.ssel[rr * a.topk + l];
+  }
+  float m = x;
+  for (int o = 1; o < L; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+  float z = (x == kNegInf) ? 0.f : __expf(x - m);
+  for (int o = 1; o < L; o <<= 1) z += __shfl_xor(z, o, kWave);
+  if (live && l == 0) a.lsel[rr] = m == kNegInf ? kNegInf : m + __logf(z);
 }
 
-// Stage one chunk of K (row-major) and V (transposed) into LDS.
-template <typename T, int D>
-__device__ __forceinline__ void stage_chunk(const T* kc, const T* vc, T* ks, T* vt) {
+// Stage one chunk of K (row-major) and V (transposed) into LDS with NT threads.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void stage_chunk(const T* kc, const T* vc, T* ks, T* vt, int64_t nvalid) {
   constexpr int EPV = 16 / sizeof(T);
   constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
 #pragma unroll
-  for (int base = 0; base < kS * D; base += 256 * EPV) {
+  for (int base = 0; base < kS * D; base += NT * EPV) {
     const int e = base + threadIdx.x * EPV;
     const int row = e / D, col = e % D;
-    const uint4 uk = *reinterpret_cast<const uint4*>(kc + e);
+    uint4 uk = make_uint4(0, 0, 0, 0), uv = make_uint4(0, 0, 0, 0);
+    if (row < nvalid) {
+      uk = *reinterpret_cast<const uint4*>(kc + e);
+      uv = *reinterpret_cast<const uint4*>(vc + e);
+    }
     *reinterpret_cast<uint4*>(ks + row * KP + col) = uk;
-    const uint4 uv = *reinterpret_cast<const uint4*>(vc + e);
     const T* tv = reinterpret_cast<const T*>(&uv);
 #pragma unroll
     for (int t = 0; t < EPV; ++t) vt[(col + t) * VP + row] = tv[t];
   }
 }
-
 // S^T tile (64 tokens x 16 rows) for one row-fragment set bq[KS]; acc[mt][i] is the
 // logit of token 16*mt + 4*grp + i for row lane%16.
 template <typename T, int D>
@@ -236,8 +246,8 @@ template <typename T>
 __device__ __forceinline__ void store4(T* p, const f32x4_t& v, float w);
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const f32x4_t& v, float w) {
-  const uint32_t lo = (uint32_t)f2bf(v[0] * w) | ((uint32_t)f2bf(v[1] * w) << 16);
-  const uint32_t hi = (uint32_t)f2bf(v[2] * w) | ((uint32_t)f2bf(v[3] * w) << 16);
+  const uint32_t lo = pack_bf16x2(v[0] * w, v[1] * w);
+  const uint32_t hi = pack_bf16x2(v[2] * w, v[3] * w);
   *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 template <>
@@ -260,6 +270,7 @@ __device__ __forceinline__ void load4_add<float>(f32x4_t& acc, const float* p) {
   acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
 }
 
+
 struct ChunkArgs {
   const void* q;
   const void* k;
@@ -275,14 +286,20 @@ struct ChunkArgs {
   float scale;
 };
 
-// Selected chunks, chunk-major: one workgroup per (b, g, c).
+// Selected chunks, chunk-major: one workgroup per (b, g, c).  The chunk's K and V
+// are staged once; each wave takes 16-row tiles (16/G entries x G heads) of the
+// entries that selected the chunk, with the next tile's q rows prefetched.  Each
+// tile's weighted output goes through a wave-private LDS tile so that every
+// partial row (d values) is written with contiguous 16-byte stores.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
-  constexpr int KS = D / 32;
+  constexpr int KS = D / 32, MD = D / 16;
   constexpr int NE = 16 / G;  // entries per 16-row tile
   constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
+  constexpr int OP = D + 16 / (int)sizeof(T);  // padded LDS output row
   __shared__ __align__(16) T ks[kS * KP];
   __shared__ __align__(16) T vt[D * VP];
+  __shared__ __align__(16) T ot[4][16 * OP];
   const int64_t c = blockIdx.x;
   const int g = a.g0 + blockIdx.y, b = blockIdx.z;
   const int64_t bucket = ((int64_t)b * a.Hkv + g) * a.NCs + c;
@@ -291,7 +308,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   const int64_t base = a.bbase[bucket];
   const T* kc = static_cast<const T*>(a.k) + (((int64_t)b * a.Hkv + g) * a.T + c * kS) * D;
   const T* vc = static_cast<const T*>(a.v) + (((int64_t)b * a.Hkv + g) * a.T + c * kS) * D;
-  stage_chunk<T, D>(kc, vc, ks, vt);
+  stage_chunk<T, D, 256>(kc, vc, ks, vt, kS);
   __syncthreads();
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -299,23 +316,29 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   const float sl2 = a.scale * kLog2e;
   const T* qbase = static_cast<const T*>(a.q);
   T* part = static_cast<T*>(a.part);
+  T* myo = ot[wave];
   const int ntile = (n + NE - 1) / NE;
-  for (int nt = wave; nt < ntile; nt += 4) {
-    const int e = nt * NE + r16 / G, hh = r16 % G;
-    const bool valid = e < n;
-    const uint32_t word = valid ? a.entries[base + e] : 0u;
-    const int64_t i = word >> 6;
-    const int slot = word & 63;
-    const int h = g * G + hh;
-    Frag<T> bq[KS];
+  const int hh = r16 % G, h = g * G + hh;
+
+  auto load_q = [&](int nt, Frag<T> (&bq)[KS], uint32_t& word) {
+    const int e = nt * NE + r16 / G;
+    const bool valid = nt < ntile && e < n;
+    word = valid ? a.entries[base + e] : 0xffffffffu;
     if (valid) {
-      const T* qrow = qbase + (((int64_t)b * a.Hq + h) * a.T + i) * D + 8 * grp;
+      const T* qrow = qbase + (((int64_t)b * a.Hq + h) * a.T + (word >> 6)) * D + 8 * grp;
 #pragma unroll
       for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
     } else {
 #pragma unroll
       for (int kq = 0; kq < KS; ++kq) zero_frag(bq[kq]);
     }
+  };
+
+  Frag<T> bq[KS], bqn[KS];
+  uint32_t word, wordn;
+  load_q(wave, bq, word);
+  for (int nt = wave; nt < ntile; nt += 4) {
+    load_q(nt + 4, bqn, wordn);  // prefetch the next tile's rows
     f32x4_t acc[4];
     score_tile<T, D>(ks, bq, acc, r16, grp);
     float mx = kNegInf;
@@ -330,22 +353,47 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        p[mt][q4] = exp2f(acc[mt][q4] * sl2 - mx);
+        p[mt][q4] = hw_exp2(fmaf(acc[mt][q4], sl2, -mx));
         ls += p[mt][q4];
       }
     ls += __shfl_xor(ls, 16, kWave);
     ls += __shfl_xor(ls, 32, kWave);
-    f32x4_t o[D / 16];
+    f32x4_t o[MD];
 #pragma unroll
-    for (int md = 0; md < D / 16; ++md) o[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int md = 0; md < MD; ++md) o[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     pv_tile<T, D>(vt, p, o, r16, grp);
+    const bool valid = word != 0xffffffffu;
+    const int64_t i = word >> 6;
+    const int slot = word & 63;
+    float w = 0.f;
     if (valid) {
       const int64_t rowq = ((int64_t)b * a.Hq + h) * a.T + i;
-      const float w = __expf(a.ssel[rowq * a.topk + slot] - a.lsel[rowq]) / ls;
-      T* prow = part + (((((int64_t)b * a.gpass + (g - a.g0)) * G + hh) * a.T + i) * a.topk + slot) * D;
-#pragma unroll
-      for (int md = 0; md < D / 16; ++md) store4<T>(prow + 16 * md + 4 * grp, o[md], w);
+      w = __expf(a.ssel[rowq * a.topk + slot] - a.lsel[rowq]) / ls;
     }
+#pragma unroll
+    for (int md = 0; md < MD; ++md) store4<T>(myo + r16 * OP + 16 * md + 4 * grp, o[md], w);
+    wave_lds_sync();
+    // 16 rows x D values: each lane stores 16-byte pieces of one row
+    constexpr int EPV = 16 / sizeof(T);
+    constexpr int PPR = D / EPV;          // 16-byte pieces per row
+    constexpr int RPI = kWave / PPR;      // rows per store instruction
+#pragma unroll
+    for (int r0 = 0; r0 < 16; r0 += RPI) {
+      const int r = r0 + lane / PPR, piece = lane % PPR;
+      const uint32_t wr = __shfl(word, r, kWave);  // lanes r (< 16) hold row r's entry
+      if (wr != 0xffffffffu) {
+        const int rh = r % G;
+        const int64_t ri = wr >> 6;
+        const int rs = wr & 63;
+        T* prow = part + (((((int64_t)b * a.gpass + (g - a.g0)) * G + rh) * a.T + ri) * a.topk + rs) * D;
+        *reinterpret_cast<uint4*>(prow + piece * EPV) =
+            *reinterpret_cast<const uint4*>(myo + r * OP + piece * EPV);
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) bq[kq] = bqn[kq];
+    word = wordn;
   }
 }
 
@@ -353,33 +401,31 @@ struct WinArgs {
   const void* q;
   const void* k;
   const void* v;
-  const int32_t* idx;
-  const float* lsel;
-  const void* part;
-  void* out;
-  float* lse;
-  int B, Hq, Hkv, topk, g0, gpass, S, W;
+  void* ow;      // [B, Hq, T, D] normalised window output
+  float* lzw;    // [B, Hq, T] window log-mass
+  int B, Hq, Hkv, S, W;
   int64_t T;
   float scale;
 };
 
-// Window attention (query-major, dense) and the fusion with the selected partials.
-// A wave owns 64 rows = (64/G queries) x G heads as four 16-row tiles.
+// Window attention, query-major and dense (flash style).  A workgroup has 4 waves;
+// a wave owns 32 rows = two 16-row tiles of (query, head) rows, the block 128 rows.
+// Chunks fully inside every row's window skip the mask.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void window_fuse_kernel(WinArgs a) {
+__global__ __launch_bounds__(256) void window_kernel(WinArgs a) {
   constexpr int KS = D / 32, MD = D / 16;
-  constexpr int QW = 64 / G;        // queries per wave
+  constexpr int QW = 32 / G;        // queries per wave
   constexpr int QB = 4 * QW;        // queries per block
   constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
   __shared__ __align__(16) T ks[kS * KP];
   __shared__ __align__(16) T vt[D * VP];
-  const int g = a.g0 + blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
   const int64_t T_ = a.T;
   // Consecutive query tiles share most window chunks: give each XCD (blocks are
-  // dealt round-robin over the 8 XCDs) a contiguous run of tiles so they meet in
-  // one L2.
+  // dealt round-robin over the 8 XCDs) a contiguous run of tiles, so those tiles
+  // meet in one L2.
   int64_t bx = blockIdx.x;
   if (gridDim.x % 8 == 0) bx = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
   const int64_t qb0 = bx * QB;
@@ -387,11 +433,10 @@ __global__ __launch_bounds__(256) void window_fuse_kernel(WinArgs a) {
   const float sl2 = a.scale * kLog2e;
   const T* qbase = static_cast<const T*>(a.q);
 
-  // rows of tile nt: R = 16*nt + r16 -> query wave*QW + R/G, head R%G
-  int64_t ir[4], lw[4];
-  Frag<T> bq[4][KS];
+  int64_t ir[2], lw[2];
+  Frag<T> bq[2][KS];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < 2; ++nt) {
     const int R = 16 * nt + r16;
     const int64_t i = qb0 + wave * QW + R / G;
     ir[nt] = i;
@@ -402,137 +447,221 @@ __global__ __launch_bounds__(256) void window_fuse_kernel(WinArgs a) {
 #pragma unroll
     for (int kq = 0; kq < KS; ++kq) load_frag(bq[nt][kq], qrow + 32 * kq);
   }
-  float m[4], ls[4];
-  f32x4_t o[4][MD];
+  float m[2], ls[2];
+  f32x4_t o[2][MD];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < 2; ++nt) {
     m[nt] = kNegInf;
     ls[nt] = 0.f;
 #pragma unroll
     for (int md = 0; md < MD; ++md) o[nt][md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
+  const int64_t lw_max = window_left(qlast, a.S, a.W);   // window edges grow with i
   const int64_t c_lo = window_left(qb0, a.S, a.W) / kS;
   const int64_t c_hi = qlast / kS;
   const T* kbase = static_cast<const T*>(a.k) + ((int64_t)b * a.Hkv + g) * T_ * D;
   const T* vbase = static_cast<const T*>(a.v) + ((int64_t)b * a.Hkv + g) * T_ * D;
+  // The next chunk's K and V are loaded into registers while this one computes.
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int NPT = kS * D / (256 * EPV);   // 16-byte pieces per thread
+  uint4 pk[NPT], pv[NPT];
+  auto fetch = [&](int64_t c) {
+    const int64_t nvalid = T_ - c * kS;
+#pragma unroll
+    for (int t = 0; t < NPT; ++t) {
+      const int e = (t * 256 + threadIdx.x) * EPV;
+      const bool in = e / D < nvalid;
+      pk[t] = in ? *reinterpret_cast<const uint4*>(kbase + c * kS * D + e) : make_uint4(0, 0, 0, 0);
+      pv[t] = in ? *reinterpret_cast<const uint4*>(vbase + c * kS * D + e) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int t = 0; t < NPT; ++t) {
+      const int e = (t * 256 + threadIdx.x) * EPV;
+      const int row = e / D, col = e % D;
+      *reinterpret_cast<uint4*>(ks + row * KP + col) = pk[t];
+      const T* tv = reinterpret_cast<const T*>(&pv[t]);
+#pragma unroll
+      for (int q = 0; q < EPV; ++q) vt[(col + q) * VP + row] = tv[q];
+    }
+  };
+  fetch(c_lo);
   for (int64_t c = c_lo; c <= c_hi; ++c) {
     __syncthreads();
-    if ((c + 1) * kS <= T_) {
-      stage_chunk<T, D>(kbase + c * kS * D, vbase + c * kS * D, ks, vt);
-    } else {
-      // trailing partial chunk: stage the valid rows, zero the rest
-      constexpr int EPV = 16 / sizeof(T);
-      for (int e = threadIdx.x * EPV; e < kS * D; e += 256 * EPV) {
-        const int row = e / D, col = e % D;
-        const bool ok = c * kS + row < T_;
-        uint4 uk = make_uint4(0, 0, 0, 0), uv = make_uint4(0, 0, 0, 0);
-        if (ok) {
-          uk = *reinterpret_cast<const uint4*>(kbase + c * kS * D + e);
-          uv = *reinterpret_cast<const uint4*>(vbase + c * kS * D + e);
-        }
-        *reinterpret_cast<uint4*>(ks + row * KP + col) = uk;
-        const T* tv = reinterpret_cast<const T*>(&uv);
-        for (int t = 0; t < EPV; ++t) vt[(col + t) * VP + row] = tv[t];
-      }
-    }
+    commit();
+    if (c < c_hi) fetch(c + 1);
     __syncthreads();
     const int64_t j0 = c * kS;
+    // no row masks a token of this chunk: its left edge is at or past every row's
+    // window edge, and its last token precedes every row's query
+    const bool full = j0 >= lw_max && j0 + kS - 1 <= qb0;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      // skip tiles with no row whose window meets this chunk (uniform per wave)
+    for (int nt = 0; nt < 2; ++nt) {
       f32x4_t acc[4];
       score_tile<T, D>(ks, bq[nt], acc, r16, grp);
       float x[4][4], mx = kNegInf;
+      if (full) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int64_t j = j0 + 16 * mt + 4 * grp + q4;
-          const bool ok = j >= lw[nt] && j <= ir[nt] && ir[nt] < T_;
-          x[mt][q4] = ok ? acc[mt][q4] * sl2 : kNegInf;
-          mx = fmaxf(mx, x[mt][q4]);
-        }
+          for (int q4 = 0; q4 < 4; ++q4) {
+            x[mt][q4] = acc[mt][q4] * sl2;
+            mx = fmaxf(mx, x[mt][q4]);
+          }
+      } else {
+        const int lo = (int)max<int64_t>(lw[nt] - j0, -1);
+        const int hi = ir[nt] < T_ ? (int)min<int64_t>(ir[nt] - j0, kS) : -1;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int t = 16 * mt + 4 * grp + q4;
+            x[mt][q4] = (t >= lo && t <= hi) ? acc[mt][q4] * sl2 : kNegInf;
+            mx = fmaxf(mx, x[mt][q4]);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float mn = fmaxf(m[nt], mx);
-      const float alpha = (m[nt] == mn) ? 1.f : exp2f(m[nt] - mn);
       float p[4][4], psum = 0.f;
+      if (mn == kNegInf) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          p[mt][q4] = x[mt][q4] == kNegInf ? 0.f : exp2f(x[mt][q4] - mn);
-          psum += p[mt][q4];
-        }
-      ls[nt] = ls[nt] * alpha + psum;
+          for (int q4 = 0; q4 < 4; ++q4) p[mt][q4] = 0.f;
+      } else {
+        const float alpha = hw_exp2(m[nt] - mn);   // 0 when m was -inf
 #pragma unroll
-      for (int md = 0; md < MD; ++md) o[nt][md] *= alpha;
-      m[nt] = mn;
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            p[mt][q4] = hw_exp2(x[mt][q4] - mn);
+            psum += p[mt][q4];
+          }
+        ls[nt] = ls[nt] * alpha + psum;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[nt][md] *= alpha;
+        m[nt] = mn;
+      }
       pv_tile<T, D>(vt, p, o[nt], r16, grp);
     }
   }
-
-  // epilogue: window log-mass, fusion with the selected partials
-  const int gl = g - a.g0;
-  const T* part = static_cast<const T*>(a.part);
-  T* outp = static_cast<T*>(a.out);
+  T* owp = static_cast<T*>(a.ow);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < 2; ++nt) {
     const int R = 16 * nt + r16;
-    const int hh = R % G, h = g * G + hh;
+    const int h = g * G + R % G;
     const int64_t i = ir[nt];
     float lsum = ls[nt];
     lsum += __shfl_xor(lsum, 16, kWave);
     lsum += __shfl_xor(lsum, 32, kWave);
     if (i >= T_) continue;
-    const float logzw = (m[nt] + __log2f(lsum)) * kLn2;
     const int64_t rowq = ((int64_t)b * a.Hq + h) * T_ + i;
-    const float lsel = a.lsel ? a.lsel[rowq] : kNegInf;
-    const float L = lsel == kNegInf ? logzw
-                                    : fmaxf(lsel, logzw) + __logf(1.f + __expf(-fabsf(lsel - logzw)));
-    const float ww = __expf(logzw - L) / lsum;
-    const float wsel = lsel == kNegInf ? 0.f : __expf(lsel - L);
-    f32x4_t sacc[MD];
+    const float inv = 1.f / lsum;
 #pragma unroll
-    for (int md = 0; md < MD; ++md) sacc[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * T_ + i) * a.topk;
-    const T* prow = part + ((((int64_t)b * a.gpass + gl) * G + hh) * T_ + i) * a.topk * D;
-    for (int s = 0; s < a.topk; ++s) {
-      if (irow[s] < 0) continue;
-#pragma unroll
-      for (int md = 0; md < MD; ++md) load4_add<T>(sacc[md], prow + s * D + 16 * md + 4 * grp);
-    }
-    T* orow = outp + rowq * D;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      f32x4_t r;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) r[q4] = o[nt][md][q4] * ww + sacc[md][q4] * wsel;
-      store4<T>(orow + 16 * md + 4 * grp, r, 1.f);
-    }
-    if (a.lse && grp == 0) a.lse[rowq] = L;
+    for (int md = 0; md < MD; ++md) store4<T>(owp + rowq * D + 16 * md + 4 * grp, o[nt][md], inv);
+    if (grp == 0) a.lzw[rowq] = (m[nt] + hw_log2(lsum)) * kLn2;
   }
 }
 
+struct CombArgs {
+  const void* ow;
+  const float* lzw;
+  const float* lsel;
+  const int32_t* idx;
+  const void* part;
+  void* out;
+  float* lse;
+  int B, Hq, Hkv, topk, g0, gpass;
+  int64_t T;
+};
+
+// Fusion: out = exp(log Z_win - L) o_win + exp(L_sel - L) * sum of the selected
+// partials, L = LSE(L_sel, log Z_win).  PPR lanes per row, 16 bytes each.
 template <typename T, int D, int G>
-hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, int gpp,
-                            hipStream_t st) {
+__global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int PPR = D / EPV;
+  const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t rowl = gl / PPR;          // row within this pass: (b, g - g0, hh, i)
+  const int piece = (int)(gl % PPR);
+  const int64_t nrows = (int64_t)a.B * a.gpass * G * a.T;
+  if (rowl >= nrows) return;
+  const int64_t i = rowl % a.T;
+  const int hh = (int)((rowl / a.T) % G);
+  const int gi = (int)((rowl / (a.T * G)) % a.gpass);
+  const int b = (int)(rowl / (a.T * G * a.gpass));
+  const int g = a.g0 + gi;
+  if (g >= a.Hkv) return;
+  const int h = g * G + hh;
+  const int64_t rowq = ((int64_t)b * a.Hq + h) * a.T + i;
+  const float lz = a.lzw[rowq];
+  const float ls = a.lsel ? a.lsel[rowq] : kNegInf;
+  const float L = ls == kNegInf ? lz : fmaxf(ls, lz) + __logf(1.f + __expf(-fabsf(ls - lz)));
+  const float ww = __expf(lz - L);
+  const float wsel = ls == kNegInf ? 0.f : __expf(ls - L);
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+  float ows[EPV];
+  {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.ow) + rowq * D + piece * EPV);
+    const T* t = reinterpret_cast<const T*>(&u);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) ows[e] = to_f<T>(t[e]);
+  }
+  if (wsel > 0.f) {
+    const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * a.topk;
+    const T* prow = static_cast<const T*>(a.part) +
+                    ((((int64_t)b * a.gpass + gi) * G + hh) * a.T + i) * a.topk * D + piece * EPV;
+    for (int s = 0; s < a.topk; ++s) {
+      if (irow[s] < 0) continue;
+      const uint4 u = *reinterpret_cast<const uint4*>(prow + (int64_t)s * D);
+      const T* t = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
+    }
+  }
+  float r[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) r[e] = ows[e] * ww + acc[e] * wsel;
+  T res[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) res[e] = from_f<T>(r[e]);
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.out) + rowq * D + piece * EPV) =
+      *reinterpret_cast<const uint4*>(res);
+  if (a.lse && piece == 0) a.lse[rowq] = L;
+}
+
+template <typename T, int D, int G>
+hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, void* ow, float* lzw,
+                            int gpp, hipStream_t st) {
+  // window part for every head at once
+  {
+    WinArgs wa{a.q, a.k, a.v, ow, lzw, a.B, a.Hq, a.Hkv, a.S, a.W, a.T, a.scale};
+    const int QB = 4 * (32 / G);
+    hipLaunchKernelGGL((window_kernel<T, D, G>), dim3((unsigned)((a.T + QB - 1) / QB), a.Hkv, a.B),
+                       dim3(256), 0, st, wa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   for (int g0 = 0; g0 < a.Hkv; g0 += gpp) {
     const int gp = min(gpp, a.Hkv - g0);
-    ChunkArgs ca{a.q, a.k, a.v, a.ssel, ia.lsel, ia.bcount, ia.bbase, ia.entries, part,
-                 a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, a.scale};
     if (ia.NCs > 0 && a.topk > 0) {
+      ChunkArgs ca{a.q, a.k, a.v, a.ssel, ia.lsel, ia.bcount, ia.bbase, ia.entries, part,
+                   a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, a.scale};
       hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)ia.NCs, gp, a.B), dim3(256),
                          0, st, ca);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    WinArgs wa{a.q, a.k, a.v, a.idx, ia.lsel, part, a.out, a.lse, a.B, a.Hq, a.Hkv, a.topk,
-               g0, gpp, a.S, a.W, a.T, a.scale};
-    const int QB = 4 * (64 / G);
-    hipLaunchKernelGGL((window_fuse_kernel<T, D, G>), dim3((unsigned)((a.T + QB - 1) / QB), gp, a.B),
-                       dim3(256), 0, st, wa);
+    CombArgs cb{ow, lzw, ia.lsel, a.idx, part, a.out, a.lse, a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T};
+    constexpr int PPR = D / (16 / (int)sizeof(T));
+    const int64_t nthreads = (int64_t)a.B * gpp * G * a.T * PPR;
+    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3((unsigned)((nthreads + 255) / 256)), dim3(256),
+                       0, st, cb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -540,12 +669,13 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, int
 }
 
 template <typename T, int D>
-hipError_t launch_attend_t(const AttArgs& a, const IdxArgs& ia, void* part, int gpp, hipStream_t st) {
+hipError_t launch_attend_t(const AttArgs& a, const IdxArgs& ia, void* part, void* ow, float* lzw,
+                           int gpp, hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, gpp, st);
-    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, gpp, st);
-    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, gpp, st);
-    default: return launch_attend_tg<T, D, 8>(a, ia, part, gpp, st);
+    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, ow, lzw, gpp, st);
+    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, ow, lzw, gpp, st);
+    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, ow, lzw, gpp, st);
+    default: return launch_attend_tg<T, D, 8>(a, ia, part, ow, lzw, gpp, st);
   }
 }
 
@@ -557,14 +687,17 @@ void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
                       size_t* fixed, size_t* per_kv_head) {
   const int64_t NCs = T / S;
   const int64_t ntiles = (T + 63) / 64;
+  const size_t esz = bf16 ? 2 : 4;
   size_t f = 0;
   f += align256((size_t)B * Hkv * ntiles * NCs * sizeof(int32_t));  // tile_cnt
   f += align256((size_t)B * Hkv * NCs * sizeof(int32_t));           // bcount
   f += align256((size_t)B * Hkv * NCs * sizeof(int64_t));           // bbase
   f += align256((size_t)B * Hkv * T * topk * sizeof(uint32_t));     // entries
   f += align256((size_t)B * Hq * T * sizeof(float));                // lsel
+  f += align256((size_t)B * Hq * T * D * esz);                      // window outputs
+  f += align256((size_t)B * Hq * T * sizeof(float));                // window log-mass
   *fixed = f + 256;
-  *per_kv_head = align256((size_t)B * (Hq / Hkv) * T * topk * D * (bf16 ? 2 : 4));
+  *per_kv_head = align256((size_t)B * (Hq / Hkv) * T * topk * D * esz);
 }
 
 hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
@@ -572,6 +705,7 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   attend_workspace(a.B, a.Hq, a.Hkv, a.T, a.S, a.D, a.topk, a.bf16, &fixed, &per);
   const int64_t NCs = a.T / a.S;
   const int64_t ntiles = (a.T + 63) / 64;
+  const size_t esz = a.bf16 ? 2 : 4;
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(a.ws) + 255) & ~(uintptr_t)255);
   IdxArgs ia{};
   ia.idx = a.idx;
@@ -585,6 +719,10 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   ia.entries = reinterpret_cast<uint32_t*>(w);
   w += align256((size_t)a.B * a.Hkv * a.T * a.topk * sizeof(uint32_t));
   ia.lsel = reinterpret_cast<float*>(w);
+  w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
+  void* ow = w;
+  w += align256((size_t)a.B * a.Hq * a.T * a.D * esz);
+  float* lzw = reinterpret_cast<float*>(w);
   w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
   ia.B = a.B; ia.Hq = a.Hq; ia.Hkv = a.Hkv; ia.topk = a.topk;
   ia.T = a.T; ia.NCs = NCs; ia.ntiles = ntiles;
@@ -603,15 +741,17 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
   }
   if (a.topk > 0) {
-    const int64_t nrow = (int64_t)a.B * a.Hq * a.T;
-    hipLaunchKernelGGL(lsel_kernel, dim3((unsigned)((nrow + 255) / 256)), dim3(256), 0, st, ia);
+    int L = 1;
+    while (L < a.topk) L <<= 1;
+    const int64_t nl = (int64_t)a.B * a.Hq * a.T * L;
+    hipLaunchKernelGGL(lsel_kernel, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0, st, ia, L);
   } else {
     ia.lsel = nullptr;  // no selection: the window is the whole normaliser
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, gpp, st);
-  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, gpp, st) : launch_attend_t<float, 64>(a, ia, part, gpp, st);
+  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, ow, lzw, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, ow, lzw, gpp, st);
+  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, ow, lzw, gpp, st) : launch_attend_t<float, 64>(a, ia, part, ow, lzw, gpp, st);
 }
 
 }  // namespace hils

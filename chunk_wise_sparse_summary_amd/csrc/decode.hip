@@ -3,21 +3,25 @@
 // The step is the prefill row i = pos[b] of the same definitions (summary page,
 // Summary and Methodology; paper-body page, RQ1 and GQA-aware selection).  One
 // query has little work per byte, so every kernel here streams memory:
-//   dec_score   appends k_new/v_new to the caches, resets this step's counters,
-//               and scores every candidate chunk of every head of the sequence:
-//               s_hat = scale * q_hat . k' + b' (16 lanes per k' row, 16-byte
-//               loads), writing s_hat and per-slice (max, sum exp) partials.
+//   dec_score   appends k_new/v_new to the caches and
+//               scores every candidate chunk of every head of the group:
+//               s_hat = scale * q_hat . k' + b'.  A lane owns one k' row (16-byte
+//               loads, all issued before use), q_hat sits in LDS.  Writes s_hat
+//               and per-slice (max, sum exp) partials of each head's LSE.
 //               Reading all of k' once dominates the step's bytes.
-//   dec_select  per (b, group, slice of candidates): L_h from the partials, the
-//               GQA rank key, a wave top-k per 64*J candidates; the last block of
-//               the (b, group) (atomic ticket) merges the per-wave lists into the
-//               final top-k, ascending, and gathers each head's s_hat.
-//   dec_attend  one block per (b, group, work item), an item being a selected
-//               chunk or a window chunk; each wave is one head: 64 keys, softmax
-//               statistics and o = sum p v.  The last block of the (b, group)
-//               fuses: L = LSE(s_hat over Sel + {log Z_win}),
+//   dec_span    one wave per span of 64*J candidates of a (b, group): L_h from the
+//               partials, the rank key, the span's top-k list.
+//   dec_merge   one wave per (b, group): the span lists' top-k, ascending, and each
+//               head's s_hat on it.
+//   dec_attend  one workgroup per (b, group, work item), an item being a selected
+//               chunk or a window chunk.  The chunk's K and V are staged once in
+//               LDS for all G heads; wave h computes head h's 64 logits, softmax
+//               statistics and o = sum p v.
+//   dec_fuse    one wave per (b, head): L = LSE(s_hat over Sel + {log Z_win}),
 //               out = sum exp(s_hat_c - L) o_c + exp(log Z_win - L) o_win.
 //   summarize   (list mode) chunks completed by this step's token.
+// Stages hand over through kernel boundaries: a device-wide fence per block (a
+// last-block ticket) costs an L2 write-back on a multi-XCD part.
 #include "hils_internal.h"
 #include "topk.h"
 
@@ -26,9 +30,8 @@ namespace hils {
 namespace {
 
 constexpr int kS = 64;
-constexpr int kSlice = 256;   // candidates per scoring block
-constexpr int kJ = 32;        // candidates per lane in dec_select (wave: 2048)
-constexpr int kSelBlock = 4 * 64 * kJ;  // candidates per select block
+constexpr int kSlice = 256;   // candidates per scoring workgroup (4 waves x 64 lanes)
+constexpr int kMergeJ = 32;   // the merge wave holds up to 64*32 span-list entries
 
 struct DecPos {
   int64_t p[64];
@@ -36,13 +39,12 @@ struct DecPos {
 
 struct DecWs {
   float* shat;        // [B, Hq, NCcap]
-  float2* lpart;      // [B, Hq, nslice] (max2, sum) in log2 units
-  uint64_t* cand;     // [B, Hkv, nsel_blocks, 4, topk]
+  float2* lpart;      // [B, Hq, nslice] (max, sum) in log2 units
+  uint64_t* cand;     // [B, Hkv, nspan, topk]
   int32_t* idx;       // [B, Hkv, topk]
   float* ssel;        // [B, Hq, topk]
   float* apart;       // [B, Hkv, nitems, G, D + 2]
-  uint32_t* ctr;      // [B, Hkv, 2]
-  int nslice, nselb, nitems;
+  int nslice, nspan, span, nitems;
 };
 
 struct DecKArgs {
@@ -64,242 +66,184 @@ struct DecKArgs {
   float scale;
 };
 
-template <typename T, int D>
+__device__ __forceinline__ void lse_merge(float& M, float& Z, float mo, float so) {
+  const float mn = fmaxf(M, mo);
+  if (mn != kNegInf)
+    Z = (M == kNegInf ? 0.f : Z * hw_exp2(M - mn)) + (mo == kNegInf ? 0.f : so * hw_exp2(mo - mn));
+  M = mn;
+}
+
+template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void dec_score_kernel(DecKArgs a) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int NV = D / EPV;  // 16-byte loads per k' row
+  __shared__ float qs[G][D];
+  __shared__ float red[G][4][2];
   const int slice = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = a.Hq / a.Hkv;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t i = a.pos.p[b];
   const int64_t nc = num_candidates(i, a.S, a.W);
+  const int64_t bg = (int64_t)b * a.Hkv + g;
   if (slice == 0) {
-    // append this step's key/value row and reset the step's tickets
-    constexpr int EPV = 16 / sizeof(T);
-    const int64_t row = (((int64_t)b * a.Hkv + g) * a.Lcap + i) * D;
-    const T* kn = static_cast<const T*>(a.k_new) + ((int64_t)b * a.Hkv + g) * D;
-    const T* vn = static_cast<const T*>(a.v_new) + ((int64_t)b * a.Hkv + g) * D;
+    // append this step's key/value row
+    const int64_t row = (bg * a.Lcap + i) * D;
+    const T* kn = static_cast<const T*>(a.k_new) + bg * D;
+    const T* vn = static_cast<const T*>(a.v_new) + bg * D;
     for (int e = threadIdx.x * EPV; e < D; e += blockDim.x * EPV) {
       *reinterpret_cast<uint4*>(static_cast<T*>(a.kc) + row + e) = *reinterpret_cast<const uint4*>(kn + e);
       *reinterpret_cast<uint4*>(static_cast<T*>(a.vc) + row + e) = *reinterpret_cast<const uint4*>(vn + e);
     }
-    if (threadIdx.x < 2) a.w.ctr[((int64_t)b * a.Hkv + g) * 2 + threadIdx.x] = 0u;
   }
   const int64_t c0 = (int64_t)slice * kSlice;
   if (c0 >= nc) {
-    // empty slice: neutral LSE partials
     for (int hh = threadIdx.x; hh < G; hh += blockDim.x)
       a.w.lpart[((int64_t)b * a.Hq + g * G + hh) * a.w.nslice + slice] = make_float2(kNegInf, 0.f);
     return;
   }
-  constexpr int EPV = 16 / sizeof(T);
-  constexpr int LPR = D / EPV;            // lanes per k' row (16 for bf16 d=128)
-  constexpr int RPW = kWave / LPR;        // rows per wave step
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int sub = lane % LPR, rsub = lane / LPR;
-  __shared__ float red[4][2];
-  const int64_t c1 = min(c0 + kSlice, nc);
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x)
+    qs[e / D][e % D] = to_f<T>(static_cast<const T*>(a.qh)[((int64_t)b * a.Hq + g * G) * D + e]);
+  __syncthreads();
+  const int64_t c = c0 + wave * kWave + lane;
+  const bool ok = c < nc;
+  const int64_t cl = ok ? c : nc - 1;
+#pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
-    float qv[EPV];
-    {
-      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) +
-                                                      ((int64_t)b * a.Hq + h) * D + sub * EPV);
-      const T* t = reinterpret_cast<const T*>(&u);
+    const T* krow = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * a.NCcap + cl) * D;
+    uint4 u[NV];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) qv[e] = to_f<T>(t[e]);
+    for (int v = 0; v < NV; ++v) u[v] = *reinterpret_cast<const uint4*>(krow + v * EPV);
+    const float bv = a.bsum[((int64_t)b * a.Hq + h) * a.NCcap + cl];
+    float acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const T* t = reinterpret_cast<const T*>(&u[v]);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc = fmaf(qs[hh][v * EPV + e], to_f<T>(t[e]), acc);
     }
-    const T* kb = static_cast<const T*>(a.ksum) + ((int64_t)b * a.Hq + h) * a.NCcap * D;
-    const float* bb = a.bsum + ((int64_t)b * a.Hq + h) * a.NCcap;
-    float* sh = a.w.shat + ((int64_t)b * a.Hq + h) * a.NCcap;
-    float m2 = kNegInf, s2 = 0.f;
-    // rows c = c0 + (wave * RPW + rsub) + 4*RPW*step
-    for (int64_t cb = c0 + wave * RPW; cb < c1; cb += 4 * RPW * 4) {
-      uint4 u[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t c = cb + rsub + (int64_t)r * 4 * RPW;
-        u[r] = c < c1 ? *reinterpret_cast<const uint4*>(kb + c * D + sub * EPV) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t c = cb + rsub + (int64_t)r * 4 * RPW;
-        const T* t = reinterpret_cast<const T*>(&u[r]);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc = fmaf(qv[e], to_f<T>(t[e]), acc);
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, kWave);
-        if (c < c1) {
-          const float s = fmaf(acc, a.scale, bb[c]);
-          if (sub == 0) sh[c] = s;
-          const float x = s * kLog2e;
-          const float mn = fmaxf(m2, x);
-          s2 = (m2 == mn ? s2 : s2 * exp2f(m2 - mn)) + exp2f(x - mn);
-          m2 = mn;
-        }
-      }
+    const float s = fmaf(acc, a.scale, bv);
+    if (ok) a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + c] = s;
+    const float x = ok ? s * kLog2e : kNegInf;
+    const float m = wave_max(x);
+    const float z = wave_sum(x == kNegInf ? 0.f : hw_exp2(x - m));
+    if (lane == 0) {
+      red[hh][wave][0] = m;
+      red[hh][wave][1] = z;
     }
-    // combine: lanes with sub == 0 hold partial (m2, s2) for their rows (others duplicate)
-    if (sub != 0) { m2 = kNegInf; s2 = 0.f; }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float mo = __shfl_xor(m2, o, kWave), so = __shfl_xor(s2, o, kWave);
-      const float mn = fmaxf(m2, mo);
-      if (mn != kNegInf)
-        s2 = (m2 == kNegInf ? 0.f : s2 * exp2f(m2 - mn)) + (mo == kNegInf ? 0.f : so * exp2f(mo - mn));
-      m2 = mn;
-    }
-    if (lane == 0) { red[wave][0] = m2; red[wave][1] = s2; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float M = kNegInf, Z = 0.f;
-      for (int w = 0; w < 4; ++w) {
-        const float mo = red[w][0], so = red[w][1];
-        const float mn = fmaxf(M, mo);
-        if (mn != kNegInf)
-          Z = (M == kNegInf ? 0.f : Z * exp2f(M - mn)) + (mo == kNegInf ? 0.f : so * exp2f(mo - mn));
-        M = mn;
-      }
-      a.w.lpart[((int64_t)b * a.Hq + h) * a.w.nslice + slice] = make_float2(M, Z);
-    }
-    __syncthreads();
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int hh = threadIdx.x;
+    float M = kNegInf, Z = 0.f;
+    for (int w = 0; w < 4; ++w) lse_merge(M, Z, red[hh][w][0], red[hh][w][1]);
+    a.w.lpart[((int64_t)b * a.Hq + g * G + hh) * a.w.nslice + slice] = make_float2(M, Z);
   }
 }
 
-// Per (b, g, candidate block): wave-local top-k lists; the last block merges.
-template <int G>
-__global__ __launch_bounds__(256) void dec_select_kernel(DecKArgs a) {
-  __shared__ uint64_t sbuf[4][64];
-  __shared__ int32_t sids[64];
+// One wave per candidate span of a (b, g): the span's top-k list (key 0 = empty).
+template <int G, int J>
+__global__ __launch_bounds__(64) void dec_span_kernel(DecKArgs a) {
+  __shared__ uint64_t sbuf[64];
   __shared__ float Ls[8];
-  __shared__ bool last;
-  const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
   const int64_t i = a.pos.p[b];
   const int64_t nc = num_candidates(i, a.S, a.W);
   const int topk = a.topk;
   const int64_t bg = (int64_t)b * a.Hkv + g;
-  int32_t* idxw = a.w.idx + bg * topk;
+  const int64_t cbase = (int64_t)sp * (64 * J);
+  if (nc <= topk || cbase >= nc) return;  // nothing to rank in this span
+  if (G > 1) {
+    if (lane < G) {
+      const float2* lp = a.w.lpart + ((int64_t)b * a.Hq + g * G + lane) * a.w.nslice;
+      float M = kNegInf, Z = 0.f;
+      const int ns = (int)((nc + kSlice - 1) / kSlice);
+      for (int s = 0; s < ns; ++s) lse_merge(M, Z, lp[s].x, lp[s].y);
+      Ls[lane] = (M + hw_log2(Z)) * kLn2;
+    }
+    wave_lds_sync();
+  }
+  uint64_t keys[J];
+  int nvalid = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t c = cbase + lane + 64 * j;
+    float r = kNegInf;
+    if (c < nc) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float s = a.w.shat[((int64_t)b * a.Hq + g * G + hh) * a.NCcap + c];
+        r = G > 1 ? fmaxf(r, s - Ls[hh]) : s;
+      }
+      ++nvalid;
+    }
+    keys[j] = c < nc ? full_key(order_key(r), c) : 0ull;
+  }
+  uint64_t* cand = a.w.cand + (bg * a.w.nspan + sp) * topk;
+  const int nv = wave_sum_i(nvalid);
+  const uint64_t thr = nv > topk ? wave_kth_u64<J>(keys, topk, lane, sbuf) : 1ull;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const bool sel = keys[j] != 0 && keys[j] >= thr;
+    const uint64_t m = __ballot(sel);
+    if (sel) cand[base + lane_prefix(m, lane)] = keys[j];
+    base += __popcll(m);
+  }
+  for (int t = base + lane; t < topk; t += kWave) cand[t] = 0ull;
+}
 
+// One wave per (b, g): the final top-k from the span lists, ascending, and each
+// head's s_hat on it.  With |C_i| <= k every candidate is selected.
+template <int G>
+__global__ __launch_bounds__(64) void dec_merge_kernel(DecKArgs a) {
+  __shared__ uint64_t sbuf[64];
+  __shared__ int32_t sids[64];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int64_t i = a.pos.p[b];
+  const int64_t nc = num_candidates(i, a.S, a.W);
+  const int topk = a.topk;
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  int32_t cs_out;
   if (nc <= topk) {
-    // every candidate is selected; one block writes the result
-    if (blk == 0) {
-      for (int t = threadIdx.x; t < topk; t += blockDim.x) idxw[t] = t < nc ? t : -1;
-      for (int e = threadIdx.x; e < G * topk; e += blockDim.x) {
-        const int hh = e / topk, t = e % topk;
-        const int h = g * G + hh;
-        a.w.ssel[((int64_t)b * a.Hq + h) * topk + t] =
-            t < nc ? a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + t] : kNegInf;
-      }
-      if (a.idx_out)
-        for (int t = threadIdx.x; t < topk; t += blockDim.x) a.idx_out[bg * topk + t] = t < nc ? t : -1;
-    }
-    return;
-  }
-  if ((int64_t)blk * kSelBlock >= nc) return;  // no candidates: takes no ticket
-  // per-head log-normaliser over C_i from the scoring partials
-  if (G > 1 && threadIdx.x < G) {
-    const int h = g * G + threadIdx.x;
-    const float2* lp = a.w.lpart + ((int64_t)b * a.Hq + h) * a.w.nslice;
-    float M = kNegInf, Z = 0.f;
-    const int ns = (int)((nc + kSlice - 1) / kSlice);
-    for (int s = 0; s < ns; ++s) {
-      const float mo = lp[s].x, so = lp[s].y;
-      const float mn = fmaxf(M, mo);
-      if (mn != kNegInf)
-        Z = (M == kNegInf ? 0.f : Z * exp2f(M - mn)) + (mo == kNegInf ? 0.f : so * exp2f(mo - mn));
-      M = mn;
-    }
-    Ls[threadIdx.x] = (M + log2f(Z)) * kLn2;
-  }
-  __syncthreads();
-  const int64_t cbase = (int64_t)blk * kSelBlock + (int64_t)wave * 64 * kJ;
-  uint64_t* cand = a.w.cand + (bg * a.w.nselb + blk) * 4 * topk;
-  if (cbase < nc) {
-    uint64_t keys[kJ];
-    int nvalid = 0;
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-      const int64_t c = cbase + lane + 64 * j;
-      float r = kNegInf;
-      if (c < nc) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float s = a.w.shat[((int64_t)b * a.Hq + g * G + hh) * a.NCcap + c];
-          r = G > 1 ? fmaxf(r, s - Ls[hh]) : s;
-        }
-        ++nvalid;
-      }
-      keys[j] = c < nc ? full_key(order_key(r), c) : 0ull;
-    }
-    const int nv = wave_sum_i(nvalid);
-    if (nv > topk) {
-      const uint64_t thr = wave_kth_u64<kJ>(keys, topk, lane, sbuf[wave]);
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        const bool sel = keys[j] != 0 && keys[j] >= thr;
-        const uint64_t m = __ballot(sel);
-        if (sel) cand[wave * topk + base + lane_prefix(m, lane)] = keys[j];
-        base += __popcll(m);
-      }
-    } else {
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < kJ; ++j) {
-        const bool sel = keys[j] != 0;
-        const uint64_t m = __ballot(sel);
-        if (sel) cand[wave * topk + base + lane_prefix(m, lane)] = keys[j];
-        base += __popcll(m);
-      }
-      for (int t = nv + lane; t < topk; t += kWave) cand[wave * topk + t] = 0ull;
-    }
+    cs_out = lane < nc ? lane : -1;
   } else {
-    for (int t = lane; t < topk; t += kWave) cand[wave * topk + t] = 0ull;
-  }
-  // ticket: the last block of this (b, g) merges
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int nb = (int)((nc + kSelBlock - 1) / kSelBlock);
-    const uint32_t t = atomicAdd(&a.w.ctr[bg * 2 + 0], 1u);
-    last = (t == (uint32_t)nb - 1);
-  }
-  __syncthreads();
-  if (!last || wave != 0) return;
-  __threadfence();
-  const int nb = (int)((nc + kSelBlock - 1) / kSelBlock);
-  const int ntot = nb * 4 * topk;  // <= 2048 for supported sizes
-  uint64_t v[kJ];
-  const uint64_t* call = a.w.cand + bg * a.w.nselb * 4 * topk;
+    const int nsp = (int)((nc + a.w.span - 1) / a.w.span);
+    const int ntot = nsp * topk;  // <= 64 * kMergeJ (checked on the host)
+    uint64_t v[kMergeJ];
+    const uint64_t* call = a.w.cand + bg * a.w.nspan * topk;
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < ntot ? call[e] : 0ull;
+    for (int j = 0; j < kMergeJ; ++j) {
+      const int e = lane + 64 * j;
+      v[j] = e < ntot ? call[e] : 0ull;
+    }
+    const uint64_t thr = wave_kth_u64<kMergeJ>(v, topk, lane, sbuf);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kMergeJ; ++j) cnt += (v[j] != 0 && v[j] >= thr) ? 1 : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int x = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += x;
+    }
+    int pos = incl - cnt;
+#pragma unroll
+    for (int j = 0; j < kMergeJ; ++j)
+      if (v[j] != 0 && v[j] >= thr) sids[pos++] = key_chunk(v[j]);
+    wave_lds_sync();
+    const uint32_t cs = lane < topk ? (uint32_t)sids[lane] : 0xffffffffu;
+    cs_out = (int32_t)bitonic_sort64<uint32_t>(cs, lane, false);
   }
-  const uint64_t thr = wave_kth_u64<kJ>(v, topk, lane, sbuf[0]);
-  // compact the chosen keys, then sort their chunk ids ascending
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < kJ; ++j) cnt += (v[j] != 0 && v[j] >= thr) ? 1 : 0;
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int x = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += x;
-  }
-  int pos = incl - cnt;
-#pragma unroll
-  for (int j = 0; j < kJ; ++j)
-    if (v[j] != 0 && v[j] >= thr) sids[pos++] = key_chunk(v[j]);
-  wave_lds_sync();
-  const uint32_t cs = lane < topk ? (uint32_t)sids[lane] : 0xffffffffu;
-  const uint32_t srt = bitonic_sort64<uint32_t>(cs, lane, false);
   if (lane < topk) {
-    idxw[lane] = (int32_t)srt;
-    if (a.idx_out) a.idx_out[bg * topk + lane] = (int32_t)srt;
+    a.w.idx[bg * topk + lane] = cs_out;
+    if (a.idx_out) a.idx_out[bg * topk + lane] = cs_out;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       const int h = g * G + hh;
-      a.w.ssel[((int64_t)b * a.Hq + h) * topk + lane] = a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + srt];
+      a.w.ssel[((int64_t)b * a.Hq + h) * topk + lane] =
+          cs_out >= 0 ? a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + cs_out] : kNegInf;
     }
   }
 }
@@ -307,10 +251,14 @@ __global__ __launch_bounds__(256) void dec_select_kernel(DecKArgs a) {
 // Work item j < nsel: selected chunk idx[j]; else window chunk l_i/S + (j - nsel).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(64 * G) void dec_attend_kernel(DecKArgs a) {
-  constexpr int DPL = D / kWave;  // dims per lane (2 for d=128)
+  constexpr int NT = 64 * G;
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int DPL = D / kWave;           // dims per lane (2 for d=128)
+  constexpr int KP = D + 16 / (int)sizeof(T);
+  __shared__ __align__(16) T ks[kS * KP];
+  __shared__ __align__(16) T vs[kS * D];
   __shared__ float ps[G][kS];
   __shared__ float qs[G][D];
-  __shared__ bool last;
   const int item = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int64_t i = a.pos.p[b];
@@ -333,21 +281,25 @@ __global__ __launch_bounds__(64 * G) void dec_attend_kernel(DecKArgs a) {
   }
   const T* kc = static_cast<const T*>(a.kc) + (bg * a.Lcap + c * kS) * D;
   const T* vc = static_cast<const T*>(a.vc) + (bg * a.Lcap + c * kS) * D;
+  for (int e = threadIdx.x * EPV; e < kS * D; e += NT * EPV) {
+    const int row = e / D, col = e % D;
+    *reinterpret_cast<uint4*>(ks + row * KP + col) = *reinterpret_cast<const uint4*>(kc + e);
+    *reinterpret_cast<uint4*>(vs + e) = *reinterpret_cast<const uint4*>(vc + e);
+  }
   {
     const T* qv = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + h) * D;
     for (int e = lane; e < D; e += kWave) qs[wave][e] = to_f<T>(qv[e]);
   }
-  wave_lds_sync();
+  __syncthreads();
   // logits: lane = token
   const int64_t j = c * kS + lane;
   const bool ok = !is_win || (j >= lw && j <= i);
   float s = kNegInf;
   if (ok) {
-    constexpr int EPV = 16 / sizeof(T);
     float acc = 0.f;
 #pragma unroll
     for (int e0 = 0; e0 < D; e0 += EPV) {
-      const uint4 u = *reinterpret_cast<const uint4*>(kc + (int64_t)lane * D + e0);
+      const uint4 u = *reinterpret_cast<const uint4*>(ks + lane * KP + e0);
       const T* t = reinterpret_cast<const T*>(&u);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) acc = fmaf(qs[wave][e0 + e], to_f<T>(t[e]), acc);
@@ -355,16 +307,17 @@ __global__ __launch_bounds__(64 * G) void dec_attend_kernel(DecKArgs a) {
     s = acc * (a.scale * kLog2e);
   }
   const float m = wave_max(s);
-  const float p = ok ? exp2f(s - m) : 0.f;
+  const float p = ok ? hw_exp2(s - m) : 0.f;
   const float l = wave_sum(p);
   ps[wave][lane] = p;
   wave_lds_sync();
   float o[DPL];
 #pragma unroll
   for (int t = 0; t < DPL; ++t) o[t] = 0.f;
+#pragma unroll 8
   for (int jj = 0; jj < kS; ++jj) {
     const float pj = ps[wave][jj];
-    const T* vr = vc + (int64_t)jj * D + lane * DPL;
+    const T* vr = vs + jj * D + lane * DPL;
 #pragma unroll
     for (int t = 0; t < DPL; ++t) o[t] = fmaf(pj, to_f<T>(vr[t]), o[t]);
   }
@@ -373,48 +326,68 @@ __global__ __launch_bounds__(64 * G) void dec_attend_kernel(DecKArgs a) {
   for (int t = 0; t < DPL; ++t) ap[lane * DPL + t] = o[t];
   if (lane == 0) { ap[D] = m; ap[D + 1] = l; }
 
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t t = atomicAdd(&a.w.ctr[bg * 2 + 1], 1u);
-    last = (t == (uint32_t)nitems - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // fusion for head h (this wave): window items merge at token level
-  const float* base = a.w.apart + (bg * a.w.nitems) * G * (D + 2);
-  float Mw = kNegInf;
-  for (int it = nsel; it < nitems; ++it) Mw = fmaxf(Mw, base[((int64_t)it * G + wave) * (D + 2) + D]);
-  float lwin = 0.f, ow[DPL];
-#pragma unroll
-  for (int t = 0; t < DPL; ++t) ow[t] = 0.f;
-  for (int it = nsel; it < nitems; ++it) {
-    const float* pp = base + ((int64_t)it * G + wave) * (D + 2);
-    const float mi = (pp + D)[0];
-    if (mi == kNegInf) continue;
-    const float f = exp2f(mi - Mw);
-    lwin += f * (pp + D + 1)[0];
-#pragma unroll
-    for (int t = 0; t < DPL; ++t) ow[t] += f * (pp + lane * DPL + t)[0];
-  }
-  const float logzw = (Mw + log2f(lwin)) * kLn2;
+}
+
+// One wave per (b, query head): fuse the window items (token level) and the
+// selected chunks (weights exp(s_hat - L)).  Lanes own items for the statistics;
+// the weighted sum over items then runs with independent loads.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64) void dec_fuse_kernel(DecKArgs a) {
+  constexpr int DPL = D / kWave;
+  __shared__ float wts[256];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int g = h / G, hl = h % G;
+  const int64_t i = a.pos.p[b];
+  const int64_t lw = window_left(i, a.S, a.W);
+  const int nsel = (int)min<int64_t>(lw / kS, a.topk);
+  const int nitems = nsel + (int)(i / kS - lw / kS + 1);   // <= 256 (checked on the host)
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  const float* ap = a.w.apart + (bg * a.w.nitems) * G * (D + 2);
   const float* ss = a.w.ssel + ((int64_t)b * a.Hq + h) * a.topk;
-  float L = logzw;
-  for (int it = 0; it < nsel; ++it) {
-    const float x = ss[it];
-    const float mx = fmaxf(L, x);
-    L = mx + __logf(__expf(L - mx) + __expf(x - mx));
+  auto mstat = [&](int it) { return ap[((int64_t)it * G + hl) * (D + 2) + D]; };
+  auto lstat = [&](int it) { return ap[((int64_t)it * G + hl) * (D + 2) + D + 1]; };
+  // window: token-level mass of all window items
+  float Mw = kNegInf;
+  for (int it = nsel + lane; it < nitems; it += kWave) Mw = fmaxf(Mw, mstat(it));
+  Mw = wave_max(Mw);
+  float lw_part = 0.f;
+  for (int it = nsel + lane; it < nitems; it += kWave) {
+    const float mi = mstat(it);
+    if (mi != kNegInf) lw_part += hw_exp2(mi - Mw) * lstat(it);
   }
-  float res[DPL];
+  const float lwin = wave_sum(lw_part);
+  const float logzw = (Mw + hw_log2(lwin)) * kLn2;
+  // normaliser over the selected chunks' s_hat and the window's log-mass
+  float mx = logzw;
+  for (int it = lane; it < nsel; it += kWave) mx = fmaxf(mx, ss[it]);
+  mx = wave_max(mx);
+  float z = 0.f;
+  for (int it = lane; it < nsel; it += kWave) z += __expf(ss[it] - mx);
+  z = wave_sum(z) + __expf(logzw - mx);
+  const float L = mx + __logf(z);
+  // per-item weights on the unnormalised o of each item
   const float fw = __expf(logzw - L) / lwin;
+  for (int it = lane; it < nitems; it += kWave) {
+    float w;
+    if (it < nsel) {
+      w = __expf(ss[it] - L) / lstat(it);
+    } else {
+      const float mi = mstat(it);
+      w = mi == kNegInf ? 0.f : hw_exp2(mi - Mw) * fw;
+    }
+    wts[it] = w;
+  }
+  wave_lds_sync();
+  float res[DPL];
 #pragma unroll
-  for (int t = 0; t < DPL; ++t) res[t] = ow[t] * fw;
-  for (int it = 0; it < nsel; ++it) {
-    const float* pp = base + ((int64_t)it * G + wave) * (D + 2);
-    const float f = __expf(ss[it] - L) / (pp + D + 1)[0];
+  for (int t = 0; t < DPL; ++t) res[t] = 0.f;
+#pragma unroll 4
+  for (int it = 0; it < nitems; ++it) {
+    const float w = wts[it];
+    const float* pp = ap + ((int64_t)it * G + hl) * (D + 2) + lane * DPL;
 #pragma unroll
-    for (int t = 0; t < DPL; ++t) res[t] += f * (pp + lane * DPL + t)[0];
+    for (int t = 0; t < DPL; ++t) res[t] = fmaf(w, pp[t], res[t]);
   }
   T* orow = static_cast<T*>(a.out) + ((int64_t)b * a.Hq + h) * D;
 #pragma unroll
@@ -422,12 +395,27 @@ __global__ __launch_bounds__(64 * G) void dec_attend_kernel(DecKArgs a) {
   if (a.lse && lane == 0) a.lse[(int64_t)b * a.Hq + h] = L;
 }
 
+template <int G>
+void launch_select_j(const DecKArgs& k, hipStream_t st) {
+  const dim3 grid(k.w.nspan, k.Hkv, k.B), block(64);
+  switch (k.w.span / 64) {
+    case 1: hipLaunchKernelGGL((dec_span_kernel<G, 1>), grid, block, 0, st, k); break;
+    case 2: hipLaunchKernelGGL((dec_span_kernel<G, 2>), grid, block, 0, st, k); break;
+    case 4: hipLaunchKernelGGL((dec_span_kernel<G, 4>), grid, block, 0, st, k); break;
+    case 8: hipLaunchKernelGGL((dec_span_kernel<G, 8>), grid, block, 0, st, k); break;
+    case 16: hipLaunchKernelGGL((dec_span_kernel<G, 16>), grid, block, 0, st, k); break;
+    case 32: hipLaunchKernelGGL((dec_span_kernel<G, 32>), grid, block, 0, st, k); break;
+    default: hipLaunchKernelGGL((dec_span_kernel<G, 64>), grid, block, 0, st, k); break;
+  }
+  hipLaunchKernelGGL((dec_merge_kernel<G>), dim3(1, k.Hkv, k.B), block, 0, st, k);
+}
+
 template <typename T, int D, int G>
 hipError_t launch_decode_tg(const DecKArgs& k, hipStream_t st) {
-  hipLaunchKernelGGL((dec_score_kernel<T, D>), dim3(k.w.nslice, k.Hkv, k.B), dim3(256), 0, st, k);
-  if (k.topk > 0)
-    hipLaunchKernelGGL((dec_select_kernel<G>), dim3(k.w.nselb, k.Hkv, k.B), dim3(256), 0, st, k);
+  hipLaunchKernelGGL((dec_score_kernel<T, D, G>), dim3(k.w.nslice, k.Hkv, k.B), dim3(256), 0, st, k);
+  if (k.topk > 0) launch_select_j<G>(k, st);
   hipLaunchKernelGGL((dec_attend_kernel<T, D, G>), dim3(k.w.nitems, k.Hkv, k.B), dim3(64 * G), 0, st, k);
+  hipLaunchKernelGGL((dec_fuse_kernel<T, D, G>), dim3(k.Hq, k.B), dim3(64), 0, st, k);
   return hipGetLastError();
 }
 
@@ -443,31 +431,47 @@ hipError_t launch_decode_t(const DecKArgs& k, hipStream_t st) {
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Candidates per selection wave: the smallest 64*J whose span lists fit one merge wave.
+int pick_span(int64_t NCcap, int topk) {
+  if (topk <= 0) return 64;
+  for (int J = 1; J <= 64; J <<= 1) {
+    const int64_t nspan = (NCcap + 64 * J - 1) / (64 * J);
+    if (nspan * topk <= 64 * kMergeJ) return 64 * J;
+  }
+  return -1;
+}
+
 void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk, DecWs* w,
             size_t* total, char* base) {
   const int64_t NCcap = Lcap / S;
   const int nslice = (int)((NCcap + kSlice - 1) / kSlice);
-  const int nselb = (int)((NCcap + kSelBlock - 1) / kSelBlock);
+  const int span = pick_span(NCcap, topk);
+  const int nspan = (int)((NCcap + span - 1) / span);
   const int nitems = topk + W / S + 2;
   const int G = Hq / Hkv;
+  const int kk = topk > 0 ? topk : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += a256(bytes); return p; };
   DecWs d{};
   d.shat = reinterpret_cast<float*>(take((size_t)B * Hq * NCcap * 4));
   d.lpart = reinterpret_cast<float2*>(take((size_t)B * Hq * nslice * 8));
-  d.cand = reinterpret_cast<uint64_t*>(take((size_t)B * Hkv * nselb * 4 * (topk > 0 ? topk : 1) * 8));
-  d.idx = reinterpret_cast<int32_t*>(take((size_t)B * Hkv * (topk > 0 ? topk : 1) * 4));
-  d.ssel = reinterpret_cast<float*>(take((size_t)B * Hq * (topk > 0 ? topk : 1) * 4));
+  d.cand = reinterpret_cast<uint64_t*>(take((size_t)B * Hkv * nspan * kk * 8));
+  d.idx = reinterpret_cast<int32_t*>(take((size_t)B * Hkv * kk * 4));
+  d.ssel = reinterpret_cast<float*>(take((size_t)B * Hq * kk * 4));
   d.apart = reinterpret_cast<float*>(take((size_t)B * Hkv * nitems * G * (D + 2) * 4));
-  d.ctr = reinterpret_cast<uint32_t*>(take((size_t)B * Hkv * 2 * 4));
   d.nslice = nslice;
-  d.nselb = nselb;
+  d.nspan = nspan;
+  d.span = span;
   d.nitems = nitems;
   if (w) *w = d;
   if (total) *total = off + 256;
 }
 
 }  // namespace
+
+bool decode_supported(int64_t Lcap, int S, int W, int topk) {
+  return pick_span(Lcap / S, topk) > 0 && topk + W / S + 2 <= 256;
+}
 
 size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk) {
   size_t t = 0;

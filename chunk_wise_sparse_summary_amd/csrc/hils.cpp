@@ -11,8 +11,6 @@
 
 namespace {
 
-using hils::kDecSelBlock;
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 enum Mode { kSummarize, kPrefill, kDecode };
@@ -35,9 +33,7 @@ hils_status check_shape(const hils_shape* s, Mode mode) {
   if (mode == kDecode) {
     if (s->batch > 64) return HILS_E_UNSUPPORTED;
     if (s->seq_len % s->chunk != 0) return HILS_E_SHAPE;
-    const int64_t nc = s->seq_len / s->chunk;
-    const int64_t nb = (nc + kDecSelBlock - 1) / kDecSelBlock;
-    if (nb * 4 * s->top_k > 2048) return HILS_E_UNSUPPORTED;
+    if (!hils::decode_supported(s->seq_len, s->chunk, s->window, s->top_k)) return HILS_E_UNSUPPORTED;
     if (s->seq_len > (int64_t(1) << 31)) return HILS_E_UNSUPPORTED;
   } else if (mode == kPrefill) {
     if (s->seq_len / s->chunk > 4096) return HILS_E_UNSUPPORTED;  // <= 4096 chunks per sequence

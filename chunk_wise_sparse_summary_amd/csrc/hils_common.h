@@ -23,14 +23,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
+// Hardware 2^x and log2(x) (v_exp_f32, v_log_f32): about 1 ulp, no range handling
+// beyond the instruction's own (2^-inf = 0); callers pass finite or -inf inputs.
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-// fp32 -> bf16, round to nearest even.
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> __device__ __forceinline__ float to_f(T x);
@@ -93,7 +98,7 @@ __device__ __forceinline__ void zero_frag(Frag<float>& f) {
 __device__ __forceinline__ void set_frag(Frag<bf16_t>& f, const float* x) {
   uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = (uint32_t)f2bf(x[2 * e]) | ((uint32_t)f2bf(x[2 * e + 1]) << 16);
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
   f.v = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 }
 __device__ __forceinline__ void set_frag(Frag<float>& f, const float* x) {

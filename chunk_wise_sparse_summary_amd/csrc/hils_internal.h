@@ -93,7 +93,7 @@ struct DecArgs {
 };
 hipError_t launch_decode(const DecArgs& a, hipStream_t st);
 size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk);
-// Candidates per decode selection block and per-wave list capacity limit.
-constexpr int64_t kDecSelBlock = 4 * 64 * 32;
+// Whether the decode selection can merge its per-span lists in one wave.
+bool decode_supported(int64_t Lcap, int S, int W, int topk);
 
 }  // namespace hils

@@ -10,26 +10,23 @@
 // go to the lower chunk index.
 //
 // Two kernels:
-//   score_lse   (G > 1 only) L_{h,i} = LSE_{c in C_i} s_hat_{h,i,c}: an MFMA score
-//               tile (16 queries x 16 chunks per wave step) with an online
-//               log-sum-exp epilogue.  One workgroup = one head x 64 queries.
-//   rank_select persistent workgroups, each owning a scratch slot.  For a tile of
-//               64 queries x one group it recomputes the score tiles for all G
-//               heads (A fragments of q_hat stay in registers), forms the rank
-//               key per (query, chunk), writes it to its slot, then each wave
-//               selects the top-k of its 16 queries (below) and recomputes each
-//               head's s_hat on the selected chunks.
+//   score_lse   (G > 1 only) L_{h,i} = LSE_{c in C_i} s_hat_{h,i,c}: MFMA score
+//               tiles with an online log-sum-exp epilogue; one workgroup = one
+//               head x 256 queries, k' tiles staged once in LDS.
+//   rank_select persistent workgroups, each owning a scratch slot of rank keys.
+//               For 64 queries x one group it recomputes every head's score
+//               tiles, forms the rank key per (query, chunk), selects the top-k of
+//               each query (below) and computes each head's s_hat on the choice.
 //
-// Wave-level top-k of n <= 64*J keys held J per lane (candidate c = lane + 64*j):
-//   total order: (key desc, chunk asc), packed as key<<32 | ~c in 64 bits;
+// Wave-level top-k of n <= 64*J rank keys held J per lane (candidate c = lane +
+// 64*j; keys are order-preserving unsigned images of the fp32 rank key):
 //   1. theta = the k-th largest of the 64 per-lane maxima: a lower bound of the
 //      k-th largest key (the top-k lane maxima are k distinct candidates);
-//   2. if at most 64 candidates reach theta, compact them into one per lane and
-//      bitonic-sort the 64-bit keys across the wave; the k-th is the threshold;
-//      otherwise find the k-th largest key exactly by bisection on the key bits
-//      and take ties in ascending chunk order;
-//   3. select every candidate whose 64-bit key reaches the threshold and write
-//      the chosen ids in ascending order with a ballot prefix scan.
+//   2. if at most 64 candidates reach theta, they are compacted one per lane and
+//      bitonic-sorted across the wave, giving the k-th largest key K exactly;
+//      otherwise K is found by bisection on the key bits;
+//   3. every key above K is chosen, plus the lowest-index keys equal to K up to k,
+//      and the ids are written in ascending order with ballot prefix scans.
 #include "hils_internal.h"
 #include "topk.h"
 
@@ -37,6 +34,53 @@ namespace hils {
 
 namespace {
 
+template <typename T> struct KPad;
+template <> struct KPad<bf16_t> { static constexpr int P = 8; };
+template <> struct KPad<float> { static constexpr int P = 4; };
+
+// A tile of k' (16 chunks of NH heads, padded LDS rows) and b', fetched into
+// registers by all 256 threads and committed to LDS later, so that the next
+// tile's loads overlap the current tile's MFMAs.
+template <typename T, int D, int NH>
+struct KTile {
+  static constexpr int EPV = 16 / sizeof(T);
+  static constexpr int PPR = D / EPV;                 // 16-byte pieces per row
+  static constexpr int KP = D + KPad<T>::P;           // padded row (elements)
+  static constexpr int NPIECE = NH * 16 * PPR;
+  static constexpr int NPT = (NPIECE + 255) / 256;    // pieces per thread
+  uint4 reg[NPT];
+  float breg;
+  __device__ void fetch(const T* kg, const float* bg, int64_t NCs, int c0, int cl_last) {
+#pragma unroll
+    for (int t = 0; t < NPT; ++t) {
+      const int p = t * 256 + threadIdx.x;
+      if (p < NPIECE) {
+        const int hh = p / (16 * PPR), rem = p % (16 * PPR), row = rem / PPR, pc = rem % PPR;
+        const int cl = min(c0 + row, cl_last);
+        reg[t] = *reinterpret_cast<const uint4*>(kg + ((int64_t)hh * NCs + cl) * D + pc * EPV);
+      }
+    }
+    if (threadIdx.x < NH * 16) {
+      const int hh = threadIdx.x / 16, row = threadIdx.x % 16;
+      breg = bg[(int64_t)hh * NCs + min(c0 + row, cl_last)];
+    }
+  }
+  __device__ void commit(T* kt, float* bt) const {
+#pragma unroll
+    for (int t = 0; t < NPT; ++t) {
+      const int p = t * 256 + threadIdx.x;
+      if (p < NPIECE) {
+        const int hh = p / (16 * PPR), rem = p % (16 * PPR), row = rem / PPR, pc = rem % PPR;
+        *reinterpret_cast<uint4*>(kt + (hh * 16 + row) * KP + pc * EPV) = reg[t];
+      }
+    }
+    if (threadIdx.x < NH * 16) bt[threadIdx.x] = breg;
+  }
+};
+
+// L_{h,i} = LSE_{c in C_i} s_hat_{h,i,c}.  Workgroup = one head x 256 queries; a
+// wave owns 64 queries (four 16-row MFMA tiles, A fragments in registers) and
+// every 16-chunk k' tile is staged once in LDS for the four waves.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh,
                                                         const T* __restrict__ ksum,
@@ -45,83 +89,119 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
                                                         int64_t T_, int64_t NCs, int S, int W,
                                                         float scale) {
   constexpr int KS = D / 32;
+  using Tile = KTile<T, D, 1>;
+  __shared__ __align__(16) T kt[16 * Tile::KP];
+  __shared__ float bt[16];
   const int h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t q0 = (int64_t)blockIdx.x * 64 + wave * 16;
-  if (q0 >= T_) return;
   const int r16 = lane % 16, grp = lane / 16;
+  const int64_t qb = (int64_t)blockIdx.x * 256;
+  const int64_t q0 = qb + wave * 64;
+  const bool live = q0 < T_;
 
-  Frag<T> a[KS];
-  {
-    const int64_t qa = min(q0 + r16, T_ - 1);
+  Frag<T> a[4][KS];
+  int ncq[4][4];
+  float m[4][4], s[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int64_t qa = min(q0 + 16 * rt + r16, T_ - 1);
     const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + qa) * D + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load_frag(a[ks], qrow + 32 * ks);
-  }
-  int64_t ncq[4];
+    for (int ks = 0; ks < KS; ++ks) load_frag(a[rt][ks], qrow + 32 * ks);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t qi = q0 + 4 * grp + i;
-    ncq[i] = qi < T_ ? num_candidates(qi, S, W) : 0;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t qi = q0 + 16 * rt + 4 * grp + i;
+      ncq[rt][i] = qi < T_ ? (int)num_candidates(qi, S, W) : 0;
+      m[rt][i] = kNegInf;
+      s[rt][i] = 0.f;
+    }
   }
-  const int64_t ncmax = num_candidates(min(q0 + 15, T_ - 1), S, W);
+  const int nc_block = (int)num_candidates(min(qb + 255, T_ - 1), S, W);
+  const int ncmin = live ? (int)num_candidates(q0, S, W) : 0;
+  const int ncmax = live ? (int)num_candidates(min(q0 + 63, T_ - 1), S, W) : 0;
   const float sl2 = scale * kLog2e;
-  float m[4], s[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { m[i] = kNegInf; s[i] = 0.f; }
-
-  const T* kb = ksum + ((int64_t)b * Hq + h) * NCs * D + 8 * grp;
-  const float* bb = bsum + ((int64_t)b * Hq + h) * NCs;
-  for (int64_t c0 = 0; c0 < ncmax; c0 += 16) {
-    const int64_t c = c0 + r16;
-    const int64_t cl = c < ncmax ? c : ncmax - 1;
+  const T* kg = ksum + ((int64_t)b * Hq + h) * NCs * D;
+  const float* bg = bsum + ((int64_t)b * Hq + h) * NCs;
+  const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
+  Tile tile;
+  if (nc_block > 0) tile.fetch(kg, bg, NCs, 0, cl_last);
+  for (int c0 = 0; c0 < nc_block; c0 += 16) {
+    __syncthreads();
+    tile.commit(kt, bt);
+    __syncthreads();
+    if (c0 + 16 < nc_block) tile.fetch(kg, bg, NCs, c0 + 16, cl_last);  // in flight meanwhile
+    if (c0 >= ncmax) continue;
     Frag<T> bf[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load_frag(bf[ks], kb + cl * D + 32 * ks);
-    const float b2 = bb[cl] * kLog2e;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks) load_frag(bf[ks], kt + r16 * Tile::KP + 8 * grp + 32 * ks);
+    const float b2 = bt[r16] * kLog2e;
+    const int c = c0 + r16;
+    const bool full = c0 + 16 <= ncmin;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) mma(acc, a[ks], bf[ks]);
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (c < ncq[i]) {
-        const float x = fmaf(acc[i], sl2, b2);
-        const float mn = fmaxf(m[i], x);
-        s[i] = (m[i] == mn ? s[i] : s[i] * exp2f(m[i] - mn)) + exp2f(x - mn);
-        m[i] = mn;
+      for (int ks = 0; ks < KS; ++ks) mma(acc, a[rt][ks], bf[ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (full || c < ncq[rt][i]) {
+          // the running reference m moves only when a score exceeds it by 16
+          const float x = fmaf(acc[i], sl2, b2);
+          if (x > m[rt][i] + 16.f) {
+            s[rt][i] *= hw_exp2(m[rt][i] - x);
+            m[rt][i] = x;
+          }
+          s[rt][i] += hw_exp2(x - m[rt][i]);
+        }
       }
     }
   }
-  // combine the 16 lanes of each row group
+  if (!live) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float mo = __shfl_xor(m[i], o, kWave);
-      const float so = __shfl_xor(s[i], o, kWave);
-      const float mn = fmaxf(m[i], mo);
-      if (mn != kNegInf) {
-        s[i] = (m[i] == kNegInf ? 0.f : s[i] * exp2f(m[i] - mn)) +
-               (mo == kNegInf ? 0.f : so * exp2f(mo - mn));
-      }
-      m[i] = mn;
-    }
-  }
-  if (r16 == 0) {
+  for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t qi = q0 + 4 * grp + i;
-      if (qi < T_)
-        Lout[((int64_t)b * Hq + h) * T_ + qi] = ncq[i] > 0 ? (m[i] + log2f(s[i])) * kLn2 : kNegInf;
+      float mm = m[rt][i], ss = s[rt][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float mo = __shfl_xor(mm, o, kWave);
+        const float so = __shfl_xor(ss, o, kWave);
+        const float mn = fmaxf(mm, mo);
+        if (mn != kNegInf)
+          ss = (mm == kNegInf ? 0.f : ss * hw_exp2(mm - mn)) + (mo == kNegInf ? 0.f : so * hw_exp2(mo - mn));
+        mm = mn;
+      }
+      const int64_t qi = q0 + 16 * rt + 4 * grp + i;
+      if (r16 == 0 && qi < T_)
+        Lout[((int64_t)b * Hq + h) * T_ + qi] = ncq[rt][i] > 0 ? (mm + log2f(ss)) * kLn2 : kNegInf;
     }
   }
 }
 
+// Rank keys, top-k and each head's s_hat on the selection, for one (b, group,
+// 64-query tile) per workgroup iteration (persistent workgroups, each owning a
+// scratch slot of rank keys).  Wave w handles heads w and w + 4 of the group:
+//   phase 1: per 16-chunk tile (k' of all G heads staged in LDS), each head's
+//            x = s_hat - L_h for the 64 queries goes to LDS, and the rank key
+//            r = max over heads (r = s_hat for one head) to the scratch slot;
+//   phase 2: each wave selects the top-k of 16 queries; then each head's wave
+//            computes its s_hat on every chosen chunk of the 64 queries.
+// Two waves per SIMD fit without spilling unless the candidate keys are wide.
+template <typename T, int D, int J>
+constexpr int rank_waves() { return (J <= 16 || (J == 32 && (sizeof(T) == 2 || D == 64))) ? 2 : 1; }
+
 template <typename T, int D, int G, int J>
-__global__ __launch_bounds__(256) void rank_select_kernel(SelArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(rank_waves<T, D, J>(), 2)))
+void rank_select_kernel(SelArgs a) {
   constexpr int KS = D / 32;
-  __shared__ uint64_t sbuf[4][64];
-  __shared__ int32_t sidx[4][64];
+  constexpr int NCP = 64 * J;
+  constexpr int HW = (G + 3) / 4;        // heads per wave
+  using Tile = KTile<T, D, G>;
+  __shared__ __align__(16) T kt[G * 16 * Tile::KP];
+  __shared__ float bt[G * 16];
+  __shared__ float xs[G][64][17];       // x = s_hat - L per head, 64 queries x 16 chunks
+  __shared__ uint32_t sbuf[4][64];
+  __shared__ int32_t sidx[64 * 64];      // 64 queries x up to 64 chosen ids
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
   const T* qh = static_cast<const T*>(a.qh);
@@ -130,113 +210,155 @@ __global__ __launch_bounds__(256) void rank_select_kernel(SelArgs a) {
   const int Hq = a.Hq, Hkv = a.Hkv, S = a.S, W = a.W, topk = a.topk;
   const int64_t nqt = (T_ + 63) / 64;
   const int64_t ntiles = (int64_t)a.B * Hkv * nqt;
-  float* slot = a.scratch + (int64_t)blockIdx.x * a.slot_stride;  // [64][64*J]
-  constexpr int NCP = 64 * J;
+  float* slot = a.scratch + (int64_t)blockIdx.x * a.slot_stride;  // [64][NCP]
 
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t qt = tile % nqt;
-    const int g = (int)((tile / nqt) % Hkv);
-    const int b = (int)(tile / (nqt * Hkv));
-    const int64_t q0 = qt * 64 + wave * 16;
+  for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const int64_t qt = tile_id % nqt;
+    const int g = (int)((tile_id / nqt) % Hkv);
+    const int b = (int)(tile_id / (nqt * Hkv));
+    const int64_t qb = qt * 64;
+    const T* kg = ksum + ((int64_t)b * Hq + g * G) * NCs * D;   // head g*G, chunk 0
+    const float* bg = a.bsum + ((int64_t)b * Hq + g * G) * NCs;
 
-    // ---------- phase 1: rank keys of every (query, candidate) of this wave
-    if (q0 < T_) {
-      Frag<T> af[G][KS];
-      {
-        const int64_t qa = min(q0 + r16, T_ - 1);
+    // this wave's heads: q_hat of the 64 queries (A operand) and L per row.  The
+    // fragments are loaded again for phase 2b so they are not live across the top-k.
+    Frag<T> af[HW][4][KS];
+    float Lr[HW][4][4];
+    auto load_a = [&](int u) {
+      const int h = g * G + wave + 4 * u;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const T* qrow = qh + (((int64_t)b * Hq + g * G + hh) * T_ + qa) * D + 8 * grp;
+      for (int rt = 0; rt < 4; ++rt) {
+        const int64_t qa = min(qb + 16 * rt + r16, T_ - 1);
+        const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + qa) * D + 8 * grp;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) load_frag(af[hh][ks], qrow + 32 * ks);
-        }
+        for (int ks = 0; ks < KS; ++ks) load_frag(af[u][rt][ks], qrow + 32 * ks);
       }
-      int64_t ncq[4];
-      float Lr[G][4];
+    };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t qi = q0 + 4 * grp + i;
-        ncq[i] = qi < T_ ? num_candidates(qi, S, W) : 0;
+    for (int u = 0; u < HW; ++u) {
+      const int hh = wave + 4 * u;
+      if (hh < G) {
+        const int h = g * G + hh;
+        load_a(u);
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-          Lr[hh][i] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + g * G + hh) * T_ + qi] : 0.f;
-      }
-      const int64_t ncmax = num_candidates(min(q0 + 15, T_ - 1), S, W);
-      for (int64_t c0 = 0; c0 < ncmax; c0 += 16) {
-        const int64_t c = c0 + r16;
-        const int64_t cl = c < ncmax ? c : ncmax - 1;
-        float r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = kNegInf;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const int h = g * G + hh;
-          const T* krow = ksum + (((int64_t)b * Hq + h) * NCs + cl) * D + 8 * grp;
-          Frag<T> bf[KS];
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) load_frag(bf[ks], krow + 32 * ks);
-          const float bv = a.bsum[((int64_t)b * Hq + h) * NCs + cl];
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) mma(acc, af[hh][ks], bf[ks]);
+        for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float sh = fmaf(acc[i], a.scale, bv);
-            const float x = G > 1 ? sh - Lr[hh][i] : sh;
-            r[i] = fmaxf(r[i], x);
+            const int64_t qi = qb + 16 * rt + 4 * grp + i;
+            Lr[u][rt][i] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
           }
         }
-        if (c < NCP) {
+      }
+    }
+
+    // ---------- phase 1
+    const int nc_block = (int)num_candidates(min(qb + 63, T_ - 1), S, W);
+    const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
+    Tile tile;
+    if (nc_block > 0) tile.fetch(kg, bg, NCs, 0, cl_last);
+    for (int c0 = 0; c0 < nc_block; c0 += 16) {
+      __syncthreads();
+      tile.commit(kt, bt);
+      __syncthreads();
+      if (c0 + 16 < nc_block) tile.fetch(kg, bg, NCs, c0 + 16, cl_last);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) slot[(wave * 16 + 4 * grp + i) * NCP + c] = r[i];
+      for (int u = 0; u < HW; ++u) {
+        const int hh = wave + 4 * u;
+        if (hh < G) {
+          Frag<T> bf[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            load_frag(bf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
+          const float bv = bt[hh * 16 + r16];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) mma(acc, af[u][rt][ks], bf[ks]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              xs[hh][16 * rt + 4 * grp + i][r16] = fmaf(acc[i], a.scale, bv) - Lr[u][rt][i];
+          }
         }
+      }
+      __syncthreads();
+      // wave w: rows 16w..16w+15 of the rank keys for this tile
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * grp + i;
+        float r = xs[0][row][r16];
+#pragma unroll
+        for (int hh = 1; hh < G; ++hh) r = fmaxf(r, xs[hh][row][r16]);
+        slot[row * NCP + c0 + r16] = r;
       }
     }
     __threadfence_block();
     __syncthreads();
 
-    // ---------- phase 2: top-k per query, then each head's s_hat on the selection
-    if (q0 < T_) {
-      for (int qq = 0; qq < 16; ++qq) {
-        const int64_t i = q0 + qq;
-        if (i >= T_) break;
-        const int64_t nc = num_candidates(i, S, W);
-        int32_t* orow = a.idx + (((int64_t)b * Hkv + g) * T_ + i) * topk;
-        int nsel;
-        if (nc <= topk) {
-          nsel = (int)nc;
-          if (lane < topk) sidx[wave][lane] = lane < nc ? lane : -1;
+    // ---------- phase 2a: top-k of the wave's 16 queries (rows 16w..16w+15)
+    for (int qq = 0; qq < 16; ++qq) {
+      const int row = 16 * wave + qq;
+      const int64_t i = qb + row;
+      int32_t* sel = sidx + row * 64;
+      const int nc = i < T_ ? (int)num_candidates(i, S, W) : 0;
+      if (nc <= topk) {
+        if (lane < topk) sel[lane] = lane < nc ? lane : -1;
+      } else {
+        uint32_t keys[J];
+        const float* rrow = slot + row * NCP;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int c = lane + 64 * j;
+          keys[j] = c < nc ? order_key(rrow[c]) : 0u;
+        }
+        wave_topk_u32<J>(keys, topk, lane, sbuf[wave], sel);
+      }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * topk; e += 256) {
+      const int row = e / topk, t = e % topk;
+      const int64_t i = qb + row;
+      if (i < T_) a.idx[(((int64_t)b * Hkv + g) * T_ + i) * topk + t] = sidx[row * 64 + t];
+    }
+    // ---------- phase 2b: each head's s_hat on the selection.  Column tiles of 16
+    // chosen slots (slot s belongs to query s / topk) against the 16-query row
+    // tile(s) that own them; only the entry in the slot's own row is kept.
+#pragma unroll
+    for (int u = 0; u < HW; ++u) {
+      const int hh = wave + 4 * u;
+      if (hh >= G) continue;
+      const int h = g * G + hh;
+      load_a(u);
+      const int nslots = 64 * topk;
+      for (int t0 = 0; t0 < nslots; t0 += 16) {
+        const int sl = t0 + r16;
+        const int sq = sl / topk, st = sl % topk;         // this lane's column: query, slot
+        const int32_t cs = sl < nslots ? sidx[sq * 64 + st] : -1;
+        Frag<T> bf[KS];
+        float bv = 0.f;
+        if (cs >= 0) {  // pad slots read nothing: there may be no summaries at all
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            load_frag(bf[ks], kg + ((int64_t)hh * NCs + cs) * D + 8 * grp + 32 * ks);
+          bv = bg[(int64_t)hh * NCs + cs];
         } else {
-          nsel = topk;
-          uint64_t keys[J];
-          const float* rrow = slot + (wave * 16 + qq) * NCP;
 #pragma unroll
-          for (int j = 0; j < J; ++j) {
-            const int64_t c = lane + 64 * j;
-            keys[j] = c < nc ? full_key(order_key(rrow[c]), c) : 0ull;
-          }
-          const uint64_t thr = wave_kth_u64<J>(keys, topk, lane, sbuf[wave]);
-          emit_ascending<J>(keys, thr, lane, sidx[wave]);
+          for (int ks = 0; ks < KS; ++ks) zero_frag(bf[ks]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int32_t cs = (lane < nsel) ? sidx[wave][lane] : -1;
-        if (lane < topk) orow[lane] = cs;
-        // each head's retrieval score on the selected chunks (lane = slot)
+        const int rt_lo = (t0 / topk) / 16, rt_hi = (min(t0 + 15, nslots - 1) / topk) / 16;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const int h = g * G + hh;
-          float v = kNegInf;
-          if (cs >= 0) {
-            const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + i) * D;
-            const T* krow = ksum + (((int64_t)b * Hq + h) * NCs + cs) * D;
-            const float acc = dot_row<T, D>(qrow, krow);
-            v = fmaf(acc, a.scale, a.bsum[((int64_t)b * Hq + h) * NCs + cs]);
+        for (int rt = 0; rt < 4; ++rt) {
+          if (rt < rt_lo || rt > rt_hi) continue;   // uniform across the wave
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) mma(acc, af[u][rt][ks], bf[ks]);
+          const int ii = sq - 16 * rt - 4 * grp;
+          if (sl < nslots && ii >= 0 && ii < 4 && qb + sq < T_) {
+            const float v = ii == 0 ? acc[0] : ii == 1 ? acc[1] : ii == 2 ? acc[2] : acc[3];
+            a.ssel[(((int64_t)b * Hq + h) * T_ + qb + sq) * topk + st] =
+                cs >= 0 ? fmaf(v, a.scale, bv) : kNegInf;
           }
-          if (lane < topk) a.ssel[(((int64_t)b * Hq + h) * T_ + i) * topk + lane] = v;
         }
-        __builtin_amdgcn_wave_barrier();
       }
     }
     __syncthreads();
@@ -260,7 +382,7 @@ template <typename T, int D>
 hipError_t launch_select_t(const SelArgs& a, int J, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   if (G > 1) {
-    dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)a.Hq, (unsigned)a.B);
+    dim3 grid((unsigned)((a.T + 255) / 256), (unsigned)a.Hq, (unsigned)a.B);
     hipLaunchKernelGGL((score_lse_kernel<T, D>), grid, dim3(256), 0, st,
                        static_cast<const T*>(a.qh), static_cast<const T*>(a.ksum), a.bsum, a.L,
                        a.Hq, a.T, a.NCs, a.S, a.W, a.scale);

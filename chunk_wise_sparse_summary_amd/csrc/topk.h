@@ -119,4 +119,64 @@ __device__ __forceinline__ void emit_ascending(const uint64_t (&v)[J], uint64_t 
   }
 }
 
+// Exact top-k of 32-bit rank keys held J per lane, candidate id lane + 64*j
+// (key 0 = absent), more than topk present.  Ties at the k-th key go to the
+// lower ids.  Writes the chosen ids ascending to out[0..topk).  buf: 64
+// wave-private uint32 in LDS.
+template <int J>
+__device__ void wave_topk_u32(const uint32_t (&keys)[J], int topk, int lane, uint32_t* buf,
+                              int32_t* out) {
+  uint32_t lm = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) lm = keys[j] > lm ? keys[j] : lm;
+  const uint32_t srt = bitonic_sort64<uint32_t>(lm, lane, true);
+  const uint32_t theta = __shfl(srt, topk - 1, kWave);   // <= the k-th largest key
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) cnt += (keys[j] != 0 && keys[j] >= theta) ? 1 : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += x;
+  }
+  const int total = __shfl(incl, 63, kWave);
+  uint32_t kstar;
+  if (total <= 64) {
+    int pos = incl - cnt;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (keys[j] != 0 && keys[j] >= theta) buf[pos++] = keys[j];
+    wave_lds_sync();
+    const uint32_t x = lane < total ? buf[lane] : 0u;
+    wave_lds_sync();
+    kstar = __shfl(bitonic_sort64<uint32_t>(x, lane, true), topk - 1, kWave);
+  } else {
+    uint32_t lo = theta > 0 ? theta : 1u, hi = __shfl(srt, 0, kWave);
+    while (lo < hi) {
+      const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < J; ++j) c += keys[j] >= mid ? 1 : 0;
+      if (wave_sum_i(c) >= topk) lo = mid; else hi = mid - 1;
+    }
+    kstar = lo;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) gt += keys[j] > kstar ? 1 : 0;
+  const int need = topk - wave_sum_i(gt);   // ties at kstar to take, lowest ids first
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const bool eq = keys[j] == kstar;
+    const uint64_t meq = __ballot(eq);
+    const bool sel = keys[j] > kstar || (eq && eq_seen + lane_prefix(meq, lane) < need);
+    eq_seen += __popcll(meq);
+    const uint64_t m = __ballot(sel);
+    if (sel) out[base + lane_prefix(m, lane)] = lane + 64 * j;
+    base += __popcll(m);
+  }
+}
+
 }  // namespace hils
