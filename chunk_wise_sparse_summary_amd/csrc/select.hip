@@ -19,14 +19,11 @@
 //               each query (below) and computes each head's s_hat on the choice.
 //
 // Wave-level top-k of n <= 64*J rank keys held J per lane (candidate c = lane +
-// 64*j; keys are order-preserving unsigned images of the fp32 rank key):
-//   1. theta = the k-th largest of the 64 per-lane maxima: a lower bound of the
-//      k-th largest key (the top-k lane maxima are k distinct candidates);
-//   2. if at most 64 candidates reach theta, they are compacted one per lane and
-//      bitonic-sorted across the wave, giving the k-th largest key K exactly;
-//      otherwise K is found by bisection on the key bits;
-//   3. every key above K is chosen, plus the lowest-index keys equal to K up to k,
-//      and the ids are written in ascending order with ballot prefix scans.
+// 64*j; keys are order-preserving unsigned images of the fp32 rank key): a
+// lower bound theta from the 64 lane maxima, the exact k-th key by bitwise
+// bisection with ballot counts over the few keys that reach theta, then the
+// chosen ids in ascending order with ballot prefix counts (ties at the k-th key
+// to the lowest ids).
 #include "hils_internal.h"
 #include "topk.h"
 
@@ -38,9 +35,9 @@ template <typename T> struct KPad;
 template <> struct KPad<bf16_t> { static constexpr int P = 8; };
 template <> struct KPad<float> { static constexpr int P = 4; };
 
-// A tile of k' (16 chunks of NH heads, padded LDS rows) and b', fetched into
-// registers by all 256 threads and committed to LDS later, so that the next
-// tile's loads overlap the current tile's MFMAs.
+// A tile of k' (16 chunks of NH heads, padded LDS rows) and b' is fetched into
+// registers by all 256 threads and committed to LDS one iteration later, so the
+// next tile's loads overlap the current tile's MFMAs.
 template <typename T, int D, int NH>
 struct KTile {
   static constexpr int EPV = 16 / sizeof(T);
@@ -48,39 +45,56 @@ struct KTile {
   static constexpr int KP = D + KPad<T>::P;           // padded row (elements)
   static constexpr int NPIECE = NH * 16 * PPR;
   static constexpr int NPT = (NPIECE + 255) / 256;    // pieces per thread
-  uint4 reg[NPT];
-  float breg;
-  __device__ void fetch(const T* kg, const float* bg, int64_t NCs, int c0, int cl_last) {
-#pragma unroll
-    for (int t = 0; t < NPT; ++t) {
-      const int p = t * 256 + threadIdx.x;
-      if (p < NPIECE) {
-        const int hh = p / (16 * PPR), rem = p % (16 * PPR), row = rem / PPR, pc = rem % PPR;
-        const int cl = min(c0 + row, cl_last);
-        reg[t] = *reinterpret_cast<const uint4*>(kg + ((int64_t)hh * NCs + cl) * D + pc * EPV);
-      }
-    }
-    if (threadIdx.x < NH * 16) {
-      const int hh = threadIdx.x / 16, row = threadIdx.x % 16;
-      breg = bg[(int64_t)hh * NCs + min(c0 + row, cl_last)];
-    }
-  }
-  __device__ void commit(T* kt, float* bt) const {
-#pragma unroll
-    for (int t = 0; t < NPT; ++t) {
-      const int p = t * 256 + threadIdx.x;
-      if (p < NPIECE) {
-        const int hh = p / (16 * PPR), rem = p % (16 * PPR), row = rem / PPR, pc = rem % PPR;
-        *reinterpret_cast<uint4*>(kt + (hh * 16 + row) * KP + pc * EPV) = reg[t];
-      }
-    }
-    if (threadIdx.x < NH * 16) bt[threadIdx.x] = breg;
-  }
 };
 
+// The prefetched pieces live in one vector value (not an array), so that they
+// stay in registers whatever the unrolling order.
+template <int N> using u32v = uint32_t __attribute__((ext_vector_type(N)));
+
+template <typename T, int D, int NH, int NPT = KTile<T, D, NH>::NPT>
+__device__ __forceinline__ void tile_fetch(u32v<4 * NPT>& reg, float& breg, const T* kg,
+                                           const float* bg, int64_t NCs, int c0, int cl_last) {
+  using K = KTile<T, D, NH>;
+#pragma unroll
+  for (int t = 0; t < NPT; ++t) {
+    const int p = t * 256 + threadIdx.x;
+    if (K::NPIECE % 256 == 0 || p < K::NPIECE) {
+      const int hh = p / (16 * K::PPR), rem = p % (16 * K::PPR), row = rem / K::PPR, pc = rem % K::PPR;
+      const int cl = min(c0 + row, cl_last);
+      const uint4 v = *reinterpret_cast<const uint4*>(kg + ((int64_t)hh * NCs + cl) * D + pc * K::EPV);
+      reg[4 * t] = v.x; reg[4 * t + 1] = v.y; reg[4 * t + 2] = v.z; reg[4 * t + 3] = v.w;
+    }
+  }
+  if (threadIdx.x < NH * 16) {
+    const int hh = threadIdx.x / 16, row = threadIdx.x % 16;
+    breg = bg[(int64_t)hh * NCs + min(c0 + row, cl_last)];
+  }
+}
+
+template <typename T, int D, int NH, int NPT = KTile<T, D, NH>::NPT>
+__device__ __forceinline__ void tile_commit(const u32v<4 * NPT>& reg, float breg, T* kt, float* bt) {
+  using K = KTile<T, D, NH>;
+#pragma unroll
+  for (int t = 0; t < NPT; ++t) {
+    const int p = t * 256 + threadIdx.x;
+    if (K::NPIECE % 256 == 0 || p < K::NPIECE) {
+      const int hh = p / (16 * K::PPR), rem = p % (16 * K::PPR), row = rem / K::PPR, pc = rem % K::PPR;
+      *reinterpret_cast<uint4*>(kt + (hh * 16 + row) * K::KP + pc * K::EPV) =
+          make_uint4(reg[4 * t], reg[4 * t + 1], reg[4 * t + 2], reg[4 * t + 3]);
+    }
+  }
+  if (threadIdx.x < NH * 16) bt[threadIdx.x] = breg;
+}
+
+// Running log-sum-exp reference: finite, so that masked (-inf) scores add zero
+// without inf - inf; any real score exceeds it by far more than the 16 slack.
+constexpr float kRefInit = -1e30f;
+
 // L_{h,i} = LSE_{c in C_i} s_hat_{h,i,c}.  Workgroup = one head x 256 queries; a
-// wave owns 64 queries (four 16-row MFMA tiles, A fragments in registers) and
-// every 16-chunk k' tile is staged once in LDS for the four waves.
+// wave owns 64 queries and every 16-chunk k' tile is staged once in LDS for the
+// four waves.  Score tiles are transposed (rows = chunks, columns = queries), so
+// each lane holds four chunks of one query and keeps one running (m, s) per
+// 16-query tile.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh,
                                                         const T* __restrict__ ksum,
@@ -93,28 +107,25 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
   __shared__ __align__(16) T kt[16 * Tile::KP];
   __shared__ float bt[16];
   const int h = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
   const int64_t qb = (int64_t)blockIdx.x * 256;
   const int64_t q0 = qb + wave * 64;
   const bool live = q0 < T_;
 
-  Frag<T> a[4][KS];
-  int ncq[4][4];
-  float m[4][4], s[4][4];
+  Frag<T> qf[4][KS];   // column r16 of query tile rt
+  int ncq[4];
+  float m[4], s[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const int64_t qa = min(q0 + 16 * rt + r16, T_ - 1);
-    const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + qa) * D + 8 * grp;
+    const int64_t qi = q0 + 16 * rt + r16;
+    const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load_frag(a[rt][ks], qrow + 32 * ks);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t qi = q0 + 16 * rt + 4 * grp + i;
-      ncq[rt][i] = qi < T_ ? (int)num_candidates(qi, S, W) : 0;
-      m[rt][i] = kNegInf;
-      s[rt][i] = 0.f;
-    }
+    for (int ks = 0; ks < KS; ++ks) load_frag(qf[rt][ks], qrow + 32 * ks);
+    ncq[rt] = qi < T_ ? (int)num_candidates(qi, S, W) : 0;
+    m[rt] = kRefInit;
+    s[rt] = 0.f;
   }
   const int nc_block = (int)num_candidates(min(qb + 255, T_ - 1), S, W);
   const int ncmin = live ? (int)num_candidates(q0, S, W) : 0;
@@ -123,86 +134,92 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
   const T* kg = ksum + ((int64_t)b * Hq + h) * NCs * D;
   const float* bg = bsum + ((int64_t)b * Hq + h) * NCs;
   const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
-  Tile tile;
-  if (nc_block > 0) tile.fetch(kg, bg, NCs, 0, cl_last);
+  u32v<4 * Tile::NPT> kreg;
+  float breg = 0.f;
+  if (nc_block > 0) tile_fetch<T, D, 1>(kreg, breg, kg, bg, NCs, 0, cl_last);
   for (int c0 = 0; c0 < nc_block; c0 += 16) {
     __syncthreads();
-    tile.commit(kt, bt);
+    tile_commit<T, D, 1>(kreg, breg, kt, bt);
     __syncthreads();
-    if (c0 + 16 < nc_block) tile.fetch(kg, bg, NCs, c0 + 16, cl_last);  // in flight meanwhile
+    if (c0 + 16 < nc_block) tile_fetch<T, D, 1>(kreg, breg, kg, bg, NCs, c0 + 16, cl_last);
     if (c0 >= ncmax) continue;
-    Frag<T> bf[KS];
+    Frag<T> kf[KS];   // row r16 = chunk c0 + r16
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load_frag(bf[ks], kt + r16 * Tile::KP + 8 * grp + 32 * ks);
-    const float b2 = bt[r16] * kLog2e;
-    const int c = c0 + r16;
-    const bool full = c0 + 16 <= ncmin;
+    for (int ks = 0; ks < KS; ++ks) load_frag(kf[ks], kt + r16 * Tile::KP + 8 * grp + 32 * ks);
+    float b2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b2[i] = bt[4 * grp + i] * kLog2e;
+    f32x4_t acc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma(acc, a[rt][ks], bf[ks]);
+      for (int ks = 0; ks < KS; ++ks) mma(acc[rt], kf[ks], qf[rt][ks]);
+    }
+    const bool full = c0 + 16 <= ncmin;   // every query of the wave sees all 16 chunks
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (full || c < ncq[rt][i]) {
-          // the running reference m moves only when a score exceeds it by 16
-          const float x = fmaf(acc[i], sl2, b2);
-          if (x > m[rt][i] + 16.f) {
-            s[rt][i] *= hw_exp2(m[rt][i] - x);
-            m[rt][i] = x;
-          }
-          s[rt][i] += hw_exp2(x - m[rt][i]);
-        }
+        x[i] = fmaf(acc[rt][i], sl2, b2[i]);
+        if (!full && c0 + 4 * grp + i >= ncq[rt]) x[i] = kNegInf;
       }
+      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (mx > m[rt] + 16.f) {   // the reference moves only when a score passes it by 16
+        s[rt] *= hw_exp2(m[rt] - mx);
+        m[rt] = mx;
+      }
+      s[rt] += (hw_exp2(x[0] - m[rt]) + hw_exp2(x[1] - m[rt])) +
+               (hw_exp2(x[2] - m[rt]) + hw_exp2(x[3] - m[rt]));
     }
   }
   if (!live) return;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
+    float mm = m[rt], ss = s[rt];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mm = m[rt][i], ss = s[rt][i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float mo = __shfl_xor(mm, o, kWave);
-        const float so = __shfl_xor(ss, o, kWave);
-        const float mn = fmaxf(mm, mo);
-        if (mn != kNegInf)
-          ss = (mm == kNegInf ? 0.f : ss * hw_exp2(mm - mn)) + (mo == kNegInf ? 0.f : so * hw_exp2(mo - mn));
-        mm = mn;
-      }
-      const int64_t qi = q0 + 16 * rt + 4 * grp + i;
-      if (r16 == 0 && qi < T_)
-        Lout[((int64_t)b * Hq + h) * T_ + qi] = ncq[rt][i] > 0 ? (mm + log2f(ss)) * kLn2 : kNegInf;
+    for (int o = 16; o < 64; o <<= 1) {
+      const float mo = __shfl_xor(mm, o, kWave);
+      const float so = __shfl_xor(ss, o, kWave);
+      const float mn = fmaxf(mm, mo);
+      ss = ss * hw_exp2(mm - mn) + so * hw_exp2(mo - mn);
+      mm = mn;
     }
+    const int64_t qi = q0 + 16 * rt + r16;
+    if (grp == 0 && qi < T_)
+      Lout[((int64_t)b * Hq + h) * T_ + qi] = ncq[rt] > 0 ? (mm + log2f(ss)) * kLn2 : kNegInf;
   }
 }
+
+// Two waves per SIMD fit without spilling unless the candidate keys are wide.
+template <typename T, int D, int J>
+constexpr int rank_waves() { return (J <= 16 || (J == 32 && (sizeof(T) == 2 || D == 64))) ? 2 : 1; }
 
 // Rank keys, top-k and each head's s_hat on the selection, for one (b, group,
 // 64-query tile) per workgroup iteration (persistent workgroups, each owning a
 // scratch slot of rank keys).  Wave w handles heads w and w + 4 of the group:
 //   phase 1: per 16-chunk tile (k' of all G heads staged in LDS), each head's
-//            x = s_hat - L_h for the 64 queries goes to LDS, and the rank key
+//            x = s_hat - L_h for the 64 queries goes to LDS (transposed score
+//            tiles: a lane holds four chunks of one query), and the rank key
 //            r = max over heads (r = s_hat for one head) to the scratch slot;
 //   phase 2: each wave selects the top-k of 16 queries; then each head's wave
 //            computes its s_hat on every chosen chunk of the 64 queries.
-// Two waves per SIMD fit without spilling unless the candidate keys are wide.
-template <typename T, int D, int J>
-constexpr int rank_waves() { return (J <= 16 || (J == 32 && (sizeof(T) == 2 || D == 64))) ? 2 : 1; }
-
 template <typename T, int D, int G, int J>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(rank_waves<T, D, J>(), 2)))
 void rank_select_kernel(SelArgs a) {
   constexpr int KS = D / 32;
   constexpr int NCP = 64 * J;
   constexpr int HW = (G + 3) / 4;        // heads per wave
+  constexpr int XP = 20;                 // padded LDS row of 16 chunk values
   using Tile = KTile<T, D, G>;
   __shared__ __align__(16) T kt[G * 16 * Tile::KP];
   __shared__ float bt[G * 16];
-  __shared__ float xs[G][64][17];       // x = s_hat - L per head, 64 queries x 16 chunks
+  __shared__ __align__(16) float xs[G][64][XP];   // x = s_hat - L per head, 64 queries x 16 chunks
   __shared__ uint32_t sbuf[4][64];
   __shared__ int32_t sidx[64 * 64];      // 64 queries x up to 64 chosen ids
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
   const T* qh = static_cast<const T*>(a.qh);
   const T* ksum = static_cast<const T*>(a.ksum);
@@ -210,7 +227,8 @@ void rank_select_kernel(SelArgs a) {
   const int Hq = a.Hq, Hkv = a.Hkv, S = a.S, W = a.W, topk = a.topk;
   const int64_t nqt = (T_ + 63) / 64;
   const int64_t ntiles = (int64_t)a.B * Hkv * nqt;
-  float* slot = a.scratch + (int64_t)blockIdx.x * a.slot_stride;  // [64][NCP]
+  // rank keys as order-preserving unsigned images of the fp32 values, [64][NCP]
+  uint32_t* slot = reinterpret_cast<uint32_t*>(a.scratch) + (int64_t)blockIdx.x * a.slot_stride;
 
   for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
     const int64_t qt = tile_id % nqt;
@@ -220,18 +238,19 @@ void rank_select_kernel(SelArgs a) {
     const T* kg = ksum + ((int64_t)b * Hq + g * G) * NCs * D;   // head g*G, chunk 0
     const float* bg = a.bsum + ((int64_t)b * Hq + g * G) * NCs;
 
-    // this wave's heads: q_hat of the 64 queries (A operand) and L per row.  The
-    // fragments are loaded again for phase 2b so they are not live across the top-k.
-    Frag<T> af[HW][4][KS];
-    float Lr[HW][4][4];
-    auto load_a = [&](int u) {
+    // this wave's heads: q_hat of the 64 queries (fragment r16 of tile rt = query
+    // 16 rt + r16) and L of those queries.  The fragments are loaded again for
+    // phase 2b so they are not live across the top-k.
+    Frag<T> qf[HW][4][KS];
+    float Lq[HW][4];
+    auto load_q = [&](int u) {
       const int h = g * G + wave + 4 * u;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const int64_t qa = min(qb + 16 * rt + r16, T_ - 1);
         const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + qa) * D + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load_frag(af[u][rt][ks], qrow + 32 * ks);
+        for (int ks = 0; ks < KS; ++ks) load_frag(qf[u][rt][ks], qrow + 32 * ks);
       }
     };
 #pragma unroll
@@ -239,14 +258,11 @@ void rank_select_kernel(SelArgs a) {
       const int hh = wave + 4 * u;
       if (hh < G) {
         const int h = g * G + hh;
-        load_a(u);
+        load_q(u);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t qi = qb + 16 * rt + 4 * grp + i;
-            Lr[u][rt][i] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
-          }
+          const int64_t qi = qb + 16 * rt + r16;
+          Lq[u][rt] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
         }
       }
     }
@@ -254,42 +270,53 @@ void rank_select_kernel(SelArgs a) {
     // ---------- phase 1
     const int nc_block = (int)num_candidates(min(qb + 63, T_ - 1), S, W);
     const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
-    Tile tile;
-    if (nc_block > 0) tile.fetch(kg, bg, NCs, 0, cl_last);
+    u32v<4 * Tile::NPT> kreg;
+    float breg = 0.f;
+    if (nc_block > 0) tile_fetch<T, D, G>(kreg, breg, kg, bg, NCs, 0, cl_last);
     for (int c0 = 0; c0 < nc_block; c0 += 16) {
       __syncthreads();
-      tile.commit(kt, bt);
+      tile_commit<T, D, G>(kreg, breg, kt, bt);
       __syncthreads();
-      if (c0 + 16 < nc_block) tile.fetch(kg, bg, NCs, c0 + 16, cl_last);
+      if (c0 + 16 < nc_block) tile_fetch<T, D, G>(kreg, breg, kg, bg, NCs, c0 + 16, cl_last);
 #pragma unroll
       for (int u = 0; u < HW; ++u) {
         const int hh = wave + 4 * u;
         if (hh < G) {
-          Frag<T> bf[KS];
+          Frag<T> kf[KS];   // row r16 = chunk c0 + r16
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            load_frag(bf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
-          const float bv = bt[hh * 16 + r16];
+            load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
+          const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
+          f32x4_t acc[4];
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) mma(acc, af[u][rt][ks], bf[ks]);
+            for (int ks = 0; ks < KS; ++ks) mma(acc[rt], kf[ks], qf[u][rt][ks]);
+          }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              xs[hh][16 * rt + 4 * grp + i][r16] = fmaf(acc[i], a.scale, bv) - Lr[u][rt][i];
+          for (int rt = 0; rt < 4; ++rt) {
+            float4 x;
+            x.x = fmaf(acc[rt][0], a.scale, bk.x) - Lq[u][rt];
+            x.y = fmaf(acc[rt][1], a.scale, bk.y) - Lq[u][rt];
+            x.z = fmaf(acc[rt][2], a.scale, bk.z) - Lq[u][rt];
+            x.w = fmaf(acc[rt][3], a.scale, bk.w) - Lq[u][rt];
+            *reinterpret_cast<float4*>(&xs[hh][16 * rt + r16][4 * grp]) = x;
           }
         }
       }
       __syncthreads();
-      // wave w: rows 16w..16w+15 of the rank keys for this tile
+      // wave w: queries 16w + r16, chunks c0 + 4 grp .. + 3
+      {
+        const int row = 16 * wave + r16;
+        float4 r = *reinterpret_cast<const float4*>(&xs[0][row][4 * grp]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * grp + i;
-        float r = xs[0][row][r16];
-#pragma unroll
-        for (int hh = 1; hh < G; ++hh) r = fmaxf(r, xs[hh][row][r16]);
-        slot[row * NCP + c0 + r16] = r;
+        for (int hh = 1; hh < G; ++hh) {
+          const float4 y = *reinterpret_cast<const float4*>(&xs[hh][row][4 * grp]);
+          r.x = fmaxf(r.x, y.x); r.y = fmaxf(r.y, y.y); r.z = fmaxf(r.z, y.z); r.w = fmaxf(r.w, y.w);
+        }
+        *reinterpret_cast<uint4*>(slot + row * NCP + c0 + 4 * grp) =
+            make_uint4(order_key(r.x), order_key(r.y), order_key(r.z), order_key(r.w));
       }
     }
     __threadfence_block();
@@ -305,13 +332,14 @@ void rank_select_kernel(SelArgs a) {
         if (lane < topk) sel[lane] = lane < nc ? lane : -1;
       } else {
         uint32_t keys[J];
-        const float* rrow = slot + row * NCP;
+        const uint32_t* rrow = slot + row * NCP;
+        const int jn = (nc + 63) / 64;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
           const int c = lane + 64 * j;
-          keys[j] = c < nc ? order_key(rrow[c]) : 0u;
+          keys[j] = (j < jn && c < nc) ? rrow[c] : 0u;
         }
-        wave_topk_u32<J>(keys, topk, lane, sbuf[wave], sel);
+        wave_topk_u32<J>(keys, jn, topk, lane, sbuf[wave], sel);
       }
     }
     __syncthreads();
@@ -328,35 +356,50 @@ void rank_select_kernel(SelArgs a) {
       const int hh = wave + 4 * u;
       if (hh >= G) continue;
       const int h = g * G + hh;
-      load_a(u);
+      load_q(u);
       const int nslots = 64 * topk;
-      for (int t0 = 0; t0 < nslots; t0 += 16) {
-        const int sl = t0 + r16;
-        const int sq = sl / topk, st = sl % topk;         // this lane's column: query, slot
-        const int32_t cs = sl < nslots ? sidx[sq * 64 + st] : -1;
-        Frag<T> bf[KS];
-        float bv = 0.f;
-        if (cs >= 0) {  // pad slots read nothing: there may be no summaries at all
+      const T* kh = kg + (int64_t)hh * NCs * D;
+      const float* bh = bg + (int64_t)hh * NCs;
+      // P column tiles are gathered together, so P gathers are in flight at once
+      constexpr int P = sizeof(T) == 2 ? 4 : (D == 64 ? 2 : 1);
+      for (int t00 = 0; t00 < nslots; t00 += 16 * P) {
+        Frag<T> bf[P][KS];
+        float bv[P];
+        int32_t cs[P];
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            load_frag(bf[ks], kg + ((int64_t)hh * NCs + cs) * D + 8 * grp + 32 * ks);
-          bv = bg[(int64_t)hh * NCs + cs];
-        } else {
+        for (int pp = 0; pp < P; ++pp) {
+          const int sl = t00 + 16 * pp + r16;
+          cs[pp] = sl < nslots ? sidx[(sl / topk) * 64 + sl % topk] : -1;
+          if (cs[pp] >= 0) {  // pad slots read nothing: there may be no summaries at all
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) zero_frag(bf[ks]);
+            for (int ks = 0; ks < KS; ++ks)
+              load_frag(bf[pp][ks], kh + (int64_t)cs[pp] * D + 8 * grp + 32 * ks);
+            bv[pp] = bh[cs[pp]];
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) zero_frag(bf[pp][ks]);
+            bv[pp] = 0.f;
+          }
         }
-        const int rt_lo = (t0 / topk) / 16, rt_hi = (min(t0 + 15, nslots - 1) / topk) / 16;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          if (rt < rt_lo || rt > rt_hi) continue;   // uniform across the wave
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int pp = 0; pp < P; ++pp) {
+          const int t0 = t00 + 16 * pp;
+          if (t0 >= nslots) break;   // uniform
+          const int sl = t0 + r16;
+          const int sq = sl / topk, st = sl % topk;       // this lane's column: query, slot
+          const int rt_lo = (t0 / topk) / 16, rt_hi = (min(t0 + 15, nslots - 1) / topk) / 16;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) mma(acc, af[u][rt][ks], bf[ks]);
-          const int ii = sq - 16 * rt - 4 * grp;
-          if (sl < nslots && ii >= 0 && ii < 4 && qb + sq < T_) {
-            const float v = ii == 0 ? acc[0] : ii == 1 ? acc[1] : ii == 2 ? acc[2] : acc[3];
-            a.ssel[(((int64_t)b * Hq + h) * T_ + qb + sq) * topk + st] =
-                cs >= 0 ? fmaf(v, a.scale, bv) : kNegInf;
+          for (int rt = 0; rt < 4; ++rt) {
+            if (rt < rt_lo || rt > rt_hi) continue;   // uniform across the wave
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) mma(acc, qf[u][rt][ks], bf[pp][ks]);
+            const int ii = sq - 16 * rt - 4 * grp;
+            if (sl < nslots && ii >= 0 && ii < 4 && qb + sq < T_) {
+              const float v = ii == 0 ? acc[0] : ii == 1 ? acc[1] : ii == 2 ? acc[2] : acc[3];
+              a.ssel[(((int64_t)b * Hq + h) * T_ + qb + sq) * topk + st] =
+                  cs[pp] >= 0 ? fmaf(v, a.scale, bv[pp]) : kNegInf;
+            }
           }
         }
       }

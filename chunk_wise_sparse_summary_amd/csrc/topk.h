@@ -119,63 +119,84 @@ __device__ __forceinline__ void emit_ascending(const uint64_t (&v)[J], uint64_t 
   }
 }
 
+// The topk-th largest of one value per lane (with multiplicity), found bit by
+// bit from the top: the largest t with count(x >= t) >= topk.  Only ballots and
+// scalar counts, no cross-lane data movement.
+__device__ __forceinline__ uint32_t wave_kth_lane_u32(uint32_t x, int topk) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    if (__popcll(__ballot(x >= c)) >= topk) t = c;
+  }
+  return t;
+}
+
 // Exact top-k of 32-bit rank keys held J per lane, candidate id lane + 64*j
-// (key 0 = absent), more than topk present.  Ties at the k-th key go to the
-// lower ids.  Writes the chosen ids ascending to out[0..topk).  buf: 64
-// wave-private uint32 in LDS.
+// (key 0 = absent; keys[j] for j >= jn are all absent), more than topk present.
+// Ties at the k-th key go to the lower ids.  Writes the chosen ids ascending to
+// out[0..topk).  buf: 64 wave-private uint32 in LDS.
+//   1. theta = the k-th largest of the 64 per-lane maxima: a lower bound of the
+//      k-th largest key K (the k lanes with the largest maxima hold k keys >= theta);
+//   2. if at most 64 keys reach theta they are compacted one per lane and K is
+//      the k-th largest of those; otherwise K is found over all keys, bit by bit;
+//   3. every key above K is chosen, plus the lowest-id keys equal to K up to k.
 template <int J>
-__device__ void wave_topk_u32(const uint32_t (&keys)[J], int topk, int lane, uint32_t* buf,
+__device__ void wave_topk_u32(const uint32_t (&keys)[J], int jn, int topk, int lane, uint32_t* buf,
                               int32_t* out) {
   uint32_t lm = 0;
 #pragma unroll
-  for (int j = 0; j < J; ++j) lm = keys[j] > lm ? keys[j] : lm;
-  const uint32_t srt = bitonic_sort64<uint32_t>(lm, lane, true);
-  const uint32_t theta = __shfl(srt, topk - 1, kWave);   // <= the k-th largest key
-  int cnt = 0;
+  for (int j = 0; j < J; ++j)
+    if (j < jn) lm = keys[j] > lm ? keys[j] : lm;
+  const uint32_t theta = wave_kth_lane_u32(lm, topk);   // >= 1: more than topk keys present
+  int total = 0;
 #pragma unroll
-  for (int j = 0; j < J; ++j) cnt += (keys[j] != 0 && keys[j] >= theta) ? 1 : 0;
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int x = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += x;
-  }
-  const int total = __shfl(incl, 63, kWave);
+  for (int j = 0; j < J; ++j)
+    if (j < jn) total += __popcll(__ballot(keys[j] >= theta));
   uint32_t kstar;
   if (total <= 64) {
-    int pos = incl - cnt;
+    int base = 0;
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-      if (keys[j] != 0 && keys[j] >= theta) buf[pos++] = keys[j];
+    for (int j = 0; j < J; ++j) {
+      if (j < jn) {
+        const bool s = keys[j] >= theta;
+        const uint64_t m = __ballot(s);
+        if (s) buf[base + lane_prefix(m, lane)] = keys[j];
+        base += __popcll(m);
+      }
+    }
     wave_lds_sync();
     const uint32_t x = lane < total ? buf[lane] : 0u;
     wave_lds_sync();
-    kstar = __shfl(bitonic_sort64<uint32_t>(x, lane, true), topk - 1, kWave);
+    kstar = wave_kth_lane_u32(x, topk);
   } else {
-    uint32_t lo = theta > 0 ? theta : 1u, hi = __shfl(srt, 0, kWave);
-    while (lo < hi) {
-      const uint32_t mid = lo + (uint32_t)(((uint64_t)hi - lo + 1) >> 1);
-      int c = 0;
+    kstar = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = kstar | (1u << bit);
+      int n = 0;
 #pragma unroll
-      for (int j = 0; j < J; ++j) c += keys[j] >= mid ? 1 : 0;
-      if (wave_sum_i(c) >= topk) lo = mid; else hi = mid - 1;
+      for (int j = 0; j < J; ++j)
+        if (j < jn) n += __popcll(__ballot(keys[j] >= c));
+      if (n >= topk) kstar = c;
     }
-    kstar = lo;
   }
   int gt = 0;
 #pragma unroll
-  for (int j = 0; j < J; ++j) gt += keys[j] > kstar ? 1 : 0;
-  const int need = topk - wave_sum_i(gt);   // ties at kstar to take, lowest ids first
+  for (int j = 0; j < J; ++j)
+    if (j < jn) gt += __popcll(__ballot(keys[j] > kstar));
+  const int need = topk - gt;   // ties at kstar to take, lowest ids first
   int base = 0, eq_seen = 0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const bool eq = keys[j] == kstar;
-    const uint64_t meq = __ballot(eq);
-    const bool sel = keys[j] > kstar || (eq && eq_seen + lane_prefix(meq, lane) < need);
-    eq_seen += __popcll(meq);
-    const uint64_t m = __ballot(sel);
-    if (sel) out[base + lane_prefix(m, lane)] = lane + 64 * j;
-    base += __popcll(m);
+    if (j < jn) {
+      const bool eq = keys[j] == kstar;
+      const uint64_t meq = __ballot(eq);
+      const bool sel = keys[j] > kstar || (eq && eq_seen + lane_prefix(meq, lane) < need);
+      eq_seen += __popcll(meq);
+      const uint64_t m = __ballot(sel);
+      if (sel) out[base + lane_prefix(m, lane)] = lane + 64 * j;
+      base += __popcll(m);
+    }
   }
 }
 
