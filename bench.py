@@ -70,6 +70,139 @@ def decode_bytes(B, Hq, Hkv, d, S, W, k, positions, esz=2):
     return tot
 
 
+def selected_entries(B, Hkv, T, S, W, k):
+    nc, _ = window_stats(T, S, W)
+    return float(B * Hkv * np.sum(np.minimum(k, nc)))
+
+
+def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
+    """Algorithmic work of one launch of each prefill kernel: (bound, amount, unit).
+
+    FLOPs count the MFMA contractions; bytes count each operand the kernel must
+    move through HBM once in this design (no cache reuse assumed or credited)."""
+    G = Hq // Hkv
+    NC = T // S
+    nc, win = window_stats(T, S, W)
+    ncand = float(np.sum(nc))
+    nsel = float(np.sum(np.minimum(k, nc)))
+    ent = selected_entries(B, Hkv, T, S, W, k)
+    rows = float(B * Hq * T)
+    return {
+        "summarize": ("hbm", summary_bytes(B, Hq, Hkv, T, d, S, esz), "B"),
+        "score_lse": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
+        "rank_select": ("mfma", B * Hq * (ncand + nsel) * 2.0 * d, "FLOP"),
+        # K and V of every chunk once per KV head; per (query, group, slot) entry:
+        # the entry word, G rows of q, G selection scores and G log-normalisers
+        # read, G weighted partial rows written
+        "chunk_attend": ("hbm", float(B * Hkv * NC * S * d * esz * 2)
+                         + ent * (4 + G * d * esz * 2 + G * 8), "B"),
+        "window": ("mfma", B * Hq * float(np.sum(win)) * 4.0 * d, "FLOP"),
+        # per row: the window output and its log-mass, the selection normaliser,
+        # the row's partials and its group's index row, the output and lse
+        "combine": ("hbm", rows * (d * esz * 2 + 12) + B * Hq * nsel * d * esz
+                    + B * Hkv * T * k * 4.0, "B"),
+    }
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# Sources a kernel's code depends on: a change to any voids its stored counters.
+KERNEL_SOURCES = {
+    "chunk_attend": ["chunk_wise_sparse_summary_amd/csrc/attend.hip",
+                     "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+                     "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "combine": ["chunk_wise_sparse_summary_amd/csrc/attend.hip",
+                "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+                "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "window": ["chunk_wise_sparse_summary_amd/csrc/attend.hip",
+               "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+               "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "rank_select": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
+                    "chunk_wise_sparse_summary_amd/csrc/topk.h",
+                    "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+                    "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "score_lse": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
+                  "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+                  "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "summarize": ["chunk_wise_sparse_summary_amd/csrc/summarize.hip",
+                  "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+                  "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_128k_prefill.txt")
+COPY_PROBE_BYTES = 1 << 30
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the stored counter summary, or None if
+    absent or taken on a different version of the kernel's sources."""
+    if not os.path.exists(TRAFFIC_FILE) or kernel not in KERNEL_SOURCES:
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get(kernel + ".source") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(vals[kernel + ".fetch_bytes"]) + float(vals[kernel + ".write_bytes"])
+    except KeyError:
+        return None
+
+
+def ingest_pmc(fetch_csv, write_csv, command, out_path=TRAFFIC_FILE):
+    """Turn two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE in KiB per dispatch)
+    into per-launch HBM bytes of each library kernel, scaled by what the same
+    counters read for the copy probe (a device copy of COPY_PROBE_BYTES)."""
+    import csv
+
+    def load(path, counter):
+        # the last dispatch of each kernel is the one of the profiled prefill step
+        per = {}
+        copy = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, v, did = r["Kernel_Name"], float(r["Counter_Value"]), int(r["Dispatch_Id"])
+            if "copyBuffer" in name:
+                copy.append(v)
+            for kname in KERNEL_SOURCES:
+                if "::%s_kernel" % kname in name and (kname not in per or did > per[kname][0]):
+                    per[kname] = (did, v)
+        return {kn: [v] for kn, (_, v) in per.items()}, max(copy) if copy else None
+
+    fetch, cf = load(fetch_csv, "FETCH_SIZE")
+    write, cw = load(write_csv, "WRITE_SIZE")
+    if not cf or not cw:
+        raise SystemExit("no copy-probe dispatch in the counter files")
+    kib = COPY_PROBE_BYTES / 1024.0
+    ff, fw = kib / cf, kib / cw
+    lines = ["# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE; KiB",
+             "# per dispatch), scaled by the copy probe: a %d-byte device copy read"
+             % COPY_PROBE_BYTES,
+             "# FETCH_SIZE %.1f KiB and WRITE_SIZE %.1f KiB (factors %.4f, %.4f)." % (cf, cw, ff, fw),
+             "# commands:"] + ["#   " + c for c in command] + [
+             "copy_probe.fetch_factor = %.6f" % ff, "copy_probe.write_factor = %.6f" % fw]
+    for kname in KERNEL_SOURCES:
+        if not fetch.get(kname) or not write.get(kname):
+            continue
+        fb = float(np.mean(fetch[kname])) * 1024.0 * ff
+        wb = float(np.mean(write[kname])) * 1024.0 * fw
+        lines += ["%s.fetch_bytes = %.0f" % (kname, fb),
+                  "%s.write_bytes = %.0f" % (kname, wb),
+                  "%s.source = %s" % (kname, source_digest(KERNEL_SOURCES[kname]))]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(x, wl, seconds=10.0):
     """The fp64 oracle on the host: summaries of every chunk plus a sample of query rows."""
     import torch
@@ -113,7 +246,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=64,
                     help="decode steps per bench step (64: one chunk completion per step)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run a %d-byte device copy first (counter calibration)" % COPY_PROBE_BYTES)
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM-traffic summary from two rocprofv3 counter runs and exit")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="with --ingest-pmc: the profiling command lines, for the record")
+    ap.add_argument("--traffic-out", default=TRAFFIC_FILE,
+                    help="with --ingest-pmc: where to write the summary")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.pmc_command, args.traffic_out)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the HiLS path here runs on a single device and has "
               "no multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -197,6 +341,15 @@ def main():
         e[4].record()
         return e, de
 
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    prefill_kernels = ["summarize", "score_lse", "rank_select", "idx_count", "idx_scan_tiles",
+                       "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend", "combine"]
     log("warmup")
     for _ in range(args.warmup):
         step(False)
@@ -204,6 +357,7 @@ def main():
     dpos[0] = 0  # decode positions restart: every timed step sees the same cache lengths
     log("timed steps")
     recs = []
+    hils.hils_timing_enable(prefill_kernels)   # per-kernel HIP events on the launch stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0 = torch.cuda.Event(enable_timing=True)
@@ -215,6 +369,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = g0.elapsed_time(g1)
+    ktime = {}
+    for kn in prefill_kernels:
+        tms, nl = hils.hils_timing_get(kn)
+        if nl:
+            ktime[kn] = (tms / nl, nl / args.steps)   # ms per launch, launches per step
+    hils.hils_timing_enable(None)
     for e, de in recs:
         times["summarize"].append(e[0].elapsed_time(e[1]))
         times["select"].append(e[1].elapsed_time(e[2]))
@@ -230,25 +390,34 @@ def main():
     sf = score_flops(B, Hq, T, d, S, W)
     sb = summary_bytes(B, Hq, Hkv, T, d, S)
     dpositions = [L0 + s for s in range(args.decode_steps)]
-    db = decode_bytes(dl.B, dl.Hq, dl.Hkv, dl.d, dl.S, dl.W, dl.k, dpositions) / len(dpositions)
+    db = decode_bytes(dl.B, dl.Hq, dl.Hkv, dl.d, dl.S, dl.W, dl.k, dpositions) / max(len(dpositions), 1)
     parts = {
         "summarize": {"bound": "hbm", "work": sb, "unit": "GB/s", "peak": PEAK_HBM},
         "select": {"bound": "mfma", "work": sf, "unit": "TFLOP/s", "peak": PEAK_BF16},
         "attend_fuse": {"bound": "mfma", "work": af, "unit": "TFLOP/s", "peak": PEAK_BF16},
         "decode": {"bound": "hbm", "work": db, "unit": "GB/s", "peak": PEAK_HBM},
     }
-    per_step_ms = {"summarize": avg["summarize"], "select": avg["select"],
-                   "attend_fuse": avg["attend_fuse"],
-                   "decode": avg["decode"] * args.decode_steps}
-    dom = max(per_step_ms, key=per_step_ms.get)
-    p = parts[dom]
-    ach = p["work"] / (avg[dom] * 1e-3)
-    scale = 1e9 if p["unit"] == "GB/s" else 1e12
-    roof = {"bound": p["bound"], "kernel": "hils_" + dom, "achieved": ach / scale,
-            "peak": p["peak"] / scale, "unit": p["unit"], "frac": ach / p["peak"],
-            "traffic": None,
-            "work_per_launch": p["work"],
-            "avg_launch_ms": avg[dom]}
+    kw = kernel_work(B, Hq, Hkv, T, d, S, W, k)
+    kernels = {}
+    for kn, (ms_l, per_step) in ktime.items():
+        ent = {"avg_launch_ms": ms_l, "launches_per_step": per_step}
+        if kn in kw:
+            bound, amount, u = kw[kn]
+            scale_ = 1e9 if u == "B" else 1e12
+            ent.update({"bound": bound, "work_per_launch": amount,
+                        "achieved": amount / (ms_l * 1e-3) / scale_,
+                        "unit": "GB/s" if u == "B" else "TFLOP/s",
+                        "frac": amount / (ms_l * 1e-3) / (PEAK_HBM if u == "B" else PEAK_BF16)})
+        kernels[kn] = ent
+    dom = max((kn for kn in kernels if kn in kw),
+              key=lambda kn: kernels[kn]["avg_launch_ms"] * kernels[kn]["launches_per_step"])
+    kd = kernels[dom]
+    traffic = read_traffic(dom)
+    roof = {"bound": kd["bound"], "kernel": dom + "_kernel", "achieved": kd["achieved"],
+            "peak": (PEAK_HBM / 1e9) if kd["unit"] == "GB/s" else (PEAK_BF16 / 1e12),
+            "unit": kd["unit"], "frac": kd["frac"],
+            "traffic": traffic, "work_per_launch": kd["work_per_launch"],
+            "avg_launch_ms": kd["avg_launch_ms"]}
     breakdown = {}
     for n_, pp in parts.items():
         a_ = pp["work"] / (avg[n_] * 1e-3)
@@ -275,6 +444,7 @@ def main():
         "summary_512k_cache_GBps": sum_dec_bytes / (min(sum_ms) * 1e-3) / 1e9,
         "roofline": roof,
         "breakdown": breakdown,
+        "kernels": kernels,
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:

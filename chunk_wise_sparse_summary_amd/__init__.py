@@ -11,6 +11,7 @@ if the library is missing, loading raises.
     hils_decode_step(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache,
                      k_sum, b_sum, out, lse, sel_idx, shape, workspace=None)
     hils_workspace_bytes(shape, op)
+    hils_timing_enable(kernels), hils_timing_get(kernel)   (diagnostics)
 
 `Shape` mirrors `hils_shape`.  `prefill()` chains the three prefill calls.
 """
@@ -34,7 +35,8 @@ STATUS = {
 }
 
 EXPORTS = ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
-           "hils_workspace_bytes", "hils_status_string", "hils_abi_version")
+           "hils_workspace_bytes", "hils_status_string", "hils_abi_version",
+           "hils_timing_enable", "hils_timing_get")
 
 
 class HilsError(RuntimeError):
@@ -78,6 +80,11 @@ def lib():
         L.hils_status_string.argtypes = [ctypes.c_int]
         L.hils_status_string.restype = ctypes.c_char_p
         L.hils_abi_version.restype = ctypes.c_int
+        L.hils_timing_enable.argtypes = [ctypes.c_char_p]
+        L.hils_timing_enable.restype = ctypes.c_int
+        L.hils_timing_get.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_int64)]
+        L.hils_timing_get.restype = ctypes.c_int
         for f in ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -155,6 +162,30 @@ def hils_decode_step(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, 
         ctypes.byref(shape), pos_arr, _p(q), _p(q_hat), _p(k_new), _p(v_new), _p(q_land_new),
         _p(k_cache), _p(v_cache), _p(k_sum), _p(b_sum), _p(out), _p(lse), _p(sel_idx),
         _p(workspace_t), workspace_t.numel(), _stream()))
+
+
+KERNELS = ("summarize", "score_lse", "rank_select", "idx_count", "idx_scan_tiles",
+           "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend", "combine",
+           "dec_score", "dec_span", "dec_merge", "dec_attend", "dec_fuse", "dec_summarize")
+
+
+def hils_timing_enable(kernels):
+    """Time launches of the named kernels (iterable of names, "*" for all, None for off)."""
+    if kernels is None:
+        arg = None
+    elif isinstance(kernels, str):
+        arg = kernels.encode()
+    else:
+        arg = ",".join(kernels).encode()
+    _check("hils_timing_enable", lib().hils_timing_enable(arg))
+
+
+def hils_timing_get(kernel: str):
+    """(total milliseconds, launches) of a kernel's timed launches since enabling."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check("hils_timing_get", lib().hils_timing_get(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def prefill(q, k, v, q_land, q_hat, *, S: int, W: int, topk: int, scale: float = 0.0,

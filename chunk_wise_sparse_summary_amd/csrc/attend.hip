@@ -642,6 +642,7 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
   {
     WinArgs wa{a.q, a.k, a.v, ow, lzw, a.B, a.Hq, a.Hkv, a.S, a.W, a.T, a.scale};
     const int QB = 4 * (32 / G);
+    KTimer tm(K_WINDOW, st);
     hipLaunchKernelGGL((window_kernel<T, D, G>), dim3((unsigned)((a.T + QB - 1) / QB), a.Hkv, a.B),
                        dim3(256), 0, st, wa);
     hipError_t e = hipGetLastError();
@@ -652,6 +653,7 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
     if (ia.NCs > 0 && a.topk > 0) {
       ChunkArgs ca{a.q, a.k, a.v, a.ssel, ia.lsel, ia.bcount, ia.bbase, ia.entries, part,
                    a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, a.scale};
+      KTimer tm(K_CHUNK_ATTEND, st);
       hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)ia.NCs, gp, a.B), dim3(256),
                          0, st, ca);
       hipError_t e = hipGetLastError();
@@ -660,6 +662,7 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
     CombArgs cb{ow, lzw, ia.lsel, a.idx, part, a.out, a.lse, a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T};
     constexpr int PPR = D / (16 / (int)sizeof(T));
     const int64_t nthreads = (int64_t)a.B * gpp * G * a.T * PPR;
+    KTimer tm(K_COMBINE, st);
     hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3((unsigned)((nthreads + 255) / 256)), dim3(256),
                        0, st, cb);
     hipError_t e = hipGetLastError();
@@ -734,16 +737,27 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
 
   if (a.topk > 0 && NCs > 0) {
     const size_t lds = (size_t)NCs * sizeof(uint64_t);
-    hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
-    hipLaunchKernelGGL(idx_scan_tiles_kernel, dim3((unsigned)((NCs + 31) / 32), a.B * a.Hkv),
-                       dim3(1024), 0, st, ia);
-    hipLaunchKernelGGL(idx_scan_buckets_kernel, dim3(1), dim3(1024), 0, st, ia);
+    {
+      KTimer tm(K_IDX_COUNT, st);
+      hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
+    }
+    {
+      KTimer tm(K_IDX_SCAN_TILES, st);
+      hipLaunchKernelGGL(idx_scan_tiles_kernel, dim3((unsigned)((NCs + 31) / 32), a.B * a.Hkv),
+                         dim3(1024), 0, st, ia);
+    }
+    {
+      KTimer tm(K_IDX_SCAN_BUCKETS, st);
+      hipLaunchKernelGGL(idx_scan_buckets_kernel, dim3(1), dim3(1024), 0, st, ia);
+    }
+    KTimer tm(K_IDX_FILL, st);
     hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
   }
   if (a.topk > 0) {
     int L = 1;
     while (L < a.topk) L <<= 1;
     const int64_t nl = (int64_t)a.B * a.Hq * a.T * L;
+    KTimer tm(K_LSEL, st);
     hipLaunchKernelGGL(lsel_kernel, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0, st, ia, L);
   } else {
     ia.lsel = nullptr;  // no selection: the window is the whole normaliser

@@ -398,6 +398,8 @@ __global__ __launch_bounds__(64) void dec_fuse_kernel(DecKArgs a) {
 template <int G>
 void launch_select_j(const DecKArgs& k, hipStream_t st) {
   const dim3 grid(k.w.nspan, k.Hkv, k.B), block(64);
+  {
+  KTimer tm(K_DEC_SPAN, st);
   switch (k.w.span / 64) {
     case 1: hipLaunchKernelGGL((dec_span_kernel<G, 1>), grid, block, 0, st, k); break;
     case 2: hipLaunchKernelGGL((dec_span_kernel<G, 2>), grid, block, 0, st, k); break;
@@ -407,15 +409,26 @@ void launch_select_j(const DecKArgs& k, hipStream_t st) {
     case 32: hipLaunchKernelGGL((dec_span_kernel<G, 32>), grid, block, 0, st, k); break;
     default: hipLaunchKernelGGL((dec_span_kernel<G, 64>), grid, block, 0, st, k); break;
   }
+  }
+  KTimer tm(K_DEC_MERGE, st);
   hipLaunchKernelGGL((dec_merge_kernel<G>), dim3(1, k.Hkv, k.B), block, 0, st, k);
 }
 
 template <typename T, int D, int G>
 hipError_t launch_decode_tg(const DecKArgs& k, hipStream_t st) {
-  hipLaunchKernelGGL((dec_score_kernel<T, D, G>), dim3(k.w.nslice, k.Hkv, k.B), dim3(256), 0, st, k);
+  {
+    KTimer tm(K_DEC_SCORE, st);
+    hipLaunchKernelGGL((dec_score_kernel<T, D, G>), dim3(k.w.nslice, k.Hkv, k.B), dim3(256), 0, st, k);
+  }
   if (k.topk > 0) launch_select_j<G>(k, st);
-  hipLaunchKernelGGL((dec_attend_kernel<T, D, G>), dim3(k.w.nitems, k.Hkv, k.B), dim3(64 * G), 0, st, k);
-  hipLaunchKernelGGL((dec_fuse_kernel<T, D, G>), dim3(k.Hq, k.B), dim3(64), 0, st, k);
+  {
+    KTimer tm(K_DEC_ATTEND, st);
+    hipLaunchKernelGGL((dec_attend_kernel<T, D, G>), dim3(k.w.nitems, k.Hkv, k.B), dim3(64 * G), 0, st, k);
+  }
+  {
+    KTimer tm(K_DEC_FUSE, st);
+    hipLaunchKernelGGL((dec_fuse_kernel<T, D, G>), dim3(k.Hq, k.B), dim3(64), 0, st, k);
+  }
   return hipGetLastError();
 }
 

@@ -92,6 +92,27 @@ struct DecArgs {
   size_t ws_bytes;
 };
 hipError_t launch_decode(const DecArgs& a, hipStream_t st);
+
+// Optional per-kernel timing (the C ABI's hils_timing_* calls): a KTimer around
+// a launch records a HIP event pair on the launch stream when that kernel is
+// selected, and does nothing otherwise.
+enum KernelId {
+  K_SUMMARIZE, K_SCORE_LSE, K_RANK_SELECT, K_IDX_COUNT, K_IDX_SCAN_TILES, K_IDX_SCAN_BUCKETS,
+  K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_COMBINE, K_DEC_SCORE, K_DEC_SPAN, K_DEC_MERGE,
+  K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_COUNT
+};
+class KTimer {
+ public:
+  KTimer(KernelId id, hipStream_t st);
+  ~KTimer();
+  KTimer(const KTimer&) = delete;
+  KTimer& operator=(const KTimer&) = delete;
+
+ private:
+  KernelId id_;
+  hipStream_t st_;
+  hipEvent_t e0_;
+};
 size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk);
 // Whether the decode selection can merge its per-span lists in one wave.
 bool decode_supported(int64_t Lcap, int S, int W, int topk);

@@ -411,6 +411,7 @@ void rank_select_kernel(SelArgs a) {
 template <typename T, int D, int G>
 hipError_t launch_rank(const SelArgs& a, int J, hipStream_t st) {
   dim3 grid((unsigned)a.n_slots), block(256);
+  KTimer tm(K_RANK_SELECT, st);
   switch (J) {
     case 1: hipLaunchKernelGGL((rank_select_kernel<T, D, G, 1>), grid, block, 0, st, a); break;
     case 4: hipLaunchKernelGGL((rank_select_kernel<T, D, G, 4>), grid, block, 0, st, a); break;
@@ -426,6 +427,7 @@ hipError_t launch_select_t(const SelArgs& a, int J, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   if (G > 1) {
     dim3 grid((unsigned)((a.T + 255) / 256), (unsigned)a.Hq, (unsigned)a.B);
+    KTimer tm(K_SCORE_LSE, st);
     hipLaunchKernelGGL((score_lse_kernel<T, D>), grid, dim3(256), 0, st,
                        static_cast<const T*>(a.qh), static_cast<const T*>(a.ksum), a.bsum, a.L,
                        a.Hq, a.T, a.NCs, a.S, a.W, a.scale);

@@ -102,6 +102,7 @@ template <typename T, int D>
 static hipError_t launch_summarize_t(const SumArgs& a, hipStream_t st) {
   dim3 grid = a.list.n > 0 ? dim3((unsigned)a.list.n, (unsigned)a.Hkv, 1u)
                            : dim3((unsigned)a.n_chunks, (unsigned)a.Hkv, (unsigned)a.B);
+  KTimer tm(a.list.n > 0 ? K_DEC_SUMMARIZE : K_SUMMARIZE, st);
   hipLaunchKernelGGL((summarize_kernel<T, D>), grid, dim3(256), 0, st,
                      static_cast<const T*>(a.k), static_cast<const T*>(a.ql),
                      static_cast<T*>(a.ksum), a.bsum, a.Hq, a.Hkv, a.kT, a.NCs, a.ql_sb, a.ql_sh,

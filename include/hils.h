@@ -201,6 +201,28 @@ const char* hils_status_string(hils_status status);
 /* HILS_ABI_VERSION of the built library. */
 int hils_abi_version(void);
 
+/* ---- Diagnostics: per-kernel timing ------------------------------------
+ * Not part of the computation.  While enabled, each launch of a selected
+ * kernel is bracketed by two HIP events recorded on the stream it is launched
+ * on, so the measured time is that kernel's own duration on the device.
+ *
+ * hils_timing_enable(kernels): kernels is a comma-separated list of kernel
+ *   names, "*" for all, or NULL to switch timing off.  Enabling clears every
+ *   earlier record (after waiting for its events).  Names: summarize,
+ *   score_lse, rank_select, idx_count, idx_scan_tiles, idx_scan_buckets,
+ *   idx_fill, lsel, window, chunk_attend, combine, dec_score, dec_span,
+ *   dec_merge, dec_attend, dec_fuse, dec_summarize (the summaries of chunks
+ *   completed by a decode step).  HILS_E_UNSUPPORTED for an unknown name
+ *   (timing is then left off).
+ * hils_timing_get(kernel, total_ms, launches): waits for the recorded events
+ *   of that kernel and returns the summed duration and the number of timed
+ *   launches since the last enable.  HILS_E_NULL for NULL outputs or name,
+ *   HILS_E_UNSUPPORTED for an unknown name.
+ * The timing state is process-wide and not thread-safe; calls that launch
+ * while timing is enabled must come from one host thread. */
+hils_status hils_timing_enable(const char* kernels);
+hils_status hils_timing_get(const char* kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -110,3 +110,18 @@ def test_decode_validation():
     s3 = _shape(B=65, T=4096, k=8)
     arr3 = (ctypes.c_int64 * 65)(*([1] * 65))
     assert L.hils_decode_step(ctypes.byref(s3), arr3, *[P(16)] * 13, 1 << 30, None) == -8
+
+
+def test_timing_names_and_errors():
+    L = hils.lib()
+    assert L.hils_timing_enable(b"no_such_kernel") == -8
+    assert L.hils_timing_enable(b"chunk_attend,window") == 0
+    ms, n = hils.hils_timing_get("chunk_attend")
+    assert (ms, n) == (0.0, 0)
+    with pytest.raises(hils.HilsError):
+        hils.hils_timing_get("nope")
+    assert L.hils_timing_get(b"window", None, None) == -1
+    for k in hils.KERNELS:
+        hils.hils_timing_enable([k])
+    hils.hils_timing_enable("*")
+    hils.hils_timing_enable(None)
