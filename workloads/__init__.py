@@ -85,6 +85,10 @@ CONFIGS = {
 NEEDLE_ALPHA = 8.0
 NEEDLE_BETA = 8.0
 NEEDLE_GAMMA = 8.0
+# A decode query spreads ALPHA_DECODE over n needles (ALPHA_DECODE/sqrt(n) each,
+# along mutually orthogonal directions), so it needs a larger total: with 8
+# needles this places every needle chunk's rank key well above the haystack.
+NEEDLE_ALPHA_DECODE = 32.0
 
 
 def prefill_config(name: str) -> Workload:
@@ -253,6 +257,9 @@ def make_decode_cache(wl: Workload | str, seed: int = 0, device="cpu", length: i
         n_far = max(1, (L - wl.W) // S - 1)
         chunks = np.sort(rng.choice(n_far, size=wl.needles, replace=False))
         u = np.stack([[_unit(rng, d) for _ in range(Hkv)] for _ in range(wl.needles)])  # [n, Hkv, d]
+        for g in range(Hkv):      # orthonormal needle directions within each KV head
+            qm, _ = np.linalg.qr(u[:, g, :].T)
+            u[:, g, :] = qm.T[:wl.needles]
         toks = chunks * S + rng.integers(0, S, size=wl.needles)
         for n in range(wl.needles):
             for b in range(B):
@@ -269,7 +276,7 @@ def make_decode_step(wl: Workload | str, step: int, seed: int = 0, device="cpu",
                      needle_dirs: np.ndarray | None = None) -> dict:
     """Per-step inputs: q, q_hat [B, Hq, d], k_new, v_new [B, Hkv, d], q_land_new [B, Hq, d].
 
-    With needles, q = q_hat = ALPHA * sum_n u_n / sqrt(n) + Gaussian noise.
+    With needles, q = q_hat = ALPHA_DECODE * sum_n u_n / sqrt(n) + Gaussian noise.
     """
     if isinstance(wl, str):
         wl = CONFIGS[wl]
@@ -285,7 +292,7 @@ def make_decode_step(wl: Workload | str, step: int, seed: int = 0, device="cpu",
     if needle_dirs is not None:
         nn = needle_dirs.shape[0]
         for h in range(Hq):
-            dirn = NEEDLE_ALPHA * needle_dirs[:, h // G, :].sum(0) / math.sqrt(nn)
+            dirn = NEEDLE_ALPHA_DECODE * needle_dirs[:, h // G, :].sum(0) / math.sqrt(nn)
             q[:, h, :] += dirn
             qh[:, h, :] = q[:, h, :]
     dev = torch.device(device)
