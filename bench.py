@@ -91,11 +91,11 @@ def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
         "summarize": ("hbm", summary_bytes(B, Hq, Hkv, T, d, S, esz), "B"),
         "score_lse": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
         "rank_select": ("mfma", B * Hq * (ncand + nsel) * 2.0 * d, "FLOP"),
-        # K and V of every chunk once per KV head; per (query, group, slot) entry:
-        # the entry word, G rows of q, G selection scores and G log-normalisers
-        # read, G weighted partial rows written
+        # K and V^T of every chunk once per KV head; per (query, group, slot)
+        # entry: the entry word, G rows of q and G chunk weights read, G weighted
+        # partial rows written
         "chunk_attend": ("hbm", float(B * Hkv * NC * S * d * esz * 2)
-                         + ent * (4 + G * d * esz * 2 + G * 8), "B"),
+                         + ent * (4 + G * d * esz * 2 + G * 4), "B"),
         "window": ("mfma", B * Hq * float(np.sum(win)) * 4.0 * d, "FLOP"),
         # per row: the window output and its log-mass, the selection normaliser,
         # the row's partials and its group's index row, the output and lse

@@ -37,9 +37,6 @@ namespace {
 
 constexpr int kS = 64;  // chunk size
 
-template <typename T> struct Pad;
-template <> struct Pad<bf16_t> { static constexpr int K = 8, V = 4; };
-template <> struct Pad<float> { static constexpr int K = 4, V = 4; };
 
 struct IdxArgs {
   const int32_t* idx;
@@ -48,6 +45,7 @@ struct IdxArgs {
   int32_t* bcount;     // [B, Hkv, NCs]
   int64_t* bbase;      // [B, Hkv, NCs]
   uint32_t* entries;   // i * 64 + slot
+  float* wq;           // [B, Hkv, T, topk, G] chunk weights exp(s_hat - L_sel) per head
   float* lsel;         // [B, Hq, T]
   int B, Hq, Hkv, topk;
   int64_t T, NCs, ntiles;
@@ -129,7 +127,7 @@ __global__ __launch_bounds__(1024) void idx_scan_buckets_kernel(IdxArgs a) {
   }
 }
 
-// Entries at their final positions, and L_sel = LSE of each head's selected s_hat.
+// Entries at their final positions.
 __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
   extern __shared__ uint64_t bm[];
   const int64_t t = blockIdx.x;
@@ -151,64 +149,147 @@ __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
 }
 
 
-// L_sel = LSE of each head's s_hat over its selected chunks (-inf if none).
-// L lanes per row (L = smallest power of two >= k), rows of 64/L per wave.
+// L_sel = LSE of each head's s_hat over its selected chunks (-inf if none), and
+// each selected chunk's weight exp(s_hat - L_sel) for the G heads of the group,
+// stored together ([B, Hkv, T, topk, G]) so the chunk-major pass reads one
+// contiguous record per (query, slot).  L lanes per (b, g, i) row (L = smallest
+// power of two >= k), lane = slot.
+template <int G>
 __global__ __launch_bounds__(256) void lsel_kernel(IdxArgs a, int L) {
   const int64_t lane_g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = lane_g / L;
+  const int64_t row = lane_g / L;                 // (b, g, i)
   const int l = (int)(lane_g % L);
-  const int64_t nrows = (int64_t)a.B * a.Hq * a.T;
+  const int64_t nrows = (int64_t)a.B * a.Hkv * a.T;
   const bool live = row < nrows;
   const int64_t rr = live ? row : nrows - 1;
   const int64_t i = rr % a.T;
-  const int h = (int)((rr / a.T) % a.Hq);
-  const int b = (int)(rr / (a.T * a.Hq));
-  const int g = h / (a.Hq / a.Hkv);
-  float x = kNegInf;
-  if (l < a.topk) {
-    const int32_t c = a.idx[(((int64_t)b * a.Hkv + g) * a.T + i) * a.topk + l];
-    if (c >= 0) x = a.ssel[rr * a.topk + l];
+  const int g = (int)((rr / a.T) % a.Hkv);
+  const int b = (int)(rr / (a.T * a.Hkv));
+  const bool sel = l < a.topk && a.idx[rr * a.topk + l] >= 0;
+  float w[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const int64_t rowq = ((int64_t)b * a.Hq + g * G + hh) * a.T + i;
+    const float x = sel ? a.ssel[rowq * a.topk + l] : kNegInf;
+    float m = x;
+    for (int o = 1; o < L; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    float z = (x == kNegInf) ? 0.f : __expf(x - m);
+    for (int o = 1; o < L; o <<= 1) z += __shfl_xor(z, o, kWave);
+    const float ls = m == kNegInf ? kNegInf : m + __logf(z);
+    if (live && l == 0) a.lsel[rowq] = ls;
+    w[hh] = sel ? __expf(x - ls) : 0.f;
   }
-  float m = x;
-  for (int o = 1; o < L; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-  float z = (x == kNegInf) ? 0.f : __expf(x - m);
-  for (int o = 1; o < L; o <<= 1) z += __shfl_xor(z, o, kWave);
-  if (live && l == 0) a.lsel[rr] = m == kNegInf ? kNegInf : m + __logf(z);
+  if (live && l < a.topk) {
+    float* dst = a.wq + (rr * a.topk + l) * G;
+    if constexpr (G % 4 == 0) {
+#pragma unroll
+      for (int q = 0; q < G; q += 4)
+        *reinterpret_cast<float4*>(dst + q) = make_float4(w[q], w[q + 1], w[q + 2], w[q + 3]);
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) dst[hh] = w[hh];
+    }
+  }
 }
 
-// Stage one chunk of K (row-major) and V (transposed) into LDS with NT threads.
-template <typename T, int D, int NT>
-__device__ __forceinline__ void stage_chunk(const T* kc, const T* vc, T* ks, T* vt, int64_t nvalid) {
+// LDS tiles of one chunk: K as [kS][D] and V^T as [D][kS], unpadded, with the
+// 16-byte pieces of each row XOR-swizzled so that the 16 rows an MFMA operand
+// read touches at one logical column land in distinct banks (rows of >= 256
+// bytes: swizzle by row mod 16; rows of 128 bytes: by (row / 2) mod 8, since two
+// consecutive rows already split the banks).
+template <int PPR>
+__device__ __forceinline__ int swz(int r, int p) {
+  return r * PPR + (p ^ (PPR >= 16 ? (r & 15) : ((r >> 1) & 7)));
+}
+
+// V^T of every chunk, [B, Hkv, ceil(T/S), D, S]; tokens past T are zero.  Lets the
+// attention kernels stage V^T tiles with plain 16-byte copies.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, T* __restrict__ vt, int Hkv,
+                                                 int64_t T_, int64_t NCf) {
   constexpr int EPV = 16 / sizeof(T);
-  constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
+  constexpr int VP = D + EPV;   // padded LDS row
+  __shared__ __align__(16) T tile[kS * VP];
+  const int64_t c = blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const T* src = v + (((int64_t)b * Hkv + g) * T_ + c * kS) * D;
+  for (int e = threadIdx.x; e < kS * D / EPV; e += 256) {
+    const int row = e / (D / EPV), pc = e % (D / EPV);
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (c * kS + row < T_) u = *reinterpret_cast<const uint4*>(src + (int64_t)row * D + pc * EPV);
+    *reinterpret_cast<uint4*>(tile + row * VP + pc * EPV) = u;
+  }
+  __syncthreads();
+  T* dst = vt + (((int64_t)b * Hkv + g) * NCf + c) * D * kS;
+  for (int e = threadIdx.x; e < D * kS / EPV; e += 256) {
+    const int drow = e / (kS / EPV), q = e % (kS / EPV);
+    T x[EPV];
 #pragma unroll
-  for (int base = 0; base < kS * D; base += NT * EPV) {
-    const int e = base + threadIdx.x * EPV;
-    const int row = e / D, col = e % D;
-    uint4 uk = make_uint4(0, 0, 0, 0), uv = make_uint4(0, 0, 0, 0);
-    if (row < nvalid) {
-      uk = *reinterpret_cast<const uint4*>(kc + e);
-      uv = *reinterpret_cast<const uint4*>(vc + e);
-    }
-    *reinterpret_cast<uint4*>(ks + row * KP + col) = uk;
-    const T* tv = reinterpret_cast<const T*>(&uv);
-#pragma unroll
-    for (int t = 0; t < EPV; ++t) vt[(col + t) * VP + row] = tv[t];
+    for (int t = 0; t < EPV; ++t) x[t] = tile[(q * EPV + t) * VP + drow];
+    *reinterpret_cast<uint4*>(dst + (int64_t)drow * kS + q * EPV) = *reinterpret_cast<const uint4*>(x);
   }
 }
+
+// Stage one chunk (K rows and V^T rows, already zero past the sequence end for
+// V^T) into the swizzled LDS tiles with NT threads.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void stage_chunk(const T* kc, const T* vtc, T* ks, T* vt, int64_t nvalid) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int PK = D / EPV, PV = kS / EPV;
+  for (int e = threadIdx.x; e < kS * PK; e += NT) {
+    const int row = e / PK, p = e % PK;
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (row < nvalid) u = *reinterpret_cast<const uint4*>(kc + (int64_t)row * D + p * EPV);
+    *reinterpret_cast<uint4*>(ks + swz<PK>(row, p) * EPV) = u;
+  }
+  for (int e = threadIdx.x; e < D * PV; e += NT) {
+    const int row = e / PV, p = e % PV;
+    *reinterpret_cast<uint4*>(vt + swz<PV>(row, p) * EPV) =
+        *reinterpret_cast<const uint4*>(vtc + (int64_t)row * kS + p * EPV);
+  }
+}
+
+// Operand fragment of 8 consecutive elements (logical column col, a multiple of
+// 8) of row `row` of a swizzled tile.
+template <int PPR>
+__device__ __forceinline__ void load_frag_swz(Frag<bf16_t>& f, const bf16_t* tile, int row, int col) {
+  f.v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(tile + swz<PPR>(row, col / 8) * 8));
+}
+template <int PPR>
+__device__ __forceinline__ void load_frag_swz(Frag<float>& f, const float* tile, int row, int col) {
+  const float4 x = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, col / 4) * 4);
+  const float4 y = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, col / 4 + 1) * 4);
+  f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
+  f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
+}
+// Two runs of 4 elements (logical columns t0.., t1.., multiples of 4).
+template <int PPR>
+__device__ __forceinline__ void load_frag2x4_swz(Frag<bf16_t>& f, const bf16_t* tile, int row, int t0, int t1) {
+  const uint2 x = *reinterpret_cast<const uint2*>(tile + swz<PPR>(row, t0 / 8) * 8 + (t0 & 7));
+  const uint2 y = *reinterpret_cast<const uint2*>(tile + swz<PPR>(row, t1 / 8) * 8 + (t1 & 7));
+  f.v = __builtin_bit_cast(bf16x8_t, make_uint4(x.x, x.y, y.x, y.y));
+}
+template <int PPR>
+__device__ __forceinline__ void load_frag2x4_swz(Frag<float>& f, const float* tile, int row, int t0, int t1) {
+  const float4 x = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, t0 / 4) * 4);
+  const float4 y = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, t1 / 4) * 4);
+  f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
+  f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
+}
+
 // S^T tile (64 tokens x 16 rows) for one row-fragment set bq[KS]; acc[mt][i] is the
 // logit of token 16*mt + 4*grp + i for row lane%16.
 template <typename T, int D>
 __device__ __forceinline__ void score_tile(const T* ks, const Frag<T> (&bq)[D / 32], f32x4_t (&acc)[4],
                                            int r16, int grp) {
-  constexpr int KP = D + Pad<T>::K;
+  constexpr int PK = D / (16 / (int)sizeof(T));
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kq = 0; kq < D / 32; ++kq) {
       Frag<T> af;
-      load_frag(af, ks + (16 * mt + r16) * KP + 8 * grp + 32 * kq);
+      load_frag_swz<PK>(af, ks, 16 * mt + r16, 8 * grp + 32 * kq);
       mma(acc[mt], af, bq[kq]);
     }
   }
@@ -218,7 +299,7 @@ __device__ __forceinline__ void score_tile(const T* ks, const Frag<T> (&bq)[D / 
 template <typename T, int D>
 __device__ __forceinline__ void pv_tile(const T* vt, const float (&p)[4][4], f32x4_t (&o)[D / 16],
                                         int r16, int grp) {
-  constexpr int VP = kS + Pad<T>::V;
+  constexpr int PV = kS / (16 / (int)sizeof(T));
   Frag<T> pf[2];
 #pragma unroll
   for (int k2 = 0; k2 < 2; ++k2) {
@@ -234,9 +315,8 @@ __device__ __forceinline__ void pv_tile(const T* vt, const float (&p)[4][4], f32
   for (int md = 0; md < D / 16; ++md) {
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      const T* row = vt + (16 * md + r16) * VP + 32 * k2 + 4 * grp;
       Frag<T> af;
-      load_frag2x4(af, row, row + 16);
+      load_frag2x4_swz<PV>(af, vt, 16 * md + r16, 32 * k2 + 4 * grp, 32 * k2 + 16 + 4 * grp);
       mma(o[md], af, pf[k2]);
     }
   }
@@ -274,15 +354,14 @@ __device__ __forceinline__ void load4_add<float>(f32x4_t& acc, const float* p) {
 struct ChunkArgs {
   const void* q;
   const void* k;
-  const void* v;
-  const float* ssel;
-  const float* lsel;
+  const void* vt;   // V^T per chunk, [B, Hkv, NCf, D, S]
+  const float* wq;  // [B, Hkv, T, topk, G] chunk weights
   const int32_t* bcount;
   const int64_t* bbase;
   const uint32_t* entries;
   void* part;   // [B, Hkv_pass, G, T, topk, D]
   int B, Hq, Hkv, topk, g0, gpass;
-  int64_t T, NCs;
+  int64_t T, NCs, NCf;
   float scale;
 };
 
@@ -295,10 +374,9 @@ template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   constexpr int KS = D / 32, MD = D / 16;
   constexpr int NE = 16 / G;  // entries per 16-row tile
-  constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
   constexpr int OP = D + 16 / (int)sizeof(T);  // padded LDS output row
-  __shared__ __align__(16) T ks[kS * KP];
-  __shared__ __align__(16) T vt[D * VP];
+  __shared__ __align__(16) T ks[kS * D];
+  __shared__ __align__(16) T vt[D * kS];
   __shared__ __align__(16) T ot[4][16 * OP];
   const int64_t c = blockIdx.x;
   const int g = a.g0 + blockIdx.y, b = blockIdx.z;
@@ -307,8 +385,8 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   if (n == 0) return;
   const int64_t base = a.bbase[bucket];
   const T* kc = static_cast<const T*>(a.k) + (((int64_t)b * a.Hkv + g) * a.T + c * kS) * D;
-  const T* vc = static_cast<const T*>(a.v) + (((int64_t)b * a.Hkv + g) * a.T + c * kS) * D;
-  stage_chunk<T, D, 256>(kc, vc, ks, vt, kS);
+  const T* vtc = static_cast<const T*>(a.vt) + (((int64_t)b * a.Hkv + g) * a.NCf + c) * D * kS;
+  stage_chunk<T, D, 256>(kc, vtc, ks, vt, kS);
   __syncthreads();
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -320,10 +398,12 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   const int ntile = (n + NE - 1) / NE;
   const int hh = r16 % G, h = g * G + hh;
 
-  auto load_q = [&](int nt, Frag<T> (&bq)[KS], uint32_t& word) {
+  auto load_q = [&](int nt, Frag<T> (&bq)[KS], uint32_t& word, float& wt) {
     const int e = nt * NE + r16 / G;
     const bool valid = nt < ntile && e < n;
     word = valid ? a.entries[base + e] : 0xffffffffu;
+    wt = valid ? a.wq[((((int64_t)b * a.Hkv + g) * a.T + (word >> 6)) * a.topk + (word & 63)) * G + hh]
+               : 0.f;
     if (valid) {
       const T* qrow = qbase + (((int64_t)b * a.Hq + h) * a.T + (word >> 6)) * D + 8 * grp;
 #pragma unroll
@@ -336,9 +416,10 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
 
   Frag<T> bq[KS], bqn[KS];
   uint32_t word, wordn;
-  load_q(wave, bq, word);
+  float wt, wtn;
+  load_q(wave, bq, word, wt);
   for (int nt = wave; nt < ntile; nt += 4) {
-    load_q(nt + 4, bqn, wordn);  // prefetch the next tile's rows
+    load_q(nt + 4, bqn, wordn, wtn);  // prefetch the next tile's rows
     f32x4_t acc[4];
     score_tile<T, D>(ks, bq, acc, r16, grp);
     float mx = kNegInf;
@@ -362,14 +443,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) o[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     pv_tile<T, D>(vt, p, o, r16, grp);
-    const bool valid = word != 0xffffffffu;
-    const int64_t i = word >> 6;
-    const int slot = word & 63;
-    float w = 0.f;
-    if (valid) {
-      const int64_t rowq = ((int64_t)b * a.Hq + h) * a.T + i;
-      w = __expf(a.ssel[rowq * a.topk + slot] - a.lsel[rowq]) / ls;
-    }
+    const float w = wt / ls;   // exp(s_hat - L_sel) / Z_c (0 for padding rows)
 #pragma unroll
     for (int md = 0; md < MD; ++md) store4<T>(myo + r16 * OP + 16 * md + 4 * grp, o[md], w);
     wave_lds_sync();
@@ -394,33 +468,43 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
 #pragma unroll
     for (int kq = 0; kq < KS; ++kq) bq[kq] = bqn[kq];
     word = wordn;
+    wt = wtn;
   }
 }
 
 struct WinArgs {
   const void* q;
   const void* k;
-  const void* v;
-  void* ow;      // [B, Hq, T, D] normalised window output
-  float* lzw;    // [B, Hq, T] window log-mass
+  const void* vt;  // V^T per chunk, [B, Hkv, NCf, D, S]
+  void* ow;        // [B, Hq, T, D] normalised window output
+  float* lzw;      // [B, Hq, T] window log-mass
   int B, Hq, Hkv, S, W;
-  int64_t T;
+  int64_t T, NCf;
   float scale;
 };
 
-// Window attention, query-major and dense (flash style).  A workgroup has 4 waves;
-// a wave owns 32 rows = two 16-row tiles of (query, head) rows, the block 128 rows.
+template <int N> using u32v = uint32_t __attribute__((ext_vector_type(N)));
+
+constexpr int kWinThreads = 512;
+
+// Window attention, query-major and dense (flash style).  A workgroup has 8 waves;
+// a wave owns one 16-row MFMA tile of (query, head) rows, the block 128 rows, so
+// each staged chunk serves 128 rows.  The next chunk's K and V^T pieces are
+// loaded into registers (held as one vector value) while this chunk computes.
 // Chunks fully inside every row's window skip the mask.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void window_kernel(WinArgs a) {
+__global__ __launch_bounds__(kWinThreads) void window_kernel(WinArgs a) {
   constexpr int KS = D / 32, MD = D / 16;
-  constexpr int QW = 32 / G;        // queries per wave
-  constexpr int QB = 4 * QW;        // queries per block
-  constexpr int KP = D + Pad<T>::K, VP = kS + Pad<T>::V;
-  __shared__ __align__(16) T ks[kS * KP];
-  __shared__ __align__(16) T vt[D * VP];
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int PK = D / EPV, PV = kS / EPV;              // 16-byte pieces per K / V^T row
+  constexpr int NPK = kS * PK / kWinThreads, NPV = D * PV / kWinThreads;
+  constexpr int QW = 16 / G;        // queries per wave
+  constexpr int QB = 8 * QW;        // queries per block
+  __shared__ __align__(16) T ks[kS * D];
+  __shared__ __align__(16) T vt[D * kS];
   const int g = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
   const int64_t T_ = a.T;
   // Consecutive query tiles share most window chunks: give each XCD (blocks are
@@ -431,139 +515,127 @@ __global__ __launch_bounds__(256) void window_kernel(WinArgs a) {
   const int64_t qb0 = bx * QB;
   const int64_t qlast = min(qb0 + QB - 1, T_ - 1);
   const float sl2 = a.scale * kLog2e;
-  const T* qbase = static_cast<const T*>(a.q);
 
-  int64_t ir[2], lw[2];
-  Frag<T> bq[2][KS];
+  const int64_t i = qb0 + wave * QW + r16 / G;   // this lane's row: query i, head h
+  const int h = g * G + r16 % G;
+  const int64_t lw = window_left(i, a.S, a.W);
+  Frag<T> bq[KS];
+  {
+    const T* qrow = static_cast<const T*>(a.q) + (((int64_t)b * a.Hq + h) * T_ + min(i, T_ - 1)) * D + 8 * grp;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int R = 16 * nt + r16;
-    const int64_t i = qb0 + wave * QW + R / G;
-    ir[nt] = i;
-    lw[nt] = window_left(i, a.S, a.W);
-    const int h = g * G + R % G;
-    const int64_t ia = i < T_ ? i : T_ - 1;
-    const T* qrow = qbase + (((int64_t)b * a.Hq + h) * T_ + ia) * D + 8 * grp;
-#pragma unroll
-    for (int kq = 0; kq < KS; ++kq) load_frag(bq[nt][kq], qrow + 32 * kq);
+    for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
   }
-  float m[2], ls[2];
-  f32x4_t o[2][MD];
+  float m = kNegInf, ls = 0.f;
+  f32x4_t o[MD];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    m[nt] = kNegInf;
-    ls[nt] = 0.f;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) o[nt][md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int md = 0; md < MD; ++md) o[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int64_t lw_max = window_left(qlast, a.S, a.W);   // window edges grow with i
   const int64_t c_lo = window_left(qb0, a.S, a.W) / kS;
   const int64_t c_hi = qlast / kS;
   const T* kbase = static_cast<const T*>(a.k) + ((int64_t)b * a.Hkv + g) * T_ * D;
-  const T* vbase = static_cast<const T*>(a.v) + ((int64_t)b * a.Hkv + g) * T_ * D;
-  // The next chunk's K and V are loaded into registers while this one computes.
-  constexpr int EPV = 16 / sizeof(T);
-  constexpr int NPT = kS * D / (256 * EPV);   // 16-byte pieces per thread
-  uint4 pk[NPT], pv[NPT];
+  const T* vtbase = static_cast<const T*>(a.vt) + ((int64_t)b * a.Hkv + g) * a.NCf * D * kS;
+  u32v<4 * NPK> pk;
+  u32v<4 * NPV> pv;
   auto fetch = [&](int64_t c) {
-    const int64_t nvalid = T_ - c * kS;
 #pragma unroll
-    for (int t = 0; t < NPT; ++t) {
-      const int e = (t * 256 + threadIdx.x) * EPV;
-      const bool in = e / D < nvalid;
-      pk[t] = in ? *reinterpret_cast<const uint4*>(kbase + c * kS * D + e) : make_uint4(0, 0, 0, 0);
-      pv[t] = in ? *reinterpret_cast<const uint4*>(vbase + c * kS * D + e) : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < NPK; ++t) {
+      const int e = t * kWinThreads + threadIdx.x;
+      const int row = e / PK, pc = e % PK;
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (c * kS + row < T_) u = *reinterpret_cast<const uint4*>(kbase + (c * kS + row) * D + pc * EPV);
+      pk[4 * t] = u.x; pk[4 * t + 1] = u.y; pk[4 * t + 2] = u.z; pk[4 * t + 3] = u.w;
+    }
+#pragma unroll
+    for (int t = 0; t < NPV; ++t) {
+      const int e = t * kWinThreads + threadIdx.x;
+      const int row = e / PV, pc = e % PV;
+      const uint4 u = *reinterpret_cast<const uint4*>(vtbase + (c * D + row) * kS + pc * EPV);
+      pv[4 * t] = u.x; pv[4 * t + 1] = u.y; pv[4 * t + 2] = u.z; pv[4 * t + 3] = u.w;
     }
   };
   auto commit = [&]() {
 #pragma unroll
-    for (int t = 0; t < NPT; ++t) {
-      const int e = (t * 256 + threadIdx.x) * EPV;
-      const int row = e / D, col = e % D;
-      *reinterpret_cast<uint4*>(ks + row * KP + col) = pk[t];
-      const T* tv = reinterpret_cast<const T*>(&pv[t]);
+    for (int t = 0; t < NPK; ++t) {
+      const int e = t * kWinThreads + threadIdx.x;
+      *reinterpret_cast<uint4*>(ks + swz<PK>(e / PK, e % PK) * EPV) =
+          make_uint4(pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]);
+    }
 #pragma unroll
-      for (int q = 0; q < EPV; ++q) vt[(col + q) * VP + row] = tv[q];
+    for (int t = 0; t < NPV; ++t) {
+      const int e = t * kWinThreads + threadIdx.x;
+      *reinterpret_cast<uint4*>(vt + swz<PV>(e / PV, e % PV) * EPV) =
+          make_uint4(pv[4 * t], pv[4 * t + 1], pv[4 * t + 2], pv[4 * t + 3]);
     }
   };
   fetch(c_lo);
   for (int64_t c = c_lo; c <= c_hi; ++c) {
     __syncthreads();
     commit();
-    if (c < c_hi) fetch(c + 1);
     __syncthreads();
+    if (c < c_hi) fetch(c + 1);
     const int64_t j0 = c * kS;
     // no row masks a token of this chunk: its left edge is at or past every row's
     // window edge, and its last token precedes every row's query
     const bool full = j0 >= lw_max && j0 + kS - 1 <= qb0;
+    f32x4_t acc[4];
+    score_tile<T, D>(ks, bq, acc, r16, grp);
+    float x[4][4], mx = kNegInf;
+    if (full) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4_t acc[4];
-      score_tile<T, D>(ks, bq[nt], acc, r16, grp);
-      float x[4][4], mx = kNegInf;
-      if (full) {
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int q4 = 0; q4 < 4; ++q4) {
+          x[mt][q4] = acc[mt][q4] * sl2;
+          mx = fmaxf(mx, x[mt][q4]);
+        }
+    } else {
+      const int lo = (int)max<int64_t>(lw - j0, -1);
+      const int hi = i < T_ ? (int)min<int64_t>(i - j0, kS) : -1;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            x[mt][q4] = acc[mt][q4] * sl2;
-            mx = fmaxf(mx, x[mt][q4]);
-          }
-      } else {
-        const int lo = (int)max<int64_t>(lw[nt] - j0, -1);
-        const int hi = ir[nt] < T_ ? (int)min<int64_t>(ir[nt] - j0, kS) : -1;
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int t = 16 * mt + 4 * grp + q4;
-            x[mt][q4] = (t >= lo && t <= hi) ? acc[mt][q4] * sl2 : kNegInf;
-            mx = fmaxf(mx, x[mt][q4]);
-          }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mn = fmaxf(m[nt], mx);
-      float p[4][4], psum = 0.f;
-      if (mn == kNegInf) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) p[mt][q4] = 0.f;
-      } else {
-        const float alpha = hw_exp2(m[nt] - mn);   // 0 when m was -inf
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            p[mt][q4] = hw_exp2(x[mt][q4] - mn);
-            psum += p[mt][q4];
-          }
-        ls[nt] = ls[nt] * alpha + psum;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) o[nt][md] *= alpha;
-        m[nt] = mn;
-      }
-      pv_tile<T, D>(vt, p, o[nt], r16, grp);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int t = 16 * mt + 4 * grp + q4;
+          x[mt][q4] = (t >= lo && t <= hi) ? acc[mt][q4] * sl2 : kNegInf;
+          mx = fmaxf(mx, x[mt][q4]);
+        }
     }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mn = fmaxf(m, mx);
+    float p[4][4], psum = 0.f;
+    if (mn == kNegInf) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) p[mt][q4] = 0.f;
+    } else {
+      const float alpha = hw_exp2(m - mn);   // 0 when m was -inf
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          p[mt][q4] = hw_exp2(x[mt][q4] - mn);
+          psum += p[mt][q4];
+        }
+      ls = ls * alpha + psum;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[md] *= alpha;
+      m = mn;
+    }
+    pv_tile<T, D>(vt, p, o, r16, grp);
   }
+  float lsum = ls;
+  lsum += __shfl_xor(lsum, 16, kWave);
+  lsum += __shfl_xor(lsum, 32, kWave);
+  if (i >= T_) return;
+  const int64_t rowq = ((int64_t)b * a.Hq + h) * T_ + i;
+  const float inv = 1.f / lsum;
   T* owp = static_cast<T*>(a.ow);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int R = 16 * nt + r16;
-    const int h = g * G + R % G;
-    const int64_t i = ir[nt];
-    float lsum = ls[nt];
-    lsum += __shfl_xor(lsum, 16, kWave);
-    lsum += __shfl_xor(lsum, 32, kWave);
-    if (i >= T_) continue;
-    const int64_t rowq = ((int64_t)b * a.Hq + h) * T_ + i;
-    const float inv = 1.f / lsum;
-#pragma unroll
-    for (int md = 0; md < MD; ++md) store4<T>(owp + rowq * D + 16 * md + 4 * grp, o[nt][md], inv);
-    if (grp == 0) a.lzw[rowq] = (m[nt] + hw_log2(lsum)) * kLn2;
-  }
+  for (int md = 0; md < MD; ++md) store4<T>(owp + rowq * D + 16 * md + 4 * grp, o[md], inv);
+  if (grp == 0) a.lzw[rowq] = (m + hw_log2(lsum)) * kLn2;
 }
 
 struct CombArgs {
@@ -616,7 +688,23 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
     const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * a.topk;
     const T* prow = static_cast<const T*>(a.part) +
                     ((((int64_t)b * a.gpass + gi) * G + hh) * a.T + i) * a.topk * D + piece * EPV;
-    for (int s = 0; s < a.topk; ++s) {
+    // eight slots' loads in flight at a time; padding slots hold no partial row
+    constexpr int U = 8;
+    int s = 0;
+    for (; s + U <= a.topk; s += U) {
+      uint4 u[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        u[j] = irow[s + j] >= 0 ? *reinterpret_cast<const uint4*>(prow + (int64_t)(s + j) * D)
+                                : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const T* t = reinterpret_cast<const T*>(&u[j]);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
+      }
+    }
+    for (; s < a.topk; ++s) {
       if (irow[s] < 0) continue;
       const uint4 u = *reinterpret_cast<const uint4*>(prow + (int64_t)s * D);
       const T* t = reinterpret_cast<const T*>(&u);
@@ -637,22 +725,28 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
 
 template <typename T, int D, int G>
 hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, void* ow, float* lzw,
-                            int gpp, hipStream_t st) {
+                            void* vt, int gpp, hipStream_t st) {
+  const int64_t NCf = (a.T + kS - 1) / kS;
+  {
+    KTimer tm(K_VT, st);
+    hipLaunchKernelGGL((vt_kernel<T, D>), dim3((unsigned)NCf, a.Hkv, a.B), dim3(256), 0, st,
+                       static_cast<const T*>(a.v), static_cast<T*>(vt), a.Hkv, a.T, NCf);
+  }
   // window part for every head at once
   {
-    WinArgs wa{a.q, a.k, a.v, ow, lzw, a.B, a.Hq, a.Hkv, a.S, a.W, a.T, a.scale};
-    const int QB = 4 * (32 / G);
+    WinArgs wa{a.q, a.k, vt, ow, lzw, a.B, a.Hq, a.Hkv, a.S, a.W, a.T, NCf, a.scale};
+    const int QB = 8 * (16 / G);
     KTimer tm(K_WINDOW, st);
     hipLaunchKernelGGL((window_kernel<T, D, G>), dim3((unsigned)((a.T + QB - 1) / QB), a.Hkv, a.B),
-                       dim3(256), 0, st, wa);
+                       dim3(kWinThreads), 0, st, wa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   for (int g0 = 0; g0 < a.Hkv; g0 += gpp) {
     const int gp = min(gpp, a.Hkv - g0);
     if (ia.NCs > 0 && a.topk > 0) {
-      ChunkArgs ca{a.q, a.k, a.v, a.ssel, ia.lsel, ia.bcount, ia.bbase, ia.entries, part,
-                   a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, a.scale};
+      ChunkArgs ca{a.q, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part,
+                   a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, NCf, a.scale};
       KTimer tm(K_CHUNK_ATTEND, st);
       hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)ia.NCs, gp, a.B), dim3(256),
                          0, st, ca);
@@ -673,12 +767,12 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
 
 template <typename T, int D>
 hipError_t launch_attend_t(const AttArgs& a, const IdxArgs& ia, void* part, void* ow, float* lzw,
-                           int gpp, hipStream_t st) {
+                           void* vt, int gpp, hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, ow, lzw, gpp, st);
-    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, ow, lzw, gpp, st);
-    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, ow, lzw, gpp, st);
-    default: return launch_attend_tg<T, D, 8>(a, ia, part, ow, lzw, gpp, st);
+    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, ow, lzw, vt, gpp, st);
+    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, ow, lzw, vt, gpp, st);
+    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, ow, lzw, vt, gpp, st);
+    default: return launch_attend_tg<T, D, 8>(a, ia, part, ow, lzw, vt, gpp, st);
   }
 }
 
@@ -696,9 +790,11 @@ void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
   f += align256((size_t)B * Hkv * NCs * sizeof(int32_t));           // bcount
   f += align256((size_t)B * Hkv * NCs * sizeof(int64_t));           // bbase
   f += align256((size_t)B * Hkv * T * topk * sizeof(uint32_t));     // entries
+  f += align256((size_t)B * Hq * T * topk * sizeof(float));         // chunk weights
   f += align256((size_t)B * Hq * T * sizeof(float));                // lsel
   f += align256((size_t)B * Hq * T * D * esz);                      // window outputs
   f += align256((size_t)B * Hq * T * sizeof(float));                // window log-mass
+  f += align256((size_t)B * Hkv * ((T + kS - 1) / kS) * kS * D * esz);  // V^T per chunk
   *fixed = f + 256;
   *per_kv_head = align256((size_t)B * (Hq / Hkv) * T * topk * D * esz);
 }
@@ -721,12 +817,16 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   w += align256((size_t)a.B * a.Hkv * NCs * sizeof(int64_t));
   ia.entries = reinterpret_cast<uint32_t*>(w);
   w += align256((size_t)a.B * a.Hkv * a.T * a.topk * sizeof(uint32_t));
+  ia.wq = reinterpret_cast<float*>(w);
+  w += align256((size_t)a.B * a.Hq * a.T * a.topk * sizeof(float));
   ia.lsel = reinterpret_cast<float*>(w);
   w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
   void* ow = w;
   w += align256((size_t)a.B * a.Hq * a.T * a.D * esz);
   float* lzw = reinterpret_cast<float*>(w);
   w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
+  void* vt = w;
+  w += align256((size_t)a.B * a.Hkv * ((a.T + kS - 1) / kS) * kS * a.D * esz);
   ia.B = a.B; ia.Hq = a.Hq; ia.Hkv = a.Hkv; ia.topk = a.topk;
   ia.T = a.T; ia.NCs = NCs; ia.ntiles = ntiles;
   void* part = w;
@@ -735,6 +835,21 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   if (gpp > a.Hkv) gpp = a.Hkv;
   if (gpp < 1) gpp = 1;  // the host checked the minimum size
 
+  if (a.topk > 0) {
+    int L = 1;
+    while (L < a.topk) L <<= 1;
+    const int64_t nl = (int64_t)a.B * a.Hkv * a.T * L;
+    const dim3 grid((unsigned)((nl + 255) / 256));
+    KTimer tm(K_LSEL, st);
+    switch (a.Hq / a.Hkv) {
+      case 1: hipLaunchKernelGGL(lsel_kernel<1>, grid, dim3(256), 0, st, ia, L); break;
+      case 2: hipLaunchKernelGGL(lsel_kernel<2>, grid, dim3(256), 0, st, ia, L); break;
+      case 4: hipLaunchKernelGGL(lsel_kernel<4>, grid, dim3(256), 0, st, ia, L); break;
+      default: hipLaunchKernelGGL(lsel_kernel<8>, grid, dim3(256), 0, st, ia, L); break;
+    }
+  } else {
+    ia.lsel = nullptr;  // no selection: the window is the whole normaliser
+  }
   if (a.topk > 0 && NCs > 0) {
     const size_t lds = (size_t)NCs * sizeof(uint64_t);
     {
@@ -753,19 +868,10 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
     KTimer tm(K_IDX_FILL, st);
     hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
   }
-  if (a.topk > 0) {
-    int L = 1;
-    while (L < a.topk) L <<= 1;
-    const int64_t nl = (int64_t)a.B * a.Hq * a.T * L;
-    KTimer tm(K_LSEL, st);
-    hipLaunchKernelGGL(lsel_kernel, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0, st, ia, L);
-  } else {
-    ia.lsel = nullptr;  // no selection: the window is the whole normaliser
-  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, ow, lzw, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, ow, lzw, gpp, st);
-  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, ow, lzw, gpp, st) : launch_attend_t<float, 64>(a, ia, part, ow, lzw, gpp, st);
+  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, ow, lzw, vt, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, ow, lzw, vt, gpp, st);
+  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, ow, lzw, vt, gpp, st) : launch_attend_t<float, 64>(a, ia, part, ow, lzw, vt, gpp, st);
 }
 
 }  // namespace hils
