@@ -378,8 +378,11 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   __shared__ __align__(16) T ks[kS * D];
   __shared__ __align__(16) T vt[D * kS];
   __shared__ __align__(16) T ot[4][16 * OP];
-  const int64_t c = blockIdx.x;
-  const int g = a.g0 + blockIdx.y, b = blockIdx.z;
+  // chunk-major over the pass's groups: the early chunks, candidates of almost
+  // every query and so the longest lists, start first for every group
+  const int gcount = min(a.gpass, a.Hkv - a.g0);   // groups in this pass
+  const int64_t c = blockIdx.x / gcount;
+  const int g = a.g0 + (int)(blockIdx.x % gcount), b = blockIdx.z;
   const int64_t bucket = ((int64_t)b * a.Hkv + g) * a.NCs + c;
   const int n = a.bcount[bucket];
   if (n == 0) return;
@@ -398,10 +401,15 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   const int ntile = (n + NE - 1) / NE;
   const int hh = r16 % G, h = g * G + hh;
 
-  auto load_q = [&](int nt, Frag<T> (&bq)[KS], uint32_t& word, float& wt) {
+  // three-stage pipeline: the entry word of tile t+8 (two of this wave's tiles
+  // ahead), the q rows and weight of tile t+4 (using the word loaded an
+  // iteration earlier), the computation of tile t
+  auto load_word = [&](int nt) -> uint32_t {
     const int e = nt * NE + r16 / G;
-    const bool valid = nt < ntile && e < n;
-    word = valid ? a.entries[base + e] : 0xffffffffu;
+    return (nt < ntile && e < n) ? a.entries[base + e] : 0xffffffffu;
+  };
+  auto load_q = [&](uint32_t word, Frag<T> (&bq)[KS], float& wt) {
+    const bool valid = word != 0xffffffffu;
     wt = valid ? a.wq[((((int64_t)b * a.Hkv + g) * a.T + (word >> 6)) * a.topk + (word & 63)) * G + hh]
                : 0.f;
     if (valid) {
@@ -415,11 +423,12 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   };
 
   Frag<T> bq[KS], bqn[KS];
-  uint32_t word, wordn;
+  uint32_t word = load_word(wave), wordn = load_word(wave + 4);
   float wt, wtn;
-  load_q(wave, bq, word, wt);
+  load_q(word, bq, wt);
   for (int nt = wave; nt < ntile; nt += 4) {
-    load_q(nt + 4, bqn, wordn, wtn);  // prefetch the next tile's rows
+    load_q(wordn, bqn, wtn);               // the next tile's rows
+    const uint32_t wordnn = load_word(nt + 8);
     f32x4_t acc[4];
     score_tile<T, D>(ks, bq, acc, r16, grp);
     float mx = kNegInf;
@@ -468,6 +477,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
 #pragma unroll
     for (int kq = 0; kq < KS; ++kq) bq[kq] = bqn[kq];
     word = wordn;
+    wordn = wordnn;
     wt = wtn;
   }
 }
@@ -748,8 +758,8 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
       ChunkArgs ca{a.q, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part,
                    a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, NCf, a.scale};
       KTimer tm(K_CHUNK_ATTEND, st);
-      hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)ia.NCs, gp, a.B), dim3(256),
-                         0, st, ca);
+      hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)(ia.NCs * gp), 1, a.B),
+                         dim3(256), 0, st, ca);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

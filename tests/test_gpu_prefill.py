@@ -273,3 +273,29 @@ def test_batch_independence(hils):
     b = _gpu_prefill(hils, y, wl)
     for key in ("k_sum", "b_sum", "idx", "ssel", "out", "lse"):
         assert torch.equal(a[key][0], b[key][0]), key
+
+
+def test_attend_in_group_passes(hils):
+    """A workspace too small for every KV head's partial outputs makes hils_attend_fuse
+    run the selected part a few groups at a time (here 1 and 3 of 4 groups per
+    pass); the outputs must equal the single-pass run bit for bit."""
+    wl = wk.custom(name="passes", dtype="bf16", B=2, Hq=8, Hkv=4, d=128, T=700, S=64, k=4, W=128)
+    say("attend passes")
+    x, xd = _inputs(wl, seed=6)
+    shape = _shape(hils, wl)
+    full = _gpu_prefill(hils, xd, wl)
+    full_bytes = hils.hils_workspace_bytes(shape, hils.OP_ATTEND_FUSE)
+    per = -(-(wl.B * wl.G * wl.T * wl.k * wl.d * 2) // 256) * 256   # one KV head's partials
+    fixed = full_bytes - wl.Hkv * per
+    for heads in (1, 3):
+        ws = torch.empty(fixed + heads * per, dtype=torch.uint8, device=DEV)
+        out = torch.empty_like(xd["q"])
+        lse = torch.empty((wl.B, wl.Hq, wl.T), dtype=torch.float32, device=DEV)
+        hils.hils_attend_fuse(xd["q"], xd["k"], xd["v"], full["idx"], full["ssel"], out, lse, shape, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, full["out"]), heads
+        assert torch.equal(lse, full["lse"]), heads
+    small = torch.empty(fixed + per - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(hils.HilsError):
+        hils.hils_attend_fuse(xd["q"], xd["k"], xd["v"], full["idx"], full["ssel"],
+                              torch.empty_like(xd["q"]), None, shape, small)
