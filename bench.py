@@ -348,8 +348,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    prefill_kernels = ["summarize", "score_lse", "rank_select", "idx_count", "idx_scan_tiles",
-                       "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend", "combine"]
+    prefill_kernels = ["summarize", "score_lse", "rank_select", "lsel", "idx_count", "idx_scan_tiles",
+                       "idx_scan_buckets", "idx_fill", "v_transpose", "q_group", "window",
+                       "chunk_attend", "combine"]
     log("warmup")
     for _ in range(args.warmup):
         step(False)

@@ -230,6 +230,26 @@ __global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, T* __r
   }
 }
 
+// q regrouped so that a KV group's G head rows of one query are contiguous,
+// [B, Hkv, T, G, D]: the chunk-major pass gathers one G*D record per entry.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void qgroup_kernel(const T* __restrict__ q, T* __restrict__ qg, int Hq,
+                                                     int64_t T_) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int PPR = D / EPV;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-byte piece of qg
+  const int64_t total = (int64_t)gridDim.y * Hq * T_ * PPR;
+  if (e >= total / gridDim.y) return;
+  const int b = blockIdx.y;
+  const int pc = (int)(e % PPR);
+  const int hh = (int)((e / PPR) % G);
+  const int64_t i = (e / (PPR * G)) % T_;
+  const int g = (int)(e / (PPR * G * T_));
+  const int64_t src = (((int64_t)b * Hq + g * G + hh) * T_ + i) * D + pc * EPV;
+  const int64_t dst = (int64_t)b * Hq * T_ * D + e * EPV;
+  *reinterpret_cast<uint4*>(qg + dst) = *reinterpret_cast<const uint4*>(q + src);
+}
+
 // Stage one chunk (K rows and V^T rows, already zero past the sequence end for
 // V^T) into the swizzled LDS tiles with NT threads.
 template <typename T, int D, int NT>
@@ -352,14 +372,14 @@ __device__ __forceinline__ void load4_add<float>(f32x4_t& acc, const float* p) {
 
 
 struct ChunkArgs {
-  const void* q;
+  const void* qg;   // q regrouped, [B, Hkv, T, G, D]
   const void* k;
   const void* vt;   // V^T per chunk, [B, Hkv, NCf, D, S]
   const float* wq;  // [B, Hkv, T, topk, G] chunk weights
   const int32_t* bcount;
   const int64_t* bbase;
   const uint32_t* entries;
-  void* part;   // [B, Hkv_pass, G, T, topk, D]
+  void* part;   // [B, Hkv_pass, T, topk, G, D]
   int B, Hq, Hkv, topk, g0, gpass;
   int64_t T, NCs, NCf;
   float scale;
@@ -395,7 +415,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
   const float sl2 = a.scale * kLog2e;
-  const T* qbase = static_cast<const T*>(a.q);
+  const T* qbase = static_cast<const T*>(a.qg);
   T* part = static_cast<T*>(a.part);
   T* myo = ot[wave];
   const int ntile = (n + NE - 1) / NE;
@@ -413,7 +433,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
     wt = valid ? a.wq[((((int64_t)b * a.Hkv + g) * a.T + (word >> 6)) * a.topk + (word & 63)) * G + hh]
                : 0.f;
     if (valid) {
-      const T* qrow = qbase + (((int64_t)b * a.Hq + h) * a.T + (word >> 6)) * D + 8 * grp;
+      const T* qrow = qbase + ((((int64_t)b * a.Hkv + g) * a.T + (word >> 6)) * G + hh) * D + 8 * grp;
 #pragma unroll
       for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
     } else {
@@ -468,7 +488,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
         const int rh = r % G;
         const int64_t ri = wr >> 6;
         const int rs = wr & 63;
-        T* prow = part + (((((int64_t)b * a.gpass + (g - a.g0)) * G + rh) * a.T + ri) * a.topk + rs) * D;
+        T* prow = part + (((((int64_t)b * a.gpass + (g - a.g0)) * a.T + ri) * a.topk + rs) * G + rh) * D;
         *reinterpret_cast<uint4*>(prow + piece * EPV) =
             *reinterpret_cast<const uint4*>(myo + r * OP + piece * EPV);
       }
@@ -667,14 +687,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
   constexpr int EPV = 16 / sizeof(T);
   constexpr int PPR = D / EPV;
   const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t rowl = gl / PPR;          // row within this pass: (b, g - g0, hh, i)
+  const int64_t rowl = gl / PPR;          // row within this pass: (b, g - g0, i, hh)
   const int piece = (int)(gl % PPR);
   const int64_t nrows = (int64_t)a.B * a.gpass * G * a.T;
   if (rowl >= nrows) return;
-  const int64_t i = rowl % a.T;
-  const int hh = (int)((rowl / a.T) % G);
-  const int gi = (int)((rowl / (a.T * G)) % a.gpass);
-  const int b = (int)(rowl / (a.T * G * a.gpass));
+  const int hh = (int)(rowl % G);
+  const int64_t i = (rowl / G) % a.T;
+  const int gi = (int)((rowl / (G * a.T)) % a.gpass);
+  const int b = (int)(rowl / (G * a.T * a.gpass));
   const int g = a.g0 + gi;
   if (g >= a.Hkv) return;
   const int h = g * G + hh;
@@ -697,7 +717,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
   if (wsel > 0.f) {
     const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * a.topk;
     const T* prow = static_cast<const T*>(a.part) +
-                    ((((int64_t)b * a.gpass + gi) * G + hh) * a.T + i) * a.topk * D + piece * EPV;
+                    ((((int64_t)b * a.gpass + gi) * a.T + i) * a.topk * G + hh) * D + piece * EPV;
     // eight slots' loads in flight at a time; padding slots hold no partial row
     constexpr int U = 8;
     int s = 0;
@@ -705,7 +725,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
       uint4 u[U];
 #pragma unroll
       for (int j = 0; j < U; ++j)
-        u[j] = irow[s + j] >= 0 ? *reinterpret_cast<const uint4*>(prow + (int64_t)(s + j) * D)
+        u[j] = irow[s + j] >= 0 ? *reinterpret_cast<const uint4*>(prow + (int64_t)(s + j) * G * D)
                                 : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int j = 0; j < U; ++j) {
@@ -716,7 +736,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
     }
     for (; s < a.topk; ++s) {
       if (irow[s] < 0) continue;
-      const uint4 u = *reinterpret_cast<const uint4*>(prow + (int64_t)s * D);
+      const uint4 u = *reinterpret_cast<const uint4*>(prow + (int64_t)s * G * D);
       const T* t = reinterpret_cast<const T*>(&u);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
@@ -735,12 +755,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
 
 template <typename T, int D, int G>
 hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, void* ow, float* lzw,
-                            void* vt, int gpp, hipStream_t st) {
+                            void* vt, void* qg, int gpp, hipStream_t st) {
   const int64_t NCf = (a.T + kS - 1) / kS;
   {
     KTimer tm(K_VT, st);
     hipLaunchKernelGGL((vt_kernel<T, D>), dim3((unsigned)NCf, a.Hkv, a.B), dim3(256), 0, st,
                        static_cast<const T*>(a.v), static_cast<T*>(vt), a.Hkv, a.T, NCf);
+  }
+  if (ia.NCs > 0 && a.topk > 0) {
+    constexpr int PPR = D / (16 / (int)sizeof(T));
+    const int64_t n = (int64_t)a.Hq * a.T * PPR;
+    KTimer tm(K_QGROUP, st);
+    hipLaunchKernelGGL((qgroup_kernel<T, D, G>), dim3((unsigned)((n + 255) / 256), a.B), dim3(256), 0, st,
+                       static_cast<const T*>(a.q), static_cast<T*>(qg), a.Hq, a.T);
   }
   // window part for every head at once
   {
@@ -755,7 +782,7 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
   for (int g0 = 0; g0 < a.Hkv; g0 += gpp) {
     const int gp = min(gpp, a.Hkv - g0);
     if (ia.NCs > 0 && a.topk > 0) {
-      ChunkArgs ca{a.q, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part,
+      ChunkArgs ca{qg, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part,
                    a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, NCf, a.scale};
       KTimer tm(K_CHUNK_ATTEND, st);
       hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)(ia.NCs * gp), 1, a.B),
@@ -777,12 +804,12 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
 
 template <typename T, int D>
 hipError_t launch_attend_t(const AttArgs& a, const IdxArgs& ia, void* part, void* ow, float* lzw,
-                           void* vt, int gpp, hipStream_t st) {
+                           void* vt, void* qg, int gpp, hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, ow, lzw, vt, gpp, st);
-    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, ow, lzw, vt, gpp, st);
-    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, ow, lzw, vt, gpp, st);
-    default: return launch_attend_tg<T, D, 8>(a, ia, part, ow, lzw, vt, gpp, st);
+    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, ow, lzw, vt, qg, gpp, st);
+    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, ow, lzw, vt, qg, gpp, st);
+    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, ow, lzw, vt, qg, gpp, st);
+    default: return launch_attend_tg<T, D, 8>(a, ia, part, ow, lzw, vt, qg, gpp, st);
   }
 }
 
@@ -805,6 +832,7 @@ void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
   f += align256((size_t)B * Hq * T * D * esz);                      // window outputs
   f += align256((size_t)B * Hq * T * sizeof(float));                // window log-mass
   f += align256((size_t)B * Hkv * ((T + kS - 1) / kS) * kS * D * esz);  // V^T per chunk
+  f += align256((size_t)B * Hq * T * D * esz);                      // q regrouped
   *fixed = f + 256;
   *per_kv_head = align256((size_t)B * (Hq / Hkv) * T * topk * D * esz);
 }
@@ -837,6 +865,8 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
   void* vt = w;
   w += align256((size_t)a.B * a.Hkv * ((a.T + kS - 1) / kS) * kS * a.D * esz);
+  void* qg = w;
+  w += align256((size_t)a.B * a.Hq * a.T * a.D * esz);
   ia.B = a.B; ia.Hq = a.Hq; ia.Hkv = a.Hkv; ia.topk = a.topk;
   ia.T = a.T; ia.NCs = NCs; ia.ntiles = ntiles;
   void* part = w;
@@ -880,8 +910,8 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, ow, lzw, vt, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, ow, lzw, vt, gpp, st);
-  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, ow, lzw, vt, gpp, st) : launch_attend_t<float, 64>(a, ia, part, ow, lzw, vt, gpp, st);
+  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, ow, lzw, vt, qg, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, ow, lzw, vt, qg, gpp, st);
+  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, ow, lzw, vt, qg, gpp, st) : launch_attend_t<float, 64>(a, ia, part, ow, lzw, vt, qg, gpp, st);
 }
 
 }  // namespace hils

@@ -212,7 +212,7 @@ int hils_abi_version(void);
  *   score_lse, rank_select, idx_count, idx_scan_tiles, idx_scan_buckets,
  *   idx_fill, lsel, window, chunk_attend, combine, dec_score, dec_span,
  *   dec_merge, dec_attend, dec_fuse, dec_summarize (the summaries of chunks
- *   completed by a decode step), v_transpose.  HILS_E_UNSUPPORTED for an unknown name
+ *   completed by a decode step), v_transpose, q_group.  HILS_E_UNSUPPORTED for an unknown name
  *   (timing is then left off).
  * hils_timing_get(kernel, total_ms, launches): waits for the recorded events
  *   of that kernel and returns the summed duration and the number of timed
