@@ -5,10 +5,11 @@
 // query has little work per byte, so every kernel here streams memory:
 //   dec_score   appends k_new/v_new to the caches and
 //               scores every candidate chunk of every head of the group:
-//               s_hat = scale * q_hat . k' + b'.  A lane owns one k' row (16-byte
-//               loads, all issued before use), q_hat sits in LDS.  Writes s_hat
-//               and per-slice (max, sum exp) partials of each head's LSE.
-//               Reading all of k' once dominates the step's bytes.
+//               s_hat = scale * q_hat . k' + b', streaming k' with contiguous
+//               whole-wave loads (one k' row per 16-byte lane group) and a
+//               butterfly reduction.  Writes s_hat and per-slice (max, sum exp)
+//               partials of each head's LSE.  Reading all of k' once dominates
+//               the step's bytes.
 //   dec_span    one wave per span of 64*J candidates of a (b, group): L_h from the
 //               partials, the rank key, the span's top-k list.
 //   dec_merge   one wave per (b, group): the span lists' top-k, ascending, and each
@@ -73,14 +74,43 @@ __device__ __forceinline__ void lse_merge(float& M, float& Z, float mo, float so
   M = mn;
 }
 
+// One butterfly step per mask M = PPR/2 .. 1 over N values: lanes with bit M set
+// keep the upper half (and send the lower), the others the lower half.
+template <int M, int N>
+__device__ __forceinline__ void butterfly(float (&v)[N], int lane) {
+  if constexpr (M >= 1) {
+    const bool up = (lane & M) != 0;
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+      const float send = up ? v[k] : v[k + N / 2];
+      const float keep = up ? v[k + N / 2] : v[k];
+      v[k] = keep + xor_lane<M>(send);
+    }
+    if constexpr (M > 1) {
+      float w[N / 2];
+#pragma unroll
+      for (int k = 0; k < N / 2; ++k) w[k] = v[k];
+      butterfly<M / 2, N / 2>(w, lane);
+      v[0] = w[0];
+    }
+  }
+}
+
+// Scoring streams k' with whole-wave contiguous loads: PPR lanes cover one k'
+// row (16 bytes each), so one load instruction reads RPI consecutive rows.  Each
+// lane multiplies its 16-byte piece by the matching piece of q_hat; a butterfly
+// over the PPR lanes of a row (PPR - 1 shuffles for PPR row sets) leaves lane t of
+// each row group with the complete dot product of row RPI*t + group.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void dec_score_kernel(DecKArgs a) {
   constexpr int EPV = 16 / sizeof(T);
-  constexpr int NV = D / EPV;  // 16-byte loads per k' row
-  __shared__ float qs[G][D];
+  constexpr int PPR = D / EPV;        // lanes per k' row
+  constexpr int RPI = kWave / PPR;    // rows per load instruction
+  constexpr int NI = PPR;             // load instructions per 64 rows (= kWave / RPI)
   __shared__ float red[G][4][2];
   const int slice = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
   const int64_t i = a.pos.p[b];
   const int64_t nc = num_candidates(i, a.S, a.W);
   const int64_t bg = (int64_t)b * a.Hkv + g;
@@ -100,35 +130,54 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecKArgs a) {
       a.w.lpart[((int64_t)b * a.Hq + g * G + hh) * a.w.nslice + slice] = make_float2(kNegInf, 0.f);
     return;
   }
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x)
-    qs[e / D][e % D] = to_f<T>(static_cast<const T*>(a.qh)[((int64_t)b * a.Hq + g * G) * D + e]);
-  __syncthreads();
-  const int64_t c = c0 + wave * kWave + lane;
+  const int pc = lane % PPR, rg = lane / PPR;
+  const int64_t cw = c0 + wave * kWave;               // this wave's first candidate
+  const int r = RPI * pc + rg;                        // row whose dot product this lane ends with
+  const int64_t c = cw + r;
   const bool ok = c < nc;
-  const int64_t cl = ok ? c : nc - 1;
-#pragma unroll
+#pragma unroll 1
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
-    const T* krow = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * a.NCcap + cl) * D;
-    uint4 u[NV];
+    float qv[EPV];
+    {
+      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) + ((int64_t)b * a.Hq + h) * D + pc * EPV);
+      const T* t = reinterpret_cast<const T*>(&u);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) u[v] = *reinterpret_cast<const uint4*>(krow + v * EPV);
-    const float bv = a.bsum[((int64_t)b * a.Hq + h) * a.NCcap + cl];
-    float acc = 0.f;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const T* t = reinterpret_cast<const T*>(&u[v]);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) acc = fmaf(qs[hh][v * EPV + e], to_f<T>(t[e]), acc);
+      for (int e = 0; e < EPV; ++e) qv[e] = to_f<T>(t[e]);
     }
-    const float s = fmaf(acc, a.scale, bv);
+    const T* kb = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * a.NCcap + cw) * D + pc * EPV;
+    const float bv = ok ? a.bsum[((int64_t)b * a.Hq + h) * a.NCcap + c] : 0.f;
+    float v[NI];
+    // two batches of loads keep the live registers within four waves per SIMD
+    constexpr int NB = NI >= 8 ? NI / 2 : NI;
+#pragma unroll
+    for (int t0 = 0; t0 < NI; t0 += NB) {
+      uint4 u[NB];
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const int row = RPI * (t0 + t) + rg;
+        u[t] = cw + row < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)row * D) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const T* x = reinterpret_cast<const T*>(&u[t]);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc = fmaf(qv[e], to_f<T>(x[e]), acc);
+        v[t0 + t] = acc;
+      }
+    }
+    // butterfly over the PPR lanes of a row: after the step with mask m, lanes
+    // with bit m set hold the upper half of the remaining row sets
+    butterfly<PPR / 2, NI>(v, lane);
+    const float s = fmaf(v[0], a.scale, bv);
     if (ok) a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + c] = s;
-    const float x = ok ? s * kLog2e : kNegInf;
-    const float m = wave_max(x);
-    const float z = wave_sum(x == kNegInf ? 0.f : hw_exp2(x - m));
+    const float xl = ok ? s * kLog2e : kNegInf;
+    const float mw = wave_max(xl);
+    const float zw = wave_sum(xl == kNegInf ? 0.f : hw_exp2(xl - mw));
     if (lane == 0) {
-      red[hh][wave][0] = m;
-      red[hh][wave][1] = z;
+      red[hh][wave][0] = mw;
+      red[hh][wave][1] = zw;
     }
   }
   __syncthreads();

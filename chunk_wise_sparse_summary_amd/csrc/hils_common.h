@@ -124,15 +124,42 @@ __device__ __forceinline__ float dot_row(const T* a, const T* b) {
 }
 
 // Wave-wide reductions (64 lanes).
+// x from lane (lane ^ M).  Masks below 16 stay inside a 16-lane row and use DPP
+// moves (quad permutes for 1 and 2, a row rotation by 8 for 8, and the two row
+// shifts by 4 selected by lane bit 2 for 4); wider masks use a permute.
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+  const int v = __float_as_int(x);
+  if constexpr (M == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0xF, false);   // row_shl 4: from lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(v, v, 0x114, 0xF, 0xF, false);   // row_shr 4: from lane - 4
+    return __int_as_float((threadIdx.x & 4) ? dn : up);
+  } else if constexpr (M == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false));  // row_ror 8
+  } else {
+    return __shfl_xor(x, M, kWave);
+  }
+}
+
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+  x = fmaxf(x, xor_lane<32>(x));
+  x = fmaxf(x, xor_lane<16>(x));
+  x = fmaxf(x, xor_lane<8>(x));
+  x = fmaxf(x, xor_lane<4>(x));
+  x = fmaxf(x, xor_lane<2>(x));
+  return fmaxf(x, xor_lane<1>(x));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+  x += xor_lane<32>(x);
+  x += xor_lane<16>(x);
+  x += xor_lane<8>(x);
+  x += xor_lane<4>(x);
+  x += xor_lane<2>(x);
+  return x + xor_lane<1>(x);
 }
 __device__ __forceinline__ int wave_sum_i(int x) {
 #pragma unroll
