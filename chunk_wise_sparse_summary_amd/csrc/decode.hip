@@ -10,10 +10,9 @@
 //               butterfly reduction.  Writes s_hat and per-slice (max, sum exp)
 //               partials of each head's LSE.  Reading all of k' once dominates
 //               the step's bytes.
-//   dec_span    one wave per span of 64*J candidates of a (b, group): L_h from the
-//               partials, the rank key, the span's top-k list.
-//   dec_merge   one wave per (b, group): the span lists' top-k, ascending, and each
-//               head's s_hat on it.
+//   dec_select  one workgroup per (b, group): L_h from the partials, the rank
+//               key, per-wave top-k lists in LDS, their merged top-k ascending,
+//               and each head's s_hat on it.
 //   dec_attend  one workgroup per (b, group, work item), an item being a selected
 //               chunk or a window chunk.  The chunk's K and V are staged once in
 //               LDS for all G heads; wave h computes head h's 64 logits, softmax
@@ -32,7 +31,6 @@ namespace {
 
 constexpr int kS = 64;
 constexpr int kSlice = 256;   // candidates per scoring workgroup (4 waves x 64 lanes)
-constexpr int kMergeJ = 32;   // the merge wave holds up to 64*32 span-list entries
 
 struct DecPos {
   int64_t p[64];
@@ -41,11 +39,10 @@ struct DecPos {
 struct DecWs {
   float* shat;        // [B, Hq, NCcap]
   float2* lpart;      // [B, Hq, nslice] (max, sum) in log2 units
-  uint64_t* cand;     // [B, Hkv, nspan, topk]
   int32_t* idx;       // [B, Hkv, topk]
   float* ssel;        // [B, Hq, topk]
   float* apart;       // [B, Hkv, nitems, G, D + 2]
-  int nslice, nspan, span, nitems;
+  int nslice, selj, nitems;
 };
 
 struct DecKArgs {
@@ -189,111 +186,126 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecKArgs a) {
   }
 }
 
-// One wave per candidate span of a (b, g): the span's top-k list (key 0 = empty).
+// One workgroup of kSelWaves waves per (b, g).  L_h from the slice partials;
+// wave w ranks the candidates [w*64J, (w+1)*64J) (rank key r = max_h(s_hat_h -
+// L_h), or s_hat for one head) and keeps its exact top-k in LDS, in ascending
+// chunk order; wave 0 then takes the top-k of the concatenated lists (whose
+// positions ascend with the chunk index, so ties still go to the lower chunk),
+// writes the ids ascending and each head's s_hat on them.  With |C_i| <= k every
+// candidate is selected.
+constexpr int kSelWaves = 16;
+
 template <int G, int J>
-__global__ __launch_bounds__(64) void dec_span_kernel(DecKArgs a) {
-  __shared__ uint64_t sbuf[64];
-  __shared__ float Ls[8];
-  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kSelWaves) void dec_select_kernel(DecKArgs a) {
+  constexpr int JM = kSelWaves;     // merge keys per lane: kSelWaves lists of <= 64 entries
+  __shared__ float Ls[G];
+  __shared__ uint32_t lkey[kSelWaves][64];
+  __shared__ int32_t lid[kSelWaves][64];
+  __shared__ int32_t wsel[kSelWaves][64];
+  __shared__ uint32_t sbuf[kSelWaves][64];
+  __shared__ int nlist[kSelWaves];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
   const int64_t i = a.pos.p[b];
   const int64_t nc = num_candidates(i, a.S, a.W);
   const int topk = a.topk;
   const int64_t bg = (int64_t)b * a.Hkv + g;
-  const int64_t cbase = (int64_t)sp * (64 * J);
-  if (nc <= topk || cbase >= nc) return;  // nothing to rank in this span
+  auto shat = [&](int hh, int64_t c) { return a.w.shat[((int64_t)b * a.Hq + g * G + hh) * a.NCcap + c]; };
+  auto rank_key = [&](int64_t c) {
+    float r = kNegInf;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) r = G > 1 ? fmaxf(r, shat(hh, c) - Ls[hh]) : shat(hh, c);
+    return order_key(r);
+  };
+  auto emit = [&](int t, int32_t c) {   // output slot t (< topk) holds chunk c (-1: none)
+    a.w.idx[bg * topk + t] = c;
+    if (a.idx_out) a.idx_out[bg * topk + t] = c;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+      a.w.ssel[((int64_t)b * a.Hq + g * G + hh) * topk + t] = c >= 0 ? shat(hh, c) : kNegInf;
+  };
+  if (nc <= topk) {
+    if (wave == 0 && lane < topk) emit(lane, lane < nc ? lane : -1);
+    return;
+  }
   if (G > 1) {
-    if (lane < G) {
-      const float2* lp = a.w.lpart + ((int64_t)b * a.Hq + g * G + lane) * a.w.nslice;
+    if (wave < G) {   // wave hh: L_h from the slice partials, lanes over slices
+      const float2* lp = a.w.lpart + ((int64_t)b * a.Hq + g * G + wave) * a.w.nslice;
       float M = kNegInf, Z = 0.f;
       const int ns = (int)((nc + kSlice - 1) / kSlice);
-      for (int s = 0; s < ns; ++s) lse_merge(M, Z, lp[s].x, lp[s].y);
-      Ls[lane] = (M + hw_log2(Z)) * kLn2;
+      for (int sl = lane; sl < ns; sl += kWave) lse_merge(M, Z, lp[sl].x, lp[sl].y);
+      const float Mw = wave_max(M);
+      const float Zw = wave_sum(M == kNegInf ? 0.f : Z * hw_exp2(M - Mw));
+      if (lane == 0) Ls[wave] = (Mw + hw_log2(Zw)) * kLn2;
     }
-    wave_lds_sync();
+    __syncthreads();
   }
-  uint64_t keys[J];
-  int nvalid = 0;
+  // ---- per-wave exact top-k over its candidate range
+  const int64_t cw = (int64_t)wave * 64 * J;
+  const int cnt = (int)max<int64_t>(0, min<int64_t>(nc - cw, 64 * J));
+  int n = 0;
+  if (cnt > topk) {
+    const int jn = (cnt + 63) / 64;
+    uint32_t keys[J];
+    constexpr int JB = (J * G <= 32) ? J : (32 / G > 0 ? 32 / G : 1);   // keys per batch of loads
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int64_t c = cbase + lane + 64 * j;
-    float r = kNegInf;
-    if (c < nc) {
+    for (int j0 = 0; j0 < J; j0 += JB) {
+      // the batch's score loads first (clamped in range), then its keys
+      float sv[G][JB];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float s = a.w.shat[((int64_t)b * a.Hq + g * G + hh) * a.NCcap + c];
-        r = G > 1 ? fmaxf(r, s - Ls[hh]) : s;
+      for (int j = 0; j < JB; ++j) {
+        const int64_t c = min<int64_t>(cw + lane + 64 * (j0 + j), nc - 1);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) sv[hh][j] = j0 + j < jn ? shat(hh, c) : 0.f;
       }
-      ++nvalid;
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        float r = kNegInf;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) r = G > 1 ? fmaxf(r, sv[hh][j] - Ls[hh]) : sv[hh][j];
+        keys[j0 + j] = (j0 + j < jn && cw + lane + 64 * (j0 + j) < nc) ? order_key(r) : 0u;
+      }
     }
-    keys[j] = c < nc ? full_key(order_key(r), c) : 0ull;
-  }
-  uint64_t* cand = a.w.cand + (bg * a.w.nspan + sp) * topk;
-  const int nv = wave_sum_i(nvalid);
-  const uint64_t thr = nv > topk ? wave_kth_u64<J>(keys, topk, lane, sbuf) : 1ull;
-  int base = 0;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const bool sel = keys[j] != 0 && keys[j] >= thr;
-    const uint64_t m = __ballot(sel);
-    if (sel) cand[base + lane_prefix(m, lane)] = keys[j];
-    base += __popcll(m);
-  }
-  for (int t = base + lane; t < topk; t += kWave) cand[t] = 0ull;
-}
-
-// One wave per (b, g): the final top-k from the span lists, ascending, and each
-// head's s_hat on it.  With |C_i| <= k every candidate is selected.
-template <int G>
-__global__ __launch_bounds__(64) void dec_merge_kernel(DecKArgs a) {
-  __shared__ uint64_t sbuf[64];
-  __shared__ int32_t sids[64];
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int64_t i = a.pos.p[b];
-  const int64_t nc = num_candidates(i, a.S, a.W);
-  const int topk = a.topk;
-  const int64_t bg = (int64_t)b * a.Hkv + g;
-  int32_t cs_out;
-  if (nc <= topk) {
-    cs_out = lane < nc ? lane : -1;
-  } else {
-    const int nsp = (int)((nc + a.w.span - 1) / a.w.span);
-    const int ntot = nsp * topk;  // <= 64 * kMergeJ (checked on the host)
-    uint64_t v[kMergeJ];
-    const uint64_t* call = a.w.cand + bg * a.w.nspan * topk;
-#pragma unroll
-    for (int j = 0; j < kMergeJ; ++j) {
-      const int e = lane + 64 * j;
-      v[j] = e < ntot ? call[e] : 0ull;
-    }
-    const uint64_t thr = wave_kth_u64<kMergeJ>(v, topk, lane, sbuf);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kMergeJ; ++j) cnt += (v[j] != 0 && v[j] >= thr) ? 1 : 0;
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int x = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += x;
-    }
-    int pos = incl - cnt;
-#pragma unroll
-    for (int j = 0; j < kMergeJ; ++j)
-      if (v[j] != 0 && v[j] >= thr) sids[pos++] = key_chunk(v[j]);
+    wave_topk_u32<J>(keys, jn, topk, lane, sbuf[wave], wsel[wave], lkey[wave]);
+    n = topk;
     wave_lds_sync();
-    const uint32_t cs = lane < topk ? (uint32_t)sids[lane] : 0xffffffffu;
-    cs_out = (int32_t)bitonic_sort64<uint32_t>(cs, lane, false);
-  }
-  if (lane < topk) {
-    a.w.idx[bg * topk + lane] = cs_out;
-    if (a.idx_out) a.idx_out[bg * topk + lane] = cs_out;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const int h = g * G + hh;
-      a.w.ssel[((int64_t)b * a.Hq + h) * topk + lane] =
-          cs_out >= 0 ? a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + cs_out] : kNegInf;
+    if (lane < n) lid[wave][lane] = (int32_t)(cw + wsel[wave][lane]);
+  } else if (cnt > 0) {
+    n = cnt;
+    if (lane < n) {
+      lkey[wave][lane] = rank_key(cw + lane);
+      lid[wave][lane] = (int32_t)(cw + lane);
     }
+  }
+  if (lane == 0) nlist[wave] = n;
+  __syncthreads();
+  if (wave != 0) return;
+  // ---- merge: positions w*64 + t, t < nlist[w]; ascending position = ascending chunk
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) total += nlist[w];
+  if (total <= topk) {   // every listed candidate is chosen (lists ascend with the chunk)
+    int base = 0;
+    for (int w = 0; w < kSelWaves; ++w) {
+      const int nw = nlist[w];
+      if (lane < nw) emit(base + lane, lid[w][lane]);
+      base += nw;
+    }
+    if (lane >= base && lane < topk) emit(lane, -1);
+    return;
+  }
+  uint32_t keys[JM];
+#pragma unroll
+  for (int w = 0; w < JM; ++w) keys[w] = lane < nlist[w] ? lkey[w][lane] : 0u;   // position w*64 + lane
+  // wave_topk_u32 numbers candidates lane + 64*j, here j = list, so its ascending
+  // ids are (list, rank in list) in ascending chunk order only after a remap:
+  // translate each chosen id back through lid.
+  wave_topk_u32<JM>(keys, JM, topk, lane, sbuf[0], wsel[0]);
+  wave_lds_sync();
+  if (lane < topk) {
+    const int id = wsel[0][lane];
+    emit(lane, lid[id / 64][id % 64]);
   }
 }
 
@@ -444,23 +456,26 @@ __global__ __launch_bounds__(64) void dec_fuse_kernel(DecKArgs a) {
   if (a.lse && lane == 0) a.lse[(int64_t)b * a.Hq + h] = L;
 }
 
+// Candidates per selection wave: 64*J with kSelWaves waves covering every candidate.
+int pick_sel_j(int64_t max_nc) {
+  for (int J = 1; J <= 64; J <<= 1)
+    if ((int64_t)64 * J * kSelWaves >= max_nc) return J;
+  return -1;
+}
+
 template <int G>
 void launch_select_j(const DecKArgs& k, hipStream_t st) {
-  const dim3 grid(k.w.nspan, k.Hkv, k.B), block(64);
-  {
-  KTimer tm(K_DEC_SPAN, st);
-  switch (k.w.span / 64) {
-    case 1: hipLaunchKernelGGL((dec_span_kernel<G, 1>), grid, block, 0, st, k); break;
-    case 2: hipLaunchKernelGGL((dec_span_kernel<G, 2>), grid, block, 0, st, k); break;
-    case 4: hipLaunchKernelGGL((dec_span_kernel<G, 4>), grid, block, 0, st, k); break;
-    case 8: hipLaunchKernelGGL((dec_span_kernel<G, 8>), grid, block, 0, st, k); break;
-    case 16: hipLaunchKernelGGL((dec_span_kernel<G, 16>), grid, block, 0, st, k); break;
-    case 32: hipLaunchKernelGGL((dec_span_kernel<G, 32>), grid, block, 0, st, k); break;
-    default: hipLaunchKernelGGL((dec_span_kernel<G, 64>), grid, block, 0, st, k); break;
+  const dim3 grid(1, k.Hkv, k.B), block(64 * kSelWaves);
+  KTimer tm(K_DEC_SELECT, st);
+  switch (k.w.selj) {
+    case 1: hipLaunchKernelGGL((dec_select_kernel<G, 1>), grid, block, 0, st, k); break;
+    case 2: hipLaunchKernelGGL((dec_select_kernel<G, 2>), grid, block, 0, st, k); break;
+    case 4: hipLaunchKernelGGL((dec_select_kernel<G, 4>), grid, block, 0, st, k); break;
+    case 8: hipLaunchKernelGGL((dec_select_kernel<G, 8>), grid, block, 0, st, k); break;
+    case 16: hipLaunchKernelGGL((dec_select_kernel<G, 16>), grid, block, 0, st, k); break;
+    case 32: hipLaunchKernelGGL((dec_select_kernel<G, 32>), grid, block, 0, st, k); break;
+    default: hipLaunchKernelGGL((dec_select_kernel<G, 64>), grid, block, 0, st, k); break;
   }
-  }
-  KTimer tm(K_DEC_MERGE, st);
-  hipLaunchKernelGGL((dec_merge_kernel<G>), dim3(1, k.Hkv, k.B), block, 0, st, k);
 }
 
 template <typename T, int D, int G>
@@ -493,22 +508,13 @@ hipError_t launch_decode_t(const DecKArgs& k, hipStream_t st) {
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Candidates per selection wave: the smallest 64*J whose span lists fit one merge wave.
-int pick_span(int64_t NCcap, int topk) {
-  if (topk <= 0) return 64;
-  for (int J = 1; J <= 64; J <<= 1) {
-    const int64_t nspan = (NCcap + 64 * J - 1) / (64 * J);
-    if (nspan * topk <= 64 * kMergeJ) return 64 * J;
-  }
-  return -1;
-}
+// Candidates of the last cache row (the most any step can see).
+int64_t max_candidates(int64_t Lcap, int S, int W) { return Lcap > 0 ? num_candidates(Lcap - 1, S, W) : 0; }
 
 void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk, DecWs* w,
             size_t* total, char* base) {
   const int64_t NCcap = Lcap / S;
   const int nslice = (int)((NCcap + kSlice - 1) / kSlice);
-  const int span = pick_span(NCcap, topk);
-  const int nspan = (int)((NCcap + span - 1) / span);
   const int nitems = topk + W / S + 2;
   const int G = Hq / Hkv;
   const int kk = topk > 0 ? topk : 1;
@@ -517,13 +523,11 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
   DecWs d{};
   d.shat = reinterpret_cast<float*>(take((size_t)B * Hq * NCcap * 4));
   d.lpart = reinterpret_cast<float2*>(take((size_t)B * Hq * nslice * 8));
-  d.cand = reinterpret_cast<uint64_t*>(take((size_t)B * Hkv * nspan * kk * 8));
   d.idx = reinterpret_cast<int32_t*>(take((size_t)B * Hkv * kk * 4));
   d.ssel = reinterpret_cast<float*>(take((size_t)B * Hq * kk * 4));
   d.apart = reinterpret_cast<float*>(take((size_t)B * Hkv * nitems * G * (D + 2) * 4));
   d.nslice = nslice;
-  d.nspan = nspan;
-  d.span = span;
+  d.selj = pick_sel_j(max_candidates(Lcap, S, W));
   d.nitems = nitems;
   if (w) *w = d;
   if (total) *total = off + 256;
@@ -532,7 +536,7 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
 }  // namespace
 
 bool decode_supported(int64_t Lcap, int S, int W, int topk) {
-  return pick_span(Lcap / S, topk) > 0 && topk + W / S + 2 <= 256;
+  return pick_sel_j(max_candidates(Lcap, S, W)) > 0 && topk + W / S + 2 <= 256;
 }
 
 size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk) {

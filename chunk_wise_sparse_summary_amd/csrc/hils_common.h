@@ -168,12 +168,12 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 }
 
 // Aligned window left edge l_i = max(0, S*floor((i-W+1)/S)) and |C_i| = l_i / S.
-__device__ __forceinline__ int64_t window_left(int64_t i, int S, int W) {
+__host__ __device__ __forceinline__ int64_t window_left(int64_t i, int S, int W) {
   int64_t a = i - (int64_t)W + 1;
   if (a <= 0) return 0;
   return (a / S) * S;
 }
-__device__ __forceinline__ int64_t num_candidates(int64_t i, int S, int W) {
+__host__ __device__ __forceinline__ int64_t num_candidates(int64_t i, int S, int W) {
   return window_left(i, S, W) / S;
 }
 

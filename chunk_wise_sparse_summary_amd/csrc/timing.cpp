@@ -15,7 +15,7 @@ namespace {
 
 const char* const kNames[K_COUNT] = {
     "summarize", "score_lse", "rank_select", "idx_count", "idx_scan_tiles", "idx_scan_buckets",
-    "idx_fill", "lsel", "window", "chunk_attend", "combine", "dec_score", "dec_span", "dec_merge",
+    "idx_fill", "lsel", "window", "chunk_attend", "combine", "dec_score", "dec_select",
     "dec_attend", "dec_fuse", "dec_summarize", "v_transpose", "q_group"};
 
 struct Rec {

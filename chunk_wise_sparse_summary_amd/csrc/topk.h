@@ -135,7 +135,8 @@ __device__ __forceinline__ uint32_t wave_kth_lane_u32(uint32_t x, int topk) {
 // Exact top-k of 32-bit rank keys held J per lane, candidate id lane + 64*j
 // (key 0 = absent; keys[j] for j >= jn are all absent), more than topk present.
 // Ties at the k-th key go to the lower ids.  Writes the chosen ids ascending to
-// out[0..topk).  buf: 64 wave-private uint32 in LDS.
+// out[0..topk) (and their keys to out_keys, if given).  buf: 64 wave-private
+// uint32 in LDS.
 //   1. theta = the k-th largest of the 64 per-lane maxima: a lower bound of the
 //      k-th largest key K (the k lanes with the largest maxima hold k keys >= theta);
 //   2. if at most 64 keys reach theta they are compacted one per lane and K is
@@ -143,7 +144,7 @@ __device__ __forceinline__ uint32_t wave_kth_lane_u32(uint32_t x, int topk) {
 //   3. every key above K is chosen, plus the lowest-id keys equal to K up to k.
 template <int J>
 __device__ void wave_topk_u32(const uint32_t (&keys)[J], int jn, int topk, int lane, uint32_t* buf,
-                              int32_t* out) {
+                              int32_t* out, uint32_t* out_keys = nullptr) {
   uint32_t lm = 0;
 #pragma unroll
   for (int j = 0; j < J; ++j)
@@ -194,7 +195,11 @@ __device__ void wave_topk_u32(const uint32_t (&keys)[J], int jn, int topk, int l
       const bool sel = keys[j] > kstar || (eq && eq_seen + lane_prefix(meq, lane) < need);
       eq_seen += __popcll(meq);
       const uint64_t m = __ballot(sel);
-      if (sel) out[base + lane_prefix(m, lane)] = lane + 64 * j;
+      if (sel) {
+        const int pos = base + lane_prefix(m, lane);
+        out[pos] = lane + 64 * j;
+        if (out_keys) out_keys[pos] = keys[j];
+      }
       base += __popcll(m);
     }
   }
