@@ -90,7 +90,10 @@ def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
     return {
         "summarize": ("hbm", summary_bytes(B, Hq, Hkv, T, d, S, esz), "B"),
         "score_lse": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
-        "rank_select": ("mfma", B * Hq * (ncand + nsel) * 2.0 * d, "FLOP"),
+        "rank_keys": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
+        # the rank keys of every (query, group, candidate) read once
+        "topk_rows": ("hbm", B * Hkv * ncand * 4.0, "B"),
+        "sel_scores": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
         # K and V^T of every chunk once per KV head; per (query, group, slot)
         # entry: the entry word, G rows of q and G chunk weights read, G weighted
         # partial rows written
@@ -124,10 +127,16 @@ KERNEL_SOURCES = {
     "window": ["chunk_wise_sparse_summary_amd/csrc/attend.hip",
                "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
                "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
-    "rank_select": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
-                    "chunk_wise_sparse_summary_amd/csrc/topk.h",
-                    "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-                    "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "rank_keys": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
+                  "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+                  "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "topk_rows": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
+                  "chunk_wise_sparse_summary_amd/csrc/topk.h",
+                  "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+                  "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "sel_scores": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
+                   "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
+                   "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
     "score_lse": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
                   "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
                   "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
@@ -348,7 +357,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    prefill_kernels = ["summarize", "score_lse", "rank_select", "lsel", "idx_count", "idx_scan_tiles",
+    prefill_kernels = ["summarize", "score_lse", "rank_keys", "topk_rows", "sel_scores", "lsel", "idx_count", "idx_scan_tiles",
                        "idx_scan_buckets", "idx_fill", "v_transpose", "q_group", "window",
                        "chunk_attend", "combine"]
     log("warmup")

@@ -164,10 +164,10 @@ def hils_decode_step(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, 
         _p(workspace_t), workspace_t.numel(), _stream()))
 
 
-KERNELS = ("summarize", "score_lse", "rank_select", "idx_count", "idx_scan_tiles",
+KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",
            "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend", "combine",
            "dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize",
-           "v_transpose", "q_group")
+           "v_transpose", "q_group", "rank_keys", "topk_rows", "sel_scores")
 
 
 def hils_timing_enable(kernels):

@@ -84,7 +84,7 @@ size_t hils_workspace_bytes(const hils_shape* s, hils_op op) {
     case HILS_OP_SUMMARIZE: return 0;
     case HILS_OP_SELECT:
       return hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
-                                    nullptr, nullptr);
+                                    s->io_dtype == HILS_BF16, nullptr, nullptr);
     case HILS_OP_ATTEND_FUSE: {
       size_t full = 0;
       attend_min_ws(s, &full);
@@ -137,7 +137,7 @@ hils_status hils_select(const hils_shape* s, const void* q_hat, const void* k_su
   int n_slots = 0;
   int64_t stride = 0;
   const size_t need = hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len,
-                                             s->chunk, &n_slots, &stride);
+                                             s->chunk, s->io_dtype == HILS_BF16, &n_slots, &stride);
   if (!ws || ws_bytes < need) return HILS_E_WORKSPACE;
   hils::SelArgs a{};
   a.qh = q_hat; a.ksum = k_sum; a.bsum = b_sum; a.idx = sel_idx; a.ssel = sel_score;

@@ -39,16 +39,17 @@ struct SelArgs {
   int32_t* idx;
   float* ssel;
   float* L;          // [B, Hq, T] scratch (G > 1)
-  float* scratch;    // rank keys, per persistent slot
+  float* scratch;    // rank keys of one (b, group): n_slots rows of slot_stride
   int B, Hq, Hkv, D, S, W, topk;
   bool bf16;
   int64_t T, NCs;
   float scale;
   int n_slots;
-  int64_t slot_stride;  // floats per slot
+  int64_t slot_stride;  // keys per row
 };
 hipError_t launch_select(const SelArgs& a, hipStream_t st);
-size_t select_workspace(int B, int Hq, int Hkv, int64_t T, int S, int* n_slots, int64_t* slot_stride);
+size_t select_workspace(int B, int Hq, int Hkv, int64_t T, int S, bool bf16, int* n_slots,
+                        int64_t* slot_stride);
 
 struct AttArgs {
   const void* q;
@@ -97,9 +98,10 @@ hipError_t launch_decode(const DecArgs& a, hipStream_t st);
 // a launch records a HIP event pair on the launch stream when that kernel is
 // selected, and does nothing otherwise.
 enum KernelId {
-  K_SUMMARIZE, K_SCORE_LSE, K_RANK_SELECT, K_IDX_COUNT, K_IDX_SCAN_TILES, K_IDX_SCAN_BUCKETS,
+  K_SUMMARIZE, K_SCORE_LSE, K_IDX_COUNT, K_IDX_SCAN_TILES, K_IDX_SCAN_BUCKETS,
   K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_COMBINE, K_DEC_SCORE, K_DEC_SELECT,
-  K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_QGROUP, K_COUNT
+  K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_QGROUP, K_RANK_KEYS, K_TOPK_ROWS, K_SEL_SCORES,
+  K_COUNT
 };
 class KTimer {
  public:

@@ -9,14 +9,13 @@
 // the max weight; for a group of one head the rank key is s_hat itself.  Ties
 // go to the lower chunk index.
 //
-// Two kernels:
+// Kernels (per (b, group) after the first):
 //   score_lse   (G > 1 only) L_{h,i} = LSE_{c in C_i} s_hat_{h,i,c}: MFMA score
 //               tiles with an online log-sum-exp epilogue; one workgroup = one
 //               head x 256 queries, k' tiles staged once in LDS.
-//   rank_select persistent workgroups, each owning a scratch slot of rank keys.
-//               For 64 queries x one group it recomputes every head's score
-//               tiles, forms the rank key per (query, chunk), selects the top-k of
-//               each query (below) and computes each head's s_hat on the choice.
+//   rank_keys   rank key per (query, candidate) into a scratch row per query;
+//   topk_rows   one wave per query: its top-k (below);
+//   sel_scores  each head's s_hat on the chosen chunks (a second score pass).
 //
 // Wave-level top-k of n <= 64*J rank keys held J per lane (candidate c = lane +
 // 64*j; keys are order-preserving unsigned images of the fp32 rank key): a
@@ -38,27 +37,27 @@ template <> struct KPad<float> { static constexpr int P = 4; };
 // A tile of k' (16 chunks of NH heads, padded LDS rows) and b' is fetched into
 // registers by all 256 threads and committed to LDS one iteration later, so the
 // next tile's loads overlap the current tile's MFMAs.
-template <typename T, int D, int NH>
+template <typename T, int D, int NH, int NT = 256>
 struct KTile {
   static constexpr int EPV = 16 / sizeof(T);
   static constexpr int PPR = D / EPV;                 // 16-byte pieces per row
   static constexpr int KP = D + KPad<T>::P;           // padded row (elements)
   static constexpr int NPIECE = NH * 16 * PPR;
-  static constexpr int NPT = (NPIECE + 255) / 256;    // pieces per thread
+  static constexpr int NPT = (NPIECE + NT - 1) / NT;  // pieces per thread (NT threads)
 };
 
 // The prefetched pieces live in one vector value (not an array), so that they
 // stay in registers whatever the unrolling order.
 template <int N> using u32v = uint32_t __attribute__((ext_vector_type(N)));
 
-template <typename T, int D, int NH, int NPT = KTile<T, D, NH>::NPT>
+template <typename T, int D, int NH, int NT = 256, int NPT = KTile<T, D, NH, NT>::NPT>
 __device__ __forceinline__ void tile_fetch(u32v<4 * NPT>& reg, float& breg, const T* kg,
                                            const float* bg, int64_t NCs, int c0, int cl_last) {
-  using K = KTile<T, D, NH>;
+  using K = KTile<T, D, NH, NT>;
 #pragma unroll
   for (int t = 0; t < NPT; ++t) {
-    const int p = t * 256 + threadIdx.x;
-    if (K::NPIECE % 256 == 0 || p < K::NPIECE) {
+    const int p = t * NT + threadIdx.x;
+    if (K::NPIECE % NT == 0 || p < K::NPIECE) {
       const int hh = p / (16 * K::PPR), rem = p % (16 * K::PPR), row = rem / K::PPR, pc = rem % K::PPR;
       const int cl = min(c0 + row, cl_last);
       const uint4 v = *reinterpret_cast<const uint4*>(kg + ((int64_t)hh * NCs + cl) * D + pc * K::EPV);
@@ -71,13 +70,13 @@ __device__ __forceinline__ void tile_fetch(u32v<4 * NPT>& reg, float& breg, cons
   }
 }
 
-template <typename T, int D, int NH, int NPT = KTile<T, D, NH>::NPT>
+template <typename T, int D, int NH, int NT = 256, int NPT = KTile<T, D, NH, NT>::NPT>
 __device__ __forceinline__ void tile_commit(const u32v<4 * NPT>& reg, float breg, T* kt, float* bt) {
-  using K = KTile<T, D, NH>;
+  using K = KTile<T, D, NH, NT>;
 #pragma unroll
   for (int t = 0; t < NPT; ++t) {
-    const int p = t * 256 + threadIdx.x;
-    if (K::NPIECE % 256 == 0 || p < K::NPIECE) {
+    const int p = t * NT + threadIdx.x;
+    if (K::NPIECE % NT == 0 || p < K::NPIECE) {
       const int hh = p / (16 * K::PPR), rem = p % (16 * K::PPR), row = rem / K::PPR, pc = rem % K::PPR;
       *reinterpret_cast<uint4*>(kt + (hh * 16 + row) * K::KP + pc * K::EPV) =
           make_uint4(reg[4 * t], reg[4 * t + 1], reg[4 * t + 2], reg[4 * t + 3]);
@@ -196,230 +195,283 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
 template <typename T, int D, int J>
 constexpr int rank_waves() { return (J <= 16 || (J == 32 && (sizeof(T) == 2 || D == 64))) ? 2 : 1; }
 
-// Rank keys, top-k and each head's s_hat on the selection, for one (b, group,
-// 64-query tile) per workgroup iteration (persistent workgroups, each owning a
-// scratch slot of rank keys).  Wave w handles heads w and w + 4 of the group:
-//   phase 1: per 16-chunk tile (k' of all G heads staged in LDS), each head's
-//            x = s_hat - L_h for the 64 queries goes to LDS (transposed score
-//            tiles: a lane holds four chunks of one query), and the rank key
-//            r = max over heads (r = s_hat for one head) to the scratch slot;
-//   phase 2: each wave selects the top-k of 16 queries; then each head's wave
-//            computes its s_hat on every chosen chunk of the 64 queries.
-template <typename T, int D, int G, int J>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(rank_waves<T, D, J>(), 2)))
-void rank_select_kernel(SelArgs a) {
-  constexpr int KS = D / 32;
-  constexpr int NCP = 64 * J;
-  constexpr int HW = (G + 3) / 4;        // heads per wave
+// Queries per workgroup: 128 (8 waves) for bf16; 64 (4 waves) for fp32, whose
+// larger tiles would not fit LDS at 128.
+template <typename T> constexpr int rank_q() { return sizeof(T) == 2 ? 128 : 64; }
+
+// The prefill selection runs as three kernels per (b, group), the rank keys of
+// one group at a time living in a [T][64 J] scratch:
+//   rank_keys  per 128-query tile and 16-chunk k' tile (k' of all G heads staged
+//              once in LDS): each head's x = s_hat - L_h (transposed score tiles:
+//              a lane holds four chunks of one query) goes to LDS, and the rank
+//              key r = max over heads (r = s_hat for one head) to the scratch.
+//              Wave w takes the 64 queries 64 (w / 4) .. and heads w % 4, w % 4 + 4.
+//   topk_rows  one wave per query: the exact top-k of its rank keys (below).
+//   sel_scores per 128-query tile, a second pass of the score tiles writes each
+//              head's s_hat on every chosen chunk: a chunk's value is kept where
+//              the query's selection bitmap has it, at slot = number of chosen
+//              chunks below it (ids ascend).
+template <typename T, int D, int G>
+struct RankTiles {
+  static constexpr int KS = D / 32;
+  static constexpr int HW = (G + 3) / 4;   // heads per wave
+  static constexpr int RQ = rank_q<T>(), NT = RQ * 4;
+  using Tile = KTile<T, D, G, NT>;
+};
+
+template <typename T, int D, int G, int NCP>
+__global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, int b, int g,
+                                                                    uint32_t* __restrict__ keys) {
+  using R = RankTiles<T, D, G>;
+  constexpr int KS = R::KS, HW = R::HW, RQ = R::RQ, NT = R::NT;
   constexpr int XP = 20;                 // padded LDS row of 16 chunk values
-  using Tile = KTile<T, D, G>;
+  using Tile = typename R::Tile;
   __shared__ __align__(16) T kt[G * 16 * Tile::KP];
   __shared__ float bt[G * 16];
-  __shared__ __align__(16) float xs[G][64][XP];   // x = s_hat - L per head, 64 queries x 16 chunks
-  __shared__ uint32_t sbuf[4][64];
-  __shared__ int32_t sidx[64 * 64];      // 64 queries x up to 64 chosen ids
+  __shared__ __align__(16) float xs[G][RQ][XP];   // x = s_hat - L per head
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
+  const int qhalf = wave / 4, hw = wave % 4;
   const T* qh = static_cast<const T*>(a.qh);
-  const T* ksum = static_cast<const T*>(a.ksum);
   const int64_t T_ = a.T, NCs = a.NCs;
-  const int Hq = a.Hq, Hkv = a.Hkv, S = a.S, W = a.W, topk = a.topk;
-  const int64_t nqt = (T_ + 63) / 64;
-  const int64_t ntiles = (int64_t)a.B * Hkv * nqt;
-  // rank keys as order-preserving unsigned images of the fp32 values, [64][NCP]
-  uint32_t* slot = reinterpret_cast<uint32_t*>(a.scratch) + (int64_t)blockIdx.x * a.slot_stride;
-
-  for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
-    const int64_t qt = tile_id % nqt;
-    const int g = (int)((tile_id / nqt) % Hkv);
-    const int b = (int)(tile_id / (nqt * Hkv));
-    const int64_t qb = qt * 64;
-    const T* kg = ksum + ((int64_t)b * Hq + g * G) * NCs * D;   // head g*G, chunk 0
-    const float* bg = a.bsum + ((int64_t)b * Hq + g * G) * NCs;
-
-    // this wave's heads: q_hat of the 64 queries (fragment r16 of tile rt = query
-    // 16 rt + r16) and L of those queries.  The fragments are loaded again for
-    // phase 2b so they are not live across the top-k.
-    Frag<T> qf[HW][4][KS];
-    float Lq[HW][4];
-    auto load_q = [&](int u) {
-      const int h = g * G + wave + 4 * u;
+  const int Hq = a.Hq;
+  const int64_t qb = (int64_t)blockIdx.x * RQ;
+  const int64_t qw = qb + 64 * qhalf;     // this wave's 64 queries
+  const T* kg = static_cast<const T*>(a.ksum) + ((int64_t)b * Hq + g * G) * NCs * D;
+  const float* bg = a.bsum + ((int64_t)b * Hq + g * G) * NCs;
+  Frag<T> qf[HW][4][KS];
+  float Lq[HW][4];
+#pragma unroll
+  for (int u = 0; u < HW; ++u) {
+    const int hh = hw + 4 * u;
+    if (hh < G) {
+      const int h = g * G + hh;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const int64_t qa = min(qb + 16 * rt + r16, T_ - 1);
-        const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + qa) * D + 8 * grp;
+        const int64_t qi = qw + 16 * rt + r16;
+        const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) load_frag(qf[u][rt][ks], qrow + 32 * ks);
+        Lq[u][rt] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
+      }
+    }
+  }
+  const int nc_block = (int)num_candidates(min(qb + RQ - 1, T_ - 1), a.S, a.W);
+  const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
+  u32v<4 * Tile::NPT> kreg;
+  float breg = 0.f;
+  if (nc_block > 0) tile_fetch<T, D, G, NT>(kreg, breg, kg, bg, NCs, 0, cl_last);
+  for (int c0 = 0; c0 < nc_block; c0 += 16) {
+    __syncthreads();
+    tile_commit<T, D, G, NT>(kreg, breg, kt, bt);
+    __syncthreads();
+    if (c0 + 16 < nc_block) tile_fetch<T, D, G, NT>(kreg, breg, kg, bg, NCs, c0 + 16, cl_last);
+#pragma unroll
+    for (int u = 0; u < HW; ++u) {
+      const int hh = hw + 4 * u;
+      if (hh < G) {
+        Frag<T> kf[KS];   // row r16 = chunk c0 + r16
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
+        const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
+        f32x4_t acc[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) mma(acc[rt], kf[ks], qf[u][rt][ks]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          float4 x;
+          x.x = fmaf(acc[rt][0], a.scale, bk.x) - Lq[u][rt];
+          x.y = fmaf(acc[rt][1], a.scale, bk.y) - Lq[u][rt];
+          x.z = fmaf(acc[rt][2], a.scale, bk.z) - Lq[u][rt];
+          x.w = fmaf(acc[rt][3], a.scale, bk.w) - Lq[u][rt];
+          *reinterpret_cast<float4*>(&xs[hh][64 * qhalf + 16 * rt + r16][4 * grp]) = x;
+        }
+      }
+    }
+    __syncthreads();
+    // wave w: queries 16w + r16 of the tile, chunks c0 + 4 grp .. + 3
+    const int row = 16 * wave + r16;
+    if (qb + row < T_) {
+      float4 r = *reinterpret_cast<const float4*>(&xs[0][row][4 * grp]);
+#pragma unroll
+      for (int hh = 1; hh < G; ++hh) {
+        const float4 y = *reinterpret_cast<const float4*>(&xs[hh][row][4 * grp]);
+        r.x = fmaxf(r.x, y.x); r.y = fmaxf(r.y, y.y); r.z = fmaxf(r.z, y.z); r.w = fmaxf(r.w, y.w);
+      }
+      *reinterpret_cast<uint4*>(keys + (qb + row) * NCP + c0 + 4 * grp) =
+          make_uint4(order_key(r.x), order_key(r.y), order_key(r.z), order_key(r.w));
+    }
+  }
+}
+
+// One wave per query of one (b, group): the exact top-k of its rank keys.
+template <int J>
+__global__ __launch_bounds__(256) void topk_rows_kernel(SelArgs a, int b, int g,
+                                                        const uint32_t* __restrict__ keys) {
+  __shared__ uint32_t sbuf[4][64];
+  __shared__ int32_t sel[4][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int64_t i = (int64_t)blockIdx.x * 4 + wave;
+  if (i >= a.T) return;
+  const int topk = a.topk;
+  const int nc = (int)num_candidates(i, a.S, a.W);
+  int32_t* out = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * topk;
+  if (nc <= topk) {
+    if (lane < topk) out[lane] = lane < nc ? lane : -1;
+    return;
+  }
+  const uint32_t* rrow = keys + i * (64 * J);
+  const int jn = (nc + 63) / 64;
+  uint32_t kv[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = lane + 64 * j;
+    kv[j] = (j < jn && c < nc) ? rrow[c] : 0u;
+  }
+  wave_topk_u32<J>(kv, jn, topk, lane, sbuf[wave], sel[wave]);
+  wave_lds_sync();
+  if (lane < topk) out[lane] = sel[wave][lane];
+}
+
+template <typename T, int D, int G, int NCP>
+__global__ __launch_bounds__(rank_q<T>() * 4) void sel_scores_kernel(SelArgs a, int b, int g) {
+  using R = RankTiles<T, D, G>;
+  constexpr int KS = R::KS, HW = R::HW, RQ = R::RQ, NT = R::NT;
+  constexpr int BMP = NCP / 32 + 1;      // padded bitmap row (words)
+  using Tile = typename R::Tile;
+  __shared__ __align__(16) T kt[G * 16 * Tile::KP];
+  __shared__ float bt[G * 16];
+  __shared__ uint32_t selbm[RQ * BMP];   // RQ queries x candidate bitmap of the choice
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r16 = lane % 16, grp = lane / 16;
+  const int qhalf = wave / 4, hw = wave % 4;
+  const T* qh = static_cast<const T*>(a.qh);
+  const int64_t T_ = a.T, NCs = a.NCs;
+  const int Hq = a.Hq, topk = a.topk;
+  const int64_t qb = (int64_t)blockIdx.x * RQ;
+  const int64_t qw = qb + 64 * qhalf;
+  const T* kg = static_cast<const T*>(a.ksum) + ((int64_t)b * Hq + g * G) * NCs * D;
+  const float* bg = a.bsum + ((int64_t)b * Hq + g * G) * NCs;
+  const int32_t* irows = a.idx + (((int64_t)b * a.Hkv + g) * T_ + qb) * topk;
+  for (int e = threadIdx.x; e < RQ * BMP; e += NT) selbm[e] = 0u;
+  __syncthreads();
+  for (int e = threadIdx.x; e < RQ * topk; e += NT) {
+    const int row = e / topk, t = e % topk;
+    if (qb + row >= T_) continue;
+    const int32_t c = irows[(int64_t)row * topk + t];
+    if (c >= 0) {
+      atomicOr(&selbm[row * BMP + c / 32], 1u << (c % 32));
+    } else {   // padding slot
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+        a.ssel[(((int64_t)b * Hq + g * G + hh) * T_ + qb + row) * topk + t] = kNegInf;
+    }
+  }
+  Frag<T> qf[HW][4][KS];
+#pragma unroll
+  for (int u = 0; u < HW; ++u) {
+    const int hh = hw + 4 * u;
+    if (hh < G) {
+      const int h = g * G + hh;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int64_t qi = qw + 16 * rt + r16;
+        const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) load_frag(qf[u][rt][ks], qrow + 32 * ks);
       }
-    };
+    }
+  }
+  const int nc_block = (int)num_candidates(min(qb + RQ - 1, T_ - 1), a.S, a.W);
+  const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
+  int below[4];   // chosen chunks of query qw + 16 rt + r16 before this tile
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) below[rt] = 0;
+  u32v<4 * Tile::NPT> kreg;
+  float breg = 0.f;
+  if (nc_block > 0) tile_fetch<T, D, G, NT>(kreg, breg, kg, bg, NCs, 0, cl_last);
+  for (int c0 = 0; c0 < nc_block; c0 += 16) {
+    __syncthreads();
+    tile_commit<T, D, G, NT>(kreg, breg, kt, bt);
+    __syncthreads();
+    if (c0 + 16 < nc_block) tile_fetch<T, D, G, NT>(kreg, breg, kg, bg, NCs, c0 + 16, cl_last);
+    uint32_t seg[4];   // the tile's 16 bitmap bits of query qw + 16 rt + r16
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      seg[rt] = (selbm[(64 * qhalf + 16 * rt + r16) * BMP + c0 / 32] >> (c0 % 32)) & 0xffffu;
 #pragma unroll
     for (int u = 0; u < HW; ++u) {
-      const int hh = wave + 4 * u;
+      const int hh = hw + 4 * u;
       if (hh < G) {
         const int h = g * G + hh;
-        load_q(u);
+        Frag<T> kf[KS];   // row r16 = chunk c0 + r16
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
+        const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
+        const float bkv[4] = {bk.x, bk.y, bk.z, bk.w};
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const int64_t qi = qb + 16 * rt + r16;
-          Lq[u][rt] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
-        }
-      }
-    }
-
-    // ---------- phase 1
-    const int nc_block = (int)num_candidates(min(qb + 63, T_ - 1), S, W);
-    const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
-    u32v<4 * Tile::NPT> kreg;
-    float breg = 0.f;
-    if (nc_block > 0) tile_fetch<T, D, G>(kreg, breg, kg, bg, NCs, 0, cl_last);
-    for (int c0 = 0; c0 < nc_block; c0 += 16) {
-      __syncthreads();
-      tile_commit<T, D, G>(kreg, breg, kt, bt);
-      __syncthreads();
-      if (c0 + 16 < nc_block) tile_fetch<T, D, G>(kreg, breg, kg, bg, NCs, c0 + 16, cl_last);
+          const uint32_t mine = (seg[rt] >> (4 * grp)) & 0xfu;
+          if (__ballot(mine != 0u) == 0ull) continue;   // no chosen chunk in this 16 x 16 tile
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < HW; ++u) {
-        const int hh = wave + 4 * u;
-        if (hh < G) {
-          Frag<T> kf[KS];   // row r16 = chunk c0 + r16
+          for (int ks = 0; ks < KS; ++ks) mma(acc, kf[ks], qf[u][rt][ks]);
+          const int64_t i = qw + 16 * rt + r16;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
-          const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
-          f32x4_t acc[4];
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) mma(acc[rt], kf[ks], qf[u][rt][ks]);
-          }
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            float4 x;
-            x.x = fmaf(acc[rt][0], a.scale, bk.x) - Lq[u][rt];
-            x.y = fmaf(acc[rt][1], a.scale, bk.y) - Lq[u][rt];
-            x.z = fmaf(acc[rt][2], a.scale, bk.z) - Lq[u][rt];
-            x.w = fmaf(acc[rt][3], a.scale, bk.w) - Lq[u][rt];
-            *reinterpret_cast<float4*>(&xs[hh][16 * rt + r16][4 * grp]) = x;
-          }
-        }
-      }
-      __syncthreads();
-      // wave w: queries 16w + r16, chunks c0 + 4 grp .. + 3
-      {
-        const int row = 16 * wave + r16;
-        float4 r = *reinterpret_cast<const float4*>(&xs[0][row][4 * grp]);
-#pragma unroll
-        for (int hh = 1; hh < G; ++hh) {
-          const float4 y = *reinterpret_cast<const float4*>(&xs[hh][row][4 * grp]);
-          r.x = fmaxf(r.x, y.x); r.y = fmaxf(r.y, y.y); r.z = fmaxf(r.z, y.z); r.w = fmaxf(r.w, y.w);
-        }
-        *reinterpret_cast<uint4*>(slot + row * NCP + c0 + 4 * grp) =
-            make_uint4(order_key(r.x), order_key(r.y), order_key(r.z), order_key(r.w));
-      }
-    }
-    __threadfence_block();
-    __syncthreads();
-
-    // ---------- phase 2a: top-k of the wave's 16 queries (rows 16w..16w+15)
-    for (int qq = 0; qq < 16; ++qq) {
-      const int row = 16 * wave + qq;
-      const int64_t i = qb + row;
-      int32_t* sel = sidx + row * 64;
-      const int nc = i < T_ ? (int)num_candidates(i, S, W) : 0;
-      if (nc <= topk) {
-        if (lane < topk) sel[lane] = lane < nc ? lane : -1;
-      } else {
-        uint32_t keys[J];
-        const uint32_t* rrow = slot + row * NCP;
-        const int jn = (nc + 63) / 64;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-          const int c = lane + 64 * j;
-          keys[j] = (j < jn && c < nc) ? rrow[c] : 0u;
-        }
-        wave_topk_u32<J>(keys, jn, topk, lane, sbuf[wave], sel);
-      }
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * topk; e += 256) {
-      const int row = e / topk, t = e % topk;
-      const int64_t i = qb + row;
-      if (i < T_) a.idx[(((int64_t)b * Hkv + g) * T_ + i) * topk + t] = sidx[row * 64 + t];
-    }
-    // ---------- phase 2b: each head's s_hat on the selection.  Column tiles of 16
-    // chosen slots (slot s belongs to query s / topk) against the 16-query row
-    // tile(s) that own them; only the entry in the slot's own row is kept.
-#pragma unroll
-    for (int u = 0; u < HW; ++u) {
-      const int hh = wave + 4 * u;
-      if (hh >= G) continue;
-      const int h = g * G + hh;
-      load_q(u);
-      const int nslots = 64 * topk;
-      const T* kh = kg + (int64_t)hh * NCs * D;
-      const float* bh = bg + (int64_t)hh * NCs;
-      // P column tiles are gathered together, so P gathers are in flight at once
-      constexpr int P = sizeof(T) == 2 ? 4 : (D == 64 ? 2 : 1);
-      for (int t00 = 0; t00 < nslots; t00 += 16 * P) {
-        Frag<T> bf[P][KS];
-        float bv[P];
-        int32_t cs[P];
-#pragma unroll
-        for (int pp = 0; pp < P; ++pp) {
-          const int sl = t00 + 16 * pp + r16;
-          cs[pp] = sl < nslots ? sidx[(sl / topk) * 64 + sl % topk] : -1;
-          if (cs[pp] >= 0) {  // pad slots read nothing: there may be no summaries at all
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-              load_frag(bf[pp][ks], kh + (int64_t)cs[pp] * D + 8 * grp + 32 * ks);
-            bv[pp] = bh[cs[pp]];
-          } else {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) zero_frag(bf[pp][ks]);
-            bv[pp] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int pp = 0; pp < P; ++pp) {
-          const int t0 = t00 + 16 * pp;
-          if (t0 >= nslots) break;   // uniform
-          const int sl = t0 + r16;
-          const int sq = sl / topk, st = sl % topk;       // this lane's column: query, slot
-          const int rt_lo = (t0 / topk) / 16, rt_hi = (min(t0 + 15, nslots - 1) / topk) / 16;
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            if (rt < rt_lo || rt > rt_hi) continue;   // uniform across the wave
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) mma(acc, qf[u][rt][ks], bf[pp][ks]);
-            const int ii = sq - 16 * rt - 4 * grp;
-            if (sl < nslots && ii >= 0 && ii < 4 && qb + sq < T_) {
-              const float v = ii == 0 ? acc[0] : ii == 1 ? acc[1] : ii == 2 ? acc[2] : acc[3];
-              a.ssel[(((int64_t)b * Hq + h) * T_ + qb + sq) * topk + st] =
-                  cs[pp] >= 0 ? fmaf(v, a.scale, bv[pp]) : kNegInf;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            if (((mine >> q4) & 1u) && i < T_) {
+              const int slot_t = below[rt] + __popc(seg[rt] & ((1u << (4 * grp + q4)) - 1u));
+              a.ssel[(((int64_t)b * Hq + h) * T_ + i) * topk + slot_t] = fmaf(acc[q4], a.scale, bkv[q4]);
             }
           }
         }
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) below[rt] += __popc(seg[rt]);
   }
+}
+
+template <typename T, int D, int G, int J>
+hipError_t launch_rank_j(const SelArgs& a, hipStream_t st) {
+  constexpr int RQ = rank_q<T>();
+  const dim3 tiles((unsigned)((a.T + RQ - 1) / RQ)), rows((unsigned)((a.T + 3) / 4));
+  uint32_t* keys = reinterpret_cast<uint32_t*>(a.scratch);
+  for (int b = 0; b < a.B; ++b) {
+    for (int g = 0; g < a.Hkv; ++g) {
+      {
+        KTimer tm(K_RANK_KEYS, st);
+        hipLaunchKernelGGL((rank_keys_kernel<T, D, G, 64 * J>), tiles, dim3(RQ * 4), 0, st, a, b, g, keys);
+      }
+      {
+        KTimer tm(K_TOPK_ROWS, st);
+        hipLaunchKernelGGL((topk_rows_kernel<J>), rows, dim3(256), 0, st, a, b, g, keys);
+      }
+      KTimer tm(K_SEL_SCORES, st);
+      hipLaunchKernelGGL((sel_scores_kernel<T, D, G, 64 * J>), tiles, dim3(RQ * 4), 0, st, a, b, g);
+    }
+  }
+  return hipGetLastError();
 }
 
 template <typename T, int D, int G>
 hipError_t launch_rank(const SelArgs& a, int J, hipStream_t st) {
-  dim3 grid((unsigned)a.n_slots), block(256);
-  KTimer tm(K_RANK_SELECT, st);
   switch (J) {
-    case 1: hipLaunchKernelGGL((rank_select_kernel<T, D, G, 1>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((rank_select_kernel<T, D, G, 4>), grid, block, 0, st, a); break;
-    case 16: hipLaunchKernelGGL((rank_select_kernel<T, D, G, 16>), grid, block, 0, st, a); break;
-    case 32: hipLaunchKernelGGL((rank_select_kernel<T, D, G, 32>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((rank_select_kernel<T, D, G, 64>), grid, block, 0, st, a); break;
+    case 1: return launch_rank_j<T, D, G, 1>(a, st);
+    case 4: return launch_rank_j<T, D, G, 4>(a, st);
+    case 16: return launch_rank_j<T, D, G, 16>(a, st);
+    case 32: return launch_rank_j<T, D, G, 32>(a, st);
+    default: return launch_rank_j<T, D, G, 64>(a, st);
   }
-  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -453,17 +505,15 @@ int pick_J(int64_t NCs) {
 
 }  // namespace
 
-size_t select_workspace(int B, int Hq, int Hkv, int64_t T, int S, int* n_slots,
+size_t select_workspace(int B, int Hq, int Hkv, int64_t T, int S, bool bf16, int* n_slots,
                         int64_t* slot_stride) {
+  (void)bf16;
   const int64_t NCs = T / S;
   const int J = pick_J(NCs);
-  const int64_t nqt = (T + 63) / 64;
-  const int64_t ntiles = (int64_t)B * Hkv * nqt;
-  const int slots = (int)(ntiles < 2048 ? ntiles : 2048);
-  const int64_t stride = 64 * 64 * (int64_t)J;
-  if (n_slots) *n_slots = slots;
+  const int64_t stride = 64 * (int64_t)J;   // rank keys of one query
+  if (n_slots) *n_slots = (int)T;            // rows of one (b, group)
   if (slot_stride) *slot_stride = stride;
-  size_t bytes = (size_t)slots * stride * sizeof(float);
+  size_t bytes = (size_t)T * stride * sizeof(uint32_t);   // one (b, group) at a time
   if (Hq / Hkv > 1) bytes += (size_t)B * Hq * T * sizeof(float);
   return bytes + 256;
 }

@@ -14,9 +14,10 @@ namespace hils {
 namespace {
 
 const char* const kNames[K_COUNT] = {
-    "summarize", "score_lse", "rank_select", "idx_count", "idx_scan_tiles", "idx_scan_buckets",
+    "summarize", "score_lse", "idx_count", "idx_scan_tiles", "idx_scan_buckets",
     "idx_fill", "lsel", "window", "chunk_attend", "combine", "dec_score", "dec_select",
-    "dec_attend", "dec_fuse", "dec_summarize", "v_transpose", "q_group"};
+    "dec_attend", "dec_fuse", "dec_summarize", "v_transpose", "q_group", "rank_keys", "topk_rows",
+    "sel_scores"};
 
 struct Rec {
   int id;
