@@ -211,13 +211,16 @@ template <typename T> constexpr int rank_q() { return sizeof(T) == 2 ? 128 : 64;
 //              head's s_hat on every chosen chunk: a chunk's value is kept where
 //              the query's selection bitmap has it, at slot = number of chosen
 //              chunks below it (ids ascend).
-template <typename T, int D, int G>
+template <typename T, int D, int G, int RQ_ = rank_q<T>()>
 struct RankTiles {
   static constexpr int KS = D / 32;
   static constexpr int HW = (G + 3) / 4;   // heads per wave
-  static constexpr int RQ = rank_q<T>(), NT = RQ * 4;
+  static constexpr int RQ = RQ_, NT = RQ * 4;
   using Tile = KTile<T, D, G, NT>;
 };
+// The score pass on the choice holds more registers; 64 queries per workgroup
+// (4 waves) let three workgroups share a compute unit.
+constexpr int kSelQ = 64;
 
 template <typename T, int D, int G, int NCP>
 __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, int b, int g,
@@ -341,8 +344,8 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(SelArgs a, int b, int g,
 }
 
 template <typename T, int D, int G, int NCP>
-__global__ __launch_bounds__(rank_q<T>() * 4) void sel_scores_kernel(SelArgs a, int b, int g) {
-  using R = RankTiles<T, D, G>;
+__global__ __launch_bounds__(kSelQ * 4) void sel_scores_kernel(SelArgs a, int b, int g) {
+  using R = RankTiles<T, D, G, kSelQ>;
   constexpr int KS = R::KS, HW = R::HW, RQ = R::RQ, NT = R::NT;
   constexpr int BMP = NCP / 32 + 1;      // padded bitmap row (words)
   using Tile = typename R::Tile;
@@ -418,19 +421,22 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void sel_scores_kernel(SelArgs a, 
           load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
         const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
         const float bkv[4] = {bk.x, bk.y, bk.z, bk.w};
+        f32x4_t acc[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) mma(acc[rt], kf[ks], qf[u][rt][ks]);
+        }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const uint32_t mine = (seg[rt] >> (4 * grp)) & 0xfu;
-          if (__ballot(mine != 0u) == 0ull) continue;   // no chosen chunk in this 16 x 16 tile
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) mma(acc, kf[ks], qf[u][rt][ks]);
           const int64_t i = qw + 16 * rt + r16;
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             if (((mine >> q4) & 1u) && i < T_) {
               const int slot_t = below[rt] + __popc(seg[rt] & ((1u << (4 * grp + q4)) - 1u));
-              a.ssel[(((int64_t)b * Hq + h) * T_ + i) * topk + slot_t] = fmaf(acc[q4], a.scale, bkv[q4]);
+              a.ssel[(((int64_t)b * Hq + h) * T_ + i) * topk + slot_t] = fmaf(acc[rt][q4], a.scale, bkv[q4]);
             }
           }
         }
@@ -445,6 +451,7 @@ template <typename T, int D, int G, int J>
 hipError_t launch_rank_j(const SelArgs& a, hipStream_t st) {
   constexpr int RQ = rank_q<T>();
   const dim3 tiles((unsigned)((a.T + RQ - 1) / RQ)), rows((unsigned)((a.T + 3) / 4));
+  const dim3 stiles((unsigned)((a.T + kSelQ - 1) / kSelQ));
   uint32_t* keys = reinterpret_cast<uint32_t*>(a.scratch);
   for (int b = 0; b < a.B; ++b) {
     for (int g = 0; g < a.Hkv; ++g) {
@@ -457,7 +464,7 @@ hipError_t launch_rank_j(const SelArgs& a, hipStream_t st) {
         hipLaunchKernelGGL((topk_rows_kernel<J>), rows, dim3(256), 0, st, a, b, g, keys);
       }
       KTimer tm(K_SEL_SCORES, st);
-      hipLaunchKernelGGL((sel_scores_kernel<T, D, G, 64 * J>), tiles, dim3(RQ * 4), 0, st, a, b, g);
+      hipLaunchKernelGGL((sel_scores_kernel<T, D, G, 64 * J>), stiles, dim3(kSelQ * 4), 0, st, a, b, g);
     }
   }
   return hipGetLastError();
