@@ -90,10 +90,11 @@ def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
     return {
         "summarize": ("hbm", summary_bytes(B, Hq, Hkv, T, d, S, esz), "B"),
         "score_lse": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
-        "rank_keys": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
-        # the rank keys of every (query, group, candidate) read once
-        "topk_rows": ("hbm", B * Hkv * ncand * 4.0, "B"),
-        "sel_scores": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
+        # these three run once per (b, KV group): one group's share per launch
+        "rank_keys": ("mfma", G * ncand * 2.0 * d, "FLOP"),
+        # the rank keys of every (query, candidate) of the group read once
+        "topk_rows": ("hbm", ncand * 4.0, "B"),
+        "sel_scores": ("mfma", G * ncand * 2.0 * d, "FLOP"),
         # K and V^T of every chunk once per KV head; per (query, group, slot)
         # entry: the entry word, G rows of q and G chunk weights read, G weighted
         # partial rows written
