@@ -57,6 +57,7 @@ def summary_bytes(B, Hq, Hkv, T, d, S, esz=2):
 
 
 def decode_bytes(B, Hq, Hkv, d, S, W, k, positions, esz=2):
+    """HBM bytes of decode steps at the given cache positions, B sequences each."""
     tot = 0.0
     for i in positions:
         a = i - W + 1
@@ -67,7 +68,7 @@ def decode_bytes(B, Hq, Hkv, d, S, W, k, positions, esz=2):
         tot += Hkv * min(k, nc) * S * d * esz * 2        # selected chunks' K and V
         tot += Hkv * win * d * esz * 2                   # window K and V
         tot += Hq * d * esz * 3 + Hkv * d * esz * 2      # q, q_hat, out; k_new, v_new
-    return tot
+    return B * tot
 
 
 def selected_entries(B, Hkv, T, S, W, k):

@@ -202,8 +202,19 @@ __device__ __forceinline__ int swz(int r, int p) {
   return r * PPR + (p ^ (PPR >= 16 ? (r & 15) : ((r >> 1) & 7)));
 }
 
-// V^T of every chunk, [B, Hkv, ceil(T/S), D, S]; tokens past T are zero.  Lets the
-// attention kernels stage V^T tiles with plain 16-byte copies.
+// Token order inside a chunk's V^T row.  The P operand of O^T += V^T P^T comes
+// straight from the S^T tile, whose lane holds tokens 16*mt + 4*grp + i
+// (i < 4) for mt = 2*k2 and 2*k2 + 1 in the k2-th 32-token step; storing those
+// eight tokens next to each other at 32*k2 + 8*grp makes each V^T operand one
+// 16-byte read.
+__device__ __forceinline__ int vt_token(int pos) {
+  const int k2 = pos >> 5, grp = (pos >> 3) & 3, h = (pos >> 2) & 1, i = pos & 3;
+  return 16 * (2 * k2 + h) + 4 * grp + i;
+}
+
+// V^T of every chunk, [B, Hkv, ceil(T/S), D, S] with the tokens of a row in
+// vt_token order; tokens past T are zero.  Lets the attention kernels stage V^T
+// tiles with plain 16-byte copies.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, T* __restrict__ vt, int Hkv,
                                                  int64_t T_, int64_t NCf) {
@@ -225,7 +236,7 @@ __global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, T* __r
     const int drow = e / (kS / EPV), q = e % (kS / EPV);
     T x[EPV];
 #pragma unroll
-    for (int t = 0; t < EPV; ++t) x[t] = tile[(q * EPV + t) * VP + drow];
+    for (int t = 0; t < EPV; ++t) x[t] = tile[vt_token(q * EPV + t) * VP + drow];
     *reinterpret_cast<uint4*>(dst + (int64_t)drow * kS + q * EPV) = *reinterpret_cast<const uint4*>(x);
   }
 }
@@ -282,21 +293,6 @@ __device__ __forceinline__ void load_frag_swz(Frag<float>& f, const float* tile,
   f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
   f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
 }
-// Two runs of 4 elements (logical columns t0.., t1.., multiples of 4).
-template <int PPR>
-__device__ __forceinline__ void load_frag2x4_swz(Frag<bf16_t>& f, const bf16_t* tile, int row, int t0, int t1) {
-  const uint2 x = *reinterpret_cast<const uint2*>(tile + swz<PPR>(row, t0 / 8) * 8 + (t0 & 7));
-  const uint2 y = *reinterpret_cast<const uint2*>(tile + swz<PPR>(row, t1 / 8) * 8 + (t1 & 7));
-  f.v = __builtin_bit_cast(bf16x8_t, make_uint4(x.x, x.y, y.x, y.y));
-}
-template <int PPR>
-__device__ __forceinline__ void load_frag2x4_swz(Frag<float>& f, const float* tile, int row, int t0, int t1) {
-  const float4 x = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, t0 / 4) * 4);
-  const float4 y = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, t1 / 4) * 4);
-  f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
-  f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
-}
-
 // S^T tile (64 tokens x 16 rows) for one row-fragment set bq[KS]; acc[mt][i] is the
 // logit of token 16*mt + 4*grp + i for row lane%16.
 template <typename T, int D>
@@ -336,7 +332,7 @@ __device__ __forceinline__ void pv_tile(const T* vt, const float (&p)[4][4], f32
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       Frag<T> af;
-      load_frag2x4_swz<PV>(af, vt, 16 * md + r16, 32 * k2 + 4 * grp, 32 * k2 + 16 + 4 * grp);
+      load_frag_swz<PV>(af, vt, 16 * md + r16, 32 * k2 + 8 * grp);
       mma(o[md], af, pf[k2]);
     }
   }
@@ -370,6 +366,8 @@ __device__ __forceinline__ void load4_add<float>(f32x4_t& acc, const float* p) {
   acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
 }
 
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct ChunkArgs {
   const void* qg;   // q regrouped, [B, Hkv, T, G, D]
@@ -489,8 +487,9 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
         const int64_t ri = wr >> 6;
         const int rs = wr & 63;
         T* prow = part + (((((int64_t)b * a.gpass + (g - a.g0)) * a.T + ri) * a.topk + rs) * G + rh) * D;
-        *reinterpret_cast<uint4*>(prow + piece * EPV) =
-            *reinterpret_cast<const uint4*>(myo + r * OP + piece * EPV);
+        // streamed out: the combine pass reads each partial row once, much later
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(myo + r * OP + piece * EPV),
+                                    reinterpret_cast<u32x4*>(prow + piece * EPV));
       }
     }
     wave_lds_sync();
@@ -516,6 +515,8 @@ struct WinArgs {
 template <int N> using u32v = uint32_t __attribute__((ext_vector_type(N)));
 
 constexpr int kWinThreads = 512;
+constexpr float kRefLog2 = -1e30f;   // initial softmax reference (log2 domain)
+constexpr float kLazyLog2 = 8.f;     // headroom before the reference must move
 
 // Window attention, query-major and dense (flash style).  A workgroup has 8 waves;
 // a wave owns one 16-row MFMA tile of (query, head) rows, the block 128 rows, so
@@ -523,7 +524,7 @@ constexpr int kWinThreads = 512;
 // loaded into registers (held as one vector value) while this chunk computes.
 // Chunks fully inside every row's window skip the mask.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kWinThreads) void window_kernel(WinArgs a) {
+__device__ __forceinline__ void window_body(const WinArgs& a) {
   constexpr int KS = D / 32, MD = D / 16;
   constexpr int EPV = 16 / sizeof(T);
   constexpr int PK = D / EPV, PV = kS / EPV;              // 16-byte pieces per K / V^T row
@@ -555,7 +556,9 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(WinArgs a) {
 #pragma unroll
     for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
   }
-  float m = kNegInf, ls = 0.f;
+  // Running reference in the log2 domain: finite, far below any logit, so the
+  // first chunk with an unmasked token always moves it.
+  float m = kRefLog2, ls = 0.f;
   f32x4_t o[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md) o[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -610,16 +613,7 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(WinArgs a) {
     const bool full = j0 >= lw_max && j0 + kS - 1 <= qb0;
     f32x4_t acc[4];
     score_tile<T, D>(ks, bq, acc, r16, grp);
-    float x[4][4], mx = kNegInf;
-    if (full) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          x[mt][q4] = acc[mt][q4] * sl2;
-          mx = fmaxf(mx, x[mt][q4]);
-        }
-    } else {
+    if (!full) {
       const int lo = (int)max<int64_t>(lw - j0, -1);
       const int hi = i < T_ ? (int)min<int64_t>(i - j0, kS) : -1;
 #pragma unroll
@@ -627,33 +621,38 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(WinArgs a) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int t = 16 * mt + 4 * grp + q4;
-          x[mt][q4] = (t >= lo && t <= hi) ? acc[mt][q4] * sl2 : kNegInf;
-          mx = fmaxf(mx, x[mt][q4]);
+          if (t < lo || t > hi) acc[mt][q4] = kNegInf;
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float mn = fmaxf(m, mx);
-    float p[4][4], psum = 0.f;
-    if (mn == kNegInf) {
+    // Lazy rescaling: the running reference m moves only when some logit of the
+    // wave exceeds it by more than kLazyLog2, so p = 2^(x - m) stays below
+    // 2^kLazyLog2 and the usual per-chunk max exchange and O rescale are skipped
+    // while the row maxima settle.  The final log-mass m + log2(l) is exact for
+    // any m.  (sl2 > 0, so the max of the raw logits picks the max of x.)
+    float mx = kNegInf;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) p[mt][q4] = 0.f;
-    } else {
-      const float alpha = hw_exp2(m - mn);   // 0 when m was -inf
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          p[mt][q4] = hw_exp2(x[mt][q4] - mn);
-          psum += p[mt][q4];
-        }
-      ls = ls * alpha + psum;
+      for (int q4 = 0; q4 < 4; ++q4) mx = fmaxf(mx, acc[mt][q4]);
+    mx *= sl2;
+    if (__any(mx > m + kLazyLog2)) {
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mn = fmaxf(m, mx);
+      const float alpha = hw_exp2(m - mn);   // 0 while m is still kRefLog2
+      ls *= alpha;
 #pragma unroll
       for (int md = 0; md < MD; ++md) o[md] *= alpha;
       m = mn;
     }
+    float p[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        p[mt][q4] = hw_exp2(fmaf(acc[mt][q4], sl2, -m));   // masked: 2^-inf = 0
+        ls += p[mt][q4];
+      }
     pv_tile<T, D>(vt, p, o, r16, grp);
   }
   float lsum = ls;
@@ -666,6 +665,17 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel(WinArgs a) {
 #pragma unroll
   for (int md = 0; md < MD; ++md) store4<T>(owp + rowq * D + 16 * md + 4 * grp, o[md], inv);
   if (grp == 0) a.lzw[rowq] = (m + hw_log2(lsum)) * kLn2;
+}
+
+// bf16 tiles fit 128 VGPRs, so two workgroups share a compute unit and their
+// barriers interleave; fp32 operands need the full register file.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kWinThreads) __attribute__((amdgpu_waves_per_eu(4))) void window_kernel(WinArgs a) {
+  window_body<T, D, G>(a);
+}
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kWinThreads) void window_kernel_f32(WinArgs a) {
+  window_body<T, D, G>(a);
 }
 
 struct CombArgs {
@@ -774,8 +784,11 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
     WinArgs wa{a.q, a.k, vt, ow, lzw, a.B, a.Hq, a.Hkv, a.S, a.W, a.T, NCf, a.scale};
     const int QB = 8 * (16 / G);
     KTimer tm(K_WINDOW, st);
-    hipLaunchKernelGGL((window_kernel<T, D, G>), dim3((unsigned)((a.T + QB - 1) / QB), a.Hkv, a.B),
-                       dim3(kWinThreads), 0, st, wa);
+    const dim3 grid((unsigned)((a.T + QB - 1) / QB), a.Hkv, a.B);
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((window_kernel<T, D, G>), grid, dim3(kWinThreads), 0, st, wa);
+    else
+      hipLaunchKernelGGL((window_kernel_f32<T, D, G>), grid, dim3(kWinThreads), 0, st, wa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
