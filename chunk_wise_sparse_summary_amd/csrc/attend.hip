@@ -192,16 +192,6 @@ __global__ __launch_bounds__(256) void lsel_kernel(IdxArgs a, int L) {
   }
 }
 
-// LDS tiles of one chunk: K as [kS][D] and V^T as [D][kS], unpadded, with the
-// 16-byte pieces of each row XOR-swizzled so that the 16 rows an MFMA operand
-// read touches at one logical column land in distinct banks (rows of >= 256
-// bytes: swizzle by row mod 16; rows of 128 bytes: by (row / 2) mod 8, since two
-// consecutive rows already split the banks).
-template <int PPR>
-__device__ __forceinline__ int swz(int r, int p) {
-  return r * PPR + (p ^ (PPR >= 16 ? (r & 15) : ((r >> 1) & 7)));
-}
-
 // Token order inside a chunk's V^T row.  The P operand of O^T += V^T P^T comes
 // straight from the S^T tile, whose lane holds tokens 16*mt + 4*grp + i
 // (i < 4) for mt = 2*k2 and 2*k2 + 1 in the k2-th 32-token step; storing those
@@ -280,19 +270,6 @@ __device__ __forceinline__ void stage_chunk(const T* kc, const T* vtc, T* ks, T*
   }
 }
 
-// Operand fragment of 8 consecutive elements (logical column col, a multiple of
-// 8) of row `row` of a swizzled tile.
-template <int PPR>
-__device__ __forceinline__ void load_frag_swz(Frag<bf16_t>& f, const bf16_t* tile, int row, int col) {
-  f.v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(tile + swz<PPR>(row, col / 8) * 8));
-}
-template <int PPR>
-__device__ __forceinline__ void load_frag_swz(Frag<float>& f, const float* tile, int row, int col) {
-  const float4 x = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, col / 4) * 4);
-  const float4 y = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, col / 4 + 1) * 4);
-  f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
-  f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
-}
 // S^T tile (64 tokens x 16 rows) for one row-fragment set bq[KS]; acc[mt][i] is the
 // logit of token 16*mt + 4*grp + i for row lane%16.
 template <typename T, int D>

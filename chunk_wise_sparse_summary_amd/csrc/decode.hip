@@ -14,11 +14,12 @@
 //               key, per-wave top-k lists in LDS, their merged top-k ascending,
 //               and each head's s_hat on it.
 //   dec_attend  one workgroup per (b, group, work item), an item being a selected
-//               chunk or a window chunk.  The chunk's K and V are staged once in
-//               LDS for all G heads; wave h computes head h's 64 logits, softmax
-//               statistics and o = sum p v.
-//   dec_fuse    one wave per (b, head): L = LSE(s_hat over Sel + {log Z_win}),
-//               out = sum exp(s_hat_c - L) o_c + exp(log Z_win - L) o_win.
+//               chunk or a window chunk: the G heads are the columns of MFMA
+//               tiles for the logits and for o = sum p v; the item's partial is
+//               its log-weight (s_hat for a selected chunk, the token-level
+//               log-mass for a window chunk) and its normalised output.
+//   dec_fuse    one wave per (b, head): the exp(log-weight) average of the
+//               items' outputs and L = LSE(s_hat over Sel + {log Z_win}).
 //   summarize   (list mode) chunks completed by this step's token.
 // Stages hand over through kernel boundaries: a device-wide fence per block (a
 // last-block ticket) costs an L2 write-back on a multi-XCD part.
@@ -41,7 +42,7 @@ struct DecWs {
   float2* lpart;      // [B, Hq, nslice] (max, sum) in log2 units
   int32_t* idx;       // [B, Hkv, topk]
   float* ssel;        // [B, Hq, topk]
-  float* apart;       // [B, Hkv, nitems, G, D + 2]
+  float* apart;       // [B, Hkv, nitems, G, D + 2] per item: normalised output, log-weight
   int nslice, selj, nitems;
 };
 
@@ -295,103 +296,159 @@ __global__ __launch_bounds__(64 * kSelWaves) void dec_select_kernel(DecKArgs a) 
     if (lane >= base && lane < topk) emit(lane, -1);
     return;
   }
+  // Each list holds at most TP = topk rounded up to a power of two entries, so
+  // lane + 64 j carries entry lane % TP of list LPJ j + lane / TP: with several
+  // lists per lane row the lane maxima span more keys, and the first bound of
+  // wave_topk_u32 leaves few enough keys for its one-pass path.  The numbering
+  // ascends with (list, entry), that is with the chunk.
+  const int TP = topk <= 16 ? 16 : (topk <= 32 ? 32 : 64);
+  const int LPJ = kWave / TP;
+  const int ml = lane / TP, me = lane % TP;
   uint32_t keys[JM];
 #pragma unroll
-  for (int w = 0; w < JM; ++w) keys[w] = lane < nlist[w] ? lkey[w][lane] : 0u;   // position w*64 + lane
-  // wave_topk_u32 numbers candidates lane + 64*j, here j = list, so its ascending
-  // ids are (list, rank in list) in ascending chunk order only after a remap:
-  // translate each chosen id back through lid.
-  wave_topk_u32<JM>(keys, JM, topk, lane, sbuf[0], wsel[0]);
+  for (int j = 0; j < JM; ++j) {
+    const int w = LPJ * j + ml;
+    keys[j] = (w < kSelWaves && me < nlist[w]) ? lkey[w][me] : 0u;
+  }
+  wave_topk_u32<JM>(keys, (kSelWaves + LPJ - 1) / LPJ, topk, lane, sbuf[0], wsel[0]);
   wave_lds_sync();
   if (lane < topk) {
     const int id = wsel[0][lane];
-    emit(lane, lid[id / 64][id % 64]);
+    const int l = id % 64;
+    emit(lane, lid[LPJ * (id / 64) + l / TP][l % TP]);
   }
 }
 
 // Work item j < nsel: selected chunk idx[j]; else window chunk l_i/S + (j - nsel).
+// One workgroup per (b, group, item), so that every item's loads are in flight
+// at once.  The G heads of the group are the 16 columns of MFMA tiles
+// (zero-padded): wave w takes the logits of tokens 16w .. 16w + 15 (S^T = K Q^T,
+// its K fragments loaded straight from HBM), the softmax statistics of each head
+// meet in LDS, V goes transposed into LDS, and O^T = V^T P^T gives wave w the
+// output dims 16(w + 4t) ...  The item's partial is its log-weight (s_hat for a
+// selected chunk, the token-level log-mass for a window chunk) and its
+// normalised output.
+constexpr int kAttThreads = 256;
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * G) void dec_attend_kernel(DecKArgs a) {
-  constexpr int NT = 64 * G;
+__global__ __launch_bounds__(kAttThreads) void dec_attend_kernel(DecKArgs a) {
   constexpr int EPV = 16 / sizeof(T);
-  constexpr int DPL = D / kWave;           // dims per lane (2 for d=128)
-  constexpr int KP = D + 16 / (int)sizeof(T);
-  __shared__ __align__(16) T ks[kS * KP];
-  __shared__ __align__(16) T vs[kS * D];
-  __shared__ float ps[G][kS];
-  __shared__ float qs[G][D];
+  constexpr int KS = D / 32, MD = D / 16;
+  constexpr int PK = D / EPV, PV = kS / EPV;         // 16-byte pieces per K / V^T row
+  constexpr int VPW = PK / 4;                        // V pieces per lane (wave w: pieces w*VPW ..)
+  constexpr int MDW = MD / 4;                        // output dim tiles per wave
+  static_assert(G <= 16 && PK % 4 == 0 && MD % 4 == 0, "tiling");
+  __shared__ __align__(16) T vt[D * kS];     // V^T rows, swizzled
+  __shared__ __align__(16) T pt[16 * kS];    // P^T as [head][token]
+  __shared__ float red[2][4][16];            // per-wave head max and sum
   const int item = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r16 = lane % 16, grp = lane / 16;
   const int64_t i = a.pos.p[b];
   const int64_t lw = window_left(i, a.S, a.W);
   const int64_t nc = lw / kS;
   const int nsel = (int)min<int64_t>(nc, a.topk);
   const int nwin = (int)(i / kS - lw / kS + 1);
-  const int nitems = nsel + nwin;
-  if (item >= nitems) return;
+  if (item >= nsel + nwin) return;
   const int64_t bg = (int64_t)b * a.Hkv + g;
-  const int h = g * G + wave;
-  int64_t c;
-  bool is_win;
-  if (item < nsel) {
-    c = a.w.idx[bg * a.topk + item];
-    is_win = false;
-  } else {
-    c = lw / kS + (item - nsel);
-    is_win = true;
-  }
+  const float sl2 = a.scale * kLog2e;
+  const bool hcol = r16 < G;                 // this lane's column is a real head
+  const int h = g * G + (hcol ? r16 : 0);
+  const bool is_win = item >= nsel;
+  const int64_t c = is_win ? lw / kS + (item - nsel) : (int64_t)a.w.idx[bg * a.topk + item];
   const T* kc = static_cast<const T*>(a.kc) + (bg * a.Lcap + c * kS) * D;
   const T* vc = static_cast<const T*>(a.vc) + (bg * a.Lcap + c * kS) * D;
-  for (int e = threadIdx.x * EPV; e < kS * D; e += NT * EPV) {
-    const int row = e / D, col = e % D;
-    *reinterpret_cast<uint4*>(ks + row * KP + col) = *reinterpret_cast<const uint4*>(kc + e);
-    *reinterpret_cast<uint4*>(vs + e) = *reinterpret_cast<const uint4*>(vc + e);
-  }
+
+  // every load up front: K fragments (row = token 16 wave + r16), V pieces
+  // (token = lane), Q^T fragments (column r16 = head)
+  Frag<T> kf[KS], bq[KS];
+#pragma unroll
+  for (int kq = 0; kq < KS; ++kq) load_frag(kf[kq], kc + (int64_t)(16 * wave + r16) * D + 8 * grp + 32 * kq);
+  uint4 vr[VPW];
+#pragma unroll
+  for (int t = 0; t < VPW; ++t) vr[t] = *reinterpret_cast<const uint4*>(vc + (int64_t)lane * D + (wave * VPW + t) * EPV);
   {
-    const T* qv = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + h) * D;
-    for (int e = lane; e < D; e += kWave) qs[wave][e] = to_f<T>(qv[e]);
+    const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + h) * D + 8 * grp;
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) {
+      if (hcol) load_frag(bq[kq], qrow + 32 * kq);
+      else zero_frag(bq[kq]);
+    }
+  }
+  const float lnw_sel = (!is_win && hcol) ? a.w.ssel[((int64_t)b * a.Hq + h) * a.topk + item] : 0.f;
+
+  // S^T tile of tokens 16 wave + (4 grp + q4), column r16
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kq = 0; kq < KS; ++kq) mma(acc, kf[kq], bq[kq]);
+  float x[4], mx = kNegInf;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int64_t j = c * kS + 16 * wave + 4 * grp + q4;
+    const bool ok = !is_win || (j >= lw && j <= i);
+    x[q4] = ok ? acc[q4] * sl2 : kNegInf;
+    mx = fmaxf(mx, x[q4]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  if (grp == 0) red[0][wave][r16] = mx;
+  // V transposed into LDS: row d, token = lane
+#pragma unroll
+  for (int t = 0; t < VPW; ++t) {
+    const T* xv = reinterpret_cast<const T*>(&vr[t]);
+    const int d0 = (wave * VPW + t) * EPV;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) vt[swz<PV>(d0 + e, lane / EPV) * EPV + lane % EPV] = xv[e];
   }
   __syncthreads();
-  // logits: lane = token
-  const int64_t j = c * kS + lane;
-  const bool ok = !is_win || (j >= lw && j <= i);
-  float s = kNegInf;
-  if (ok) {
-    float acc = 0.f;
+  const float m = fmaxf(fmaxf(red[0][0][r16], red[0][1][r16]), fmaxf(red[0][2][r16], red[0][3][r16]));
+  float p[4], ps = 0.f;
 #pragma unroll
-    for (int e0 = 0; e0 < D; e0 += EPV) {
-      const uint4 u = *reinterpret_cast<const uint4*>(ks + lane * KP + e0);
-      const T* t = reinterpret_cast<const T*>(&u);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) acc = fmaf(qs[wave][e0 + e], to_f<T>(t[e]), acc);
-    }
-    s = acc * (a.scale * kLog2e);
+  for (int q4 = 0; q4 < 4; ++q4) {
+    p[q4] = hw_exp2(x[q4] - m);   // every head has an unmasked token in every item
+    ps += p[q4];
   }
-  const float m = wave_max(s);
-  const float p = ok ? hw_exp2(s - m) : 0.f;
-  const float l = wave_sum(p);
-  ps[wave][lane] = p;
-  wave_lds_sync();
-  float o[DPL];
+  ps += __shfl_xor(ps, 16, kWave);
+  ps += __shfl_xor(ps, 32, kWave);
+  if (grp == 0) red[1][wave][r16] = ps;
+  {
+    T* prow = pt + r16 * kS + 16 * wave + 4 * grp;
 #pragma unroll
-  for (int t = 0; t < DPL; ++t) o[t] = 0.f;
-#pragma unroll 8
-  for (int jj = 0; jj < kS; ++jj) {
-    const float pj = ps[wave][jj];
-    const T* vr = vs + jj * D + lane * DPL;
-#pragma unroll
-    for (int t = 0; t < DPL; ++t) o[t] = fmaf(pj, to_f<T>(vr[t]), o[t]);
+    for (int q4 = 0; q4 < 4; ++q4) prow[q4] = from_f<T>(p[q4]);
   }
-  float* ap = a.w.apart + ((bg * a.w.nitems + item) * G + wave) * (D + 2);
-#pragma unroll
-  for (int t = 0; t < DPL; ++t) ap[lane * DPL + t] = o[t];
-  if (lane == 0) { ap[D] = m; ap[D + 1] = l; }
+  __syncthreads();
+  const float l = (red[1][0][r16] + red[1][1][r16]) + (red[1][2][r16] + red[1][3][r16]);
 
+  // O^T tiles: dims 16 md + 4 grp + q4, column r16
+  f32x4_t o[MDW];
+#pragma unroll
+  for (int t = 0; t < MDW; ++t) {
+    const int md = wave + 4 * t;
+    o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < kS / 32; ++k2) {
+      Frag<T> af, pf;
+      load_frag_swz<PV>(af, vt, 16 * md + r16, 8 * grp + 32 * k2);
+      load_frag(pf, pt + r16 * kS + 8 * grp + 32 * k2);
+      mma(o[t], af, pf);
+    }
+  }
+  // partial: log-weight (natural log) and the normalised output
+  if (hcol) {
+    float* ap = a.w.apart + ((bg * a.w.nitems + item) * G + r16) * (D + 2);
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int t = 0; t < MDW; ++t)
+      *reinterpret_cast<float4*>(ap + 16 * (wave + 4 * t) + 4 * grp) =
+          make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
+    if (wave == 0 && grp == 0) ap[D] = is_win ? (m + hw_log2(l)) * kLn2 : lnw_sel;
+  }
 }
 
-// One wave per (b, query head): fuse the window items (token level) and the
-// selected chunks (weights exp(s_hat - L)).  Lanes own items for the statistics;
-// the weighted sum over items then runs with independent loads.
+// One wave per (b, query head): the output is the average of the items'
+// normalised outputs weighted by exp(log-weight), and L the log of the total
+// weight (the LSE over the selected chunks' s_hat and the window's log-mass).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(64) void dec_fuse_kernel(DecKArgs a) {
   constexpr int DPL = D / kWave;
@@ -404,41 +461,17 @@ __global__ __launch_bounds__(64) void dec_fuse_kernel(DecKArgs a) {
   const int nsel = (int)min<int64_t>(lw / kS, a.topk);
   const int nitems = nsel + (int)(i / kS - lw / kS + 1);   // <= 256 (checked on the host)
   const int64_t bg = (int64_t)b * a.Hkv + g;
-  const float* ap = a.w.apart + (bg * a.w.nitems) * G * (D + 2);
-  const float* ss = a.w.ssel + ((int64_t)b * a.Hq + h) * a.topk;
-  auto mstat = [&](int it) { return ap[((int64_t)it * G + hl) * (D + 2) + D]; };
-  auto lstat = [&](int it) { return ap[((int64_t)it * G + hl) * (D + 2) + D + 1]; };
-  // window: token-level mass of all window items
-  float Mw = kNegInf;
-  for (int it = nsel + lane; it < nitems; it += kWave) Mw = fmaxf(Mw, mstat(it));
-  Mw = wave_max(Mw);
-  float lw_part = 0.f;
-  for (int it = nsel + lane; it < nitems; it += kWave) {
-    const float mi = mstat(it);
-    if (mi != kNegInf) lw_part += hw_exp2(mi - Mw) * lstat(it);
-  }
-  const float lwin = wave_sum(lw_part);
-  const float logzw = (Mw + hw_log2(lwin)) * kLn2;
-  // normaliser over the selected chunks' s_hat and the window's log-mass
-  float mx = logzw;
-  for (int it = lane; it < nsel; it += kWave) mx = fmaxf(mx, ss[it]);
+  const float* ap = a.w.apart + (bg * a.w.nitems * G + hl) * (D + 2);
+  float mx = kNegInf;
+  for (int it = lane; it < nitems; it += kWave) mx = fmaxf(mx, ap[(int64_t)it * G * (D + 2) + D]);
   mx = wave_max(mx);
   float z = 0.f;
-  for (int it = lane; it < nsel; it += kWave) z += __expf(ss[it] - mx);
-  z = wave_sum(z) + __expf(logzw - mx);
-  const float L = mx + __logf(z);
-  // per-item weights on the unnormalised o of each item
-  const float fw = __expf(logzw - L) / lwin;
   for (int it = lane; it < nitems; it += kWave) {
-    float w;
-    if (it < nsel) {
-      w = __expf(ss[it] - L) / lstat(it);
-    } else {
-      const float mi = mstat(it);
-      w = mi == kNegInf ? 0.f : hw_exp2(mi - Mw) * fw;
-    }
+    const float w = __expf(ap[(int64_t)it * G * (D + 2) + D] - mx);
     wts[it] = w;
+    z += w;
   }
+  z = wave_sum(z);
   wave_lds_sync();
   float res[DPL];
 #pragma unroll
@@ -446,14 +479,15 @@ __global__ __launch_bounds__(64) void dec_fuse_kernel(DecKArgs a) {
 #pragma unroll 4
   for (int it = 0; it < nitems; ++it) {
     const float w = wts[it];
-    const float* pp = ap + ((int64_t)it * G + hl) * (D + 2) + lane * DPL;
+    const float* pp = ap + (int64_t)it * G * (D + 2) + lane * DPL;
 #pragma unroll
     for (int t = 0; t < DPL; ++t) res[t] = fmaf(w, pp[t], res[t]);
   }
+  const float inv = 1.f / z;
   T* orow = static_cast<T*>(a.out) + ((int64_t)b * a.Hq + h) * D;
 #pragma unroll
-  for (int t = 0; t < DPL; ++t) orow[lane * DPL + t] = from_f<T>(res[t]);
-  if (a.lse && lane == 0) a.lse[(int64_t)b * a.Hq + h] = L;
+  for (int t = 0; t < DPL; ++t) orow[lane * DPL + t] = from_f<T>(res[t] * inv);
+  if (a.lse && lane == 0) a.lse[(int64_t)b * a.Hq + h] = mx + __logf(z);
 }
 
 // Candidates per selection wave: 64*J with kSelWaves waves covering every candidate.
@@ -487,7 +521,7 @@ hipError_t launch_decode_tg(const DecKArgs& k, hipStream_t st) {
   if (k.topk > 0) launch_select_j<G>(k, st);
   {
     KTimer tm(K_DEC_ATTEND, st);
-    hipLaunchKernelGGL((dec_attend_kernel<T, D, G>), dim3(k.w.nitems, k.Hkv, k.B), dim3(64 * G), 0, st, k);
+    hipLaunchKernelGGL((dec_attend_kernel<T, D, G>), dim3(k.w.nitems, k.Hkv, k.B), dim3(kAttThreads), 0, st, k);
   }
   {
     KTimer tm(K_DEC_FUSE, st);

@@ -123,6 +123,29 @@ __device__ __forceinline__ float dot_row(const T* a, const T* b) {
   return acc;
 }
 
+// LDS tiles of one chunk: K as [kS][D] and V^T as [D][kS], unpadded, with the
+// 16-byte pieces of each row XOR-swizzled so that the 16 rows an MFMA operand
+// read touches at one logical column land in distinct banks (rows of >= 256
+// bytes: swizzle by row mod 16; rows of 128 bytes: by (row / 2) mod 8, since two
+// consecutive rows already split the banks).
+template <int PPR>
+__device__ __forceinline__ int swz(int r, int p) {
+  return r * PPR + (p ^ (PPR >= 16 ? (r & 15) : ((r >> 1) & 7)));
+}
+
+// Operand fragment of 8 consecutive elements (logical column col, a multiple of
+// 8) of row `row` of a swizzled tile.
+template <int PPR>
+__device__ __forceinline__ void load_frag_swz(Frag<bf16_t>& f, const bf16_t* tile, int row, int col) {
+  f.v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(tile + swz<PPR>(row, col / 8) * 8));
+}
+template <int PPR>
+__device__ __forceinline__ void load_frag_swz(Frag<float>& f, const float* tile, int row, int col) {
+  const float4 x = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, col / 4) * 4);
+  const float4 y = *reinterpret_cast<const float4*>(tile + swz<PPR>(row, col / 4 + 1) * 4);
+  f.v[0] = x.x; f.v[1] = x.y; f.v[2] = x.z; f.v[3] = x.w;
+  f.v[4] = y.x; f.v[5] = y.y; f.v[6] = y.z; f.v[7] = y.w;
+}
 // Wave-wide reductions (64 lanes).
 // x from lane (lane ^ M).  Masks below 16 stay inside a 16-lane row and use DPP
 // moves (quad permutes for 1 and 2, a row rotation by 8 for 8, and the two row
