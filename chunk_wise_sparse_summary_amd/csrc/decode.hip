@@ -202,6 +202,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void dec_select_kernel(DecKArgs a) 
   __shared__ float Ls[G];
   __shared__ uint32_t lkey[kSelWaves][64];
   __shared__ int32_t lid[kSelWaves][64];
+  __shared__ float lsv[kSelWaves][64][G];   // each listed candidate's s_hat per head
   __shared__ int32_t wsel[kSelWaves][64];
   __shared__ uint32_t sbuf[kSelWaves][64];
   __shared__ int nlist[kSelWaves];
@@ -213,22 +214,39 @@ __global__ __launch_bounds__(64 * kSelWaves) void dec_select_kernel(DecKArgs a) 
   const int topk = a.topk;
   const int64_t bg = (int64_t)b * a.Hkv + g;
   auto shat = [&](int hh, int64_t c) { return a.w.shat[((int64_t)b * a.Hq + g * G + hh) * a.NCcap + c]; };
-  auto rank_key = [&](int64_t c) {
-    float r = kNegInf;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) r = G > 1 ? fmaxf(r, shat(hh, c) - Ls[hh]) : shat(hh, c);
-    return order_key(r);
-  };
-  auto emit = [&](int t, int32_t c) {   // output slot t (< topk) holds chunk c (-1: none)
+  // output slot t (< topk) holds chunk c (-1: none) with scores sv[0..G)
+  auto emit = [&](int t, int32_t c, const float* sv) {
     a.w.idx[bg * topk + t] = c;
     if (a.idx_out) a.idx_out[bg * topk + t] = c;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
-      a.w.ssel[((int64_t)b * a.Hq + g * G + hh) * topk + t] = c >= 0 ? shat(hh, c) : kNegInf;
+      a.w.ssel[((int64_t)b * a.Hq + g * G + hh) * topk + t] = c >= 0 ? sv[hh] : kNegInf;
   };
   if (nc <= topk) {
-    if (wave == 0 && lane < topk) emit(lane, lane < nc ? lane : -1);
+    if (wave == 0 && lane < topk) {
+      float sv[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) sv[hh] = lane < nc ? shat(hh, lane) : kNegInf;
+      emit(lane, lane < nc ? lane : -1, sv);
+    }
     return;
+  }
+  // this wave's candidates c = cw + lane + 64 j.  With few enough per lane their
+  // scores are loaded first, so that the loads overlap the L_h merge below, and
+  // stay in registers; otherwise they are loaded in batches after it.
+  constexpr bool kHold = J * G <= 64 && J <= 16;
+  constexpr int JH = kHold ? J : 1;
+  const int64_t cw = (int64_t)wave * 64 * J;
+  const int cnt = (int)max<int64_t>(0, min<int64_t>(nc - cw, 64 * J));
+  const int jn = (cnt + 63) / 64;
+  float sv[G][JH];
+  if constexpr (kHold) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t c = min<int64_t>(cw + lane + 64 * j, nc - 1);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) sv[hh][j] = j < jn ? shat(hh, c) : 0.f;
+    }
   }
   if (G > 1) {
     if (wave < G) {   // wave hh: L_h from the slice partials, lanes over slices
@@ -242,41 +260,64 @@ __global__ __launch_bounds__(64 * kSelWaves) void dec_select_kernel(DecKArgs a) 
     }
     __syncthreads();
   }
-  // ---- per-wave exact top-k over its candidate range
-  const int64_t cw = (int64_t)wave * 64 * J;
-  const int cnt = (int)max<int64_t>(0, min<int64_t>(nc - cw, 64 * J));
+  uint32_t keys[J];
+  constexpr int JB = kHold ? J : (32 / G > 0 ? 32 / G : 1);   // keys per batch of loads
+#pragma unroll
+  for (int j0 = 0; j0 < J; j0 += JB) {
+    float xb[G][JB];
+    if constexpr (!kHold) {   // the batch's score loads first (clamped in range)
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+          xb[hh][j] = j0 + j < jn ? shat(hh, min<int64_t>(cw + lane + 64 * (j0 + j), nc - 1)) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      float r = kNegInf;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float x = kHold ? sv[hh][j0 + j] : xb[hh][j];
+        r = G > 1 ? fmaxf(r, x - Ls[hh]) : x;
+      }
+      keys[j0 + j] = (j0 + j < jn && cw + lane + 64 * (j0 + j) < nc) ? order_key(r) : 0u;
+    }
+  }
+  // ---- per-wave exact top-k over its candidate range, with the scores of the
+  // listed candidates gathered from the lanes that hold them
   int n = 0;
   if (cnt > topk) {
-    const int jn = (cnt + 63) / 64;
-    uint32_t keys[J];
-    constexpr int JB = (J * G <= 32) ? J : (32 / G > 0 ? 32 / G : 1);   // keys per batch of loads
-#pragma unroll
-    for (int j0 = 0; j0 < J; j0 += JB) {
-      // the batch's score loads first (clamped in range), then its keys
-      float sv[G][JB];
-#pragma unroll
-      for (int j = 0; j < JB; ++j) {
-        const int64_t c = min<int64_t>(cw + lane + 64 * (j0 + j), nc - 1);
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) sv[hh][j] = j0 + j < jn ? shat(hh, c) : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < JB; ++j) {
-        float r = kNegInf;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) r = G > 1 ? fmaxf(r, sv[hh][j] - Ls[hh]) : sv[hh][j];
-        keys[j0 + j] = (j0 + j < jn && cw + lane + 64 * (j0 + j) < nc) ? order_key(r) : 0u;
-      }
-    }
     wave_topk_u32<J>(keys, jn, topk, lane, sbuf[wave], wsel[wave], lkey[wave]);
     n = topk;
     wave_lds_sync();
-    if (lane < n) lid[wave][lane] = (int32_t)(cw + wsel[wave][lane]);
+    const int id = lane < n ? wsel[wave][lane] : 0;
+    if constexpr (kHold) {
+      const int src = id % 64, jj = id / 64;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const float x = __shfl(sv[hh][j], src, kWave);
+          if (j == jj) v = x;
+        }
+        if (lane < n) lsv[wave][lane][hh] = v;
+      }
+    } else if (lane < n) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) lsv[wave][lane][hh] = shat(hh, cw + id);
+    }
+    if (lane < n) lid[wave][lane] = (int32_t)(cw + id);
   } else if (cnt > 0) {
     n = cnt;
     if (lane < n) {
-      lkey[wave][lane] = rank_key(cw + lane);
+      lkey[wave][lane] = keys[0];
       lid[wave][lane] = (int32_t)(cw + lane);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        if constexpr (kHold) lsv[wave][lane][hh] = sv[hh][0];
+        else lsv[wave][lane][hh] = shat(hh, cw + lane);
+      }
     }
   }
   if (lane == 0) nlist[wave] = n;
@@ -290,10 +331,10 @@ __global__ __launch_bounds__(64 * kSelWaves) void dec_select_kernel(DecKArgs a) 
     int base = 0;
     for (int w = 0; w < kSelWaves; ++w) {
       const int nw = nlist[w];
-      if (lane < nw) emit(base + lane, lid[w][lane]);
+      if (lane < nw) emit(base + lane, lid[w][lane], lsv[w][lane]);
       base += nw;
     }
-    if (lane >= base && lane < topk) emit(lane, -1);
+    if (lane >= base && lane < topk) emit(lane, -1, lsv[0][0]);
     return;
   }
   // Each list holds at most TP = topk rounded up to a power of two entries, so
@@ -304,18 +345,19 @@ __global__ __launch_bounds__(64 * kSelWaves) void dec_select_kernel(DecKArgs a) 
   const int TP = topk <= 16 ? 16 : (topk <= 32 ? 32 : 64);
   const int LPJ = kWave / TP;
   const int ml = lane / TP, me = lane % TP;
-  uint32_t keys[JM];
+  uint32_t mkeys[JM];
 #pragma unroll
   for (int j = 0; j < JM; ++j) {
     const int w = LPJ * j + ml;
-    keys[j] = (w < kSelWaves && me < nlist[w]) ? lkey[w][me] : 0u;
+    mkeys[j] = (w < kSelWaves && me < nlist[w]) ? lkey[w][me] : 0u;
   }
-  wave_topk_u32<JM>(keys, (kSelWaves + LPJ - 1) / LPJ, topk, lane, sbuf[0], wsel[0]);
+  wave_topk_u32<JM>(mkeys, (kSelWaves + LPJ - 1) / LPJ, topk, lane, sbuf[0], wsel[0]);
   wave_lds_sync();
   if (lane < topk) {
     const int id = wsel[0][lane];
     const int l = id % 64;
-    emit(lane, lid[LPJ * (id / 64) + l / TP][l % TP]);
+    const int w = LPJ * (id / 64) + l / TP, e = l % TP;
+    emit(lane, lid[w][e], lsv[w][e]);
   }
 }
 
