@@ -118,34 +118,42 @@ def source_digest(files):
     return h.hexdigest()[:16]
 
 
-# Sources a kernel's code depends on: a change to any voids its stored counters.
+# Sources a kernel's code depends on (its translation unit and every header it
+# includes): a change to any voids its stored counters.
+_CSRC = "chunk_wise_sparse_summary_amd/csrc/"
+_HDRS = [_CSRC + h for h in ("hils_common.h", "hils_internal.h", "topk.h")]
 KERNEL_SOURCES = {
-    "chunk_attend": ["chunk_wise_sparse_summary_amd/csrc/attend.hip",
-                     "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-                     "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
-    "combine": ["chunk_wise_sparse_summary_amd/csrc/attend.hip",
-                "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-                "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
-    "window": ["chunk_wise_sparse_summary_amd/csrc/attend.hip",
-               "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-               "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
-    "rank_keys": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
-                  "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-                  "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
-    "topk_rows": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
-                  "chunk_wise_sparse_summary_amd/csrc/topk.h",
-                  "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-                  "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
-    "sel_scores": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
-                   "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-                   "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
-    "score_lse": ["chunk_wise_sparse_summary_amd/csrc/select.hip",
-                  "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-                  "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
-    "summarize": ["chunk_wise_sparse_summary_amd/csrc/summarize.hip",
-                  "chunk_wise_sparse_summary_amd/csrc/hils_common.h",
-                  "chunk_wise_sparse_summary_amd/csrc/hils_internal.h"],
+    "summarize": [_CSRC + "summarize.hip"] + _HDRS,
+    "score_lse": [_CSRC + "select.hip"] + _HDRS,
+    "rank_keys": [_CSRC + "select.hip"] + _HDRS,
+    "topk_rows": [_CSRC + "select.hip"] + _HDRS,
+    "sel_scores": [_CSRC + "select.hip"] + _HDRS,
+    "window": [_CSRC + "attend.hip"] + _HDRS,
+    "chunk_attend": [_CSRC + "attend.hip"] + _HDRS,
+    "combine": [_CSRC + "attend.hip"] + _HDRS,
 }
+
+
+def stats_summary(csv_path, out_path, title, command):
+    """Write a short text summary of a rocprofv3 --stats kernel table."""
+    import csv
+    rows = list(csv.DictReader(open(csv_path)))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["# rocprofv3 kernel statistics: " + title,
+             "# command (repository root, one MI355X):"] + ["#   " + c for c in command] + [
+             "# source: %s; torch kernels generate the synthetic inputs." % csv_path, "",
+             "%-64s %6s %14s %12s %8s" % ("kernel", "calls", "total_us", "avg_us", "pct")]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].replace("void ", "").replace("hils::(anonymous namespace)::", "").replace("hils::", "")
+        name = name.split("(")[0] if not name.startswith("__") else name
+        t = float(r["TotalDurationNs"])
+        lines.append("%-64s %6s %14.1f %12.1f %8.2f" % (name[:64], r["Calls"], t / 1e3,
+                                                       t / 1e3 / max(int(r["Calls"]), 1), 100.0 * t / tot))
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_128k_prefill.txt")
 COPY_PROBE_BYTES = 1 << 30
 
@@ -265,9 +273,15 @@ def main():
                     help="with --ingest-pmc: the profiling command lines, for the record")
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE,
                     help="with --ingest-pmc: where to write the summary")
+    ap.add_argument("--stats-summary", nargs=3, metavar=("STATS_CSV", "OUT", "TITLE"),
+                    help="write a text summary of a rocprofv3 --stats kernel table and exit "
+                         "(the profiling command goes in --pmc-command)")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.pmc_command, args.traffic_out)
+        return
+    if args.stats_summary:
+        stats_summary(args.stats_summary[0], args.stats_summary[1], args.stats_summary[2], args.pmc_command)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the HiLS path here runs on a single device and has "
