@@ -94,8 +94,9 @@ def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
         # these three run once per (b, KV group): one group's share per launch
         "rank_keys": ("mfma", G * ncand * 2.0 * d, "FLOP"),
         # the rank keys of every (query, candidate) of the group read once
-        "topk_rows": ("hbm", ncand * 4.0, "B"),
-        "sel_scores": ("mfma", G * ncand * 2.0 * d, "FLOP"),
+        # the group's rank keys read once, its q_hat rows, and per (query, head,
+        # slot) the chosen k' row (an L2 hit in practice), b' and s_hat
+        "topk_scores": ("hbm", ncand * 4.0 + T * G * d * esz + G * nsel * (d * esz + 8.0), "B"),
         # K and V^T of every chunk once per KV head; per (query, group, slot)
         # entry: the entry word, G rows of q and G chunk weights read, G weighted
         # partial rows written
@@ -126,8 +127,7 @@ KERNEL_SOURCES = {
     "summarize": [_CSRC + "summarize.hip"] + _HDRS,
     "score_lse": [_CSRC + "select.hip"] + _HDRS,
     "rank_keys": [_CSRC + "select.hip"] + _HDRS,
-    "topk_rows": [_CSRC + "select.hip"] + _HDRS,
-    "sel_scores": [_CSRC + "select.hip"] + _HDRS,
+    "topk_scores": [_CSRC + "select.hip"] + _HDRS,
     "window": [_CSRC + "attend.hip"] + _HDRS,
     "chunk_attend": [_CSRC + "attend.hip"] + _HDRS,
     "combine": [_CSRC + "attend.hip"] + _HDRS,
@@ -373,8 +373,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    prefill_kernels = ["summarize", "score_lse", "rank_keys", "topk_rows", "sel_scores", "lsel", "idx_count", "idx_scan_tiles",
-                       "idx_scan_buckets", "idx_fill", "v_transpose", "q_group", "window",
+    prefill_kernels = ["summarize", "score_lse", "rank_keys", "topk_scores", "lsel", "idx_count", "idx_scan_tiles",
+                       "idx_scan_buckets", "idx_fill", "v_transpose", "window",
                        "chunk_attend", "combine"]
     log("warmup")
     for _ in range(args.warmup):

@@ -231,26 +231,6 @@ __global__ __launch_bounds__(256) void vt_kernel(const T* __restrict__ v, T* __r
   }
 }
 
-// q regrouped so that a KV group's G head rows of one query are contiguous,
-// [B, Hkv, T, G, D]: the chunk-major pass gathers one G*D record per entry.
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void qgroup_kernel(const T* __restrict__ q, T* __restrict__ qg, int Hq,
-                                                     int64_t T_) {
-  constexpr int EPV = 16 / sizeof(T);
-  constexpr int PPR = D / EPV;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-byte piece of qg
-  const int64_t total = (int64_t)gridDim.y * Hq * T_ * PPR;
-  if (e >= total / gridDim.y) return;
-  const int b = blockIdx.y;
-  const int pc = (int)(e % PPR);
-  const int hh = (int)((e / PPR) % G);
-  const int64_t i = (e / (PPR * G)) % T_;
-  const int g = (int)(e / (PPR * G * T_));
-  const int64_t src = (((int64_t)b * Hq + g * G + hh) * T_ + i) * D + pc * EPV;
-  const int64_t dst = (int64_t)b * Hq * T_ * D + e * EPV;
-  *reinterpret_cast<uint4*>(qg + dst) = *reinterpret_cast<const uint4*>(q + src);
-}
-
 // Stage one chunk (K rows and V^T rows, already zero past the sequence end for
 // V^T) into the swizzled LDS tiles with NT threads.
 template <typename T, int D, int NT>
@@ -484,6 +464,7 @@ struct WinArgs {
   const void* vt;  // V^T per chunk, [B, Hkv, NCf, D, S]
   void* ow;        // [B, Hq, T, D] normalised window output
   float* lzw;      // [B, Hq, T] window log-mass
+  void* qg;        // q regrouped, [B, Hkv, T, G, D] (written here; null: not needed)
   int B, Hq, Hkv, S, W;
   int64_t T, NCf;
   float scale;
@@ -532,6 +513,18 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
     const T* qrow = static_cast<const T*>(a.q) + (((int64_t)b * a.Hq + h) * T_ + min(i, T_ - 1)) * D + 8 * grp;
 #pragma unroll
     for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
+  }
+  // The chunk pass gathers one query's G head rows as one contiguous record: this
+  // workgroup holds exactly the rows of its queries, so it writes them regrouped.
+  if (a.qg && i < T_) {
+    T* qgr = static_cast<T*>(a.qg) + ((((int64_t)b * a.Hkv + g) * T_ + i) * G + r16 % G) * D + 8 * grp;
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(&bq[kq]);
+#pragma unroll
+      for (int v = 0; v < 8 / EPV; ++v)
+        *reinterpret_cast<uint4*>(qgr + 32 * kq + v * EPV) = make_uint4(w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]);
+    }
   }
   // Running reference in the log2 domain: finite, far below any logit, so the
   // first chunk with an unmasked token always moves it.
@@ -749,16 +742,10 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
     hipLaunchKernelGGL((vt_kernel<T, D>), dim3((unsigned)NCf, a.Hkv, a.B), dim3(256), 0, st,
                        static_cast<const T*>(a.v), static_cast<T*>(vt), a.Hkv, a.T, NCf);
   }
-  if (ia.NCs > 0 && a.topk > 0) {
-    constexpr int PPR = D / (16 / (int)sizeof(T));
-    const int64_t n = (int64_t)a.Hq * a.T * PPR;
-    KTimer tm(K_QGROUP, st);
-    hipLaunchKernelGGL((qgroup_kernel<T, D, G>), dim3((unsigned)((n + 255) / 256), a.B), dim3(256), 0, st,
-                       static_cast<const T*>(a.q), static_cast<T*>(qg), a.Hq, a.T);
-  }
-  // window part for every head at once
+  // window part for every head at once (it also writes the regrouped q rows)
   {
-    WinArgs wa{a.q, a.k, vt, ow, lzw, a.B, a.Hq, a.Hkv, a.S, a.W, a.T, NCf, a.scale};
+    WinArgs wa{a.q, a.k, vt, ow, lzw, (ia.NCs > 0 && a.topk > 0) ? qg : nullptr,
+               a.B, a.Hq, a.Hkv, a.S, a.W, a.T, NCf, a.scale};
     const int QB = 8 * (16 / G);
     KTimer tm(K_WINDOW, st);
     const dim3 grid((unsigned)((a.T + QB - 1) / QB), a.Hkv, a.B);

@@ -14,8 +14,8 @@
 //               tiles with an online log-sum-exp epilogue; one workgroup = one
 //               head x 256 queries, k' tiles staged once in LDS.
 //   rank_keys   rank key per (query, candidate) into a scratch row per query;
-//   topk_rows   one wave per query: its top-k (below);
-//   sel_scores  each head's s_hat on the chosen chunks (a second score pass).
+//   topk_scores one wave per query: its top-k (below), then each head's s_hat
+//               on the chosen chunks from the chosen k' rows.
 //
 // Wave-level top-k of n <= 64*J rank keys held J per lane (candidate c = lane +
 // 64*j; keys are order-preserving unsigned images of the fp32 rank key): a
@@ -29,6 +29,8 @@
 namespace hils {
 
 namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T> struct KPad;
 template <> struct KPad<bf16_t> { static constexpr int P = 8; };
@@ -199,18 +201,15 @@ constexpr int rank_waves() { return (J <= 16 || (J == 32 && (sizeof(T) == 2 || D
 // larger tiles would not fit LDS at 128.
 template <typename T> constexpr int rank_q() { return sizeof(T) == 2 ? 128 : 64; }
 
-// The prefill selection runs as three kernels per (b, group), the rank keys of
+// The prefill selection runs as two kernels per (b, group), the rank keys of
 // one group at a time living in a [T][64 J] scratch:
 //   rank_keys  per 128-query tile and 16-chunk k' tile (k' of all G heads staged
 //              once in LDS): each head's x = s_hat - L_h (transposed score tiles:
 //              a lane holds four chunks of one query) goes to LDS, and the rank
 //              key r = max over heads (r = s_hat for one head) to the scratch.
 //              Wave w takes the 64 queries 64 (w / 4) .. and heads w % 4, w % 4 + 4.
-//   topk_rows  one wave per query: the exact top-k of its rank keys (below).
-//   sel_scores per 128-query tile, a second pass of the score tiles writes each
-//              head's s_hat on every chosen chunk: a chunk's value is kept where
-//              the query's selection bitmap has it, at slot = number of chosen
-//              chunks below it (ids ascend).
+//   topk_scores one wave per query: the exact top-k of its rank keys (below)
+//              and each head's s_hat on the chosen chunks.
 template <typename T, int D, int G, int RQ_ = rank_q<T>()>
 struct RankTiles {
   static constexpr int KS = D / 32;
@@ -218,9 +217,6 @@ struct RankTiles {
   static constexpr int RQ = RQ_, NT = RQ * 4;
   using Tile = KTile<T, D, G, NT>;
 };
-// The score pass on the choice holds more registers; 64 queries per workgroup
-// (4 waves) let three workgroups share a compute unit.
-constexpr int kSelQ = 64;
 
 template <typename T, int D, int G, int NCP>
 __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, int b, int g,
@@ -313,10 +309,36 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
   }
 }
 
-// One wave per query of one (b, group): the exact top-k of its rank keys.
-template <int J>
-__global__ __launch_bounds__(256) void topk_rows_kernel(SelArgs a, int b, int g,
-                                                        const uint32_t* __restrict__ keys) {
+// One reduce-scatter step over lane mask M on the first N entries of v: lanes
+// with bit M set keep the upper half and send the lower, the others the
+// reverse; each kept entry gains the partner's copy.  Steps run for masks M,
+// M/2, ..., 1, so the kept entry's index is the lane's low bits.
+template <int M, int N, int CAP>
+__device__ __forceinline__ void rs_rows(float (&v)[CAP], int lane) {
+  const bool up = (lane & M) != 0;
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float send = up ? v[k] : v[k + N / 2];
+    const float keep = up ? v[k + N / 2] : v[k];
+    v[k] = keep + xor_lane<M>(send);
+  }
+  if constexpr (M > 1) rs_rows<M / 2, N / 2, CAP>(v, lane);
+}
+
+// One wave per query of one (b, group): the exact top-k of its rank keys, then
+// each head's s_hat on the chosen chunks.  The chosen (slot, head) rows of k'
+// (the group's k' is a few MB, resident in L2) are read 64 at a time with
+// whole-wave contiguous loads, PPR lanes per row; each lane takes the packed
+// dot products (fp32 accumulation) of its 16-byte pieces with the matching
+// piece of its row's q_hat, and a reduce-scatter over the PPR lanes of a row
+// group leaves one row's s_hat per lane.
+template <typename T, int D, int G, int J>
+__global__ __launch_bounds__(256) void topk_scores_kernel(SelArgs a, int b, int g,
+                                                          const uint32_t* __restrict__ keys) {
+  constexpr int EPP = 16 / (int)sizeof(T);   // elements per 16-byte piece
+  constexpr int PPR = D / EPP;               // pieces per row
+  constexpr int RPI = kWave / PPR;           // rows per load instruction
+  constexpr int NQ = G > RPI ? G / RPI : 1;  // q_hat pieces per lane
   __shared__ uint32_t sbuf[4][64];
   __shared__ int32_t sel[4][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -325,125 +347,68 @@ __global__ __launch_bounds__(256) void topk_rows_kernel(SelArgs a, int b, int g,
   if (i >= a.T) return;
   const int topk = a.topk;
   const int nc = (int)num_candidates(i, a.S, a.W);
-  int32_t* out = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * topk;
-  if (nc <= topk) {
-    if (lane < topk) out[lane] = lane < nc ? lane : -1;
-    return;
-  }
-  const uint32_t* rrow = keys + i * (64 * J);
-  const int jn = (nc + 63) / 64;
-  uint32_t kv[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int c = lane + 64 * j;
-    kv[j] = (j < jn && c < nc) ? rrow[c] : 0u;
-  }
-  wave_topk_u32<J>(kv, jn, topk, lane, sbuf[wave], sel[wave]);
-  wave_lds_sync();
-  if (lane < topk) out[lane] = sel[wave][lane];
-}
-
-template <typename T, int D, int G, int NCP>
-__global__ __launch_bounds__(kSelQ * 4) void sel_scores_kernel(SelArgs a, int b, int g) {
-  using R = RankTiles<T, D, G, kSelQ>;
-  constexpr int KS = R::KS, HW = R::HW, RQ = R::RQ, NT = R::NT;
-  constexpr int BMP = NCP / 32 + 1;      // padded bitmap row (words)
-  using Tile = typename R::Tile;
-  __shared__ __align__(16) T kt[G * 16 * Tile::KP];
-  __shared__ float bt[G * 16];
-  __shared__ uint32_t selbm[RQ * BMP];   // RQ queries x candidate bitmap of the choice
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int r16 = lane % 16, grp = lane / 16;
-  const int qhalf = wave / 4, hw = wave % 4;
-  const T* qh = static_cast<const T*>(a.qh);
   const int64_t T_ = a.T, NCs = a.NCs;
-  const int Hq = a.Hq, topk = a.topk;
-  const int64_t qb = (int64_t)blockIdx.x * RQ;
-  const int64_t qw = qb + 64 * qhalf;
-  const T* kg = static_cast<const T*>(a.ksum) + ((int64_t)b * Hq + g * G) * NCs * D;
-  const float* bg = a.bsum + ((int64_t)b * Hq + g * G) * NCs;
-  const int32_t* irows = a.idx + (((int64_t)b * a.Hkv + g) * T_ + qb) * topk;
-  for (int e = threadIdx.x; e < RQ * BMP; e += NT) selbm[e] = 0u;
-  __syncthreads();
-  for (int e = threadIdx.x; e < RQ * topk; e += NT) {
-    const int row = e / topk, t = e % topk;
-    if (qb + row >= T_) continue;
-    const int32_t c = irows[(int64_t)row * topk + t];
-    if (c >= 0) {
-      atomicOr(&selbm[row * BMP + c / 32], 1u << (c % 32));
-    } else {   // padding slot
+  const int Hq = a.Hq;
+  const int p = lane % PPR, grp = lane / PPR;
+  // q_hat pieces: row r = slot*G + head has head r % G = (grp + RPI t) % G
+  uint32_t qp[NQ][4];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh)
-        a.ssel[(((int64_t)b * Hq + g * G + hh) * T_ + qb + row) * topk + t] = kNegInf;
-    }
+  for (int u = 0; u < NQ; ++u) {
+    const int hh = (grp + RPI * u) % G;
+    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) +
+                                                   (((int64_t)b * Hq + g * G + hh) * T_ + i) * D + p * EPP);
+    qp[u][0] = q.x; qp[u][1] = q.y; qp[u][2] = q.z; qp[u][3] = q.w;
   }
-  Frag<T> qf[HW][4][KS];
+  int nsel;
+  if (nc <= topk) {
+    if (lane < topk) sel[wave][lane] = lane < nc ? lane : -1;
+    nsel = nc;
+  } else {
+    const uint32_t* rrow = keys + i * (64 * J);
+    const int jn = (nc + 63) / 64;
+    uint32_t kv[J];
 #pragma unroll
-  for (int u = 0; u < HW; ++u) {
-    const int hh = hw + 4 * u;
-    if (hh < G) {
+    for (int j = 0; j < J; ++j) {
+      const int c = lane + 64 * j;
+      kv[j] = (j < jn && c < nc) ? rrow[c] : 0u;
+    }
+    wave_topk_u32<J>(kv, jn, topk, lane, sbuf[wave], sel[wave]);
+    nsel = topk;
+  }
+  wave_lds_sync();
+  if (lane < topk) a.idx[(((int64_t)b * a.Hkv + g) * T_ + i) * topk + lane] = sel[wave][lane];
+  // 64 rows per batch: lane (grp, p) loads piece p of rows r0 + grp + RPI t
+  for (int r0 = 0; r0 < topk * G; r0 += kWave) {
+    float part[PPR];
+#pragma unroll
+    for (int t = 0; t < PPR; ++t) {
+      const int r = r0 + grp + RPI * t, slot = r / G, hh = r % G;
+      float acc = 0.f;
+      if (slot < nsel) {
+        const int c = sel[wave][slot];
+        const uint4 ku = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.ksum) +
+                                                        (((int64_t)b * Hq + g * G + hh) * NCs + c) * D + p * EPP);
+        const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
+        const int u = NQ > 1 ? t % NQ : 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (sizeof(T) == 2)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[u][e]),
+                                                  __builtin_bit_cast(bf16x2_t, kw[e]), acc, false);
+          else
+            acc = fmaf(__uint_as_float(qp[u][e]), __uint_as_float(kw[e]), acc);
+        }
+      }
+      part[t] = acc;
+    }
+    rs_rows<PPR / 2, PPR, PPR>(part, lane);
+    const int r = r0 + grp + RPI * p, slot = r / G, hh = r % G;   // the row this lane now holds
+    if (slot < topk) {
       const int h = g * G + hh;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int64_t qi = qw + 16 * rt + r16;
-        const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load_frag(qf[u][rt][ks], qrow + 32 * ks);
-      }
+      float sh = kNegInf;
+      if (slot < nsel) sh = fmaf(part[0], a.scale, a.bsum[((int64_t)b * Hq + h) * NCs + sel[wave][slot]]);
+      a.ssel[(((int64_t)b * Hq + h) * T_ + i) * topk + slot] = sh;
     }
-  }
-  const int nc_block = (int)num_candidates(min(qb + RQ - 1, T_ - 1), a.S, a.W);
-  const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
-  int below[4];   // chosen chunks of query qw + 16 rt + r16 before this tile
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) below[rt] = 0;
-  u32v<4 * Tile::NPT> kreg;
-  float breg = 0.f;
-  if (nc_block > 0) tile_fetch<T, D, G, NT>(kreg, breg, kg, bg, NCs, 0, cl_last);
-  for (int c0 = 0; c0 < nc_block; c0 += 16) {
-    __syncthreads();
-    tile_commit<T, D, G, NT>(kreg, breg, kt, bt);
-    __syncthreads();
-    if (c0 + 16 < nc_block) tile_fetch<T, D, G, NT>(kreg, breg, kg, bg, NCs, c0 + 16, cl_last);
-    uint32_t seg[4];   // the tile's 16 bitmap bits of query qw + 16 rt + r16
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-      seg[rt] = (selbm[(64 * qhalf + 16 * rt + r16) * BMP + c0 / 32] >> (c0 % 32)) & 0xffffu;
-#pragma unroll
-    for (int u = 0; u < HW; ++u) {
-      const int hh = hw + 4 * u;
-      if (hh < G) {
-        const int h = g * G + hh;
-        Frag<T> kf[KS];   // row r16 = chunk c0 + r16
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
-        const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
-        const float bkv[4] = {bk.x, bk.y, bk.z, bk.w};
-        f32x4_t acc[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) mma(acc[rt], kf[ks], qf[u][rt][ks]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const uint32_t mine = (seg[rt] >> (4 * grp)) & 0xfu;
-          const int64_t i = qw + 16 * rt + r16;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            if (((mine >> q4) & 1u) && i < T_) {
-              const int slot_t = below[rt] + __popc(seg[rt] & ((1u << (4 * grp + q4)) - 1u));
-              a.ssel[(((int64_t)b * Hq + h) * T_ + i) * topk + slot_t] = fmaf(acc[rt][q4], a.scale, bkv[q4]);
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) below[rt] += __popc(seg[rt]);
   }
 }
 
@@ -451,7 +416,6 @@ template <typename T, int D, int G, int J>
 hipError_t launch_rank_j(const SelArgs& a, hipStream_t st) {
   constexpr int RQ = rank_q<T>();
   const dim3 tiles((unsigned)((a.T + RQ - 1) / RQ)), rows((unsigned)((a.T + 3) / 4));
-  const dim3 stiles((unsigned)((a.T + kSelQ - 1) / kSelQ));
   uint32_t* keys = reinterpret_cast<uint32_t*>(a.scratch);
   for (int b = 0; b < a.B; ++b) {
     for (int g = 0; g < a.Hkv; ++g) {
@@ -459,12 +423,8 @@ hipError_t launch_rank_j(const SelArgs& a, hipStream_t st) {
         KTimer tm(K_RANK_KEYS, st);
         hipLaunchKernelGGL((rank_keys_kernel<T, D, G, 64 * J>), tiles, dim3(RQ * 4), 0, st, a, b, g, keys);
       }
-      {
-        KTimer tm(K_TOPK_ROWS, st);
-        hipLaunchKernelGGL((topk_rows_kernel<J>), rows, dim3(256), 0, st, a, b, g, keys);
-      }
-      KTimer tm(K_SEL_SCORES, st);
-      hipLaunchKernelGGL((sel_scores_kernel<T, D, G, 64 * J>), stiles, dim3(kSelQ * 4), 0, st, a, b, g);
+      KTimer tm(K_TOPK_SCORES, st);
+      hipLaunchKernelGGL((topk_scores_kernel<T, D, G, J>), rows, dim3(256), 0, st, a, b, g, keys);
     }
   }
   return hipGetLastError();

@@ -212,8 +212,8 @@ int hils_abi_version(void);
  *   score_lse, idx_count, idx_scan_tiles, idx_scan_buckets,
  *   idx_fill, lsel, window, chunk_attend, combine, dec_score, dec_select,
  *   dec_attend, dec_fuse, dec_summarize (the summaries of chunks
- *   completed by a decode step), v_transpose, q_group, rank_keys, topk_rows,
- *   sel_scores.  HILS_E_UNSUPPORTED for an unknown name
+ *   completed by a decode step), v_transpose, rank_keys,
+ *   topk_scores.  HILS_E_UNSUPPORTED for an unknown name
  *   (timing is then left off).
  * hils_timing_get(kernel, total_ms, launches): waits for the recorded events
  *   of that kernel and returns the summed duration and the number of timed
