@@ -94,9 +94,11 @@ def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
         # these three run once per (b, KV group): one group's share per launch
         "rank_keys": ("mfma", G * ncand * 2.0 * d, "FLOP"),
         # the rank keys of every (query, candidate) of the group read once
-        # the group's rank keys read once, its q_hat rows, and per (query, head,
-        # slot) the chosen k' row (an L2 hit in practice), b' and s_hat
-        "topk_scores": ("hbm", ncand * 4.0 + T * G * d * esz + G * nsel * (d * esz + 8.0), "B"),
+        # the group's rank keys and q_hat rows read once, its k' and b' once (the
+        # chosen rows are gathered from L2), the index rows and each head's
+        # s_hat on the choice written
+        "topk_scores": ("hbm", ncand * 4.0 + T * G * d * esz + G * NC * (d * esz + 4.0)
+                        + T * k * 4.0 + G * nsel * 4.0, "B"),
         # K and V^T of every chunk once per KV head; per (query, group, slot)
         # entry: the entry word, G rows of q and G chunk weights read, G weighted
         # partial rows written
