@@ -157,23 +157,40 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) mma(acc[rt], kf[ks], qf[rt][ks]);
     }
-    const bool full = c0 + 16 <= ncmin;   // every query of the wave sees all 16 chunks
+    float x[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[rt][i] = fmaf(acc[rt][i], sl2, b2[i]);
+    if (c0 + 16 > ncmin) {   // some query of the wave does not see all 16 chunks
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c0 + 4 * grp + i >= ncq[rt]) x[rt][i] = kNegInf;
+    }
+    // The reference moves only when a score passes it by 16, which after the
+    // first tiles is rare: the check is one wave vote, the rescale a branch.
+    float mx[4];
+    bool move = false;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = fmaf(acc[rt][i], sl2, b2[i]);
-        if (!full && c0 + 4 * grp + i >= ncq[rt]) x[i] = kNegInf;
-      }
-      const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (mx > m[rt] + 16.f) {   // the reference moves only when a score passes it by 16
-        s[rt] *= hw_exp2(m[rt] - mx);
-        m[rt] = mx;
-      }
-      s[rt] += (hw_exp2(x[0] - m[rt]) + hw_exp2(x[1] - m[rt])) +
-               (hw_exp2(x[2] - m[rt]) + hw_exp2(x[3] - m[rt]));
+      mx[rt] = fmaxf(fmaxf(x[rt][0], x[rt][1]), fmaxf(x[rt][2], x[rt][3]));
+      move |= mx[rt] > m[rt] + 16.f;
     }
+    if (__any(move)) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        if (mx[rt] > m[rt] + 16.f) {
+          s[rt] *= hw_exp2(m[rt] - mx[rt]);
+          m[rt] = mx[rt];
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      s[rt] += (hw_exp2(x[rt][0] - m[rt]) + hw_exp2(x[rt][1] - m[rt])) +
+               (hw_exp2(x[rt][2] - m[rt]) + hw_exp2(x[rt][3] - m[rt]));
   }
   if (!live) return;
 #pragma unroll
