@@ -107,11 +107,12 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
   using Tile = KTile<T, D, 1>;
   __shared__ __align__(16) T kt[16 * Tile::KP];
   __shared__ float bt[16];
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
-  const int64_t qb = (int64_t)blockIdx.x * 256;
+  // the query tiles with the most candidates first, so the last wave of blocks is short
+  const int64_t qb = (int64_t)(gridDim.y - 1 - blockIdx.y) * 256;
   const int64_t q0 = qb + wave * 64;
   const bool live = q0 < T_;
 
@@ -210,10 +211,6 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
   }
 }
 
-// Two waves per SIMD fit without spilling unless the candidate keys are wide.
-template <typename T, int D, int J>
-constexpr int rank_waves() { return (J <= 16 || (J == 32 && (sizeof(T) == 2 || D == 64))) ? 2 : 1; }
-
 // Queries per workgroup: 128 (8 waves) for bf16; 64 (4 waves) for fp32, whose
 // larger tiles would not fit LDS at 128.
 template <typename T> constexpr int rank_q() { return sizeof(T) == 2 ? 128 : 64; }
@@ -221,17 +218,17 @@ template <typename T> constexpr int rank_q() { return sizeof(T) == 2 ? 128 : 64;
 // The prefill selection runs as two kernels per (b, group), the rank keys of
 // one group at a time living in a [T][64 J] scratch:
 //   rank_keys  per 128-query tile and 16-chunk k' tile (k' of all G heads staged
-//              once in LDS): each head's x = s_hat - L_h (transposed score tiles:
-//              a lane holds four chunks of one query) goes to LDS, and the rank
-//              key r = max over heads (r = s_hat for one head) to the scratch.
-//              Wave w takes the 64 queries 64 (w / 4) .. and heads w % 4, w % 4 + 4.
+//              once in LDS): wave w owns queries 16 w .. 16 w + 15 of the tile and
+//              every head of the group, so the rank key r = max over heads of
+//              s_hat - L_h (r = s_hat for one head) forms in registers
+//              (transposed score tiles: a lane holds four chunks of one query)
+//              and goes straight to the scratch.
 //   topk_scores one wave per query: the exact top-k of its rank keys (below)
 //              and each head's s_hat on the chosen chunks.
 template <typename T, int D, int G, int RQ_ = rank_q<T>()>
 struct RankTiles {
   static constexpr int KS = D / 32;
-  static constexpr int HW = (G + 3) / 4;   // heads per wave
-  static constexpr int RQ = RQ_, NT = RQ * 4;
+  static constexpr int RQ = RQ_, NT = RQ * 4;   // 16 queries per wave
   using Tile = KTile<T, D, G, NT>;
 };
 
@@ -239,41 +236,32 @@ template <typename T, int D, int G, int NCP>
 __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, int b, int g,
                                                                     uint32_t* __restrict__ keys) {
   using R = RankTiles<T, D, G>;
-  constexpr int KS = R::KS, HW = R::HW, RQ = R::RQ, NT = R::NT;
-  constexpr int XP = 20;                 // padded LDS row of 16 chunk values
+  constexpr int KS = R::KS, RQ = R::RQ, NT = R::NT;
   using Tile = typename R::Tile;
   __shared__ __align__(16) T kt[G * 16 * Tile::KP];
   __shared__ float bt[G * 16];
-  __shared__ __align__(16) float xs[G][RQ][XP];   // x = s_hat - L per head
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
-  const int qhalf = wave / 4, hw = wave % 4;
   const T* qh = static_cast<const T*>(a.qh);
   const int64_t T_ = a.T, NCs = a.NCs;
   const int Hq = a.Hq;
-  const int64_t qb = (int64_t)blockIdx.x * RQ;
-  const int64_t qw = qb + 64 * qhalf;     // this wave's 64 queries
+  const int64_t qb = (int64_t)(gridDim.x - 1 - blockIdx.x) * RQ;   // longest rows first
+  const int64_t qi = qb + 16 * wave + r16;   // this lane's query (column r16 of the tiles)
   const T* kg = static_cast<const T*>(a.ksum) + ((int64_t)b * Hq + g * G) * NCs * D;
   const float* bg = a.bsum + ((int64_t)b * Hq + g * G) * NCs;
-  Frag<T> qf[HW][4][KS];
-  float Lq[HW][4];
+  Frag<T> qf[G][KS];
+  float Lq[G];
 #pragma unroll
-  for (int u = 0; u < HW; ++u) {
-    const int hh = hw + 4 * u;
-    if (hh < G) {
-      const int h = g * G + hh;
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = g * G + hh;
+    const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int64_t qi = qw + 16 * rt + r16;
-        const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) load_frag(qf[u][rt][ks], qrow + 32 * ks);
-        Lq[u][rt] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
-      }
-    }
+    for (int ks = 0; ks < KS; ++ks) load_frag(qf[hh][ks], qrow + 32 * ks);
+    Lq[hh] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
   }
   const int nc_block = (int)num_candidates(min(qb + RQ - 1, T_ - 1), a.S, a.W);
+  const int nc_wave = (int)num_candidates(min(qb + 16 * wave + 15, T_ - 1), a.S, a.W);
   const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
   u32v<4 * Tile::NPT> kreg;
   float breg = 0.f;
@@ -283,46 +271,26 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
     tile_commit<T, D, G, NT>(kreg, breg, kt, bt);
     __syncthreads();
     if (c0 + 16 < nc_block) tile_fetch<T, D, G, NT>(kreg, breg, kg, bg, NCs, c0 + 16, cl_last);
+    if (c0 >= nc_wave) continue;   // no query of this wave has these candidates
+    float r[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
-    for (int u = 0; u < HW; ++u) {
-      const int hh = hw + 4 * u;
-      if (hh < G) {
-        Frag<T> kf[KS];   // row r16 = chunk c0 + r16
+    for (int hh = 0; hh < G; ++hh) {
+      Frag<T> kf[KS];   // row r16 = chunk c0 + r16
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
-        const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
-        f32x4_t acc[4];
+      for (int ks = 0; ks < KS; ++ks)
+        load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
+      const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) mma(acc[rt], kf[ks], qf[u][rt][ks]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          float4 x;
-          x.x = fmaf(acc[rt][0], a.scale, bk.x) - Lq[u][rt];
-          x.y = fmaf(acc[rt][1], a.scale, bk.y) - Lq[u][rt];
-          x.z = fmaf(acc[rt][2], a.scale, bk.z) - Lq[u][rt];
-          x.w = fmaf(acc[rt][3], a.scale, bk.w) - Lq[u][rt];
-          *reinterpret_cast<float4*>(&xs[hh][64 * qhalf + 16 * rt + r16][4 * grp]) = x;
-        }
-      }
+      for (int ks = 0; ks < KS; ++ks) mma(acc, kf[ks], qf[hh][ks]);
+      r[0] = fmaxf(r[0], fmaf(acc[0], a.scale, bk.x) - Lq[hh]);
+      r[1] = fmaxf(r[1], fmaf(acc[1], a.scale, bk.y) - Lq[hh]);
+      r[2] = fmaxf(r[2], fmaf(acc[2], a.scale, bk.z) - Lq[hh]);
+      r[3] = fmaxf(r[3], fmaf(acc[3], a.scale, bk.w) - Lq[hh]);
     }
-    __syncthreads();
-    // wave w: queries 16w + r16 of the tile, chunks c0 + 4 grp .. + 3
-    const int row = 16 * wave + r16;
-    if (qb + row < T_) {
-      float4 r = *reinterpret_cast<const float4*>(&xs[0][row][4 * grp]);
-#pragma unroll
-      for (int hh = 1; hh < G; ++hh) {
-        const float4 y = *reinterpret_cast<const float4*>(&xs[hh][row][4 * grp]);
-        r.x = fmaxf(r.x, y.x); r.y = fmaxf(r.y, y.y); r.z = fmaxf(r.z, y.z); r.w = fmaxf(r.w, y.w);
-      }
-      *reinterpret_cast<uint4*>(keys + (qb + row) * NCP + c0 + 4 * grp) =
-          make_uint4(order_key(r.x), order_key(r.y), order_key(r.z), order_key(r.w));
-    }
+    if (qi < T_)
+      *reinterpret_cast<uint4*>(keys + qi * NCP + c0 + 4 * grp) =
+          make_uint4(order_key(r[0]), order_key(r[1]), order_key(r[2]), order_key(r[3]));
   }
 }
 
@@ -360,7 +328,7 @@ __global__ __launch_bounds__(256) void topk_scores_kernel(SelArgs a, int b, int 
   __shared__ int32_t sel[4][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  const int64_t i = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t i = (int64_t)(gridDim.x - 1 - blockIdx.x) * 4 + wave;   // longest rows first
   if (i >= a.T) return;
   const int topk = a.topk;
   const int nc = (int)num_candidates(i, a.S, a.W);
@@ -462,7 +430,7 @@ template <typename T, int D>
 hipError_t launch_select_t(const SelArgs& a, int J, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   if (G > 1) {
-    dim3 grid((unsigned)((a.T + 255) / 256), (unsigned)a.Hq, (unsigned)a.B);
+    dim3 grid((unsigned)a.Hq, (unsigned)((a.T + 255) / 256), (unsigned)a.B);
     KTimer tm(K_SCORE_LSE, st);
     hipLaunchKernelGGL((score_lse_kernel<T, D>), grid, dim3(256), 0, st,
                        static_cast<const T*>(a.qh), static_cast<const T*>(a.ksum), a.bsum, a.L,
