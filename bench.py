@@ -104,11 +104,12 @@ def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
         # partial rows written
         "chunk_attend": ("hbm", float(B * Hkv * NC * S * d * esz * 2)
                          + ent * (4 + G * d * esz * 2 + G * 4), "B"),
-        "window": ("mfma", B * Hq * float(np.sum(win)) * 4.0 * d, "FLOP"),
-        # per row: the window output and its log-mass, the selection normaliser,
-        # the row's partials and its group's index row, the output and lse
-        "combine": ("hbm", rows * (d * esz * 2 + 12) + B * Hq * nsel * d * esz
-                    + B * Hkv * T * k * 4.0, "B"),
+        # window attention with the fusion: 4d FLOP per (head, query, window
+        # token) on the MFMA, while the bytes it must move bound it -- per row the
+        # q row, the selection normaliser, the row's partials, its group's index
+        # row, the output and lse; K and V^T once per chunk and KV head
+        "window": ("hbm", rows * (d * esz * 2 + 8) + B * Hq * nsel * d * esz
+                   + B * Hkv * T * k * 4.0 + float(B * Hkv * NC * S * d * esz * 2), "B"),
     }
 
 
@@ -132,7 +133,6 @@ KERNEL_SOURCES = {
     "topk_scores": [_CSRC + "select.hip"] + _HDRS,
     "window": [_CSRC + "attend.hip"] + _HDRS,
     "chunk_attend": [_CSRC + "attend.hip"] + _HDRS,
-    "combine": [_CSRC + "attend.hip"] + _HDRS,
 }
 
 
@@ -377,7 +377,7 @@ def main():
         del src, dst
     prefill_kernels = ["summarize", "score_lse", "rank_keys", "topk_scores", "lsel", "idx_count", "idx_scan_tiles",
                        "idx_scan_buckets", "idx_fill", "v_transpose", "window",
-                       "chunk_attend", "combine"]
+                       "chunk_attend"]
     log("warmup")
     for _ in range(args.warmup):
         step(False)

@@ -165,7 +165,7 @@ def hils_decode_step(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, 
 
 
 KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",
-           "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend", "combine",
+           "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend",
            "dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize",
            "v_transpose", "rank_keys", "topk_scores")
 

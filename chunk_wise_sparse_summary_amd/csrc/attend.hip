@@ -327,7 +327,7 @@ __device__ __forceinline__ void load4_add<float>(f32x4_t& acc, const float* p) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct ChunkArgs {
-  const void* qg;   // q regrouped, [B, Hkv, T, G, D]
+  const void* q;    // [B, Hq, T, D]
   const void* k;
   const void* vt;   // V^T per chunk, [B, Hkv, NCf, D, S]
   const float* wq;  // [B, Hkv, T, topk, G] chunk weights
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
   const float sl2 = a.scale * kLog2e;
-  const T* qbase = static_cast<const T*>(a.qg);
+  const T* qbase = static_cast<const T*>(a.q);
   T* part = static_cast<T*>(a.part);
   T* myo = ot[wave];
   const int ntile = (n + NE - 1) / NE;
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
     wt = valid ? a.wq[((((int64_t)b * a.Hkv + g) * a.T + (word >> 6)) * a.topk + (word & 63)) * G + hh]
                : 0.f;
     if (valid) {
-      const T* qrow = qbase + ((((int64_t)b * a.Hkv + g) * a.T + (word >> 6)) * G + hh) * D + 8 * grp;
+      const T* qrow = qbase + (((int64_t)b * a.Hq + g * G + hh) * a.T + (word >> 6)) * D + 8 * grp;
 #pragma unroll
       for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
     } else {
@@ -461,11 +461,13 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
 struct WinArgs {
   const void* q;
   const void* k;
-  const void* vt;  // V^T per chunk, [B, Hkv, NCf, D, S]
-  void* ow;        // [B, Hq, T, D] normalised window output
-  float* lzw;      // [B, Hq, T] window log-mass
-  void* qg;        // q regrouped, [B, Hkv, T, G, D] (written here; null: not needed)
-  int B, Hq, Hkv, S, W;
+  const void* vt;        // V^T per chunk, [B, Hkv, NCf, D, S]
+  const float* lsel;     // [B, Hq, T] L_sel (null: no selection)
+  const int32_t* idx;    // [B, Hkv, T, topk]
+  const void* part;      // this pass's weighted partials, [B, gpass, T, topk, G, D]
+  void* out;             // [B, Hq, T, D]
+  float* lse;            // [B, Hq, T] or null
+  int B, Hq, Hkv, S, W, topk, g0, gpass;
   int64_t T, NCf;
   float scale;
 };
@@ -489,9 +491,14 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
   constexpr int NPK = kS * PK / kWinThreads, NPV = D * PV / kWinThreads;
   constexpr int QW = 16 / G;        // queries per wave
   constexpr int QB = 8 * QW;        // queries per block
-  __shared__ __align__(16) T ks[kS * D];
-  __shared__ __align__(16) T vt[D * kS];
-  const int g = blockIdx.y, b = blockIdx.z;
+  constexpr int NR = 8 * 16;        // (query, head) rows per block
+  // K and V^T tiles during the window loop, then the block's normalised window
+  // outputs (NR rows of D) for the fusion epilogue
+  __shared__ __align__(16) T tiles[2 * kS * D];
+  __shared__ float lzs[NR];
+  T* ks = tiles;
+  T* vt = tiles + kS * D;
+  const int g = a.g0 + (int)blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
@@ -513,18 +520,6 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
     const T* qrow = static_cast<const T*>(a.q) + (((int64_t)b * a.Hq + h) * T_ + min(i, T_ - 1)) * D + 8 * grp;
 #pragma unroll
     for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
-  }
-  // The chunk pass gathers one query's G head rows as one contiguous record: this
-  // workgroup holds exactly the rows of its queries, so it writes them regrouped.
-  if (a.qg && i < T_) {
-    T* qgr = static_cast<T*>(a.qg) + ((((int64_t)b * a.Hkv + g) * T_ + i) * G + r16 % G) * D + 8 * grp;
-#pragma unroll
-    for (int kq = 0; kq < KS; ++kq) {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(&bq[kq]);
-#pragma unroll
-      for (int v = 0; v < 8 / EPV; ++v)
-        *reinterpret_cast<uint4*>(qgr + 32 * kq + v * EPV) = make_uint4(w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]);
-    }
   }
   // Running reference in the log2 domain: finite, far below any logit, so the
   // first chunk with an unmasked token always moves it.
@@ -628,13 +623,77 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
   float lsum = ls;
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);
-  if (i >= T_) return;
-  const int64_t rowq = ((int64_t)b * a.Hq + h) * T_ + i;
-  const float inv = 1.f / lsum;
-  T* owp = static_cast<T*>(a.ow);
+
+  // Fusion (summary page, Methodology 2, Eq. 10, with the window at its
+  // token-level log-mass): out = exp(log Z_win - L) o_win + exp(L_sel - L) *
+  // (sum of the selected chunks' weighted partials), L = LSE(L_sel, log Z_win).
+  // The normalised window rows go through LDS so that the partial rows, read
+  // once here, are read with whole-wave contiguous 16-byte loads; meanwhile
+  // another workgroup on the compute unit keeps the MFMA busy.
+  const int rho = wave * 16 + r16;   // row (query, head) = (rho / G, rho % G) of the block
+  __syncthreads();                   // every wave is done with the K / V^T tiles
+  {
+    const float inv = 1.f / lsum;
 #pragma unroll
-  for (int md = 0; md < MD; ++md) store4<T>(owp + rowq * D + 16 * md + 4 * grp, o[md], inv);
-  if (grp == 0) a.lzw[rowq] = (m + hw_log2(lsum)) * kLn2;
+    for (int md = 0; md < MD; ++md) {
+      const int d = 16 * md + 4 * grp;
+      store4<T>(tiles + swz<PK>(rho, d / EPV) * EPV + d % EPV, o[md], inv);
+    }
+    if (grp == 0) lzs[rho] = (m + hw_log2(lsum)) * kLn2;
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < NR * PK; it += kWinThreads) {
+    const int rr = it / PK, pc = it % PK;
+    const int64_t iq = qb0 + rr / G;
+    if (iq >= T_) continue;
+    const int hq = rr % G;
+    const int64_t rowq = ((int64_t)b * a.Hq + g * G + hq) * T_ + iq;
+    const float lz = lzs[rr];
+    const float lsl = a.lsel ? a.lsel[rowq] : kNegInf;
+    const float L = lsl == kNegInf ? lz : fmaxf(lsl, lz) + __logf(1.f + __expf(-fabsf(lsl - lz)));
+    const float ww = __expf(lz - L);
+    const float wsel = lsl == kNegInf ? 0.f : __expf(lsl - L);
+    float ows[EPV], acc[EPV];
+    {
+      const uint4 u = *reinterpret_cast<const uint4*>(tiles + swz<PK>(rr, pc) * EPV);
+      const T* t = reinterpret_cast<const T*>(&u);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) { ows[e] = to_f<T>(t[e]); acc[e] = 0.f; }
+    }
+    if (wsel > 0.f) {
+      const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * T_ + iq) * a.topk;
+      const T* prow = static_cast<const T*>(a.part) +
+                      ((((int64_t)b * a.gpass + (g - a.g0)) * T_ + iq) * a.topk * G + hq) * D + pc * EPV;
+      // eight slots' loads in flight at a time; padding slots hold no partial row
+      constexpr int U = 8;
+      int s = 0;
+      for (; s + U <= a.topk; s += U) {
+        uint4 u[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+          u[j] = irow[s + j] >= 0 ? *reinterpret_cast<const uint4*>(prow + (int64_t)(s + j) * G * D)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const T* t = reinterpret_cast<const T*>(&u[j]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
+        }
+      }
+      for (; s < a.topk; ++s) {
+        if (irow[s] < 0) continue;
+        const uint4 u = *reinterpret_cast<const uint4*>(prow + (int64_t)s * G * D);
+        const T* t = reinterpret_cast<const T*>(&u);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
+      }
+    }
+    T res[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) res[e] = from_f<T>(ww * ows[e] + wsel * acc[e]);
+    *reinterpret_cast<uint4*>(static_cast<T*>(a.out) + rowq * D + pc * EPV) = *reinterpret_cast<const uint4*>(res);
+    if (a.lse && pc == 0) a.lse[rowq] = L;
+  }
 }
 
 // bf16 tiles fit 128 VGPRs, so two workgroups share a compute unit and their
@@ -648,118 +707,22 @@ __global__ __launch_bounds__(kWinThreads) void window_kernel_f32(WinArgs a) {
   window_body<T, D, G>(a);
 }
 
-struct CombArgs {
-  const void* ow;
-  const float* lzw;
-  const float* lsel;
-  const int32_t* idx;
-  const void* part;
-  void* out;
-  float* lse;
-  int B, Hq, Hkv, topk, g0, gpass;
-  int64_t T;
-};
-
-// Fusion: out = exp(log Z_win - L) o_win + exp(L_sel - L) * sum of the selected
-// partials, L = LSE(L_sel, log Z_win).  PPR lanes per row, 16 bytes each.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void combine_kernel(CombArgs a) {
-  constexpr int EPV = 16 / sizeof(T);
-  constexpr int PPR = D / EPV;
-  const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t rowl = gl / PPR;          // row within this pass: (b, g - g0, i, hh)
-  const int piece = (int)(gl % PPR);
-  const int64_t nrows = (int64_t)a.B * a.gpass * G * a.T;
-  if (rowl >= nrows) return;
-  const int hh = (int)(rowl % G);
-  const int64_t i = (rowl / G) % a.T;
-  const int gi = (int)((rowl / (G * a.T)) % a.gpass);
-  const int b = (int)(rowl / (G * a.T * a.gpass));
-  const int g = a.g0 + gi;
-  if (g >= a.Hkv) return;
-  const int h = g * G + hh;
-  const int64_t rowq = ((int64_t)b * a.Hq + h) * a.T + i;
-  const float lz = a.lzw[rowq];
-  const float ls = a.lsel ? a.lsel[rowq] : kNegInf;
-  const float L = ls == kNegInf ? lz : fmaxf(ls, lz) + __logf(1.f + __expf(-fabsf(ls - lz)));
-  const float ww = __expf(lz - L);
-  const float wsel = ls == kNegInf ? 0.f : __expf(ls - L);
-  float acc[EPV];
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
-  float ows[EPV];
-  {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.ow) + rowq * D + piece * EPV);
-    const T* t = reinterpret_cast<const T*>(&u);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) ows[e] = to_f<T>(t[e]);
-  }
-  if (wsel > 0.f) {
-    const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * a.topk;
-    const T* prow = static_cast<const T*>(a.part) +
-                    ((((int64_t)b * a.gpass + gi) * a.T + i) * a.topk * G + hh) * D + piece * EPV;
-    // eight slots' loads in flight at a time; padding slots hold no partial row
-    constexpr int U = 8;
-    int s = 0;
-    for (; s + U <= a.topk; s += U) {
-      uint4 u[U];
-#pragma unroll
-      for (int j = 0; j < U; ++j)
-        u[j] = irow[s + j] >= 0 ? *reinterpret_cast<const uint4*>(prow + (int64_t)(s + j) * G * D)
-                                : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const T* t = reinterpret_cast<const T*>(&u[j]);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
-      }
-    }
-    for (; s < a.topk; ++s) {
-      if (irow[s] < 0) continue;
-      const uint4 u = *reinterpret_cast<const uint4*>(prow + (int64_t)s * G * D);
-      const T* t = reinterpret_cast<const T*>(&u);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
-    }
-  }
-  float r[EPV];
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) r[e] = ows[e] * ww + acc[e] * wsel;
-  T res[EPV];
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) res[e] = from_f<T>(r[e]);
-  *reinterpret_cast<uint4*>(static_cast<T*>(a.out) + rowq * D + piece * EPV) =
-      *reinterpret_cast<const uint4*>(res);
-  if (a.lse && piece == 0) a.lse[rowq] = L;
-}
-
-template <typename T, int D, int G>
-hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, void* ow, float* lzw,
-                            void* vt, void* qg, int gpp, hipStream_t st) {
+hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, void* vt, int gpp,
+                            hipStream_t st) {
   const int64_t NCf = (a.T + kS - 1) / kS;
   {
     KTimer tm(K_VT, st);
     hipLaunchKernelGGL((vt_kernel<T, D>), dim3((unsigned)NCf, a.Hkv, a.B), dim3(256), 0, st,
                        static_cast<const T*>(a.v), static_cast<T*>(vt), a.Hkv, a.T, NCf);
   }
-  // window part for every head at once (it also writes the regrouped q rows)
-  {
-    WinArgs wa{a.q, a.k, vt, ow, lzw, (ia.NCs > 0 && a.topk > 0) ? qg : nullptr,
-               a.B, a.Hq, a.Hkv, a.S, a.W, a.T, NCf, a.scale};
-    const int QB = 8 * (16 / G);
-    KTimer tm(K_WINDOW, st);
-    const dim3 grid((unsigned)((a.T + QB - 1) / QB), a.Hkv, a.B);
-    if constexpr (sizeof(T) == 2)
-      hipLaunchKernelGGL((window_kernel<T, D, G>), grid, dim3(kWinThreads), 0, st, wa);
-    else
-      hipLaunchKernelGGL((window_kernel_f32<T, D, G>), grid, dim3(kWinThreads), 0, st, wa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const bool chunks = ia.NCs > 0 && a.topk > 0;
+  // per pass of KV groups: the selected chunks (chunk-major), then the window
+  // with the fusion of that pass's partials
   for (int g0 = 0; g0 < a.Hkv; g0 += gpp) {
     const int gp = min(gpp, a.Hkv - g0);
-    if (ia.NCs > 0 && a.topk > 0) {
-      ChunkArgs ca{qg, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part,
+    if (chunks) {
+      ChunkArgs ca{a.q, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part,
                    a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, NCf, a.scale};
       KTimer tm(K_CHUNK_ATTEND, st);
       hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)(ia.NCs * gp), 1, a.B),
@@ -767,12 +730,15 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    CombArgs cb{ow, lzw, ia.lsel, a.idx, part, a.out, a.lse, a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T};
-    constexpr int PPR = D / (16 / (int)sizeof(T));
-    const int64_t nthreads = (int64_t)a.B * gpp * G * a.T * PPR;
-    KTimer tm(K_COMBINE, st);
-    hipLaunchKernelGGL((combine_kernel<T, D, G>), dim3((unsigned)((nthreads + 255) / 256)), dim3(256),
-                       0, st, cb);
+    WinArgs wa{a.q, a.k, vt, chunks ? ia.lsel : nullptr, a.idx, part, a.out, a.lse,
+               a.B, a.Hq, a.Hkv, a.S, a.W, a.topk, g0, gpp, a.T, NCf, a.scale};
+    const int QB = 8 * (16 / G);
+    const dim3 grid((unsigned)((a.T + QB - 1) / QB), (unsigned)gp, a.B);
+    KTimer tm(K_WINDOW, st);
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL((window_kernel<T, D, G>), grid, dim3(kWinThreads), 0, st, wa);
+    else
+      hipLaunchKernelGGL((window_kernel_f32<T, D, G>), grid, dim3(kWinThreads), 0, st, wa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -780,13 +746,13 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
 }
 
 template <typename T, int D>
-hipError_t launch_attend_t(const AttArgs& a, const IdxArgs& ia, void* part, void* ow, float* lzw,
-                           void* vt, void* qg, int gpp, hipStream_t st) {
+hipError_t launch_attend_t(const AttArgs& a, const IdxArgs& ia, void* part, void* vt, int gpp,
+                           hipStream_t st) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, ow, lzw, vt, qg, gpp, st);
-    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, ow, lzw, vt, qg, gpp, st);
-    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, ow, lzw, vt, qg, gpp, st);
-    default: return launch_attend_tg<T, D, 8>(a, ia, part, ow, lzw, vt, qg, gpp, st);
+    case 1: return launch_attend_tg<T, D, 1>(a, ia, part, vt, gpp, st);
+    case 2: return launch_attend_tg<T, D, 2>(a, ia, part, vt, gpp, st);
+    case 4: return launch_attend_tg<T, D, 4>(a, ia, part, vt, gpp, st);
+    default: return launch_attend_tg<T, D, 8>(a, ia, part, vt, gpp, st);
   }
 }
 
@@ -806,10 +772,7 @@ void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
   f += align256((size_t)B * Hkv * T * topk * sizeof(uint32_t));     // entries
   f += align256((size_t)B * Hq * T * topk * sizeof(float));         // chunk weights
   f += align256((size_t)B * Hq * T * sizeof(float));                // lsel
-  f += align256((size_t)B * Hq * T * D * esz);                      // window outputs
-  f += align256((size_t)B * Hq * T * sizeof(float));                // window log-mass
   f += align256((size_t)B * Hkv * ((T + kS - 1) / kS) * kS * D * esz);  // V^T per chunk
-  f += align256((size_t)B * Hq * T * D * esz);                      // q regrouped
   *fixed = f + 256;
   *per_kv_head = align256((size_t)B * (Hq / Hkv) * T * topk * D * esz);
 }
@@ -836,14 +799,8 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   w += align256((size_t)a.B * a.Hq * a.T * a.topk * sizeof(float));
   ia.lsel = reinterpret_cast<float*>(w);
   w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
-  void* ow = w;
-  w += align256((size_t)a.B * a.Hq * a.T * a.D * esz);
-  float* lzw = reinterpret_cast<float*>(w);
-  w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
   void* vt = w;
   w += align256((size_t)a.B * a.Hkv * ((a.T + kS - 1) / kS) * kS * a.D * esz);
-  void* qg = w;
-  w += align256((size_t)a.B * a.Hq * a.T * a.D * esz);
   ia.B = a.B; ia.Hq = a.Hq; ia.Hkv = a.Hkv; ia.topk = a.topk;
   ia.T = a.T; ia.NCs = NCs; ia.ntiles = ntiles;
   void* part = w;
@@ -887,8 +844,8 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, ow, lzw, vt, qg, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, ow, lzw, vt, qg, gpp, st);
-  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, ow, lzw, vt, qg, gpp, st) : launch_attend_t<float, 64>(a, ia, part, ow, lzw, vt, qg, gpp, st);
+  if (a.bf16) return a.D == 128 ? launch_attend_t<bf16_t, 128>(a, ia, part, vt, gpp, st) : launch_attend_t<bf16_t, 64>(a, ia, part, vt, gpp, st);
+  return a.D == 128 ? launch_attend_t<float, 128>(a, ia, part, vt, gpp, st) : launch_attend_t<float, 64>(a, ia, part, vt, gpp, st);
 }
 
 }  // namespace hils

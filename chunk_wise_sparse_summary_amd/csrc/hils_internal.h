@@ -99,7 +99,7 @@ hipError_t launch_decode(const DecArgs& a, hipStream_t st);
 // selected, and does nothing otherwise.
 enum KernelId {
   K_SUMMARIZE, K_SCORE_LSE, K_IDX_COUNT, K_IDX_SCAN_TILES, K_IDX_SCAN_BUCKETS,
-  K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_COMBINE, K_DEC_SCORE, K_DEC_SELECT,
+  K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_DEC_SCORE, K_DEC_SELECT,
   K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_RANK_KEYS, K_TOPK_SCORES,
   K_COUNT
 };

@@ -15,7 +15,7 @@ namespace {
 
 const char* const kNames[K_COUNT] = {
     "summarize", "score_lse", "idx_count", "idx_scan_tiles", "idx_scan_buckets",
-    "idx_fill", "lsel", "window", "chunk_attend", "combine", "dec_score", "dec_select",
+    "idx_fill", "lsel", "window", "chunk_attend", "dec_score", "dec_select",
     "dec_attend", "dec_fuse", "dec_summarize", "v_transpose", "rank_keys", "topk_scores"};
 
 struct Rec {

@@ -210,7 +210,8 @@ int hils_abi_version(void);
  *   names, "*" for all, or NULL to switch timing off.  Enabling clears every
  *   earlier record (after waiting for its events).  Names: summarize,
  *   score_lse, idx_count, idx_scan_tiles, idx_scan_buckets,
- *   idx_fill, lsel, window, chunk_attend, combine, dec_score, dec_select,
+ *   idx_fill, lsel, window (window attention and the fusion), chunk_attend,
+ *   dec_score, dec_select,
  *   dec_attend, dec_fuse, dec_summarize (the summaries of chunks
  *   completed by a decode step), v_transpose, rank_keys,
  *   topk_scores.  HILS_E_UNSUPPORTED for an unknown name
