@@ -172,9 +172,19 @@ __global__ __launch_bounds__(256) void lsel_kernel(IdxArgs a, int L) {
     const int64_t rowq = ((int64_t)b * a.Hq + g * G + hh) * a.T + i;
     const float x = sel ? a.ssel[rowq * a.topk + l] : kNegInf;
     float m = x;
-    for (int o = 1; o < L; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if (L > 1) m = fmaxf(m, xor_lane<1>(m));
+    if (L > 2) m = fmaxf(m, xor_lane<2>(m));
+    if (L > 4) m = fmaxf(m, xor_lane<4>(m));
+    if (L > 8) m = fmaxf(m, xor_lane<8>(m));
+    if (L > 16) m = fmaxf(m, xor_lane<16>(m));
+    if (L > 32) m = fmaxf(m, xor_lane<32>(m));
     float z = (x == kNegInf) ? 0.f : __expf(x - m);
-    for (int o = 1; o < L; o <<= 1) z += __shfl_xor(z, o, kWave);
+    if (L > 1) z += xor_lane<1>(z);
+    if (L > 2) z += xor_lane<2>(z);
+    if (L > 4) z += xor_lane<4>(z);
+    if (L > 8) z += xor_lane<8>(z);
+    if (L > 16) z += xor_lane<16>(z);
+    if (L > 32) z += xor_lane<32>(z);
     const float ls = m == kNegInf ? kNegInf : m + __logf(z);
     if (live && l == 0) a.lsel[rowq] = ls;
     w[hh] = sel ? __expf(x - ls) : 0.f;
