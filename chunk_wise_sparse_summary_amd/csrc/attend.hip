@@ -674,28 +674,29 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
       const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * T_ + iq) * a.topk;
       const T* prow = static_cast<const T*>(a.part) +
                       ((((int64_t)b * a.gpass + (g - a.g0)) * T_ + iq) * a.topk * G + hq) * D + pc * EPV;
-      // eight slots' loads in flight at a time; padding slots hold no partial row
-      constexpr int U = 8;
-      int s = 0;
-      for (; s + U <= a.topk; s += U) {
+      // U slots' idx and partial loads in flight together, with no load waiting
+      // on another: a padding slot's partial row lies inside the buffer but holds
+      // no value, so it is loaded and then dropped by a select
+      constexpr int U = 16;
+      for (int s = 0; s < a.topk; s += U) {
         uint4 u[U];
+        int32_t ix[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j)
-          u[j] = irow[s + j] >= 0 ? *reinterpret_cast<const uint4*>(prow + (int64_t)(s + j) * G * D)
-                                  : make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < U; ++j) {
+          const bool in = s + j < a.topk;
+          ix[j] = in ? irow[s + j] : -1;
+          u[j] = in ? *reinterpret_cast<const uint4*>(prow + (int64_t)(s + j) * G * D)
+                    : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
           const T* t = reinterpret_cast<const T*>(&u[j]);
 #pragma unroll
-          for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
+          for (int e = 0; e < EPV; ++e) {
+            const float f = to_f<T>(t[e]);
+            acc[e] += ix[j] >= 0 ? f : 0.f;
+          }
         }
-      }
-      for (; s < a.topk; ++s) {
-        if (irow[s] < 0) continue;
-        const uint4 u = *reinterpret_cast<const uint4*>(prow + (int64_t)s * G * D);
-        const T* t = reinterpret_cast<const T*>(&u);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc[e] += to_f<T>(t[e]);
       }
     }
     T res[EPV];
