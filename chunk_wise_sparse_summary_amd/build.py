@@ -2,7 +2,7 @@
 
 Every source under csrc/ is compiled to an object in _build/ (in parallel), then
 linked into chunk_wise_sparse_summary_amd/libhils.so.  All HIP code is compiled
-with packed-fp32 instructions disabled.
+with packed-fp32 instructions disabled and MFMA results kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -23,6 +23,9 @@ FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Wno-unused-function", "-Wno-unused-variable",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: no accumulator-register copies
+    # between the MFMA and the VALU work on its results
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
 

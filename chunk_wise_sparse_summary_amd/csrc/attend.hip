@@ -354,15 +354,22 @@ struct ChunkArgs {
 // are staged once; each wave takes 16-row tiles (16/G entries x G heads) of the
 // entries that selected the chunk, with the next tile's q rows prefetched.  Each
 // tile's weighted output goes through a wave-private LDS tile so that every
-// partial row (d values) is written with contiguous 16-byte stores.
+// partial row (d values) is written with contiguous 16-byte stores (pieces of
+// rows written straight from the accumulators, 32 bytes per row and store,
+// run three times slower).  Each wave holds the chunk's K fragments (the A
+// operands of its score tiles) in registers for all of its tiles, so per tile
+// only the V^T fragments and the output staging pass through LDS.
+template <typename T> constexpr int chunk_waves() { return 4; }
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
+__device__ __forceinline__ void chunk_attend_body(const ChunkArgs& a) {
   constexpr int KS = D / 32, MD = D / 16;
   constexpr int NE = 16 / G;  // entries per 16-row tile
+  constexpr int NW = chunk_waves<T>();
   constexpr int OP = D + 16 / (int)sizeof(T);  // padded LDS output row
   __shared__ __align__(16) T ks[kS * D];
   __shared__ __align__(16) T vt[D * kS];
-  __shared__ __align__(16) T ot[4][16 * OP];
+  __shared__ __align__(16) T ot[NW][16 * OP];
   // chunk-major over the pass's groups: the early chunks, candidates of almost
   // every query and so the longest lists, start first for every group
   const int gcount = min(a.gpass, a.Hkv - a.g0);   // groups in this pass
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
   const int64_t base = a.bbase[bucket];
   const T* kc = static_cast<const T*>(a.k) + (((int64_t)b * a.Hkv + g) * a.T + c * kS) * D;
   const T* vtc = static_cast<const T*>(a.vt) + (((int64_t)b * a.Hkv + g) * a.NCf + c) * D * kS;
-  stage_chunk<T, D, 256>(kc, vtc, ks, vt, kS);
+  stage_chunk<T, D, NW * kWave>(kc, vtc, ks, vt, kS);
   __syncthreads();
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -393,36 +400,67 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
     const int e = nt * NE + r16 / G;
     return (nt < ntile && e < n) ? a.entries[base + e] : 0xffffffffu;
   };
-  auto load_q = [&](uint32_t word, Frag<T> (&bq)[KS], float& wt) {
-    const bool valid = word != 0xffffffffu;
-    wt = valid ? a.wq[((((int64_t)b * a.Hkv + g) * a.T + (word >> 6)) * a.topk + (word & 63)) * G + hh]
-               : 0.f;
-    if (valid) {
-      const T* qrow = qbase + (((int64_t)b * a.Hq + g * G + hh) * a.T + (word >> 6)) * D + 8 * grp;
+  // A tile's q rows are read row-contiguous (PPR lanes on the 16-byte pieces of
+  // a row, RPI rows per load, NI loads), so each load touches few cache lines
+  // (one lane per row per load, as the fragments want them, costs a cache-line
+  // lookup per lane), and become MFMA fragments through the wave's LDS tile.
+  constexpr int EPV = 16 / (int)sizeof(T);
+  constexpr int PPR = D / EPV, RPI = kWave / PPR, NI = 16 / RPI;
+  const int qp = lane % PPR, qr = lane / PPR;
+  auto load_q = [&](uint32_t word, uint4 (&raw)[NI], float& wt) {
+    wt = word != 0xffffffffu
+             ? a.wq[((((int64_t)b * a.Hkv + g) * a.T + (word >> 6)) * a.topk + (word & 63)) * G + hh]
+             : 0.f;
 #pragma unroll
-      for (int kq = 0; kq < KS; ++kq) load_frag(bq[kq], qrow + 32 * kq);
-    } else {
-#pragma unroll
-      for (int kq = 0; kq < KS; ++kq) zero_frag(bq[kq]);
+    for (int j = 0; j < NI; ++j) {
+      const int r = RPI * j + qr;                  // tile row: entry r / G, head r % G
+      const uint32_t wr = __shfl(word, r, kWave);  // lanes r (< 16) hold row r's entry
+      raw[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (wr != 0xffffffffu)
+        raw[j] = *reinterpret_cast<const uint4*>(
+            qbase + (((int64_t)b * a.Hq + g * G + r % G) * a.T + (wr >> 6)) * D + qp * EPV);
     }
   };
+  auto to_frags = [&](const uint4 (&raw)[NI], Frag<T> (&f)[KS]) {
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      *reinterpret_cast<uint4*>(myo + (RPI * j + qr) * OP + qp * EPV) = raw[j];
+    wave_lds_sync();
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) load_frag(f[kq], myo + r16 * OP + 8 * grp + 32 * kq);
+    wave_lds_sync();
+  };
 
-  Frag<T> bq[KS], bqn[KS];
-  uint32_t word = load_word(wave), wordn = load_word(wave + 4);
+  constexpr int PKs = D / (16 / (int)sizeof(T));
+  Frag<T> kf[4][KS];   // K rows 16 mt + r16, dims 32 kq + 8 grp .. + 7
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) load_frag_swz<PKs>(kf[mt][kq], ks, 16 * mt + r16, 8 * grp + 32 * kq);
+  Frag<T> bq[KS];
+  uint4 raw[NI];
+  uint32_t word = load_word(wave), wordn = load_word(wave + NW);
   float wt, wtn;
-  load_q(word, bq, wt);
-  for (int nt = wave; nt < ntile; nt += 4) {
-    load_q(wordn, bqn, wtn);               // the next tile's rows
-    const uint32_t wordnn = load_word(nt + 8);
+  load_q(word, raw, wt);
+  to_frags(raw, bq);
+  for (int nt = wave; nt < ntile; nt += NW) {
+    load_q(wordn, raw, wtn);               // the next tile's rows, in flight meanwhile
+    const uint32_t wordnn = load_word(nt + 2 * NW);
     f32x4_t acc[4];
-    score_tile<T, D>(ks, bq, acc, r16, grp);
-    float mx = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kq = 0; kq < KS; ++kq) mma(acc[mt], kf[mt][kq], bq[kq]);
+    }
+    float mx = kNegInf;   // sl2 > 0: the max of the raw logits, scaled once
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) mx = fmaxf(mx, acc[mt][q4] * sl2);
+      for (int q4 = 0; q4 < 4; ++q4) mx = fmaxf(mx, acc[mt][q4]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx *= sl2;
     float p[4][4], ls = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -441,31 +479,39 @@ __global__ __launch_bounds__(256) void chunk_attend_kernel(ChunkArgs a) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) store4<T>(myo + r16 * OP + 16 * md + 4 * grp, o[md], w);
     wave_lds_sync();
-    // 16 rows x D values: each lane stores 16-byte pieces of one row
-    constexpr int EPV = 16 / sizeof(T);
-    constexpr int PPR = D / EPV;          // 16-byte pieces per row
-    constexpr int RPI = kWave / PPR;      // rows per store instruction
+    // 16 rows x D values: PPR lanes store the 16-byte pieces of a row, RPI rows
+    // per store
 #pragma unroll
     for (int r0 = 0; r0 < 16; r0 += RPI) {
-      const int r = r0 + lane / PPR, piece = lane % PPR;
+      const int r = r0 + qr, piece = qp;
       const uint32_t wr = __shfl(word, r, kWave);  // lanes r (< 16) hold row r's entry
       if (wr != 0xffffffffu) {
         const int rh = r % G;
         const int64_t ri = wr >> 6;
         const int rs = wr & 63;
         T* prow = part + (((((int64_t)b * a.gpass + (g - a.g0)) * a.T + ri) * a.topk + rs) * G + rh) * D;
-        // streamed out: the combine pass reads each partial row once, much later
+        // streamed out: the fusion reads each partial row once, much later
         __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(myo + r * OP + piece * EPV),
                                     reinterpret_cast<u32x4*>(prow + piece * EPV));
       }
     }
     wave_lds_sync();
-#pragma unroll
-    for (int kq = 0; kq < KS; ++kq) bq[kq] = bqn[kq];
+    to_frags(raw, bq);
     word = wordn;
     wordn = wordnn;
     wt = wtn;
   }
+}
+
+// bf16 fits 168 VGPRs (three workgroups per compute unit); fp32 operands need
+// the full register file.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(chunk_waves<T>() * kWave) __attribute__((amdgpu_waves_per_eu(3))) void chunk_attend_kernel(ChunkArgs a) {
+  chunk_attend_body<T, D, G>(a);
+}
+template <typename T, int D, int G>
+__global__ __launch_bounds__(chunk_waves<T>() * kWave) void chunk_attend_kernel_f32(ChunkArgs a) {
+  chunk_attend_body<T, D, G>(a);
 }
 
 struct WinArgs {
@@ -736,8 +782,11 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
       ChunkArgs ca{a.q, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part,
                    a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, NCf, a.scale};
       KTimer tm(K_CHUNK_ATTEND, st);
-      hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), dim3((unsigned)(ia.NCs * gp), 1, a.B),
-                         dim3(256), 0, st, ca);
+      const dim3 grid((unsigned)(ia.NCs * gp), 1, a.B);
+      if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), grid, dim3(chunk_waves<T>() * kWave), 0, st, ca);
+      else
+        hipLaunchKernelGGL((chunk_attend_kernel_f32<T, D, G>), grid, dim3(chunk_waves<T>() * kWave), 0, st, ca);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
