@@ -211,9 +211,9 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
   }
 }
 
-// Queries per workgroup: 128 (8 waves) for bf16; 64 (4 waves) for fp32, whose
-// larger tiles would not fit LDS at 128.
-template <typename T> constexpr int rank_q() { return sizeof(T) == 2 ? 128 : 64; }
+// Queries per workgroup: 64 (4 waves; with 8 waves, 128, the 139 VGPRs leave one
+// workgroup per compute unit, and fewer registers spill).
+template <typename T> constexpr int rank_q() { return 64; }
 
 // The prefill selection runs as two kernels per (b, group), the rank keys of
 // one group at a time living in a [T][64 J] scratch:
@@ -238,8 +238,14 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
   using R = RankTiles<T, D, G>;
   constexpr int KS = R::KS, RQ = R::RQ, NT = R::NT;
   using Tile = typename R::Tile;
+  constexpr int NW = RQ / 16;        // waves: 16 queries each
+  constexpr int KSP = 64 + 4;        // padded staging row (words)
   __shared__ __align__(16) T kt[G * 16 * Tile::KP];
   __shared__ float bt[G * 16];
+  // each wave's rank keys of 64 candidates x 16 queries, written back to HBM as
+  // row-contiguous 256-byte runs (one lane per query row and 16-byte piece, as
+  // the score tiles leave them, costs a cache line per lane)
+  __shared__ __align__(16) uint32_t kst[NW][16 * KSP];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
@@ -288,9 +294,24 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
       r[2] = fmaxf(r[2], fmaf(acc[2], a.scale, bk.z) - Lq[hh]);
       r[3] = fmaxf(r[3], fmaf(acc[3], a.scale, bk.w) - Lq[hh]);
     }
-    if (qi < T_)
-      *reinterpret_cast<uint4*>(keys + qi * NCP + c0 + 4 * grp) =
-          make_uint4(order_key(r[0]), order_key(r[1]), order_key(r[2]), order_key(r[3]));
+    uint32_t* kw = kst[wave];
+    *reinterpret_cast<uint4*>(kw + r16 * KSP + c0 % 64 + 4 * grp) =
+        make_uint4(order_key(r[0]), order_key(r[1]), order_key(r[2]), order_key(r[3]));
+    if (c0 % 64 == 48 || c0 + 16 >= nc_wave) {   // a run of 64 candidates, or the wave's last
+      wave_lds_sync();
+      // (one group's keys, T x NCP words, stay below 2^32 words)
+      const uint32_t qw0 = (uint32_t)(qb + 16 * wave);
+      const uint32_t off = qw0 * NCP + (uint32_t)(c0 - c0 % 64) + 4u * (lane % 16);
+      const int qr = lane / 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qq = 4 * j + qr;
+        if (qw0 + qq < (uint32_t)T_)
+          *reinterpret_cast<uint4*>(keys + off + (uint32_t)qq * NCP) =
+              *reinterpret_cast<const uint4*>(kw + qq * KSP + 4 * (lane % 16));
+      }
+      wave_lds_sync();
+    }
   }
 }
 
@@ -317,9 +338,12 @@ __device__ __forceinline__ void rs_rows(float (&v)[CAP], int lane) {
 // dot products (fp32 accumulation) of its 16-byte pieces with the matching
 // piece of its row's q_hat, and a reduce-scatter over the PPR lanes of a row
 // group leaves one row's s_hat per lane.
+// The kernel waits on its loads most of the time (the rank-key row, then the
+// chosen k' rows), so it runs as many waves as the compute unit holds: at most
+// 64 VGPRs (a few spill) for bf16 up to 2048 candidates.
 template <typename T, int D, int G, int J>
-__global__ __launch_bounds__(256) void topk_scores_kernel(SelArgs a, int b, int g,
-                                                          const uint32_t* __restrict__ keys) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(J <= 32 && sizeof(T) == 2 ? 8 : 1)))
+void topk_scores_kernel(SelArgs a, int b, int g, const uint32_t* __restrict__ keys) {
   constexpr int EPP = 16 / (int)sizeof(T);   // elements per 16-byte piece
   constexpr int PPR = D / EPP;               // pieces per row
   constexpr int RPI = kWave / PPR;           // rows per load instruction
