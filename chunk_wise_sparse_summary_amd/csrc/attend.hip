@@ -127,15 +127,22 @@ __global__ __launch_bounds__(1024) void idx_scan_buckets_kernel(IdxArgs a) {
   }
 }
 
-// Entries at their final positions.
+// Entries at their final positions.  Each chunk's position base for this tile
+// (its bucket's base, relative to the first bucket of (b, g), plus the tile's
+// offset in the bucket) is read once, with coalesced loads, into LDS beside the
+// bitmap, so an entry costs LDS lookups and its one store.  (Relative bases fit
+// 32 bits: a (b, g) has T * topk entries.)
 __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
   extern __shared__ uint64_t bm[];
+  int32_t* pos = reinterpret_cast<int32_t*>(bm + a.NCs);
   const int64_t t = blockIdx.x;
   const int g = blockIdx.y, b = blockIdx.z;
-  build_bitmap(a, bm, b, g, t);
-  const int64_t i0 = t * 64;
   const int32_t* toff = a.tile_cnt + (((int64_t)b * a.Hkv + g) * a.ntiles + t) * a.NCs;
   const int64_t* bbase = a.bbase + ((int64_t)b * a.Hkv + g) * a.NCs;
+  const int64_t base0 = bbase[0];
+  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) pos[c] = (int32_t)(bbase[c] - base0) + toff[c];
+  build_bitmap(a, bm, b, g, t);   // its barriers also publish pos
+  const int64_t i0 = t * 64;
   const int n = 64 * a.topk;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
     const int ql = e / a.topk, s = e % a.topk;
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
     const int32_t c = a.idx[(((int64_t)b * a.Hkv + g) * a.T + i) * a.topk + s];
     if (c < 0 || c >= a.NCs) continue;
     const int rank = __popcll(bm[c] & ((1ull << ql) - 1ull));
-    a.entries[bbase[c] + toff[c] + rank] = (uint32_t)(i * 64 + s);
+    a.entries[base0 + pos[c] + rank] = (uint32_t)(i * 64 + s);
   }
 }
 
@@ -900,7 +907,8 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
       hipLaunchKernelGGL(idx_scan_buckets_kernel, dim3(1), dim3(1024), 0, st, ia);
     }
     KTimer tm(K_IDX_FILL, st);
-    hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
+    hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256),
+                       lds + (size_t)NCs * sizeof(int32_t), st, ia);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
