@@ -105,14 +105,17 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecKArgs a) {
   constexpr int PPR = D / EPV;        // lanes per k' row
   constexpr int RPI = kWave / PPR;    // rows per load instruction
   constexpr int NI = PPR;             // load instructions per 64 rows (= kWave / RPI)
-  __shared__ float red[G][4][2];
-  const int slice = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  __shared__ float red[4][2];
+  // one workgroup per (candidate slice, query head, b): a wave's loads are two
+  // batches in flight, not one pair per head of the group in turn
+  const int slice = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int64_t i = a.pos.p[b];
   const int64_t nc = num_candidates(i, a.S, a.W);
   const int64_t bg = (int64_t)b * a.Hkv + g;
-  if (slice == 0) {
+  if (slice == 0 && h % G == 0) {
     // append this step's key/value row
     const int64_t row = (bg * a.Lcap + i) * D;
     const T* kn = static_cast<const T*>(a.k_new) + bg * D;
@@ -123,9 +126,9 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecKArgs a) {
     }
   }
   const int64_t c0 = (int64_t)slice * kSlice;
+  float2* lp = a.w.lpart + ((int64_t)b * a.Hq + h) * a.w.nslice + slice;
   if (c0 >= nc) {
-    for (int hh = threadIdx.x; hh < G; hh += blockDim.x)
-      a.w.lpart[((int64_t)b * a.Hq + g * G + hh) * a.w.nslice + slice] = make_float2(kNegInf, 0.f);
+    if (threadIdx.x == 0) *lp = make_float2(kNegInf, 0.f);
     return;
   }
   const int pc = lane % PPR, rg = lane / PPR;
@@ -133,57 +136,52 @@ __global__ __launch_bounds__(256) void dec_score_kernel(DecKArgs a) {
   const int r = RPI * pc + rg;                        // row whose dot product this lane ends with
   const int64_t c = cw + r;
   const bool ok = c < nc;
-#pragma unroll 1
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    float qv[EPV];
-    {
-      const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) + ((int64_t)b * a.Hq + h) * D + pc * EPV);
-      const T* t = reinterpret_cast<const T*>(&u);
+  float qv[EPV];
+  {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) + ((int64_t)b * a.Hq + h) * D + pc * EPV);
+    const T* t = reinterpret_cast<const T*>(&u);
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) qv[e] = to_f<T>(t[e]);
+    for (int e = 0; e < EPV; ++e) qv[e] = to_f<T>(t[e]);
+  }
+  const T* kb = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * a.NCcap + cw) * D + pc * EPV;
+  const float bv = ok ? a.bsum[((int64_t)b * a.Hq + h) * a.NCcap + c] : 0.f;
+  float v[NI];
+  // two batches of loads keep the live registers within four waves per SIMD
+  constexpr int NB = NI >= 8 ? NI / 2 : NI;
+#pragma unroll
+  for (int t0 = 0; t0 < NI; t0 += NB) {
+    uint4 u[NB];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const int row = RPI * (t0 + t) + rg;
+      u[t] = cw + row < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)row * D) : make_uint4(0u, 0u, 0u, 0u);
     }
-    const T* kb = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * a.NCcap + cw) * D + pc * EPV;
-    const float bv = ok ? a.bsum[((int64_t)b * a.Hq + h) * a.NCcap + c] : 0.f;
-    float v[NI];
-    // two batches of loads keep the live registers within four waves per SIMD
-    constexpr int NB = NI >= 8 ? NI / 2 : NI;
 #pragma unroll
-    for (int t0 = 0; t0 < NI; t0 += NB) {
-      uint4 u[NB];
+    for (int t = 0; t < NB; ++t) {
+      const T* x = reinterpret_cast<const T*>(&u[t]);
+      float acc = 0.f;
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const int row = RPI * (t0 + t) + rg;
-        u[t] = cw + row < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)row * D) : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const T* x = reinterpret_cast<const T*>(&u[t]);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) acc = fmaf(qv[e], to_f<T>(x[e]), acc);
-        v[t0 + t] = acc;
-      }
-    }
-    // butterfly over the PPR lanes of a row: after the step with mask m, lanes
-    // with bit m set hold the upper half of the remaining row sets
-    butterfly<PPR / 2, NI>(v, lane);
-    const float s = fmaf(v[0], a.scale, bv);
-    if (ok) a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + c] = s;
-    const float xl = ok ? s * kLog2e : kNegInf;
-    const float mw = wave_max(xl);
-    const float zw = wave_sum(xl == kNegInf ? 0.f : hw_exp2(xl - mw));
-    if (lane == 0) {
-      red[hh][wave][0] = mw;
-      red[hh][wave][1] = zw;
+      for (int e = 0; e < EPV; ++e) acc = fmaf(qv[e], to_f<T>(x[e]), acc);
+      v[t0 + t] = acc;
     }
   }
+  // butterfly over the PPR lanes of a row: after the step with mask m, lanes
+  // with bit m set hold the upper half of the remaining row sets
+  butterfly<PPR / 2, NI>(v, lane);
+  const float s = fmaf(v[0], a.scale, bv);
+  if (ok) a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + c] = s;
+  const float xl = ok ? s * kLog2e : kNegInf;
+  const float mw = wave_max(xl);
+  const float zw = wave_sum(xl == kNegInf ? 0.f : hw_exp2(xl - mw));
+  if (lane == 0) {
+    red[wave][0] = mw;
+    red[wave][1] = zw;
+  }
   __syncthreads();
-  if (threadIdx.x < G) {
-    const int hh = threadIdx.x;
+  if (threadIdx.x == 0) {
     float M = kNegInf, Z = 0.f;
-    for (int w = 0; w < 4; ++w) lse_merge(M, Z, red[hh][w][0], red[hh][w][1]);
-    a.w.lpart[((int64_t)b * a.Hq + g * G + hh) * a.w.nslice + slice] = make_float2(M, Z);
+    for (int w = 0; w < 4; ++w) lse_merge(M, Z, red[w][0], red[w][1]);
+    *lp = make_float2(M, Z);
   }
 }
 
@@ -558,7 +556,7 @@ template <typename T, int D, int G>
 hipError_t launch_decode_tg(const DecKArgs& k, hipStream_t st) {
   {
     KTimer tm(K_DEC_SCORE, st);
-    hipLaunchKernelGGL((dec_score_kernel<T, D, G>), dim3(k.w.nslice, k.Hkv, k.B), dim3(256), 0, st, k);
+    hipLaunchKernelGGL((dec_score_kernel<T, D, G>), dim3(k.w.nslice, k.Hq, k.B), dim3(256), 0, st, k);
   }
   if (k.topk > 0) launch_select_j<G>(k, st);
   {
