@@ -486,15 +486,21 @@ __global__ __launch_bounds__(kAttThreads) void dec_attend_kernel(DecKArgs a) {
   }
 }
 
-// One wave per (b, query head): the output is the average of the items'
-// normalised outputs weighted by exp(log-weight), and L the log of the total
-// weight (the LSE over the selected chunks' s_hat and the window's log-mass).
+// One workgroup of kFuseWaves waves per (b, query head): the output is the
+// average of the items' normalised outputs weighted by exp(log-weight), and L
+// the log of the total weight (the LSE over the selected chunks' s_hat and the
+// window's log-mass).  The weights take one item per thread; wave w sums every
+// kFuseWaves-th item and the waves' sums meet in LDS.
+constexpr int kFuseWaves = 4;
+static_assert(64 * kFuseWaves >= 256, "one thread per item (at most 256 items)");
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64) void dec_fuse_kernel(DecKArgs a) {
+__global__ __launch_bounds__(64 * kFuseWaves) void dec_fuse_kernel(DecKArgs a) {
   constexpr int DPL = D / kWave;
   __shared__ float wts[256];
+  __shared__ float red[kFuseWaves][D];
+  __shared__ float mz[kFuseWaves][2];
   const int h = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int g = h / G, hl = h % G;
   const int64_t i = a.pos.p[b];
   const int64_t lw = window_left(i, a.S, a.W);
@@ -502,31 +508,57 @@ __global__ __launch_bounds__(64) void dec_fuse_kernel(DecKArgs a) {
   const int nitems = nsel + (int)(i / kS - lw / kS + 1);   // <= 256 (checked on the host)
   const int64_t bg = (int64_t)b * a.Hkv + g;
   const float* ap = a.w.apart + (bg * a.w.nitems * G + hl) * (D + 2);
-  float mx = kNegInf;
-  for (int it = lane; it < nitems; it += kWave) mx = fmaxf(mx, ap[(int64_t)it * G * (D + 2) + D]);
-  mx = wave_max(mx);
+  // item weights exp(lw_item - max): one item per thread, block max and sum
+  const int it0 = threadIdx.x;
+  const float lwi = it0 < nitems ? ap[(int64_t)it0 * G * (D + 2) + D] : kNegInf;
+  float mx = wave_max(lwi);
+  if (lane == 0) mz[wave][0] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kFuseWaves; ++w) mx = fmaxf(mx, mz[w][0]);
+  const float wi = it0 < nitems ? __expf(lwi - mx) : 0.f;
+  wts[it0] = wi;
+  const float zw = wave_sum(wi);
+  if (lane == 0) mz[wave][1] = zw;
+  __syncthreads();
   float z = 0.f;
-  for (int it = lane; it < nitems; it += kWave) {
-    const float w = __expf(ap[(int64_t)it * G * (D + 2) + D] - mx);
-    wts[it] = w;
-    z += w;
-  }
-  z = wave_sum(z);
-  wave_lds_sync();
+#pragma unroll
+  for (int w = 0; w < kFuseWaves; ++w) z += mz[w][1];
+  // wave w sums items w, w + kFuseWaves, ..., eight loads in flight per lane
   float res[DPL];
 #pragma unroll
   for (int t = 0; t < DPL; ++t) res[t] = 0.f;
-#pragma unroll 4
-  for (int it = 0; it < nitems; ++it) {
-    const float w = wts[it];
-    const float* pp = ap + (int64_t)it * G * (D + 2) + lane * DPL;
+  constexpr int U = 8;
+  for (int itb = wave; itb < nitems; itb += U * kFuseWaves) {
+    float x[U][DPL];
 #pragma unroll
-    for (int t = 0; t < DPL; ++t) res[t] = fmaf(w, pp[t], res[t]);
+    for (int u = 0; u < U; ++u) {
+      const int it = itb + u * kFuseWaves;
+      const float* pp = ap + (int64_t)min(it, nitems - 1) * G * (D + 2) + lane * DPL;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) x[u][t] = pp[t];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = itb + u * kFuseWaves;
+      const float w = it < nitems ? wts[it] : 0.f;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) res[t] = fmaf(w, x[u][t], res[t]);
+    }
   }
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) red[wave][lane * DPL + t] = res[t];
+  __syncthreads();
+  if (wave != 0) return;
   const float inv = 1.f / z;
   T* orow = static_cast<T*>(a.out) + ((int64_t)b * a.Hq + h) * D;
 #pragma unroll
-  for (int t = 0; t < DPL; ++t) orow[lane * DPL + t] = from_f<T>(res[t] * inv);
+  for (int t = 0; t < DPL; ++t) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFuseWaves; ++w) v += red[w][lane * DPL + t];
+    orow[lane * DPL + t] = from_f<T>(v * inv);
+  }
   if (a.lse && lane == 0) a.lse[(int64_t)b * a.Hq + h] = mx + __logf(z);
 }
 
@@ -565,7 +597,7 @@ hipError_t launch_decode_tg(const DecKArgs& k, hipStream_t st) {
   }
   {
     KTimer tm(K_DEC_FUSE, st);
-    hipLaunchKernelGGL((dec_fuse_kernel<T, D, G>), dim3(k.Hq, k.B), dim3(64), 0, st, k);
+    hipLaunchKernelGGL((dec_fuse_kernel<T, D, G>), dim3(k.Hq, k.B), dim3(64 * kFuseWaves), 0, st, k);
   }
   return hipGetLastError();
 }
