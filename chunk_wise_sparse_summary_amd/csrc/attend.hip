@@ -537,7 +537,8 @@ struct WinArgs {
 
 template <int N> using u32v = uint32_t __attribute__((ext_vector_type(N)));
 
-constexpr int kWinThreads = 512;
+constexpr int kWinWaves = 8;
+constexpr int kWinThreads = 64 * kWinWaves;
 constexpr float kRefLog2 = -1e30f;   // initial softmax reference (log2 domain)
 constexpr float kLazyLog2 = 8.f;     // headroom before the reference must move
 
@@ -553,8 +554,8 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
   constexpr int PK = D / EPV, PV = kS / EPV;              // 16-byte pieces per K / V^T row
   constexpr int NPK = kS * PK / kWinThreads, NPV = D * PV / kWinThreads;
   constexpr int QW = 16 / G;        // queries per wave
-  constexpr int QB = 8 * QW;        // queries per block
-  constexpr int NR = 8 * 16;        // (query, head) rows per block
+  constexpr int QB = kWinWaves * QW;   // queries per block
+  constexpr int NR = kWinWaves * 16;   // (query, head) rows per block
   // K and V^T tiles during the window loop, then the block's normalised window
   // outputs (NR rows of D) for the fusion epilogue
   __shared__ __align__(16) T tiles[2 * kS * D];
@@ -799,7 +800,7 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
     }
     WinArgs wa{a.q, a.k, vt, chunks ? ia.lsel : nullptr, a.idx, part, a.out, a.lse,
                a.B, a.Hq, a.Hkv, a.S, a.W, a.topk, g0, gpp, a.T, NCf, a.scale};
-    const int QB = 8 * (16 / G);
+    const int QB = kWinWaves * (16 / G);
     const dim3 grid((unsigned)((a.T + QB - 1) / QB), (unsigned)gp, a.B);
     KTimer tm(K_WINDOW, st);
     if constexpr (sizeof(T) == 2)
