@@ -377,11 +377,11 @@ __device__ __forceinline__ void chunk_attend_body(const ChunkArgs& a) {
   __shared__ __align__(16) T ks[kS * D];
   __shared__ __align__(16) T vt[D * kS];
   __shared__ __align__(16) T ot[NW][16 * OP];
-  // chunk-major over the pass's groups: the early chunks, candidates of almost
-  // every query and so the longest lists, start first for every group
-  const int gcount = min(a.gpass, a.Hkv - a.g0);   // groups in this pass
-  const int64_t c = blockIdx.x / gcount;
-  const int g = a.g0 + (int)(blockIdx.x % gcount), b = blockIdx.z;
+  // group by group (one group's q, G rows of every query, fits the last-level
+  // cache while its chunks gather them), and within a group the early chunks,
+  // candidates of almost every query and so the longest lists, first
+  const int64_t c = blockIdx.x % a.NCs;
+  const int g = a.g0 + (int)(blockIdx.x / a.NCs), b = blockIdx.z;
   const int64_t bucket = ((int64_t)b * a.Hkv + g) * a.NCs + c;
   const int n = a.bcount[bucket];
   if (n == 0) return;
