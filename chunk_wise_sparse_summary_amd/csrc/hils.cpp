@@ -136,14 +136,19 @@ hils_status hils_select(const hils_shape* s, const void* q_hat, const void* k_su
   if (s->top_k == 0) return HILS_OK;  // nothing to select
   int n_slots = 0;
   int64_t stride = 0;
-  const size_t need = hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len,
-                                             s->chunk, s->io_dtype == HILS_BF16, &n_slots, &stride);
-  if (!ws || ws_bytes < need) return HILS_E_WORKSPACE;
+  size_t fixed = 0, per_group = 0;
+  hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
+                         s->io_dtype == HILS_BF16, &n_slots, &stride, &fixed, &per_group);
+  if (!ws || ws_bytes < fixed + per_group) return HILS_E_WORKSPACE;
   hils::SelArgs a{};
   a.qh = q_hat; a.ksum = k_sum; a.bsum = b_sum; a.idx = sel_idx; a.ssel = sel_score;
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
-  a.scratch = reinterpret_cast<float*>(w);
-  a.L = reinterpret_cast<float*>(w + (size_t)n_slots * stride * sizeof(float));
+  a.L = reinterpret_cast<float*>(w);
+  a.scratch = reinterpret_cast<float*>(w + (fixed - 256));
+  const size_t groups = (ws_bytes - fixed) / per_group;
+  const int nbg = s->batch * s->heads_kv;
+  a.gpass = groups < (size_t)nbg ? (int)groups : nbg;
+  a.group_words = (int64_t)(per_group / sizeof(uint32_t));
   a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
   a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
   a.T = s->seq_len; a.NCs = s->seq_len / s->chunk; a.scale = eff_scale(s);

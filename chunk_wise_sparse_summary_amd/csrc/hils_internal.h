@@ -39,17 +39,22 @@ struct SelArgs {
   int32_t* idx;
   float* ssel;
   float* L;          // [B, Hq, T] scratch (G > 1)
-  float* scratch;    // rank keys of one (b, group): n_slots rows of slot_stride
+  float* scratch;    // rank keys of gpass (b, group) pairs, group_words apart:
+                     // n_slots rows of slot_stride each
   int B, Hq, Hkv, D, S, W, topk;
   bool bf16;
   int64_t T, NCs;
   float scale;
   int n_slots;
   int64_t slot_stride;  // keys per row
+  int gpass;            // (b, group) pairs per launch
+  int64_t group_words;  // keys of one (b, group), padded
 };
 hipError_t launch_select(const SelArgs& a, hipStream_t st);
+// Bytes for every (b, group) at once; a workspace of fixed + k * per_group
+// bytes (k >= 1) runs the selection k pairs per launch.
 size_t select_workspace(int B, int Hq, int Hkv, int64_t T, int S, bool bf16, int* n_slots,
-                        int64_t* slot_stride);
+                        int64_t* slot_stride, size_t* fixed = nullptr, size_t* per_group = nullptr);
 
 struct AttArgs {
   const void* q;

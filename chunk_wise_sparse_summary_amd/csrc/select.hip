@@ -233,8 +233,11 @@ struct RankTiles {
 };
 
 template <typename T, int D, int G, int NCP>
-__global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, int b, int g,
+__global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, int bg0,
                                                                     uint32_t* __restrict__ keys) {
+  // (b, group) bg0 + blockIdx.y of this launch's groups, each with its own keys
+  const int b = (bg0 + (int)blockIdx.y) / a.Hkv, g = (bg0 + (int)blockIdx.y) % a.Hkv;
+  keys += (int64_t)blockIdx.y * a.group_words;
   using R = RankTiles<T, D, G>;
   constexpr int KS = R::KS, RQ = R::RQ, NT = R::NT;
   using Tile = typename R::Tile;
@@ -343,7 +346,9 @@ __device__ __forceinline__ void rs_rows(float (&v)[CAP], int lane) {
 // 64 VGPRs (a few spill) for bf16 up to 2048 candidates.
 template <typename T, int D, int G, int J>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(J <= 32 && sizeof(T) == 2 ? 8 : 1)))
-void topk_scores_kernel(SelArgs a, int b, int g, const uint32_t* __restrict__ keys) {
+void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
+  const int b = (bg0 + (int)blockIdx.y) / a.Hkv, g = (bg0 + (int)blockIdx.y) % a.Hkv;
+  keys += (int64_t)blockIdx.y * a.group_words;
   constexpr int EPP = 16 / (int)sizeof(T);   // elements per 16-byte piece
   constexpr int PPR = D / EPP;               // pieces per row
   constexpr int RPI = kWave / PPR;           // rows per load instruction
@@ -426,15 +431,17 @@ hipError_t launch_rank_j(const SelArgs& a, hipStream_t st) {
   constexpr int RQ = rank_q<T>();
   const dim3 tiles((unsigned)((a.T + RQ - 1) / RQ)), rows((unsigned)((a.T + 3) / 4));
   uint32_t* keys = reinterpret_cast<uint32_t*>(a.scratch);
-  for (int b = 0; b < a.B; ++b) {
-    for (int g = 0; g < a.Hkv; ++g) {
-      {
-        KTimer tm(K_RANK_KEYS, st);
-        hipLaunchKernelGGL((rank_keys_kernel<T, D, G, 64 * J>), tiles, dim3(RQ * 4), 0, st, a, b, g, keys);
-      }
-      KTimer tm(K_TOPK_SCORES, st);
-      hipLaunchKernelGGL((topk_scores_kernel<T, D, G, J>), rows, dim3(256), 0, st, a, b, g, keys);
+  // as many (b, group) pairs per launch as the workspace holds rank keys for
+  const int nbg = a.B * a.Hkv;
+  for (int bg0 = 0; bg0 < nbg; bg0 += a.gpass) {
+    const int n = min(a.gpass, nbg - bg0);
+    {
+      KTimer tm(K_RANK_KEYS, st);
+      hipLaunchKernelGGL((rank_keys_kernel<T, D, G, 64 * J>), dim3(tiles.x, (unsigned)n), dim3(RQ * 4), 0, st,
+                         a, bg0, keys);
     }
+    KTimer tm(K_TOPK_SCORES, st);
+    hipLaunchKernelGGL((topk_scores_kernel<T, D, G, J>), dim3(rows.x, (unsigned)n), dim3(256), 0, st, a, bg0, keys);
   }
   return hipGetLastError();
 }
@@ -482,16 +489,19 @@ int pick_J(int64_t NCs) {
 }  // namespace
 
 size_t select_workspace(int B, int Hq, int Hkv, int64_t T, int S, bool bf16, int* n_slots,
-                        int64_t* slot_stride) {
+                        int64_t* slot_stride, size_t* fixed, size_t* per_group) {
   (void)bf16;
   const int64_t NCs = T / S;
   const int J = pick_J(NCs);
   const int64_t stride = 64 * (int64_t)J;   // rank keys of one query
   if (n_slots) *n_slots = (int)T;            // rows of one (b, group)
   if (slot_stride) *slot_stride = stride;
-  size_t bytes = (size_t)T * stride * sizeof(uint32_t);   // one (b, group) at a time
-  if (Hq / Hkv > 1) bytes += (size_t)B * Hq * T * sizeof(float);
-  return bytes + 256;
+  // the per-head LSE, then the rank keys of every (b, group) (fewer make passes)
+  const size_t f = ((Hq / Hkv > 1 ? (size_t)B * Hq * T * sizeof(float) : 0) + 255) / 256 * 256 + 256;
+  const size_t pg = ((size_t)T * stride * sizeof(uint32_t) + 255) / 256 * 256;
+  if (fixed) *fixed = f;
+  if (per_group) *per_group = pg;
+  return f + (size_t)B * Hkv * pg;
 }
 
 hipError_t launch_select(const SelArgs& a, hipStream_t st) {

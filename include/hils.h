@@ -129,6 +129,9 @@ hils_status hils_summarize(const hils_shape* shape, const void* k, const void* q
  * sel_idx   [B, Hkv, T, k]       int32 out: chunk ids ascending, -1 padded
  * sel_score [B, Hq, T, k]        fp32 out: each head's s_hat at sel_idx, -inf padded
  * Requires T <= 64 * 4096 (at most 4096 chunks) for this build.
+ * The workspace holds each head's LSE and the rank keys of every (b, group); a
+ * workspace smaller than hils_workspace_bytes() but holding at least one
+ * (b, group)'s keys runs the same computation a few (b, group) pairs at a time.
  */
 hils_status hils_select(const hils_shape* shape, const void* q_hat, const void* k_sum,
                         const float* b_sum, int32_t* sel_idx, float* sel_score,

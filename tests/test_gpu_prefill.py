@@ -275,6 +275,38 @@ def test_batch_independence(hils):
         assert torch.equal(a[key][0], b[key][0]), key
 
 
+def test_select_in_group_passes(hils):
+    """A workspace too small for every (b, group)'s rank keys makes hils_select
+    rank a few pairs per launch (here 1 and 3 of 8); idx and s_hat must equal the
+    one-pass run bit for bit, and one byte less than a single pair is refused."""
+    wl = wk.custom(name="selpasses", dtype="bf16", B=2, Hq=8, Hkv=4, d=128, T=3000, S=64, k=8, W=128)
+    say("select passes")
+    x, xd = _inputs(wl, seed=7)
+    shape = _shape(hils, wl)
+    full = _gpu_prefill(hils, xd, wl)
+    NC = wl.T // wl.S
+    ks = torch.empty((wl.B, wl.Hq, NC, wl.d), dtype=wl.torch_dtype, device=DEV)
+    bs = torch.empty((wl.B, wl.Hq, NC), dtype=torch.float32, device=DEV)
+    hils.hils_summarize(xd["k"], xd["q_land"], ks, bs, shape)
+    al = lambda n: -(-n // 256) * 256
+    J = next(j for j in (1, 4, 16, 32, 64) if 64 * j >= NC)
+    fixed = al(wl.B * wl.Hq * wl.T * 4) + 256          # per-head LSE (G > 1)
+    per = al(wl.T * 64 * J * 4)                        # one (b, group)'s rank keys
+    assert hils.hils_workspace_bytes(shape, hils.OP_SELECT) == fixed + wl.B * wl.Hkv * per
+    for pairs in (1, 3):
+        ws = torch.empty(fixed + pairs * per, dtype=torch.uint8, device=DEV)
+        idx = torch.empty((wl.B, wl.Hkv, wl.T, wl.k), dtype=torch.int32, device=DEV)
+        ssel = torch.empty((wl.B, wl.Hq, wl.T, wl.k), dtype=torch.float32, device=DEV)
+        hils.hils_select(xd["q_hat"], ks, bs, idx, ssel, shape, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, full["idx"]), pairs
+        assert torch.equal(ssel, full["ssel"]), pairs
+    small = torch.empty(fixed + per - 256, dtype=torch.uint8, device=DEV)
+    with pytest.raises(hils.HilsError):
+        hils.hils_select(xd["q_hat"], ks, bs, torch.empty_like(full["idx"]),
+                         torch.empty_like(full["ssel"]), shape, small)
+
+
 def test_attend_in_group_passes(hils):
     """A workspace too small for every KV head's partial outputs makes hils_attend_fuse
     run the selected part a few groups at a time (here 1 and 3 of 4 groups per
