@@ -172,12 +172,22 @@ __global__ __launch_bounds__(256) void lsel_kernel(IdxArgs a, int L) {
   const int64_t i = rr % a.T;
   const int g = (int)((rr / a.T) % a.Hkv);
   const int b = (int)(rr / (a.T * a.Hkv));
-  const bool sel = l < a.topk && a.idx[rr * a.topk + l] >= 0;
+  // the index and every head's score load together (a slot below k lies inside
+  // its row either way); a padding slot is dropped afterwards
+  const bool inrow = l < a.topk;
+  const int32_t id = inrow ? a.idx[rr * a.topk + l] : -1;
+  float xs[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const int64_t rowq = ((int64_t)b * a.Hq + g * G + hh) * a.T + i;
+    xs[hh] = inrow ? a.ssel[rowq * a.topk + l] : kNegInf;
+  }
+  const bool sel = id >= 0;
   float w[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const int64_t rowq = ((int64_t)b * a.Hq + g * G + hh) * a.T + i;
-    const float x = sel ? a.ssel[rowq * a.topk + l] : kNegInf;
+    const float x = sel ? xs[hh] : kNegInf;
     float m = x;
     if (L > 1) m = fmaxf(m, xor_lane<1>(m));
     if (L > 2) m = fmaxf(m, xor_lane<2>(m));
