@@ -91,14 +91,14 @@ def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
     return {
         "summarize": ("hbm", summary_bytes(B, Hq, Hkv, T, d, S, esz), "B"),
         "score_lse": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
-        # these three run once per (b, KV group): one group's share per launch
-        "rank_keys": ("mfma", G * ncand * 2.0 * d, "FLOP"),
-        # the rank keys of every (query, candidate) of the group read once
-        # the group's rank keys and q_hat rows read once, its k' and b' once (the
-        # chosen rows are gathered from L2), the index rows and each head's
+        # these two run once per pass of (b, KV group) pairs, every pair in one
+        # pass with the full workspace: per launch, all B * Hkv groups' shares
+        "rank_keys": ("mfma", B * Hkv * G * ncand * 2.0 * d, "FLOP"),
+        # per group: its rank keys and q_hat rows read once, its k' and b' once
+        # (the chosen rows are gathered from L2), the index rows and each head's
         # s_hat on the choice written
-        "topk_scores": ("hbm", ncand * 4.0 + T * G * d * esz + G * NC * (d * esz + 4.0)
-                        + T * k * 4.0 + G * nsel * 4.0, "B"),
+        "topk_scores": ("hbm", B * Hkv * (ncand * 4.0 + T * G * d * esz + G * NC * (d * esz + 4.0)
+                                          + T * k * 4.0 + G * nsel * 4.0), "B"),
         # K and V^T of every chunk once per KV head; per (query, group, slot)
         # entry: the entry word, G rows of q and G chunk weights read, G weighted
         # partial rows written
