@@ -16,8 +16,8 @@
 // attended by every query that selected it, in MFMA tiles of 16 (query, head)
 // rows; each visit writes its weighted output exp(s_hat_c - L_sel) o_c
 // (L_sel = LSE over the selected chunks only) to a partial slot.  The window
-// part is dense and runs query-major, flash-style, writing o_win and log Z_win;
-// a last, fully coalesced pass fuses:
+// part is dense and runs query-major, flash-style; its epilogue fuses, reading
+// each row's partials with coalesced loads:
 //   out_i = exp(log Z_win - L) o_win + exp(L_sel - L) * sum_slots partial,
 //   L = LSE(L_sel, log Z_win).
 // The (query, slot) lists per chunk are built deterministically: per 64-query

@@ -215,9 +215,10 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
 // workgroup per compute unit, and fewer registers spill).
 template <typename T> constexpr int rank_q() { return 64; }
 
-// The prefill selection runs as two kernels per (b, group), the rank keys of
-// one group at a time living in a [T][64 J] scratch:
-//   rank_keys  per 128-query tile and 16-chunk k' tile (k' of all G heads staged
+// The prefill selection runs as two kernels over every (b, group) of a pass
+// (the grids' second dimension), each group's rank keys in its own [T][64 J]
+// scratch:
+//   rank_keys  per 64-query tile and 16-chunk k' tile (k' of all G heads staged
 //              once in LDS): wave w owns queries 16 w .. 16 w + 15 of the tile and
 //              every head of the group, so the rank key r = max over heads of
 //              s_hat - L_h (r = s_hat for one head) forms in registers
