@@ -4,10 +4,16 @@
 One step = one pass of the whole path over synthetic inputs already resident in
 HBM: a 128K-token prefill forward (hils_summarize + hils_select +
 hils_attend_fuse; B=1, 32 query / 8 KV heads, d=128, S=64, k=32, W=1024,
-per-head scales U[0.5, 2]) followed by 64 decode steps over the 512K-token
-caches of 4 sequences (hils_decode_step; k=32, W=1024).  Every call is timed
-with HIP events on the stream the library launches on (torch's current
-stream).  Prints one JSON line.
+per-head scales U[0.5, 2]) followed by 256 decode steps over the 512K-token
+caches of 4 sequences (hils_decode_step; k=32, W=1024; four chunk completions).
+`value` is the prefill rate (tokens/s of the 128K forward); the decode rate is
+reported beside it (decode_us_per_step, decode_us_per_token).  After the timed
+steps, two more workloads are timed on their own: the 8K prefill (32/8 heads,
+k=16, W=512) and 256 decode steps over one 4M-token cache (k=64, 8 needles).
+
+Every call is timed with HIP events on the stream the library launches on
+(torch's current stream); per-kernel durations come from the library's own
+HIP-event timing.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -76,11 +82,22 @@ def selected_entries(B, Hkv, T, S, W, k):
     return float(B * Hkv * np.sum(np.minimum(k, nc)))
 
 
-def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
-    """Algorithmic work of one launch of each prefill kernel: (bound, amount, unit).
+def attended_parts(B, Hq, T, d, S, W, k):
+    """Attended FLOPs of the selected chunks and of the window (4d per attended
+    (head, query, token): QK^T and PV), the two parts of sum_{i,h} 4d(min(k,|C_i|)S + |Win_i|)."""
+    nc, win = window_stats(T, S, W)
+    return (float(B * Hq * np.sum(4.0 * d * np.minimum(k, nc) * S)),
+            float(B * Hq * np.sum(4.0 * d * win)))
 
-    FLOPs count the MFMA contractions; bytes count each operand the kernel must
-    move through HBM once in this design (no cache reuse assumed or credited)."""
+
+def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
+    """Work of one launch of each prefill kernel: {kernel: (bound, amount, unit, design_bytes)}.
+
+    The bound and amount are the ones the method prices the kernel on: attended
+    FLOPs on the bf16 MFMA peak for the two attention kernels, score FLOPs for
+    the score passes, HBM bytes for the memory-bound ones.  design_bytes counts
+    each operand the kernel must move through HBM once in this design (no cache
+    reuse assumed or credited); the counters' traffic is compared with it."""
     G = Hq // Hkv
     NC = T // S
     nc, win = window_stats(T, S, W)
@@ -88,29 +105,45 @@ def kernel_work(B, Hq, Hkv, T, d, S, W, k, esz=2):
     nsel = float(np.sum(np.minimum(k, nc)))
     ent = selected_entries(B, Hkv, T, S, W, k)
     rows = float(B * Hq * T)
+    f_sel, f_win = attended_parts(B, Hq, T, d, S, W, k)
+    sumb = summary_bytes(B, Hq, Hkv, T, d, S, esz)
+    # per group: its rank keys and q_hat rows read once, its k' and b' once (the
+    # chosen rows are gathered from L2), the index rows and each head's s_hat on
+    # the choice written
+    topk_b = B * Hkv * (ncand * 4.0 + T * G * d * esz + G * NC * (d * esz + 4.0) + T * k * 4.0
+                        + G * nsel * 4.0)
+    # K and V^T of every chunk once per KV head; per (query, group, slot) entry:
+    # the entry word, G rows of q and G chunk weights read, G weighted partial
+    # rows written
+    chunk_b = float(B * Hkv * NC * S * d * esz * 2) + ent * (4 + G * d * esz * 2 + G * 4)
+    # per row the q row, the selection normaliser, the row's partials, its
+    # group's index row, the output and lse; K and V^T once per chunk and KV head
+    win_b = (rows * (d * esz * 2 + 8) + B * Hq * nsel * d * esz + B * Hkv * T * k * 4.0
+             + float(B * Hkv * NC * S * d * esz * 2))
     return {
-        "summarize": ("hbm", summary_bytes(B, Hq, Hkv, T, d, S, esz), "B"),
-        "score_lse": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP"),
-        # these two run once per pass of (b, KV group) pairs, every pair in one
-        # pass with the full workspace: per launch, all B * Hkv groups' shares
-        "rank_keys": ("mfma", B * Hkv * G * ncand * 2.0 * d, "FLOP"),
-        # per group: its rank keys and q_hat rows read once, its k' and b' once
-        # (the chosen rows are gathered from L2), the index rows and each head's
-        # s_hat on the choice written
-        "topk_scores": ("hbm", B * Hkv * (ncand * 4.0 + T * G * d * esz + G * NC * (d * esz + 4.0)
-                                          + T * k * 4.0 + G * nsel * 4.0), "B"),
-        # K and V^T of every chunk once per KV head; per (query, group, slot)
-        # entry: the entry word, G rows of q and G chunk weights read, G weighted
-        # partial rows written
-        "chunk_attend": ("hbm", float(B * Hkv * NC * S * d * esz * 2)
-                         + ent * (4 + G * d * esz * 2 + G * 4), "B"),
-        # window attention with the fusion: 4d FLOP per (head, query, window
-        # token) on the MFMA, while the bytes it must move bound it -- per row the
-        # q row, the selection normaliser, the row's partials, its group's index
-        # row, the output and lse; K and V^T once per chunk and KV head
-        "window": ("hbm", rows * (d * esz * 2 + 8) + B * Hq * nsel * d * esz
-                   + B * Hkv * T * k * 4.0 + float(B * Hkv * NC * S * d * esz * 2), "B"),
+        "summarize": ("hbm", sumb, "B", sumb),
+        "score_lse": ("mfma", B * Hq * ncand * 2.0 * d, "FLOP", None),
+        # these run once per pass of (b, KV group) pairs, every pair in one pass
+        # with the full workspace: per launch, all B * Hkv groups' shares
+        "rank_keys": ("mfma", B * Hkv * G * ncand * 2.0 * d, "FLOP", None),
+        "topk_scores": ("hbm", topk_b, "B", topk_b),
+        "chunk_attend": ("mfma", f_sel, "FLOP", chunk_b),
+        "window": ("mfma", f_win, "FLOP", win_b),
     }
+
+
+def overlap_m5(idx_t, T, S, W, k):
+    """Mean fraction of a query's selected chunks that the next query also selected
+    (rows where both have more candidates than k): the adjacent-query overlap
+    that query packing would reuse."""
+    import torch
+    nc, _ = window_stats(T, S, W)
+    x = idx_t.to(torch.int64)                                   # [B, Hkv, T, k]
+    a, b = x[:, :, :-1, :], x[:, :, 1:, :]
+    hit = (a.unsqueeze(-1) == b.unsqueeze(-2)).any(-1).sum(-1)  # [B, Hkv, T-1]
+    rows = torch.from_numpy((nc[:-1] > k) & (nc[1:] > k)).to(x.device)
+    n = int(rows.sum()) * x.shape[0] * x.shape[1]
+    return float(hit[:, :, rows].sum()) / max(n * k, 1)
 
 
 def source_digest(files):
@@ -224,9 +257,32 @@ def ingest_pmc(fetch_csv, write_csv, command, out_path=TRAFFIC_FILE):
     print("\n".join(lines))
 
 
+def ingest_counters(csv_path, out_path, title, command):
+    """Summarise a rocprofv3 counter run (any counters): for each library kernel, the
+    mean per-dispatch value of each counter over its dispatches in the run."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        name = r["Kernel_Name"]
+        if "hils::" not in name:
+            continue
+        kn = name.replace("void ", "").replace("hils::(anonymous namespace)::", "").replace("hils::", "")
+        kn = kn.split("(")[0]
+        per.setdefault(kn, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = ["# rocprofv3 counters per dispatch (mean over the kernel's dispatches): " + title,
+             "# command (repository root, one MI355X):"] + ["#   " + c for c in command] + [""]
+    for kn in sorted(per):
+        for cn in sorted(per[kn]):
+            v = per[kn][cn]
+            lines.append("%s.%s = %.6g    # %d dispatches" % (kn, cn, float(np.mean(v)), len(v)))
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(x, wl, seconds=10.0):
-    """The fp64 oracle on the host: summaries of every chunk plus a sample of query rows."""
-    import torch
+    """The fp64 oracle on the host: summaries of every chunk plus a sample of query
+    rows, with all of the oracle's threads, then the same rows on one thread."""
     import oracle
     L = oracle.lib()
     threads = int(L.orc_max_threads())
@@ -237,26 +293,86 @@ def cpu_baseline(x, wl, seconds=10.0):
     t_sum = time.perf_counter() - t0
     v_h = x["v"].cpu()
     T = wl.T
-    n = 8
-    while True:
+
+    def rows_time(n):
         pos = np.linspace(T // 2, T - 1, n).astype(np.int64)
         q_rows = x["q"][:, :, pos].cpu()
         qh_rows = x["q_hat"][:, :, pos].cpu()
         rb, rg, rq = np.meshgrid(np.arange(wl.B), np.arange(wl.Hkv), np.arange(n), indexing="ij")
         rb, rg, rq = rb.ravel(), rg.ravel(), rq.ravel()
-        ri = pos[rq]
-        t0 = time.perf_counter()
-        oracle.rows(rb, rg, ri, rq, q_rows, qh_rows, k_h, v_h, ks, bs, S=wl.S, W=wl.W, topk=wl.k)
-        t_rows = time.perf_counter() - t0
+        t0_ = time.perf_counter()
+        oracle.rows(rb, rg, pos[rq], rq, q_rows, qh_rows, k_h, v_h, ks, bs, S=wl.S, W=wl.W,
+                    topk=wl.k)
+        return time.perf_counter() - t0_
+
+    n = 8
+    while True:
+        t_rows = rows_time(n)
         if t_rows + t_sum > seconds * 0.4 or n >= 512:
             break
         n *= 2
     per_token = t_sum / T + t_rows / n
+    # one thread: the summaries of a 1/16 share of the chunks and 8 positions
+    prev = oracle.set_threads(1)
+    try:
+        nc1 = (T // wl.S) // 16
+        t0 = time.perf_counter()
+        oracle.summarize(k_h, ql_h, wl.S, wl.Hq, ks_round=oracle.ORND_BF16, nc=nc1)
+        t_sum1 = (time.perf_counter() - t0) * (T // wl.S) / nc1
+        n1 = 8
+        t_rows1 = rows_time(n1)
+    finally:
+        oracle.set_threads(prev)
+    per_token1 = t_sum1 / T + t_rows1 / n1
     return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "single_core_value": 1.0 / per_token1,
             "sample": "128K prefill: fp64 summaries of all %d chunks x %d heads (%.1f s) plus all "
                       "%d KV groups of %d query positions from the second half of the sequence "
-                      "(%.1f s); tokens/s = 1/(t_summaries/T + t_rows/positions)"
-                      % (T // wl.S, wl.Hq, t_sum, wl.Hkv, n, t_rows)}
+                      "(%.1f s) on %d threads; tokens/s = 1/(t_summaries/T + t_rows/positions). "
+                      "single_core_value: one thread, summaries of %d chunks scaled to all "
+                      "(%.1f s) plus %d positions (%.1f s)"
+                      % (T // wl.S, wl.Hq, t_sum, wl.Hkv, n, t_rows, threads, nc1, t_sum1, n1,
+                         t_rows1)}
+
+
+def time_decode(hils, wl, cache, shape, ks, bs, steps, nrep, warm):
+    """Per-step HIP-event times (ms) of `steps` decode steps from the cache length,
+    run nrep times (positions restart each time; the cache rows they write and the
+    summaries of the chunks they complete are rewritten with the same values)."""
+    import torch
+    dev = ks.device
+    L0 = cache["length"]
+    ws = hils.workspace(shape, hils.OP_DECODE, dev)
+    dirs = cache["meta"].get("needle_dirs")
+    import workloads as wk
+    inputs = [wk.make_decode_step(wl, s, seed=cache["seed"], device=dev, needle_dirs=dirs)
+              for s in range(steps)]
+    out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.B, wl.Hq), dtype=torch.float32, device=dev)
+    idx = torch.empty((wl.B, wl.Hkv, wl.k), dtype=torch.int32, device=dev)
+
+    def one(s):
+        st = inputs[s]
+        hils.hils_decode_step([L0 + s] * wl.B, st["q"], st["q_hat"], st["k_new"], st["v_new"],
+                              st["q_land_new"], cache["k_cache"], cache["v_cache"], ks, bs, out,
+                              lse, idx, shape, ws)
+
+    for s in range(warm):
+        one(s)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(nrep):
+        ev = []
+        for s in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a.record()
+            one(s)
+            b_.record()
+            ev.append((a, b_))
+        torch.cuda.synchronize()
+        times += [a.elapsed_time(b_) for a, b_ in ev]
+    return times
 
 
 def main():
@@ -265,22 +381,29 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--decode-steps", type=int, default=64,
-                    help="decode steps per bench step (64: one chunk completion per step)")
+    ap.add_argument("--decode-steps", type=int, default=256,
+                    help="decode steps per bench step (256: four chunk completions)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 8K prefill and 4M decode legs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a %d-byte device copy first (counter calibration)" % COPY_PROBE_BYTES)
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM-traffic summary from two rocprofv3 counter runs and exit")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("CSV", "OUT", "TITLE"),
+                    help="write a per-kernel summary of a rocprofv3 counter run and exit")
     ap.add_argument("--pmc-command", action="append", default=[],
-                    help="with --ingest-pmc: the profiling command lines, for the record")
+                    help="with --ingest-pmc / --ingest-counters / --stats-summary: the "
+                         "profiling command lines, for the record")
     ap.add_argument("--traffic-out", default=TRAFFIC_FILE,
                     help="with --ingest-pmc: where to write the summary")
     ap.add_argument("--stats-summary", nargs=3, metavar=("STATS_CSV", "OUT", "TITLE"),
-                    help="write a text summary of a rocprofv3 --stats kernel table and exit "
-                         "(the profiling command goes in --pmc-command)")
+                    help="write a text summary of a rocprofv3 --stats kernel table and exit")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.pmc_command, args.traffic_out)
+        return
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, args.pmc_command)
         return
     if args.stats_summary:
         stats_summary(args.stats_summary[0], args.stats_summary[1], args.stats_summary[2], args.pmc_command)
@@ -315,6 +438,7 @@ def main():
 
     log("generating 512K decode caches on device")
     cache = wk.make_decode_cache(dl, seed=1, device=dev)
+    cache["seed"] = 1
     cap = cache["capacity"]
     dshape = hils.Shape.make(dl.B, dl.Hq, dl.Hkv, dl.d, dl.S, dl.W, dl.k, cap, torch.bfloat16)
     dks = torch.empty((dl.B, dl.Hq, cap // dl.S, dl.d), dtype=torch.bfloat16, device=dev)
@@ -331,18 +455,16 @@ def main():
         torch.cuda.synchronize()
         sum_ms.append(ev[0].elapsed_time(ev[1]))
     sum_dec_bytes = summary_bytes(dl.B, dl.Hq, dl.Hkv, L0, dl.d, dl.S)
-    nsteps_total = (args.warmup + args.steps) * args.decode_steps
-    nsteps_total = min(nsteps_total, cap - L0)
-    dsteps = [wk.make_decode_step(dl, s, seed=1, device=dev) for s in range(nsteps_total)]
+    nsteps = min(args.decode_steps, cap - L0)
+    dsteps = [wk.make_decode_step(dl, s, seed=1, device=dev) for s in range(nsteps)]
     dout = torch.empty((dl.B, dl.Hq, dl.d), dtype=torch.bfloat16, device=dev)
     dlse = torch.empty((dl.B, dl.Hq), dtype=torch.float32, device=dev)
     didx = torch.empty((dl.B, dl.Hkv, dl.k), dtype=torch.int32, device=dev)
-    dpos = [0]
 
     names = ["summarize", "select", "attend_fuse", "decode"]
     times = {n_: [] for n_ in names}
 
-    def step(record: bool):
+    def step():
         e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         e[0].record()
         hils.hils_summarize(x["k"], x["q_land"], k_sum, b_sum, shape)
@@ -352,15 +474,12 @@ def main():
         hils.hils_attend_fuse(x["q"], x["k"], x["v"], idx, ssel, out, lse, shape, ws_att)
         e[3].record()
         de = []
-        for _ in range(args.decode_steps):
-            s = dpos[0] % nsteps_total
-            dpos[0] += 1
+        for s in range(nsteps):    # every step restarts at the same cache length
             st = dsteps[s]
-            p = L0 + s
             a = torch.cuda.Event(enable_timing=True)
             b_ = torch.cuda.Event(enable_timing=True)
             a.record()
-            hils.hils_decode_step([p] * dl.B, st["q"], st["q_hat"], st["k_new"], st["v_new"],
+            hils.hils_decode_step([L0 + s] * dl.B, st["q"], st["q_hat"], st["k_new"], st["v_new"],
                                   st["q_land_new"], cache["k_cache"], cache["v_cache"], dks, dbs,
                                   dout, dlse, didx, dshape, ws_dec)
             b_.record()
@@ -375,30 +494,30 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    prefill_kernels = ["summarize", "score_lse", "rank_keys", "topk_scores", "lsel", "idx_count", "idx_scan_tiles",
-                       "idx_scan_buckets", "idx_fill", "v_transpose", "window",
-                       "chunk_attend"]
+    timed_kernels = ["summarize", "score_lse", "rank_keys", "topk_scores", "lsel", "idx_count",
+                     "idx_scan_tiles", "idx_scan_buckets", "idx_fill", "v_transpose", "window",
+                     "chunk_attend", "dec_score", "dec_select", "dec_attend", "dec_fuse",
+                     "dec_summarize"]
     log("warmup")
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
-    dpos[0] = 0  # decode positions restart: every timed step sees the same cache lengths
     log("timed steps")
     recs = []
-    hils.hils_timing_enable(prefill_kernels)   # per-kernel HIP events on the launch stream
+    hils.hils_timing_enable(timed_kernels)   # per-kernel HIP events on the launch stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0 = torch.cuda.Event(enable_timing=True)
     g1 = torch.cuda.Event(enable_timing=True)
     g0.record()
     for _ in range(args.steps):
-        recs.append(step(True))
+        recs.append(step())
     g1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = g0.elapsed_time(g1)
     ktime = {}
-    for kn in prefill_kernels:
+    for kn in timed_kernels:
         tms, nl = hils.hils_timing_get(kn)
         if nl:
             ktime[kn] = (tms / nl, nl / args.steps)   # ms per launch, launches per step
@@ -409,72 +528,154 @@ def main():
         times["attend_fuse"].append(e[2].elapsed_time(e[3]))
         for a, b_ in de:
             times["decode"].append(a.elapsed_time(b_))
-    avg = {n_: float(np.mean(v)) for n_, v in times.items()}
-    med = {n_: float(np.median(v)) for n_, v in times.items()}
+    avg = {n_: float(np.mean(v)) if v else float("nan") for n_, v in times.items()}
+    med = {n_: float(np.median(v)) if v else float("nan") for n_, v in times.items()}
     ms_per_step = total_ms / args.steps
     prefill_ms = avg["summarize"] + avg["select"] + avg["attend_fuse"]
+    m5_128k = overlap_m5(idx, T, S, W, k)
 
     af = attended_flops(B, Hq, T, d, S, W, k)
     sf = score_flops(B, Hq, T, d, S, W)
     sb = summary_bytes(B, Hq, Hkv, T, d, S)
-    dpositions = [L0 + s for s in range(args.decode_steps)]
+    dpositions = [L0 + s for s in range(nsteps)]
     db = decode_bytes(dl.B, dl.Hq, dl.Hkv, dl.d, dl.S, dl.W, dl.k, dpositions) / max(len(dpositions), 1)
     parts = {
         "summarize": {"bound": "hbm", "work": sb, "unit": "GB/s", "peak": PEAK_HBM},
         "select": {"bound": "mfma", "work": sf, "unit": "TFLOP/s", "peak": PEAK_BF16},
         "attend_fuse": {"bound": "mfma", "work": af, "unit": "TFLOP/s", "peak": PEAK_BF16},
+        "prefill": {"bound": "mfma", "work": af, "unit": "TFLOP/s", "peak": PEAK_BF16},
         "decode": {"bound": "hbm", "work": db, "unit": "GB/s", "peak": PEAK_HBM},
     }
+    avg["prefill"] = prefill_ms
+    med["prefill"] = float(np.median([a_ + b_ + c_ for a_, b_, c_ in zip(times["summarize"], times["select"],
+                                                                       times["attend_fuse"])]))
     kw = kernel_work(B, Hq, Hkv, T, d, S, W, k)
     kernels = {}
     for kn, (ms_l, per_step) in ktime.items():
         ent = {"avg_launch_ms": ms_l, "launches_per_step": per_step}
         if kn in kw:
-            bound, amount, u = kw[kn]
-            scale_ = 1e9 if u == "B" else 1e12
+            bound, amount, u, dbytes = kw[kn]
+            rate = amount / (ms_l * 1e-3)
             ent.update({"bound": bound, "work_per_launch": amount,
-                        "achieved": amount / (ms_l * 1e-3) / scale_,
+                        "achieved": rate / (1e9 if u == "B" else 1e12),
                         "unit": "GB/s" if u == "B" else "TFLOP/s",
-                        "frac": amount / (ms_l * 1e-3) / (PEAK_HBM if u == "B" else PEAK_BF16)})
+                        "frac": rate / (PEAK_HBM if u == "B" else PEAK_BF16)})
+            if dbytes is not None:
+                ent["design_bytes_per_launch"] = dbytes
+                ent["design_GBps"] = dbytes / (ms_l * 1e-3) / 1e9
+                tr = read_traffic(kn)
+                if tr is not None:
+                    ent["counter_bytes_per_launch"] = tr
         kernels[kn] = ent
-    dom = max((kn for kn in kernels if kn in kw),
-              key=lambda kn: kernels[kn]["avg_launch_ms"] * kernels[kn]["launches_per_step"])
+    pre_k = [kn for kn in kernels if kn in kw]
+    dom = max(pre_k, key=lambda kn: kernels[kn]["avg_launch_ms"] * kernels[kn]["launches_per_step"])
     kd = kernels[dom]
-    traffic = read_traffic(dom)
     roof = {"bound": kd["bound"], "kernel": dom + "_kernel", "achieved": kd["achieved"],
             "peak": (PEAK_HBM / 1e9) if kd["unit"] == "GB/s" else (PEAK_BF16 / 1e12),
-            "unit": kd["unit"], "frac": kd["frac"],
-            "traffic": traffic, "work_per_launch": kd["work_per_launch"],
-            "avg_launch_ms": kd["avg_launch_ms"]}
+            "unit": kd["unit"], "frac": kd["frac"], "traffic": read_traffic(dom),
+            "work_per_launch": kd["work_per_launch"], "avg_launch_ms": kd["avg_launch_ms"]}
+    if "design_bytes_per_launch" in kd:
+        roof["bytes_roof"] = {"design_bytes": kd["design_bytes_per_launch"],
+                              "achieved_GBps": kd["design_GBps"],
+                              "frac": kd["design_GBps"] * 1e9 / PEAK_HBM,
+                              "counter_bytes": roof["traffic"]}
     breakdown = {}
     for n_, pp in parts.items():
         a_ = pp["work"] / (avg[n_] * 1e-3)
         breakdown[n_] = {"avg_ms": avg[n_], "median_ms": med[n_], "bound": pp["bound"],
                          "achieved": a_ / (1e9 if pp["unit"] == "GB/s" else 1e12),
                          "unit": pp["unit"], "frac": a_ / pp["peak"]}
-    tokens = B * T + dl.B * args.decode_steps
     res = {
         "metric": METRIC,
-        "value": tokens / (ms_per_step * 1e-3),
+        "value": B * T / (prefill_ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "128K prefill (B=1, 32q/8kv, d=128, S=64, k=32, W=1024) + %d decode "
-                               "steps over 512K caches (B=4, k=32, W=1024)" % args.decode_steps,
-                   "prefill_tokens": B * T, "decode_batch": dl.B, "decode_cache_len": L0},
-        "prefill_tokens_per_s": B * T / (prefill_ms * 1e-3),
+                               "steps over 512K caches (B=4, k=32, W=1024)" % nsteps,
+                   "value": "128K prefill tokens/s (summarize + select + attend_fuse)",
+                   "prefill_tokens": B * T, "decode_batch": dl.B, "decode_cache_len": L0,
+                   "decode_steps": nsteps},
         "prefill_ms": prefill_ms,
+        "prefill_mfma_frac": breakdown["prefill"]["frac"],
         "decode_us_per_step": avg["decode"] * 1e3,
         "decode_us_per_step_median": med["decode"] * 1e3,
         "decode_us_per_token": avg["decode"] * 1e3 / dl.B,
+        "decode_hbm_frac": breakdown["decode"]["frac"],
         "summary_512k_cache_GBps": sum_dec_bytes / (min(sum_ms) * 1e-3) / 1e9,
+        "m5_overlap_128k": m5_128k,
         "roofline": roof,
         "breakdown": breakdown,
         "kernels": kernels,
         "wall_s_timed": wall,
     }
+    del ws_dec
+
+    if not args.no_extra:
+        # ---- 8K prefill (32/8 heads, d=128, k=16, W=512, one planted needle)
+        log("8K prefill")
+        w8 = wk.CONFIGS["8k"]
+        x8 = {kk: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+              for kk, v in wk.make_prefill(w8, seed=0).items()}
+        p8 = {}
+
+        def run8():
+            return hils.prefill(x8["q"], x8["k"], x8["v"], x8["q_land"], x8["q_hat"], S=w8.S,
+                                W=w8.W, topk=w8.k, ws_select=p8.get("wss"), ws_attend=p8.get("wsa"))
+        sh8 = hils.Shape.make(w8.B, w8.Hq, w8.Hkv, w8.d, w8.S, w8.W, w8.k, w8.T, torch.bfloat16)
+        p8["wss"] = hils.workspace(sh8, hils.OP_SELECT, dev)
+        p8["wsa"] = hils.workspace(sh8, hils.OP_ATTEND_FUSE, dev)
+        for _ in range(3):
+            r8 = run8()
+        torch.cuda.synchronize()
+        t8 = []
+        for _ in range(20):
+            a = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a.record()
+            r8 = run8()
+            b_.record()
+            torch.cuda.synchronize()
+            t8.append(a.elapsed_time(b_))
+        ms8 = float(np.median(t8))
+        af8 = attended_flops(w8.B, w8.Hq, w8.T, w8.d, w8.S, w8.W, w8.k)
+        res["prefill_8k"] = {"ms_median": ms8, "tokens_per_s": w8.B * w8.T / (ms8 * 1e-3),
+                             "attended_flops": af8,
+                             "mfma_frac": af8 / (ms8 * 1e-3) / PEAK_BF16,
+                             "m5_overlap": overlap_m5(r8["idx"], w8.T, w8.S, w8.W, w8.k),
+                             "note": "median of 20 calls of summarize + select + attend_fuse "
+                                     "(output buffers allocated inside each call)"}
+        del x8, p8, r8
+        # ---- 4M decode (B=1, k=64, 8 needles, 256 steps with 4 chunk completions)
+        log("4M decode: drawing the cache")
+        w4 = wk.CONFIGS["4m_decode"]
+        c4 = wk.make_decode_cache(w4, seed=2, device=dev)
+        c4["seed"] = 2
+        cap4 = c4["capacity"]
+        sh4 = hils.Shape.make(w4.B, w4.Hq, w4.Hkv, w4.d, w4.S, w4.W, w4.k, cap4, torch.bfloat16)
+        ks4 = torch.empty((w4.B, w4.Hq, cap4 // w4.S, w4.d), dtype=torch.bfloat16, device=dev)
+        bs4 = torch.empty((w4.B, w4.Hq, cap4 // w4.S), dtype=torch.float32, device=dev)
+        s4 = []
+        for _ in range(2):
+            ev[0].record()
+            hils.hils_summarize(c4["k_cache"], c4["q_land"], ks4, bs4, sh4, 0, c4["length"] // w4.S)
+            ev[1].record()
+            torch.cuda.synchronize()
+            s4.append(ev[0].elapsed_time(ev[1]))
+        log("4M decode: 256 steps")
+        t4 = time_decode(hils, w4, c4, sh4, ks4, bs4, min(256, cap4 - c4["length"]), 2, 8)
+        pos4 = [c4["length"] + s_ for s_ in range(min(256, cap4 - c4["length"]))]
+        db4 = decode_bytes(w4.B, w4.Hq, w4.Hkv, w4.d, w4.S, w4.W, w4.k, pos4) / len(pos4)
+        us4 = float(np.mean(t4)) * 1e3
+        res["decode_4m"] = {"us_per_step": us4, "us_per_step_median": float(np.median(t4)) * 1e3,
+                            "bytes_per_step": db4, "hbm_frac": db4 / (us4 * 1e-6) / PEAK_HBM,
+                            "summary_GBps": summary_bytes(w4.B, w4.Hq, w4.Hkv, c4["length"], w4.d, w4.S)
+                                            / (min(s4) * 1e-3) / 1e9,
+                            "note": "mean of 2 x 256 individually timed steps from 4194304 tokens "
+                                    "(4 chunk completions per pass)"}
+        del c4, ks4, bs4
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(x, wl)

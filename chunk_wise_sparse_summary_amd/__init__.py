@@ -189,9 +189,20 @@ def hils_timing_get(kernel: str):
     return ms.value, n.value
 
 
+def select_lse(workspace_t: torch.Tensor, shape: Shape) -> torch.Tensor:
+    """Each head's L_{h,i} = LSE over the candidates of s_hat, as hils_select leaves
+    it at the start of its workspace for groups of more than one head ([B, Hq, T]
+    fp32 view of the workspace; hils.h states the layout)."""
+    n = shape.batch * shape.heads_q * shape.seq_len
+    off = (-workspace_t.data_ptr()) % 256
+    return workspace_t[off:off + 4 * n].view(torch.float32).view(shape.batch, shape.heads_q,
+                                                                   shape.seq_len)
+
+
 def prefill(q, k, v, q_land, q_hat, *, S: int, W: int, topk: int, scale: float = 0.0,
             ws_select=None, ws_attend=None):
-    """summarize -> select -> attend_fuse for [B,H,T,d] inputs; returns a dict of outputs."""
+    """summarize -> select -> attend_fuse for [B,H,T,d] inputs; returns a dict of outputs
+    (and the select workspace, whose start holds each head's L_h)."""
     B, Hq, T, d = q.shape
     Hkv = k.shape[1]
     shape = Shape.make(B, Hq, Hkv, d, S, W, topk, T, q.dtype, scale)
@@ -202,9 +213,11 @@ def prefill(q, k, v, q_land, q_hat, *, S: int, W: int, topk: int, scale: float =
     ssel = torch.empty((B, Hq, T, topk), dtype=torch.float32, device=q.device)
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if ws_select is None:
+        ws_select = workspace(shape, OP_SELECT, q.device)
     if NC > 0:
         hils_summarize(k, q_land, k_sum, b_sum, shape)
     hils_select(q_hat, k_sum, b_sum, idx, ssel, shape, ws_select)
     hils_attend_fuse(q, k, v, idx, ssel, out, lse, shape, ws_attend)
     return {"k_sum": k_sum, "b_sum": b_sum, "idx": idx, "ssel": ssel, "out": out, "lse": lse,
-            "shape": shape}
+            "shape": shape, "ws_select": ws_select}

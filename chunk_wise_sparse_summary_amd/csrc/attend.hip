@@ -2,8 +2,8 @@
 //
 // Summary page, Methodology 2, Eq. 10: w_ij = exp(s_ij)/Z_{i,c(j)} * Zhat_{i,c(j)}/Zhat_i
 // with Zhat_{i,c} = exp(s_hat_{i,c}) for a selected chunk and, for the window, its
-// true token-level mass Z_{i,win} (paper-body page, implementation: the partition
-// estimate combines chunk-level surrogates with token-level attention mass).  So
+// true token-level mass Z_{i,win} (paper-body page, implementation: the normaliser
+// adds the window's exact mass to the selected chunks' surrogate masses).  So
 //   out_i = sum_{c in Sel} exp(s_hat_c - L) o_c + exp(log Z_win - L) o_win,
 //   L = LSE({s_hat_c} + {log Z_win}),
 // where o_gamma is ordinary softmax attention of q_i over the group's tokens.

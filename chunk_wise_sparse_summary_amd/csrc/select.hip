@@ -1,8 +1,9 @@
 // select.hip -- retrieval scores and GQA-aware top-k chunk selection (prefill).
 //
 // Paper-body page, RQ1: each query scores every chunk summary with the linear
-// surrogate of Eq. 7 and keeps the top-k ("the routing cost is the only
-// quadratic term").  Summary page, Eq. 10: s_hat = q_hat . k' / sqrt(d) + b'.
+// surrogate of Eq. 7 and keeps the top-k; this scoring is the one part of the
+// method whose cost grows with T^2.  Summary page, Eq. 10: s_hat = q_hat . k' /
+// sqrt(d) + b'.
 // Paper-body page, GQA-aware chunk selection: per-head normalised chunk weights,
 // max over the heads of a group, top-k per group.  The normalised weight is
 // exp(s_hat - LSE_{C_i} s_hat), so ranking by max_h (s_hat_h - L_h) is ranking by

@@ -24,11 +24,12 @@
  *
  * Conventions for every call:
  *  - Tensors are caller-owned device memory, contiguous and row-major,
- *    head-major ([B, H, T, d]), 16-byte aligned.  The library allocates no
- *    memory, keeps no pointer after returning and holds no mutable global
- *    state, so calls on different streams may run concurrently as long as
- *    their buffers are disjoint.  Scratch memory is the caller's workspace,
- *    sized by hils_workspace_bytes().
+ *    head-major ([B, H, T, d]), 16-byte aligned.  The compute calls allocate no
+ *    memory and keep no pointer after returning; their scratch memory is the
+ *    caller's workspace, sized by hils_workspace_bytes().  Calls on different
+ *    streams may run concurrently as long as their buffers are disjoint.  The
+ *    only process-wide state is the optional kernel timing below (off unless
+ *    hils_timing_enable() switched it on), which keeps a pool of HIP events.
  *  - Every check runs on the host before anything is enqueued.  A nonzero
  *    status means nothing was enqueued and nothing was written.  Work is
  *    asynchronous on `stream` (NULL = the default stream); a fault inside a
@@ -132,6 +133,10 @@ hils_status hils_summarize(const hils_shape* shape, const void* k, const void* q
  * The workspace holds each head's LSE and the rank keys of every (b, group); a
  * workspace smaller than hils_workspace_bytes() but holding at least one
  * (b, group)'s keys runs the same computation a few (b, group) pairs at a time.
+ * On return, for G > 1, the workspace starts (at its first 256-byte aligned
+ * address) with L [B, Hq, T] fp32: each head's L_{h,i} = LSE_{c in C_i} s_hat_{h,i,c}
+ * as used in the rank keys (-inf where C_i is empty), so that a caller can
+ * rebuild the rank key of every chosen chunk from sel_score.
  */
 hils_status hils_select(const hils_shape* shape, const void* q_hat, const void* k_sum,
                         const float* b_sum, int32_t* sel_idx, float* sel_score,
@@ -139,9 +144,9 @@ hils_status hils_select(const hils_shape* shape, const void* q_hat, const void* 
 
 /*
  * Per-group attention and fusion (summary page, Methodology 2, Eq. 10, the
- * hierarchical softmax; paper-body page, implementation: the partition
- * estimate combines chunk-level mass surrogates with token-level attention
- * mass).  For every b, query head h (group g), position i:
+ * hierarchical softmax; paper-body page, implementation: the normaliser adds
+ * the window's exact token-level mass to the selected chunks' surrogate
+ * masses).  For every b, query head h (group g), position i:
  *     for each selected chunk c and for the window Win_i = [l_i, i]:
  *         s_ij = scale * q_{h,i} . k_{g,j}
  *         log Z_gamma = LSE_j s_ij,   o_gamma = sum_j exp(s_ij - log Z_gamma) v_{g,j}

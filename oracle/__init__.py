@@ -68,6 +68,8 @@ def lib():
         L.orc_num_candidates.argtypes = [I64, I, I]
         L.orc_num_candidates.restype = I64
         L.orc_max_threads.restype = I
+        L.orc_set_threads.argtypes = [I]
+        L.orc_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -98,6 +100,13 @@ def _as_np(x):
 
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def set_threads(n: int) -> int:
+    """Use n OpenMP threads from now on; returns the previous count."""
+    prev = int(lib().orc_max_threads())
+    lib().orc_set_threads(int(n))
+    return prev
 
 
 def window_left(i: int, S: int, W: int) -> int:

@@ -10,8 +10,8 @@
  *   [p1 BSA]   paper-body page, section "Block Sparse Attention" preliminaries
  *              (chunk partition, aligned window, candidate set, token logits,
  *              chunk masses, top-k selection).
- *   [p1 RQ1]   paper-body page, RQ1 (LogSumExp linearization, landmark query,
- *              "each query routes over all chunk summaries, keeps the top-k").
+ *   [p1 RQ1]   paper-body page, RQ1 (LogSumExp linearization, landmark query;
+ *              every query scores all chunk summaries and retains k of them).
  *   [p1 RQ2]   paper-body page, RQ2 (hierarchical factorisation of weights).
  *   [p1 GQA]   paper-body page, implementation: GQA-aware chunk selection.
  *   [p1 Q-Cal] paper-body page, implementation: the partition estimate combines
@@ -99,6 +99,15 @@ int orc_max_threads(void) {
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Set the number of threads later OpenMP regions use (no-op without OpenMP). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }
 

@@ -13,6 +13,11 @@ Comparison rules
     end in bf16, where the GPU's own k' may differ from the oracle's by one bf16
     rounding (|q_hat| |dk'| / sqrt(d) below about 7e-6).
   * Floating-point outputs: bf16 max-abs 2e-2 and rel-L2 5e-3; fp32 max-abs 1e-5.
+  * The band itself is checked: the GPU's rank keys on its chosen chunks, rebuilt
+    from its own outputs (each head's s_hat on the choice and each head's L_h),
+    must agree with the oracle's keys on the same stored summaries within TAU/4
+    (check_rank_keys).  End to end in bf16 the two sides' k' may also differ by
+    one bf16 rounding; that part is bounded separately (kprime_rank_bound).
 """
 from __future__ import annotations
 
@@ -88,6 +93,53 @@ def check_selection(gpu_idx: np.ndarray, orc: dict, topk: int, tau: float) -> di
         assert must <= set(valid), ("undecided set misses a sure chunk", t)
         differ[t] = True
     return {"decided": n_dec, "undecided": n_und, "differ": differ}
+
+
+def gpu_rank_keys(ssel_rows: np.ndarray, L_rows, G: int) -> np.ndarray:
+    """The GPU's rank key of each chosen slot, from its own outputs: s_hat for a
+    group of one head, else max over heads of (s_hat_h - L_h).  ssel_rows [n, G, k],
+    L_rows [n, G] (ignored for G == 1).  Pads come out -inf."""
+    if G == 1:
+        return ssel_rows[:, 0, :].copy()
+    with np.errstate(invalid="ignore"):      # rows without candidates: -inf - -inf
+        return np.max(ssel_rows - np.asarray(L_rows)[:, :, None], axis=1)
+
+
+def check_rank_keys(gpu_idx: np.ndarray, r_gpu: np.ndarray, orc: dict, topk: int,
+                    limit: float, what: str = "") -> dict:
+    """max |r_gpu - r_oracle| over every chosen slot of every row with candidates.
+
+    orc must come from oracle.rows(..., want_r=True) on the same stored summaries.
+    Asserts the maximum is at most `limit`; returns it with the number of keys."""
+    err = 0.0
+    n = 0
+    for t in range(gpu_idx.shape[0]):
+        nc = int(orc["ncand"][t])
+        if nc == 0 or topk == 0:
+            continue
+        c = gpu_idx[t][gpu_idx[t] >= 0]
+        ro = orc["r"][t, c]
+        rg_ = r_gpu[t, :len(c)]
+        assert np.all(np.isfinite(rg_)), ("non-finite GPU rank key", t)
+        e = np.abs(rg_ - ro)
+        err = max(err, float(e.max()))
+        n += len(c)
+    assert err <= limit, "%s: max |r_gpu - r_oracle| = %.3g > %.3g" % (what, err, limit)
+    return {"max_err": err, "keys": n}
+
+
+def kprime_rank_bound(ks_gpu: np.ndarray, ks_orc: np.ndarray, qh_rows: np.ndarray, rb, rg, G: int,
+                      scale: float) -> float:
+    """Largest change of any rank key that the difference between two stores of k'
+    can cause on the given rows: scale * sum_e |q_hat_e| |dk'_e| per (row, head,
+    chunk), doubled for the shift of L_h.  qh_rows [n, G, d] (the rows' q_hat)."""
+    dk = np.abs(f64(ks_gpu) - f64(ks_orc))                 # [B, Hq, NC, d]
+    bound = 0.0
+    for t in range(len(rb)):
+        heads = slice(rg[t] * G, (rg[t] + 1) * G)
+        m = scale * np.einsum("hd,hcd->hc", np.abs(qh_rows[t]), dk[rb[t], heads])
+        bound = max(bound, 2.0 * float(m.max()) if m.size else 0.0)
+    return bound
 
 
 def rows_layout(B: int, Hkv: int, positions) -> tuple:

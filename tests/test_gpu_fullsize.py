@@ -17,8 +17,9 @@ import torch
 
 import oracle
 import workloads as wk
-from hils_testlib import (TAU_E2E_BF16, assert_close, check_selection, gather_rows, rows_layout,
-                          tol_lse, tol_out)
+from hils_testlib import (TAU_E2E_BF16, TAU_STAGE, assert_close, check_rank_keys, check_selection,
+                          f64, gather_rows, gpu_rank_keys, kprime_rank_bound, rows_layout, tol_lse,
+                          tol_out)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -102,6 +103,21 @@ def test_prefill_128k_sampled(hils):
     gi = gather_rows(idx, rb, rg, ri, 1)[:, 0].astype(np.int64)
     res = check_selection(gi, orc, k, TAU_E2E_BF16)
     say("  decided %d undecided %d differ %d" % (res["decided"], res["undecided"], res["differ"].sum()))
+    # rank keys of the GPU's choice rebuilt from its outputs (s_hat on the choice,
+    # each head's L_h from the select workspace) vs the oracle on the same summaries
+    G = wl.G
+    gs_all = gather_rows(ssel, rb, rg, ri, G)
+    gL = gather_rows(hils.select_lse(ws_sel, shape), rb, rg, ri, G)
+    rgpu = gpu_rank_keys(gs_all, gL, G)
+    orc_g = oracle.rows(rb, rg, ri, rq, q_rows, qh_rows, k_h, v_h, f64(k_sum), f64(b_sum), S=S,
+                        W=W, topk=k, want_r=True)
+    rk = check_rank_keys(gi, rgpu, orc_g, k, TAU_STAGE / 4, "rank keys (same summaries)")
+    qh64 = qh_rows.to(torch.float64).numpy()
+    qh_r = np.stack([qh64[b_, g_ * G:(g_ + 1) * G, rq_] for b_, g_, rq_ in zip(rb, rg, rq)])
+    kb = kprime_rank_bound(k_sum, oks, qh_r, rb, rg, G, 1.0 / np.sqrt(d))
+    rk2 = check_rank_keys(gi, rgpu, orc, k, TAU_STAGE / 4 + kb, "rank keys (oracle k')")
+    say("  rank keys: same summaries max err %.3g on %d keys; vs oracle k' %.3g (k' bound %.3g)"
+        % (rk["max_err"], rk["keys"], rk2["max_err"], kb))
     want_out, want_lse = orc["out"].copy(), orc["lse"].copy()
     dm = res["differ"]
     if dm.any():

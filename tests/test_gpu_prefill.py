@@ -14,8 +14,9 @@ import torch
 
 import oracle
 import workloads as wk
-from hils_testlib import (TAU_E2E_BF16, TAU_E2E_F32, TAU_STAGE, assert_close, check_selection,
-                          f64, gather_rows, rows_layout, tol_lse, tol_out)
+from hils_testlib import (TAU_E2E_BF16, TAU_E2E_F32, TAU_STAGE, assert_close, check_rank_keys,
+                          check_selection, f64, gather_rows, gpu_rank_keys, kprime_rank_bound,
+                          rows_layout, tol_lse, tol_out)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,16 +103,20 @@ def test_select_stage_parity(hils, name):
     sh = _shape(hils, wl)
     idx = torch.empty((wl.B, wl.Hkv, wl.T, wl.k), dtype=torch.int32, device=DEV)
     ssel = torch.empty((wl.B, wl.Hq, wl.T, wl.k), dtype=torch.float32, device=DEV)
-    hils.hils_select(xd["q_hat"], ks.to(DEV), bs.to(DEV), idx, ssel, sh)
+    ws = hils.workspace(sh, hils.OP_SELECT, DEV)
+    hils.hils_select(xd["q_hat"], ks.to(DEV), bs.to(DEV), idx, ssel, sh, ws)
     torch.cuda.synchronize()
     rb, rg, ri = rows_layout(wl.B, wl.Hkv, range(wl.T))
     orc = oracle.rows(rb, rg, ri, ri, x["q"], x["q_hat"], x["k"], x["v"], ks.double().numpy(),
                       bs.double().numpy(), S=wl.S, W=wl.W, topk=wl.k, want_r=True)
     gi = idx.cpu().numpy().reshape(-1, wl.k)
     res = check_selection(gi, orc, wl.k, TAU_STAGE)
-    say("  decided", res["decided"], "undecided", res["undecided"], "differ", res["differ"].sum())
     G = wl.G
     gs = gather_rows(ssel, rb, rg, ri, G)
+    gL = gather_rows(hils.select_lse(ws, sh), rb, rg, ri, G) if G > 1 else None
+    rk = check_rank_keys(gi, gpu_rank_keys(gs, gL, G), orc, wl.k, TAU_STAGE / 4, "rank keys")
+    say("  decided", res["decided"], "undecided", res["undecided"], "differ", res["differ"].sum(),
+        "rank-key max err %.3g on %d keys" % (rk["max_err"], rk["keys"]))
     same = ~res["differ"]
     o = orc["ssel"][same]
     g = gs[same]
@@ -164,6 +169,22 @@ def _e2e_check(hils, x, xd, wl, positions=None, seed_note=""):
         np.zeros((len(rb), 0), np.int64)
     res = check_selection(gi, orc, wl.k, tau) if wl.k > 0 else {"differ": np.zeros(len(rb), bool),
                                                                  "decided": 0, "undecided": 0}
+    if wl.k > 0:
+        # the band's premise: the GPU's own rank keys on its choice, rebuilt from its
+        # outputs, agree with the oracle's on the same stored summaries within TAU/4
+        gs = gather_rows(r["ssel"], rb, rg, ri, G)
+        gL = gather_rows(hils.select_lse(r["ws_select"], r["shape"]), rb, rg, ri, G) if G > 1 else None
+        rgpu = gpu_rank_keys(gs, gL, G)
+        orc_g = oracle.rows(rb, rg, ri, ri, x["q"], x["q_hat"], x["k"], x["v"], f64(r["k_sum"]),
+                            f64(r["b_sum"]), S=wl.S, W=wl.W, topk=wl.k, want_r=True)
+        rk = check_rank_keys(gi, rgpu, orc_g, wl.k, TAU_STAGE / 4, "rank keys (same summaries)")
+        # against the oracle's own summaries the keys may move further by the two
+        # sides' k' rounding, which is bounded from the measured k' difference
+        qh_rows = gather_rows(xd["q_hat"], rb, rg, ri, G)
+        kb = kprime_rank_bound(r["k_sum"], oks, qh_rows, rb, rg, G, oracle.default_scale(wl.d))
+        rk2 = check_rank_keys(gi, rgpu, orc, wl.k, TAU_STAGE / 4 + kb, "rank keys (oracle k')")
+        say("  rank keys: same summaries max err %.3g on %d keys; vs oracle k' %.3g (k' bound %.3g,"
+            " tau/4 %.3g)" % (rk["max_err"], rk["keys"], rk2["max_err"], kb, tau / 4))
     say("  %s decided %d undecided %d differ %d" % (seed_note, res["decided"], res["undecided"],
                                                     res["differ"].sum()))
     out_g = gather_rows(r["out"], rb, rg, ri, G)

@@ -37,6 +37,9 @@ MUTANTS = [
      "        s[j] = acc;\n    }\n    const double logZ"),
     ("fused weight uses window mass for chunks", "const double w = exp(ws[sidx] - Lhat);",
      "const double w = exp(logZw - Lhat);"),
+    ("forced selection ignored", "sel[s] = forced_idx[t * topk + s];", "sel[s] = 0;"),
+    ("forced selection shifted", "sel[s] = forced_idx[t * topk + s];",
+     "sel[s] = forced_idx[t * topk + s] > 0 ? forced_idx[t * topk + s] - 1 : 0;"),
 ]
 
 PIN_TESTS = [
@@ -55,6 +58,8 @@ PIN_TESTS = [
     lambda g: pins.test_p9_brute_force_matrix_form(dict(B=1, Hq=1, Hkv=1, T=32, d=4, S=2, W=4, k=3)),
     lambda g: pins.test_psel_exact_ties_lower_index_wins(1, 1),
     lambda g: pins.test_p11_gqa_identical_heads_equals_mha(),
+    lambda g: pins.test_golden_forced_selection(g),
+    lambda g: pins.test_forced_own_selection_is_identical(4, 2),
 ]
 
 

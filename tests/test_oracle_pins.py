@@ -53,6 +53,41 @@ def test_golden_hand_example(golden):
     assert r["lse"][0, 0] == pytest.approx(g["lse"], abs=1e-14)
 
 
+def test_golden_forced_selection(golden):
+    """The forced-selection branch (used when a GPU's near-tie selection differs):
+    forcing chunk 1 in the hand example gives its hand-derived out = 23/5, lse = ln 5."""
+    g = golden("hand_example.txt")
+    k = np.array([0, math.log(3), 0, 0, math.log(2), 0], np.float64).reshape(1, 1, 6, 1)
+    v = np.arange(1, 7, dtype=np.float64).reshape(1, 1, 6, 1)
+    q = np.ones((1, 1, 6, 1))
+    ks = np.array([[[[g["ksum0"]], [g["ksum1"]], [0.0]]]])
+    bs = np.array([[[g["bsum0"], g["bsum1"], math.log(2)]]])
+    r = oracle.rows([0], [0], [5], [5], q, q, k, v, ks, bs, S=2, W=2, topk=1, scale=1.0,
+                    forced_idx=np.array([[1]]))
+    assert r["idx"][0].tolist() == [1]
+    assert r["ssel"][0, 0, 0] == pytest.approx(g["forced1_shat"], abs=1e-14)
+    assert r["out"][0, 0, 0] == pytest.approx(g["forced1_out"], abs=1e-14)
+    assert r["lse"][0, 0] == pytest.approx(g["forced1_lse"], abs=1e-14)
+
+
+@pytest.mark.parametrize("G,topk", [(1, 3), (4, 2)])
+def test_forced_own_selection_is_identical(G, topk):
+    """Forcing the oracle's own selection reproduces its out, lse and scores bit for bit,
+    on every row (rows with fewer candidates than k included)."""
+    x = _gen(B=2, Hq=2 * G, Hkv=2, T=160, d=8, NC=20, seed=31, scale=0.8)
+    S, W = 8, 16
+    ks, bs = oracle.summarize(x["k"], x["q_land"], S=S, Hq=2 * G, scale=0.4)
+    rb, rg, ri = np.meshgrid(np.arange(2), np.arange(2), np.arange(160), indexing="ij")
+    rb, rg, ri = rb.ravel(), rg.ravel(), ri.ravel()
+    a = oracle.rows(rb, rg, ri, ri, x["q"], x["q_hat"], x["k"], x["v"], ks, bs, S=S, W=W,
+                    topk=topk, scale=0.4)
+    assert np.sum(a["ncand"] > topk) > 100
+    b = oracle.rows(rb, rg, ri, ri, x["q"], x["q_hat"], x["k"], x["v"], ks, bs, S=S, W=W,
+                    topk=topk, scale=0.4, forced_idx=a["idx"])
+    for key in ("idx", "ssel", "out", "lse", "ncand"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_golden_gqa_rule(golden):
     """GQA rule: max over heads of per-head normalised weights (tests/golden/gqa_rule.txt)."""
     g = golden("gqa_rule.txt")
