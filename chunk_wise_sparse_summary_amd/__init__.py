@@ -31,10 +31,11 @@ OP_SUMMARIZE, OP_SELECT, OP_ATTEND_FUSE, OP_DECODE = 0, 1, 2, 3
 STATUS = {
     0: "HILS_OK", -1: "HILS_E_NULL", -2: "HILS_E_SHAPE", -3: "HILS_E_DTYPE", -4: "HILS_E_ALIGN",
     -5: "HILS_E_WORKSPACE", -6: "HILS_E_POS", -7: "HILS_E_NEED_QLAND", -8: "HILS_E_UNSUPPORTED",
-    -9: "HILS_E_LAUNCH",
+    -9: "HILS_E_LAUNCH", -10: "HILS_E_SCRATCH",
 }
 
 EXPORTS = ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
+           "hils_decode_step_noalloc",
            "hils_workspace_bytes", "hils_status_string", "hils_abi_version",
            "hils_timing_enable", "hils_timing_get")
 
@@ -75,6 +76,7 @@ def lib():
         L.hils_select.argtypes = [SP, P, P, P, P, P, P, SZ, P]
         L.hils_attend_fuse.argtypes = [SP, P, P, P, P, P, P, P, P, SZ, P]
         L.hils_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        L.hils_decode_step_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.hils_workspace_bytes.argtypes = [SP, ctypes.c_int]
         L.hils_workspace_bytes.restype = SZ
         L.hils_status_string.argtypes = [ctypes.c_int]
@@ -85,7 +87,8 @@ def lib():
         L.hils_timing_get.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
         L.hils_timing_get.restype = ctypes.c_int
-        for f in ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step"):
+        for f in ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
+                  "hils_decode_step_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -162,6 +165,16 @@ def hils_decode_step(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, 
         ctypes.byref(shape), pos_arr, _p(q), _p(q_hat), _p(k_new), _p(v_new), _p(q_land_new),
         _p(k_cache), _p(v_cache), _p(k_sum), _p(b_sum), _p(out), _p(lse), _p(sel_idx),
         _p(workspace_t), workspace_t.numel(), _stream()))
+
+
+def hils_decode_step_noalloc(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, k_sum,
+                             b_sum, out, lse, sel_idx, shape: Shape):
+    """hils_decode_step on the library's built-in scratch (no workspace, no allocation)."""
+    _dev(q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, k_sum, b_sum, out, lse, sel_idx)
+    pos_arr = (ctypes.c_int64 * shape.batch)(*[int(p) for p in pos])
+    _check("hils_decode_step_noalloc", lib().hils_decode_step_noalloc(
+        ctypes.byref(shape), pos_arr, _p(q), _p(q_hat), _p(k_new), _p(v_new), _p(q_land_new),
+        _p(k_cache), _p(v_cache), _p(k_sum), _p(b_sum), _p(out), _p(lse), _p(sel_idx), _stream()))
 
 
 KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",

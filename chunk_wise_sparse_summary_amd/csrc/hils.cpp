@@ -73,6 +73,7 @@ const char* hils_status_string(hils_status st) {
     case HILS_E_NEED_QLAND: return "a chunk completes but no landmark query was given";
     case HILS_E_UNSUPPORTED: return "configuration not supported by this build";
     case HILS_E_LAUNCH: return "the HIP runtime refused a launch";
+    case HILS_E_SCRATCH: return "the shape needs more than the built-in scratch of the allocation-free decode step";
   }
   return "unknown status";
 }

@@ -64,7 +64,9 @@ typedef enum {
     HILS_E_POS = -6,           /* decode position outside the cache */
     HILS_E_NEED_QLAND = -7,    /* a chunk completes but no landmark query was given */
     HILS_E_UNSUPPORTED = -8,   /* valid, but outside what this build implements */
-    HILS_E_LAUNCH = -9         /* the HIP runtime refused a launch */
+    HILS_E_LAUNCH = -9,        /* the HIP runtime refused a launch */
+    HILS_E_SCRATCH = -10       /* the shape needs more than the built-in scratch
+                                  of hils_decode_step_noalloc */
 } hils_status;
 
 typedef enum { HILS_F32 = 0, HILS_BF16 = 1 } hils_dtype;
@@ -198,6 +200,30 @@ hils_status hils_decode_step(const hils_shape* shape, const int64_t* pos,
                              void* k_cache, void* v_cache, void* k_sum, float* b_sum,
                              void* out, float* lse, int32_t* sel_idx,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The decode step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments and results are those of
+ * hils_decode_step; the scratch memory is the library's own, a static device
+ * array of HILS_NOALLOC_SCRATCH_BYTES bytes that each GPU holds until the
+ * process ends (its address is looked up once per device, on the first call
+ * with that device current).  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library call.  A shape whose decode workspace
+ * (hils_workspace_bytes(shape, HILS_OP_DECODE)) exceeds the scratch returns
+ * HILS_E_SCRATCH with nothing enqueued (512K tokens x 4 sequences, 32/8 heads,
+ * needs about 8 MiB; 4M tokens x 1 sequence about 9 MiB).  Every call on one
+ * GPU shares that GPU's scratch: calls that may overlap on one GPU (different
+ * streams, different host threads) race and must be serialised by the caller.
+ * Each call writes every scratch element it reads, so no clearing is needed
+ * between calls.
+ */
+#define HILS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hils_status hils_decode_step_noalloc(const hils_shape* shape, const int64_t* pos,
+                                     const void* q, const void* q_hat,
+                                     const void* k_new, const void* v_new, const void* q_land_new,
+                                     void* k_cache, void* v_cache, void* k_sum, float* b_sum,
+                                     void* out, float* lse, int32_t* sel_idx, hipStream_t stream);
 
 /* Workspace bytes `op` needs for `shape` (0 for HILS_OP_SUMMARIZE); 0 as well
  * for an invalid shape. */
