@@ -494,10 +494,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # per-kernel HIP events around the prefill kernels only: events between the
+    # few-microsecond decode kernels would stretch the decode step they measure
     timed_kernels = ["summarize", "score_lse", "rank_keys", "topk_scores", "lsel", "idx_count",
                      "idx_scan_tiles", "idx_scan_buckets", "idx_fill", "v_transpose", "window",
-                     "chunk_attend", "dec_score", "dec_select", "dec_attend", "dec_fuse",
-                     "dec_summarize"]
+                     "chunk_attend"]
+    dec_kernels = ["dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize"]
     log("warmup")
     for _ in range(args.warmup):
         step()
@@ -611,6 +613,21 @@ def main():
         "kernels": kernels,
         "wall_s_timed": wall,
     }
+    # decode kernel breakdown: one more pass of the decode steps with per-kernel
+    # events (these stretch the step; the step time above is measured without them)
+    hils.hils_timing_enable(dec_kernels)
+    for s in range(nsteps):
+        st = dsteps[s]
+        hils.hils_decode_step([L0 + s] * dl.B, st["q"], st["q_hat"], st["k_new"], st["v_new"],
+                              st["q_land_new"], cache["k_cache"], cache["v_cache"], dks, dbs,
+                              dout, dlse, didx, dshape, ws_dec)
+    torch.cuda.synchronize()
+    res["decode_kernels_us"] = {}
+    for kn in dec_kernels:
+        tms, nl = hils.hils_timing_get(kn)
+        if nl:
+            res["decode_kernels_us"][kn] = {"avg_us": tms / nl * 1e3, "launches_per_step": nl / nsteps}
+    hils.hils_timing_enable(None)
     del ws_dec
 
     if not args.no_extra:
@@ -666,6 +683,14 @@ def main():
             s4.append(ev[0].elapsed_time(ev[1]))
         log("4M decode: 256 steps")
         t4 = time_decode(hils, w4, c4, sh4, ks4, bs4, min(256, cap4 - c4["length"]), 2, 8)
+        hils.hils_timing_enable(dec_kernels)
+        time_decode(hils, w4, c4, sh4, ks4, bs4, min(256, cap4 - c4["length"]), 1, 0)
+        k4 = {}
+        for kn in dec_kernels:
+            tms, nl = hils.hils_timing_get(kn)
+            if nl:
+                k4[kn] = {"avg_us": tms / nl * 1e3, "launches": nl}
+        hils.hils_timing_enable(None)
         pos4 = [c4["length"] + s_ for s_ in range(min(256, cap4 - c4["length"]))]
         db4 = decode_bytes(w4.B, w4.Hq, w4.Hkv, w4.d, w4.S, w4.W, w4.k, pos4) / len(pos4)
         us4 = float(np.mean(t4)) * 1e3
@@ -673,8 +698,10 @@ def main():
                             "bytes_per_step": db4, "hbm_frac": db4 / (us4 * 1e-6) / PEAK_HBM,
                             "summary_GBps": summary_bytes(w4.B, w4.Hq, w4.Hkv, c4["length"], w4.d, w4.S)
                                             / (min(s4) * 1e-3) / 1e9,
+                            "kernels_us": k4,
                             "note": "mean of 2 x 256 individually timed steps from 4194304 tokens "
-                                    "(4 chunk completions per pass)"}
+                                    "(4 chunk completions per pass); kernels_us from a third pass "
+                                    "with per-kernel events"}
         del c4, ks4, bs4
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -3,24 +3,33 @@
 // The step is the prefill row i = pos[b] of the same definitions (summary page,
 // Summary and Methodology; paper-body page, RQ1 and GQA-aware selection).  One
 // query has little work per byte, so every kernel here streams memory:
-//   dec_score   appends k_new/v_new to the caches and
-//               scores every candidate chunk of every head of the group:
-//               s_hat = scale * q_hat . k' + b', streaming k' with contiguous
-//               whole-wave loads (one k' row per 16-byte lane group) and a
-//               butterfly reduction.  Writes s_hat and per-slice (max, sum exp)
-//               partials of each head's LSE.  Reading all of k' once dominates
-//               the step's bytes.
-//   dec_select  one workgroup per (b, group): L_h from the partials, the rank
-//               key, per-wave top-k lists in LDS, their merged top-k ascending,
-//               and each head's s_hat on it.
-//   dec_attend  one workgroup per (b, group, work item), an item being a selected
-//               chunk or a window chunk: the G heads are the columns of MFMA
-//               tiles for the logits and for o = sum p v; the item's partial is
-//               its log-weight (s_hat for a selected chunk, the token-level
-//               log-mass for a window chunk) and its normalised output.
-//   dec_fuse    one wave per (b, head): the exp(log-weight) average of the
+//   dec_score   two roles in one launch.  Scoring blocks stream every
+//               candidate's k' once (whole-wave contiguous loads, a butterfly
+//               reduction) and write s_hat, a (max, sum exp) partial of the
+//               head's LSE, the slice's top-k of s_hat and its four largest
+//               keys.  Window blocks (after them in the grid) attend the query
+//               to each chunk of its window, which needs no selection; the one
+//               holding the new token appends its key/value row to the caches.
+//   dec_headsel one wave per (b, head, share of slices): the share's top-k of
+//               s_hat from its slice lists, pruned by its slices' largest keys;
+//               the first share also forms L_h.
+//   dec_attend  one workgroup per (b, group, selected slot): every workgroup of
+//               a group forms the group's selection from the heads' share lists
+//               (for several heads: the top-k by rank key
+//               r = max_h (s_hat_h - L_h) over the union of the heads'
+//               choices), then attends the chunk of its slot.
+//   dec_fuse    one workgroup per (b, head): the exp(log-weight) average of the
 //               items' outputs and L = LSE(s_hat over Sel + {log Z_win}).
 //   summarize   (list mode) chunks completed by this step's token.
+//
+// Why the union holds the selection: r_c is attained at some head h*; if c were
+// not in h*'s top-k by s_hat (equal s_hat: lower chunk first), k chunks would
+// precede it there, and each has r >= s_hat_{h*} - L_{h*} >= r_c, so c would
+// not be chosen either.  Only an exact fp32 tie of two rank keys whose s_hat
+// differ (a rounding tie, far below any decided gap) can make the choice differ
+// from ranking every candidate.  A slice's top-k likewise holds every candidate
+// of the slice that is in the head's top-k.
+//
 // Stages hand over through kernel boundaries: a device-wide fence per block (a
 // last-block ticket) costs an L2 write-back on a multi-XCD part.
 #include "hils_internal.h"
@@ -31,19 +40,23 @@ namespace hils {
 namespace {
 
 constexpr int kS = 64;
-constexpr int kSlice = 256;   // candidates per scoring workgroup (4 waves x 64 lanes)
+constexpr int kThreads = 256;
 
 struct DecPos {
   int64_t p[64];
 };
 
 struct DecWs {
-  float* shat;        // [B, Hq, NCcap]
+  float* shat;        // [B, Hq, NCcap] every candidate's s_hat
   float2* lpart;      // [B, Hq, nslice] (max, sum) in log2 units
-  int32_t* idx;       // [B, Hkv, topk]
-  float* ssel;        // [B, Hq, topk]
-  float* apart;       // [B, Hkv, nitems, G, D + 2] per item: normalised output, log-weight
-  int nslice, selj, nitems;
+  uint32_t* lkey;     // [B, Hq, nslice, kk] each slice's top-k keys of s_hat (0: none)
+  int32_t* lid;       // [B, Hq, nslice, kk] their chunk ids (ascending within a slice)
+  uint32_t* lk4;      // [B, Hq, nslice, 4] the four largest keys of each slice (0: none)
+  uint32_t* hkey;     // [B, Hq, kMaxShares, kk] each share's top-k keys of s_hat (0: none)
+  int32_t* hid;       // [B, Hq, kMaxShares, kk] their chunk ids
+  float* Lh;          // [B, Hq] each head's LSE over the candidates
+  float* apart;       // [B, Hkv, nitems, G, D + 2]: items [0, kk) selected, [kk, kk + nwin) window
+  int nslice, sj, kk, nwin, nitems, mj;
 };
 
 struct DecKArgs {
@@ -94,320 +107,69 @@ __device__ __forceinline__ void butterfly(float (&v)[N], int lane) {
   }
 }
 
-// Scoring streams k' with whole-wave contiguous loads: PPR lanes cover one k'
-// row (16 bytes each), so one load instruction reads RPI consecutive rows.  Each
-// lane multiplies its 16-byte piece by the matching piece of q_hat; a butterfly
-// over the PPR lanes of a row (PPR - 1 shuffles for PPR row sets) leaves lane t of
-// each row group with the complete dot product of row RPI*t + group.
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void dec_score_kernel(DecKArgs a) {
-  constexpr int EPV = 16 / sizeof(T);
-  constexpr int PPR = D / EPV;        // lanes per k' row
-  constexpr int RPI = kWave / PPR;    // rows per load instruction
-  constexpr int NI = PPR;             // load instructions per 64 rows (= kWave / RPI)
-  __shared__ float red[4][2];
-  // one workgroup per (candidate slice, query head, b): a wave's loads are two
-  // batches in flight, not one pair per head of the group in turn
-  const int slice = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int g = h / G;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int64_t i = a.pos.p[b];
-  const int64_t nc = num_candidates(i, a.S, a.W);
-  const int64_t bg = (int64_t)b * a.Hkv + g;
-  if (slice == 0 && h % G == 0) {
-    // append this step's key/value row
-    const int64_t row = (bg * a.Lcap + i) * D;
-    const T* kn = static_cast<const T*>(a.k_new) + bg * D;
-    const T* vn = static_cast<const T*>(a.v_new) + bg * D;
-    for (int e = threadIdx.x * EPV; e < D; e += blockDim.x * EPV) {
-      *reinterpret_cast<uint4*>(static_cast<T*>(a.kc) + row + e) = *reinterpret_cast<const uint4*>(kn + e);
-      *reinterpret_cast<uint4*>(static_cast<T*>(a.vc) + row + e) = *reinterpret_cast<const uint4*>(vn + e);
-    }
-  }
-  const int64_t c0 = (int64_t)slice * kSlice;
-  float2* lp = a.w.lpart + ((int64_t)b * a.Hq + h) * a.w.nslice + slice;
-  if (c0 >= nc) {
-    if (threadIdx.x == 0) *lp = make_float2(kNegInf, 0.f);
-    return;
-  }
-  const int pc = lane % PPR, rg = lane / PPR;
-  const int64_t cw = c0 + wave * kWave;               // this wave's first candidate
-  const int r = RPI * pc + rg;                        // row whose dot product this lane ends with
-  const int64_t c = cw + r;
-  const bool ok = c < nc;
-  float qv[EPV];
-  {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) + ((int64_t)b * a.Hq + h) * D + pc * EPV);
-    const T* t = reinterpret_cast<const T*>(&u);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) qv[e] = to_f<T>(t[e]);
-  }
-  const T* kb = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * a.NCcap + cw) * D + pc * EPV;
-  const float bv = ok ? a.bsum[((int64_t)b * a.Hq + h) * a.NCcap + c] : 0.f;
-  float v[NI];
-  // two batches of loads keep the live registers within four waves per SIMD
-  constexpr int NB = NI >= 8 ? NI / 2 : NI;
-#pragma unroll
-  for (int t0 = 0; t0 < NI; t0 += NB) {
-    uint4 u[NB];
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const int row = RPI * (t0 + t) + rg;
-      u[t] = cw + row < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)row * D) : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const T* x = reinterpret_cast<const T*>(&u[t]);
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) acc = fmaf(qv[e], to_f<T>(x[e]), acc);
-      v[t0 + t] = acc;
-    }
-  }
-  // butterfly over the PPR lanes of a row: after the step with mask m, lanes
-  // with bit m set hold the upper half of the remaining row sets
-  butterfly<PPR / 2, NI>(v, lane);
-  const float s = fmaf(v[0], a.scale, bv);
-  if (ok) a.w.shat[((int64_t)b * a.Hq + h) * a.NCcap + c] = s;
-  const float xl = ok ? s * kLog2e : kNegInf;
-  const float mw = wave_max(xl);
-  const float zw = wave_sum(xl == kNegInf ? 0.f : hw_exp2(xl - mw));
-  if (lane == 0) {
-    red[wave][0] = mw;
-    red[wave][1] = zw;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = kNegInf, Z = 0.f;
-    for (int w = 0; w < 4; ++w) lse_merge(M, Z, red[w][0], red[w][1]);
-    *lp = make_float2(M, Z);
-  }
-}
-
-// One workgroup of kSelWaves waves per (b, g).  L_h from the slice partials;
-// wave w ranks the candidates [w*64J, (w+1)*64J) (rank key r = max_h(s_hat_h -
-// L_h), or s_hat for one head) and keeps its exact top-k in LDS, in ascending
-// chunk order; wave 0 then takes the top-k of the concatenated lists (whose
-// positions ascend with the chunk index, so ties still go to the lower chunk),
-// writes the ids ascending and each head's s_hat on them.  With |C_i| <= k every
-// candidate is selected.
-constexpr int kSelWaves = 16;
-
-template <int G, int J>
-__global__ __launch_bounds__(64 * kSelWaves) void dec_select_kernel(DecKArgs a) {
-  constexpr int JM = kSelWaves;     // merge keys per lane: kSelWaves lists of <= 64 entries
-  __shared__ float Ls[G];
-  __shared__ uint32_t lkey[kSelWaves][64];
-  __shared__ int32_t lid[kSelWaves][64];
-  __shared__ float lsv[kSelWaves][64][G];   // each listed candidate's s_hat per head
-  __shared__ int32_t wsel[kSelWaves][64];
-  __shared__ uint32_t sbuf[kSelWaves][64];
-  __shared__ int nlist[kSelWaves];
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int64_t i = a.pos.p[b];
-  const int64_t nc = num_candidates(i, a.S, a.W);
-  const int topk = a.topk;
-  const int64_t bg = (int64_t)b * a.Hkv + g;
-  auto shat = [&](int hh, int64_t c) { return a.w.shat[((int64_t)b * a.Hq + g * G + hh) * a.NCcap + c]; };
-  // output slot t (< topk) holds chunk c (-1: none) with scores sv[0..G)
-  auto emit = [&](int t, int32_t c, const float* sv) {
-    a.w.idx[bg * topk + t] = c;
-    if (a.idx_out) a.idx_out[bg * topk + t] = c;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-      a.w.ssel[((int64_t)b * a.Hq + g * G + hh) * topk + t] = c >= 0 ? sv[hh] : kNegInf;
-  };
-  if (nc <= topk) {
-    if (wave == 0 && lane < topk) {
-      float sv[G];
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) sv[hh] = lane < nc ? shat(hh, lane) : kNegInf;
-      emit(lane, lane < nc ? lane : -1, sv);
-    }
-    return;
-  }
-  // this wave's candidates c = cw + lane + 64 j.  With few enough per lane their
-  // scores are loaded first, so that the loads overlap the L_h merge below, and
-  // stay in registers; otherwise they are loaded in batches after it.
-  constexpr bool kHold = J * G <= 64 && J <= 16;
-  constexpr int JH = kHold ? J : 1;
-  const int64_t cw = (int64_t)wave * 64 * J;
-  const int cnt = (int)max<int64_t>(0, min<int64_t>(nc - cw, 64 * J));
-  const int jn = (cnt + 63) / 64;
-  float sv[G][JH];
-  if constexpr (kHold) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int64_t c = min<int64_t>(cw + lane + 64 * j, nc - 1);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) sv[hh][j] = j < jn ? shat(hh, c) : 0.f;
-    }
-  }
-  if (G > 1) {
-    if (wave < G) {   // wave hh: L_h from the slice partials, lanes over slices
-      const float2* lp = a.w.lpart + ((int64_t)b * a.Hq + g * G + wave) * a.w.nslice;
-      float M = kNegInf, Z = 0.f;
-      const int ns = (int)((nc + kSlice - 1) / kSlice);
-      for (int sl = lane; sl < ns; sl += kWave) lse_merge(M, Z, lp[sl].x, lp[sl].y);
-      const float Mw = wave_max(M);
-      const float Zw = wave_sum(M == kNegInf ? 0.f : Z * hw_exp2(M - Mw));
-      if (lane == 0) Ls[wave] = (Mw + hw_log2(Zw)) * kLn2;
-    }
-    __syncthreads();
-  }
-  uint32_t keys[J];
-  constexpr int JB = kHold ? J : (32 / G > 0 ? 32 / G : 1);   // keys per batch of loads
-#pragma unroll
-  for (int j0 = 0; j0 < J; j0 += JB) {
-    float xb[G][JB];
-    if constexpr (!kHold) {   // the batch's score loads first (clamped in range)
-#pragma unroll
-      for (int j = 0; j < JB; ++j)
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-          xb[hh][j] = j0 + j < jn ? shat(hh, min<int64_t>(cw + lane + 64 * (j0 + j), nc - 1)) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < JB; ++j) {
-      float r = kNegInf;
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float x = kHold ? sv[hh][j0 + j] : xb[hh][j];
-        r = G > 1 ? fmaxf(r, x - Ls[hh]) : x;
-      }
-      keys[j0 + j] = (j0 + j < jn && cw + lane + 64 * (j0 + j) < nc) ? order_key(r) : 0u;
-    }
-  }
-  // ---- per-wave exact top-k over its candidate range, with the scores of the
-  // listed candidates gathered from the lanes that hold them
-  int n = 0;
-  if (cnt > topk) {
-    wave_topk_u32<J>(keys, jn, topk, lane, sbuf[wave], wsel[wave], lkey[wave]);
-    n = topk;
-    wave_lds_sync();
-    const int id = lane < n ? wsel[wave][lane] : 0;
-    if constexpr (kHold) {
-      const int src = id % 64, jj = id / 64;
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float v = 0.f;
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-          const float x = __shfl(sv[hh][j], src, kWave);
-          if (j == jj) v = x;
-        }
-        if (lane < n) lsv[wave][lane][hh] = v;
-      }
-    } else if (lane < n) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) lsv[wave][lane][hh] = shat(hh, cw + id);
-    }
-    if (lane < n) lid[wave][lane] = (int32_t)(cw + id);
-  } else if (cnt > 0) {
-    n = cnt;
-    if (lane < n) {
-      lkey[wave][lane] = keys[0];
-      lid[wave][lane] = (int32_t)(cw + lane);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        if constexpr (kHold) lsv[wave][lane][hh] = sv[hh][0];
-        else lsv[wave][lane][hh] = shat(hh, cw + lane);
-      }
-    }
-  }
-  if (lane == 0) nlist[wave] = n;
-  __syncthreads();
-  if (wave != 0) return;
-  // ---- merge: positions w*64 + t, t < nlist[w]; ascending position = ascending chunk
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) total += nlist[w];
-  if (total <= topk) {   // every listed candidate is chosen (lists ascend with the chunk)
-    int base = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const int nw = nlist[w];
-      if (lane < nw) emit(base + lane, lid[w][lane], lsv[w][lane]);
-      base += nw;
-    }
-    if (lane >= base && lane < topk) emit(lane, -1, lsv[0][0]);
-    return;
-  }
-  // Each list holds at most TP = topk rounded up to a power of two entries, so
-  // lane + 64 j carries entry lane % TP of list LPJ j + lane / TP: with several
-  // lists per lane row the lane maxima span more keys, and the first bound of
-  // wave_topk_u32 leaves few enough keys for its one-pass path.  The numbering
-  // ascends with (list, entry), that is with the chunk.
-  const int TP = topk <= 16 ? 16 : (topk <= 32 ? 32 : 64);
-  const int LPJ = kWave / TP;
-  const int ml = lane / TP, me = lane % TP;
-  uint32_t mkeys[JM];
-#pragma unroll
-  for (int j = 0; j < JM; ++j) {
-    const int w = LPJ * j + ml;
-    mkeys[j] = (w < kSelWaves && me < nlist[w]) ? lkey[w][me] : 0u;
-  }
-  wave_topk_u32<JM>(mkeys, (kSelWaves + LPJ - 1) / LPJ, topk, lane, sbuf[0], wsel[0]);
-  wave_lds_sync();
-  if (lane < topk) {
-    const int id = wsel[0][lane];
-    const int l = id % 64;
-    const int w = LPJ * (id / 64) + l / TP, e = l % TP;
-    emit(lane, lid[w][e], lsv[w][e]);
-  }
-}
-
-// Work item j < nsel: selected chunk idx[j]; else window chunk l_i/S + (j - nsel).
-// One workgroup per (b, group, item), so that every item's loads are in flight
-// at once.  The G heads of the group are the 16 columns of MFMA tiles
-// (zero-padded): wave w takes the logits of tokens 16w .. 16w + 15 (S^T = K Q^T,
-// its K fragments loaded straight from HBM), the softmax statistics of each head
-// meet in LDS, V goes transposed into LDS, and O^T = V^T P^T gives wave w the
-// output dims 16(w + 4t) ...  The item's partial is its log-weight (s_hat for a
-// selected chunk, the token-level log-mass for a window chunk) and its
-// normalised output.
-constexpr int kAttThreads = 256;
+// ---------------------------------------------------------------- item attention
+// One work item = one chunk c of (b, group g): the G heads of the group are the 16
+// columns of MFMA tiles (zero-padded).  Wave w takes the logits of tokens 16w ..
+// 16w + 15 (S^T = K Q^T, its K fragments loaded straight from HBM), the softmax
+// statistics of each head meet in LDS, V goes transposed into LDS, and
+// O^T = V^T P^T gives wave w the output dims 16(w + 4t) ...  The item's partial
+// is its log-weight (s_hat for a selected chunk, the token-level log-mass for a
+// window chunk) and its normalised output.  A window chunk masks tokens outside
+// [l_i, i]; in the chunk holding i, row i is taken from k_new / v_new (and
+// written to the caches here), and rows past i are read as zero.
+template <typename T, int D>
+struct ItemSmem {
+  T vt[D * kS];       // V^T rows, swizzled
+  T pt[16 * kS];      // P^T as [head][token]
+  float red[2][4][16];
+};
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttThreads) void dec_attend_kernel(DecKArgs a) {
+__device__ __forceinline__ void attend_item(const DecKArgs& a, ItemSmem<T, D>& sm, int b, int g,
+                                            int slot, int64_t c, bool is_win, const float* lnw) {
   constexpr int EPV = 16 / sizeof(T);
   constexpr int KS = D / 32, MD = D / 16;
   constexpr int PK = D / EPV, PV = kS / EPV;         // 16-byte pieces per K / V^T row
   constexpr int VPW = PK / 4;                        // V pieces per lane (wave w: pieces w*VPW ..)
   constexpr int MDW = MD / 4;                        // output dim tiles per wave
   static_assert(G <= 16 && PK % 4 == 0 && MD % 4 == 0, "tiling");
-  __shared__ __align__(16) T vt[D * kS];     // V^T rows, swizzled
-  __shared__ __align__(16) T pt[16 * kS];    // P^T as [head][token]
-  __shared__ float red[2][4][16];            // per-wave head max and sum
-  const int item = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
   const int64_t i = a.pos.p[b];
   const int64_t lw = window_left(i, a.S, a.W);
-  const int64_t nc = lw / kS;
-  const int nsel = (int)min<int64_t>(nc, a.topk);
-  const int nwin = (int)(i / kS - lw / kS + 1);
-  if (item >= nsel + nwin) return;
   const int64_t bg = (int64_t)b * a.Hkv + g;
   const float sl2 = a.scale * kLog2e;
   const bool hcol = r16 < G;                 // this lane's column is a real head
   const int h = g * G + (hcol ? r16 : 0);
-  const bool is_win = item >= nsel;
-  const int64_t c = is_win ? lw / kS + (item - nsel) : (int64_t)a.w.idx[bg * a.topk + item];
   const T* kc = static_cast<const T*>(a.kc) + (bg * a.Lcap + c * kS) * D;
   const T* vc = static_cast<const T*>(a.vc) + (bg * a.Lcap + c * kS) * D;
+  const T* kn = static_cast<const T*>(a.k_new) + bg * D;
+  const T* vn = static_cast<const T*>(a.v_new) + bg * D;
+  const int64_t j0 = c * kS;
+  const bool last = is_win && c == i / kS;   // the chunk holding the new row
+  const int tn = (int)(i - j0);              // its position in that chunk
 
   // every load up front: K fragments (row = token 16 wave + r16), V pieces
   // (token = lane), Q^T fragments (column r16 = head)
   Frag<T> kf[KS], bq[KS];
+  {
+    const int t = 16 * wave + r16;
+    const T* kr = (last && t == tn) ? kn : kc + (int64_t)t * D;
 #pragma unroll
-  for (int kq = 0; kq < KS; ++kq) load_frag(kf[kq], kc + (int64_t)(16 * wave + r16) * D + 8 * grp + 32 * kq);
+    for (int kq = 0; kq < KS; ++kq) {
+      if (!last || t <= tn) load_frag(kf[kq], kr + 8 * grp + 32 * kq);
+      else zero_frag(kf[kq]);
+    }
+  }
   uint4 vr[VPW];
+  {
+    const T* vrow = (last && lane == tn) ? vn : vc + (int64_t)lane * D;
 #pragma unroll
-  for (int t = 0; t < VPW; ++t) vr[t] = *reinterpret_cast<const uint4*>(vc + (int64_t)lane * D + (wave * VPW + t) * EPV);
+    for (int t = 0; t < VPW; ++t)
+      vr[t] = (!last || lane <= tn) ? *reinterpret_cast<const uint4*>(vrow + (wave * VPW + t) * EPV)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+  }
   {
     const T* qrow = static_cast<const T*>(a.q) + ((int64_t)b * a.Hq + h) * D + 8 * grp;
 #pragma unroll
@@ -416,7 +178,14 @@ __global__ __launch_bounds__(kAttThreads) void dec_attend_kernel(DecKArgs a) {
       else zero_frag(bq[kq]);
     }
   }
-  const float lnw_sel = (!is_win && hcol) ? a.w.ssel[((int64_t)b * a.Hq + h) * a.topk + item] : 0.f;
+  if (last && threadIdx.x < PK) {   // append this step's key/value row
+    const int64_t row = (bg * a.Lcap + i) * D + threadIdx.x * EPV;
+    *reinterpret_cast<uint4*>(static_cast<T*>(a.kc) + row) =
+        *reinterpret_cast<const uint4*>(kn + threadIdx.x * EPV);
+    *reinterpret_cast<uint4*>(static_cast<T*>(a.vc) + row) =
+        *reinterpret_cast<const uint4*>(vn + threadIdx.x * EPV);
+  }
+  const float lnw_sel = (!is_win && hcol) ? lnw[r16] : 0.f;
 
   // S^T tile of tokens 16 wave + (4 grp + q4), column r16
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -425,40 +194,40 @@ __global__ __launch_bounds__(kAttThreads) void dec_attend_kernel(DecKArgs a) {
   float x[4], mx = kNegInf;
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    const int64_t j = c * kS + 16 * wave + 4 * grp + q4;
+    const int64_t j = j0 + 16 * wave + 4 * grp + q4;
     const bool ok = !is_win || (j >= lw && j <= i);
     x[q4] = ok ? acc[q4] * sl2 : kNegInf;
     mx = fmaxf(mx, x[q4]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
   mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  if (grp == 0) red[0][wave][r16] = mx;
+  if (grp == 0) sm.red[0][wave][r16] = mx;
   // V transposed into LDS: row d, token = lane
 #pragma unroll
   for (int t = 0; t < VPW; ++t) {
     const T* xv = reinterpret_cast<const T*>(&vr[t]);
     const int d0 = (wave * VPW + t) * EPV;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) vt[swz<PV>(d0 + e, lane / EPV) * EPV + lane % EPV] = xv[e];
+    for (int e = 0; e < EPV; ++e) sm.vt[swz<PV>(d0 + e, lane / EPV) * EPV + lane % EPV] = xv[e];
   }
   __syncthreads();
-  const float m = fmaxf(fmaxf(red[0][0][r16], red[0][1][r16]), fmaxf(red[0][2][r16], red[0][3][r16]));
+  const float m = fmaxf(fmaxf(sm.red[0][0][r16], sm.red[0][1][r16]), fmaxf(sm.red[0][2][r16], sm.red[0][3][r16]));
   float p[4], ps = 0.f;
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
-    p[q4] = hw_exp2(x[q4] - m);   // every head has an unmasked token in every item
+    p[q4] = hw_exp2(x[q4] - m);   // every item has an unmasked token for every head
     ps += p[q4];
   }
   ps += __shfl_xor(ps, 16, kWave);
   ps += __shfl_xor(ps, 32, kWave);
-  if (grp == 0) red[1][wave][r16] = ps;
+  if (grp == 0) sm.red[1][wave][r16] = ps;
   {
-    T* prow = pt + r16 * kS + 16 * wave + 4 * grp;
+    T* prow = sm.pt + r16 * kS + 16 * wave + 4 * grp;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) prow[q4] = from_f<T>(p[q4]);
   }
   __syncthreads();
-  const float l = (red[1][0][r16] + red[1][1][r16]) + (red[1][2][r16] + red[1][3][r16]);
+  const float l = (sm.red[1][0][r16] + sm.red[1][1][r16]) + (sm.red[1][2][r16] + sm.red[1][3][r16]);
 
   // O^T tiles: dims 16 md + 4 grp + q4, column r16
   f32x4_t o[MDW];
@@ -469,14 +238,14 @@ __global__ __launch_bounds__(kAttThreads) void dec_attend_kernel(DecKArgs a) {
 #pragma unroll
     for (int k2 = 0; k2 < kS / 32; ++k2) {
       Frag<T> af, pf;
-      load_frag_swz<PV>(af, vt, 16 * md + r16, 8 * grp + 32 * k2);
-      load_frag(pf, pt + r16 * kS + 8 * grp + 32 * k2);
+      load_frag_swz<PV>(af, sm.vt, 16 * md + r16, 8 * grp + 32 * k2);
+      load_frag(pf, sm.pt + r16 * kS + 8 * grp + 32 * k2);
       mma(o[t], af, pf);
     }
   }
   // partial: log-weight (natural log) and the normalised output
   if (hcol) {
-    float* ap = a.w.apart + ((bg * a.w.nitems + item) * G + r16) * (D + 2);
+    float* ap = a.w.apart + ((bg * a.w.nitems + slot) * G + r16) * (D + 2);
     const float inv = 1.f / l;
 #pragma unroll
     for (int t = 0; t < MDW; ++t)
@@ -486,6 +255,523 @@ __global__ __launch_bounds__(kAttThreads) void dec_attend_kernel(DecKArgs a) {
   }
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, kWave));
+  return x;
+}
+
+// The k-th largest of the keys held J per lane (0 when fewer than k are nonzero),
+// bit by bit from the top with ballot counts.
+template <int J>
+__device__ __forceinline__ uint32_t wave_kth_u32(const uint32_t (&keys)[J], int jn, int k) {
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (j < jn) n += __popcll(__ballot(keys[j] >= c));
+    if (n >= k) t = c;
+  }
+  return t;
+}
+
+// ---------------------------------------------------------------- scoring
+struct ListSmem {
+  float red[4][2];
+  uint32_t wkey[4][64];   // each wave's top-k keys, ascending chunk order
+  int32_t wpos[4][64];
+  uint32_t sbuf[4][64];
+  int nw[4];
+  int32_t msel[64];
+};
+
+// The top-k (lists of at most 64) as keys and positions of n <= 64*J keys held J
+// per lane at position lane + 64 j; fewer than or exactly k present: all of them.
+// Writes n_out entries ascending by position.
+template <int J>
+__device__ __forceinline__ int list_topk(const uint32_t (&keys)[J], int jn, int npresent, int topk,
+                                         int lane, uint32_t* sbuf, int32_t* opos, uint32_t* okey) {
+  if (npresent > topk) {
+    wave_topk_u32<J>(keys, jn, topk, lane, sbuf, opos, okey);
+    return topk;
+  }
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < jn) {
+      const bool s = keys[j] != 0u;
+      const uint64_t msk = __ballot(s);
+      if (s) {
+        const int ps = base + lane_prefix(msk, lane);
+        opos[ps] = lane + 64 * j;
+        okey[ps] = keys[j];
+      }
+      base += __popcll(msk);
+    }
+  }
+  return base;
+}
+
+// A slice of 256*SJ candidates of one (b, head): wave w streams candidates
+// [c0 + 64 SJ w, + 64 SJ) in SJ blocks of 64.  PPR lanes cover one k' row with
+// 16-byte pieces, so one load instruction reads RPI consecutive rows; each lane
+// multiplies its piece by the matching piece of q_hat and a butterfly over the
+// PPR lanes of a row leaves one row's dot product per lane, which a permute moves
+// to lane order (lane l: candidate l of the block).
+template <typename T, int D, int SJ>
+__device__ __forceinline__ void score_slice(const DecKArgs& a, ListSmem& sm, int sblk) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int PPR = D / EPV;        // lanes per k' row
+  constexpr int RPI = kWave / PPR;    // rows per load instruction
+  constexpr int NI = PPR;             // load instructions per 64 rows
+  const int slice = sblk % a.w.nslice;
+  const int h = (sblk / a.w.nslice) % a.Hq;
+  const int b = sblk / (a.w.nslice * a.Hq);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int64_t i = a.pos.p[b];
+  const int64_t nc = num_candidates(i, a.S, a.W);
+  const int64_t c0 = (int64_t)slice * (kThreads * SJ);
+  if (c0 >= nc) return;                                 // the selection reads slices < nc only
+  const int64_t bh = (int64_t)b * a.Hq + h;
+  const int kk = a.w.kk;
+  const int pc = lane % PPR, rg = lane / PPR;
+  float qv[EPV];
+  {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) + bh * D + pc * EPV);
+    const T* t = reinterpret_cast<const T*>(&u);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) qv[e] = to_f<T>(t[e]);
+  }
+  const int64_t cw0 = c0 + (int64_t)wave * 64 * SJ;     // this wave's first candidate
+  const T* kb = static_cast<const T*>(a.ksum) + (bh * a.NCcap + cw0) * D + pc * EPV;
+  const int src = (lane % RPI) * PPR + lane / RPI;      // lane holding row `lane`'s dot product
+  // Loads go out in batches of NB, two batches ahead of the arithmetic, so every
+  // wave keeps a steady number of loads in flight across its SJ blocks.
+  constexpr int NB = NI >= 8 ? NI / 2 : NI;             // loads per batch
+  constexpr int NBS = NI / NB;                          // batches per block of 64 rows
+  constexpr int NBAT = NBS * SJ;
+  auto issue = [&](int q, uint4 (&u)[NB]) {
+    const int j = q / NBS, t0 = (q % NBS) * NB;
+    const int64_t cb = cw0 + 64 * j;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const int row = RPI * (t0 + t) + rg;
+      u[t] = cb + row < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)(64 * j + row) * D)
+                           : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  float bv[SJ];
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) {
+    const int64_t c = cw0 + 64 * j + lane;
+    bv[j] = c < nc ? a.bsum[bh * a.NCcap + c] : 0.f;
+  }
+  uint4 buf[2][NB];
+  issue(0, buf[0]);
+  if (NBAT > 1) issue(1, buf[1]);
+  float sv[SJ];
+  float v[NI];
+#pragma unroll
+  for (int q = 0; q < NBAT; ++q) {
+    const int t0 = (q % NBS) * NB;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const T* x = reinterpret_cast<const T*>(&buf[q % 2][t]);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc = fmaf(qv[e], to_f<T>(x[e]), acc);
+      v[t0 + t] = acc;
+    }
+    if (q + 2 < NBAT) issue(q + 2, buf[q % 2]);
+    // keep the loads where they are: hoisting every block's loads to the top
+    // would hold all of them in registers at once
+    __builtin_amdgcn_sched_barrier(0);
+    if (q % NBS == NBS - 1) {   // a block of 64 rows is complete
+      const int j = q / NBS;
+      float w[NI];
+#pragma unroll
+      for (int t = 0; t < NI; ++t) w[t] = v[t];
+      butterfly<PPR / 2, NI>(w, lane);
+      const float dot = __shfl(w[0], src, kWave);
+      const int64_t c = cw0 + 64 * j + lane;
+      const bool ok = c < nc;
+      const float sc = fmaf(dot, a.scale, bv[j]);
+      if (ok) a.w.shat[bh * a.NCcap + c] = sc;
+      sv[j] = ok ? sc : kNegInf;
+    }
+  }
+  // the head's LSE partial of the slice (log2 units)
+  float mw = kNegInf;
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) mw = fmaxf(mw, sv[j] * kLog2e);
+  mw = wave_max(mw);
+  float zl = 0.f;
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) zl += sv[j] == kNegInf ? 0.f : hw_exp2(sv[j] * kLog2e - mw);
+  const float zw = wave_sum(zl);
+  // this wave's top-k of s_hat (ties: lower chunk), ascending chunk order
+  const int nvw = (int)max<int64_t>(0, min<int64_t>(nc - cw0, 64 * SJ));
+  uint32_t keys[SJ];
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) keys[j] = sv[j] == kNegInf ? 0u : order_key(sv[j]);
+  const int nl = list_topk<SJ>(keys, (nvw + 63) / 64, nvw, kk, lane, sm.sbuf[wave], sm.wpos[wave],
+                               sm.wkey[wave]);
+  if (lane == 0) {
+    sm.red[wave][0] = mw;
+    sm.red[wave][1] = zw;
+    sm.nw[wave] = nl;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  if (lane == 0) {
+    float M = kNegInf, Z = 0.f;
+    for (int w = 0; w < 4; ++w) lse_merge(M, Z, sm.red[w][0], sm.red[w][1]);
+    a.w.lpart[bh * a.w.nslice + slice] = make_float2(M, Z);
+  }
+  // merge the four wave lists: entry e of wave w's list sits at position
+  // 64 jj + lane with w = LPJ jj + lane / TP, e = lane % TP (ascending chunk order)
+  const int TP = kk <= 16 ? 16 : (kk <= 32 ? 32 : 64);
+  const int LPJ = kWave / TP;
+  const int ml = lane / TP, me = lane % TP;
+  uint32_t mk[4];
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) tot += sm.nw[w];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int w = LPJ * jj + ml;
+    mk[jj] = (w < 4 && me < sm.nw[w]) ? sm.wkey[w][me] : 0u;
+  }
+  const int jn = (4 + LPJ - 1) / LPJ;
+  int32_t* mpos = sm.msel;
+  uint32_t* mkey = sm.sbuf[1];   // wave 1's buffer is free once the lists are merged
+  const int n = list_topk<4>(mk, jn, tot, kk, lane, sm.sbuf[0], mpos, mkey);
+  wave_lds_sync();
+  if (lane < kk) {
+    uint32_t key = 0u;
+    int32_t id = -1;
+    if (lane < n) {
+      const int ps = mpos[lane];
+      const int w = LPJ * (ps / 64) + (ps % 64) / TP, e = (ps % 64) % TP;
+      key = mkey[lane];
+      id = (int32_t)(c0 + (int64_t)w * 64 * SJ + sm.wpos[w][e]);
+    }
+    const int64_t o = (bh * a.w.nslice + slice) * kk + lane;
+    a.w.lkey[o] = key;
+    a.w.lid[o] = id;
+  }
+  // the slice's four largest keys: the selection prunes the lists with them
+  uint32_t x = lane < n ? mkey[lane] : 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t m = wave_max_u32(x);
+    if (lane == 0) a.w.lk4[(bh * a.w.nslice + slice) * 4 + r] = m;
+    const uint64_t at = __ballot(x == m && m != 0u);
+    if (at && lane == __ffsll((long long)at) - 1) x = 0u;
+  }
+}
+
+template <typename T, int D>
+union ScoreSmem {
+  ItemSmem<T, D> it;
+  ListSmem l;
+};
+
+template <typename T, int D, int G, int SJ>
+__global__ __launch_bounds__(kThreads) void dec_score_kernel(DecKArgs a) {
+  __shared__ __align__(16) ScoreSmem<T, D> sm;
+  // scoring blocks first: the window blocks fill the tail of the k' stream
+  const int nsb = a.B * a.Hq * a.w.nslice;
+  if ((int)blockIdx.x >= nsb) {   // a window item: chunk lw/S + w of (b, g)
+    const int x = (int)blockIdx.x - nsb;
+    const int w = x % a.w.nwin;
+    const int g = (x / a.w.nwin) % a.Hkv;
+    const int b = x / (a.w.nwin * a.Hkv);
+    const int64_t i = a.pos.p[b];
+    const int64_t lw = window_left(i, a.S, a.W);
+    if (w > (int)(i / kS - lw / kS)) return;
+    attend_item<T, D, G>(a, sm.it, b, g, a.w.kk + w, lw / kS + w, true, nullptr);
+    return;
+  }
+  score_slice<T, D, SJ>(a, sm.l, (int)blockIdx.x);
+}
+
+// ---------------------------------------------------------------- selection
+// Two stages, spread over many workgroups (one compute unit per (b, group)
+// would run thousands of ballot steps while the rest of the chip idles):
+//  dec_headsel  one wave per (b, head, share of kSPS slices): the share's top-k
+//               of s_hat from its slices' lists (entry e of slice s at position
+//               s*kk + e: ascending chunk order).  The share's k-th largest key is
+//               at least theta, the k-th largest of its slices' four largest keys
+//               (at least k entries reach theta), so entries below theta cannot
+//               be chosen: when few reach it, the exact top-k runs on those
+//               survivors (compacted in position order), otherwise on every
+//               entry.  The first share's wave also forms L_h from the slice
+//               partials.
+//  dec_attend   each workgroup of a (b, group) forms the group's selection in
+//               its prologue, the same in every workgroup: each head's top-k
+//               from its share lists; for one head that is the selection,
+//               otherwise the union of the heads' choices is marked in an LDS
+//               bitmap over the candidates, listed in ascending chunk order with
+//               a block prefix count, each member's rank key
+//               r = max_h (s_hat_h - L_h) is formed from every head's s_hat, and
+//               wave 0 takes the top-k of the union by r.  The workgroup then
+//               attends the chunk of its slot.
+constexpr int kSPS = 32;          // slices per share
+constexpr int kMaxShares = 8;     // shares per head (<= kSPS * kMaxShares slices)
+constexpr int kMaxUnion = 8 * 64;
+
+// Entries present in slices [s0, s1) of a head: min(kk, candidates) each.
+__device__ __forceinline__ int slice_entries(int64_t nc, int slen, int kk, int s0, int s1) {
+  int n = 0;
+  for (int s = s0; s < s1; ++s) n += (int)min<int64_t>(kk, min<int64_t>(slen, nc - (int64_t)s * slen));
+  return n;
+}
+
+struct HeadSelSmem {
+  uint32_t sbuf[64];
+  uint32_t pkey[128];
+  int32_t ppos[128];
+  int32_t opos[64];
+  uint32_t okey[64];
+};
+
+template <int MJ>
+__global__ __launch_bounds__(64) void dec_headsel_kernel(DecKArgs a) {
+  __shared__ HeadSelSmem sm;
+  const int q = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int64_t i = a.pos.p[b];
+  const int64_t nc = num_candidates(i, a.S, a.W);
+  const int topk = a.topk, kk = a.w.kk;
+  if (nc <= topk) return;                 // every candidate is chosen: nothing to rank
+  const int slen = kThreads * a.w.sj;
+  const int ns = (int)((nc + slen - 1) / slen);
+  const int s0 = q * kSPS;
+  if (s0 >= ns) return;
+  const int s1 = min(ns, s0 + kSPS);
+  const int64_t bh = (int64_t)b * a.Hq + h;
+  const int64_t lbase = (bh * a.w.nslice + s0) * kk;
+  const int nent = (s1 - s0) * kk;
+  const int jn = (nent + 63) / 64;
+  uint32_t keys[MJ];
+#pragma unroll
+  for (int j = 0; j < MJ; ++j) {
+    const int p = lane + 64 * j;
+    keys[j] = p < nent ? a.w.lkey[lbase + p] : 0u;
+  }
+  uint32_t pool[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = lane + 64 * j;
+    pool[j] = p < 4 * (s1 - s0) ? a.w.lk4[(bh * a.w.nslice + s0) * 4 + p] : 0u;
+  }
+  if (q == 0) {   // the head's LSE from the slice partials
+    const float2* lp = a.w.lpart + bh * a.w.nslice;
+    float M = kNegInf, Z = 0.f;
+    for (int s = lane; s < ns; s += kWave) lse_merge(M, Z, lp[s].x, lp[s].y);
+    const float Mw = wave_max(M);
+    const float Zw = wave_sum(M == kNegInf ? 0.f : Z * hw_exp2(M - Mw));
+    if (lane == 0) a.w.Lh[bh] = (Mw + hw_log2(Zw)) * kLn2;
+  }
+  const int npw = slice_entries(nc, slen, kk, s0, s1);
+  int nl = 0;
+  bool pruned = false;
+  if (npw > topk) {
+    const uint32_t theta = wave_kth_u32<2>(pool, 2, topk);
+    int nsv = 0;
+#pragma unroll
+    for (int j = 0; j < MJ; ++j)
+      if (j < jn) nsv += __popcll(__ballot(theta != 0u && keys[j] >= theta));
+    if (theta != 0u && nsv <= 128) {
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
+        if (j < jn) {
+          const bool sv = keys[j] >= theta;
+          const uint64_t msk = __ballot(sv);
+          if (sv) {
+            const int ps = base + lane_prefix(msk, lane);
+            sm.pkey[ps] = keys[j];
+            sm.ppos[ps] = lane + 64 * j;
+          }
+          base += __popcll(msk);
+        }
+      }
+      wave_lds_sync();
+      uint32_t k2[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) k2[j] = lane + 64 * j < nsv ? sm.pkey[lane + 64 * j] : 0u;
+      nl = list_topk<2>(k2, 2, nsv, topk, lane, sm.sbuf, sm.opos, sm.okey);
+      wave_lds_sync();
+      if (lane < nl) sm.opos[lane] = sm.ppos[sm.opos[lane]];
+      pruned = true;
+    }
+  }
+  if (!pruned) nl = list_topk<MJ>(keys, jn, npw, topk, lane, sm.sbuf, sm.opos, sm.okey);
+  wave_lds_sync();
+  if (lane < kk) {
+    const int64_t o = (bh * kMaxShares + q) * kk + lane;
+    a.w.hkey[o] = lane < nl ? sm.okey[lane] : 0u;
+    a.w.hid[o] = lane < nl ? a.w.lid[lbase + sm.opos[lane]] : -1;
+  }
+}
+
+struct GroupSelSmem {
+  float L[8];
+  uint32_t sbuf[4][64];
+  int32_t hpos[4][64];
+  uint32_t hkey[8][64];
+  int32_t hid[8][64];
+  int nh[8];
+  int32_t ulist[kMaxUnion];
+  uint32_t ukey[kMaxUnion];
+  int32_t scan[4];
+  int32_t osel[64];
+  int32_t chosen[64];
+  float lnw[8];
+};
+
+// The group's selection (ascending chunk ids in sm.chosen[0..min(nc, k))) and, for
+// slot `slot`, each head's s_hat in sm.lnw.  Every workgroup of (b, g) forms the
+// same selection; the one of slot 0 writes it to idx_out.
+template <int G>
+__device__ void group_select(const DecKArgs& a, GroupSelSmem& sm, uint32_t* bitmap, int b, int g,
+                             int slot) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int64_t i = a.pos.p[b];
+  const int64_t nc = num_candidates(i, a.S, a.W);
+  const int topk = a.topk, kk = a.w.kk;
+  auto shat = [&](int hh, int64_t c) { return a.w.shat[((int64_t)b * a.Hq + g * G + hh) * a.NCcap + c]; };
+  if (nc <= topk) {   // every candidate is chosen
+    for (int t = threadIdx.x; t < topk; t += kThreads) sm.chosen[t] = t < nc ? t : -1;
+  } else {
+    const int slen = kThreads * a.w.sj;
+    const int ns = (int)((nc + slen - 1) / slen);
+    const int nsh = (ns + kSPS - 1) / kSPS;
+    // each head's top-k from its share lists (share q: position q*kk + e)
+    for (int hh = wave; hh < G; hh += kThreads / kWave) {
+      const int64_t bh = (int64_t)b * a.Hq + g * G + hh;
+      const int64_t hb = bh * kMaxShares * kk;
+      constexpr int JH = kMaxShares;   // kk <= 64 keys per share
+      uint32_t keys[JH];
+      int npres = 0;
+#pragma unroll
+      for (int j = 0; j < JH; ++j) {
+        const int p = lane + 64 * j;
+        keys[j] = p < nsh * kk ? a.w.hkey[hb + p] : 0u;
+      }
+      for (int q = 0; q < nsh; ++q)
+        npres += min(kk, slice_entries(nc, slen, kk, q * kSPS, min(ns, (q + 1) * kSPS)));
+      const int n = list_topk<JH>(keys, (nsh * kk + 63) / 64, npres, topk, lane, sm.sbuf[wave],
+                                  sm.hpos[wave], sm.hkey[hh]);
+      wave_lds_sync();
+      if (lane < n) sm.hid[hh][lane] = a.w.hid[hb + sm.hpos[wave][lane]];
+      if (lane == 0) {
+        sm.nh[hh] = n;
+        sm.L[hh] = a.w.Lh[bh];
+      }
+      wave_lds_sync();
+    }
+    __syncthreads();
+    if constexpr (G == 1) {
+      for (int t = threadIdx.x; t < topk; t += kThreads) sm.chosen[t] = sm.hid[0][t];   // nh = topk
+    } else {
+      // union of the heads' choices, in ascending chunk order
+      const int nwords = (int)((nc + 31) / 32);
+      for (int t = threadIdx.x; t < nwords; t += kThreads) bitmap[t] = 0u;
+      __syncthreads();
+      for (int t = threadIdx.x; t < G * 64; t += kThreads) {
+        const int hh = t / 64, e = t % 64;
+        if (e < sm.nh[hh]) {
+          const int32_t c = sm.hid[hh][e];
+          atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+        }
+      }
+      __syncthreads();
+      const int wpt = (nwords + kThreads - 1) / kThreads;
+      const int w0 = min(nwords, (int)threadIdx.x * wpt), w1 = min(w0 + wpt, nwords);
+      int cnt = 0;
+      for (int t = w0; t < w1; ++t) cnt += __popc(bitmap[t]);
+      int incl = cnt;   // block prefix count: within the wave, then over the waves
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+      }
+      if (lane == kWave - 1) sm.scan[wave] = incl;
+      __syncthreads();
+      int pos = incl - cnt, nu = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / kWave; ++w) {
+        pos += w < wave ? sm.scan[w] : 0;
+        nu += sm.scan[w];
+      }
+      for (int t = w0; t < w1; ++t) {
+        uint32_t m = bitmap[t];
+        while (m) {
+          const int bit = __ffs(m) - 1;
+          m &= m - 1u;
+          sm.ulist[pos++] = t * 32 + bit;
+        }
+      }
+      __syncthreads();   // nu >= topk: each head chose topk distinct chunks
+      for (int u = threadIdx.x; u < nu; u += kThreads) {
+        const int32_t c = sm.ulist[u];
+        float r = kNegInf;
+#pragma unroll
+        for (int h2 = 0; h2 < G; ++h2) r = fmaxf(r, shat(h2, c) - sm.L[h2]);
+        sm.ukey[u] = order_key(r);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        constexpr int JU = kMaxUnion / 64;
+        uint32_t uk[JU];
+#pragma unroll
+        for (int j = 0; j < JU; ++j) {
+          const int u = lane + 64 * j;
+          uk[j] = u < nu ? sm.ukey[u] : 0u;
+        }
+        const int n = list_topk<JU>(uk, (nu + 63) / 64, nu, topk, lane, sm.sbuf[0], sm.osel, sm.hkey[0]);
+        wave_lds_sync();
+        if (lane < topk) sm.chosen[lane] = lane < n ? sm.ulist[sm.osel[lane]] : -1;
+      }
+    }
+  }
+  __syncthreads();
+  if (slot == 0 && a.idx_out) {
+    const int64_t bg = (int64_t)b * a.Hkv + g;
+    for (int t = threadIdx.x; t < topk; t += kThreads) a.idx_out[bg * topk + t] = sm.chosen[t];
+  }
+  const int32_t c = sm.chosen[slot];
+  if ((int)threadIdx.x < G) sm.lnw[threadIdx.x] = c >= 0 ? shat((int)threadIdx.x, c) : 0.f;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- selected items
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kThreads) void dec_attend_kernel(DecKArgs a) {
+  __shared__ __align__(16) ItemSmem<T, D> it;
+  __shared__ GroupSelSmem sel;
+  extern __shared__ uint32_t bitmap[];   // ceil(candidates / 32) words
+  const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int64_t i = a.pos.p[b];
+  const int64_t nc = num_candidates(i, a.S, a.W);
+  if (slot >= (int)min<int64_t>(nc, a.topk)) {
+    if (slot == 0 && a.idx_out)   // no candidate yet: the selection is all padding
+      for (int t = threadIdx.x; t < a.topk; t += kThreads)
+        a.idx_out[((int64_t)b * a.Hkv + g) * a.topk + t] = -1;
+    return;
+  }
+  group_select<G>(a, sel, bitmap, b, g, slot);
+  attend_item<T, D, G>(a, it, b, g, slot, sel.chosen[slot], false, sel.lnw);
+}
+
+// ---------------------------------------------------------------- fusion
 // One workgroup of kFuseWaves waves per (b, query head): the output is the
 // average of the items' normalised outputs weighted by exp(log-weight), and L
 // the log of the total weight (the LSE over the selected chunks' s_hat and the
@@ -508,9 +794,11 @@ __global__ __launch_bounds__(64 * kFuseWaves) void dec_fuse_kernel(DecKArgs a) {
   const int nitems = nsel + (int)(i / kS - lw / kS + 1);   // <= 256 (checked on the host)
   const int64_t bg = (int64_t)b * a.Hkv + g;
   const float* ap = a.w.apart + (bg * a.w.nitems * G + hl) * (D + 2);
+  const int kk = a.w.kk;
+  auto slot_of = [&](int it) { return it < nsel ? it : kk + (it - nsel); };
   // item weights exp(lw_item - max): one item per thread, block max and sum
   const int it0 = threadIdx.x;
-  const float lwi = it0 < nitems ? ap[(int64_t)it0 * G * (D + 2) + D] : kNegInf;
+  const float lwi = it0 < nitems ? ap[(int64_t)slot_of(it0) * G * (D + 2) + D] : kNegInf;
   float mx = wave_max(lwi);
   if (lane == 0) mz[wave][0] = mx;
   __syncthreads();
@@ -534,7 +822,7 @@ __global__ __launch_bounds__(64 * kFuseWaves) void dec_fuse_kernel(DecKArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int it = itb + u * kFuseWaves;
-      const float* pp = ap + (int64_t)min(it, nitems - 1) * G * (D + 2) + lane * DPL;
+      const float* pp = ap + (int64_t)slot_of(min(it, nitems - 1)) * G * (D + 2) + lane * DPL;
 #pragma unroll
       for (int t = 0; t < DPL; ++t) x[u][t] = pp[t];
     }
@@ -562,43 +850,50 @@ __global__ __launch_bounds__(64 * kFuseWaves) void dec_fuse_kernel(DecKArgs a) {
   if (a.lse && lane == 0) a.lse[(int64_t)b * a.Hq + h] = mx + __logf(z);
 }
 
-// Candidates per selection wave: 64*J with kSelWaves waves covering every candidate.
-int pick_sel_j(int64_t max_nc) {
-  for (int J = 1; J <= 64; J <<= 1)
-    if ((int64_t)64 * J * kSelWaves >= max_nc) return J;
-  return -1;
+// ---------------------------------------------------------------- host side
+template <typename T, int D, int G, int SJ>
+hipError_t launch_score_sj(const DecKArgs& k, hipStream_t st) {
+  const int nsb = k.B * k.Hq * k.w.nslice;
+  KTimer tm(K_DEC_SCORE, st);
+  const int nwb = k.B * k.Hkv * k.w.nwin;   // window blocks after the scoring blocks
+  hipLaunchKernelGGL((dec_score_kernel<T, D, G, SJ>), dim3((unsigned)(nsb + nwb)), dim3(kThreads), 0, st, k);
+  return hipGetLastError();
 }
 
-template <int G>
-void launch_select_j(const DecKArgs& k, hipStream_t st) {
-  const dim3 grid(1, k.Hkv, k.B), block(64 * kSelWaves);
+hipError_t launch_headsel(const DecKArgs& k, hipStream_t st) {
+  const int nsh = (k.w.nslice + kSPS - 1) / kSPS;
+  const dim3 grid(nsh, k.Hq, k.B);
   KTimer tm(K_DEC_SELECT, st);
-  switch (k.w.selj) {
-    case 1: hipLaunchKernelGGL((dec_select_kernel<G, 1>), grid, block, 0, st, k); break;
-    case 2: hipLaunchKernelGGL((dec_select_kernel<G, 2>), grid, block, 0, st, k); break;
-    case 4: hipLaunchKernelGGL((dec_select_kernel<G, 4>), grid, block, 0, st, k); break;
-    case 8: hipLaunchKernelGGL((dec_select_kernel<G, 8>), grid, block, 0, st, k); break;
-    case 16: hipLaunchKernelGGL((dec_select_kernel<G, 16>), grid, block, 0, st, k); break;
-    case 32: hipLaunchKernelGGL((dec_select_kernel<G, 32>), grid, block, 0, st, k); break;
-    default: hipLaunchKernelGGL((dec_select_kernel<G, 64>), grid, block, 0, st, k); break;
+  switch (k.w.mj) {
+    case 1: hipLaunchKernelGGL((dec_headsel_kernel<1>), grid, dim3(64), 0, st, k); break;
+    case 2: hipLaunchKernelGGL((dec_headsel_kernel<2>), grid, dim3(64), 0, st, k); break;
+    case 4: hipLaunchKernelGGL((dec_headsel_kernel<4>), grid, dim3(64), 0, st, k); break;
+    case 8: hipLaunchKernelGGL((dec_headsel_kernel<8>), grid, dim3(64), 0, st, k); break;
+    case 16: hipLaunchKernelGGL((dec_headsel_kernel<16>), grid, dim3(64), 0, st, k); break;
+    default: hipLaunchKernelGGL((dec_headsel_kernel<32>), grid, dim3(64), 0, st, k); break;
   }
+  return hipGetLastError();
 }
 
 template <typename T, int D, int G>
 hipError_t launch_decode_tg(const DecKArgs& k, hipStream_t st) {
-  {
-    KTimer tm(K_DEC_SCORE, st);
-    hipLaunchKernelGGL((dec_score_kernel<T, D, G>), dim3(k.w.nslice, k.Hq, k.B), dim3(256), 0, st, k);
+  hipError_t e;
+  switch (k.w.sj) {
+    case 1: e = launch_score_sj<T, D, G, 1>(k, st); break;
+    default: e = launch_score_sj<T, D, G, 2>(k, st); break;
   }
-  if (k.topk > 0) launch_select_j<G>(k, st);
-  {
+  if (e != hipSuccess) return e;
+  if (k.topk > 0) {
+    e = launch_headsel(k, st);
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)((k.NCcap + 31) / 32) * 4;
     KTimer tm(K_DEC_ATTEND, st);
-    hipLaunchKernelGGL((dec_attend_kernel<T, D, G>), dim3(k.w.nitems, k.Hkv, k.B), dim3(kAttThreads), 0, st, k);
+    hipLaunchKernelGGL((dec_attend_kernel<T, D, G>), dim3(k.topk, k.Hkv, k.B), dim3(kThreads), lds, st, k);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  {
-    KTimer tm(K_DEC_FUSE, st);
-    hipLaunchKernelGGL((dec_fuse_kernel<T, D, G>), dim3(k.Hq, k.B), dim3(64 * kFuseWaves), 0, st, k);
-  }
+  KTimer tm(K_DEC_FUSE, st);
+  hipLaunchKernelGGL((dec_fuse_kernel<T, D, G>), dim3(k.Hq, k.B), dim3(64 * kFuseWaves), 0, st, k);
   return hipGetLastError();
 }
 
@@ -617,23 +912,47 @@ size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Candidates of the last cache row (the most any step can see).
 int64_t max_candidates(int64_t Lcap, int S, int W) { return Lcap > 0 ? num_candidates(Lcap - 1, S, W) : 0; }
 
+// Candidates per scoring thread SJ (a slice is 256 SJ candidates: 2 once a head
+// has more than 64 slices of 256), keys per lane MJ of one share (kSPS slice
+// lists of kk entries) and the number of slices; sj = 0 when the shares cannot
+// cover the candidates.
+void plan(int64_t NCcap, int kk, int* sj, int* mj, int* nslice) {
+  const int s = NCcap > 64 * 256 ? 2 : 1;
+  const int64_t ns = (NCcap + 256 * s - 1) / (256 * s);
+  const int m = (kSPS * kk + 63) / 64;
+  int j = 1;
+  while (j < m) j <<= 1;
+  *sj = ns <= (int64_t)kSPS * kMaxShares ? s : 0;
+  *mj = j;
+  *nslice = (int)(ns > 0 ? ns : 1);
+}
+
 void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk, DecWs* w,
             size_t* total, char* base) {
   const int64_t NCcap = Lcap / S;
-  const int nslice = (int)((NCcap + kSlice - 1) / kSlice);
-  const int nitems = topk + W / S + 2;
-  const int G = Hq / Hkv;
   const int kk = topk > 0 ? topk : 1;
+  int sj = 0, mj = 1, nslice = 1;
+  plan(NCcap, kk, &sj, &mj, &nslice);
+  const int nwin = W / S + 2;
+  const int nitems = kk + nwin;
+  const int G = Hq / Hkv;
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += a256(bytes); return p; };
   DecWs d{};
   d.shat = reinterpret_cast<float*>(take((size_t)B * Hq * NCcap * 4));
   d.lpart = reinterpret_cast<float2*>(take((size_t)B * Hq * nslice * 8));
-  d.idx = reinterpret_cast<int32_t*>(take((size_t)B * Hkv * kk * 4));
-  d.ssel = reinterpret_cast<float*>(take((size_t)B * Hq * kk * 4));
+  d.lkey = reinterpret_cast<uint32_t*>(take((size_t)B * Hq * nslice * kk * 4));
+  d.lid = reinterpret_cast<int32_t*>(take((size_t)B * Hq * nslice * kk * 4));
+  d.lk4 = reinterpret_cast<uint32_t*>(take((size_t)B * Hq * nslice * 4 * 4));
+  d.hkey = reinterpret_cast<uint32_t*>(take((size_t)B * Hq * kMaxShares * kk * 4));
+  d.hid = reinterpret_cast<int32_t*>(take((size_t)B * Hq * kMaxShares * kk * 4));
+  d.Lh = reinterpret_cast<float*>(take((size_t)B * Hq * 4));
   d.apart = reinterpret_cast<float*>(take((size_t)B * Hkv * nitems * G * (D + 2) * 4));
   d.nslice = nslice;
-  d.selj = pick_sel_j(max_candidates(Lcap, S, W));
+  d.sj = sj;
+  d.mj = mj;
+  d.kk = kk;
+  d.nwin = nwin;
   d.nitems = nitems;
   if (w) *w = d;
   if (total) *total = off + 256;
@@ -641,8 +960,12 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
 
 }  // namespace
 
-bool decode_supported(int64_t Lcap, int S, int W, int topk) {
-  return pick_sel_j(max_candidates(Lcap, S, W)) > 0 && topk + W / S + 2 <= 256;
+bool decode_supported(int64_t Lcap, int S, int W, int topk, int G) {
+  int sj = 0, mj = 0, ns = 0;
+  (void)G;
+  plan(Lcap / S, topk > 0 ? topk : 1, &sj, &mj, &ns);
+  // the union bitmap (one bit per candidate) must fit the LDS beside the rest
+  return sj > 0 && topk + W / S + 2 <= 256 && (Lcap / S + 31) / 32 * 4 <= 16384;
 }
 
 size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk) {

@@ -33,7 +33,7 @@ hils_status check_shape(const hils_shape* s, Mode mode) {
   if (mode == kDecode) {
     if (s->batch > 64) return HILS_E_UNSUPPORTED;
     if (s->seq_len % s->chunk != 0) return HILS_E_SHAPE;
-    if (!hils::decode_supported(s->seq_len, s->chunk, s->window, s->top_k)) return HILS_E_UNSUPPORTED;
+    if (!hils::decode_supported(s->seq_len, s->chunk, s->window, s->top_k, G)) return HILS_E_UNSUPPORTED;
     if (s->seq_len > (int64_t(1) << 31)) return HILS_E_UNSUPPORTED;
   } else if (mode == kPrefill) {
     if (s->seq_len / s->chunk > 4096) return HILS_E_UNSUPPORTED;  // <= 4096 chunks per sequence

@@ -122,6 +122,6 @@ class KTimer {
 };
 size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk);
 // Whether the decode selection can merge its per-span lists in one wave.
-bool decode_supported(int64_t Lcap, int S, int W, int topk);
+bool decode_supported(int64_t Lcap, int S, int W, int topk, int G);
 
 }  // namespace hils

@@ -30,7 +30,7 @@ def hils():
     return h
 
 
-def run_decode(hils, wl, starts, nsteps, seed=0, check_every=1):
+def run_decode(hils, wl, starts, nsteps, seed=0, check_every=1, poison=False):
     B, Hq, Hkv, d, S = wl.B, wl.Hq, wl.Hkv, wl.d, wl.S
     G = Hq // Hkv
     cap = -(-(max(starts) + nsteps) // S) * S + S
@@ -41,6 +41,10 @@ def run_decode(hils, wl, starts, nsteps, seed=0, check_every=1):
         kc_h[b, :, starts[b]:] = 0
         vc_h[b, :, starts[b]:] = 0
     kc, vc = kc_h.to(DEV), vc_h.to(DEV)
+    if poison:   # rows past each sequence's length hold NaN until a step writes them
+        for b in range(B):
+            kc[b, :, starts[b]:] = float("nan")
+            vc[b, :, starts[b]:] = float("nan")
     NCcap = cap // S
     ks = torch.zeros((B, Hq, NCcap, d), dtype=dt, device=DEV)
     bs = torch.zeros((B, Hq, NCcap), dtype=torch.float32, device=DEV)
@@ -135,3 +139,12 @@ def test_decode_matches_oracle(hils, name, wl, starts, nsteps):
             assert_close(bs[b, :, :c_hi], r["obs"][b, :, :c_hi], 1e-5, what="b' seq %d" % b)
             assert_close(ks[b, :, :c_hi], r["oks"][b, :, :c_hi], 2e-2 if wl.dtype == "bf16" else 1e-5,
                          5e-3, what="k' seq %d" % b)
+
+
+def test_decode_ignores_unwritten_rows(hils):
+    """Cache rows past each position hold NaN: the step must read only rows <= pos."""
+    wl = wk.custom(name="d4", kind="decode", dtype="bf16", B=2, Hq=8, Hkv=2, d=128, T=1500, S=64,
+                   k=4, W=192)
+    say("decode with NaN past the written rows")
+    run_decode(hils, wl, [1500, 1473], 70, seed=12, poison=True)
+
