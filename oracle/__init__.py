@@ -63,6 +63,9 @@ def lib():
         L.orc_rows.argtypes = [I, I, I, I, I, I, I, D, I64, P, P, P, P, P, P, I, I64, P, P, I, I64,
                                P, P, I64, P, P, P, P, P, P, P, P, I64]
         L.orc_rows.restype = I
+        L.orc_prefill_backward.argtypes = [I, I, I, I, I, I, I, D, I64, P, P, P, I, P, P, I, P, P, I64,
+                                           P, P, P, P, P, P, P, P, P, P]
+        L.orc_prefill_backward.restype = I
         L.orc_window_left.argtypes = [I64, I, I]
         L.orc_window_left.restype = I64
         L.orc_num_candidates.argtypes = [I64, I, I]
@@ -239,3 +242,44 @@ def to_dense(res: dict, B: int, Hq: int, Hkv: int, T: int, topk: int):
     lse = res["lse"].reshape(B, Hkv, T, G).transpose(0, 1, 3, 2).reshape(B, Hq, T)
     res = {"idx": idx, "gap": gap, "ncand": ncand, "ssel": ssel, "out": out, "lse": lse}
     return {k: np.ascontiguousarray(v) for k, v in res.items()}
+
+
+def prefill_backward(inp: dict, sel_idx, dout, dlse=None, *, S: int, W: int, topk: int,
+                     scale: float | None = None, ksum=None, bsum=None) -> dict:
+    """Gradients of sum(dout * out) + sum(dlse * lse) of the prefill forward with the
+    selection held at sel_idx [B,Hkv,T,k]: dq, dq_hat [B,Hq,T,d], dk, dv [B,Hkv,T,d]
+    (dk includes the summaries' part), dk_sum [B,Hq,NC,d], db_sum [B,Hq,NC] and
+    dq_land [B,Hq,NC,d], as float64.  ksum / bsum: the summaries the forward used
+    (default: the oracle's own, unrounded k')."""
+    q, k, v, ql, qh = inp["q"], inp["k"], inp["v"], inp["q_land"], inp["q_hat"]
+    qa, qdt = _as_np(q)
+    qha, _ = _as_np(qh)
+    qla, qldt = _as_np(ql)
+    assert qldt == qdt
+    ka, kdt = _as_np(k)
+    va, _ = _as_np(v)
+    B, Hq, T, d = qa.shape
+    Hkv = ka.shape[1]
+    NC = T // S
+    if scale is None:
+        scale = default_scale(d)
+    if ksum is None:
+        ksum, bsum = summarize(k, ql, S, Hq, scale=scale, ks_round=ORND_NONE, nc=NC)
+    ksum = np.ascontiguousarray(ksum, np.float64)
+    bsum = np.ascontiguousarray(bsum, np.float64)
+    si = np.ascontiguousarray(sel_idx, np.int32)
+    assert si.shape == (B, Hkv, T, topk)
+    g = np.ascontiguousarray(dout, np.float64)
+    gl = None if dlse is None else np.ascontiguousarray(dlse, np.float64)
+    out = {"dq": np.zeros((B, Hq, T, d)), "dq_hat": np.zeros((B, Hq, T, d)),
+           "dk": np.zeros((B, Hkv, T, d)), "dv": np.zeros((B, Hkv, T, d)),
+           "dk_sum": np.zeros((B, Hq, NC, d)), "db_sum": np.zeros((B, Hq, NC)),
+           "dq_land": np.zeros((B, Hq, NC, d))}
+    rc = lib().orc_prefill_backward(B, Hq, Hkv, d, S, W, topk, float(scale), T, _ptr(qa), _ptr(qha),
+                                    _ptr(qla), qdt, _ptr(ka), _ptr(va), kdt, _ptr(ksum), _ptr(bsum), NC,
+                                    _ptr(si), _ptr(g), _ptr(gl) if gl is not None else None,
+                                    *[_ptr(out[n]) for n in ("dq", "dq_hat", "dk", "dv", "dk_sum",
+                                                             "db_sum", "dq_land")])
+    if rc != 0:
+        raise RuntimeError("orc_prefill_backward failed: %d" % rc)
+    return out

@@ -356,3 +356,192 @@ int orc_rows(int B, int Hq, int Hkv, int d, int S, int W, int topk, double scale
     }
     return err;
 }
+
+/*
+ * Backward of the prefill forward ([p1 RQ2] and [p2 Eq.10]: the model's loss
+ * reaches the landmark summaries and the calibrated query through the fused
+ * weights; [p2 Eq.8] carries it on to the landmark queries and the keys).
+ * The selection is held fixed (it is piecewise constant in the inputs): the
+ * gradient is that of the forward with sel_idx forced.  Straight-through for
+ * the storage rounding of k' (ksum holds the values the forward used).
+ *
+ * For each row (b, h, i) with upstream gradients g = dout, gl = dlse:
+ *   w_c = exp(s_hat_c - lse), w_win = exp(log Z_win - lse)
+ *   D = g . out,  D_c = g . o_c
+ *   d s_hat_c = w_c (D_c - D + gl)
+ *   chunk token j of c:  ds_ij = w_c p_cj (g . v_j - D_c),  dv_j += w_c p_cj g
+ *   window token j:      ds_ij = a_ij (g . v_j - D + gl),    dv_j += a_ij g,
+ *                        a_ij = exp(s_ij - lse)
+ *   dq_i += scale sum_j ds_ij k_j,  dk_j += scale ds_ij q_i
+ *   dq_hat_i += scale sum_c d s_hat_c k'_c,  dk'_c += scale d s_hat_c q_hat_i,
+ *   db'_c += d s_hat_c
+ * and for every summarised chunk (b, h, c), with p = softmax(s), s_j = scale q'_c . k_j:
+ *   e_j = dk'_c . k_j - db'_c s_j,   ds_j = p_j (e_j - sum_l p_l e_l)
+ *   dq'_c = scale sum_j ds_j k_j,    dk_j += p_j dk'_c + scale ds_j q'_c
+ *
+ * Arrays as in orc_summarize / orc_rows, all rows of all positions (T = q_T = kv_T):
+ * sel_idx [B,Hkv,T,topk] (ascending, -1 pads), dout [B,Hq,T,d], dlse [B,Hq,T] or NULL
+ * (doubles).  Outputs (doubles, overwritten): dq, dqh [B,Hq,T,d]; dk, dv [B,Hkv,T,d]
+ * (dk includes the summaries' part); dks [B,Hq,NC,d]; dbs [B,Hq,NC]; dql [B,Hq,NC,d].
+ */
+int orc_prefill_backward(int B, int Hq, int Hkv, int d, int S, int W, int topk, double scale,
+                         int64_t T, const void* q, const void* qh, const void* ql, int q_dt,
+                         const void* k, const void* v, int kv_dt,
+                         const double* ksum, const double* bsum, int64_t NC,
+                         const int32_t* sel_idx, const double* dout, const double* dlse,
+                         double* dq, double* dqh, double* dk, double* dv, double* dks,
+                         double* dbs, double* dql) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || topk < 0 || NC != T / S) return -1;
+    const int G = Hq / Hkv;
+    memset(dq, 0, sizeof(double) * (size_t)(B * Hq * T * d));
+    memset(dqh, 0, sizeof(double) * (size_t)(B * Hq * T * d));
+    memset(dk, 0, sizeof(double) * (size_t)(B * Hkv * T * d));
+    memset(dv, 0, sizeof(double) * (size_t)(B * Hkv * T * d));
+    memset(dks, 0, sizeof(double) * (size_t)(B * Hq * NC * d));
+    memset(dbs, 0, sizeof(double) * (size_t)(B * Hq * NC));
+    memset(dql, 0, sizeof(double) * (size_t)(B * Hq * NC * d));
+    int err = 0;
+    /* one (b, g) per iteration: every accumulation stays inside it */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < (int64_t)B * Hkv; ++bg) {
+        const int b = (int)(bg / Hkv), g = (int)(bg % Hkv);
+        const int64_t kvb = ((int64_t)b * Hkv + g) * T * d;
+        const int64_t smax = (int64_t)W + S > S ? (int64_t)W + 2 * S : 2 * S;
+        double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+        double* gv = (double*)malloc(sizeof(double) * (size_t)d);
+        double* s = (double*)malloc(sizeof(double) * (size_t)(smax > T ? smax : T + 1));
+        double* oc = (double*)malloc(sizeof(double) * (size_t)d * (topk > 0 ? topk : 1));
+        double* ow = (double*)malloc(sizeof(double) * (size_t)d);
+        double* lz = (double*)malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1));
+        double* sh = (double*)malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1));
+        for (int hh = 0; hh < G; ++hh) {
+            const int h = g * G + hh;
+            for (int64_t i = 0; i < T; ++i) {
+                const int64_t lw = orc_window_left(i, S, W);
+                const int64_t nc = lw / S;
+                const int64_t nsel = nc < topk ? nc : topk;
+                const int64_t qo = (((int64_t)b * Hq + h) * T + i) * d;
+                const int32_t* sel = sel_idx + (((int64_t)b * Hkv + g) * T + i) * topk;
+                for (int e = 0; e < d; ++e) {
+                    qv[e] = ld(q, q_dt, qo + e);
+                    gv[e] = dout[qo + e];
+                }
+                const double gl = dlse ? dlse[((int64_t)b * Hq + h) * T + i] : 0.0;
+                /* forward pieces */
+                for (int64_t t = 0; t < nsel; ++t) {
+                    const int64_t c = sel[t];
+                    if (c < 0 || c >= nc) {
+#pragma omp atomic write
+                        err = -4;
+                        continue;
+                    }
+                    const double* kk = ksum + (((int64_t)b * Hq + h) * NC + c) * d;
+                    double acc = 0.0;
+                    for (int e = 0; e < d; ++e) acc += ld(qh, q_dt, qo + e) * kk[e];
+                    sh[t] = scale * acc + bsum[((int64_t)b * Hq + h) * NC + c];
+                    lz[t] = group_attend(qv, d, scale, k, v, kv_dt, kvb, c * S, c * S + S, s, oc + t * d);
+                }
+                const double lzw = group_attend(qv, d, scale, k, v, kv_dt, kvb, lw, i + 1, s, ow);
+                double lhat = lzw;
+                {
+                    double m = lzw;
+                    for (int64_t t = 0; t < nsel; ++t) if (sh[t] > m) m = sh[t];
+                    double z = exp(lzw - m);
+                    for (int64_t t = 0; t < nsel; ++t) z += exp(sh[t] - m);
+                    lhat = m + log(z);
+                }
+                const double ww = exp(lzw - lhat);
+                double Dd = 0.0, Dw = 0.0;
+                for (int e = 0; e < d; ++e) Dw += gv[e] * ow[e];
+                Dd = ww * Dw;
+                for (int64_t t = 0; t < nsel; ++t) {
+                    double Dc = 0.0;
+                    for (int e = 0; e < d; ++e) Dc += gv[e] * oc[t * d + e];
+                    Dd += exp(sh[t] - lhat) * Dc;
+                }
+                /* selected chunks */
+                for (int64_t t = 0; t < nsel; ++t) {
+                    const int64_t c = sel[t];
+                    if (c < 0 || c >= nc) continue;
+                    const double wc = exp(sh[t] - lhat);
+                    double Dc = 0.0;
+                    for (int e = 0; e < d; ++e) Dc += gv[e] * oc[t * d + e];
+                    const double dsh = wc * (Dc - Dd + gl);
+                    const double* kk = ksum + (((int64_t)b * Hq + h) * NC + c) * d;
+                    double* dkk = dks + (((int64_t)b * Hq + h) * NC + c) * d;
+                    for (int e = 0; e < d; ++e) {
+                        dqh[qo + e] += scale * dsh * kk[e];
+                        dkk[e] += scale * dsh * ld(qh, q_dt, qo + e);
+                    }
+                    dbs[((int64_t)b * Hq + h) * NC + c] += dsh;
+                    for (int64_t j = c * S; j < c * S + S; ++j) {
+                        double sj = 0.0, gvj = 0.0;
+                        for (int e = 0; e < d; ++e) {
+                            sj += qv[e] * ld(k, kv_dt, kvb + j * d + e);
+                            gvj += gv[e] * ld(v, kv_dt, kvb + j * d + e);
+                        }
+                        const double pj = exp(scale * sj - lz[t]);
+                        const double dsj = wc * pj * (gvj - Dc);
+                        for (int e = 0; e < d; ++e) {
+                            dq[qo + e] += scale * dsj * ld(k, kv_dt, kvb + j * d + e);
+                            dk[kvb + j * d + e] += scale * dsj * qv[e];
+                            dv[kvb + j * d + e] += wc * pj * gv[e];
+                        }
+                    }
+                }
+                /* window tokens */
+                for (int64_t j = lw; j <= i; ++j) {
+                    double sj = 0.0, gvj = 0.0;
+                    for (int e = 0; e < d; ++e) {
+                        sj += qv[e] * ld(k, kv_dt, kvb + j * d + e);
+                        gvj += gv[e] * ld(v, kv_dt, kvb + j * d + e);
+                    }
+                    const double aj = exp(scale * sj - lhat);
+                    const double dsj = aj * (gvj - Dd + gl);
+                    for (int e = 0; e < d; ++e) {
+                        dq[qo + e] += scale * dsj * ld(k, kv_dt, kvb + j * d + e);
+                        dk[kvb + j * d + e] += scale * dsj * qv[e];
+                        dv[kvb + j * d + e] += aj * gv[e];
+                    }
+                }
+            }
+            /* summaries of this head: Eq. 8 backward */
+            for (int64_t c = 0; c < NC; ++c) {
+                const int64_t qlo = (((int64_t)b * Hq + h) * NC + c) * d;
+                const double* dkc = dks + qlo;
+                const double dbc = dbs[((int64_t)b * Hq + h) * NC + c];
+                double* pp = s;   /* p_j, then reuse */
+                double m = -INFINITY;
+                double* sj = (double*)malloc(sizeof(double) * (size_t)S);
+                double* ej = (double*)malloc(sizeof(double) * (size_t)S);
+                for (int j = 0; j < S; ++j) {
+                    double acc = 0.0;
+                    for (int e = 0; e < d; ++e) acc += ld(ql, q_dt, qlo + e) * ld(k, kv_dt, kvb + (c * S + j) * d + e);
+                    sj[j] = scale * acc;
+                    if (sj[j] > m) m = sj[j];
+                }
+                double z = 0.0;
+                for (int j = 0; j < S; ++j) z += exp(sj[j] - m);
+                double pe = 0.0;
+                for (int j = 0; j < S; ++j) {
+                    pp[j] = exp(sj[j] - m) / z;
+                    double acc = 0.0;
+                    for (int e = 0; e < d; ++e) acc += dkc[e] * ld(k, kv_dt, kvb + (c * S + j) * d + e);
+                    ej[j] = acc - dbc * sj[j];
+                    pe += pp[j] * ej[j];
+                }
+                for (int j = 0; j < S; ++j) {
+                    const double dsj = pp[j] * (ej[j] - pe);
+                    for (int e = 0; e < d; ++e) {
+                        dql[qlo + e] += scale * dsj * ld(k, kv_dt, kvb + (c * S + j) * d + e);
+                        dk[kvb + (c * S + j) * d + e] += pp[j] * dkc[e] + scale * dsj * ld(ql, q_dt, qlo + e);
+                    }
+                }
+                free(sj);
+                free(ej);
+            }
+        }
+        free(qv); free(gv); free(s); free(oc); free(ow); free(lz); free(sh);
+    }
+    return err;
+}

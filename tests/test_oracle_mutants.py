@@ -9,6 +9,7 @@ import subprocess
 import pytest
 
 import oracle
+import test_oracle_backward as bwd
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "hils_oracle.c")
@@ -40,6 +41,15 @@ MUTANTS = [
     ("forced selection ignored", "sel[s] = forced_idx[t * topk + s];", "sel[s] = 0;"),
     ("forced selection shifted", "sel[s] = forced_idx[t * topk + s];",
      "sel[s] = forced_idx[t * topk + s] > 0 ? forced_idx[t * topk + s] - 1 : 0;"),
+    ("backward: window gradient drops dlse", "const double dsj = aj * (gvj - Dd + gl);",
+     "const double dsj = aj * (gvj - Dd);"),
+    ("backward: chunk logits centred on D", "const double dsj = wc * pj * (gvj - Dc);",
+     "const double dsj = wc * pj * (gvj - Dd);"),
+    ("backward: s_hat gradient drops dlse", "const double dsh = wc * (Dc - Dd + gl);",
+     "const double dsh = wc * (Dc - Dd);"),
+    ("backward: entropy term sign", "ej[j] = acc - dbc * sj[j];", "ej[j] = acc + dbc * sj[j];"),
+    ("backward: k' path to the keys missing", "dk[kvb + (c * S + j) * d + e] += pp[j] * dkc[e] + scale * dsj",
+     "dk[kvb + (c * S + j) * d + e] += 0.0 * dkc[e] + scale * dsj"),
 ]
 
 PIN_TESTS = [
@@ -60,6 +70,9 @@ PIN_TESTS = [
     lambda g: pins.test_p11_gqa_identical_heads_equals_mha(),
     lambda g: pins.test_golden_forced_selection(g),
     lambda g: pins.test_forced_own_selection_is_identical(4, 2),
+    lambda g: bwd.test_backward_matches_finite_differences(2),
+    lambda g: bwd.test_backward_chunk_size_one_is_dense_attention_backward(),
+    lambda g: bwd.test_backward_values_of_ones(),
 ]
 
 
