@@ -1,6 +1,6 @@
 """HiLS-Attention forward path on MI355X: Python binding of libhils.so.
 
-The four calls keep the names of the C ABI (include/hils.h) and only marshal
+The calls keep the names of the C ABI (include/hils.h) and only marshal
 arguments: torch tensors supply device memory and the current HIP stream, every
 step of the computation runs in the library's kernels.  There is no fallback:
 if the library is missing, loading raises.
@@ -10,6 +10,10 @@ if the library is missing, loading raises.
     hils_attend_fuse(q, k, v, sel_idx, sel_score, out, lse, shape, workspace=None)
     hils_decode_step(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache,
                      k_sum, b_sum, out, lse, sel_idx, shape, workspace=None)
+    hils_attend_fuse_backward(q, k, v, q_hat, k_sum, sel_idx, sel_score, out, lse, dout,
+                              dlse, dq, dk, dv, dq_hat, dk_sum, db_sum, shape, workspace=None)
+    hils_summarize_backward(k, q_land, dk_sum, db_sum, dk, dq_land, shape, chunk_begin=0,
+                            n_chunks=None)
     hils_workspace_bytes(shape, op)
     hils_timing_enable(kernels), hils_timing_get(kernel)   (diagnostics)
 
@@ -26,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhils.so")
 
 HILS_F32, HILS_BF16 = 0, 1
-OP_SUMMARIZE, OP_SELECT, OP_ATTEND_FUSE, OP_DECODE = 0, 1, 2, 3
+OP_SUMMARIZE, OP_SELECT, OP_ATTEND_FUSE, OP_DECODE, OP_ATTEND_BACKWARD = 0, 1, 2, 3, 4
 
 STATUS = {
     0: "HILS_OK", -1: "HILS_E_NULL", -2: "HILS_E_SHAPE", -3: "HILS_E_DTYPE", -4: "HILS_E_ALIGN",
@@ -35,7 +39,7 @@ STATUS = {
 }
 
 EXPORTS = ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
-           "hils_decode_step_noalloc",
+           "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
            "hils_workspace_bytes", "hils_status_string", "hils_abi_version",
            "hils_timing_enable", "hils_timing_get")
 
@@ -77,6 +81,8 @@ def lib():
         L.hils_attend_fuse.argtypes = [SP, P, P, P, P, P, P, P, P, SZ, P]
         L.hils_decode_step.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.hils_decode_step_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        L.hils_attend_fuse_backward.argtypes = [SP] + [P] * 18 + [SZ, P]
+        L.hils_summarize_backward.argtypes = [SP, P, P, P, P, I64, I64, P, P, P]
         L.hils_workspace_bytes.argtypes = [SP, ctypes.c_int]
         L.hils_workspace_bytes.restype = SZ
         L.hils_status_string.argtypes = [ctypes.c_int]
@@ -88,7 +94,7 @@ def lib():
                                       ctypes.POINTER(ctypes.c_int64)]
         L.hils_timing_get.restype = ctypes.c_int
         for f in ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
-                  "hils_decode_step_noalloc"):
+                  "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,6 +173,30 @@ def hils_decode_step(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, 
         _p(workspace_t), workspace_t.numel(), _stream()))
 
 
+def hils_attend_fuse_backward(q, k, v, q_hat, k_sum, sel_idx, sel_score, out, lse, dout, dlse,
+                              dq, dk, dv, dq_hat, dk_sum, db_sum, shape: Shape, workspace_t=None):
+    """Gradients of hils_attend_fuse (and of the selection scores), selection held fixed."""
+    _dev(q, k, v, q_hat, k_sum, sel_idx, sel_score, out, lse, dout, dlse, dq, dk, dv, dq_hat,
+         dk_sum, db_sum)
+    if workspace_t is None:
+        workspace_t = workspace(shape, OP_ATTEND_BACKWARD, q.device)
+    _check("hils_attend_fuse_backward", lib().hils_attend_fuse_backward(
+        ctypes.byref(shape), _p(q), _p(k), _p(v), _p(q_hat), _p(k_sum), _p(sel_idx), _p(sel_score),
+        _p(out), _p(lse), _p(dout), _p(dlse), _p(dq), _p(dk), _p(dv), _p(dq_hat), _p(dk_sum),
+        _p(db_sum), _p(workspace_t), workspace_t.numel(), _stream()))
+
+
+def hils_summarize_backward(k, q_land, dk_sum, db_sum, dk, dq_land, shape: Shape,
+                            chunk_begin: int = 0, n_chunks: int | None = None):
+    """Gradients of hils_summarize: adds into dk, writes dq_land."""
+    _dev(k, q_land, dk_sum, db_sum, dk, dq_land)
+    if n_chunks is None:
+        n_chunks = shape.seq_len // shape.chunk - chunk_begin
+    _check("hils_summarize_backward", lib().hils_summarize_backward(
+        ctypes.byref(shape), _p(k), _p(q_land), _p(dk_sum), _p(db_sum), chunk_begin, n_chunks,
+        _p(dk), _p(dq_land), _stream()))
+
+
 def hils_decode_step_noalloc(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, k_sum,
                              b_sum, out, lse, sel_idx, shape: Shape):
     """hils_decode_step on the library's built-in scratch (no workspace, no allocation)."""
@@ -180,7 +210,8 @@ def hils_decode_step_noalloc(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v
 KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",
            "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend",
            "dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize",
-           "v_transpose", "rank_keys", "topk_scores")
+           "v_transpose", "rank_keys", "topk_scores",
+           "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "bwd_ksum", "summarize_bwd")
 
 
 def hils_timing_enable(kernels):

@@ -94,6 +94,12 @@ size_t hils_workspace_bytes(const hils_shape* s, hils_op op) {
     case HILS_OP_DECODE:
       return hils::decode_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
                                     s->window, s->head_dim, s->top_k);
+    case HILS_OP_ATTEND_BACKWARD: {
+      size_t fixed, per;
+      hils::attend_backward_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
+                                      s->head_dim, s->top_k, &fixed, &per);
+      return fixed + per * (size_t)s->heads_kv;
+    }
   }
   return 0;
 }
@@ -207,6 +213,62 @@ hils_status hils_decode_step(const hils_shape* s, const int64_t* pos, const void
   a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
   a.Lcap = s->seq_len; a.scale = eff_scale(s); a.ws = ws; a.ws_bytes = ws_bytes;
   return from_hip(hils::launch_decode(a, stream));
+}
+
+hils_status hils_attend_fuse_backward(const hils_shape* s, const void* q, const void* k,
+                                      const void* v, const void* q_hat, const void* k_sum,
+                                      const int32_t* sel_idx, const float* sel_score,
+                                      const void* out, const float* lse, const void* dout,
+                                      const float* dlse, float* dq, float* dk, float* dv,
+                                      float* dq_hat, float* dk_sum, float* db_sum, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  const hils_status st = check_shape(s, kPrefill);
+  if (st != HILS_OK) return st;
+  const bool has_chunks = s->seq_len / s->chunk > 0;
+  if (!q || !k || !v || !q_hat || !out || !lse || !dout || !dq || !dk || !dv || !dq_hat)
+    return HILS_E_NULL;
+  if (s->top_k > 0 && (!sel_idx || !sel_score)) return HILS_E_NULL;
+  if (has_chunks && (!k_sum || !dk_sum || !db_sum)) return HILS_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_hat) || !aligned16(k_sum) ||
+      !aligned16(sel_idx) || !aligned16(sel_score) || !aligned16(out) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dlse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(dq_hat) || !aligned16(dk_sum) || !aligned16(db_sum))
+    return HILS_E_ALIGN;
+  if (s->seq_len > (int64_t(1) << 25)) return HILS_E_UNSUPPORTED;
+  size_t fixed, per;
+  hils::attend_backward_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk, s->head_dim,
+                                  s->top_k, &fixed, &per);
+  if (!ws || ws_bytes < fixed + per) return HILS_E_WORKSPACE;
+  hils::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.qh = q_hat; a.ksum = k_sum; a.idx = sel_idx; a.ssel = sel_score;
+  a.out = out; a.lse = lse; a.dout = dout; a.dlse = dlse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dqh = dq_hat; a.dks = dk_sum; a.dbs = db_sum;
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
+  a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
+  a.T = s->seq_len; a.scale = eff_scale(s); a.ws = ws; a.ws_bytes = ws_bytes;
+  return from_hip(hils::launch_attend_backward(a, stream));
+}
+
+hils_status hils_summarize_backward(const hils_shape* s, const void* k, const void* q_land,
+                                    const float* dk_sum, const float* db_sum, int64_t chunk_begin,
+                                    int64_t n_chunks, float* dk, float* dq_land, hipStream_t stream) {
+  const hils_status st = check_shape(s, kSummarize);
+  if (st != HILS_OK) return st;
+  if (!k || !q_land || !dk_sum || !db_sum || !dk || !dq_land) return HILS_E_NULL;
+  if (!aligned16(k) || !aligned16(q_land) || !aligned16(dk_sum) || !aligned16(db_sum) ||
+      !aligned16(dk) || !aligned16(dq_land))
+    return HILS_E_ALIGN;
+  const int64_t NC = s->seq_len / s->chunk;
+  if (chunk_begin < 0 || n_chunks < 0 || chunk_begin + n_chunks > NC) return HILS_E_SHAPE;
+  if (n_chunks > 0x7fffffff) return HILS_E_UNSUPPORTED;
+  if (n_chunks == 0) return HILS_OK;
+  hils::SumBwdArgs a{};
+  a.k = k; a.ql = q_land; a.dks = dk_sum; a.dbs = db_sum; a.dk = dk; a.dql = dq_land;
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim;
+  a.bf16 = s->io_dtype == HILS_BF16;
+  a.kT = s->seq_len; a.NCs = NC; a.c0 = chunk_begin; a.n_chunks = n_chunks;
+  a.scale = eff_scale(s);
+  return from_hip(hils::launch_summarize_backward(a, stream));
 }
 
 }  // extern "C"

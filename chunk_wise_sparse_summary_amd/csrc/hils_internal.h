@@ -76,6 +76,68 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st);
 void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, bool bf16,
                       size_t* fixed, size_t* per_kv_head);
 
+// Per-(b, group, chunk) lists of the (query, slot) entries that selected the
+// chunk (entry word i * 64 + slot), in ascending query order: bucket (b, g, c)
+// holds entries[bbase[.] .. bbase[.] + bcount[.]).
+struct EntryLists {
+  const int32_t* bcount;
+  const int64_t* bbase;
+  const uint32_t* entries;
+  int64_t NCs;
+};
+size_t entry_lists_bytes(int B, int Hkv, int64_t T, int S, int topk);
+hipError_t launch_entry_lists(const int32_t* idx, int B, int Hq, int Hkv, int64_t T, int S, int topk,
+                              void* ws, EntryLists* el, hipStream_t st);
+
+// Backward of the prefill attention and fusion (gradients in fp32).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* qh;
+  const void* ksum;
+  const int32_t* idx;
+  const float* ssel;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  const float* dlse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dqh;
+  float* dks;
+  float* dbs;
+  int B, Hq, Hkv, D, S, W, topk;
+  bool bf16;
+  int64_t T;
+  float scale;
+  void* ws;
+  size_t ws_bytes;
+};
+hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t st);
+// Workspace of the attention backward: `fixed` bytes (entry lists, row
+// statistics, d s_hat) plus `per_group` bytes for each KV head whose dq parts are
+// held at once (at least one).
+void attend_backward_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
+                               size_t* fixed, size_t* per_group);
+
+// Backward of the landmark summaries: dk (accumulated) and dq_land.
+struct SumBwdArgs {
+  const void* k;
+  const void* ql;
+  const float* dks;
+  const float* dbs;
+  float* dk;
+  float* dql;
+  int B, Hq, Hkv, D;
+  bool bf16;
+  int64_t kT, NCs;
+  int64_t c0, n_chunks;
+  float scale;
+};
+hipError_t launch_summarize_backward(const SumBwdArgs& a, hipStream_t st);
+
 struct DecArgs {
   const int64_t* pos;  // host
   const void* q;
@@ -106,6 +168,7 @@ enum KernelId {
   K_SUMMARIZE, K_SCORE_LSE, K_IDX_COUNT, K_IDX_SCAN_TILES, K_IDX_SCAN_BUCKETS,
   K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_DEC_SCORE, K_DEC_SELECT,
   K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_RANK_KEYS, K_TOPK_SCORES,
+  K_BWD_ROWSTAT, K_BWD_KV, K_BWD_DQ, K_BWD_QHAT, K_BWD_KSUM, K_SUM_BWD,
   K_COUNT
 };
 class KTimer {

@@ -13,6 +13,11 @@
  *   hils_attend_fuse  per-group attention and the fusion
  *   hils_decode_step  all of the above for one new token per sequence
  *
+ * and the gradients of the prefill path in two more:
+ *
+ *   hils_attend_fuse_backward  attention and fusion, given the selection
+ *   hils_summarize_backward    the landmark summaries
+ *
  * Notation: B batch, Hq query heads, Hkv key/value heads, G = Hq/Hkv heads per
  * group, d head dimension, S chunk size, W window, k top-k, T tokens,
  * NC = floor(T/S) complete chunks, scale = 1/sqrt(d) unless given.  Token i
@@ -52,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 1
+#define HILS_ABI_VERSION 2
 
 typedef enum {
     HILS_OK = 0,
@@ -75,7 +80,8 @@ typedef enum {
     HILS_OP_SUMMARIZE = 0,
     HILS_OP_SELECT = 1,
     HILS_OP_ATTEND_FUSE = 2,
-    HILS_OP_DECODE = 3
+    HILS_OP_DECODE = 3,
+    HILS_OP_ATTEND_BACKWARD = 4
 } hils_op;
 
 typedef struct {
@@ -225,6 +231,62 @@ hils_status hils_decode_step_noalloc(const hils_shape* shape, const int64_t* pos
                                      void* k_cache, void* v_cache, void* k_sum, float* b_sum,
                                      void* out, float* lse, int32_t* sel_idx, hipStream_t stream);
 
+/*
+ * Backward of hils_attend_fuse and of the retrieval scores that weight it
+ * (paper-body page, RQ2: the chunk scores enter the fused token weights, so the
+ * loss gradient reaches the summaries and the calibrated query; summary page,
+ * Methodology 2, Eq. 10).  The selection is held fixed: top-k is piecewise
+ * constant in the inputs and has no gradient.  With upstream gradients
+ * g = dout and gl = dlse of a row (b, h, i), its forward output out and lse = L:
+ *     D = g . out;  window token j: a_j = exp(s_ij - L),
+ *         ds_ij = a_j (g . v_j - D + gl),  dv_j += a_j g
+ *     selected chunk c, w_c = exp(s_hat_c - L), p = the chunk's softmax of s_ij,
+ *         D_c = sum_j p_j g . v_j,  ds_ij = w_c p_j (g . v_j - D_c),
+ *         dv_j += w_c p_j g,  d s_hat_c = w_c (D_c - D + gl)
+ *     dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_(h,i) ds_ij q_i
+ *     dq_hat_i = scale sum_c d s_hat_c k'_c,  dk'_c = scale sum_i d s_hat_c q_hat_i,
+ *     db'_c = sum_i d s_hat_c
+ * (sums over the G heads of a group for dk and dv).
+ *
+ * q, k, v, q_hat, k_sum, sel_idx, sel_score: the inputs of the forward calls
+ *   (k_sum [B,Hq,T/S,d] summary_dtype; sel_idx and sel_score as from hils_select)
+ * out [B,Hq,T,d] io_dtype and lse [B,Hq,T] fp32: as written by hils_attend_fuse
+ * dout [B,Hq,T,d] io_dtype; dlse [B,Hq,T] fp32, or NULL for a zero gradient
+ * dq, dq_hat [B,Hq,T,d], dk, dv [B,Hkv,T,d], dk_sum [B,Hq,T/S,d], db_sum [B,Hq,T/S]:
+ *   fp32 outputs, overwritten (zero where nothing reaches them)
+ * The workspace (hils_workspace_bytes(shape, HILS_OP_ATTEND_BACKWARD)) holds
+ * per-(query, head, selected chunk) dq parts; one smaller than that but with
+ * room for one KV head's parts runs several passes.  Same limits as
+ * hils_attend_fuse.
+ */
+hils_status hils_attend_fuse_backward(const hils_shape* shape, const void* q, const void* k,
+                                      const void* v, const void* q_hat, const void* k_sum,
+                                      const int32_t* sel_idx, const float* sel_score,
+                                      const void* out, const float* lse, const void* dout,
+                                      const float* dlse, float* dq, float* dk, float* dv,
+                                      float* dq_hat, float* dk_sum, float* db_sum,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward of hils_summarize (summary page, Methodology 1, Eq. 8: the gradients
+ * of k'_c and b'_c flow through the chunk's softmax to the landmark query and
+ * the chunk's keys).  For each b, h, chunk c in range, with s_j, p as in
+ * hils_summarize:
+ *     e_j = dk'_c . k_j - db'_c s_j,   ds_j = p_j (e_j - sum_l p_l e_l)
+ *     dq_land_c = scale sum_j ds_j k_j
+ *     dk_j += p_j dk'_c + scale ds_j q_land_c      (summed over the group's heads)
+ * k [B,Hkv,seq_len,d] and q_land [B,Hq,seq_len/S,d] io_dtype: the forward inputs
+ * dk_sum [B,Hq,seq_len/S,d] and db_sum [B,Hq,seq_len/S] fp32: the gradients of k_sum, b_sum
+ * dk [B,Hkv,seq_len,d] fp32: added to (rows of chunks in range only)
+ * dq_land [B,Hq,seq_len/S,d] fp32: written for the chunks in range
+ * Requires 0 <= chunk_begin, chunk_begin + n_chunks <= seq_len/S; n_chunks == 0
+ * is a no-op.  Needs no workspace.  The summary's forward rounding of k' to
+ * summary_dtype is passed through unchanged.
+ */
+hils_status hils_summarize_backward(const hils_shape* shape, const void* k, const void* q_land,
+                                    const float* dk_sum, const float* db_sum, int64_t chunk_begin,
+                                    int64_t n_chunks, float* dk, float* dq_land, hipStream_t stream);
+
 /* Workspace bytes `op` needs for `shape` (0 for HILS_OP_SUMMARIZE); 0 as well
  * for an invalid shape. */
 size_t hils_workspace_bytes(const hils_shape* shape, hils_op op);
@@ -248,7 +310,9 @@ int hils_abi_version(void);
  *   dec_score, dec_select,
  *   dec_attend, dec_fuse, dec_summarize (the summaries of chunks
  *   completed by a decode step), v_transpose, rank_keys,
- *   topk_scores.  HILS_E_UNSUPPORTED for an unknown name
+ *   topk_scores, and for the backward calls bwd_rowstat, bwd_kv, bwd_dq,
+ *   bwd_qhat, bwd_ksum and summarize_bwd (the entry lists of the
+ *   backward count under the idx_* names).  HILS_E_UNSUPPORTED for an unknown name
  *   (timing is then left off).
  * hils_timing_get(kernel, total_ms, launches): waits for the recorded events
  *   of that kernel and returns the summed duration and the number of timed

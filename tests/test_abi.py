@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     L = hils.lib()
-    assert L.hils_abi_version() == 1
+    assert L.hils_abi_version() == 2
     for code in hils.STATUS:
         assert L.hils_status_string(code)
     assert L.hils_status_string(-99) == b"unknown status"
@@ -125,3 +125,35 @@ def test_timing_names_and_errors():
         hils.hils_timing_enable([k])
     hils.hils_timing_enable("*")
     hils.hils_timing_enable(None)
+
+
+def test_backward_validation():
+    L = hils.lib()
+    P = ctypes.c_void_p
+    s = _shape(T=8192, k=16, W=512)
+    full = hils.hils_workspace_bytes(s, hils.OP_ATTEND_BACKWARD)
+    # dq parts of every (query, head, selected chunk) in fp32 dominate
+    assert full >= 32 * 8192 * 16 * 128 * 4
+
+    def call(ptrs=None, nws=full, shape=s, dlse=16):
+        a = [P(16)] * 17 if ptrs is None else ptrs
+        a = list(a)
+        a[10] = P(dlse)
+        return L.hils_attend_fuse_backward(ctypes.byref(shape), *a, P(16), nws, None)
+
+    bad = [P(16)] * 17
+    bad[0] = P(0)
+    assert call(bad) == -1                       # q NULL
+    bad = [P(16)] * 17
+    bad[11] = P(8)
+    assert call(bad) == -4                       # dq misaligned
+    assert call(nws=1024) == -5                  # workspace below one KV head's share
+    assert call(shape=_shape(T=8192, k=16, W=512, d=96)) == -8
+    assert hils.hils_workspace_bytes(_shape(d=96), hils.OP_ATTEND_BACKWARD) == 0
+    # summarize backward: range checks and the no-op
+    assert L.hils_summarize_backward(ctypes.byref(s), P(16), P(16), P(16), P(16), 127, 2, P(16), P(16),
+                                     None) == -2
+    assert L.hils_summarize_backward(ctypes.byref(s), P(16), P(16), P(16), P(16), 0, 0, P(16), P(16),
+                                     None) == 0
+    assert L.hils_summarize_backward(ctypes.byref(s), P(0), P(16), P(16), P(16), 0, 1, P(16), P(16),
+                                     None) == -1
