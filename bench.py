@@ -375,6 +375,72 @@ def time_decode(hils, wl, cache, shape, ks, bs, steps, nrep, warm):
     return times
 
 
+BWD_KERNELS = ["idx_count", "idx_scan_tiles", "idx_scan_buckets", "idx_fill", "bwd_rowstat", "bwd_kv",
+               "bwd_dq", "bwd_qhat", "bwd_ksum", "summarize_bwd"]
+
+
+def time_backward(hils, x, fwd, shape, reps=3):
+    """hils_attend_fuse_backward + hils_summarize_backward on the forward's own
+    outputs (random upstream gradients), median of `reps` timed calls, then one
+    call with per-kernel events."""
+    import torch
+    q = x["q"]
+    dev = q.device
+    B, Hq, T, d = q.shape
+    Hkv = x["k"].shape[1]
+    NC = T // shape.chunk
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    dout = (torch.randn(q.shape, generator=gen, device=dev) * 0.5).to(q.dtype)
+    dlse = torch.randn((B, Hq, T), generator=gen, device=dev) * 0.5
+    f = dict(dtype=torch.float32, device=dev)
+    g = {"dq": torch.empty((B, Hq, T, d), **f), "dq_hat": torch.empty((B, Hq, T, d), **f),
+         "dk": torch.empty((B, Hkv, T, d), **f), "dv": torch.empty((B, Hkv, T, d), **f),
+         "dk_sum": torch.empty((B, Hq, NC, d), **f), "db_sum": torch.empty((B, Hq, NC), **f),
+         "dq_land": torch.empty((B, Hq, NC, d), **f)}
+    ws = hils.workspace(shape, hils.OP_ATTEND_BACKWARD, dev)
+
+    def one():
+        hils.hils_attend_fuse_backward(x["q"], x["k"], x["v"], x["q_hat"], fwd["k_sum"], fwd["idx"],
+                                       fwd["ssel"], fwd["out"], fwd["lse"], dout, dlse, g["dq"], g["dk"],
+                                       g["dv"], g["dq_hat"], g["dk_sum"], g["db_sum"], shape, ws)
+        hils.hils_summarize_backward(x["k"], x["q_land"], g["dk_sum"], g["db_sum"], g["dk"], g["dq_land"],
+                                     shape)
+    one()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a.record()
+        one()
+        b_.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b_))
+    hils.hils_timing_enable(BWD_KERNELS)
+    one()
+    torch.cuda.synchronize()
+    kern = {}
+    for kn in BWD_KERNELS:
+        tms, nl = hils.hils_timing_get(kn)
+        if nl:
+            kern[kn] = {"ms": tms, "launches": nl}
+    hils.hils_timing_enable(None)
+    ms = float(np.median(ts))
+    af = attended_flops(B, Hq, T, d, shape.chunk, shape.window, shape.top_k)
+    # five products per attended (row, token) pair instead of the forward's two:
+    # S and U = dout V^T recomputed, then dV, dK and dq
+    bf = 2.5 * af
+    del ws, g
+    return {"ms_median": ms, "attended_flops_bwd": bf,
+            "mfma_frac": bf / (ms * 1e-3) / PEAK_BF16,
+            "tokens_per_s": B * T / (ms * 1e-3),
+            "kernels_ms": kern,
+            "workspace_GiB": hils.hils_workspace_bytes(shape, hils.OP_ATTEND_BACKWARD) / 2**30,
+            "note": "median of %d calls of attend_fuse_backward + summarize_backward; "
+                    "FLOPs = 2.5 x the forward's attended FLOPs" % reps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -629,6 +695,11 @@ def main():
             res["decode_kernels_us"][kn] = {"avg_us": tms / nl * 1e3, "launches_per_step": nl / nsteps}
     hils.hils_timing_enable(None)
     del ws_dec
+    if not args.no_extra:
+        log("128K backward")
+        del ws_att
+        res["backward_128k"] = time_backward(hils, x, {"k_sum": k_sum, "idx": idx, "ssel": ssel, "out": out,
+                                                       "lse": lse}, shape)
 
     if not args.no_extra:
         # ---- 8K prefill (32/8 heads, d=128, k=16, W=512, one planted needle)
@@ -664,6 +735,8 @@ def main():
                              "m5_overlap": overlap_m5(r8["idx"], w8.T, w8.S, w8.W, w8.k),
                              "note": "median of 20 calls of summarize + select + attend_fuse "
                                      "(output buffers allocated inside each call)"}
+        log("8K backward")
+        res["backward_8k"] = time_backward(hils, x8, r8, sh8, reps=10)
         del x8, p8, r8
         # ---- 4M decode (B=1, k=64, 8 needles, 256 steps with 4 chunk completions)
         log("4M decode: drawing the cache")
