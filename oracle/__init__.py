@@ -66,6 +66,9 @@ def lib():
         L.orc_prefill_backward.argtypes = [I, I, I, I, I, I, I, D, I64, P, P, P, I, P, P, I, P, P, I64,
                                            P, P, P, P, P, P, P, P, P, P]
         L.orc_prefill_backward.restype = I
+        L.orc_bsa_rows.argtypes = [I, I, I, I, I, I, I, D, I64, P, P, P, P, P, I, I64, P, I, I64,
+                                   P, P, P, P, I64, P, I64]
+        L.orc_bsa_rows.restype = I
         L.orc_window_left.argtypes = [I64, I, I]
         L.orc_window_left.restype = I64
         L.orc_num_candidates.argtypes = [I64, I, I]
@@ -198,6 +201,59 @@ def rows(rb, rg, ri, rq, q, q_hat, k, v, ksum, bsum, *, S: int, W: int, topk: in
     if want_r:
         res["r"] = r
     return res
+
+
+def bsa_rows(rb, rg, ri, rq, q, k, *, S: int, W: int, topk: int, scale: float | None = None,
+             want_r: bool = False, want_lz: bool = False):
+    """Naive BSA selection (exact chunk mass) on a list of query rows (b, g, i, iq).
+
+    Returns idx [n,k], gap [n], ncand [n], and if asked r [n, NC] (rank key per
+    candidate) and lz [n, G, NC] (log chunk mass per head and candidate)."""
+    qa, qdt = _as_np(q)
+    ka, kdt = _as_np(k)
+    B, Hq, qT, d = qa.shape
+    Hkv, kvT = ka.shape[1], ka.shape[2]
+    G = Hq // Hkv
+    NC = max(kvT // S, 1)
+    if scale is None:
+        scale = default_scale(d)
+    rb = np.ascontiguousarray(rb, np.int32)
+    rg = np.ascontiguousarray(rg, np.int32)
+    ri = np.ascontiguousarray(ri, np.int64)
+    rq = np.ascontiguousarray(rq, np.int64)
+    n = rb.shape[0]
+    kk = max(topk, 1)
+    idx = np.zeros((n, kk), np.int32)
+    gap = np.zeros(n, np.float64)
+    ncand = np.zeros(n, np.int64)
+    r = np.full((n, NC), np.nan, np.float64) if want_r else None
+    lz = np.full((n, G, NC), np.nan, np.float64) if want_lz else None
+    rc = lib().orc_bsa_rows(B, Hq, Hkv, d, S, W, topk, float(scale), n, _ptr(rb), _ptr(rg), _ptr(ri),
+                            _ptr(rq), _ptr(qa), qdt, qT, _ptr(ka), kdt, kvT, _ptr(idx), _ptr(gap),
+                            _ptr(ncand), _ptr(r) if r is not None else None, NC if r is not None else 0,
+                            _ptr(lz) if lz is not None else None, NC if lz is not None else 0)
+    if rc != 0:
+        raise RuntimeError("orc_bsa_rows failed: %d" % rc)
+    res = {"idx": idx[:, :topk], "gap": gap, "ncand": ncand}
+    if want_r:
+        res["r"] = r
+    if want_lz:
+        res["lz"] = lz
+    return res
+
+
+def selection_recall(idx_a, idx_b, ncand, topk: int) -> dict:
+    """Recall of selection A against selection B over the rows where a choice is
+    made (|C_i| > k): the fraction of B's chunks that A also holds."""
+    a = np.asarray(idx_a).reshape(-1, topk)
+    b = np.asarray(idx_b).reshape(-1, topk)
+    nc = np.asarray(ncand).reshape(-1)
+    ev = nc > topk
+    hits = 0
+    for x, y in zip(a[ev], b[ev]):
+        hits += len(set(x[x >= 0].tolist()) & set(y[y >= 0].tolist()))
+    n = int(ev.sum())
+    return {"events": n, "hits": hits, "recall": hits / (n * topk) if n else float("nan")}
 
 
 def ks_round_for(summary_dtype) -> int:

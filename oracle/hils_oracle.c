@@ -545,3 +545,96 @@ int orc_prefill_backward(int B, int Hq, int Hkv, int d, int S, int W, int topk, 
     }
     return err;
 }
+
+/*
+ * Naive Block Sparse Attention selection ([p1 BSA]: the chunk mass of a
+ * candidate chunk is the sum of the exponentiated token logits of the query
+ * against the chunk's keys; naive BSA keeps the k candidates of largest mass,
+ * which needs every token logit).  For each row (b, g, i) and head h of g:
+ *   log Z_{h,c} = LSE_{j in chunk c} scale * q_{h,i} . k_j,   c in C_i
+ * and the selection takes the group rule of the retrieval scores with log Z in
+ * place of s_hat ([p1 GQA]): r_c = log Z_c for a group of one head, else
+ * r_c = max_h (log Z_{h,c} - LSE_{c'} log Z_{h,c'}); top-k by r, ties to the
+ * lower chunk index; all of C_i when |C_i| <= k.
+ *
+ * q [B,Hq,q_T,d] (row iq is the query of position i), k [B,Hkv,kv_T,d].
+ * idx_out [nrows, topk] ascending, -1 padded; gap_out [nrows] r_(k) - r_(k+1)
+ * (+inf when |C_i| <= k); ncand_out [nrows]; r_out NULL or [nrows, r_stride];
+ * lz_out NULL or [nrows, G, lz_stride]: log Z of every candidate per head.
+ */
+int orc_bsa_rows(int B, int Hq, int Hkv, int d, int S, int W, int topk, double scale,
+                 int64_t nrows, const int32_t* rb, const int32_t* rg, const int64_t* ri,
+                 const int64_t* rq, const void* q, int q_dt, int64_t q_T,
+                 const void* k, int kv_dt, int64_t kv_T,
+                 int32_t* idx_out, double* gap_out, int64_t* ncand_out,
+                 double* r_out, int64_t r_stride, double* lz_out, int64_t lz_stride) {
+    if (Hkv <= 0 || Hq % Hkv != 0 || topk < 0) return -1;
+    const int G = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int b = rb[t], g = rg[t];
+        const int64_t i = ri[t], iq = rq[t];
+        if (b < 0 || b >= B || g < 0 || g >= Hkv || i < 0 || i >= kv_T || iq < 0 || iq >= q_T) {
+#pragma omp atomic write
+            err = -2;
+            continue;
+        }
+        const int64_t nc = orc_window_left(i, S, W) / S;
+        if ((r_out && nc > r_stride) || (lz_out && nc > lz_stride)) {
+#pragma omp atomic write
+            err = -3;
+            continue;
+        }
+        ncand_out[t] = nc;
+        const int64_t nsel = nc < topk ? nc : topk;
+        double* lz = (double*)malloc(sizeof(double) * (size_t)(G * (nc > 0 ? nc : 1)));
+        double* qx = (double*)malloc(sizeof(double) * (size_t)d);
+        double* s = (double*)malloc(sizeof(double) * (size_t)S);
+        int64_t* sel = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1));
+        const int64_t kvb = ((int64_t)b * Hkv + g) * kv_T * d;
+        /* exact chunk masses per head */
+        for (int hh = 0; hh < G; ++hh) {
+            const int h = g * G + hh;
+            const int64_t qo = (((int64_t)b * Hq + h) * q_T + iq) * d;
+            for (int e = 0; e < d; ++e) qx[e] = ld(q, q_dt, qo + e);
+            for (int64_t c = 0; c < nc; ++c) {
+                for (int j = 0; j < S; ++j) {
+                    double acc = 0.0;
+                    const int64_t off = kvb + (c * S + j) * d;
+                    for (int e = 0; e < d; ++e) acc += qx[e] * ld(k, kv_dt, off + e);
+                    s[j] = scale * acc;
+                }
+                lz[hh * nc + c] = lse(s, S);
+                if (lz_out) lz_out[(t * G + hh) * lz_stride + c] = lz[hh * nc + c];
+            }
+        }
+        double gap = INFINITY;
+        if (nc > 0) {
+            rank_entry* re = (rank_entry*)malloc(sizeof(rank_entry) * (size_t)nc);
+            double* L = (double*)malloc(sizeof(double) * (size_t)G);
+            for (int hh = 0; hh < G; ++hh) L[hh] = lse(lz + hh * nc, nc);
+            for (int64_t c = 0; c < nc; ++c) {
+                double best = -INFINITY;
+                if (G == 1) {
+                    best = lz[c];
+                } else {
+                    for (int hh = 0; hh < G; ++hh) best = fmax(best, lz[hh * nc + c] - L[hh]);
+                }
+                re[c].r = best;
+                re[c].c = c;
+                if (r_out) r_out[t * r_stride + c] = best;
+            }
+            qsort(re, (size_t)nc, sizeof(rank_entry), rank_cmp);
+            for (int64_t sidx = 0; sidx < nsel; ++sidx) sel[sidx] = re[sidx].c;
+            if (nc > topk && topk > 0) gap = re[topk - 1].r - re[topk].r;
+            free(re);
+            free(L);
+        }
+        qsort(sel, (size_t)nsel, sizeof(int64_t), cmp_i64);
+        gap_out[t] = gap;
+        for (int sidx = 0; sidx < topk; ++sidx) idx_out[t * topk + sidx] = sidx < nsel ? (int32_t)sel[sidx] : -1;
+        free(lz); free(qx); free(s); free(sel);
+    }
+    return err;
+}

@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 import test_oracle_backward as bwd
+import test_oracle_bsa as bsa
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "hils_oracle.c")
@@ -50,6 +51,14 @@ MUTANTS = [
     ("backward: entropy term sign", "ej[j] = acc - dbc * sj[j];", "ej[j] = acc + dbc * sj[j];"),
     ("backward: k' path to the keys missing", "dk[kvb + (c * S + j) * d + e] += pp[j] * dkc[e] + scale * dsj",
      "dk[kvb + (c * S + j) * d + e] += 0.0 * dkc[e] + scale * dsj"),
+    ("BSA: chunk mass misses its last token", "lz[hh * nc + c] = lse(s, S);",
+     "lz[hh * nc + c] = lse(s, S - 1);"),
+    ("BSA: mean logit instead of log-mass", "lz[hh * nc + c] = lse(s, S);",
+     "lz[hh * nc + c] = lse(s, S) - log((double)S);"),
+    ("BSA: GQA without per-head normalisation", "best = fmax(best, lz[hh * nc + c] - L[hh]);",
+     "best = fmax(best, lz[hh * nc + c]);"),
+    ("BSA: logits of the next chunk", "const int64_t off = kvb + (c * S + j) * d;",
+     "const int64_t off = kvb + ((c + 1) * S + j) * d;"),
 ]
 
 PIN_TESTS = [
@@ -73,6 +82,11 @@ PIN_TESTS = [
     lambda g: bwd.test_backward_matches_finite_differences(2),
     lambda g: bwd.test_backward_chunk_size_one_is_dense_attention_backward(),
     lambda g: bwd.test_backward_values_of_ones(),
+    lambda g: bsa.test_bsa_matches_numpy_route(1),
+    lambda g: bsa.test_bsa_matches_numpy_route(2),
+    lambda g: bsa.test_bsa_chunk_size_one_is_top_logits(),
+    lambda g: bsa.test_bsa_identical_keys_per_chunk(),
+    lambda g: bsa.test_hils_equals_bsa_at_the_landmark_query(4),
 ]
 
 
