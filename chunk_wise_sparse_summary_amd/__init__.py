@@ -14,6 +14,8 @@ if the library is missing, loading raises.
                               dlse, dq, dk, dv, dq_hat, dk_sum, db_sum, shape, workspace=None)
     hils_summarize_backward(k, q_land, dk_sum, db_sum, dk, dq_land, shape, chunk_begin=0,
                             n_chunks=None)
+    hils_bsa_select(q, k, sel_idx, shape, workspace=None)
+    hils_selection_overlap(idx_a, idx_b, count, shape)
     hils_workspace_bytes(shape, op)
     hils_timing_enable(kernels), hils_timing_get(kernel)   (diagnostics)
 
@@ -40,6 +42,7 @@ STATUS = {
 
 EXPORTS = ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
            "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
+           "hils_bsa_select", "hils_selection_overlap",
            "hils_workspace_bytes", "hils_status_string", "hils_abi_version",
            "hils_timing_enable", "hils_timing_get")
 
@@ -83,6 +86,8 @@ def lib():
         L.hils_decode_step_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         L.hils_attend_fuse_backward.argtypes = [SP] + [P] * 18 + [SZ, P]
         L.hils_summarize_backward.argtypes = [SP, P, P, P, P, I64, I64, P, P, P]
+        L.hils_bsa_select.argtypes = [SP, P, P, P, P, SZ, P]
+        L.hils_selection_overlap.argtypes = [SP, P, P, P, P]
         L.hils_workspace_bytes.argtypes = [SP, ctypes.c_int]
         L.hils_workspace_bytes.restype = SZ
         L.hils_status_string.argtypes = [ctypes.c_int]
@@ -94,7 +99,8 @@ def lib():
                                       ctypes.POINTER(ctypes.c_int64)]
         L.hils_timing_get.restype = ctypes.c_int
         for f in ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
-                  "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward"):
+                  "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
+                  "hils_bsa_select", "hils_selection_overlap"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -197,6 +203,22 @@ def hils_summarize_backward(k, q_land, dk_sum, db_sum, dk, dq_land, shape: Shape
         _p(dk), _p(dq_land), _stream()))
 
 
+def hils_bsa_select(q, k, sel_idx, shape: Shape, workspace_t=None):
+    """Naive Block Sparse Attention selection (exact chunk masses), a diagnostic."""
+    _dev(q, k, sel_idx)
+    if workspace_t is None:
+        workspace_t = workspace(shape, OP_SELECT, q.device)
+    _check("hils_bsa_select", lib().hils_bsa_select(ctypes.byref(shape), _p(q), _p(k), _p(sel_idx),
+                                                    _p(workspace_t), workspace_t.numel(), _stream()))
+
+
+def hils_selection_overlap(idx_a, idx_b, count, shape: Shape):
+    """count[b,g,i] = number of chunk ids rows (b,g,i) of two selections share."""
+    _dev(idx_a, idx_b, count)
+    _check("hils_selection_overlap", lib().hils_selection_overlap(ctypes.byref(shape), _p(idx_a),
+                                                                  _p(idx_b), _p(count), _stream()))
+
+
 def hils_decode_step_noalloc(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, k_sum,
                              b_sum, out, lse, sel_idx, shape: Shape):
     """hils_decode_step on the library's built-in scratch (no workspace, no allocation)."""
@@ -211,7 +233,8 @@ KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",
            "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend",
            "dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize",
            "v_transpose", "rank_keys", "topk_scores",
-           "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "bwd_ksum", "summarize_bwd")
+           "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "bwd_ksum", "summarize_bwd",
+           "bsa_keys", "bsa_topk")
 
 
 def hils_timing_enable(kernels):

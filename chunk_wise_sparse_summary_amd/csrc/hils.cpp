@@ -215,6 +215,46 @@ hils_status hils_decode_step(const hils_shape* s, const int64_t* pos, const void
   return from_hip(hils::launch_decode(a, stream));
 }
 
+hils_status hils_bsa_select(const hils_shape* s, const void* q, const void* k, int32_t* sel_idx, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  const hils_status st = check_shape(s, kPrefill);
+  if (st != HILS_OK) return st;
+  if (!q || !k || (s->top_k > 0 && !sel_idx)) return HILS_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(sel_idx)) return HILS_E_ALIGN;
+  if (s->top_k == 0) return HILS_OK;
+  int n_slots = 0;
+  int64_t stride = 0;
+  size_t fixed = 0, per_group = 0;
+  hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
+                         s->io_dtype == HILS_BF16, &n_slots, &stride, &fixed, &per_group);
+  if (!ws || ws_bytes < fixed + per_group) return HILS_E_WORKSPACE;
+  hils::SelArgs a{};
+  a.qh = q; a.ksum = k; a.bsum = nullptr; a.idx = sel_idx; a.ssel = nullptr;
+  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+  a.L = nullptr;
+  a.scratch = reinterpret_cast<float*>(w + (fixed - 256));
+  const size_t groups = (ws_bytes - fixed) / per_group;
+  const int nbg = s->batch * s->heads_kv;
+  a.gpass = groups < (size_t)nbg ? (int)groups : nbg;
+  a.group_words = (int64_t)(per_group / sizeof(uint32_t));
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
+  a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
+  a.T = s->seq_len; a.NCs = s->seq_len / s->chunk; a.scale = eff_scale(s);
+  a.n_slots = n_slots; a.slot_stride = stride;
+  return from_hip(hils::launch_bsa_select(a, stream));
+}
+
+hils_status hils_selection_overlap(const hils_shape* s, const int32_t* idx_a, const int32_t* idx_b,
+                                   int32_t* count, hipStream_t stream) {
+  const hils_status st = check_shape(s, kPrefill);
+  if (st != HILS_OK) return st;
+  if (!count || (s->top_k > 0 && (!idx_a || !idx_b))) return HILS_E_NULL;
+  if (!aligned16(idx_a) || !aligned16(idx_b) || !aligned16(count)) return HILS_E_ALIGN;
+  const int64_t nrows = (int64_t)s->batch * s->heads_kv * s->seq_len;
+  if (s->top_k == 0) return from_hip(hipMemsetAsync(count, 0, (size_t)nrows * sizeof(int32_t), stream));
+  return from_hip(hils::launch_overlap(idx_a, idx_b, count, nrows, s->top_k, stream));
+}
+
 hils_status hils_attend_fuse_backward(const hils_shape* s, const void* q, const void* k,
                                       const void* v, const void* q_hat, const void* k_sum,
                                       const int32_t* sel_idx, const float* sel_score,

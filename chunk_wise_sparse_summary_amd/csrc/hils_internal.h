@@ -51,6 +51,11 @@ struct SelArgs {
   int64_t group_words;  // keys of one (b, group), padded
 };
 hipError_t launch_select(const SelArgs& a, hipStream_t st);
+// Naive BSA selection: SelArgs with qh = the token query q, ksum = the keys k,
+// bsum unused and ssel = nullptr; the same workspace layout as the selection.
+hipError_t launch_bsa_select(const SelArgs& a, hipStream_t st);
+hipError_t launch_overlap(const int32_t* ia, const int32_t* ib, int32_t* cnt, int64_t nrows, int topk,
+                          hipStream_t st);
 // Bytes for every (b, group) at once; a workspace of fixed + k * per_group
 // bytes (k >= 1) runs the selection k pairs per launch.
 size_t select_workspace(int B, int Hq, int Hkv, int64_t T, int S, bool bf16, int* n_slots,
@@ -168,7 +173,7 @@ enum KernelId {
   K_SUMMARIZE, K_SCORE_LSE, K_IDX_COUNT, K_IDX_SCAN_TILES, K_IDX_SCAN_BUCKETS,
   K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_DEC_SCORE, K_DEC_SELECT,
   K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_RANK_KEYS, K_TOPK_SCORES,
-  K_BWD_ROWSTAT, K_BWD_KV, K_BWD_DQ, K_BWD_QHAT, K_BWD_KSUM, K_SUM_BWD,
+  K_BWD_ROWSTAT, K_BWD_KV, K_BWD_DQ, K_BWD_QHAT, K_BWD_KSUM, K_SUM_BWD, K_BSA_KEYS, K_BSA_TOPK,
   K_COUNT
 };
 class KTimer {

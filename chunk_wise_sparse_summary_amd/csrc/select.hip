@@ -24,6 +24,7 @@
 // bisection with ballot counts over the few keys that reach theta, then the
 // chosen ids in ascending order with ballot prefix counts (ties at the k-th key
 // to the lowest ids).
+#include "attend_tiles.h"   // score_tile (naive BSA)
 #include "hils_internal.h"
 #include "topk.h"
 
@@ -393,6 +394,7 @@ void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
   }
   wave_lds_sync();
   if (lane < topk) a.idx[(((int64_t)b * a.Hkv + g) * T_ + i) * topk + lane] = sel[wave][lane];
+  if (a.ssel == nullptr) return;   // selection only (naive BSA)
   // 64 rows per batch: lane (grp, p) loads piece p of rows r0 + grp + RPI t
   for (int r0 = 0; r0 < topk * G; r0 += kWave) {
     float part[PPR];
@@ -479,6 +481,191 @@ hipError_t launch_select_t(const SelArgs& a, int J, hipStream_t st) {
   }
 }
 
+// ---------------------------------------------------------------- naive BSA
+// Exact chunk masses (paper-body page, Block Sparse Attention preliminaries):
+// log Z_{h,i,c} = LSE over the chunk's 64 tokens of scale q_{h,i} . k_j, for
+// every candidate c of every query, from MFMA score tiles of the chunk's keys
+// (staged once per workgroup in LDS) against 16-row query tiles (16/G queries x
+// G heads, TPW tiles per wave).  For G > 1 a first sweep over the chunks forms
+// each head's L_{h,i} = LSE_c log Z_{h,i,c}, the second the rank keys
+// max_h (log Z - L); a group of one head ranks by log Z.  Keys go to the same
+// per-query rows as the retrieval rank keys (16-chunk runs staged in LDS), and
+// the same wave top-k picks the selection.  Cost: every token logit left of the
+// window, twice for G > 1; a diagnostic, not part of the path.
+template <typename T> constexpr int bsa_tpw() { return sizeof(T) == 2 ? 4 : 2; }
+
+template <typename T, int D, int G, int NCP>
+__global__ __launch_bounds__(256) void bsa_keys_kernel(SelArgs a, int bg0, uint32_t* __restrict__ keys) {
+  const int b = (bg0 + (int)blockIdx.y) / a.Hkv, g = (bg0 + (int)blockIdx.y) % a.Hkv;
+  keys += (int64_t)blockIdx.y * a.group_words;
+  constexpr int TPW = bsa_tpw<T>();
+  constexpr int KS = D / 32, EPV = 16 / (int)sizeof(T), PK = D / EPV;
+  constexpr int NE = 16 / G;        // queries per 16-row tile
+  constexpr int QW = TPW * NE;      // queries per wave
+  constexpr int QB = 4 * QW;        // queries per workgroup
+  constexpr int RUN = 16;           // chunks per flush of the staged keys
+  constexpr int KSP = RUN + 4;      // padded words per query
+  __shared__ __align__(16) T ks[64 * D];
+  __shared__ __align__(16) uint32_t kst[4][QW * KSP];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r16 = lane % 16, grp = lane / 16;
+  const int64_t T_ = a.T;
+  const int64_t qb = (int64_t)(gridDim.x - 1 - blockIdx.x) * QB;   // longest rows first
+  const int64_t qw0 = qb + (int64_t)wave * QW;
+  const T* qg = static_cast<const T*>(a.qh);
+  const T* kg = static_cast<const T*>(a.ksum) + ((int64_t)b * a.Hkv + g) * T_ * D;
+  Frag<T> bq[TPW][KS];
+  int nct[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int64_t qi = qw0 + t * NE + r16 / G;
+    const int h = g * G + r16 % G;
+    const T* qrow = qg + (((int64_t)b * a.Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) load_frag(bq[t][kq], qrow + 32 * kq);
+    nct[t] = qi < T_ ? (int)num_candidates(qi, a.S, a.W) : 0;
+  }
+  const int nc_block = (int)num_candidates(min(qb + QB - 1, T_ - 1), a.S, a.W);
+  const int nc_wave = (int)num_candidates(min(qw0 + QW - 1, T_ - 1), a.S, a.W);
+  const float sl2 = a.scale * kLog2e;
+  constexpr float kLn2 = 0.6931471805599453f;
+  float L2[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) L2[t] = 0.f;
+  for (int sweep = G > 1 ? 0 : 1; sweep < 2; ++sweep) {
+    float M[TPW], Z[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      M[t] = -1e30f;
+      Z[t] = 0.f;
+    }
+    for (int c = 0; c < nc_block; ++c) {
+      __syncthreads();
+      for (int e = threadIdx.x; e < 64 * PK; e += 256) {
+        const int row = e / PK, p = e % PK;
+        *reinterpret_cast<uint4*>(ks + swz<PK>(row, p) * EPV) =
+            *reinterpret_cast<const uint4*>(kg + ((int64_t)c * 64 + row) * D + p * EPV);
+      }
+      __syncthreads();
+      if (c >= nc_wave) continue;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        f32x4_t acc[4];
+        score_tile<T, D>(ks, bq[t], acc, r16, grp);
+        float mx = kNegInf;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) mx = fmaxf(mx, acc[mt][q4]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        mx *= sl2;
+        float z = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) z += hw_exp2(fmaf(acc[mt][q4], sl2, -mx));
+        z += __shfl_xor(z, 16, kWave);
+        z += __shfl_xor(z, 32, kWave);
+        const float lz2 = mx + __log2f(z);   // log2 of the chunk mass
+        const bool valid = c < nct[t];
+        if (sweep == 0) {
+          if (valid) {
+            const float m2 = fmaxf(M[t], lz2);
+            Z[t] = Z[t] * hw_exp2(M[t] - m2) + hw_exp2(lz2 - m2);
+            M[t] = m2;
+          }
+        } else {
+          float r = valid ? (G > 1 ? lz2 - L2[t] : lz2) : kNegInf;
+#pragma unroll
+          for (int o = 1; o < G; o <<= 1) r = fmaxf(r, __shfl_xor(r, o, kWave));
+          if (grp == 0 && r16 % G == 0) kst[wave][(t * NE + r16 / G) * KSP + c % RUN] = order_key(r * kLn2);
+        }
+      }
+      if (sweep == 1 && (c % RUN == RUN - 1 || c == nc_wave - 1)) {
+        wave_lds_sync();
+#pragma unroll
+        for (int qq0 = 0; qq0 < QW; qq0 += 16) {
+          const int qq = qq0 + lane / 4, p = lane % 4;
+          const int64_t qi = qw0 + qq;
+          if (qq < QW && qi < T_)
+            *reinterpret_cast<uint4*>(keys + qi * NCP + (c - c % RUN) + 4 * p) =
+                *reinterpret_cast<const uint4*>(&kst[wave][qq * KSP + 4 * p]);
+        }
+        wave_lds_sync();
+      }
+    }
+    if (sweep == 0) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) L2[t] = nct[t] > 0 ? M[t] + __log2f(Z[t]) : 0.f;
+    }
+  }
+}
+
+// |A n B| per row of two selections (ascending ids, -1 pads at the end).
+__global__ __launch_bounds__(256) void overlap_kernel(const int32_t* __restrict__ ia,
+                                                      const int32_t* __restrict__ ib,
+                                                      int32_t* __restrict__ cnt, int64_t nrows, int topk) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= nrows) return;
+  const int32_t* x = ia + r * topk;
+  const int32_t* y = ib + r * topk;
+  int u = 0, v = 0, n = 0;
+  while (u < topk && v < topk && x[u] >= 0 && y[v] >= 0) {
+    if (x[u] == y[v]) {
+      ++n;
+      ++u;
+      ++v;
+    } else if (x[u] < y[v]) {
+      ++u;
+    } else {
+      ++v;
+    }
+  }
+  cnt[r] = n;
+}
+
+template <typename T, int D, int G, int J>
+hipError_t launch_bsa_j(const SelArgs& a, hipStream_t st) {
+  constexpr int QB = 4 * bsa_tpw<T>() * (16 / G);
+  const dim3 tiles((unsigned)((a.T + QB - 1) / QB)), rows((unsigned)((a.T + 3) / 4));
+  uint32_t* keys = reinterpret_cast<uint32_t*>(a.scratch);
+  const int nbg = a.B * a.Hkv;
+  for (int bg0 = 0; bg0 < nbg; bg0 += a.gpass) {
+    const int n = min(a.gpass, nbg - bg0);
+    {
+      KTimer tm(K_BSA_KEYS, st);
+      hipLaunchKernelGGL((bsa_keys_kernel<T, D, G, 64 * J>), dim3(tiles.x, (unsigned)n), dim3(256), 0, st, a,
+                         bg0, keys);
+    }
+    KTimer tm(K_BSA_TOPK, st);
+    hipLaunchKernelGGL((topk_scores_kernel<T, D, G, J>), dim3(rows.x, (unsigned)n), dim3(256), 0, st, a, bg0, keys);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t launch_bsa_g(const SelArgs& a, int J, hipStream_t st) {
+  switch (J) {
+    case 1: return launch_bsa_j<T, D, G, 1>(a, st);
+    case 4: return launch_bsa_j<T, D, G, 4>(a, st);
+    case 16: return launch_bsa_j<T, D, G, 16>(a, st);
+    case 32: return launch_bsa_j<T, D, G, 32>(a, st);
+    default: return launch_bsa_j<T, D, G, 64>(a, st);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_bsa_t(const SelArgs& a, int J, hipStream_t st) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_bsa_g<T, D, 1>(a, J, st);
+    case 2: return launch_bsa_g<T, D, 2>(a, J, st);
+    case 4: return launch_bsa_g<T, D, 4>(a, J, st);
+    default: return launch_bsa_g<T, D, 8>(a, J, st);
+  }
+}
+
 int pick_J(int64_t NCs) {
   const int64_t need = (NCs + 63) / 64;
   if (need <= 1) return 1;
@@ -510,6 +697,20 @@ hipError_t launch_select(const SelArgs& a, hipStream_t st) {
   const int J = pick_J(a.NCs);
   if (a.bf16) return a.D == 128 ? launch_select_t<bf16_t, 128>(a, J, st) : launch_select_t<bf16_t, 64>(a, J, st);
   return a.D == 128 ? launch_select_t<float, 128>(a, J, st) : launch_select_t<float, 64>(a, J, st);
+}
+
+hipError_t launch_bsa_select(const SelArgs& a, hipStream_t st) {
+  const int J = pick_J(a.NCs);
+  if (a.bf16) return a.D == 128 ? launch_bsa_t<bf16_t, 128>(a, J, st) : launch_bsa_t<bf16_t, 64>(a, J, st);
+  return a.D == 128 ? launch_bsa_t<float, 128>(a, J, st) : launch_bsa_t<float, 64>(a, J, st);
+}
+
+hipError_t launch_overlap(const int32_t* ia, const int32_t* ib, int32_t* cnt, int64_t nrows, int topk,
+                          hipStream_t st) {
+  if (nrows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(overlap_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, st, ia, ib, cnt,
+                     nrows, topk);
+  return hipGetLastError();
 }
 
 }  // namespace hils

@@ -18,6 +18,11 @@
  *   hils_attend_fuse_backward  attention and fusion, given the selection
  *   hils_summarize_backward    the landmark summaries
  *
+ * plus a selection diagnostic (naive Block Sparse Attention's exact chunk-mass
+ * top-k, and the overlap of two selections):
+ *
+ *   hils_bsa_select, hils_selection_overlap
+ *
  * Notation: B batch, Hq query heads, Hkv key/value heads, G = Hq/Hkv heads per
  * group, d head dimension, S chunk size, W window, k top-k, T tokens,
  * NC = floor(T/S) complete chunks, scale = 1/sqrt(d) unless given.  Token i
@@ -287,6 +292,32 @@ hils_status hils_summarize_backward(const hils_shape* shape, const void* k, cons
                                     const float* dk_sum, const float* db_sum, int64_t chunk_begin,
                                     int64_t n_chunks, float* dk, float* dq_land, hipStream_t stream);
 
+/*
+ * Naive Block Sparse Attention selection, a diagnostic of the retrieval
+ * (paper-body page, Block Sparse Attention preliminaries: a chunk's mass is the
+ * sum of the query's exponentiated token logits over the chunk, and naive BSA
+ * keeps the k candidates of largest mass; it needs every token logit, so its
+ * cost grows as T^2 d, and it is not part of the HiLS path).  For every b,
+ * position i < T and group g:
+ *     log Z_{h,i,c} = LSE_{j in chunk c} scale * q_{h,i} . k_{g,j},   c in C_i
+ *     rank key and Sel exactly as hils_select, with log Z in place of s_hat.
+ * q [B,Hq,T,d] and k [B,Hkv,T,d]: io_dtype (the token query, not q_hat)
+ * sel_idx [B,Hkv,T,k] int32 out: chunk ids ascending, -1 padded
+ * Workspace: hils_workspace_bytes(shape, HILS_OP_SELECT), with the same rule for
+ * a smaller one (at least one (b, group)'s keys: several passes).
+ */
+hils_status hils_bsa_select(const hils_shape* shape, const void* q, const void* k, int32_t* sel_idx,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Overlap of two selections of the same shape (for the recall of HiLS's
+ * selection against naive BSA's): count[b,g,i] = the number of chunk ids that
+ * rows (b, g, i) of idx_a and idx_b [B,Hkv,T,k] (ascending, -1 padded) share.
+ * count [B,Hkv,T] int32 out.  Needs no workspace.
+ */
+hils_status hils_selection_overlap(const hils_shape* shape, const int32_t* idx_a, const int32_t* idx_b,
+                                   int32_t* count, hipStream_t stream);
+
 /* Workspace bytes `op` needs for `shape` (0 for HILS_OP_SUMMARIZE); 0 as well
  * for an invalid shape. */
 size_t hils_workspace_bytes(const hils_shape* shape, hils_op op);
@@ -310,9 +341,9 @@ int hils_abi_version(void);
  *   dec_score, dec_select,
  *   dec_attend, dec_fuse, dec_summarize (the summaries of chunks
  *   completed by a decode step), v_transpose, rank_keys,
- *   topk_scores, and for the backward calls bwd_rowstat, bwd_kv, bwd_dq,
+ *   topk_scores, for the backward calls bwd_rowstat, bwd_kv, bwd_dq,
  *   bwd_qhat, bwd_ksum and summarize_bwd (the entry lists of the
- *   backward count under the idx_* names).  HILS_E_UNSUPPORTED for an unknown name
+ *   backward count under the idx_* names), and bsa_keys, bsa_topk.  HILS_E_UNSUPPORTED for an unknown name
  *   (timing is then left off).
  * hils_timing_get(kernel, total_ms, launches): waits for the recorded events
  *   of that kernel and returns the summed duration and the number of timed
