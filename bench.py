@@ -441,6 +441,60 @@ def time_backward(hils, x, fwd, shape, reps=3):
                     "FLOPs = 2.5 x the forward's attended FLOPs" % reps}
 
 
+def time_bsa(hils, x, idx_hils, shape, ws, reps=2):
+    """Naive-BSA selection (exact chunk masses, a diagnostic): median time of
+    `reps` calls, and HiLS's recall against it over every row with a choice."""
+    import torch
+    q = x["q"]
+    dev = q.device
+    B, Hq, T, d = q.shape
+    Hkv = x["k"].shape[1]
+    S, W, k = shape.chunk, shape.window, shape.top_k
+    bsa = torch.empty_like(idx_hils)
+
+    def one():
+        hils.hils_bsa_select(x["q"], x["k"], bsa, shape, ws)
+    one()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a.record()
+        one()
+        b_.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b_))
+    hils.hils_timing_enable(["bsa_keys", "bsa_topk"])
+    one()
+    torch.cuda.synchronize()
+    kern = {}
+    for kn in ("bsa_keys", "bsa_topk"):
+        tms, nl = hils.hils_timing_get(kn)
+        if nl:
+            kern[kn] = {"ms": tms, "launches": nl}
+    hils.hils_timing_enable(None)
+    cnt = torch.empty((B, Hkv, T), dtype=torch.int32, device=dev)
+    hils.hils_selection_overlap(idx_hils, bsa, cnt, shape)
+    torch.cuda.synchronize()
+    i = np.arange(T)
+    a_ = i - W + 1
+    nc = np.where(a_ <= 0, 0, (a_ // S) * S) // S
+    ev = nc > k
+    hits = int(cnt.cpu().numpy()[:, :, ev].sum())
+    n_ev = int(ev.sum()) * B * Hkv
+    sweeps = 2 if Hq // Hkv > 1 else 1
+    logits = float(B * Hq) * float(np.sum(nc)) * S     # (row, token) logits per sweep
+    ms = float(np.median(ts))
+    flops = sweeps * 2.0 * d * logits
+    return {"ms_median": ms, "logit_flops": flops, "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16,
+            "exp_count": sweeps * logits, "kernels_ms": kern,
+            "hils_recall": hits / (n_ev * k) if n_ev else None, "events": n_ev,
+            "chance_recall": float(np.mean(k / nc[ev])) if ev.any() else None,
+            "note": "exact chunk masses of every candidate (two sweeps for GQA) + wave top-k; "
+                    "recall = shared chunk ids / (k x rows with |C_i| > k); chance = mean k/|C_i|"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -700,6 +754,8 @@ def main():
         del ws_att
         res["backward_128k"] = time_backward(hils, x, {"k_sum": k_sum, "idx": idx, "ssel": ssel, "out": out,
                                                        "lse": lse}, shape)
+        log("128K naive-BSA selection")
+        res["bsa_128k"] = time_bsa(hils, x, idx, shape, ws_sel, reps=1)
 
     if not args.no_extra:
         # ---- 8K prefill (32/8 heads, d=128, k=16, W=512, one planted needle)
@@ -737,6 +793,8 @@ def main():
                                      "(output buffers allocated inside each call)"}
         log("8K backward")
         res["backward_8k"] = time_backward(hils, x8, r8, sh8, reps=10)
+        log("8K naive-BSA selection")
+        res["bsa_8k"] = time_bsa(hils, x8, r8["idx"], sh8, p8["wss"], reps=5)
         del x8, p8, r8
         # ---- 4M decode (B=1, k=64, 8 needles, 256 steps with 4 chunk completions)
         log("4M decode: drawing the cache")
