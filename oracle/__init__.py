@@ -69,6 +69,8 @@ def lib():
         L.orc_bsa_rows.argtypes = [I, I, I, I, I, I, I, D, I64, P, P, P, P, P, I, I64, P, I, I64,
                                    P, P, P, P, I64, P, I64]
         L.orc_bsa_rows.restype = I
+        L.orc_qcal.argtypes = [I, I, I, I64, I, I, P, P, P, P, I, I, P]
+        L.orc_qcal.restype = I
         L.orc_window_left.argtypes = [I64, I, I]
         L.orc_window_left.restype = I64
         L.orc_num_candidates.argtypes = [I64, I, I]
@@ -254,6 +256,26 @@ def selection_recall(idx_a, idx_b, ncand, topk: int) -> dict:
         hits += len(set(x[x >= 0].tolist()) & set(y[y >= 0].tolist()))
     n = int(ev.sum())
     return {"events": n, "hits": hits, "recall": hits / (n * topk) if n else float("nan")}
+
+
+def qcal(q, h, w_down, w_up, round_mode: int = ORND_NONE) -> np.ndarray:
+    """Calibrated retrieval query q_hat = q + W_up W_down h [B,Hq,T,d] (float64,
+    rounded once to round_mode).  h [B,T,dm], w_down [r,dm], w_up [Hq,d,r]."""
+    qa, dt = _as_np(q)
+    ha, hdt = _as_np(h)
+    wd, wddt = _as_np(w_down)
+    wu, wudt = _as_np(w_up)
+    assert dt == hdt == wddt == wudt
+    B, Hq, T, d = qa.shape
+    dm = ha.shape[2]
+    r = wd.shape[0]
+    assert ha.shape == (B, T, dm) and wd.shape == (r, dm) and wu.shape == (Hq, d, r)
+    out = np.zeros((B, Hq, T, d), np.float64)
+    rc = lib().orc_qcal(B, Hq, d, T, dm, r, _ptr(ha), _ptr(wd), _ptr(wu), _ptr(qa), dt, round_mode,
+                        _ptr(out))
+    if rc != 0:
+        raise RuntimeError("orc_qcal failed: %d" % rc)
+    return out
 
 
 def ks_round_for(summary_dtype) -> int:

@@ -638,3 +638,44 @@ int orc_bsa_rows(int B, int Hq, int Hkv, int d, int S, int W, int topk, double s
     }
     return err;
 }
+
+/*
+ * Low-rank query calibration ([p1 Q-Cal] and the summary page's practical
+ * enhancements: the retrieval query is the token query plus a rank-r correction
+ * of the token's hidden state, q_hat = q + W_up W_down h).  For every b, t:
+ *   z_j = sum_m w_down[j, m] h[b, t, m]                         (j < r)
+ *   q_hat[b, hd, t, e] = q[b, hd, t, e] + sum_j w_up[hd, e, j] z_j
+ * rounded once to `round_mode` (the stored query the scoring reads).
+ * h [B, T, dm], w_down [r, dm], w_up [Hq, d, r], q [B, Hq, T, d], all of dtype dt;
+ * out [B, Hq, T, d] doubles.
+ */
+int orc_qcal(int B, int Hq, int d, int64_t T, int dm, int r, const void* h, const void* w_down,
+             const void* w_up, const void* q, int dt, int round_mode, double* out) {
+    if (B < 0 || Hq < 0 || d < 0 || T < 0 || dm < 0 || r < 0) return -1;
+    int err = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t bt = 0; bt < (int64_t)B * T; ++bt) {
+        const int64_t b = bt / T, t = bt % T;
+        double* z = (double*)malloc(sizeof(double) * (size_t)(r > 0 ? r : 1));
+        if (!z) {
+#pragma omp atomic write
+            err = -2;
+            continue;
+        }
+        for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int m = 0; m < dm; ++m) acc += ld(w_down, dt, (int64_t)j * dm + m) * ld(h, dt, bt * dm + m);
+            z[j] = acc;
+        }
+        for (int hd = 0; hd < Hq; ++hd) {
+            for (int e = 0; e < d; ++e) {
+                double acc = 0.0;
+                for (int j = 0; j < r; ++j) acc += ld(w_up, dt, ((int64_t)hd * d + e) * r + j) * z[j];
+                const int64_t o = (((int64_t)b * Hq + hd) * T + t) * d + e;
+                out[o] = round_to(ld(q, dt, o) + acc, round_mode);
+            }
+        }
+        free(z);
+    }
+    return err;
+}

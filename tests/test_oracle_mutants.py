@@ -12,6 +12,7 @@ import oracle
 import test_oracle_backward as bwd
 import test_oracle_bsa as bsa
 import test_oracle_pins as pins
+import test_oracle_qcal as qc
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "hils_oracle.c")
 
@@ -57,6 +58,16 @@ MUTANTS = [
      "lz[hh * nc + c] = lse(s, S) - log((double)S);"),
     ("BSA: GQA without per-head normalisation", "best = fmax(best, lz[hh * nc + c] - L[hh]);",
      "best = fmax(best, lz[hh * nc + c]);"),
+    ("Q-Cal: residual query dropped", "out[o] = round_to(ld(q, dt, o) + acc, round_mode);",
+     "out[o] = round_to(acc, round_mode);"),
+    ("Q-Cal: down-projection transposed",
+     "acc += ld(w_down, dt, (int64_t)j * dm + m) * ld(h, dt, bt * dm + m);",
+     "acc += ld(w_down, dt, (int64_t)m * r + j) * ld(h, dt, bt * dm + m);"),
+    ("Q-Cal: up-projection of head 0 for every head",
+     "acc += ld(w_up, dt, ((int64_t)hd * d + e) * r + j) * z[j];",
+     "acc += ld(w_up, dt, ((int64_t)0 * d + e) * r + j) * z[j];"),
+    ("Q-Cal: rounding skipped", "out[o] = round_to(ld(q, dt, o) + acc, round_mode);",
+     "out[o] = ld(q, dt, o) + acc;"),
     ("BSA: logits of the next chunk", "const int64_t off = kvb + (c * S + j) * d;",
      "const int64_t off = kvb + ((c + 1) * S + j) * d;"),
 ]
@@ -87,6 +98,10 @@ PIN_TESTS = [
     lambda g: bsa.test_bsa_chunk_size_one_is_top_logits(),
     lambda g: bsa.test_bsa_identical_keys_per_chunk(),
     lambda g: bsa.test_hils_equals_bsa_at_the_landmark_query(4),
+    lambda g: qc.test_zero_up_projection_or_hidden_state_is_identity(),
+    lambda g: qc.test_rank_one_one_hot_closed_form(),
+    lambda g: qc.test_correction_is_linear_in_h(),
+    lambda g: qc.test_stored_query_rounds_to_nearest_even(),
 ]
 
 
