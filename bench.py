@@ -495,6 +495,41 @@ def time_bsa(hils, x, idx_hils, shape, ws, reps=2):
                     "recall = shared chunk ids / (k x rows with |C_i| > k); chance = mean k/|C_i|"}
 
 
+def time_qcal(hils, x, wl, shape, d_model=4096, rank=64, reps=5):
+    """Q-Cal (q_hat = q + W_up W_down h) at the workload's size with random
+    weights: median of `reps` calls; HBM roof on q, h and q_hat (the weights
+    stay in cache)."""
+    import torch
+    import workloads as wk
+    q = x["q"]
+    dev = q.device
+    c = wk.make_qcal(wl, d_model, rank, seed=5, device=dev)
+    qh = torch.empty_like(q)
+
+    def one():
+        hils.hils_qcal(q, c["h"], c["w_down"], c["w_up"], qh, shape)
+    one()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a.record()
+        one()
+        b_.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b_))
+    ms = float(np.median(ts))
+    esz = q.element_size()
+    byts = 2 * q.numel() * esz + c["h"].numel() * esz + (c["w_down"].numel() + c["w_up"].numel()) * esz
+    B, Hq, T, d = q.shape
+    flops = 2.0 * B * T * rank * (d_model + Hq * d)
+    del c, qh
+    return {"ms_median": ms, "bytes": byts, "GBps": byts / (ms * 1e-3) / 1e9,
+            "hbm_frac": byts / (ms * 1e-3) / PEAK_HBM, "flops": flops, "d_model": d_model, "rank": rank,
+            "note": "median of %d calls; bytes = q + h + q_hat + weights" % reps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -754,6 +789,8 @@ def main():
         del ws_att
         res["backward_128k"] = time_backward(hils, x, {"k_sum": k_sum, "idx": idx, "ssel": ssel, "out": out,
                                                        "lse": lse}, shape)
+        log("128K Q-Cal")
+        res["qcal_128k"] = time_qcal(hils, x, wl, shape)
         log("128K naive-BSA selection")
         res["bsa_128k"] = time_bsa(hils, x, idx, shape, ws_sel, reps=1)
 

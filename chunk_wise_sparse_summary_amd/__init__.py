@@ -14,6 +14,8 @@ if the library is missing, loading raises.
                               dlse, dq, dk, dv, dq_hat, dk_sum, db_sum, shape, workspace=None)
     hils_summarize_backward(k, q_land, dk_sum, db_sum, dk, dq_land, shape, chunk_begin=0,
                             n_chunks=None)
+    hils_qcal(q, hs, w_down, w_up, q_hat, shape)
+    hils_summarize_shared(k, q_shared, k_sum, b_sum, shape, chunk_begin=0, n_chunks=None)
     hils_bsa_select(q, k, sel_idx, shape, workspace=None)
     hils_selection_overlap(idx_a, idx_b, count, shape)
     hils_workspace_bytes(shape, op)
@@ -42,7 +44,7 @@ STATUS = {
 
 EXPORTS = ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
            "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
-           "hils_bsa_select", "hils_selection_overlap",
+           "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_summarize_shared",
            "hils_workspace_bytes", "hils_status_string", "hils_abi_version",
            "hils_timing_enable", "hils_timing_get")
 
@@ -88,6 +90,8 @@ def lib():
         L.hils_summarize_backward.argtypes = [SP, P, P, P, P, I64, I64, P, P, P]
         L.hils_bsa_select.argtypes = [SP, P, P, P, P, SZ, P]
         L.hils_selection_overlap.argtypes = [SP, P, P, P, P]
+        L.hils_qcal.argtypes = [SP, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P]
+        L.hils_summarize_shared.argtypes = [SP, P, P, I64, I64, P, P, P]
         L.hils_workspace_bytes.argtypes = [SP, ctypes.c_int]
         L.hils_workspace_bytes.restype = SZ
         L.hils_status_string.argtypes = [ctypes.c_int]
@@ -100,7 +104,7 @@ def lib():
         L.hils_timing_get.restype = ctypes.c_int
         for f in ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
                   "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
-                  "hils_bsa_select", "hils_selection_overlap"):
+                  "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_summarize_shared"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -203,6 +207,23 @@ def hils_summarize_backward(k, q_land, dk_sum, db_sum, dk, dq_land, shape: Shape
         _p(dk), _p(dq_land), _stream()))
 
 
+def hils_qcal(q, hs, w_down, w_up, q_hat, shape: Shape):
+    """q_hat = q + W_up (W_down hs), rounded once to the io dtype."""
+    _dev(q, hs, w_down, w_up, q_hat)
+    _check("hils_qcal", lib().hils_qcal(ctypes.byref(shape), _p(q), _p(hs), _p(w_down), _p(w_up),
+                                        int(hs.shape[-1]), int(w_down.shape[0]), _p(q_hat), _stream()))
+
+
+def hils_summarize_shared(k, q_shared, k_sum, b_sum, shape: Shape, chunk_begin: int = 0,
+                          n_chunks: int | None = None):
+    """Summaries with one shared landmark query per head (q_shared [Hq, d])."""
+    _dev(k, q_shared, k_sum, b_sum)
+    if n_chunks is None:
+        n_chunks = shape.seq_len // shape.chunk - chunk_begin
+    _check("hils_summarize_shared", lib().hils_summarize_shared(
+        ctypes.byref(shape), _p(k), _p(q_shared), chunk_begin, n_chunks, _p(k_sum), _p(b_sum), _stream()))
+
+
 def hils_bsa_select(q, k, sel_idx, shape: Shape, workspace_t=None):
     """Naive Block Sparse Attention selection (exact chunk masses), a diagnostic."""
     _dev(q, k, sel_idx)
@@ -234,7 +255,7 @@ KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",
            "dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize",
            "v_transpose", "rank_keys", "topk_scores",
            "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "bwd_ksum", "summarize_bwd",
-           "bsa_keys", "bsa_topk")
+           "bsa_keys", "bsa_topk", "qcal")
 
 
 def hils_timing_enable(kernels):

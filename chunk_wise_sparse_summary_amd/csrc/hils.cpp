@@ -129,6 +129,49 @@ hils_status hils_summarize(const hils_shape* s, const void* k, const void* q_lan
   return from_hip(hils::launch_summarize(a, stream));
 }
 
+hils_status hils_summarize_shared(const hils_shape* s, const void* k, const void* q_shared,
+                                  int64_t chunk_begin, int64_t n_chunks, void* k_sum, float* b_sum,
+                                  hipStream_t stream) {
+  const hils_status st = check_shape(s, kSummarize);
+  if (st != HILS_OK) return st;
+  if (!k || !q_shared || !k_sum || !b_sum) return HILS_E_NULL;
+  if (!aligned16(k) || !aligned16(q_shared) || !aligned16(k_sum) || !aligned16(b_sum)) return HILS_E_ALIGN;
+  const int64_t NC = s->seq_len / s->chunk;
+  if (chunk_begin < 0 || n_chunks < 0 || chunk_begin + n_chunks > NC) return HILS_E_SHAPE;
+  if (n_chunks > 0x7fffffff) return HILS_E_UNSUPPORTED;
+  if (n_chunks == 0) return HILS_OK;
+  hils::SumArgs a{};
+  a.k = k; a.ql = q_shared; a.ksum = k_sum; a.bsum = b_sum;
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim;
+  a.bf16 = s->io_dtype == HILS_BF16;
+  a.kT = s->seq_len; a.NCs = NC;
+  a.ql_sb = 0;                 // one query per head, for every sequence and chunk
+  a.ql_sh = s->head_dim;
+  a.ql_sc = 0;
+  a.c0 = chunk_begin; a.n_chunks = n_chunks;
+  a.scale = eff_scale(s);
+  a.list.n = 0;
+  return from_hip(hils::launch_summarize(a, stream));
+}
+
+hils_status hils_qcal(const hils_shape* s, const void* q, const void* h, const void* w_down,
+                      const void* w_up, int32_t d_model, int32_t rank, void* q_hat, hipStream_t stream) {
+  const hils_status st = check_shape(s, kSummarize);
+  if (st != HILS_OK) return st;
+  if (!q || !h || !w_down || !w_up || !q_hat) return HILS_E_NULL;
+  if (!aligned16(q) || !aligned16(h) || !aligned16(w_down) || !aligned16(w_up) || !aligned16(q_hat))
+    return HILS_E_ALIGN;
+  if (d_model < 32 || d_model % 32 != 0 || d_model > 65536) return HILS_E_UNSUPPORTED;
+  if (rank != 16 && rank != 32 && rank != 64 && rank != 128) return HILS_E_UNSUPPORTED;
+  if (q == q_hat) return HILS_E_SHAPE;
+  if (s->seq_len > 0x7fffffffLL * 64) return HILS_E_UNSUPPORTED;
+  hils::QcalArgs a{};
+  a.q = q; a.h = h; a.wd = w_down; a.wu = w_up; a.qh = q_hat;
+  a.B = s->batch; a.Hq = s->heads_q; a.D = s->head_dim; a.dm = d_model; a.r = rank;
+  a.bf16 = s->io_dtype == HILS_BF16; a.T = s->seq_len;
+  return from_hip(hils::launch_qcal(a, stream));
+}
+
 hils_status hils_select(const hils_shape* s, const void* q_hat, const void* k_sum,
                         const float* b_sum, int32_t* sel_idx, float* sel_score, void* ws,
                         size_t ws_bytes, hipStream_t stream) {

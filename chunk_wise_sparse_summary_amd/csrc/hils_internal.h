@@ -143,6 +143,19 @@ struct SumBwdArgs {
 };
 hipError_t launch_summarize_backward(const SumBwdArgs& a, hipStream_t st);
 
+// Low-rank query calibration: q_hat = q + W_up (W_down h).
+struct QcalArgs {
+  const void* q;
+  const void* h;    // [B, T, dm]
+  const void* wd;   // [r, dm]
+  const void* wu;   // [Hq, D, r]
+  void* qh;
+  int B, Hq, D, dm, r;
+  bool bf16;
+  int64_t T;
+};
+hipError_t launch_qcal(const QcalArgs& a, hipStream_t st);
+
 struct DecArgs {
   const int64_t* pos;  // host
   const void* q;
@@ -174,7 +187,7 @@ enum KernelId {
   K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_DEC_SCORE, K_DEC_SELECT,
   K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_RANK_KEYS, K_TOPK_SCORES,
   K_BWD_ROWSTAT, K_BWD_KV, K_BWD_DQ, K_BWD_QHAT, K_BWD_KSUM, K_SUM_BWD, K_BSA_KEYS, K_BSA_TOPK,
-  K_COUNT
+  K_QCAL, K_COUNT
 };
 class KTimer {
  public:

@@ -23,6 +23,11 @@
  *
  *   hils_bsa_select, hils_selection_overlap
  *
+ * and the two variants of the steps before scoring: the calibrated retrieval
+ * query and summaries from one shared query per head:
+ *
+ *   hils_qcal, hils_summarize_shared
+ *
  * Notation: B batch, Hq query heads, Hkv key/value heads, G = Hq/Hkv heads per
  * group, d head dimension, S chunk size, W window, k top-k, T tokens,
  * NC = floor(T/S) complete chunks, scale = 1/sqrt(d) unless given.  Token i
@@ -123,6 +128,35 @@ typedef struct {
 hils_status hils_summarize(const hils_shape* shape, const void* k, const void* q_land,
                            int64_t chunk_begin, int64_t n_chunks,
                            void* k_sum, float* b_sum, hipStream_t stream);
+
+/*
+ * Landmark summaries with one shared query per head (paper-body page,
+ * implementation: a learnable query shared by every chunk of a layer, in place
+ * of the landmark tokens): hils_summarize with q'_{h,c} = q_shared[h] for every
+ * sequence b and chunk c.
+ * q_shared [Hq, d] io_dtype; the other arguments, limits and errors as
+ * hils_summarize.
+ */
+hils_status hils_summarize_shared(const hils_shape* shape, const void* k, const void* q_shared,
+                                  int64_t chunk_begin, int64_t n_chunks,
+                                  void* k_sum, float* b_sum, hipStream_t stream);
+
+/*
+ * Low-rank query calibration of the retrieval query (paper-body page,
+ * implementation: Q-Cal; summary page, practical enhancements): the query that
+ * scores the chunk summaries is the token query plus a rank-r correction of
+ * the token's hidden state,
+ *     q_hat[b,h,t,:] = q[b,h,t,:] + W_up[h] (W_down hs[b,t,:])
+ * computed in fp32 (both products and the add) and rounded once to io_dtype:
+ * the q_hat that hils_select and hils_decode_step read.
+ * q [B,Hq,T,d], hs [B,T,d_model], w_down [rank,d_model], w_up [Hq,d,rank]: io_dtype
+ * q_hat [B,Hq,T,d] io_dtype out (must not be q: HILS_E_SHAPE).
+ * Requires d_model a multiple of 32 (at most 65536) and rank in {16, 32, 64, 128},
+ * else HILS_E_UNSUPPORTED.  Needs no workspace.
+ */
+hils_status hils_qcal(const hils_shape* shape, const void* q, const void* hs, const void* w_down,
+                      const void* w_up, int32_t d_model, int32_t rank, void* q_hat,
+                      hipStream_t stream);
 
 /*
  * Retrieval scores and top-k selection (paper-body page, RQ1: each query scores
@@ -343,7 +377,7 @@ int hils_abi_version(void);
  *   completed by a decode step), v_transpose, rank_keys,
  *   topk_scores, for the backward calls bwd_rowstat, bwd_kv, bwd_dq,
  *   bwd_qhat, bwd_ksum and summarize_bwd (the entry lists of the
- *   backward count under the idx_* names), and bsa_keys, bsa_topk.  HILS_E_UNSUPPORTED for an unknown name
+ *   backward count under the idx_* names), bsa_keys, bsa_topk, and qcal.  HILS_E_UNSUPPORTED for an unknown name
  *   (timing is then left off).
  * hils_timing_get(kernel, total_ms, launches): waits for the recorded events
  *   of that kernel and returns the summed duration and the number of timed

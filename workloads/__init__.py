@@ -330,3 +330,28 @@ def make_dyadic_select(B=1, Hq=4, Hkv=1, T=512, d=64, S=16, k=8, W=32, seed=0,
     return {"q_hat": torch.from_numpy(qh), "k_sum": torch.from_numpy(ks),
             "b_sum": torch.from_numpy(bs), "scale": 2.0 ** -3,
             "wl": custom(B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, S=S, k=k, W=W)}
+
+
+def make_qcal(wl: Workload, d_model: int, rank: int, seed: int = 0, device="cpu") -> dict:
+    """Hidden states and low-rank calibration weights for q_hat = q + W_up W_down h.
+
+    h ~ N(0,1) [B, T, d_model]; W_down ~ N(0,1)/sqrt(d_model) [rank, d_model] (so
+    W_down h has unit-variance entries); W_up ~ N(0,1) d^-1/4 / sqrt(rank)
+    [Hq, d, rank] (so the correction has the spread of q itself).  Random weights
+    stand in for trained ones.  Host numpy PCG64 (seed) for sizes up to 2^27
+    elements of h, else the device generator.
+    """
+    B, T, Hq, d = wl.B, wl.T, wl.Hq, wl.d
+    if B * T * d_model <= (1 << 27):
+        rng = np.random.Generator(np.random.PCG64(seed + 7919))
+        h = _np_normal(rng, (B, T, d_model), 1.0)
+        wd = _np_normal(rng, (rank, d_model), d_model ** -0.5)
+        wu = _np_normal(rng, (Hq, d, rank), d ** -0.25 * rank ** -0.5)
+        return {n: _to_dtype(a, wl, torch.device(device)) for n, a in (("h", h), ("w_down", wd), ("w_up", wu))}
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 7919)
+    dt = wl.torch_dtype
+    return {"h": _dev_normal(gen, (B, T, d_model), 1.0, torch.float32, dev).to(dt),
+            "w_down": _dev_normal(gen, (rank, d_model), d_model ** -0.5, torch.float32, dev).to(dt),
+            "w_up": _dev_normal(gen, (Hq, d, rank), d ** -0.25 * rank ** -0.5, torch.float32, dev).to(dt)}
