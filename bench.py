@@ -47,6 +47,11 @@ def window_stats(T, S, W):
     return lw // S, i - lw + 1       # |C_i|, |Win_i|
 
 
+def num_cand(i, S, W):
+    a = i - W + 1
+    return 0 if a <= 0 else (a // S)
+
+
 def attended_flops(B, Hq, T, d, S, W, k):
     nc, win = window_stats(T, S, W)
     return float(B * Hq * np.sum(4.0 * d * (np.minimum(k, nc) * S + win)))
@@ -373,6 +378,61 @@ def time_decode(hils, wl, cache, shape, ks, bs, steps, nrep, warm):
         torch.cuda.synchronize()
         times += [a.elapsed_time(b_) for a, b_ in ev]
     return times
+
+
+def time_decode_multi(hils, wl, cache, shape, ks, bs, M, calls, nrep=2, warm=4):
+    """hils_decode_multi with M adjacent tokens per sequence: per-call HIP-event
+    times (ms) of `calls` calls from the cache length (positions restart each
+    repetition, as in time_decode), and per-kernel times of one more pass."""
+    import torch
+    import workloads as wk
+    dev = ks.device
+    L0 = cache["length"]
+    nws = hils.hils_decode_multi_workspace_bytes(shape, M)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    inputs = []
+    for c in range(calls):
+        xs = [wk.make_decode_step(wl, c * M + m, seed=cache["seed"], device=dev) for m in range(M)]
+        cat = lambda n: torch.stack([x[n] for x in xs], dim=1).contiguous()
+        inputs.append({"q": cat("q"), "q_hat": cat("q_hat"), "k_new": cat("k_new"), "v_new": cat("v_new"),
+                       "q_land_new": xs[-1]["q_land_new"]})
+    out = torch.empty((wl.B, M, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.B, M, wl.Hq), dtype=torch.float32, device=dev)
+    idx = torch.empty((wl.B, M, wl.Hkv, wl.k), dtype=torch.int32, device=dev)
+
+    def one(c):
+        st = inputs[c]
+        hils.hils_decode_multi([L0 + c * M] * wl.B, M, st["q"], st["q_hat"], st["k_new"], st["v_new"],
+                               st["q_land_new"], cache["k_cache"], cache["v_cache"], ks, bs, out, lse, idx,
+                               shape, ws)
+    for c in range(warm):
+        one(c)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(nrep):
+        ev = []
+        for c in range(calls):
+            a = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a.record()
+            one(c)
+            b_.record()
+            ev.append((a, b_))
+        torch.cuda.synchronize()
+        times += [a.elapsed_time(b_) for a, b_ in ev]
+    names = ["dec_append", "dec_score", "dec_select", "dec_gsel", "dec_attend", "dec_fuse", "dec_summarize"]
+    hils.hils_timing_enable(names)
+    for c in range(calls):
+        one(c)
+    torch.cuda.synchronize()
+    kern = {}
+    for kn in names:
+        tms, nl = hils.hils_timing_get(kn)
+        if nl:
+            kern[kn] = {"avg_us": tms / nl * 1e3, "launches_per_call": nl / calls}
+    hils.hils_timing_enable(None)
+    del ws
+    return times, kern
 
 
 BWD_KERNELS = ["idx_count", "idx_scan_tiles", "idx_scan_buckets", "idx_fill", "bwd_rowstat", "bwd_kv",
@@ -784,6 +844,27 @@ def main():
             res["decode_kernels_us"][kn] = {"avg_us": tms / nl * 1e3, "launches_per_step": nl / nsteps}
     hils.hils_timing_enable(None)
     del ws_dec
+    if not args.no_extra:
+        log("512K multi-query decode (4 adjacent tokens per sequence)")
+        Mq = 4
+        calls = max(1, nsteps // Mq)
+        tm_, km_ = time_decode_multi(hils, dl, cache, dshape, dks, dbs, Mq, calls)
+        pos_m = [L0 + s for s in range(calls * Mq)]
+        # bytes of one call: the k' stream once per sequence (shared by the M queries),
+        # the selected and window chunks of each token as for one query
+        db1 = decode_bytes(dl.B, dl.Hq, dl.Hkv, dl.d, dl.S, dl.W, dl.k, pos_m) / len(pos_m)
+        kprime = dl.B * dl.Hq * (num_cand(L0 + calls * Mq // 2, dl.S, dl.W)) * (dl.d * 2 + 4)
+        us_call = float(np.mean(tm_)) * 1e3
+        res["decode_multi_512k"] = {
+            "queries_per_sequence": Mq, "calls": calls, "us_per_call": us_call,
+            "us_per_call_median": float(np.median(tm_)) * 1e3,
+            "us_per_token": us_call / (dl.B * Mq),
+            "single_query_us_per_token": avg["decode"] * 1e3 / dl.B,
+            "bytes_per_call": Mq * db1 - (Mq - 1) * kprime,
+            "hbm_frac": (Mq * db1 - (Mq - 1) * kprime) / (us_call * 1e-6) / PEAK_HBM,
+            "kernels_us": km_,
+            "note": "mean of 2 x %d calls (each: 4 tokens for each of the 4 sequences); bytes count the "
+                    "k' stream once per sequence" % calls}
     if not args.no_extra:
         log("128K backward")
         del ws_att

@@ -14,6 +14,9 @@ if the library is missing, loading raises.
                               dlse, dq, dk, dv, dq_hat, dk_sum, db_sum, shape, workspace=None)
     hils_summarize_backward(k, q_land, dk_sum, db_sum, dk, dq_land, shape, chunk_begin=0,
                             n_chunks=None)
+    hils_decode_multi(pos, n_queries, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache,
+                      k_sum, b_sum, out, lse, sel_idx, shape, workspace=None)
+    hils_decode_multi_workspace_bytes(shape, n_queries)
     hils_qcal(q, hs, w_down, w_up, q_hat, shape)
     hils_summarize_shared(k, q_shared, k_sum, b_sum, shape, chunk_begin=0, n_chunks=None)
     hils_bsa_select(q, k, sel_idx, shape, workspace=None)
@@ -45,6 +48,7 @@ STATUS = {
 EXPORTS = ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
            "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
            "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_summarize_shared",
+           "hils_decode_multi", "hils_decode_multi_workspace_bytes",
            "hils_workspace_bytes", "hils_status_string", "hils_abi_version",
            "hils_timing_enable", "hils_timing_get")
 
@@ -92,6 +96,9 @@ def lib():
         L.hils_selection_overlap.argtypes = [SP, P, P, P, P]
         L.hils_qcal.argtypes = [SP, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P]
         L.hils_summarize_shared.argtypes = [SP, P, P, I64, I64, P, P, P]
+        L.hils_decode_multi.argtypes = [SP, ctypes.c_int32, P] + [P] * 12 + [P, SZ, P]
+        L.hils_decode_multi_workspace_bytes.argtypes = [SP, ctypes.c_int32]
+        L.hils_decode_multi_workspace_bytes.restype = SZ
         L.hils_workspace_bytes.argtypes = [SP, ctypes.c_int]
         L.hils_workspace_bytes.restype = SZ
         L.hils_status_string.argtypes = [ctypes.c_int]
@@ -104,7 +111,8 @@ def lib():
         L.hils_timing_get.restype = ctypes.c_int
         for f in ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
                   "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
-                  "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_summarize_shared"):
+                  "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_summarize_shared",
+                  "hils_decode_multi"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -240,6 +248,24 @@ def hils_selection_overlap(idx_a, idx_b, count, shape: Shape):
                                                                   _p(idx_b), _p(count), _stream()))
 
 
+def hils_decode_multi_workspace_bytes(shape: Shape, n_queries: int) -> int:
+    return int(lib().hils_decode_multi_workspace_bytes(ctypes.byref(shape), int(n_queries)))
+
+
+def hils_decode_multi(pos, n_queries, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, k_sum,
+                      b_sum, out, lse, sel_idx, shape: Shape, workspace_t=None):
+    """n_queries adjacent new tokens per sequence at positions pos[b] .. pos[b] + n_queries - 1."""
+    _dev(q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, k_sum, b_sum, out, lse, sel_idx)
+    pos_arr = (ctypes.c_int64 * shape.batch)(*[int(p) for p in pos])
+    if workspace_t is None:
+        n = hils_decode_multi_workspace_bytes(shape, n_queries)
+        workspace_t = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check("hils_decode_multi", lib().hils_decode_multi(
+        ctypes.byref(shape), int(n_queries), pos_arr, _p(q), _p(q_hat), _p(k_new), _p(v_new),
+        _p(q_land_new), _p(k_cache), _p(v_cache), _p(k_sum), _p(b_sum), _p(out), _p(lse), _p(sel_idx),
+        _p(workspace_t), workspace_t.numel(), _stream()))
+
+
 def hils_decode_step_noalloc(pos, q, q_hat, k_new, v_new, q_land_new, k_cache, v_cache, k_sum,
                              b_sum, out, lse, sel_idx, shape: Shape):
     """hils_decode_step on the library's built-in scratch (no workspace, no allocation)."""
@@ -255,7 +281,7 @@ KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",
            "dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize",
            "v_transpose", "rank_keys", "topk_scores",
            "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "bwd_ksum", "summarize_bwd",
-           "bsa_keys", "bsa_topk", "qcal")
+           "bsa_keys", "bsa_topk", "qcal", "dec_append", "dec_gsel")
 
 
 def hils_timing_enable(kernels):

@@ -56,7 +56,10 @@ struct DecWs {
   int32_t* hid;       // [B, Hq, kMaxShares, kk] their chunk ids
   float* Lh;          // [B, Hq] each head's LSE over the candidates
   float* apart;       // [B, Hkv, nitems, G, D + 2]: items [0, kk) selected, [kk, kk + nwin) window
-  int nslice, sj, kk, nwin, nitems, mj;
+  // several queries per sequence (rows b*M + m of the arrays above):
+  float* mpart;       // [Breal, Hkv, nitems_mq, 16, D + 2]: union slots [0, M kk), then window chunks
+  int32_t* selw;      // [B, Hkv, kk] each row's selection (ascending, -1 pads)
+  int nslice, sj, kk, nwin, nitems, mj, nwin_mq, nitems_mq;
 };
 
 struct DecKArgs {
@@ -76,6 +79,8 @@ struct DecKArgs {
   int B, Hq, Hkv, S, W, topk;
   int64_t Lcap, NCcap;
   float scale;
+  int M;                // queries per sequence: rows b*M + m of q, q_hat, out, lse, pos
+  int32_t* idx_user;    // several queries: the caller's selection output (or null)
 };
 
 __device__ __forceinline__ void lse_merge(float& M, float& Z, float mo, float so) {
@@ -314,6 +319,90 @@ __device__ __forceinline__ int list_topk(const uint32_t (&keys)[J], int jn, int 
   return base;
 }
 
+// The slice's outputs for one query row (bh = its (row, head) index): the head's
+// LSE partial over the slice, the slice's top-k of s_hat (keys and chunk ids,
+// ascending chunk order) and its four largest keys.  sv[j]: the wave's s_hat of
+// candidate cw0 + 64 j + lane (-inf where absent).  AGAIN: another row follows
+// in the same workgroup (a closing barrier frees the LDS lists).
+template <int SJ, bool AGAIN = false>
+__device__ __forceinline__ void slice_lists(const DecKArgs& a, ListSmem& sm, int64_t bh, int slice, int64_t c0,
+                                            int64_t cw0, int64_t nc, const float (&sv)[SJ]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int kk = a.w.kk;
+  // the head's LSE partial of the slice (log2 units)
+  float mw = kNegInf;
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) mw = fmaxf(mw, sv[j] * kLog2e);
+  mw = wave_max(mw);
+  float zl = 0.f;
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) zl += sv[j] == kNegInf ? 0.f : hw_exp2(sv[j] * kLog2e - mw);
+  const float zw = wave_sum(zl);
+  // this wave's top-k of s_hat (ties: lower chunk), ascending chunk order
+  const int nvw = (int)max<int64_t>(0, min<int64_t>(nc - cw0, 64 * SJ));
+  uint32_t keys[SJ];
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) keys[j] = sv[j] == kNegInf ? 0u : order_key(sv[j]);
+  const int nl = list_topk<SJ>(keys, (nvw + 63) / 64, nvw, kk, lane, sm.sbuf[wave], sm.wpos[wave],
+                               sm.wkey[wave]);
+  if (lane == 0) {
+    sm.red[wave][0] = mw;
+    sm.red[wave][1] = zw;
+    sm.nw[wave] = nl;
+  }
+  __syncthreads();
+  if (wave == 0) {
+  if (lane == 0) {
+    float M = kNegInf, Z = 0.f;
+    for (int w = 0; w < 4; ++w) lse_merge(M, Z, sm.red[w][0], sm.red[w][1]);
+    a.w.lpart[bh * a.w.nslice + slice] = make_float2(M, Z);
+  }
+  // merge the four wave lists: entry e of wave w's list sits at position
+  // 64 jj + lane with w = LPJ jj + lane / TP, e = lane % TP (ascending chunk order)
+  const int TP = kk <= 16 ? 16 : (kk <= 32 ? 32 : 64);
+  const int LPJ = kWave / TP;
+  const int ml = lane / TP, me = lane % TP;
+  uint32_t mk[4];
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) tot += sm.nw[w];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int w = LPJ * jj + ml;
+    mk[jj] = (w < 4 && me < sm.nw[w]) ? sm.wkey[w][me] : 0u;
+  }
+  const int jn = (4 + LPJ - 1) / LPJ;
+  int32_t* mpos = sm.msel;
+  uint32_t* mkey = sm.sbuf[1];   // wave 1's buffer is free once the lists are merged
+  const int n = list_topk<4>(mk, jn, tot, kk, lane, sm.sbuf[0], mpos, mkey);
+  wave_lds_sync();
+  if (lane < kk) {
+    uint32_t key = 0u;
+    int32_t id = -1;
+    if (lane < n) {
+      const int ps = mpos[lane];
+      const int w = LPJ * (ps / 64) + (ps % 64) / TP, e = (ps % 64) % TP;
+      key = mkey[lane];
+      id = (int32_t)(c0 + (int64_t)w * 64 * SJ + sm.wpos[w][e]);
+    }
+    const int64_t o = (bh * a.w.nslice + slice) * kk + lane;
+    a.w.lkey[o] = key;
+    a.w.lid[o] = id;
+  }
+  // the slice's four largest keys: the selection prunes the lists with them
+  uint32_t x = lane < n ? mkey[lane] : 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t m = wave_max_u32(x);
+    if (lane == 0) a.w.lk4[(bh * a.w.nslice + slice) * 4 + r] = m;
+    const uint64_t at = __ballot(x == m && m != 0u);
+    if (at && lane == __ffsll((long long)at) - 1) x = 0u;
+  }
+  }
+  if constexpr (AGAIN) __syncthreads();   // the LDS lists are used again by the next row
+}
+
 // A slice of 256*SJ candidates of one (b, head): wave w streams candidates
 // [c0 + 64 SJ w, + 64 SJ) in SJ blocks of 64.  PPR lanes cover one k' row with
 // 16-byte pieces, so one load instruction reads RPI consecutive rows; each lane
@@ -403,75 +492,7 @@ __device__ __forceinline__ void score_slice(const DecKArgs& a, ListSmem& sm, int
       sv[j] = ok ? sc : kNegInf;
     }
   }
-  // the head's LSE partial of the slice (log2 units)
-  float mw = kNegInf;
-#pragma unroll
-  for (int j = 0; j < SJ; ++j) mw = fmaxf(mw, sv[j] * kLog2e);
-  mw = wave_max(mw);
-  float zl = 0.f;
-#pragma unroll
-  for (int j = 0; j < SJ; ++j) zl += sv[j] == kNegInf ? 0.f : hw_exp2(sv[j] * kLog2e - mw);
-  const float zw = wave_sum(zl);
-  // this wave's top-k of s_hat (ties: lower chunk), ascending chunk order
-  const int nvw = (int)max<int64_t>(0, min<int64_t>(nc - cw0, 64 * SJ));
-  uint32_t keys[SJ];
-#pragma unroll
-  for (int j = 0; j < SJ; ++j) keys[j] = sv[j] == kNegInf ? 0u : order_key(sv[j]);
-  const int nl = list_topk<SJ>(keys, (nvw + 63) / 64, nvw, kk, lane, sm.sbuf[wave], sm.wpos[wave],
-                               sm.wkey[wave]);
-  if (lane == 0) {
-    sm.red[wave][0] = mw;
-    sm.red[wave][1] = zw;
-    sm.nw[wave] = nl;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  if (lane == 0) {
-    float M = kNegInf, Z = 0.f;
-    for (int w = 0; w < 4; ++w) lse_merge(M, Z, sm.red[w][0], sm.red[w][1]);
-    a.w.lpart[bh * a.w.nslice + slice] = make_float2(M, Z);
-  }
-  // merge the four wave lists: entry e of wave w's list sits at position
-  // 64 jj + lane with w = LPJ jj + lane / TP, e = lane % TP (ascending chunk order)
-  const int TP = kk <= 16 ? 16 : (kk <= 32 ? 32 : 64);
-  const int LPJ = kWave / TP;
-  const int ml = lane / TP, me = lane % TP;
-  uint32_t mk[4];
-  int tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) tot += sm.nw[w];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const int w = LPJ * jj + ml;
-    mk[jj] = (w < 4 && me < sm.nw[w]) ? sm.wkey[w][me] : 0u;
-  }
-  const int jn = (4 + LPJ - 1) / LPJ;
-  int32_t* mpos = sm.msel;
-  uint32_t* mkey = sm.sbuf[1];   // wave 1's buffer is free once the lists are merged
-  const int n = list_topk<4>(mk, jn, tot, kk, lane, sm.sbuf[0], mpos, mkey);
-  wave_lds_sync();
-  if (lane < kk) {
-    uint32_t key = 0u;
-    int32_t id = -1;
-    if (lane < n) {
-      const int ps = mpos[lane];
-      const int w = LPJ * (ps / 64) + (ps % 64) / TP, e = (ps % 64) % TP;
-      key = mkey[lane];
-      id = (int32_t)(c0 + (int64_t)w * 64 * SJ + sm.wpos[w][e]);
-    }
-    const int64_t o = (bh * a.w.nslice + slice) * kk + lane;
-    a.w.lkey[o] = key;
-    a.w.lid[o] = id;
-  }
-  // the slice's four largest keys: the selection prunes the lists with them
-  uint32_t x = lane < n ? mkey[lane] : 0u;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t m = wave_max_u32(x);
-    if (lane == 0) a.w.lk4[(bh * a.w.nslice + slice) * 4 + r] = m;
-    const uint64_t at = __ballot(x == m && m != 0u);
-    if (at && lane == __ffsll((long long)at) - 1) x = 0u;
-  }
+  slice_lists<SJ>(a, sm, bh, slice, c0, cw0, nc, sv);
 }
 
 template <typename T, int D>
@@ -850,6 +871,472 @@ __global__ __launch_bounds__(64 * kFuseWaves) void dec_fuse_kernel(DecKArgs a) {
   if (a.lse && lane == 0) a.lse[(int64_t)b * a.Hq + h] = mx + __logf(z);
 }
 
+
+// ---------------------------------------------------------------- several queries
+// M adjacent queries per sequence (speculative or multi-token decoding; the
+// paper-body page's kernel design: adjacent queries attend the union of their
+// selected chunks, which fills the matrix tiles with M x G rows and loads each
+// chunk once for all of them).  Row v = b M + m is the prefill row
+// i = pos[b] + m: the M new key/value rows go to the caches first, every query
+// scores all its candidates (each k' row is read once for up to four queries of
+// a sequence), selection runs per row as for one query, and the attention takes
+// one workgroup per chunk of the union of the M selections of (b, group), the
+// M G (query, head) pairs as the 16 columns of the tiles, each column masked to
+// the chunks it selected (or, for window chunks, to its own window).
+
+// The new rows into the caches (one workgroup per (row, KV head)).
+template <typename T, int D>
+__global__ __launch_bounds__(64) void dec_append_kernel(DecKArgs a) {
+  constexpr int EPV = 16 / sizeof(T);
+  const int g = blockIdx.x, v = blockIdx.y;
+  const int br = v / a.M;
+  const int64_t row = (((int64_t)br * a.Hkv + g) * a.Lcap + a.pos.p[v]) * D;
+  const int64_t src = ((int64_t)v * a.Hkv + g) * D;
+  for (int p = threadIdx.x; p < D / EPV; p += 64) {
+    *reinterpret_cast<uint4*>(static_cast<T*>(a.kc) + row + p * EPV) =
+        *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k_new) + src + p * EPV);
+    *reinterpret_cast<uint4*>(static_cast<T*>(a.vc) + row + p * EPV) =
+        *reinterpret_cast<const uint4*>(static_cast<const T*>(a.v_new) + src + p * EPV);
+  }
+}
+
+// One chunk c of (b, group g) for every (query, head) column col = m G + hh of
+// the group's M G pairs: as attend_item, with the keys and values read from the
+// caches (rows past the group's last position read as zero), and each column's
+// tokens masked to its window (is_win) or to all of c when bit m of `member`
+// is set.  A column with no token gets log-weight -inf and a zero output.
+template <typename T, int D, int G>
+__device__ __forceinline__ void attend_item_mq(const DecKArgs& a, ItemSmem<T, D>& sm, int br, int g, int slot,
+                                               int64_t c, bool is_win, uint32_t member) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int KS = D / 32, MD = D / 16;
+  constexpr int PK = D / EPV, PV = kS / EPV;
+  constexpr int VPW = PK / 4;
+  constexpr int MDW = MD / 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r16 = lane % 16, grp = lane / 16;
+  const int M = a.M;
+  const bool hcol = r16 < M * G;
+  const int m = hcol ? r16 / G : 0, hh = r16 % G;
+  const int v = br * M + m;
+  const int64_t i = a.pos.p[v];
+  const int64_t lw = window_left(i, a.S, a.W);
+  const int64_t ilast = a.pos.p[br * M + M - 1];   // the group's last written row
+  const int64_t bg = (int64_t)br * a.Hkv + g;
+  const float sl2 = a.scale * kLog2e;
+  const T* kc = static_cast<const T*>(a.kc) + (bg * a.Lcap + c * kS) * D;
+  const T* vc = static_cast<const T*>(a.vc) + (bg * a.Lcap + c * kS) * D;
+  const int64_t j0 = c * kS;
+  const bool colon = hcol && (is_win || ((member >> m) & 1u));
+  Frag<T> kf[KS], bq[KS];
+  {
+    const int t = 16 * wave + r16;
+    const bool ok = j0 + t <= ilast;
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) {
+      if (ok) load_frag(kf[kq], kc + (int64_t)t * D + 8 * grp + 32 * kq);
+      else zero_frag(kf[kq]);
+    }
+  }
+  uint4 vr[VPW];
+  {
+    const bool ok = j0 + lane <= ilast;
+#pragma unroll
+    for (int t = 0; t < VPW; ++t)
+      vr[t] = ok ? *reinterpret_cast<const uint4*>(vc + (int64_t)lane * D + (wave * VPW + t) * EPV)
+                 : make_uint4(0u, 0u, 0u, 0u);
+  }
+  {
+    const T* qrow = static_cast<const T*>(a.q) + ((int64_t)v * a.Hq + g * G + hh) * D + 8 * grp;
+#pragma unroll
+    for (int kq = 0; kq < KS; ++kq) {
+      if (colon) load_frag(bq[kq], qrow + 32 * kq);
+      else zero_frag(bq[kq]);
+    }
+  }
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kq = 0; kq < KS; ++kq) mma(acc, kf[kq], bq[kq]);
+  float x[4], mx = kNegInf;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int64_t j = j0 + 16 * wave + 4 * grp + q4;
+    const bool ok = colon && (!is_win || (j >= lw && j <= i));
+    x[q4] = ok ? acc[q4] * sl2 : kNegInf;
+    mx = fmaxf(mx, x[q4]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  if (grp == 0) sm.red[0][wave][r16] = mx;
+#pragma unroll
+  for (int t = 0; t < VPW; ++t) {
+    const T* xv = reinterpret_cast<const T*>(&vr[t]);
+    const int d0 = (wave * VPW + t) * EPV;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) sm.vt[swz<PV>(d0 + e, lane / EPV) * EPV + lane % EPV] = xv[e];
+  }
+  __syncthreads();
+  const float mm = fmaxf(fmaxf(sm.red[0][0][r16], sm.red[0][1][r16]), fmaxf(sm.red[0][2][r16], sm.red[0][3][r16]));
+  float p[4], ps = 0.f;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    p[q4] = x[q4] == kNegInf ? 0.f : hw_exp2(x[q4] - mm);
+    ps += p[q4];
+  }
+  ps += __shfl_xor(ps, 16, kWave);
+  ps += __shfl_xor(ps, 32, kWave);
+  if (grp == 0) sm.red[1][wave][r16] = ps;
+  {
+    T* prow = sm.pt + r16 * kS + 16 * wave + 4 * grp;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) prow[q4] = from_f<T>(p[q4]);
+  }
+  __syncthreads();
+  const float l = (sm.red[1][0][r16] + sm.red[1][1][r16]) + (sm.red[1][2][r16] + sm.red[1][3][r16]);
+  f32x4_t o[MDW];
+#pragma unroll
+  for (int t = 0; t < MDW; ++t) {
+    const int md = wave + 4 * t;
+    o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < kS / 32; ++k2) {
+      Frag<T> af, pf;
+      load_frag_swz<PV>(af, sm.vt, 16 * md + r16, 8 * grp + 32 * k2);
+      load_frag(pf, sm.pt + r16 * kS + 8 * grp + 32 * k2);
+      mma(o[t], af, pf);
+    }
+  }
+  if (hcol) {
+    float* ap = a.w.mpart + ((bg * a.w.nitems_mq + slot) * 16 + r16) * (D + 2);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int t = 0; t < MDW; ++t)
+      *reinterpret_cast<float4*>(ap + 16 * (wave + 4 * t) + 4 * grp) =
+          make_float4(o[t][0] * inv, o[t][1] * inv, o[t][2] * inv, o[t][3] * inv);
+    if (wave == 0 && grp == 0) {
+      float lw_ = kNegInf;
+      if (l > 0.f)
+        lw_ = is_win ? (mm + hw_log2(l)) * kLn2
+                     : a.w.shat[((int64_t)v * a.Hq + g * G + hh) * a.NCcap + c];
+      ap[D] = lw_;
+    }
+  }
+  __syncthreads();   // the LDS tiles are free for the caller
+}
+
+// Scoring of up to four queries of one sequence per block: (b, query group mg,
+// head, slice); each k' row piece is loaded once and dotted with every query.
+// Window blocks follow: chunk lw(first query)/S + w of (b, group).
+template <typename T, int D, int SJ>
+union MScoreSmem {
+  ItemSmem<T, D> it;
+  struct {
+    ListSmem l;
+    float svs[4][kThreads * SJ];   // each query's s_hat of the slice
+  } s;
+};
+
+template <typename T, int D, int G, int SJ>
+__global__ __launch_bounds__(kThreads) void dec_mscore_kernel(DecKArgs a) {
+  __shared__ __align__(16) MScoreSmem<T, D, SJ> sm;
+  constexpr int MQ = 4;
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int PPR = D / EPV;
+  constexpr int RPI = kWave / PPR;
+  constexpr int NI = PPR;
+  const int Br = a.B / a.M;
+  const int nmg = (a.M + MQ - 1) / MQ;
+  const int nsb = Br * nmg * a.Hq * a.w.nslice;
+  if ((int)blockIdx.x >= nsb) {
+    const int x = (int)blockIdx.x - nsb;
+    const int w = x % a.w.nwin_mq;
+    const int g = (x / a.w.nwin_mq) % a.Hkv;
+    const int br = x / (a.w.nwin_mq * a.Hkv);
+    const int64_t cfirst = window_left(a.pos.p[br * a.M], a.S, a.W) / kS;
+    const int64_t clast = a.pos.p[br * a.M + a.M - 1] / kS;
+    if (cfirst + w > clast) return;
+    attend_item_mq<T, D, G>(a, sm.it, br, g, a.M * a.w.kk + w, cfirst + w, true, 0u);
+    return;
+  }
+  const int slice = (int)blockIdx.x % a.w.nslice;
+  const int h = ((int)blockIdx.x / a.w.nslice) % a.Hq;
+  const int mg = ((int)blockIdx.x / (a.w.nslice * a.Hq)) % nmg;
+  const int br = (int)blockIdx.x / (a.w.nslice * a.Hq * nmg);
+  const int m0 = mg * MQ;
+  const int mn = min(MQ, a.M - m0);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  int64_t ncm[MQ];
+#pragma unroll
+  for (int u = 0; u < MQ; ++u) ncm[u] = u < mn ? num_candidates(a.pos.p[br * a.M + m0 + u], a.S, a.W) : 0;
+  const int64_t nc = ncm[mn - 1];   // the group's last query has the most candidates
+  const int64_t c0 = (int64_t)slice * (kThreads * SJ);
+  if (c0 >= nc) return;
+  const int64_t bhr = (int64_t)br * a.Hq + h;   // k', b' of the real sequence
+  const int pc = lane % PPR, rg = lane / PPR;
+  float qv[MQ][EPV];
+#pragma unroll
+  for (int u = 0; u < MQ; ++u) {
+    const int v = br * a.M + m0 + min(u, mn - 1);
+    const uint4 q4 = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) +
+                                                    ((int64_t)v * a.Hq + h) * D + pc * EPV);
+    const T* t = reinterpret_cast<const T*>(&q4);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) qv[u][e] = to_f<T>(t[e]);
+  }
+  const int64_t cw0 = c0 + (int64_t)wave * 64 * SJ;
+  const T* kb = static_cast<const T*>(a.ksum) + (bhr * a.NCcap + cw0) * D + pc * EPV;
+  const int src = (lane % RPI) * PPR + lane / RPI;
+  float bv[SJ];
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) {
+    const int64_t c = cw0 + 64 * j + lane;
+    bv[j] = c < nc ? a.bsum[bhr * a.NCcap + c] : 0.f;
+  }
+  // loads in batches of NB, two batches ahead of the arithmetic (as score_slice)
+  constexpr int NB = NI >= 8 ? NI / 2 : NI;
+  constexpr int NBS = NI / NB;
+  constexpr int NBAT = NBS * SJ;
+  auto issue = [&](int qb, uint4 (&u)[NB]) {
+    const int j = qb / NBS, t0 = (qb % NBS) * NB;
+    const int64_t cb = cw0 + 64 * j;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const int row = RPI * (t0 + t) + rg;
+      u[t] = cb + row < nc ? *reinterpret_cast<const uint4*>(kb + (int64_t)(64 * j + row) * D)
+                           : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 buf[2][NB];
+  issue(0, buf[0]);
+  if (NBAT > 1) issue(1, buf[1]);
+  float sv[MQ][SJ];
+  float vacc[MQ][NI];
+#pragma unroll
+  for (int qb = 0; qb < NBAT; ++qb) {
+    const int t0 = (qb % NBS) * NB;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const T* xk = reinterpret_cast<const T*>(&buf[qb % 2][t]);
+      float kx[EPV];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) kx[e] = to_f<T>(xk[e]);
+#pragma unroll
+      for (int u = 0; u < MQ; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc = fmaf(qv[u][e], kx[e], acc);
+        vacc[u][t0 + t] = acc;
+      }
+    }
+    if (qb + 2 < NBAT) issue(qb + 2, buf[qb % 2]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (qb % NBS == NBS - 1) {   // a block of 64 rows is complete
+      const int j = qb / NBS;
+      const int64_t c = cw0 + 64 * j + lane;
+#pragma unroll
+      for (int u = 0; u < MQ; ++u) {
+        float w[NI];
+#pragma unroll
+        for (int t = 0; t < NI; ++t) w[t] = vacc[u][t];
+        butterfly<PPR / 2, NI>(w, lane);
+        const float dot = __shfl(w[0], src, kWave);
+        const bool ok = u < mn && c < ncm[u];
+        const float sc = fmaf(dot, a.scale, bv[j]);
+        if (ok) a.w.shat[((int64_t)(br * a.M + m0 + u) * a.Hq + h) * a.NCcap + c] = sc;
+        sv[u][j] = ok ? sc : kNegInf;
+      }
+    }
+  }
+  // each query's slice outputs from one wave: wave u takes query u's s_hat of the
+  // whole slice (through LDS) and forms its LSE partial, its top-k list
+  // (ascending chunk order, ties to the lower chunk) and its four largest keys
+#pragma unroll
+  for (int u = 0; u < MQ; ++u)
+#pragma unroll
+    for (int j = 0; j < SJ; ++j) sm.s.svs[u][(int)(cw0 - c0) + 64 * j + lane] = sv[u][j];
+  __syncthreads();
+  const int u = wave;
+  if (u >= mn || c0 >= ncm[u]) return;
+  const int64_t bh = (int64_t)(br * a.M + m0 + u) * a.Hq + h;
+  const int kk = a.w.kk;
+  constexpr int JS = 4 * SJ;
+  float x[JS];
+#pragma unroll
+  for (int jj = 0; jj < JS; ++jj) x[jj] = sm.s.svs[u][64 * jj + lane];
+  float mw = kNegInf;
+#pragma unroll
+  for (int jj = 0; jj < JS; ++jj) mw = fmaxf(mw, x[jj] * kLog2e);
+  mw = wave_max(mw);
+  float zl = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < JS; ++jj) zl += x[jj] == kNegInf ? 0.f : hw_exp2(x[jj] * kLog2e - mw);
+  const float zw = wave_sum(zl);
+  if (lane == 0) a.w.lpart[bh * a.w.nslice + slice] = make_float2(mw, zw);
+  const int nv = (int)min<int64_t>(ncm[u] - c0, kThreads * SJ);
+  uint32_t keys[JS];
+#pragma unroll
+  for (int jj = 0; jj < JS; ++jj) keys[jj] = x[jj] == kNegInf ? 0u : order_key(x[jj]);
+  const int n = list_topk<JS>(keys, (nv + 63) / 64, nv, kk, lane, sm.s.l.sbuf[u], sm.s.l.wpos[u],
+                              sm.s.l.wkey[u]);
+  wave_lds_sync();
+  if (lane < kk) {
+    const int64_t o = (bh * a.w.nslice + slice) * kk + lane;
+    a.w.lkey[o] = lane < n ? sm.s.l.wkey[u][lane] : 0u;
+    a.w.lid[o] = lane < n ? (int32_t)(c0 + sm.s.l.wpos[u][lane]) : -1;
+  }
+  uint32_t y = lane < n ? sm.s.l.wkey[u][lane] : 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t mk = wave_max_u32(y);
+    if (lane == 0) a.w.lk4[(bh * a.w.nslice + slice) * 4 + r] = mk;
+    const uint64_t at = __ballot(y == mk && mk != 0u);
+    if (at && lane == __ffsll((long long)at) - 1) y = 0u;
+  }
+}
+
+// Each row's group selection (one workgroup per (KV head, row)).
+template <int G>
+__global__ __launch_bounds__(kThreads) void dec_gsel_kernel(DecKArgs a) {
+  __shared__ GroupSelSmem sel;
+  extern __shared__ uint32_t bitmap[];
+  const int g = blockIdx.x, v = blockIdx.y;
+  DecKArgs k = a;
+  k.idx_out = a.w.selw;   // slot 0 of group_select writes the selection here
+  group_select<G>(k, sel, bitmap, v, g, 0);
+  if (a.idx_user)
+    for (int t = threadIdx.x; t < a.topk; t += kThreads)
+      a.idx_user[((int64_t)v * a.Hkv + g) * a.topk + t] = sel.chosen[t];
+}
+
+// Union attention: workgroup (uslot, g, b) attends the uslot-th chunk (in
+// ascending order) of the union of the M rows' selections, for the columns of
+// the rows that selected it.  Slots past the union write -inf log-weights.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kThreads) void dec_uattend_kernel(DecKArgs a) {
+  __shared__ __align__(16) ItemSmem<T, D> it;
+  __shared__ int32_t ulist[16 * 64];
+  __shared__ int32_t scan[4];
+  __shared__ uint32_t member;
+  extern __shared__ uint32_t bitmap[];
+  const int uslot = blockIdx.x, g = blockIdx.y, br = blockIdx.z;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int M = a.M, kk = a.topk;
+  const int64_t ncmax = num_candidates(a.pos.p[br * M + M - 1], a.S, a.W);
+  const int nwords = (int)((ncmax + 31) / 32);
+  for (int t = threadIdx.x; t < nwords; t += kThreads) bitmap[t] = 0u;
+  if (threadIdx.x == 0) member = 0u;
+  __syncthreads();
+  for (int t = threadIdx.x; t < M * kk; t += kThreads) {
+    const int32_t c = a.w.selw[(((int64_t)br * M + t / kk) * a.Hkv + g) * kk + t % kk];
+    if (c >= 0) atomicOr(&bitmap[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
+  // ascending list of the union (block prefix count over the words)
+  const int wpt = (nwords + kThreads - 1) / kThreads;
+  const int w0 = min(nwords, (int)threadIdx.x * wpt), w1 = min(w0 + wpt, nwords);
+  int cnt = 0;
+  for (int t = w0; t < w1; ++t) cnt += __popc(bitmap[t]);
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) scan[wave] = incl;
+  __syncthreads();
+  int pos = incl - cnt, nu = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / kWave; ++w) {
+    pos += w < wave ? scan[w] : 0;
+    nu += scan[w];
+  }
+  for (int t = w0; t < w1; ++t) {
+    uint32_t mbits = bitmap[t];
+    while (mbits) {
+      const int bit = __ffs(mbits) - 1;
+      mbits &= mbits - 1u;
+      ulist[pos++] = t * 32 + bit;
+    }
+  }
+  __syncthreads();
+  const int64_t bg = (int64_t)br * a.Hkv + g;
+  if (uslot >= nu) {   // past the union: no weight for any column
+    if (threadIdx.x < 16) a.w.mpart[((bg * a.w.nitems_mq + uslot) * 16 + threadIdx.x) * (D + 2) + D] = kNegInf;
+    return;
+  }
+  const int32_t c = ulist[uslot];
+  for (int t = threadIdx.x; t < M * kk; t += kThreads)
+    if (a.w.selw[(((int64_t)br * M + t / kk) * a.Hkv + g) * kk + t % kk] == c) atomicOr(&member, 1u << (t / kk));
+  __syncthreads();
+  attend_item_mq<T, D, G>(a, it, br, g, uslot, c, false, member);
+}
+
+// Fusion of one (row, head): the union slots it selected and its window chunks,
+// weighted by exp(log-weight) (-inf: no weight).
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64 * kFuseWaves) void dec_mfuse_kernel(DecKArgs a) {
+  constexpr int DPL = D / kWave;
+  __shared__ float red[kFuseWaves][D];
+  __shared__ float mz[kFuseWaves][2];
+  const int h = blockIdx.x, v = blockIdx.y;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int M = a.M;
+  const int br = v / M, m = v % M;
+  const int g = h / G, col = m * G + h % G;
+  const int64_t cfirst = window_left(a.pos.p[br * M], a.S, a.W) / kS;
+  const int64_t clast = a.pos.p[br * M + M - 1] / kS;
+  const int nu = M * a.topk;
+  const int nitems = nu + (int)(clast - cfirst + 1);
+  const int64_t bg = (int64_t)br * a.Hkv + g;
+  const float* ap = a.w.mpart + (bg * a.w.nitems_mq * 16 + col) * (D + 2);
+  auto slot_of = [&](int x) { return x < nu ? x : M * a.w.kk + (x - nu); };
+  auto lwt = [&](int x) { return ap[(int64_t)slot_of(x) * 16 * (D + 2) + D]; };
+  float mx = kNegInf;
+  for (int x = threadIdx.x; x < nitems; x += 64 * kFuseWaves) mx = fmaxf(mx, lwt(x));
+  mx = wave_max(mx);
+  if (lane == 0) mz[wave][0] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kFuseWaves; ++w) mx = fmaxf(mx, mz[w][0]);
+  float zs = 0.f;
+  for (int x = threadIdx.x; x < nitems; x += 64 * kFuseWaves) {
+    const float l = lwt(x);
+    zs += l == kNegInf ? 0.f : __expf(l - mx);
+  }
+  zs = wave_sum(zs);
+  if (lane == 0) mz[wave][1] = zs;
+  float res[DPL];
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) res[t] = 0.f;
+  for (int x = wave; x < nitems; x += kFuseWaves) {
+    const float l = lwt(x);
+    if (l == kNegInf) continue;   // wave-uniform: one item per wave
+    const float w = __expf(l - mx);
+    const float* pp = ap + (int64_t)slot_of(x) * 16 * (D + 2) + lane * DPL;
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) res[t] = fmaf(w, pp[t], res[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) red[wave][lane * DPL + t] = res[t];
+  __syncthreads();
+  if (wave != 0) return;
+  float z = 0.f;
+#pragma unroll
+  for (int w = 0; w < kFuseWaves; ++w) z += mz[w][1];
+  const float inv = 1.f / z;
+  T* orow = static_cast<T*>(a.out) + ((int64_t)v * a.Hq + h) * D;
+#pragma unroll
+  for (int t = 0; t < DPL; ++t) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFuseWaves; ++w) acc += red[w][lane * DPL + t];
+    orow[lane * DPL + t] = from_f<T>(acc * inv);
+  }
+  if (a.lse && lane == 0) a.lse[(int64_t)v * a.Hq + h] = mx + __logf(z);
+}
+
 // ---------------------------------------------------------------- host side
 template <typename T, int D, int G, int SJ>
 hipError_t launch_score_sj(const DecKArgs& k, hipStream_t st) {
@@ -907,6 +1394,52 @@ hipError_t launch_decode_t(const DecKArgs& k, hipStream_t st) {
   }
 }
 
+template <typename T, int D, int G, int SJ>
+hipError_t launch_mscore_sj(const DecKArgs& k, int Br, hipStream_t st) {
+  const int nmg = (k.M + 3) / 4;
+  const int nsb = Br * nmg * k.Hq * k.w.nslice;
+  const int nwb = Br * k.Hkv * k.w.nwin_mq;
+  KTimer tm(K_DEC_SCORE, st);
+  hipLaunchKernelGGL((dec_mscore_kernel<T, D, G, SJ>), dim3((unsigned)(nsb + nwb)), dim3(kThreads), 0, st, k);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int G>
+hipError_t launch_mq_tg(const DecKArgs& k, int Br, hipStream_t st) {
+  {
+    KTimer tm(K_DEC_APPEND, st);
+    hipLaunchKernelGGL((dec_append_kernel<T, D>), dim3(k.Hkv, k.B), dim3(64), 0, st, k);
+  }
+  hipError_t e = k.w.sj == 1 ? launch_mscore_sj<T, D, G, 1>(k, Br, st) : launch_mscore_sj<T, D, G, 2>(k, Br, st);
+  if (e != hipSuccess) return e;
+  if (k.topk > 0) {
+    e = launch_headsel(k, st);
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)((k.NCcap + 31) / 32) * 4;
+    {
+      KTimer tm(K_DEC_GSEL, st);
+      hipLaunchKernelGGL((dec_gsel_kernel<G>), dim3(k.Hkv, k.B), dim3(kThreads), lds, st, k);
+    }
+    KTimer tm(K_DEC_ATTEND, st);
+    hipLaunchKernelGGL((dec_uattend_kernel<T, D, G>), dim3(k.M * k.topk, k.Hkv, Br), dim3(kThreads), lds, st, k);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  KTimer tm(K_DEC_FUSE, st);
+  hipLaunchKernelGGL((dec_mfuse_kernel<T, D, G>), dim3(k.Hq, k.B), dim3(64 * kFuseWaves), 0, st, k);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_mq_t(const DecKArgs& k, int Br, hipStream_t st) {
+  switch (k.Hq / k.Hkv) {
+    case 1: return launch_mq_tg<T, D, 1>(k, Br, st);
+    case 2: return launch_mq_tg<T, D, 2>(k, Br, st);
+    case 4: return launch_mq_tg<T, D, 4>(k, Br, st);
+    default: return launch_mq_tg<T, D, 8>(k, Br, st);
+  }
+}
+
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Candidates of the last cache row (the most any step can see).
@@ -927,7 +1460,8 @@ void plan(int64_t NCcap, int kk, int* sj, int* mj, int* nslice) {
   *nslice = (int)(ns > 0 ? ns : 1);
 }
 
-void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk, DecWs* w,
+// B: sequences; M: queries per sequence (rows B M of the per-row arrays).
+void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk, int M, DecWs* w,
             size_t* total, char* base) {
   const int64_t NCcap = Lcap / S;
   const int kk = topk > 0 ? topk : 1;
@@ -935,7 +1469,11 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
   plan(NCcap, kk, &sj, &mj, &nslice);
   const int nwin = W / S + 2;
   const int nitems = kk + nwin;
+  const int nwin_mq = W / S + 3;   // the union of M <= S windows spans one chunk more
+  const int nitems_mq = M * kk + nwin_mq;
   const int G = Hq / Hkv;
+  const int Br = B;
+  B *= M;
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += a256(bytes); return p; };
   DecWs d{};
@@ -947,13 +1485,20 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
   d.hkey = reinterpret_cast<uint32_t*>(take((size_t)B * Hq * kMaxShares * kk * 4));
   d.hid = reinterpret_cast<int32_t*>(take((size_t)B * Hq * kMaxShares * kk * 4));
   d.Lh = reinterpret_cast<float*>(take((size_t)B * Hq * 4));
-  d.apart = reinterpret_cast<float*>(take((size_t)B * Hkv * nitems * G * (D + 2) * 4));
+  if (M == 1) {
+    d.apart = reinterpret_cast<float*>(take((size_t)B * Hkv * nitems * G * (D + 2) * 4));
+  } else {
+    d.mpart = reinterpret_cast<float*>(take((size_t)Br * Hkv * nitems_mq * 16 * (D + 2) * 4));
+    d.selw = reinterpret_cast<int32_t*>(take((size_t)B * Hkv * kk * 4));
+  }
   d.nslice = nslice;
   d.sj = sj;
   d.mj = mj;
   d.kk = kk;
   d.nwin = nwin;
   d.nitems = nitems;
+  d.nwin_mq = nwin_mq;
+  d.nitems_mq = nitems_mq;
   if (w) *w = d;
   if (total) *total = off + 256;
 }
@@ -968,14 +1513,16 @@ bool decode_supported(int64_t Lcap, int S, int W, int topk, int G) {
   return sj > 0 && topk + W / S + 2 <= 256 && (Lcap / S + 31) / 32 * 4 <= 16384;
 }
 
-size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk) {
+size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk, int M) {
   size_t t = 0;
-  layout(B, Hq, Hkv, Lcap, S, W, D, topk, nullptr, &t, nullptr);
+  layout(B, Hq, Hkv, Lcap, S, W, D, topk, M, nullptr, &t, nullptr);
   return t;
 }
 
 hipError_t launch_decode(const DecArgs& d, hipStream_t st) {
+  if (d.M > 1) return launch_decode_multi(d, st);
   DecKArgs k{};
+  k.M = 1;
   for (int b = 0; b < d.B; ++b) k.pos.p[b] = d.pos[b];
   k.q = d.q; k.qh = d.qh; k.k_new = d.k_new; k.v_new = d.v_new;
   k.kc = d.kc; k.vc = d.vc; k.ksum = d.ksum; k.bsum = d.bsum;
@@ -983,7 +1530,7 @@ hipError_t launch_decode(const DecArgs& d, hipStream_t st) {
   k.B = d.B; k.Hq = d.Hq; k.Hkv = d.Hkv; k.S = d.S; k.W = d.W; k.topk = d.topk;
   k.Lcap = d.Lcap; k.NCcap = d.Lcap / d.S; k.scale = d.scale;
   char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(d.ws) + 255) & ~(uintptr_t)255);
-  layout(d.B, d.Hq, d.Hkv, d.Lcap, d.S, d.W, d.D, d.topk, &k.w, nullptr, base);
+  layout(d.B, d.Hq, d.Hkv, d.Lcap, d.S, d.W, d.D, d.topk, 1, &k.w, nullptr, base);
   hipError_t e;
   if (d.bf16) e = d.D == 128 ? launch_decode_t<bf16_t, 128>(k, st) : launch_decode_t<bf16_t, 64>(k, st);
   else e = d.D == 128 ? launch_decode_t<float, 128>(k, st) : launch_decode_t<float, 64>(k, st);
@@ -995,6 +1542,45 @@ hipError_t launch_decode(const DecArgs& d, hipStream_t st) {
       s.list.b[s.list.n] = b;
       s.list.c[s.list.n] = d.pos[b] / d.S;
       ++s.list.n;
+    }
+  }
+  if (s.list.n > 0) {
+    s.k = d.kc; s.ql = d.ql_new; s.ksum = d.ksum; s.bsum = d.bsum;
+    s.B = d.B; s.Hq = d.Hq; s.Hkv = d.Hkv; s.D = d.D; s.bf16 = d.bf16;
+    s.kT = d.Lcap; s.NCs = d.Lcap / d.S;
+    s.ql_sb = (int64_t)d.Hq * d.D; s.ql_sh = d.D; s.ql_sc = 0;
+    s.scale = d.scale;
+    e = launch_summarize(s, st);
+  }
+  return e;
+}
+
+hipError_t launch_decode_multi(const DecArgs& d, hipStream_t st) {
+  DecKArgs k{};
+  const int M = d.M;
+  for (int b = 0; b < d.B; ++b)
+    for (int m = 0; m < M; ++m) k.pos.p[b * M + m] = d.pos[b] + m;
+  k.q = d.q; k.qh = d.qh; k.k_new = d.k_new; k.v_new = d.v_new;
+  k.kc = d.kc; k.vc = d.vc; k.ksum = d.ksum; k.bsum = d.bsum;
+  k.out = d.out; k.lse = d.lse; k.idx_out = nullptr; k.idx_user = d.idx;
+  k.B = d.B * M; k.Hq = d.Hq; k.Hkv = d.Hkv; k.S = d.S; k.W = d.W; k.topk = d.topk;
+  k.Lcap = d.Lcap; k.NCcap = d.Lcap / d.S; k.scale = d.scale;
+  k.M = M;
+  char* base = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(d.ws) + 255) & ~(uintptr_t)255);
+  layout(d.B, d.Hq, d.Hkv, d.Lcap, d.S, d.W, d.D, d.topk, M, &k.w, nullptr, base);
+  hipError_t e;
+  if (d.bf16) e = d.D == 128 ? launch_mq_t<bf16_t, 128>(k, d.B, st) : launch_mq_t<bf16_t, 64>(k, d.B, st);
+  else e = d.D == 128 ? launch_mq_t<float, 128>(k, d.B, st) : launch_mq_t<float, 64>(k, d.B, st);
+  if (e != hipSuccess) return e;
+  // summaries of chunks completed by these tokens (at most one per sequence: M <= S)
+  SumArgs s{};
+  for (int b = 0; b < d.B; ++b) {
+    for (int m = 0; m < M; ++m) {
+      if ((d.pos[b] + m + 1) % d.S == 0) {
+        s.list.b[s.list.n] = b;
+        s.list.c[s.list.n] = (d.pos[b] + m) / d.S;
+        ++s.list.n;
+      }
     }
   }
   if (s.list.n > 0) {

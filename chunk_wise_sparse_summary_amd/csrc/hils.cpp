@@ -354,4 +354,52 @@ hils_status hils_summarize_backward(const hils_shape* s, const void* k, const vo
   return from_hip(hils::launch_summarize_backward(a, stream));
 }
 
+size_t hils_decode_multi_workspace_bytes(const hils_shape* s, int32_t n_queries) {
+  if (check_shape(s, kDecode) != HILS_OK) return 0;
+  const int G = s->heads_q / s->heads_kv;
+  if (n_queries < 1 || n_queries > 16 || n_queries * G > 16 || n_queries > s->window ||
+      s->batch * n_queries > 64)
+    return 0;
+  return hils::decode_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk, s->window,
+                                s->head_dim, s->top_k, n_queries);
+}
+
+hils_status hils_decode_multi(const hils_shape* s, int32_t n_queries, const int64_t* pos, const void* q,
+                              const void* q_hat, const void* k_new, const void* v_new,
+                              const void* q_land_new, void* k_cache, void* v_cache, void* k_sum,
+                              float* b_sum, void* out, float* lse, int32_t* sel_idx, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  const hils_status st = check_shape(s, kDecode);
+  if (st != HILS_OK) return st;
+  const int G = s->heads_q / s->heads_kv;
+  const int M = n_queries;
+  if (M < 1 || M > 16 || M > s->window) return HILS_E_SHAPE;
+  if (M * G > 16 || s->batch * M > 64) return HILS_E_UNSUPPORTED;
+  if (!pos || !q || !q_hat || !k_new || !v_new || !k_cache || !v_cache || !k_sum || !b_sum || !out)
+    return HILS_E_NULL;
+  if (!aligned16(q) || !aligned16(q_hat) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned16(q_land_new) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_sum) ||
+      !aligned16(b_sum) || !aligned16(out) || !aligned16(lse) || !aligned16(sel_idx))
+    return HILS_E_ALIGN;
+  bool completes = false;
+  for (int b = 0; b < s->batch; ++b) {
+    if (pos[b] < 0 || pos[b] + M > s->seq_len) return HILS_E_POS;
+    for (int m = 0; m < M; ++m)
+      if ((pos[b] + m + 1) % s->chunk == 0) completes = true;
+  }
+  if (completes && !q_land_new) return HILS_E_NEED_QLAND;
+  const size_t need = hils::decode_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
+                                             s->window, s->head_dim, s->top_k, M);
+  if (!ws || ws_bytes < need) return HILS_E_WORKSPACE;
+  hils::DecArgs a{};
+  a.pos = pos; a.q = q; a.qh = q_hat; a.k_new = k_new; a.v_new = v_new; a.ql_new = q_land_new;
+  a.kc = k_cache; a.vc = v_cache; a.ksum = k_sum; a.bsum = b_sum; a.out = out; a.lse = lse;
+  a.idx = sel_idx;
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
+  a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
+  a.Lcap = s->seq_len; a.scale = eff_scale(s); a.ws = ws; a.ws_bytes = ws_bytes;
+  a.M = M;
+  return from_hip(M == 1 ? hils::launch_decode(a, stream) : hils::launch_decode_multi(a, stream));
+}
+
 }  // extern "C"

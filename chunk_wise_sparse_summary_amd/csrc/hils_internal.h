@@ -176,8 +176,10 @@ struct DecArgs {
   float scale;
   void* ws;
   size_t ws_bytes;
+  int M = 1;           // queries per sequence (positions pos[b] .. pos[b] + M - 1)
 };
 hipError_t launch_decode(const DecArgs& a, hipStream_t st);
+hipError_t launch_decode_multi(const DecArgs& a, hipStream_t st);
 
 // Optional per-kernel timing (the C ABI's hils_timing_* calls): a KTimer around
 // a launch records a HIP event pair on the launch stream when that kernel is
@@ -187,7 +189,7 @@ enum KernelId {
   K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_DEC_SCORE, K_DEC_SELECT,
   K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_RANK_KEYS, K_TOPK_SCORES,
   K_BWD_ROWSTAT, K_BWD_KV, K_BWD_DQ, K_BWD_QHAT, K_BWD_KSUM, K_SUM_BWD, K_BSA_KEYS, K_BSA_TOPK,
-  K_QCAL, K_COUNT
+  K_QCAL, K_DEC_APPEND, K_DEC_GSEL, K_COUNT
 };
 class KTimer {
  public:
@@ -201,7 +203,7 @@ class KTimer {
   hipStream_t st_;
   hipEvent_t e0_;
 };
-size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk);
+size_t decode_workspace(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk, int M = 1);
 // Whether the decode selection can merge its per-span lists in one wave.
 bool decode_supported(int64_t Lcap, int S, int W, int topk, int G);
 

@@ -12,6 +12,7 @@
  *   hils_select       retrieval scores and top-k chunk selection
  *   hils_attend_fuse  per-group attention and the fusion
  *   hils_decode_step  all of the above for one new token per sequence
+ *   hils_decode_multi the same for several adjacent new tokens per sequence
  *
  * and the gradients of the prefill path in two more:
  *
@@ -352,6 +353,40 @@ hils_status hils_bsa_select(const hils_shape* shape, const void* q, const void* 
 hils_status hils_selection_overlap(const hils_shape* shape, const int32_t* idx_a, const int32_t* idx_b,
                                    int32_t* count, hipStream_t stream);
 
+/*
+ * Several adjacent queries per sequence in one step: speculative or multi-token
+ * decoding (paper-body page, implementation, kernel design: adjacent queries
+ * attend the union of their selected chunks, which fills the matrix tiles with
+ * M x G rows and loads each chunk once; the summary page's practical
+ * enhancements).  For each b the n_queries = M new tokens sit at positions
+ * pos[b] + m (m < M); token m is exactly the prefill row i = pos[b] + m of the
+ * definitions above, so it sees the earlier new tokens of its sequence:
+ *   1. write k_new, v_new row m into cache row pos[b] + m;
+ *   2. for each m: select over C_i (as hils_select), attend and fuse (as
+ *      hils_attend_fuse) over the cache rows <= i;
+ *   3. summarise the chunk completed by these tokens, if any (at most one per
+ *      sequence), with q_land_new[b] (as hils_decode_step).
+ * Every k' row is read once for up to four queries of a sequence, and each chunk
+ * of the union of a (b, group)'s M selections is attended once for all M G
+ * (query, head) pairs.
+ * q, q_hat [B, M, Hq, d]; k_new, v_new [B, M, Hkv, d]; q_land_new [B, Hq, d] or NULL
+ * (io_dtype); caches, k_sum, b_sum as hils_decode_step;
+ * out [B, M, Hq, d] io_dtype; lse [B, M, Hq] fp32 or NULL; sel_idx [B, M, Hkv, k] or NULL.
+ * Requires 1 <= M <= min(16, W) (else HILS_E_SHAPE), M G <= 16 and B M <= 64 (else
+ * HILS_E_UNSUPPORTED), pos[b] + M <= cache capacity (else HILS_E_POS), the same
+ * shape limits as hils_decode_step; workspace hils_decode_multi_workspace_bytes().
+ * M = 1 runs hils_decode_step.
+ */
+hils_status hils_decode_multi(const hils_shape* shape, int32_t n_queries, const int64_t* pos,
+                              const void* q, const void* q_hat, const void* k_new, const void* v_new,
+                              const void* q_land_new, void* k_cache, void* v_cache, void* k_sum,
+                              float* b_sum, void* out, float* lse, int32_t* sel_idx,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of hils_decode_multi for `shape` and n_queries (0 when either
+ * is outside its limits). */
+size_t hils_decode_multi_workspace_bytes(const hils_shape* shape, int32_t n_queries);
+
 /* Workspace bytes `op` needs for `shape` (0 for HILS_OP_SUMMARIZE); 0 as well
  * for an invalid shape. */
 size_t hils_workspace_bytes(const hils_shape* shape, hils_op op);
@@ -377,7 +412,9 @@ int hils_abi_version(void);
  *   completed by a decode step), v_transpose, rank_keys,
  *   topk_scores, for the backward calls bwd_rowstat, bwd_kv, bwd_dq,
  *   bwd_qhat, bwd_ksum and summarize_bwd (the entry lists of the
- *   backward count under the idx_* names), bsa_keys, bsa_topk, and qcal.  HILS_E_UNSUPPORTED for an unknown name
+ *   backward count under the idx_* names), bsa_keys, bsa_topk, qcal, and
+ *   for hils_decode_multi dec_append and dec_gsel (its other kernels count
+ *   under the dec_* names above).  HILS_E_UNSUPPORTED for an unknown name
  *   (timing is then left off).
  * hils_timing_get(kernel, total_ms, launches): waits for the recorded events
  *   of that kernel and returns the summed duration and the number of timed
