@@ -157,3 +157,37 @@ def test_backward_validation():
                                      None) == 0
     assert L.hils_summarize_backward(ctypes.byref(s), P(0), P(16), P(16), P(16), 0, 1, P(16), P(16),
                                      None) == -1
+
+
+def _nc(i, S, W):
+    a = i - W + 1
+    return 0 if a <= 0 else a // S
+
+
+@pytest.mark.parametrize("T", [37, 64, 150, 192, 1000])
+def test_short_sequences_tile_and_workspace_math(T):
+    """Host model of the selection kernels' summary-row reads for short sequences
+    (no complete chunk, or no candidate anywhere): a workgroup whose queries have
+    no candidate reads no k' row, and every row read lies in [0, T/S).  Before
+    the guard that skips the prefetch when a block has no candidate, the clamp
+    min(c0 + row, nc_block - 1) reached row -1, i.e. just before k_sum, or any
+    row of an empty k_sum when T < S.  Also: the workspace sizes of every
+    prefill call are defined for these shapes."""
+    S, W = 64, 128
+    NCs = T // S
+    for rows_per_block in (256, 64):            # score_lse, rank_keys query blocks
+        for qb in range(0, T, rows_per_block):
+            nc_block = _nc(min(qb + rows_per_block - 1, T - 1), S, W)
+            assert nc_block <= NCs
+            if nc_block == 0:
+                continue                         # no fetch at all
+            cl_last = nc_block - 1
+            for c0 in range(0, nc_block, 16):
+                for row in range(16):
+                    cl = min(c0 + row, cl_last)
+                    assert 0 <= cl < NCs, (T, qb, c0, row)
+    for i in range(T):                           # per-query reads c < nc(i)
+        assert _nc(i, S, W) <= NCs
+    s = _shape(B=1, Hq=4, Hkv=2, d=64, T=T, k=2, W=W)
+    for op in (hils.OP_SELECT, hils.OP_ATTEND_FUSE, hils.OP_ATTEND_BACKWARD):
+        assert hils.hils_workspace_bytes(s, op) > 0
