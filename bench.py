@@ -164,13 +164,14 @@ def source_digest(files):
 # includes): a change to any voids its stored counters.
 _CSRC = "chunk_wise_sparse_summary_amd/csrc/"
 _HDRS = [_CSRC + h for h in ("hils_common.h", "hils_internal.h", "topk.h")]
+_TILES = [_CSRC + "attend_tiles.h"]
 KERNEL_SOURCES = {
     "summarize": [_CSRC + "summarize.hip"] + _HDRS,
-    "score_lse": [_CSRC + "select.hip"] + _HDRS,
-    "rank_keys": [_CSRC + "select.hip"] + _HDRS,
-    "topk_scores": [_CSRC + "select.hip"] + _HDRS,
-    "window": [_CSRC + "attend.hip"] + _HDRS,
-    "chunk_attend": [_CSRC + "attend.hip"] + _HDRS,
+    "score_lse": [_CSRC + "select.hip"] + _TILES + _HDRS,
+    "rank_keys": [_CSRC + "select.hip"] + _TILES + _HDRS,
+    "topk_scores": [_CSRC + "select.hip"] + _TILES + _HDRS,
+    "window": [_CSRC + "attend.hip"] + _TILES + _HDRS,
+    "chunk_attend": [_CSRC + "attend.hip"] + _TILES + _HDRS,
 }
 
 
