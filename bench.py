@@ -437,7 +437,7 @@ def time_decode_multi(hils, wl, cache, shape, ks, bs, M, calls, nrep=2, warm=4):
 
 
 BWD_KERNELS = ["idx_count", "idx_scan_tiles", "idx_scan_buckets", "idx_fill", "bwd_rowstat", "bwd_kv",
-               "bwd_dq", "bwd_qhat", "bwd_ksum", "summarize_bwd"]
+               "bwd_dq", "bwd_qhat", "summarize_bwd"]
 
 
 def time_backward(hils, x, fwd, shape, reps=3):

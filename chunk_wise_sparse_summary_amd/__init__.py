@@ -280,7 +280,7 @@ KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",
            "idx_scan_buckets", "idx_fill", "lsel", "window", "chunk_attend",
            "dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize",
            "v_transpose", "rank_keys", "topk_scores",
-           "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "bwd_ksum", "summarize_bwd",
+           "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "summarize_bwd",
            "bsa_keys", "bsa_topk", "qcal", "dec_append", "dec_gsel")
 
 

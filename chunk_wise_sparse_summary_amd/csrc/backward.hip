@@ -17,13 +17,14 @@
 //   bwd_rowstat  D per row.
 //   bwd_kv       key-major, one workgroup per (b, group, chunk): every row that
 //                attends the chunk (the window's queries and the entries that
-//                selected it) in 16-row MFMA tiles; the four waves split d for
-//                the dK / dV accumulators (kept in registers for the whole
-//                chunk, so each key row is written once, deterministically).
-//                For selected rows it also writes d s_hat and the row's dq part
-//                from this chunk (scale ds K).
+//                selected it) in 16-row MFMA tiles fetched one tile ahead; the
+//                four waves split d for the dK / dV accumulators (kept in
+//                registers for the whole chunk, so each key row is written once,
+//                deterministically).  For selected rows it also writes d s_hat
+//                and the row's dq part from this chunk (scale ds K, in the I/O
+//                dtype), and it accumulates the chunk's dk', db'.
 //   bwd_dq       query-major: the window's part of dq plus the selected parts.
-//   bwd_qhat     dq_hat per row; bwd_ksum dk', db' per chunk over its entries.
+//   bwd_qhat     dq_hat per row.
 //   sum_bwd      Eq. 8 backward per (b, group, chunk): dq' and dk += ... .
 #include "attend_tiles.h"
 #include "hils_internal.h"
@@ -41,7 +42,7 @@ struct BwdKArgs {
   EntryLists el;
   float* Drow;    // [B, Hq, T]
   float* dshat;   // [B, Hq, T, topk]
-  float* dqp;     // [ng, B, T, topk, G, D]: the selected chunks' dq parts of groups g0 ..
+  void* dqp;      // [ng, B, T, topk, G, D] io dtype: the selected chunks' dq parts of groups g0 ..
   int g0;         // first KV head of this pass
 };
 
@@ -129,20 +130,34 @@ __global__ __launch_bounds__(256) void bwd_rowstat_kernel(BwdKArgs k) {
 template <typename T, int D>
 struct KvSmem {
   static constexpr int EPV = 16 / (int)sizeof(T);
-  static constexpr int OP = D + EPV;    // padded row of the q / dout tiles
+  static constexpr int OP = D + EPV;    // padded row of the q / dout / q_hat tiles
   static constexpr int DRP = kS + EPV;  // padded row of ds as [row][token]
   T ks[kS * D];
   T vs[kS * D];
   T kt[D * kS];
   T qt[16 * OP];
   T gt[16 * OP];
+  T ht[16 * OP];    // q_hat rows (selected tiles)
   T at[kS * 16];    // alpha as [token][row]
   T dt[kS * 16];    // ds as [token][row]
   T dr[16 * DRP];   // ds as [row][token]
   float rp[4][3][16];   // each wave's row max, sum and sum of p (g . v) over its tokens
-  float rl[16], rd[16], rg[16], rw[16];
+  float rl[16], rd[16], rg[16], rw[16], rds[16];
   int64_t ri[16];
   int rs[16];
+};
+
+// The rows of one 16-row tile, fetched into registers one tile ahead: this
+// thread's 16-byte pieces of the q, dout (and, for selected tiles, q_hat) rows,
+// and for threads < 16 the row's statistics.
+template <typename T, int D>
+struct TileRegs {
+  static constexpr int EPV = 16 / (int)sizeof(T), PK = D / EPV;
+  static constexpr int NP = (16 * PK + kBT - 1) / kBT;   // pieces per thread
+  uint4 q[NP], g[NP], h[NP];
+  float L, Dr, gl, w;
+  int64_t i;
+  int slot;
 };
 
 // One workgroup per (b, KV head, 64-token chunk).  Wave w scores the chunk's
@@ -150,15 +165,21 @@ struct KvSmem {
 // rows' dout), forms alpha and ds, and shares them through LDS; then each wave
 // accumulates dV^T += G^T alpha^T and dK^T += Q^T ds^T for its quarter of d.
 // Tiles: the queries whose window holds the chunk (16/G queries x G heads), then
-// the entries that selected it.  For a selected row it also writes d s_hat and
-// the row's dq part from this chunk, scale K^T ds^T.
+// the entries that selected it; each tile's rows are fetched one tile ahead.
+// For a selected row it also writes the row's dq part from this chunk
+// (scale K^T ds^T) and accumulates the chunk's dk' = scale sum d s_hat q_hat and
+// db' = sum d s_hat (every entry of the chunk passes through this workgroup).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
   const BwdArgs& a = k.a;
   using SM = KvSmem<T, D>;
+  using TR = TileRegs<T, D>;
   constexpr int KS = D / 32, MDW = D / 64;   // d tiles of 16 per wave
   constexpr int EPV = SM::EPV, PK = D / EPV, PV = kS / EPV, OP = SM::OP, DRP = SM::DRP;
   constexpr int NE = 16 / G;                 // queries / entries per tile
+  constexpr int DPW = D / 4;                 // dims of dk' per wave
+  constexpr int LPH = kWave / G;             // lanes per head for dk'
+  constexpr int DPLH = DPW > LPH ? DPW / LPH : 1;
   __shared__ __align__(16) SM sm;
   const int64_t c = blockIdx.x;
   const int g = k.g0 + blockIdx.y, b = blockIdx.z;
@@ -170,6 +191,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
   const int nvalid = (int)min<int64_t>(kS, T_ - j0);
   const int64_t bgo = (int64_t)b * a.Hkv + g;
   const float sl2 = a.scale * kLog2e;
+  const bool has_sum = c < k.el.NCs;        // a complete chunk: it has k', b'
   stage_kv<T, D, false>(static_cast<const T*>(a.k) + (bgo * T_ + j0) * D,
                         static_cast<const T*>(a.v) + (bgo * T_ + j0) * D, sm.ks, sm.vs, sm.kt, nvalid);
   // rows that attend this chunk: the window's queries [j0, iw1], then the entries
@@ -178,12 +200,62 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
   const int nwt = (int)((iw1 - j0 + 1 + NE - 1) / NE);
   int nsel = 0;
   int64_t ebase = 0;
-  if (a.topk > 0 && c < k.el.NCs) {
+  if (a.topk > 0 && has_sum) {
     const int64_t bucket = bgo * k.el.NCs + c;
     nsel = k.el.bcount[bucket];
     ebase = k.el.bbase[bucket];
   }
   const int nst = (nsel + NE - 1) / NE;
+  const int ntile = nwt + nst;
+  // row rho of tile `tile`: (query or entry, head)
+  auto row_of = [&](int tile, int rho, int64_t& i, int& slot) -> bool {
+    slot = 0;
+    if (tile < nwt) {
+      i = j0 + (int64_t)tile * NE + rho / G;
+      return i <= iw1;
+    }
+    const int en = (tile - nwt) * NE + rho / G;
+    if (en >= nsel) {
+      i = 0;
+      return false;
+    }
+    const uint32_t word = k.el.entries[ebase + en];
+    i = word >> 6;
+    slot = (int)(word & 63u);
+    return true;
+  };
+  auto fetch = [&](int tile, TR& r) {
+    const bool selt = tile >= nwt;
+#pragma unroll
+    for (int t = 0; t < TR::NP; ++t) {
+      const int e = threadIdx.x + t * kBT;
+      r.q[t] = r.g[t] = r.h[t] = make_uint4(0u, 0u, 0u, 0u);
+      if (TR::NP * kBT == 16 * PK || e < 16 * PK) {
+        const int rho = e / PK, p = e % PK;
+        int64_t i;
+        int slot;
+        if (row_of(tile, rho, i, slot)) {
+          const int64_t ro = (((int64_t)b * a.Hq + g * G + rho % G) * T_ + i) * D + p * EPV;
+          r.q[t] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.q) + ro);
+          r.g[t] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.dout) + ro);
+          if (selt) r.h[t] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.qh) + ro);
+        }
+      }
+    }
+    if (threadIdx.x < 16) {
+      const int rho = threadIdx.x;
+      int64_t i;
+      int slot;
+      const bool valid = row_of(tile, rho, i, slot);
+      const int64_t rq = ((int64_t)b * a.Hq + g * G + rho % G) * T_ + (valid ? i : 0);
+      r.L = valid ? a.lse[rq] : 0.f;
+      r.Dr = valid ? k.Drow[rq] : 0.f;
+      r.gl = (valid && a.dlse) ? a.dlse[rq] : 0.f;
+      r.w = (valid && selt) ? a.ssel[rq * a.topk + slot] : 0.f;
+      r.i = valid ? i : -1;
+      r.slot = slot;
+    }
+  };
   f32x4_t dka[MDW][4], dva[MDW][4];
 #pragma unroll
   for (int t = 0; t < MDW; ++t)
@@ -192,54 +264,36 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
       dka[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       dva[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-  for (int tile = 0; tile < nwt + nst; ++tile) {
+  float dks_acc[DPLH];
+#pragma unroll
+  for (int j = 0; j < DPLH; ++j) dks_acc[j] = 0.f;
+  float dbs_acc = 0.f;
+  const int hk = lane / LPH, lk = lane % LPH;   // this lane's dk' head and its dims
+  TR nxt;
+  if (ntile > 0) fetch(0, nxt);
+  for (int tile = 0; tile < ntile; ++tile) {
     const bool selt = tile >= nwt;
     __syncthreads();   // the previous tile is done with the shared tiles
-    for (int e = threadIdx.x; e < 16 * PK; e += kBT) {
-      const int rho = e / PK, p = e % PK;
-      int64_t i;
-      bool valid;
-      if (!selt) {
-        i = j0 + (int64_t)tile * NE + rho / G;
-        valid = i <= iw1;
-      } else {
-        const int en = (tile - nwt) * NE + rho / G;
-        valid = en < nsel;
-        i = valid ? (int64_t)(k.el.entries[ebase + en] >> 6) : 0;
+#pragma unroll
+    for (int t = 0; t < TR::NP; ++t) {
+      const int e = threadIdx.x + t * kBT;
+      if (TR::NP * kBT == 16 * PK || e < 16 * PK) {
+        const int rho = e / PK, p = e % PK;
+        *reinterpret_cast<uint4*>(sm.qt + rho * OP + p * EPV) = nxt.q[t];
+        *reinterpret_cast<uint4*>(sm.gt + rho * OP + p * EPV) = nxt.g[t];
+        if (selt) *reinterpret_cast<uint4*>(sm.ht + rho * OP + p * EPV) = nxt.h[t];
       }
-      const int64_t ro = (((int64_t)b * a.Hq + g * G + rho % G) * T_ + i) * D + p * EPV;
-      uint4 uq = make_uint4(0u, 0u, 0u, 0u), ug = make_uint4(0u, 0u, 0u, 0u);
-      if (valid) {
-        uq = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.q) + ro);
-        ug = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.dout) + ro);
-      }
-      *reinterpret_cast<uint4*>(sm.qt + rho * OP + p * EPV) = uq;
-      *reinterpret_cast<uint4*>(sm.gt + rho * OP + p * EPV) = ug;
     }
     if (threadIdx.x < 16) {
       const int rho = threadIdx.x;
-      int64_t i;
-      bool valid;
-      int slot = 0;
-      if (!selt) {
-        i = j0 + (int64_t)tile * NE + rho / G;
-        valid = i <= iw1;
-      } else {
-        const int en = (tile - nwt) * NE + rho / G;
-        valid = en < nsel;
-        const uint32_t word = valid ? k.el.entries[ebase + en] : 0u;
-        i = word >> 6;
-        slot = (int)(word & 63u);
-      }
-      const int64_t rq = ((int64_t)b * a.Hq + g * G + rho % G) * T_ + (valid ? i : 0);
-      const float L = valid ? a.lse[rq] : 0.f;
-      sm.rl[rho] = L * kLog2e;
-      sm.rd[rho] = valid ? k.Drow[rq] : 0.f;
-      sm.rg[rho] = (valid && a.dlse) ? a.dlse[rq] : 0.f;
-      sm.rw[rho] = (valid && selt) ? __expf(a.ssel[rq * a.topk + slot] - L) : 0.f;
-      sm.ri[rho] = valid ? i : -1;
-      sm.rs[rho] = slot;
+      sm.rl[rho] = nxt.L * kLog2e;
+      sm.rd[rho] = nxt.Dr;
+      sm.rg[rho] = nxt.gl;
+      sm.rw[rho] = selt && nxt.i >= 0 ? __expf(nxt.w - nxt.L) : 0.f;
+      sm.ri[rho] = nxt.i;
+      sm.rs[rho] = nxt.slot;
     }
+    if (tile + 1 < ntile) fetch(tile + 1, nxt);   // in flight during this tile
     __syncthreads();
     // this wave's 16 tokens: S^T and U^T (token 16 wave + 4 grp + q4, row r16)
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, ua = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -299,9 +353,13 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
         al[q4] = sc * e[q4];
         ds[q4] = al[q4] * (ua[q4] - dc);
       }
-      if (wave == 0 && grp == 0 && valid) {
-        const int64_t rq = ((int64_t)b * a.Hq + g * G + r16 % G) * T_ + i;
-        k.dshat[rq * a.topk + sm.rs[r16]] = wr * (dc - Dr + gl);
+      const float dsh = valid ? wr * (dc - Dr + gl) : 0.f;
+      if (wave == 0 && grp == 0) {
+        sm.rds[r16] = dsh;
+        if (valid) {
+          const int64_t rq = ((int64_t)b * a.Hq + g * G + r16 % G) * T_ + i;
+          k.dshat[rq * a.topk + sm.rs[r16]] = dsh;
+        }
       }
     } else {
       const int64_t lw = valid ? window_left(i, a.S, a.W) : 0;
@@ -353,7 +411,8 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
         mma16(dka[t][mt], aq, bd);
       }
     }
-    if (selt) {   // dq part^T (d slice, 16 rows) = scale K^T ds^T over the chunk
+    if (selt) {
+      // dq part^T (d slice, 16 rows) = scale K^T ds^T over the chunk
       const bool vrow = sm.ri[r16] >= 0;
       const int slot = sm.rs[r16];
       const int64_t ir = sm.ri[r16];
@@ -368,11 +427,22 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
           load_frag(bf, sm.dr + r16 * DRP + 32 * k2 + 8 * grp);
           mma(o, af, bf);
         }
-        if (vrow) {
-          float* dst = k.dqp + (((((int64_t)blockIdx.y * a.B + b) * T_ + ir) * a.topk + slot) * G + r16 % G) * D +
-                       16 * md + 4 * grp;
-          *reinterpret_cast<float4*>(dst) =
-              make_float4(o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale);
+        if (vrow)
+          store4<T>(static_cast<T*>(k.dqp) +
+                        (((((int64_t)blockIdx.y * a.B + b) * T_ + ir) * a.topk + slot) * G + r16 % G) * D +
+                        16 * md + 4 * grp,
+                    o, a.scale);
+      }
+      // dk' (this wave's dims, lane's head) and db' over the tile's rows of that head
+      if (lk * DPLH < DPW) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+          const int rho = e * G + hk;
+          const float w = sm.rds[rho];
+#pragma unroll
+          for (int j = 0; j < DPLH; ++j)
+            dks_acc[j] = fmaf(w, to_f<T>(sm.ht[rho * OP + wave * DPW + lk * DPLH + j]), dks_acc[j]);
+          if (wave == 0 && lk == 0) dbs_acc += w;
         }
       }
     }
@@ -391,6 +461,13 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
             make_float4(dva[t][mt][0], dva[t][mt][1], dva[t][mt][2], dva[t][mt][3]);
       }
     }
+  // the chunk's summary gradients (zero when nothing selected it)
+  if (has_sum && lk * DPLH < DPW) {
+    const int64_t bhc = ((int64_t)b * a.Hq + g * G + hk) * k.el.NCs + c;
+#pragma unroll
+    for (int j = 0; j < DPLH; ++j) a.dks[bhc * D + wave * DPW + lk * DPLH + j] = dks_acc[j] * a.scale;
+    if (wave == 0 && lk == 0) a.dbs[bhc] = dbs_acc;
+  }
 }
 
 // ---------------------------------------------------------------- query-major dq
@@ -462,13 +539,14 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdKArgs k) {
   for (int md = 0; md < MD; ++md) {
     float4 r = make_float4(acc[md][0] * a.scale, acc[md][1] * a.scale, acc[md][2] * a.scale,
                            acc[md][3] * a.scale);
+    f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < a.topk; ++s) {
       const int32_t cs = ir[s];
       if (cs < 0 || cs >= NCs) continue;
-      const float4 p = *reinterpret_cast<const float4*>(
-          k.dqp + (((((int64_t)blockIdx.y * a.B + b) * T_ + i) * a.topk + s) * G + hh) * D + 16 * md + 4 * grp);
-      r.x += p.x; r.y += p.y; r.z += p.z; r.w += p.w;
+      load4_add<T>(p, static_cast<const T*>(k.dqp) +
+                          (((((int64_t)blockIdx.y * a.B + b) * T_ + i) * a.topk + s) * G + hh) * D + 16 * md + 4 * grp);
     }
+    r.x += p[0]; r.y += p[1]; r.z += p[2]; r.w += p[3];
     *reinterpret_cast<float4*>(dst + 16 * md + 4 * grp) = r;
   }
 }
@@ -502,34 +580,6 @@ __global__ __launch_bounds__(256) void bwd_qhat_kernel(BwdKArgs k) {
   }
 #pragma unroll
   for (int e = 0; e < DPL; ++e) a.dqh[row * D + lane * DPL + e] = acc[e] * a.scale;
-}
-
-// dk'_c = scale sum over the entries that selected c of d s_hat q_hat_i, and
-// db'_c = sum of d s_hat: one workgroup per (b, group, chunk), entries in order.
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void bwd_ksum_kernel(BwdKArgs k) {
-  const BwdArgs& a = k.a;
-  const int64_t c = blockIdx.x;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int64_t NCs = k.el.NCs;
-  const int64_t bucket = ((int64_t)b * a.Hkv + g) * NCs + c;
-  const int n = a.topk > 0 ? k.el.bcount[bucket] : 0;
-  const int64_t base = a.topk > 0 ? k.el.bbase[bucket] : 0;
-  for (int x = threadIdx.x; x < G * D; x += 256) {
-    const int hh = x / D, d = x % D;
-    const int64_t bh = (int64_t)b * a.Hq + g * G + hh;
-    float acc = 0.f, accb = 0.f;
-    for (int e = 0; e < n; ++e) {
-      const uint32_t word = k.el.entries[base + e];
-      const int64_t i = word >> 6;
-      const int slot = (int)(word & 63u);
-      const float dsh = k.dshat[(bh * a.T + i) * a.topk + slot];
-      acc = fmaf(dsh, to_f<T>(static_cast<const T*>(a.qh)[(bh * a.T + i) * D + d]), acc);
-      accb += dsh;
-    }
-    a.dks[(bh * NCs + c) * D + d] = acc * a.scale;
-    if (d == 0) a.dbs[bh * NCs + c] = accb;
-  }
 }
 
 // ---------------------------------------------------------------- summaries
@@ -625,10 +675,6 @@ hipError_t launch_bwd_tg(BwdKArgs k, int gpp, hipStream_t st) {
     KTimer tm(K_BWD_QHAT, st);
     hipLaunchKernelGGL((bwd_qhat_kernel<T, D, G>), dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, k);
   }
-  if (k.el.NCs > 0) {
-    KTimer tm(K_BWD_KSUM, st);
-    hipLaunchKernelGGL((bwd_ksum_kernel<T, D, G>), dim3((unsigned)k.el.NCs, a.Hkv, a.B), dim3(256), 0, st, k);
-  }
   return hipGetLastError();
 }
 
@@ -657,18 +703,18 @@ hipError_t launch_sum_bwd_t(const SumBwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-void attend_backward_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, size_t* fixed,
-                               size_t* per_group) {
+void attend_backward_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, bool bf16,
+                               size_t* fixed, size_t* per_group) {
   const int kk = topk > 0 ? topk : 1;
   const int G = Hq / Hkv;
   *fixed = entry_lists_bytes(B, Hkv, T, S, topk) + al256((size_t)B * Hq * T * 4) +
            al256((size_t)B * Hq * T * kk * 4) + 256;
-  *per_group = topk > 0 ? al256((size_t)B * T * kk * G * D * 4) : 0;
+  *per_group = topk > 0 ? al256((size_t)B * T * kk * G * D * (bf16 ? 2 : 4)) : 0;
 }
 
 hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t st) {
   size_t fixed, per;
-  attend_backward_workspace(a.B, a.Hq, a.Hkv, a.T, a.S, a.D, a.topk, &fixed, &per);
+  attend_backward_workspace(a.B, a.Hq, a.Hkv, a.T, a.S, a.D, a.topk, a.bf16, &fixed, &per);
   BwdKArgs k{};
   k.a = a;
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(a.ws) + 255) & ~(uintptr_t)255);
@@ -680,7 +726,7 @@ hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t st) {
   w += al256((size_t)a.B * a.Hq * a.T * 4);
   k.dshat = reinterpret_cast<float*>(w);
   w += al256((size_t)a.B * a.Hq * a.T * kk * 4);
-  k.dqp = reinterpret_cast<float*>(w);
+  k.dqp = w;
   // KV heads whose dq parts fit at once (the host checked room for one)
   int gpp = per > 0 ? (int)((a.ws_bytes - fixed) / per) : a.Hkv;
   if (gpp > a.Hkv) gpp = a.Hkv;

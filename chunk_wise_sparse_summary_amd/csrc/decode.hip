@@ -1450,7 +1450,7 @@ int64_t max_candidates(int64_t Lcap, int S, int W) { return Lcap > 0 ? num_candi
 // lists of kk entries) and the number of slices; sj = 0 when the shares cannot
 // cover the candidates.
 void plan(int64_t NCcap, int kk, int* sj, int* mj, int* nslice) {
-  const int s = NCcap > 64 * 256 ? 2 : 1;
+  const int s = NCcap > 16 * 256 ? 2 : 1;
   const int64_t ns = (NCcap + 256 * s - 1) / (256 * s);
   const int m = (kSPS * kk + 63) / 64;
   int j = 1;

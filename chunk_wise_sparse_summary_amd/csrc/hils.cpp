@@ -97,7 +97,7 @@ size_t hils_workspace_bytes(const hils_shape* s, hils_op op) {
     case HILS_OP_ATTEND_BACKWARD: {
       size_t fixed, per;
       hils::attend_backward_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
-                                      s->head_dim, s->top_k, &fixed, &per);
+                                      s->head_dim, s->top_k, s->io_dtype == HILS_BF16, &fixed, &per);
       return fixed + per * (size_t)s->heads_kv;
     }
   }
@@ -320,7 +320,7 @@ hils_status hils_attend_fuse_backward(const hils_shape* s, const void* q, const 
   if (s->seq_len > (int64_t(1) << 25)) return HILS_E_UNSUPPORTED;
   size_t fixed, per;
   hils::attend_backward_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk, s->head_dim,
-                                  s->top_k, &fixed, &per);
+                                  s->top_k, s->io_dtype == HILS_BF16, &fixed, &per);
   if (!ws || ws_bytes < fixed + per) return HILS_E_WORKSPACE;
   hils::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.qh = q_hat; a.ksum = k_sum; a.idx = sel_idx; a.ssel = sel_score;

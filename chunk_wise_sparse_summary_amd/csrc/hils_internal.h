@@ -124,7 +124,7 @@ hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t st);
 // Workspace of the attention backward: `fixed` bytes (entry lists, row
 // statistics, d s_hat) plus `per_group` bytes for each KV head whose dq parts are
 // held at once (at least one).
-void attend_backward_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
+void attend_backward_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, bool bf16,
                                size_t* fixed, size_t* per_group);
 
 // Backward of the landmark summaries: dk (accumulated) and dq_land.
@@ -188,7 +188,7 @@ enum KernelId {
   K_SUMMARIZE, K_SCORE_LSE, K_IDX_COUNT, K_IDX_SCAN_TILES, K_IDX_SCAN_BUCKETS,
   K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_DEC_SCORE, K_DEC_SELECT,
   K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_RANK_KEYS, K_TOPK_SCORES,
-  K_BWD_ROWSTAT, K_BWD_KV, K_BWD_DQ, K_BWD_QHAT, K_BWD_KSUM, K_SUM_BWD, K_BSA_KEYS, K_BSA_TOPK,
+  K_BWD_ROWSTAT, K_BWD_KV, K_BWD_DQ, K_BWD_QHAT, K_SUM_BWD, K_BSA_KEYS, K_BSA_TOPK,
   K_QCAL, K_DEC_APPEND, K_DEC_GSEL, K_COUNT
 };
 class KTimer {

@@ -411,7 +411,7 @@ int hils_abi_version(void);
  *   dec_attend, dec_fuse, dec_summarize (the summaries of chunks
  *   completed by a decode step), v_transpose, rank_keys,
  *   topk_scores, for the backward calls bwd_rowstat, bwd_kv, bwd_dq,
- *   bwd_qhat, bwd_ksum and summarize_bwd (the entry lists of the
+ *   bwd_qhat and summarize_bwd (the entry lists of the
  *   backward count under the idx_* names), bsa_keys, bsa_topk, qcal, and
  *   for hils_decode_multi dec_append and dec_gsel (its other kernels count
  *   under the dec_* names above).  HILS_E_UNSUPPORTED for an unknown name
