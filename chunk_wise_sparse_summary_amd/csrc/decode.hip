@@ -292,33 +292,6 @@ struct ListSmem {
   int32_t msel[64];
 };
 
-// The top-k (lists of at most 64) as keys and positions of n <= 64*J keys held J
-// per lane at position lane + 64 j; fewer than or exactly k present: all of them.
-// Writes n_out entries ascending by position.
-template <int J>
-__device__ __forceinline__ int list_topk(const uint32_t (&keys)[J], int jn, int npresent, int topk,
-                                         int lane, uint32_t* sbuf, int32_t* opos, uint32_t* okey) {
-  if (npresent > topk) {
-    wave_topk_u32<J>(keys, jn, topk, lane, sbuf, opos, okey);
-    return topk;
-  }
-  int base = 0;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    if (j < jn) {
-      const bool s = keys[j] != 0u;
-      const uint64_t msk = __ballot(s);
-      if (s) {
-        const int ps = base + lane_prefix(msk, lane);
-        opos[ps] = lane + 64 * j;
-        okey[ps] = keys[j];
-      }
-      base += __popcll(msk);
-    }
-  }
-  return base;
-}
-
 // The slice's outputs for one query row (bh = its (row, head) index): the head's
 // LSE partial over the slice, the slice's top-k of s_hat (keys and chunk ids,
 // ascending chunk order) and its four largest keys.  sv[j]: the wave's s_hat of

@@ -113,4 +113,31 @@ __device__ void wave_topk_u32(const uint32_t (&keys)[J], int jn, int topk, int l
   }
 }
 
+// The top-k (lists of at most 64) as keys and positions of n <= 64*J keys held J
+// per lane at position lane + 64 j; fewer than or exactly k present: all of them.
+// Writes n_out entries ascending by position.
+template <int J>
+__device__ __forceinline__ int list_topk(const uint32_t (&keys)[J], int jn, int npresent, int topk,
+                                         int lane, uint32_t* sbuf, int32_t* opos, uint32_t* okey) {
+  if (npresent > topk) {
+    wave_topk_u32<J>(keys, jn, topk, lane, sbuf, opos, okey);
+    return topk;
+  }
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < jn) {
+      const bool s = keys[j] != 0u;
+      const uint64_t msk = __ballot(s);
+      if (s) {
+        const int ps = base + lane_prefix(msk, lane);
+        opos[ps] = lane + 64 * j;
+        okey[ps] = keys[j];
+      }
+      base += __popcll(msk);
+    }
+  }
+  return base;
+}
+
 }  // namespace hils
