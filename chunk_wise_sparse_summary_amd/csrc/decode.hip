@@ -57,7 +57,7 @@ struct DecWs {
   float* Lh;          // [B, Hq] each head's LSE over the candidates
   float* apart;       // [B, Hkv, nitems, G, D + 2]: items [0, kk) selected, [kk, kk + nwin) window
   // several queries per sequence (rows b*M + m of the arrays above):
-  float* mpart;       // [Breal, Hkv, nitems_mq, 16, D + 2]: union slots [0, M kk), then window chunks
+  float* mpart;       // [Breal, Hkv, M, nitems_mq, G, D + 2]: each row's selected slots [0, kk), then window chunks
   int32_t* selw;      // [B, Hkv, kk] each row's selection (ascending, -1 pads)
   int nslice, sj, kk, nwin, nitems, mj, nwin_mq, nitems_mq;
 };
@@ -877,10 +877,11 @@ __global__ __launch_bounds__(64) void dec_append_kernel(DecKArgs a) {
 // the group's M G pairs: as attend_item, with the keys and values read from the
 // caches (rows past the group's last position read as zero), and each column's
 // tokens masked to its window (is_win) or to all of c when bit m of `member`
-// is set.  A column with no token gets log-weight -inf and a zero output.
+// is set (the chunk is then slot memslot[m] of row m's selection).  A window
+// column with no token gets log-weight -inf and a zero output.
 template <typename T, int D, int G>
-__device__ __forceinline__ void attend_item_mq(const DecKArgs& a, ItemSmem<T, D>& sm, int br, int g, int slot,
-                                               int64_t c, bool is_win, uint32_t member) {
+__device__ __forceinline__ void attend_item_mq(const DecKArgs& a, ItemSmem<T, D>& sm, int br, int g, int win_slot,
+                                               int64_t c, bool is_win, uint32_t member, const int* memslot) {
   constexpr int EPV = 16 / sizeof(T);
   constexpr int KS = D / 32, MD = D / 16;
   constexpr int PK = D / EPV, PV = kS / EPV;
@@ -980,8 +981,10 @@ __device__ __forceinline__ void attend_item_mq(const DecKArgs& a, ItemSmem<T, D>
       mma(o[t], af, pf);
     }
   }
-  if (hcol) {
-    float* ap = a.w.mpart + ((bg * a.w.nitems_mq + slot) * 16 + r16) * (D + 2);
+  if (colon) {
+    // the column's own slot: its position in its row's selection, or window slot
+    const int slot = is_win ? win_slot : memslot[m];
+    float* ap = a.w.mpart + ((((int64_t)bg * M + m) * a.w.nitems_mq + slot) * G + hh) * (D + 2);
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int t = 0; t < MDW; ++t)
@@ -1029,7 +1032,7 @@ __global__ __launch_bounds__(kThreads) void dec_mscore_kernel(DecKArgs a) {
     const int64_t cfirst = window_left(a.pos.p[br * a.M], a.S, a.W) / kS;
     const int64_t clast = a.pos.p[br * a.M + a.M - 1] / kS;
     if (cfirst + w > clast) return;
-    attend_item_mq<T, D, G>(a, sm.it, br, g, a.M * a.w.kk + w, cfirst + w, true, 0u);
+    attend_item_mq<T, D, G>(a, sm.it, br, g, a.w.kk + w, cfirst + w, true, 0u, nullptr);
     return;
   }
   const int slice = (int)blockIdx.x % a.w.nslice;
@@ -1185,13 +1188,14 @@ __global__ __launch_bounds__(kThreads) void dec_gsel_kernel(DecKArgs a) {
 
 // Union attention: workgroup (uslot, g, b) attends the uslot-th chunk (in
 // ascending order) of the union of the M rows' selections, for the columns of
-// the rows that selected it.  Slots past the union write -inf log-weights.
+// the rows that selected it.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kThreads) void dec_uattend_kernel(DecKArgs a) {
   __shared__ __align__(16) ItemSmem<T, D> it;
   __shared__ int32_t ulist[16 * 64];
   __shared__ int32_t scan[4];
   __shared__ uint32_t member;
+  __shared__ int memslot[16];
   extern __shared__ uint32_t bitmap[];
   const int uslot = blockIdx.x, g = blockIdx.y, br = blockIdx.z;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -1234,70 +1238,81 @@ __global__ __launch_bounds__(kThreads) void dec_uattend_kernel(DecKArgs a) {
     }
   }
   __syncthreads();
-  const int64_t bg = (int64_t)br * a.Hkv + g;
-  if (uslot >= nu) {   // past the union: no weight for any column
-    if (threadIdx.x < 16) a.w.mpart[((bg * a.w.nitems_mq + uslot) * 16 + threadIdx.x) * (D + 2) + D] = kNegInf;
-    return;
-  }
+  if (uslot >= nu) return;   // past the union
   const int32_t c = ulist[uslot];
   for (int t = threadIdx.x; t < M * kk; t += kThreads)
-    if (a.w.selw[(((int64_t)br * M + t / kk) * a.Hkv + g) * kk + t % kk] == c) atomicOr(&member, 1u << (t / kk));
+    if (a.w.selw[(((int64_t)br * M + t / kk) * a.Hkv + g) * kk + t % kk] == c) {
+      atomicOr(&member, 1u << (t / kk));
+      memslot[t / kk] = t % kk;   // ids within a row are distinct: one writer per row
+    }
   __syncthreads();
-  attend_item_mq<T, D, G>(a, it, br, g, uslot, c, false, member);
+  attend_item_mq<T, D, G>(a, it, br, g, 0, c, false, member, memslot);
 }
 
-// Fusion of one (row, head): the union slots it selected and its window chunks,
-// weighted by exp(log-weight) (-inf: no weight).
+// Fusion of one (row, head): its selected chunks (slots [0, nsel) of the row) and
+// the window chunks of the group (slots kk + w; -inf where the row's window has
+// no token of the chunk), weighted by exp(log-weight): one item per thread for
+// the weights, waves summing every kFuseWaves-th item (as dec_fuse).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(64 * kFuseWaves) void dec_mfuse_kernel(DecKArgs a) {
   constexpr int DPL = D / kWave;
+  __shared__ float wts[256];
   __shared__ float red[kFuseWaves][D];
   __shared__ float mz[kFuseWaves][2];
   const int h = blockIdx.x, v = blockIdx.y;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int M = a.M;
   const int br = v / M, m = v % M;
-  const int g = h / G, col = m * G + h % G;
+  const int g = h / G, hl = h % G;
+  const int64_t i = a.pos.p[v];
   const int64_t cfirst = window_left(a.pos.p[br * M], a.S, a.W) / kS;
   const int64_t clast = a.pos.p[br * M + M - 1] / kS;
-  const int nu = M * a.topk;
-  const int nitems = nu + (int)(clast - cfirst + 1);
+  const int nsel = (int)min<int64_t>(num_candidates(i, a.S, a.W), a.topk);
+  const int nitems = nsel + (int)(clast - cfirst + 1);   // <= 64 + W/S + 3 <= 256 (checked on the host)
   const int64_t bg = (int64_t)br * a.Hkv + g;
-  const float* ap = a.w.mpart + (bg * a.w.nitems_mq * 16 + col) * (D + 2);
-  auto slot_of = [&](int x) { return x < nu ? x : M * a.w.kk + (x - nu); };
-  auto lwt = [&](int x) { return ap[(int64_t)slot_of(x) * 16 * (D + 2) + D]; };
-  float mx = kNegInf;
-  for (int x = threadIdx.x; x < nitems; x += 64 * kFuseWaves) mx = fmaxf(mx, lwt(x));
-  mx = wave_max(mx);
+  const float* ap = a.w.mpart + (((int64_t)bg * M + m) * a.w.nitems_mq * G + hl) * (D + 2);
+  const int kk = a.w.kk;
+  auto slot_of = [&](int x) { return x < nsel ? x : kk + (x - nsel); };
+  const int it0 = threadIdx.x;
+  const float lwi = it0 < nitems ? ap[(int64_t)slot_of(it0) * G * (D + 2) + D] : kNegInf;
+  float mx = wave_max(lwi);
   if (lane == 0) mz[wave][0] = mx;
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kFuseWaves; ++w) mx = fmaxf(mx, mz[w][0]);
-  float zs = 0.f;
-  for (int x = threadIdx.x; x < nitems; x += 64 * kFuseWaves) {
-    const float l = lwt(x);
-    zs += l == kNegInf ? 0.f : __expf(l - mx);
-  }
-  zs = wave_sum(zs);
-  if (lane == 0) mz[wave][1] = zs;
+  const float wi = (it0 < nitems && lwi != kNegInf) ? __expf(lwi - mx) : 0.f;
+  wts[it0] = wi;
+  const float zw = wave_sum(wi);
+  if (lane == 0) mz[wave][1] = zw;
+  __syncthreads();
+  float z = 0.f;
+#pragma unroll
+  for (int w = 0; w < kFuseWaves; ++w) z += mz[w][1];
   float res[DPL];
 #pragma unroll
   for (int t = 0; t < DPL; ++t) res[t] = 0.f;
-  for (int x = wave; x < nitems; x += kFuseWaves) {
-    const float l = lwt(x);
-    if (l == kNegInf) continue;   // wave-uniform: one item per wave
-    const float w = __expf(l - mx);
-    const float* pp = ap + (int64_t)slot_of(x) * 16 * (D + 2) + lane * DPL;
+  constexpr int U = 8;
+  for (int itb = wave; itb < nitems; itb += U * kFuseWaves) {
+    float x[U][DPL];
 #pragma unroll
-    for (int t = 0; t < DPL; ++t) res[t] = fmaf(w, pp[t], res[t]);
+    for (int u = 0; u < U; ++u) {
+      const int it = itb + u * kFuseWaves;
+      const float* pp = ap + (int64_t)slot_of(min(it, nitems - 1)) * G * (D + 2) + lane * DPL;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) x[u][t] = pp[t];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = itb + u * kFuseWaves;
+      const float w = it < nitems ? wts[it] : 0.f;
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) res[t] = w != 0.f ? fmaf(w, x[u][t], res[t]) : res[t];
+    }
   }
 #pragma unroll
   for (int t = 0; t < DPL; ++t) red[wave][lane * DPL + t] = res[t];
   __syncthreads();
   if (wave != 0) return;
-  float z = 0.f;
-#pragma unroll
-  for (int w = 0; w < kFuseWaves; ++w) z += mz[w][1];
   const float inv = 1.f / z;
   T* orow = static_cast<T*>(a.out) + ((int64_t)v * a.Hq + h) * D;
 #pragma unroll
@@ -1418,13 +1433,18 @@ size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Candidates of the last cache row (the most any step can see).
 int64_t max_candidates(int64_t Lcap, int S, int W) { return Lcap > 0 ? num_candidates(Lcap - 1, S, W) : 0; }
 
-// Candidates per scoring thread SJ (a slice is 256 SJ candidates: 2 once a head
-// has more than 64 slices of 256), keys per lane MJ of one share (kSPS slice
-// lists of kk entries) and the number of slices; sj = 0 when the shares cannot
-// cover the candidates.
-void plan(int64_t NCcap, int kk, int* sj, int* mj, int* nslice) {
-  const int s = NCcap > 16 * 256 ? 2 : 1;
-  const int64_t ns = (NCcap + 256 * s - 1) / (256 * s);
+// Candidates per scoring thread SJ (a slice is 256 SJ candidates), keys per
+// lane MJ of one share (kSPS slice lists of kk entries) and the number of
+// slices; sj = 0 when the shares cannot cover the candidates.  One query per
+// sequence takes SJ = 2 once a head has more than 16 slices of 256 (fewer,
+// longer workgroups stream k' faster there); several queries per sequence do
+// M times the arithmetic per k' row and keep SJ = 1 (twice the workgroups)
+// while the shares cover the candidates.
+void plan(int64_t NCcap, int kk, int M, int* sj, int* mj, int* nslice) {
+  auto slices = [&](int s_) { return (NCcap + 256 * s_ - 1) / (256 * s_); };
+  int s = (M == 1 && NCcap > 16 * 256) ? 2 : 1;
+  if (s == 1 && slices(1) > (int64_t)kSPS * kMaxShares) s = 2;
+  const int64_t ns = slices(s);
   const int m = (kSPS * kk + 63) / 64;
   int j = 1;
   while (j < m) j <<= 1;
@@ -1439,11 +1459,11 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
   const int64_t NCcap = Lcap / S;
   const int kk = topk > 0 ? topk : 1;
   int sj = 0, mj = 1, nslice = 1;
-  plan(NCcap, kk, &sj, &mj, &nslice);
+  plan(NCcap, kk, M, &sj, &mj, &nslice);
   const int nwin = W / S + 2;
   const int nitems = kk + nwin;
   const int nwin_mq = W / S + 3;   // the union of M <= S windows spans one chunk more
-  const int nitems_mq = M * kk + nwin_mq;
+  const int nitems_mq = kk + nwin_mq; // per row: its selection, then the window chunks
   const int G = Hq / Hkv;
   const int Br = B;
   B *= M;
@@ -1461,7 +1481,7 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
   if (M == 1) {
     d.apart = reinterpret_cast<float*>(take((size_t)B * Hkv * nitems * G * (D + 2) * 4));
   } else {
-    d.mpart = reinterpret_cast<float*>(take((size_t)Br * Hkv * nitems_mq * 16 * (D + 2) * 4));
+    d.mpart = reinterpret_cast<float*>(take((size_t)Br * Hkv * M * nitems_mq * G * (D + 2) * 4));
     d.selw = reinterpret_cast<int32_t*>(take((size_t)B * Hkv * kk * 4));
   }
   d.nslice = nslice;
@@ -1481,7 +1501,7 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
 bool decode_supported(int64_t Lcap, int S, int W, int topk, int G) {
   int sj = 0, mj = 0, ns = 0;
   (void)G;
-  plan(Lcap / S, topk > 0 ? topk : 1, &sj, &mj, &ns);
+  plan(Lcap / S, topk > 0 ? topk : 1, 1, &sj, &mj, &ns);
   // the union bitmap (one bit per candidate) must fit the LDS beside the rest
   return sj > 0 && topk + W / S + 2 <= 256 && (Lcap / S + 31) / 32 * 4 <= 16384;
 }

@@ -358,7 +358,7 @@ size_t hils_decode_multi_workspace_bytes(const hils_shape* s, int32_t n_queries)
   if (check_shape(s, kDecode) != HILS_OK) return 0;
   const int G = s->heads_q / s->heads_kv;
   if (n_queries < 1 || n_queries > 16 || n_queries * G > 16 || n_queries > s->window ||
-      s->batch * n_queries > 64)
+      s->batch * n_queries > 64 || (n_queries > 1 && s->top_k + s->window / s->chunk + 3 > 256))
     return 0;
   return hils::decode_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk, s->window,
                                 s->head_dim, s->top_k, n_queries);
@@ -374,7 +374,10 @@ hils_status hils_decode_multi(const hils_shape* s, int32_t n_queries, const int6
   const int G = s->heads_q / s->heads_kv;
   const int M = n_queries;
   if (M < 1 || M > 16 || M > s->window) return HILS_E_SHAPE;
-  if (M * G > 16 || s->batch * M > 64) return HILS_E_UNSUPPORTED;
+  // a row fuses its selection and the union of the M windows (one chunk more
+  // than one window spans): at most 256 items
+  if (M * G > 16 || s->batch * M > 64 || (M > 1 && s->top_k + s->window / s->chunk + 3 > 256))
+    return HILS_E_UNSUPPORTED;
   if (!pos || !q || !q_hat || !k_new || !v_new || !k_cache || !v_cache || !k_sum || !b_sum || !out)
     return HILS_E_NULL;
   if (!aligned16(q) || !aligned16(q_hat) || !aligned16(k_new) || !aligned16(v_new) ||

@@ -372,8 +372,9 @@ hils_status hils_selection_overlap(const hils_shape* shape, const int32_t* idx_a
  * q, q_hat [B, M, Hq, d]; k_new, v_new [B, M, Hkv, d]; q_land_new [B, Hq, d] or NULL
  * (io_dtype); caches, k_sum, b_sum as hils_decode_step;
  * out [B, M, Hq, d] io_dtype; lse [B, M, Hq] fp32 or NULL; sel_idx [B, M, Hkv, k] or NULL.
- * Requires 1 <= M <= min(16, W) (else HILS_E_SHAPE), M G <= 16 and B M <= 64 (else
- * HILS_E_UNSUPPORTED), pos[b] + M <= cache capacity (else HILS_E_POS), the same
+ * Requires 1 <= M <= min(16, W) (else HILS_E_SHAPE), M G <= 16, B M <= 64 and, for
+ * M > 1, k + W / S + 3 <= 256 (else HILS_E_UNSUPPORTED), pos[b] + M <= cache
+ * capacity (else HILS_E_POS), the same
  * shape limits as hils_decode_step; workspace hils_decode_multi_workspace_bytes().
  * M = 1 runs hils_decode_step.
  */

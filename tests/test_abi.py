@@ -112,6 +112,17 @@ def test_decode_validation():
     assert L.hils_decode_step(ctypes.byref(s3), arr3, *[P(16)] * 13, 1 << 30, None) == -8
 
 
+def test_decode_multi_item_limit():
+    """A multi-query row fuses k selected chunks and the union of M windows, one
+    chunk more than a single window spans: k + W/S + 3 items at most 256."""
+    ok = _shape(B=1, T=65536, k=64, W=189 * 64)       # 64 + 189 + 3 = 256
+    edge = _shape(B=1, T=65536, k=64, W=190 * 64)     # 257 with M > 1
+    assert hils.hils_decode_multi_workspace_bytes(ok, 4) > 0
+    assert hils.hils_decode_multi_workspace_bytes(edge, 4) == 0
+    assert hils.hils_decode_multi_workspace_bytes(edge, 1) > 0   # M = 1 is the single-query step
+    assert hils.hils_workspace_bytes(edge, hils.OP_DECODE) > 0
+
+
 def test_timing_names_and_errors():
     L = hils.lib()
     assert L.hils_timing_enable(b"no_such_kernel") == -8
