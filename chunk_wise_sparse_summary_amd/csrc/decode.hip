@@ -60,6 +60,7 @@ struct DecWs {
   float* mpart;       // [Breal, Hkv, M, nitems_mq, G, D + 2]: each row's selected slots [0, kk), then window chunks
   int32_t* selw;      // [B, Hkv, kk] each row's selection (ascending, -1 pads)
   int nslice, sj, kk, nwin, nitems, mj, nwin_mq, nitems_mq;
+  int direct;         // the group selection ranks the slice lists itself (no dec_headsel)
 };
 
 struct DecKArgs {
@@ -516,6 +517,8 @@ __global__ __launch_bounds__(kThreads) void dec_score_kernel(DecKArgs a) {
 //               attends the chunk of its slot.
 constexpr int kSPS = 32;          // slices per share
 constexpr int kMaxShares = 8;     // shares per head (<= kSPS * kMaxShares slices)
+constexpr int kDirectJ = 16;      // list entries per lane when the group selection ranks
+                                  // a head's slice lists itself (<= 1024 entries)
 constexpr int kMaxUnion = 8 * 64;
 
 // Entries present in slices [s0, s1) of a head: min(kk, candidates) each.
@@ -533,29 +536,47 @@ struct HeadSelSmem {
   uint32_t okey[64];
 };
 
-template <int MJ>
-__global__ __launch_bounds__(64) void dec_headsel_kernel(DecKArgs a) {
-  __shared__ HeadSelSmem sm;
-  const int q = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int64_t i = a.pos.p[b];
-  const int64_t nc = num_candidates(i, a.S, a.W);
+// The natural-log LSE of the lanes' (max, sum) partials in log2 units.
+__device__ __forceinline__ float wave_lse(float M, float Z) {
+  const float Mw = wave_max(M);
+  const float Zw = wave_sum(M == kNegInf ? 0.f : Z * hw_exp2(M - Mw));
+  return (Mw + hw_log2(Zw)) * kLn2;
+}
+
+// Head bh's LSE over its candidates, from the slice partials (one wave).
+__device__ __forceinline__ float head_lse(const DecKArgs& a, int64_t bh, int ns, int lane) {
+  const float2* lp = a.w.lpart + bh * a.w.nslice;
+  float M = kNegInf, Z = 0.f;
+  for (int s = lane; s < ns; s += kWave) lse_merge(M, Z, lp[s].x, lp[s].y);
+  return wave_lse(M, Z);
+}
+
+// One wave: the top-k of s_hat of head bh over the lists of slices [s0, s1)
+// (entry e of slice s at position (s - s0) kk + e: ascending chunk order).  The
+// share's k-th largest key is at least theta, the k-th largest of its slices'
+// four largest keys (at least k entries reach theta), so entries below theta
+// cannot be chosen: when few reach it, the exact top-k runs on those survivors
+// (compacted in position order), otherwise on every entry.  Leaves the chosen
+// entries' positions in sm.opos and keys in sm.okey (ascending chunk order) and
+// returns their number; with IDS, their chunk ids go to oid as well (the ids are
+// loaded with the keys and picked by lane permutes, saving a dependent gather).
+// MJ >= entries / 64.
+template <int MJ, bool IDS = false>
+__device__ __forceinline__ int share_topk(const DecKArgs& a, HeadSelSmem& sm, int64_t bh, int s0, int s1,
+                                          int64_t nc, int lane, int32_t* oid = nullptr) {
   const int topk = a.topk, kk = a.w.kk;
-  if (nc <= topk) return;                 // every candidate is chosen: nothing to rank
   const int slen = kThreads * a.w.sj;
-  const int ns = (int)((nc + slen - 1) / slen);
-  const int s0 = q * kSPS;
-  if (s0 >= ns) return;
-  const int s1 = min(ns, s0 + kSPS);
-  const int64_t bh = (int64_t)b * a.Hq + h;
   const int64_t lbase = (bh * a.w.nslice + s0) * kk;
   const int nent = (s1 - s0) * kk;
   const int jn = (nent + 63) / 64;
   uint32_t keys[MJ];
+  int32_t ids[IDS ? MJ : 1];
 #pragma unroll
   for (int j = 0; j < MJ; ++j) {
     const int p = lane + 64 * j;
-    keys[j] = p < nent ? a.w.lkey[lbase + p] : 0u;
+    const bool in = j < jn && p < nent;
+    keys[j] = in ? a.w.lkey[lbase + p] : 0u;
+    if constexpr (IDS) ids[j] = in ? a.w.lid[lbase + p] : -1;
   }
   uint32_t pool[2];
 #pragma unroll
@@ -563,17 +584,8 @@ __global__ __launch_bounds__(64) void dec_headsel_kernel(DecKArgs a) {
     const int p = lane + 64 * j;
     pool[j] = p < 4 * (s1 - s0) ? a.w.lk4[(bh * a.w.nslice + s0) * 4 + p] : 0u;
   }
-  if (q == 0) {   // the head's LSE from the slice partials
-    const float2* lp = a.w.lpart + bh * a.w.nslice;
-    float M = kNegInf, Z = 0.f;
-    for (int s = lane; s < ns; s += kWave) lse_merge(M, Z, lp[s].x, lp[s].y);
-    const float Mw = wave_max(M);
-    const float Zw = wave_sum(M == kNegInf ? 0.f : Z * hw_exp2(M - Mw));
-    if (lane == 0) a.w.Lh[bh] = (Mw + hw_log2(Zw)) * kLn2;
-  }
   const int npw = slice_entries(nc, slen, kk, s0, s1);
-  int nl = 0;
-  bool pruned = false;
+  int nl = -1;
   if (npw > topk) {
     const uint32_t theta = wave_kth_u32<2>(pool, 2, topk);
     int nsv = 0;
@@ -602,15 +614,50 @@ __global__ __launch_bounds__(64) void dec_headsel_kernel(DecKArgs a) {
       nl = list_topk<2>(k2, 2, nsv, topk, lane, sm.sbuf, sm.opos, sm.okey);
       wave_lds_sync();
       if (lane < nl) sm.opos[lane] = sm.ppos[sm.opos[lane]];
-      pruned = true;
     }
   }
-  if (!pruned) nl = list_topk<MJ>(keys, jn, npw, topk, lane, sm.sbuf, sm.opos, sm.okey);
+  if (nl < 0) nl = list_topk<MJ>(keys, jn, npw, topk, lane, sm.sbuf, sm.opos, sm.okey);
+  if constexpr (IDS) {
+    wave_lds_sync();
+    const int p = lane < nl ? sm.opos[lane] : 0;
+    int32_t id = -1;
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+      if (j < jn) {
+        const int32_t v = __shfl(ids[j], p % 64, kWave);
+        if (p / 64 == j) id = v;
+      }
+    }
+    if (lane < nl) oid[lane] = id;
+  }
+  return nl;
+}
+
+template <int MJ>
+__global__ __launch_bounds__(64) void dec_headsel_kernel(DecKArgs a) {
+  __shared__ HeadSelSmem sm;
+  const int q = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int64_t i = a.pos.p[b];
+  const int64_t nc = num_candidates(i, a.S, a.W);
+  const int topk = a.topk, kk = a.w.kk;
+  if (nc <= topk) return;                 // every candidate is chosen: nothing to rank
+  const int slen = kThreads * a.w.sj;
+  const int ns = (int)((nc + slen - 1) / slen);
+  const int s0 = q * kSPS;
+  if (s0 >= ns) return;
+  const int s1 = min(ns, s0 + kSPS);
+  const int64_t bh = (int64_t)b * a.Hq + h;
+  if (q == 0) {   // the head's LSE from the slice partials
+    const float L = head_lse(a, bh, ns, lane);
+    if (lane == 0) a.w.Lh[bh] = L;
+  }
+  const int nl = share_topk<MJ>(a, sm, bh, s0, s1, nc, lane);
   wave_lds_sync();
   if (lane < kk) {
     const int64_t o = (bh * kMaxShares + q) * kk + lane;
     a.w.hkey[o] = lane < nl ? sm.okey[lane] : 0u;
-    a.w.hid[o] = lane < nl ? a.w.lid[lbase + sm.opos[lane]] : -1;
+    a.w.hid[o] = lane < nl ? a.w.lid[(bh * a.w.nslice + s0) * kk + sm.opos[lane]] : -1;
   }
 }
 
@@ -627,6 +674,7 @@ struct GroupSelSmem {
   int32_t osel[64];
   int32_t chosen[64];
   float lnw[8];
+  HeadSelSmem hs[4];   // per wave, when the heads' lists are ranked here
 };
 
 // The group's selection (ascending chunk ids in sm.chosen[0..min(nc, k))) and, for
@@ -647,9 +695,23 @@ __device__ void group_select(const DecKArgs& a, GroupSelSmem& sm, uint32_t* bitm
     const int slen = kThreads * a.w.sj;
     const int ns = (int)((nc + slen - 1) / slen);
     const int nsh = (ns + kSPS - 1) / kSPS;
-    // each head's top-k from its share lists (share q: position q*kk + e)
+    // each head's top-k: from its slices' lists directly when they form one
+    // share (no head-selection kernel ran), else from its share lists (share q:
+    // position q*kk + e)
     for (int hh = wave; hh < G; hh += kThreads / kWave) {
       const int64_t bh = (int64_t)b * a.Hq + g * G + hh;
+      if (a.w.direct) {
+        // the slice partials are loaded first, so their latency overlaps the ranking
+        const float2 lp = lane < ns ? a.w.lpart[bh * a.w.nslice + lane] : make_float2(kNegInf, 0.f);
+        const int n = share_topk<kDirectJ, true>(a, sm.hs[wave], bh, 0, ns, nc, lane, sm.hid[hh]);
+        const float L = wave_lse(lp.x, lp.y);   // ns <= kSPS <= 64: one partial per lane
+        if (lane == 0) {
+          sm.nh[hh] = n;
+          sm.L[hh] = L;
+        }
+        wave_lds_sync();
+        continue;
+      }
       const int64_t hb = bh * kMaxShares * kk;
       constexpr int JH = kMaxShares;   // kk <= 64 keys per share
       uint32_t keys[JH];
@@ -1359,8 +1421,10 @@ hipError_t launch_decode_tg(const DecKArgs& k, hipStream_t st) {
   }
   if (e != hipSuccess) return e;
   if (k.topk > 0) {
-    e = launch_headsel(k, st);
-    if (e != hipSuccess) return e;
+    if (!k.w.direct) {   // else the selection ranks the slice lists itself
+      e = launch_headsel(k, st);
+      if (e != hipSuccess) return e;
+    }
     const size_t lds = (size_t)((k.NCcap + 31) / 32) * 4;
     KTimer tm(K_DEC_ATTEND, st);
     hipLaunchKernelGGL((dec_attend_kernel<T, D, G>), dim3(k.topk, k.Hkv, k.B), dim3(kThreads), lds, st, k);
@@ -1401,8 +1465,10 @@ hipError_t launch_mq_tg(const DecKArgs& k, int Br, hipStream_t st) {
   hipError_t e = k.w.sj == 1 ? launch_mscore_sj<T, D, G, 1>(k, Br, st) : launch_mscore_sj<T, D, G, 2>(k, Br, st);
   if (e != hipSuccess) return e;
   if (k.topk > 0) {
-    e = launch_headsel(k, st);
-    if (e != hipSuccess) return e;
+    if (!k.w.direct) {
+      e = launch_headsel(k, st);
+      if (e != hipSuccess) return e;
+    }
     const size_t lds = (size_t)((k.NCcap + 31) / 32) * 4;
     {
       KTimer tm(K_DEC_GSEL, st);
@@ -1485,6 +1551,7 @@ void layout(int B, int Hq, int Hkv, int64_t Lcap, int S, int W, int D, int topk,
     d.selw = reinterpret_cast<int32_t*>(take((size_t)B * Hkv * kk * 4));
   }
   d.nslice = nslice;
+  d.direct = nslice <= kSPS && nslice * kk <= 64 * kDirectJ;
   d.sj = sj;
   d.mj = mj;
   d.kk = kk;
