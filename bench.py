@@ -559,7 +559,8 @@ def time_bsa(hils, x, idx_hils, shape, ws, reps=2):
 def time_qcal(hils, x, wl, shape, d_model=4096, rank=64, reps=5):
     """Q-Cal (q_hat = q + W_up W_down h) at the workload's size with random
     weights: median of `reps` calls; HBM roof on q, h and q_hat (the weights
-    stay in cache)."""
+    stay in cache).  Also the selection with Q-Cal fused into its scoring pass
+    (hils_select_qcal) against Q-Cal followed by the selection."""
     import torch
     import workloads as wk
     q = x["q"]
@@ -567,28 +568,45 @@ def time_qcal(hils, x, wl, shape, d_model=4096, rank=64, reps=5):
     c = wk.make_qcal(wl, d_model, rank, seed=5, device=dev)
     qh = torch.empty_like(q)
 
-    def one():
-        hils.hils_qcal(q, c["h"], c["w_down"], c["w_up"], qh, shape)
-    one()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b_ = torch.cuda.Event(enable_timing=True)
-        a.record()
-        one()
-        b_.record()
+    def med(fn):
+        fn()
         torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b_))
-    ms = float(np.median(ts))
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b_.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b_))
+        return float(np.median(ts))
+
+    ms = med(lambda: hils.hils_qcal(q, c["h"], c["w_down"], c["w_up"], qh, shape))
     esz = q.element_size()
     byts = 2 * q.numel() * esz + c["h"].numel() * esz + (c["w_down"].numel() + c["w_up"].numel()) * esz
     B, Hq, T, d = q.shape
     flops = 2.0 * B * T * rank * (d_model + Hq * d)
-    del c, qh
-    return {"ms_median": ms, "bytes": byts, "GBps": byts / (ms * 1e-3) / 1e9,
-            "hbm_frac": byts / (ms * 1e-3) / PEAK_HBM, "flops": flops, "d_model": d_model, "rank": rank,
-            "note": "median of %d calls; bytes = q + h + q_hat + weights" % reps}
+    res = {"ms_median": ms, "bytes": byts, "GBps": byts / (ms * 1e-3) / 1e9,
+           "hbm_frac": byts / (ms * 1e-3) / PEAK_HBM, "flops": flops, "d_model": d_model, "rank": rank,
+           "note": "median of %d calls; bytes = q + h + q_hat + weights" % reps}
+    NC = T // wl.S
+    ks = torch.empty((B, Hq, NC, d), dtype=q.dtype, device=dev)
+    bs = torch.empty((B, Hq, NC), dtype=torch.float32, device=dev)
+    hils.hils_summarize(x["k"], x["q_land"], ks, bs, shape)
+    idx = torch.empty((B, wl.Hkv, T, wl.k), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, Hq, T, wl.k), dtype=torch.float32, device=dev)
+    ws = torch.empty(hils.hils_select_qcal_workspace_bytes(shape, rank), dtype=torch.uint8, device=dev)
+    # the selection's own workspace sits after z in the fused call's; same size here
+    ws_sel = ws[ws.numel() - hils.hils_workspace_bytes(shape, hils.OP_SELECT):]
+    sel_ms = med(lambda: hils.hils_select(qh, ks, bs, idx, sc, shape, ws_sel))
+    fused_ms = med(lambda: hils.hils_select_qcal(q, c["h"], c["w_down"], c["w_up"], ks, bs, qh, idx, sc,
+                                                 shape, ws))
+    res["select_ms_median"] = sel_ms
+    res["qcal_then_select_ms"] = ms + sel_ms
+    res["select_qcal_fused_ms_median"] = fused_ms
+    del c, qh, ks, bs, idx, sc, ws, ws_sel
+    return res
 
 
 def main():

@@ -18,6 +18,9 @@ if the library is missing, loading raises.
                       k_sum, b_sum, out, lse, sel_idx, shape, workspace=None)
     hils_decode_multi_workspace_bytes(shape, n_queries)
     hils_qcal(q, hs, w_down, w_up, q_hat, shape)
+    hils_select_qcal(q, hs, w_down, w_up, k_sum, b_sum, q_hat, sel_idx, sel_score, shape,
+                     workspace=None)
+    hils_select_qcal_workspace_bytes(shape, rank)
     hils_summarize_shared(k, q_shared, k_sum, b_sum, shape, chunk_begin=0, n_chunks=None)
     hils_bsa_select(q, k, sel_idx, shape, workspace=None)
     hils_selection_overlap(idx_a, idx_b, count, shape)
@@ -47,7 +50,8 @@ STATUS = {
 
 EXPORTS = ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
            "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
-           "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_summarize_shared",
+           "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_select_qcal",
+           "hils_select_qcal_workspace_bytes", "hils_summarize_shared",
            "hils_decode_multi", "hils_decode_multi_workspace_bytes",
            "hils_workspace_bytes", "hils_status_string", "hils_abi_version",
            "hils_timing_enable", "hils_timing_get")
@@ -95,6 +99,10 @@ def lib():
         L.hils_bsa_select.argtypes = [SP, P, P, P, P, SZ, P]
         L.hils_selection_overlap.argtypes = [SP, P, P, P, P]
         L.hils_qcal.argtypes = [SP, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P]
+        L.hils_select_qcal.argtypes = [SP, P, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P,
+                                       P, SZ, P]
+        L.hils_select_qcal_workspace_bytes.argtypes = [SP, ctypes.c_int32]
+        L.hils_select_qcal_workspace_bytes.restype = SZ
         L.hils_summarize_shared.argtypes = [SP, P, P, I64, I64, P, P, P]
         L.hils_decode_multi.argtypes = [SP, ctypes.c_int32, P] + [P] * 12 + [P, SZ, P]
         L.hils_decode_multi_workspace_bytes.argtypes = [SP, ctypes.c_int32]
@@ -111,8 +119,8 @@ def lib():
         L.hils_timing_get.restype = ctypes.c_int
         for f in ("hils_summarize", "hils_select", "hils_attend_fuse", "hils_decode_step",
                   "hils_decode_step_noalloc", "hils_attend_fuse_backward", "hils_summarize_backward",
-                  "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_summarize_shared",
-                  "hils_decode_multi"):
+                  "hils_bsa_select", "hils_selection_overlap", "hils_qcal", "hils_select_qcal",
+                  "hils_summarize_shared", "hils_decode_multi"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -222,6 +230,24 @@ def hils_qcal(q, hs, w_down, w_up, q_hat, shape: Shape):
                                         int(hs.shape[-1]), int(w_down.shape[0]), _p(q_hat), _stream()))
 
 
+def hils_select_qcal_workspace_bytes(shape: Shape, rank: int) -> int:
+    return int(lib().hils_select_qcal_workspace_bytes(ctypes.byref(shape), int(rank)))
+
+
+def hils_select_qcal(q, hs, w_down, w_up, k_sum, b_sum, q_hat, sel_idx, sel_score, shape: Shape,
+                     workspace_t=None):
+    """hils_select with q_hat = q + W_up (W_down hs) formed inside its first scoring pass
+    (q_hat is written too)."""
+    _dev(q, hs, w_down, w_up, k_sum, b_sum, q_hat, sel_idx, sel_score)
+    rank = int(w_down.shape[0])
+    if workspace_t is None:
+        n = hils_select_qcal_workspace_bytes(shape, rank)
+        workspace_t = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check("hils_select_qcal", lib().hils_select_qcal(
+        ctypes.byref(shape), _p(q), _p(hs), _p(w_down), _p(w_up), int(hs.shape[-1]), rank, _p(k_sum),
+        _p(b_sum), _p(q_hat), _p(sel_idx), _p(sel_score), _p(workspace_t), workspace_t.numel(), _stream()))
+
+
 def hils_summarize_shared(k, q_shared, k_sum, b_sum, shape: Shape, chunk_begin: int = 0,
                           n_chunks: int | None = None):
     """Summaries with one shared landmark query per head (q_shared [Hq, d])."""
@@ -281,7 +307,7 @@ KERNELS = ("summarize", "score_lse", "idx_count", "idx_scan_tiles",
            "dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize",
            "v_transpose", "rank_keys", "topk_scores",
            "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "summarize_bwd",
-           "bsa_keys", "bsa_topk", "qcal", "dec_append", "dec_gsel")
+           "bsa_keys", "bsa_topk", "qcal", "dec_append", "dec_gsel", "qcal_zdown")
 
 
 def hils_timing_enable(kernels):

@@ -154,6 +154,11 @@ hils_status hils_summarize_shared(const hils_shape* s, const void* k, const void
   return from_hip(hils::launch_summarize(a, stream));
 }
 
+static bool qcal_dims_ok(int32_t d_model, int32_t rank) {
+  return d_model >= 32 && d_model % 32 == 0 && d_model <= 65536 &&
+         (rank == 16 || rank == 32 || rank == 64 || rank == 128);
+}
+
 hils_status hils_qcal(const hils_shape* s, const void* q, const void* h, const void* w_down,
                       const void* w_up, int32_t d_model, int32_t rank, void* q_hat, hipStream_t stream) {
   const hils_status st = check_shape(s, kSummarize);
@@ -161,8 +166,7 @@ hils_status hils_qcal(const hils_shape* s, const void* q, const void* h, const v
   if (!q || !h || !w_down || !w_up || !q_hat) return HILS_E_NULL;
   if (!aligned16(q) || !aligned16(h) || !aligned16(w_down) || !aligned16(w_up) || !aligned16(q_hat))
     return HILS_E_ALIGN;
-  if (d_model < 32 || d_model % 32 != 0 || d_model > 65536) return HILS_E_UNSUPPORTED;
-  if (rank != 16 && rank != 32 && rank != 64 && rank != 128) return HILS_E_UNSUPPORTED;
+  if (!qcal_dims_ok(d_model, rank)) return HILS_E_UNSUPPORTED;
   if (q == q_hat) return HILS_E_SHAPE;
   if (s->seq_len > 0x7fffffffLL * 64) return HILS_E_UNSUPPORTED;
   hils::QcalArgs a{};
@@ -170,6 +174,28 @@ hils_status hils_qcal(const hils_shape* s, const void* q, const void* h, const v
   a.B = s->batch; a.Hq = s->heads_q; a.D = s->head_dim; a.dm = d_model; a.r = rank;
   a.bf16 = s->io_dtype == HILS_BF16; a.T = s->seq_len;
   return from_hip(hils::launch_qcal(a, stream));
+}
+
+// The selection's workspace carve-up and launch arguments (shape checked).
+static hils_status select_setup(const hils_shape* s, void* ws, size_t ws_bytes, hils::SelArgs& a) {
+  int n_slots = 0;
+  int64_t stride = 0;
+  size_t fixed = 0, per_group = 0;
+  hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
+                         s->io_dtype == HILS_BF16, &n_slots, &stride, &fixed, &per_group);
+  if (!ws || ws_bytes < fixed + per_group) return HILS_E_WORKSPACE;
+  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+  a.L = reinterpret_cast<float*>(w);
+  a.scratch = reinterpret_cast<float*>(w + (fixed - 256));
+  const size_t groups = (ws_bytes - fixed) / per_group;
+  const int nbg = s->batch * s->heads_kv;
+  a.gpass = groups < (size_t)nbg ? (int)groups : nbg;
+  a.group_words = (int64_t)(per_group / sizeof(uint32_t));
+  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
+  a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
+  a.T = s->seq_len; a.NCs = s->seq_len / s->chunk; a.scale = eff_scale(s);
+  a.n_slots = n_slots; a.slot_stride = stride;
+  return HILS_OK;
 }
 
 hils_status hils_select(const hils_shape* s, const void* q_hat, const void* k_sum,
@@ -184,25 +210,55 @@ hils_status hils_select(const hils_shape* s, const void* q_hat, const void* k_su
       !aligned16(sel_score))
     return HILS_E_ALIGN;
   if (s->top_k == 0) return HILS_OK;  // nothing to select
-  int n_slots = 0;
-  int64_t stride = 0;
-  size_t fixed = 0, per_group = 0;
-  hils::select_workspace(s->batch, s->heads_q, s->heads_kv, s->seq_len, s->chunk,
-                         s->io_dtype == HILS_BF16, &n_slots, &stride, &fixed, &per_group);
-  if (!ws || ws_bytes < fixed + per_group) return HILS_E_WORKSPACE;
   hils::SelArgs a{};
+  const hils_status sw = select_setup(s, ws, ws_bytes, a);
+  if (sw != HILS_OK) return sw;
   a.qh = q_hat; a.ksum = k_sum; a.bsum = b_sum; a.idx = sel_idx; a.ssel = sel_score;
-  char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
-  a.L = reinterpret_cast<float*>(w);
-  a.scratch = reinterpret_cast<float*>(w + (fixed - 256));
-  const size_t groups = (ws_bytes - fixed) / per_group;
-  const int nbg = s->batch * s->heads_kv;
-  a.gpass = groups < (size_t)nbg ? (int)groups : nbg;
-  a.group_words = (int64_t)(per_group / sizeof(uint32_t));
-  a.B = s->batch; a.Hq = s->heads_q; a.Hkv = s->heads_kv; a.D = s->head_dim; a.S = s->chunk;
-  a.W = s->window; a.topk = s->top_k; a.bf16 = s->io_dtype == HILS_BF16;
-  a.T = s->seq_len; a.NCs = s->seq_len / s->chunk; a.scale = eff_scale(s);
-  a.n_slots = n_slots; a.slot_stride = stride;
+  return from_hip(hils::launch_select(a, stream));
+}
+
+// z = W_down h (fp32 [B, T, rank]) at the workspace's first 256-byte boundary.
+static size_t qcal_z_bytes(const hils_shape* s, int32_t rank) {
+  return ((size_t)s->batch * (size_t)s->seq_len * (size_t)rank * sizeof(float) + 255) / 256 * 256 + 256;
+}
+
+size_t hils_select_qcal_workspace_bytes(const hils_shape* s, int32_t rank) {
+  if (check_shape(s, kPrefill) != HILS_OK || !qcal_dims_ok(32, rank)) return 0;
+  return qcal_z_bytes(s, rank) + hils_workspace_bytes(s, HILS_OP_SELECT);
+}
+
+hils_status hils_select_qcal(const hils_shape* s, const void* q, const void* h, const void* w_down,
+                             const void* w_up, int32_t d_model, int32_t rank, const void* k_sum,
+                             const float* b_sum, void* q_hat, int32_t* sel_idx, float* sel_score,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  const hils_status st = check_shape(s, kPrefill);
+  if (st != HILS_OK) return st;
+  const bool has_chunks = s->seq_len / s->chunk > 0;
+  if (!q || !h || !w_down || !w_up || !q_hat || (has_chunks && (!k_sum || !b_sum)) ||
+      (s->top_k > 0 && (!sel_idx || !sel_score)))
+    return HILS_E_NULL;
+  if (!aligned16(q) || !aligned16(h) || !aligned16(w_down) || !aligned16(w_up) || !aligned16(q_hat) ||
+      !aligned16(k_sum) || !aligned16(b_sum) || !aligned16(sel_idx) || !aligned16(sel_score))
+    return HILS_E_ALIGN;
+  if (!qcal_dims_ok(d_model, rank)) return HILS_E_UNSUPPORTED;
+  if (q == q_hat) return HILS_E_SHAPE;
+  if (s->seq_len > 0x7fffffffLL * 64) return HILS_E_UNSUPPORTED;
+  hils::QcalArgs qa{};
+  qa.q = q; qa.h = h; qa.wd = w_down; qa.wu = w_up; qa.qh = q_hat;
+  qa.B = s->batch; qa.Hq = s->heads_q; qa.D = s->head_dim; qa.dm = d_model; qa.r = rank;
+  qa.bf16 = s->io_dtype == HILS_BF16; qa.T = s->seq_len;
+  if (s->top_k == 0) return from_hip(hils::launch_qcal(qa, stream));   // nothing to select: q_hat alone
+  const size_t zb = qcal_z_bytes(s, rank);
+  if (!ws || ws_bytes < zb) return HILS_E_WORKSPACE;
+  float* z = reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+  hils::SelArgs a{};
+  const hils_status sw = select_setup(s, static_cast<char*>(ws) + zb, ws_bytes - zb, a);
+  if (sw != HILS_OK) return sw;
+  a.qh = q_hat; a.ksum = k_sum; a.bsum = b_sum; a.idx = sel_idx; a.ssel = sel_score;
+  a.qc = hils::QcFuse{q, z, w_up, q_hat};
+  a.qc_r = rank;
+  hipError_t e = hils::launch_zdown(qa, z, stream);
+  if (e != hipSuccess) return from_hip(e);
   return from_hip(hils::launch_select(a, stream));
 }
 

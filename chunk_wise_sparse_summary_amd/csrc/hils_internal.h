@@ -32,6 +32,14 @@ struct SumArgs {
 };
 hipError_t launch_summarize(const SumArgs& a, hipStream_t st);
 
+// The low-rank query calibration fused into the selection's first scoring pass.
+struct QcFuse {
+  const void* q;     // [B, Hq, T, D] token queries
+  const float* z;    // [B, T, r] W_down h, fp32
+  const void* wu;    // [Hq, D, r]
+  void* qh;          // [B, Hq, T, D] q_hat, written by the pass (the same buffer as SelArgs::qh)
+};
+
 struct SelArgs {
   const void* qh;
   const void* ksum;
@@ -49,6 +57,8 @@ struct SelArgs {
   int64_t slot_stride;  // keys per row
   int gpass;            // (b, group) pairs per launch
   int64_t group_words;  // keys of one (b, group), padded
+  QcFuse qc{};          // used when qc_r > 0
+  int qc_r = 0;         // rank of the fused Q-Cal, 0: q_hat is an input
 };
 hipError_t launch_select(const SelArgs& a, hipStream_t st);
 // Naive BSA selection: SelArgs with qh = the token query q, ksum = the keys k,
@@ -155,6 +165,8 @@ struct QcalArgs {
   int64_t T;
 };
 hipError_t launch_qcal(const QcalArgs& a, hipStream_t st);
+// z = W_down h alone, fp32 [B, T, r], for the selection that fuses the rest.
+hipError_t launch_zdown(const QcalArgs& a, float* z, hipStream_t st);
 
 struct DecArgs {
   const int64_t* pos;  // host
@@ -189,7 +201,7 @@ enum KernelId {
   K_IDX_FILL, K_LSEL, K_WINDOW, K_CHUNK_ATTEND, K_DEC_SCORE, K_DEC_SELECT,
   K_DEC_ATTEND, K_DEC_FUSE, K_DEC_SUMMARIZE, K_VT, K_RANK_KEYS, K_TOPK_SCORES,
   K_BWD_ROWSTAT, K_BWD_KV, K_BWD_DQ, K_BWD_QHAT, K_SUM_BWD, K_BSA_KEYS, K_BSA_TOPK,
-  K_QCAL, K_DEC_APPEND, K_DEC_GSEL, K_COUNT
+  K_QCAL, K_DEC_APPEND, K_DEC_GSEL, K_QCAL_ZDOWN, K_COUNT
 };
 class KTimer {
  public:

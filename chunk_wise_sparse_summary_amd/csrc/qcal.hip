@@ -8,18 +8,46 @@
 //      operands read straight from HBM / L2 (h rows once, W_down shared by all);
 //      z stays fp32.
 //   2. each wave takes whole heads for the 64 tokens: (q_hat - q)^T = W_up z^T
-//      with fp32 MFMA (16x16x4), so z is never rounded, W_up rows read straight
-//      from L2; each lane adds its four q values, rounds once and stores them.
+//      with fp32 MFMA (16x16x4, qcal_tile.h), so z is never rounded, W_up rows
+//      read straight from L2; each lane adds its four q values, rounds once and
+//      stores them.
+// zdown_kernel runs step 1 alone and stores z (fp32), for the selection pass
+// that fuses step 2 into its scoring.
 #include "attend_tiles.h"   // load4_add, store4
 #include "hils_internal.h"
+#include "qcal_tile.h"
 
 namespace hils {
 
 namespace {
 
+// z (tokens x r) of 16 tokens 16 wave .. of the workgroup's 64: lane holds
+// zacc[nt][i] = z of token 16 wave + 4 grp + i, column 16 nt + r16.
+template <typename T, int R>
+__device__ __forceinline__ void zdown_tile(const QcalArgs& a, int b, int64_t tb, int wave, int lane,
+                                           f32x4_t (&zacc)[R / 16]) {
+  constexpr int KS = 32;          // contraction step of one fragment
+  constexpr int NT = R / 16;      // r tiles
+  const int r16 = lane % 16, grp = lane / 16;
+  const int64_t T_ = a.T;
+  const int dm = a.dm;
+  const T* hg = static_cast<const T*>(a.h) + ((int64_t)b * T_ + min(tb + 16 * wave + r16, T_ - 1)) * dm;
+  const T* wd = static_cast<const T*>(a.wd);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) zacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4   // four steps' loads in flight: the chain is latency-bound
+  for (int m0 = 0; m0 < dm; m0 += KS) {
+    Frag<T> ah, bw[NT];
+    load_frag(ah, hg + m0 + 8 * grp);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) load_frag(bw[nt], wd + (int64_t)(16 * nt + r16) * dm + m0 + 8 * grp);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) mma(zacc[nt], ah, bw[nt]);
+  }
+}
+
 template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void qcal_kernel(QcalArgs a) {
-  constexpr int KS = 32;          // contraction step of one fragment
   constexpr int NT = R / 16;      // r tiles of step 1
   constexpr int RG = R / 4;       // contraction elements per lane group in step 2
   constexpr int ZP = R + 4;       // padded LDS row of z (fp32 words)
@@ -30,34 +58,16 @@ __global__ __launch_bounds__(256) void qcal_kernel(QcalArgs a) {
   const int b = blockIdx.y;
   const int64_t T_ = a.T;
   const int64_t tb = (int64_t)blockIdx.x * 64;
-  const int dm = a.dm;
-  // 1. z (tokens x r) of this wave's 16 tokens: lane holds tokens 4 grp + i of
-  //    column j = 16 nt + r16
   {
-    const T* hg = static_cast<const T*>(a.h) + ((int64_t)b * T_ + min(tb + 16 * wave + r16, T_ - 1)) * dm;
-    const T* wd = static_cast<const T*>(a.wd);
     f32x4_t zacc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) zacc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int m0 = 0; m0 < dm; m0 += KS) {
-      Frag<T> ah, bw[NT];
-      load_frag(ah, hg + m0 + 8 * grp);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) load_frag(bw[nt], wd + (int64_t)(16 * nt + r16) * dm + m0 + 8 * grp);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) mma(zacc[nt], ah, bw[nt]);
-    }
+    zdown_tile<T, R>(a, b, tb, wave, lane, zacc);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) zl[(16 * wave + 4 * grp + i) * ZP + 16 * nt + r16] = zacc[nt][i];
   }
   __syncthreads();
-  // 2. every wave takes whole heads for all 64 tokens.  The contraction over j
-  //    runs in the order j = RG grp + s (step s of the 16x16x4 products), so a
-  //    lane's W_up operand is RG consecutive elements of one row and its z
-  //    operand RG consecutive values of one token.
+  // 2. every wave takes whole heads for all 64 tokens
   float zr[4][RG];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
@@ -66,33 +76,15 @@ __global__ __launch_bounds__(256) void qcal_kernel(QcalArgs a) {
       const float4 v = *reinterpret_cast<const float4*>(&zl[(16 * tt + r16) * ZP + RG * grp + s]);
       zr[tt][s] = v.x; zr[tt][s + 1] = v.y; zr[tt][s + 2] = v.z; zr[tt][s + 3] = v.w;
     }
-  const T* wu = static_cast<const T*>(a.wu);
   for (int hd = wave; hd < a.Hq; hd += 4) {
     const int64_t rb = ((int64_t)b * a.Hq + hd) * T_;
 #pragma unroll 1
     for (int md = 0; md < D / 16; ++md) {
-      // W_up[hd][16 md + r16][RG grp .. RG grp + RG - 1]
       float wa[RG];
-      const T* wr = wu + ((int64_t)hd * D + 16 * md + r16) * R + RG * grp;
-      if constexpr (RG * sizeof(T) >= 16) {
-#pragma unroll
-        for (int s = 0; s < RG; s += 16 / (int)sizeof(T)) {
-          const uint4 u = *reinterpret_cast<const uint4*>(wr + s);
-          const T* x = reinterpret_cast<const T*>(&u);
-#pragma unroll
-          for (int e = 0; e < 16 / (int)sizeof(T); ++e) wa[s + e] = to_f<T>(x[e]);
-        }
-      } else {   // bf16 with r = 16: four elements, 8 bytes
-        const uint2 u = *reinterpret_cast<const uint2*>(wr);
-        const T* x = reinterpret_cast<const T*>(&u);
-#pragma unroll
-        for (int e = 0; e < RG; ++e) wa[e] = to_f<T>(x[e]);
-      }
+      qcal_wup_piece<T, D, R>(static_cast<const T*>(a.wu), hd, 16 * md + r16, grp, wa);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < RG; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[s], zr[tt][s], acc, 0, 0, 0);
+        const f32x4_t acc = qcal_chain<R>(wa, zr[tt]);
         // acc[i]: element 16 md + 4 grp + i of token 16 tt + r16
         const int64_t tq = tb + 16 * tt + r16;
         if (tq < T_) {
@@ -104,6 +96,38 @@ __global__ __launch_bounds__(256) void qcal_kernel(QcalArgs a) {
       }
     }
   }
+}
+
+// Step 1 alone: z of 64 tokens per workgroup into zout [B, T, R] (fp32).
+template <typename T, int R>
+__global__ __launch_bounds__(256) void zdown_kernel(QcalArgs a, float* __restrict__ zout) {
+  constexpr int NT = R / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r16 = lane % 16, grp = lane / 16;
+  const int b = blockIdx.y;
+  const int64_t tb = (int64_t)blockIdx.x * 64;
+  f32x4_t zacc[NT];
+  zdown_tile<T, R>(a, b, tb, wave, lane, zacc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = tb + 16 * wave + 4 * grp + i;
+    if (t < a.T)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) zout[((int64_t)b * a.T + t) * R + 16 * nt + r16] = zacc[nt][i];
+  }
+}
+
+template <typename T>
+hipError_t launch_zdown_t(const QcalArgs& a, float* z, hipStream_t st) {
+  const dim3 grid((unsigned)((a.T + 63) / 64), (unsigned)a.B);
+  switch (a.r) {
+    case 16: hipLaunchKernelGGL((zdown_kernel<T, 16>), grid, dim3(256), 0, st, a, z); break;
+    case 32: hipLaunchKernelGGL((zdown_kernel<T, 32>), grid, dim3(256), 0, st, a, z); break;
+    case 64: hipLaunchKernelGGL((zdown_kernel<T, 64>), grid, dim3(256), 0, st, a, z); break;
+    default: hipLaunchKernelGGL((zdown_kernel<T, 128>), grid, dim3(256), 0, st, a, z); break;
+  }
+  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -119,6 +143,11 @@ hipError_t launch_qcal_td(const QcalArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_zdown(const QcalArgs& a, float* z, hipStream_t st) {
+  KTimer tm(K_QCAL_ZDOWN, st);
+  return a.bf16 ? launch_zdown_t<bf16_t>(a, z, st) : launch_zdown_t<float>(a, z, st);
+}
 
 hipError_t launch_qcal(const QcalArgs& a, hipStream_t st) {
   KTimer tm(K_QCAL, st);

@@ -24,8 +24,9 @@
 // bisection with ballot counts over the few keys that reach theta, then the
 // chosen ids in ascending order with ballot prefix counts (ties at the k-th key
 // to the lowest ids).
-#include "attend_tiles.h"   // score_tile (naive BSA)
+#include "attend_tiles.h"   // score_tile (naive BSA), load4_add, store4
 #include "hils_internal.h"
+#include "qcal_tile.h"
 #include "topk.h"
 
 namespace hils {
@@ -98,13 +99,19 @@ constexpr float kRefInit = -1e30f;
 // four waves.  Score tiles are transposed (rows = chunks, columns = queries), so
 // each lane holds four chunks of one query and keeps one running (m, s) per
 // 16-query tile.
-template <typename T, int D>
+// With R > 0 the low-rank query calibration is fused in (paper-body page,
+// implementation: Q-Cal): each wave forms its queries' q_hat = q + W_up[h] z
+// (z = W_down h from zdown_kernel) with the arithmetic of the Q-Cal kernel
+// (qcal_tile.h), stores it for the later passes and reads its score operands
+// back from the stored (rounded) rows.  Lout = null (a group of one head needs
+// no LSE) stops after that.
+template <typename T, int D, int R = 0>
 __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh,
                                                         const T* __restrict__ ksum,
                                                         const float* __restrict__ bsum,
                                                         float* __restrict__ Lout, int Hq,
                                                         int64_t T_, int64_t NCs, int S, int W,
-                                                        float scale) {
+                                                        float scale, QcFuse qc) {
   constexpr int KS = D / 32;
   using Tile = KTile<T, D, 1>;
   __shared__ __align__(16) T kt[16 * Tile::KP];
@@ -121,15 +128,63 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
   Frag<T> qf[4][KS];   // column r16 of query tile rt
   int ncq[4];
   float m[4], s[4];
+  if constexpr (R > 0) {
+    constexpr int RG = R / 4;
+    const T* qtok = static_cast<const T*>(qc.q);
+    T* qout = static_cast<T*>(qc.qh);
+    float zr[4][RG];   // z of this lane's token (an MFMA column) in each query tile
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int64_t qi = q0 + 16 * rt + r16;
-    const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
+    for (int rt = 0; rt < 4; ++rt) {
+      const float* zp = qc.z + ((int64_t)b * T_ + min(q0 + 16 * rt + r16, T_ - 1)) * R + RG * grp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load_frag(qf[rt][ks], qrow + 32 * ks);
-    ncq[rt] = qi < T_ ? (int)num_candidates(qi, S, W) : 0;
-    m[rt] = kRefInit;
-    s[rt] = 0.f;
+      for (int e = 0; e < RG; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(zp + e);
+        zr[rt][e] = v.x; zr[rt][e + 1] = v.y; zr[rt][e + 2] = v.z; zr[rt][e + 3] = v.w;
+      }
+    }
+    // one W_up piece per 16 elements serves the four tiles: four independent chains
+#pragma unroll 1
+    for (int md = 0; md < D / 16; ++md) {
+      float wa[RG];
+      qcal_wup_piece<T, D, R>(static_cast<const T*>(qc.wu), h, 16 * md + r16, grp, wa);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const f32x4_t acc = qcal_chain<R>(wa, zr[rt]);   // elements 16 md + 4 grp + i
+        const int64_t qi = q0 + 16 * rt + r16;
+        const int64_t o = (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 16 * md + 4 * grp;
+        f32x4_t val = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        load4_add<T>(val, qtok + o);
+        val += acc;
+        if (qi < T_) store4<T>(qout + o, val, 1.f);
+      }
+    }
+    // the wave reads back the rows it has just stored (other lanes' stores):
+    // workgroup-scope release and acquire make them visible
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int64_t qi = q0 + 16 * rt + r16;
+      // a column past T reads a row it did not store; its scores are never kept
+      const T* qrow = qout + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) load_frag(qf[rt][ks], qrow + 32 * ks);
+      ncq[rt] = qi < T_ ? (int)num_candidates(qi, S, W) : 0;
+      m[rt] = kRefInit;
+      s[rt] = 0.f;
+    }
+    if (Lout == nullptr) return;   // uniform over the workgroup
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int64_t qi = q0 + 16 * rt + r16;
+      const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) load_frag(qf[rt][ks], qrow + 32 * ks);
+      ncq[rt] = qi < T_ ? (int)num_candidates(qi, S, W) : 0;
+      m[rt] = kRefInit;
+      s[rt] = 0.f;
+    }
   }
   const int nc_block = (int)num_candidates(min(qb + 255, T_ - 1), S, W);
   const int ncmin = live ? (int)num_candidates(q0, S, W) : 0;
@@ -461,15 +516,26 @@ hipError_t launch_rank(const SelArgs& a, int J, hipStream_t st) {
   }
 }
 
+template <typename T, int D, int R>
+void launch_score_lse_r(const SelArgs& a, float* L, hipStream_t st) {
+  const dim3 grid((unsigned)a.Hq, (unsigned)((a.T + 255) / 256), (unsigned)a.B);
+  hipLaunchKernelGGL((score_lse_kernel<T, D, R>), grid, dim3(256), 0, st, static_cast<const T*>(a.qh),
+                     static_cast<const T*>(a.ksum), a.bsum, L, a.Hq, a.T, a.NCs, a.S, a.W, a.scale, a.qc);
+}
+
 template <typename T, int D>
 hipError_t launch_select_t(const SelArgs& a, int J, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
-  if (G > 1) {
-    dim3 grid((unsigned)a.Hq, (unsigned)((a.T + 255) / 256), (unsigned)a.B);
+  if (G > 1 || a.qc_r > 0) {   // with Q-Cal fused, the first pass also forms q_hat
+    float* L = G > 1 ? a.L : nullptr;
     KTimer tm(K_SCORE_LSE, st);
-    hipLaunchKernelGGL((score_lse_kernel<T, D>), grid, dim3(256), 0, st,
-                       static_cast<const T*>(a.qh), static_cast<const T*>(a.ksum), a.bsum, a.L,
-                       a.Hq, a.T, a.NCs, a.S, a.W, a.scale);
+    switch (a.qc_r) {
+      case 0: launch_score_lse_r<T, D, 0>(a, L, st); break;
+      case 16: launch_score_lse_r<T, D, 16>(a, L, st); break;
+      case 32: launch_score_lse_r<T, D, 32>(a, L, st); break;
+      case 64: launch_score_lse_r<T, D, 64>(a, L, st); break;
+      default: launch_score_lse_r<T, D, 128>(a, L, st); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -18,7 +18,7 @@ const char* const kNames[K_COUNT] = {
     "idx_fill", "lsel", "window", "chunk_attend", "dec_score", "dec_select",
     "dec_attend", "dec_fuse", "dec_summarize", "v_transpose", "rank_keys", "topk_scores",
     "bwd_rowstat", "bwd_kv", "bwd_dq", "bwd_qhat", "summarize_bwd", "bsa_keys", "bsa_topk",
-    "qcal", "dec_append", "dec_gsel"};
+    "qcal", "dec_append", "dec_gsel", "qcal_zdown"};
 
 struct Rec {
   int id;

@@ -27,7 +27,7 @@
  * and the two variants of the steps before scoring: the calibrated retrieval
  * query and summaries from one shared query per head:
  *
- *   hils_qcal, hils_summarize_shared
+ *   hils_qcal, hils_select_qcal, hils_summarize_shared
  *
  * Notation: B batch, Hq query heads, Hkv key/value heads, G = Hq/Hkv heads per
  * group, d head dimension, S chunk size, W window, k top-k, T tokens,
@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define HILS_ABI_VERSION 2
+#define HILS_ABI_VERSION 3
 
 typedef enum {
     HILS_OK = 0,
@@ -189,6 +189,29 @@ hils_status hils_qcal(const hils_shape* shape, const void* q, const void* hs, co
 hils_status hils_select(const hils_shape* shape, const void* q_hat, const void* k_sum,
                         const float* b_sum, int32_t* sel_idx, float* sel_score,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * hils_select with the query calibration fused into scoring (paper-body page,
+ * implementation: Q-Cal, applied to the retrieval query only; summary page,
+ * practical enhancements).  The down-projection z = W_down hs (fp32, shared by
+ * every head) runs once per token; the first scoring pass then forms each
+ * query's q_hat = q + W_up[h] z, rounds it once and scores with it, and stores
+ * it for the later passes (it is also the caller's q_hat).  The results are bit
+ * for bit those of hils_qcal followed by hils_select.
+ * q, hs, w_down, w_up, d_model, rank: as hils_qcal; k_sum, b_sum, sel_idx,
+ * sel_score: as hils_select; q_hat [B,Hq,T,d] io_dtype out (must not be q).
+ * Workspace: hils_select_qcal_workspace_bytes(shape, rank) (z first, then the
+ * selection's workspace with the same rules as hils_select's; its L table
+ * starts at the first 256-byte boundary after z).  With k = 0 only q_hat is
+ * computed.  Same limits and errors as hils_qcal and hils_select.
+ */
+hils_status hils_select_qcal(const hils_shape* shape, const void* q, const void* hs, const void* w_down,
+                             const void* w_up, int32_t d_model, int32_t rank, const void* k_sum,
+                             const float* b_sum, void* q_hat, int32_t* sel_idx, float* sel_score,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of hils_select_qcal for `shape` and `rank` (0 when unsupported). */
+size_t hils_select_qcal_workspace_bytes(const hils_shape* shape, int32_t rank);
 
 /*
  * Per-group attention and fusion (summary page, Methodology 2, Eq. 10, the
@@ -413,9 +436,10 @@ int hils_abi_version(void);
  *   completed by a decode step), v_transpose, rank_keys,
  *   topk_scores, for the backward calls bwd_rowstat, bwd_kv, bwd_dq,
  *   bwd_qhat and summarize_bwd (the entry lists of the
- *   backward count under the idx_* names), bsa_keys, bsa_topk, qcal, and
- *   for hils_decode_multi dec_append and dec_gsel (its other kernels count
- *   under the dec_* names above).  HILS_E_UNSUPPORTED for an unknown name
+ *   backward count under the idx_* names), bsa_keys, bsa_topk, qcal,
+ *   qcal_zdown (the down-projection of hils_select_qcal, whose fused scoring
+ *   pass counts as score_lse), and for hils_decode_multi dec_append and
+ *   dec_gsel (its other kernels count under the dec_* names above).  HILS_E_UNSUPPORTED for an unknown name
  *   (timing is then left off).
  * hils_timing_get(kernel, total_ms, launches): waits for the recorded events
  *   of that kernel and returns the summed duration and the number of timed

@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_abi_version_and_status_strings():
     L = hils.lib()
-    assert L.hils_abi_version() == 2
+    assert L.hils_abi_version() == 3
     for code in hils.STATUS:
         assert L.hils_status_string(code)
     assert L.hils_status_string(-99) == b"unknown status"
@@ -85,6 +85,30 @@ def test_validation_before_launch():
     # attend: workspace below one KV head's share
     assert L.hils_attend_fuse(ctypes.byref(s), P(16), P(16), P(16), P(16), P(16), P(16), P(16),
                               P(16), 1024, None) == -5
+
+
+def test_select_qcal_validation():
+    """The fused select + Q-Cal call checks everything before launching."""
+    L = hils.lib()
+    P = ctypes.c_void_p
+    s = _shape()
+    need = L.hils_select_qcal_workspace_bytes(ctypes.byref(s), 64)
+    # z (B T rank fp32, 256-byte padded) ahead of the selection's own workspace
+    assert need >= hils.hils_workspace_bytes(s, hils.OP_SELECT) + s.batch * s.seq_len * 64 * 4
+    assert L.hils_select_qcal_workspace_bytes(ctypes.byref(s), 48) == 0
+
+    def call(q=16, qh=32, rank=64, dm=4096, nws=need, shape=s):
+        return L.hils_select_qcal(ctypes.byref(shape), P(q), P(16), P(16), P(16), dm, rank, P(16), P(16),
+                                  P(qh), P(16), P(16), P(16), nws, None)
+
+    assert call(q=0) == -1
+    assert call(q=8) == -4
+    assert call(rank=48) == -8
+    assert call(dm=100) == -8
+    assert call(q=16, qh=16) == -2             # q_hat must not alias q
+    assert call(nws=1024) == -5                  # below z
+    assert call(nws=s.batch * s.seq_len * 64 * 4 + 1024) == -5   # z, but no room for the rank keys
+    assert call(shape=_shape(d=96)) == -8
 
 
 def test_decode_validation():

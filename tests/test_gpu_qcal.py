@@ -159,3 +159,39 @@ def test_summarize_shared_query(hils, dtype):
     assert_close(bs1, obs, 1e-5, what="b'")
     tol = 2e-2 if dtype == "bf16" else 1e-5
     assert_close(ks1, oks, tol, 5e-3 if dtype == "bf16" else 1e-5, what="k'")
+
+
+@pytest.mark.parametrize("name", ["bf16_h8_d128_ragged", "f32_h4_d128_r32", "bf16_h2_d128_r16",
+                                  "bf16_h4_d64_r128", "f32_h1_d64"])
+def test_select_qcal_fused_is_qcal_then_select(hils, name):
+    """Q-Cal fused into the selection's scoring pass stores the same q_hat and
+    makes the same selection and scores as hils_qcal followed by hils_select,
+    bit for bit (G = 1 included, where the pass only forms q_hat); q_hat itself
+    is pinned to the oracle above."""
+    wl, dm, r = QCASES[name]
+    say("select with fused qcal", name)
+    x = wk.make_prefill(wl, seed=34)
+    c = wk.make_qcal(wl, dm, r, seed=34)
+    xd = {k_: (v_.to(DEV) if isinstance(v_, torch.Tensor) else v_) for k_, v_ in x.items()}
+    cd = {k_: v_.to(DEV) for k_, v_ in c.items()}
+    sh = hils.Shape.make(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, wl.W, wl.k, wl.T, wl.torch_dtype)
+    NC = wl.T // wl.S
+    ks = torch.empty((wl.B, wl.Hq, NC, wl.d), dtype=wl.torch_dtype, device=DEV)
+    bs = torch.empty((wl.B, wl.Hq, NC), dtype=torch.float32, device=DEV)
+    hils.hils_summarize(xd["k"], xd["q_land"], ks, bs, sh)
+    # separate: Q-Cal, then the selection on its output
+    qh1 = _gpu_qcal(hils, wl, xd, cd)
+    idx1 = torch.full((wl.B, wl.Hkv, wl.T, wl.k), -7, dtype=torch.int32, device=DEV)
+    sc1 = torch.full((wl.B, wl.Hq, wl.T, wl.k), 7.0, dtype=torch.float32, device=DEV)
+    hils.hils_select(qh1, ks, bs, idx1, sc1, sh)
+    # fused
+    qh2 = torch.full_like(qh1, float("nan"))
+    idx2 = torch.full_like(idx1, -7)
+    sc2 = torch.full_like(sc1, 7.0)
+    hils.hils_select_qcal(xd["q"], cd["h"], cd["w_down"], cd["w_up"], ks, bs, qh2, idx2, sc2, sh)
+    torch.cuda.synchronize()
+    assert torch.equal(qh1.view(torch.int16) if qh1.dtype == torch.bfloat16 else qh1.view(torch.int32),
+                       qh2.view(torch.int16) if qh2.dtype == torch.bfloat16 else qh2.view(torch.int32))
+    assert torch.equal(idx1, idx2)
+    assert torch.equal(sc1.view(torch.int32), sc2.view(torch.int32))
+    _check_qcal(qh2, x, c, wl)
