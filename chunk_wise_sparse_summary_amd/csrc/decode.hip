@@ -611,7 +611,7 @@ __device__ __forceinline__ int share_topk(const DecKArgs& a, HeadSelSmem& sm, in
       uint32_t k2[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) k2[j] = lane + 64 * j < nsv ? sm.pkey[lane + 64 * j] : 0u;
-      nl = list_topk<2>(k2, 2, nsv, topk, lane, sm.sbuf, sm.opos, sm.okey);
+      nl = list_topk<2>(k2, nsv <= 64 ? 1 : 2, nsv, topk, lane, sm.sbuf, sm.opos, sm.okey);
       wave_lds_sync();
       if (lane < nl) sm.opos[lane] = sm.ppos[sm.opos[lane]];
     }

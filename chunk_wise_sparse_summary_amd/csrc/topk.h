@@ -30,7 +30,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // The topk-th largest of one value per lane (with multiplicity), found bit by
 // bit from the top: the largest t with count(x >= t) >= topk.  Only ballots and
-// scalar counts, no cross-lane data movement.
+// scalar counts, no cross-lane data movement.  (Starting below the bits that the
+// wave's smallest and largest values share saves steps but measured slower: the
+// two wave reductions and the data-dependent loop cost more than the steps.)
 __device__ __forceinline__ uint32_t wave_kth_lane_u32(uint32_t x, int topk) {
   uint32_t t = 0;
 #pragma unroll
@@ -56,6 +58,20 @@ __device__ __forceinline__ uint32_t wave_kth_lane_u32(uint32_t x, int topk) {
 template <int J>
 __device__ void wave_topk_u32(const uint32_t (&keys)[J], int jn, int topk, int lane, uint32_t* buf,
                               int32_t* out, uint32_t* out_keys = nullptr) {
+  if (jn == 1) {   // one key per lane: K directly, no bound needed
+    const uint32_t x = keys[0];
+    const uint32_t kstar = wave_kth_lane_u32(x, topk);
+    const int need = topk - __popcll(__ballot(x > kstar));
+    const uint64_t meq = __ballot(x == kstar);
+    const bool sel = x > kstar || (x == kstar && lane_prefix(meq, lane) < need);
+    const uint64_t m = __ballot(sel);
+    if (sel) {
+      const int pos = lane_prefix(m, lane);
+      out[pos] = lane;
+      if (out_keys) out_keys[pos] = x;
+    }
+    return;
+  }
   uint32_t lm = 0;
 #pragma unroll
   for (int j = 0; j < J; ++j)
