@@ -535,18 +535,41 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdKArgs k) {
   float* dst = a.dq + rq * D;
   const int32_t* ir = a.idx + (bgo * T_ + i) * a.topk;
   const int64_t NCs = T_ / a.S;
+  // the selected chunks' parts, slot by slot (the same sum order for every
+  // element); each step loads US slots' pieces of every 16 elements before adding
+  // any, so US * MD loads are in flight instead of one.  A padding slot's piece is
+  // read from slot 0's row (inside the buffer) and dropped by a select.
+  const T* pb = static_cast<const T*>(k.dqp) +
+                ((((int64_t)blockIdx.y * a.B + b) * T_ + i) * a.topk * G + hh) * D + 4 * grp;
+  f32x4_t p[MD];
+#pragma unroll
+  for (int md = 0; md < MD; ++md) p[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int US = 2;
+  for (int s0 = 0; s0 < a.topk; s0 += US) {
+    f32x4_t v[US][MD];
+    bool ok[US];
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+      const int s = s0 + u;
+      const int32_t cs = s < a.topk ? ir[s] : -1;
+      ok[u] = cs >= 0 && cs < NCs;
+      const T* src = pb + (int64_t)(ok[u] ? s : 0) * G * D;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        v[u][md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        load4_add<T>(v[u][md], src + 16 * md);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < US; ++u)
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        if (ok[u]) p[md] += v[u][md];
+  }
 #pragma unroll
   for (int md = 0; md < MD; ++md) {
-    float4 r = make_float4(acc[md][0] * a.scale, acc[md][1] * a.scale, acc[md][2] * a.scale,
-                           acc[md][3] * a.scale);
-    f32x4_t p = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.topk; ++s) {
-      const int32_t cs = ir[s];
-      if (cs < 0 || cs >= NCs) continue;
-      load4_add<T>(p, static_cast<const T*>(k.dqp) +
-                          (((((int64_t)blockIdx.y * a.B + b) * T_ + i) * a.topk + s) * G + hh) * D + 16 * md + 4 * grp);
-    }
-    r.x += p[0]; r.y += p[1]; r.z += p[2]; r.w += p[3];
+    const float4 r = make_float4(acc[md][0] * a.scale + p[md][0], acc[md][1] * a.scale + p[md][1],
+                                 acc[md][2] * a.scale + p[md][2], acc[md][3] * a.scale + p[md][3]);
     *reinterpret_cast<float4*>(dst + 16 * md + 4 * grp) = r;
   }
 }
@@ -570,14 +593,27 @@ __global__ __launch_bounds__(256) void bwd_qhat_kernel(BwdKArgs k) {
 #pragma unroll
   for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
   const int32_t* ir = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * a.topk;
-  for (int s = 0; s < a.topk; ++s) {
-    const int32_t c = ir[s];
-    if (c < 0 || c >= NCs) continue;
-    const float dsh = k.dshat[row * a.topk + s];
-    const T* kr = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * NCs + c) * D + lane * DPL;
+  // US slots per step, their loads issued before any is used (same slot order);
+  // a padding slot reads chunk 0's row and adds nothing
+  constexpr int US = 8;
+  if (NCs > 0)
+    for (int s0 = 0; s0 < a.topk; s0 += US) {
+      float dsh[US], kv[US][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = fmaf(dsh, to_f<T>(kr[e]), acc[e]);
-  }
+      for (int u = 0; u < US; ++u) {
+        const int s = s0 + u;
+        const int32_t c = s < a.topk ? ir[s] : -1;
+        const bool ok = c >= 0 && c < NCs;
+        dsh[u] = ok ? k.dshat[row * a.topk + s] : 0.f;
+        const T* kr = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * NCs + (ok ? c : 0)) * D + lane * DPL;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) kv[u][e] = to_f<T>(kr[e]);
+      }
+#pragma unroll
+      for (int u = 0; u < US; ++u)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(dsh[u], kv[u][e], acc[e]);
+    }
 #pragma unroll
   for (int e = 0; e < DPL; ++e) a.dqh[row * D + lane * DPL + e] = acc[e] * a.scale;
 }
