@@ -207,22 +207,35 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
   }
   const int nst = (nsel + NE - 1) / NE;
   const int ntile = nwt + nst;
+  // The entry word (query << 6 | slot) of row rho of a selected tile, or none.
+  // Words are loaded a tile before the rows they name, so a tile's row loads
+  // never wait on its entry loads.
+  auto word_of = [&](int tile, int rho) -> uint32_t {
+    if (tile < nwt || tile >= ntile) return 0xffffffffu;
+    const int en = (tile - nwt) * NE + rho / G;
+    return en < nsel ? k.el.entries[ebase + en] : 0xffffffffu;
+  };
   // row rho of tile `tile`: (query or entry, head)
-  auto row_of = [&](int tile, int rho, int64_t& i, int& slot) -> bool {
+  auto row_of = [&](int tile, int rho, uint32_t word, int64_t& i, int& slot) -> bool {
     slot = 0;
     if (tile < nwt) {
       i = j0 + (int64_t)tile * NE + rho / G;
       return i <= iw1;
     }
-    const int en = (tile - nwt) * NE + rho / G;
-    if (en >= nsel) {
+    if (word == 0xffffffffu) {
       i = 0;
       return false;
     }
-    const uint32_t word = k.el.entries[ebase + en];
     i = word >> 6;
     slot = (int)(word & 63u);
     return true;
+  };
+  // the rows this thread fetches: its pieces' rows, and for threads < 16 row threadIdx.x
+  uint32_t wp[TR::NP], wst;
+  auto load_words = [&](int tile) {
+#pragma unroll
+    for (int t = 0; t < TR::NP; ++t) wp[t] = word_of(tile, (int)((threadIdx.x + t * kBT) / PK));
+    wst = threadIdx.x < 16 ? word_of(tile, (int)threadIdx.x) : 0xffffffffu;
   };
   auto fetch = [&](int tile, TR& r) {
     const bool selt = tile >= nwt;
@@ -234,7 +247,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
         const int rho = e / PK, p = e % PK;
         int64_t i;
         int slot;
-        if (row_of(tile, rho, i, slot)) {
+        if (row_of(tile, rho, wp[t], i, slot)) {
           const int64_t ro = (((int64_t)b * a.Hq + g * G + rho % G) * T_ + i) * D + p * EPV;
           r.q[t] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.q) + ro);
           r.g[t] = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.dout) + ro);
@@ -246,7 +259,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
       const int rho = threadIdx.x;
       int64_t i;
       int slot;
-      const bool valid = row_of(tile, rho, i, slot);
+      const bool valid = row_of(tile, rho, wst, i, slot);
       const int64_t rq = ((int64_t)b * a.Hq + g * G + rho % G) * T_ + (valid ? i : 0);
       r.L = valid ? a.lse[rq] : 0.f;
       r.Dr = valid ? k.Drow[rq] : 0.f;
@@ -270,7 +283,11 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
   float dbs_acc = 0.f;
   const int hk = lane / LPH, lk = lane % LPH;   // this lane's dk' head and its dims
   TR nxt;
-  if (ntile > 0) fetch(0, nxt);
+  if (ntile > 0) {
+    load_words(0);
+    fetch(0, nxt);
+    load_words(1);
+  }
   for (int tile = 0; tile < ntile; ++tile) {
     const bool selt = tile >= nwt;
     __syncthreads();   // the previous tile is done with the shared tiles
@@ -293,7 +310,10 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
       sm.ri[rho] = nxt.i;
       sm.rs[rho] = nxt.slot;
     }
-    if (tile + 1 < ntile) fetch(tile + 1, nxt);   // in flight during this tile
+    if (tile + 1 < ntile) {   // in flight during this tile: the next tile's rows, the words after
+      fetch(tile + 1, nxt);
+      load_words(tile + 2);
+    }
     __syncthreads();
     // this wave's 16 tokens: S^T and U^T (token 16 wave + 4 grp + q4, row r16)
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, ua = f32x4_t{0.f, 0.f, 0.f, 0.f};
