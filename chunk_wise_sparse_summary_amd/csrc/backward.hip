@@ -594,14 +594,19 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdKArgs k) {
   }
 }
 
-// ---------------------------------------------------------------- dq_hat, dk', db'
-// dq_hat_i = scale sum_slots d s_hat k'_c: one wave per row, lanes over d.
+// ---------------------------------------------------------------- dq_hat
+// dq_hat_i = scale sum_slots d s_hat k'_c: one wave per row.  Lanes take 16-byte
+// pieces of the k' rows, so one load instruction covers SG slots' rows at once;
+// the SG slot groups' sums are added across lanes at the end.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void bwd_qhat_kernel(BwdKArgs k) {
   const BwdArgs& a = k.a;
-  constexpr int DPL = D / kWave;
+  constexpr int EPV = 16 / (int)sizeof(T);   // elements per 16-byte piece
+  constexpr int PPR = D / EPV;               // pieces per row
+  constexpr int SG = kWave / PPR;            // slot groups
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;   // (b, h, i)
   const int lane = threadIdx.x % kWave;
+  const int sg = lane / PPR, pc = lane % PPR;
   const int64_t nrows = (int64_t)a.B * a.Hq * a.T;
   if (row >= nrows) return;
   const int64_t i = row % a.T;
@@ -609,33 +614,44 @@ __global__ __launch_bounds__(256) void bwd_qhat_kernel(BwdKArgs k) {
   const int b = (int)(row / (a.T * a.Hq));
   const int g = h / G;
   const int64_t NCs = a.T / a.S;
-  float acc[DPL];
+  float acc[EPV];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
   const int32_t* ir = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i) * a.topk;
-  // US slots per step, their loads issued before any is used (same slot order);
-  // a padding slot reads chunk 0's row and adds nothing
-  constexpr int US = 8;
+  const T* kb = static_cast<const T*>(a.ksum) + ((int64_t)b * a.Hq + h) * NCs * D + pc * EPV;
+  // US slot steps per batch, their loads issued before any is used; a padding
+  // slot reads chunk 0's row and adds nothing
+  constexpr int US = 4;
   if (NCs > 0)
-    for (int s0 = 0; s0 < a.topk; s0 += US) {
-      float dsh[US], kv[US][DPL];
+    for (int s0 = 0; s0 < a.topk; s0 += US * SG) {
+      float dsh[US];
+      uint4 kv[US];
 #pragma unroll
       for (int u = 0; u < US; ++u) {
-        const int s = s0 + u;
+        const int s = s0 + u * SG + sg;
         const int32_t c = s < a.topk ? ir[s] : -1;
         const bool ok = c >= 0 && c < NCs;
         dsh[u] = ok ? k.dshat[row * a.topk + s] : 0.f;
-        const T* kr = static_cast<const T*>(a.ksum) + (((int64_t)b * a.Hq + h) * NCs + (ok ? c : 0)) * D + lane * DPL;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) kv[u][e] = to_f<T>(kr[e]);
+        kv[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)(ok ? c : 0) * D);
       }
 #pragma unroll
-      for (int u = 0; u < US; ++u)
+      for (int u = 0; u < US; ++u) {
+        const T* x = reinterpret_cast<const T*>(&kv[u]);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] = fmaf(dsh[u], kv[u][e], acc[e]);
+        for (int e = 0; e < EPV; ++e) acc[e] = fmaf(dsh[u], to_f<T>(x[e]), acc[e]);
+      }
     }
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) a.dqh[row * D + lane * DPL + e] = acc[e] * a.scale;
+  for (int e = 0; e < EPV; ++e)
+#pragma unroll
+    for (int o = PPR; o < kWave; o <<= 1) acc[e] += __shfl_xor(acc[e], o, kWave);
+  if (sg == 0) {
+    float* dst = a.dqh + row * D + pc * EPV;
+#pragma unroll
+    for (int e = 0; e < EPV; e += 4)
+      *reinterpret_cast<float4*>(dst + e) =
+          make_float4(acc[e] * a.scale, acc[e + 1] * a.scale, acc[e + 2] * a.scale, acc[e + 3] * a.scale);
+  }
 }
 
 // ---------------------------------------------------------------- summaries
