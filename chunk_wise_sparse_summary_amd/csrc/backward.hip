@@ -288,6 +288,15 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
     fetch(0, nxt);
     load_words(1);
   }
+  // this wave's 16 key and value rows are the A operands of every tile's S and
+  // U: held in registers for the whole chunk instead of re-read from LDS per tile
+  __syncthreads();   // the staged chunk
+  Frag<T> akf[KS], avf[KS];
+#pragma unroll
+  for (int kq = 0; kq < KS; ++kq) {
+    load_frag_swz<PK>(akf[kq], sm.ks, 16 * wave + r16, 8 * grp + 32 * kq);
+    load_frag_swz<PK>(avf[kq], sm.vs, 16 * wave + r16, 8 * grp + 32 * kq);
+  }
   for (int tile = 0; tile < ntile; ++tile) {
     const bool selt = tile >= nwt;
     __syncthreads();   // the previous tile is done with the shared tiles
@@ -319,13 +328,11 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
     f32x4_t sa = f32x4_t{0.f, 0.f, 0.f, 0.f}, ua = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kq = 0; kq < KS; ++kq) {
-      Frag<T> bq, bg, ak, av;
+      Frag<T> bq, bg;
       load_frag(bq, sm.qt + r16 * OP + 8 * grp + 32 * kq);
       load_frag(bg, sm.gt + r16 * OP + 8 * grp + 32 * kq);
-      load_frag_swz<PK>(ak, sm.ks, 16 * wave + r16, 8 * grp + 32 * kq);
-      load_frag_swz<PK>(av, sm.vs, 16 * wave + r16, 8 * grp + 32 * kq);
-      mma(sa, ak, bq);
-      mma(ua, av, bg);
+      mma(sa, akf[kq], bq);
+      mma(ua, avf[kq], bg);
     }
     const int64_t i = sm.ri[r16];
     const bool valid = i >= 0;
