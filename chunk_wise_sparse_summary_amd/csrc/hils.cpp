@@ -36,7 +36,7 @@ hils_status check_shape(const hils_shape* s, Mode mode) {
     if (!hils::decode_supported(s->seq_len, s->chunk, s->window, s->top_k, G)) return HILS_E_UNSUPPORTED;
     if (s->seq_len > (int64_t(1) << 31)) return HILS_E_UNSUPPORTED;
   } else if (mode == kPrefill) {
-    if (s->seq_len / s->chunk > 4096) return HILS_E_UNSUPPORTED;  // <= 4096 chunks per sequence
+    if (s->seq_len / s->chunk > 8192) return HILS_E_UNSUPPORTED;  // <= 8192 chunks per sequence
   }
   return HILS_OK;
 }

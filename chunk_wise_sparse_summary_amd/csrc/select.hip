@@ -360,15 +360,14 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
         make_uint4(order_key(r[0]), order_key(r[1]), order_key(r[2]), order_key(r[3]));
     if (c0 % 64 == 48 || c0 + 16 >= nc_wave) {   // a run of 64 candidates, or the wave's last
       wave_lds_sync();
-      // (one group's keys, T x NCP words, stay below 2^32 words)
-      const uint32_t qw0 = (uint32_t)(qb + 16 * wave);
-      const uint32_t off = qw0 * NCP + (uint32_t)(c0 - c0 % 64) + 4u * (lane % 16);
+      const int64_t qw0 = qb + 16 * wave;
+      const int64_t off = qw0 * NCP + (c0 - c0 % 64) + 4 * (lane % 16);
       const int qr = lane / 16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int qq = 4 * j + qr;
-        if (qw0 + qq < (uint32_t)T_)
-          *reinterpret_cast<uint4*>(keys + off + (uint32_t)qq * NCP) =
+        if (qw0 + qq < T_)
+          *reinterpret_cast<uint4*>(keys + off + (int64_t)qq * NCP) =
               *reinterpret_cast<const uint4*>(kw + qq * KSP + 4 * (lane % 16));
       }
       wave_lds_sync();
@@ -512,7 +511,8 @@ hipError_t launch_rank(const SelArgs& a, int J, hipStream_t st) {
     case 4: return launch_rank_j<T, D, G, 4>(a, st);
     case 16: return launch_rank_j<T, D, G, 16>(a, st);
     case 32: return launch_rank_j<T, D, G, 32>(a, st);
-    default: return launch_rank_j<T, D, G, 64>(a, st);
+    case 64: return launch_rank_j<T, D, G, 64>(a, st);
+    default: return launch_rank_j<T, D, G, 128>(a, st);
   }
 }
 
@@ -718,7 +718,8 @@ hipError_t launch_bsa_g(const SelArgs& a, int J, hipStream_t st) {
     case 4: return launch_bsa_j<T, D, G, 4>(a, st);
     case 16: return launch_bsa_j<T, D, G, 16>(a, st);
     case 32: return launch_bsa_j<T, D, G, 32>(a, st);
-    default: return launch_bsa_j<T, D, G, 64>(a, st);
+    case 64: return launch_bsa_j<T, D, G, 64>(a, st);
+    default: return launch_bsa_j<T, D, G, 128>(a, st);
   }
 }
 
@@ -738,7 +739,8 @@ int pick_J(int64_t NCs) {
   if (need <= 4) return 4;
   if (need <= 16) return 16;
   if (need <= 32) return 32;
-  return 64;
+  if (need <= 64) return 64;
+  return 128;   // up to 8192 candidates: 128 keys per lane
 }
 
 }  // namespace

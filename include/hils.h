@@ -177,7 +177,7 @@ hils_status hils_qcal(const hils_shape* shape, const void* q, const void* hs, co
  * b_sum     [B, Hq, T/S]         fp32
  * sel_idx   [B, Hkv, T, k]       int32 out: chunk ids ascending, -1 padded
  * sel_score [B, Hq, T, k]        fp32 out: each head's s_hat at sel_idx, -inf padded
- * Requires T <= 64 * 4096 (at most 4096 chunks) for this build.
+ * Requires T <= 64 * 8192 (at most 8192 chunks: the 512K context) for this build.
  * The workspace holds each head's LSE and the rank keys of every (b, group); a
  * workspace smaller than hils_workspace_bytes() but holding at least one
  * (b, group)'s keys runs the same computation a few (b, group) pairs at a time.

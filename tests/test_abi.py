@@ -68,7 +68,7 @@ def test_validation_before_launch():
     assert _call_select(_shape(Hq=30)) == -2                       # Hq % Hkv
     assert _call_select(_shape(d=96)) == -8                        # unsupported head dim
     assert _call_select(_shape(k=65)) == -8
-    assert _call_select(_shape(T=64 * 4097)) == -8                 # > 4096 chunks
+    assert _call_select(_shape(T=64 * 8193)) == -8                 # > 8192 chunks
     assert _call_select(_shape(), nws=10) == -5                    # workspace
     bad = _shape()
     bad.io_dtype = 7

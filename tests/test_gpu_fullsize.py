@@ -222,6 +222,71 @@ def _decode_run(hils, wl, seed, nsteps, check_steps, needles=False):
     return hist, meta
 
 
+def test_prefill_512k_sampled(hils):
+    """The 512K context as one prefill (8192 chunks, 128 rank keys per lane): the
+    selection and the chunk pass each run one KV group at a time (workspaces of
+    one group's share), sampled rows against the oracle."""
+    wl = wk.custom(name="512k_prefill", kind="prefill", dtype="bf16", B=1, Hq=32, Hkv=8, d=128,
+                   T=524288, S=64, k=32, W=1024, head_scale=(0.5, 2.0))
+    B, Hq, Hkv, d, S, W, k, T = wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, wl.W, wl.k, wl.T
+    G = Hq // Hkv
+    say("512k prefill: drawing inputs on the device")
+    x = wk.make_prefill(wl, seed=5, device=DEV)
+    NC = T // S
+    shape = hils.Shape.make(B, Hq, Hkv, d, S, W, k, T, torch.bfloat16)
+    k_sum = torch.empty((B, Hq, NC, d), dtype=torch.bfloat16, device=DEV)
+    b_sum = torch.empty((B, Hq, NC), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, Hkv, T, k), dtype=torch.int32, device=DEV)
+    ssel = torch.empty((B, Hq, T, k), dtype=torch.float32, device=DEV)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=DEV)
+    # one (b, group) pair's share of each workspace: the calls make passes
+    per_sel = T * 64 * 128 * 4                       # rank keys of one group
+    per_att = T * k * G * d * 2                      # partial records of one group
+    n_sel = hils.hils_workspace_bytes(shape, hils.OP_SELECT) - (B * Hkv - 1) * per_sel
+    n_att = hils.hils_workspace_bytes(shape, hils.OP_ATTEND_FUSE) - (Hkv - 1) * per_att
+    say("512k prefill: workspaces %.1f + %.1f GiB" % (n_sel / 2**30, n_att / 2**30))
+    ws_sel = torch.empty(n_sel, dtype=torch.uint8, device=DEV)
+    ws_att = torch.empty(n_att, dtype=torch.uint8, device=DEV)
+    say("512k prefill: GPU path")
+    hils.hils_summarize(x["k"], x["q_land"], k_sum, b_sum, shape)
+    hils.hils_select(x["q_hat"], k_sum, b_sum, idx, ssel, shape, ws_sel)
+    hils.hils_attend_fuse(x["q"], x["k"], x["v"], idx, ssel, out, lse, shape, ws_att)
+    torch.cuda.synchronize()
+    del ws_sel, ws_att
+    _free()
+    _check_idx_all_rows(idx, T, S, W, k)
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.Generator(np.random.PCG64(512))
+    pos = sorted(set([1087, 131071, 262143, 262144, 393216, T - 1] + rng.integers(1087, T, size=10).tolist()))
+    say("512k prefill: oracle on %d positions x %d groups" % (len(pos), Hkv))
+    k_h, v_h, ql_h = x["k"].cpu(), x["v"].cpu(), x["q_land"].cpu()
+    oks, obs = oracle.summarize(k_h, ql_h, S, Hq, ks_round=oracle.ks_round_for("bf16"))
+    assert_close(b_sum.cpu(), obs, 1e-5, what="b'")
+    assert_close(k_sum.cpu(), oks, 2e-2, 5e-3, what="k'")
+    q_rows = x["q"][:, :, pos].cpu()
+    qh_rows = x["q_hat"][:, :, pos].cpu()
+    rb, rg, rq = rows_layout(B, Hkv, range(len(pos)))
+    ri = np.asarray(pos, np.int64)[rq]
+    orc = oracle.rows(rb, rg, ri, rq, q_rows, qh_rows, k_h, v_h, oks, obs, S=S, W=W, topk=k,
+                      want_r=True)
+    gi = gather_rows(idx, rb, rg, ri, 1)[:, 0].astype(np.int64)
+    res = check_selection(gi, orc, k, TAU_E2E_BF16)
+    say("  decided %d undecided %d differ %d" % (res["decided"], res["undecided"], res["differ"].sum()))
+    assert res["decided"] > 0
+    want_out, want_lse = orc["out"].copy(), orc["lse"].copy()
+    dm = res["differ"]
+    if dm.any():
+        alt = oracle.rows(rb[dm], rg[dm], ri[dm], rq[dm], q_rows, qh_rows, k_h, v_h, oks, obs, S=S,
+                          W=W, topk=k, forced_idx=gi[dm])
+        want_out[dm], want_lse[dm] = alt["out"], alt["lse"]
+    t = tol_out(torch.bfloat16)
+    assert_close(gather_rows(out, rb, rg, ri, G), want_out, t["max_abs"], t["rel_l2"], what="out")
+    assert_close(gather_rows(lse, rb, rg, ri, G), want_lse, tol_lse(torch.bfloat16), what="lse")
+    del x, k_sum, b_sum, idx, ssel, out, lse
+    _free()
+
+
 def test_decode_512k_sampled(hils):
     """Four 512K-token sequences, through a chunk completion (step 63)."""
     wl = wk.CONFIGS["512k_decode"]
