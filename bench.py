@@ -436,6 +436,9 @@ def time_decode_multi(hils, wl, cache, shape, ks, bs, M, calls, nrep=2, warm=4):
     return times, kern
 
 
+PREFILL_KERNELS = ("summarize", "score_lse", "rank_keys", "topk_scores", "lsel", "idx_count",
+                   "idx_scan_tiles", "idx_scan_buckets", "idx_fill", "v_transpose", "window",
+                   "chunk_attend")
 BWD_KERNELS = ["idx_count", "idx_scan_tiles", "idx_scan_buckets", "idx_fill", "bwd_rowstat", "bwd_kv",
                "bwd_dq", "bwd_qhat", "summarize_bwd"]
 
@@ -609,6 +612,58 @@ def time_qcal(hils, x, wl, shape, d_model=4096, rank=64, reps=5):
     return res
 
 
+def time_prefill_512k(hils, dev, reps=2):
+    """The 512K context as one prefill (B=1, 32/8 heads, d=128, S=64, k=32, W=1024,
+    per-head scales): 8192 chunks, selection and chunk pass one KV group at a time
+    (workspaces of one group's share).  Median of `reps` calls after a warm-up,
+    and a per-kernel breakdown from one more call."""
+    import torch
+    import workloads as wk
+    wl = wk.custom(name="512k_prefill", kind="prefill", dtype="bf16", B=1, Hq=32, Hkv=8, d=128,
+                   T=524288, S=64, k=32, W=1024, head_scale=(0.5, 2.0))
+    x = wk.make_prefill(wl, seed=5, device=dev)
+    sh = hils.Shape.make(wl.B, wl.Hq, wl.Hkv, wl.d, wl.S, wl.W, wl.k, wl.T, torch.bfloat16)
+    G = wl.Hq // wl.Hkv
+    per_sel = wl.T * 64 * 128 * 4
+    per_att = wl.T * wl.k * G * wl.d * 2
+    wss = torch.empty(hils.hils_workspace_bytes(sh, hils.OP_SELECT) - (wl.B * wl.Hkv - 1) * per_sel,
+                      dtype=torch.uint8, device=dev)
+    wsa = torch.empty(hils.hils_workspace_bytes(sh, hils.OP_ATTEND_FUSE) - (wl.Hkv - 1) * per_att,
+                      dtype=torch.uint8, device=dev)
+
+    def run():
+        return hils.prefill(x["q"], x["k"], x["v"], x["q_land"], x["q_hat"], S=wl.S, W=wl.W, topk=wl.k,
+                            ws_select=wss, ws_attend=wsa)
+    run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b_.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b_))
+    ms = float(np.median(ts))
+    names = list(PREFILL_KERNELS)
+    hils.hils_timing_enable(names)
+    run()
+    torch.cuda.synchronize()
+    kern = {}
+    for kn in names:
+        tms, nl = hils.hils_timing_get(kn)
+        if nl:
+            kern[kn] = {"ms": tms, "launches": nl}
+    hils.hils_timing_enable(None)
+    af = attended_flops(wl.B, wl.Hq, wl.T, wl.d, wl.S, wl.W, wl.k)
+    del x, wss, wsa
+    return {"ms_median": ms, "tokens_per_s": wl.B * wl.T / (ms * 1e-3), "attended_flops": af,
+            "mfma_frac": af / (ms * 1e-3) / PEAK_BF16, "kernels_ms": kern,
+            "note": "median of %d calls of summarize + select + attend_fuse after a warm-up; "
+                    "one KV group per selection and chunk pass (16 + 22 GiB of workspace)" % reps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -730,9 +785,7 @@ def main():
         del src, dst
     # per-kernel HIP events around the prefill kernels only: events between the
     # few-microsecond decode kernels would stretch the decode step they measure
-    timed_kernels = ["summarize", "score_lse", "rank_keys", "topk_scores", "lsel", "idx_count",
-                     "idx_scan_tiles", "idx_scan_buckets", "idx_fill", "v_transpose", "window",
-                     "chunk_attend"]
+    timed_kernels = list(PREFILL_KERNELS)
     dec_kernels = ["dec_score", "dec_select", "dec_attend", "dec_fuse", "dec_summarize"]
     log("warmup")
     for _ in range(args.warmup):
@@ -971,6 +1024,12 @@ def main():
                                     "(4 chunk completions per pass); kernels_us from a third pass "
                                     "with per-kernel events"}
         del c4, ks4, bs4
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        # ---- 512K prefill (the 512K context in one prefill: 8192 chunks)
+        log("512K prefill")
+        res["prefill_512k"] = time_prefill_512k(hils, dev)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(x, wl)

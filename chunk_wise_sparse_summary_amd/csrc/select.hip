@@ -434,7 +434,7 @@ void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
   if (nc <= topk) {
     if (lane < topk) sel[wave][lane] = lane < nc ? lane : -1;
     nsel = nc;
-  } else {
+  } else if constexpr (J <= 64) {
     const uint32_t* rrow = keys + i * (64 * J);
     const int jn = (nc + 63) / 64;
     uint32_t kv[J];
@@ -444,6 +444,49 @@ void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
       kv[j] = (j < jn && c < nc) ? rrow[c] : 0u;
     }
     wave_topk_u32<J>(kv, jn, topk, lane, sbuf[wave], sel[wave]);
+    nsel = topk;
+  } else {
+    // more keys than a lane holds: the top-k of each half (64 J/2 candidates),
+    // then the top-k of the two lists, kept in candidate order (so equal keys
+    // still go to the lower chunk)
+    constexpr int JH = J / 2;
+    __shared__ uint32_t hkey[4][64], mkey[4][128];
+    __shared__ int32_t hpos[4][64], mid[4][128];
+    const uint32_t* rrow = keys + i * (64 * J);
+    int n2 = 0;
+    auto half = [&](const int base) {   // candidates [base, base + 64 JH)
+      const int nch = min(nc - base, 64 * JH);
+      const int jn = (nch + 63) / 64;
+      uint32_t kv[JH];
+#pragma unroll
+      for (int j = 0; j < JH; ++j) {
+        const int c = lane + 64 * j;
+        kv[j] = (j < jn && c < nch) ? rrow[base + c] : 0u;
+      }
+      int n = nch;
+      if (nch > topk) {
+        wave_topk_u32<JH>(kv, jn, topk, lane, sbuf[wave], hpos[wave], hkey[wave]);
+        n = topk;
+      } else if (lane < nch) {   // a short half: every candidate (one per lane)
+        hpos[wave][lane] = lane;
+        hkey[wave][lane] = kv[0];
+      }
+      wave_lds_sync();
+      if (lane < n) {
+        mkey[wave][n2 + lane] = hkey[wave][lane];
+        mid[wave][n2 + lane] = base + hpos[wave][lane];
+      }
+      n2 += n;
+      wave_lds_sync();
+    };
+    half(0);
+    if (nc > 64 * JH) half(64 * JH);
+    uint32_t k2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) k2[j] = lane + 64 * j < n2 ? mkey[wave][lane + 64 * j] : 0u;
+    const int n = list_topk<2>(k2, (n2 + 63) / 64, n2, topk, lane, sbuf[wave], hpos[wave], hkey[wave]);
+    wave_lds_sync();
+    if (lane < topk) sel[wave][lane] = lane < n ? mid[wave][hpos[wave][lane]] : -1;
     nsel = topk;
   }
   wave_lds_sync();
