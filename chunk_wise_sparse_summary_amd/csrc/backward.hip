@@ -27,6 +27,8 @@
 //   bwd_qhat     dq_hat per row.
 //   sum_bwd      Eq. 8 backward per (b, group, chunk): dq' and dk += ... .
 #include "attend_tiles.h"
+#include <type_traits>
+
 #include "hils_internal.h"
 #include "topk.h"   // wave_lds_sync
 
@@ -507,9 +509,10 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdKArgs k) {
   constexpr int KS = D / 32, MD = D / 16;
   constexpr int NE = 16 / G;
   constexpr int QB = 4 * NE;   // queries per workgroup
-  __shared__ __align__(16) T ks[kS * D];
-  __shared__ __align__(16) T vs[kS * D];
+  __shared__ __align__(16) T kvs[2 * kS * D];   // K then V tiles; the window part of dq at the end
   __shared__ __align__(16) T kt[D * kS];
+  T* ks = kvs;
+  T* vs = kvs + kS * D;
   const int g = k.g0 + blockIdx.y, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -558,46 +561,69 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdKArgs k) {
       }
     pv_tile<T, D>(kt, ds, acc, r16, grp);
   }
-  if (!valid) return;
-  float* dst = a.dq + rq * D;
-  const int32_t* ir = a.idx + (bgo * T_ + i) * a.topk;
-  const int64_t NCs = T_ / a.S;
-  // the selected chunks' parts, slot by slot (the same sum order for every
-  // element); each step loads US slots' pieces of every 16 elements before adding
-  // any, so US * MD loads are in flight instead of one.  A padding slot's piece is
-  // read from slot 0's row (inside the buffer) and dropped by a select.
-  const T* pb = static_cast<const T*>(k.dqp) +
-                ((((int64_t)blockIdx.y * a.B + b) * T_ + i) * a.topk * G + hh) * D + 4 * grp;
-  f32x4_t p[MD];
+  // The window part goes through LDS (the K/V tiles are free now), so that the
+  // selected chunks' dq parts are read as whole 16-byte row pieces, RPI rows
+  // per load instruction, and summed slot by slot (the same order for every
+  // element).  A padding slot's piece is read from slot 0's row (inside the
+  // buffer) and dropped by a select.
+  __syncthreads();   // every wave is done with the staged chunk
+  float* accl = reinterpret_cast<float*>(kvs) + wave * 16 * D;   // [16 rows][D]
 #pragma unroll
-  for (int md = 0; md < MD; ++md) p[md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) accl[r16 * D + 16 * md + 4 * grp + e] = acc[md][e] * a.scale;
+  wave_lds_sync();
+  constexpr int EPV = 16 / (int)sizeof(T), PPR = D / EPV, RPI = kWave / PPR, NR = 16 / RPI;
+  using Raw = typename std::conditional<sizeof(T) == 2, uint4, float4>::type;   // EPV elements
+  const int pr = lane % PPR, rr0 = lane / PPR;   // this lane's piece and first row
+  const int64_t NCs = T_ / a.S;
+  float sum[NR][EPV];
+  const int32_t* irr[NR];
+  const T* pbr[NR];
+  bool vr[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int r = rr0 + RPI * j;   // row r of the wave: query r / G, head r % G
+    const int64_t qj = qb0 + wave * NE + r / G;
+    vr[j] = qj < T_;
+    const int64_t qc = vr[j] ? qj : T_ - 1;
+    irr[j] = a.idx + (bgo * T_ + qc) * a.topk;
+    pbr[j] = static_cast<const T*>(k.dqp) +
+             ((((int64_t)blockIdx.y * a.B + b) * T_ + qc) * a.topk * G + r % G) * D + pr * EPV;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) sum[j][e] = accl[r * D + pr * EPV + e];
+  }
   constexpr int US = 2;
   for (int s0 = 0; s0 < a.topk; s0 += US) {
-    f32x4_t v[US][MD];
-    bool ok[US];
-#pragma unroll
-    for (int u = 0; u < US; ++u) {
-      const int s = s0 + u;
-      const int32_t cs = s < a.topk ? ir[s] : -1;
-      ok[u] = cs >= 0 && cs < NCs;
-      const T* src = pb + (int64_t)(ok[u] ? s : 0) * G * D;
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        v[u][md] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        load4_add<T>(v[u][md], src + 16 * md);
-      }
-    }
+    Raw v[US][NR];
+    bool ok[US][NR];
 #pragma unroll
     for (int u = 0; u < US; ++u)
 #pragma unroll
-      for (int md = 0; md < MD; ++md)
-        if (ok[u]) p[md] += v[u][md];
+      for (int j = 0; j < NR; ++j) {
+        const int s = s0 + u;
+        const int32_t cs = s < a.topk ? irr[j][s] : -1;
+        ok[u][j] = cs >= 0 && cs < NCs;
+        v[u][j] = *reinterpret_cast<const Raw*>(pbr[j] + (int64_t)(ok[u][j] ? s : 0) * G * D);
+      }
+#pragma unroll
+    for (int u = 0; u < US; ++u)
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const T* x = reinterpret_cast<const T*>(&v[u][j]);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) sum[j][e] += ok[u][j] ? to_f<T>(x[e]) : 0.f;
+      }
   }
 #pragma unroll
-  for (int md = 0; md < MD; ++md) {
-    const float4 r = make_float4(acc[md][0] * a.scale + p[md][0], acc[md][1] * a.scale + p[md][1],
-                                 acc[md][2] * a.scale + p[md][2], acc[md][3] * a.scale + p[md][3]);
-    *reinterpret_cast<float4*>(dst + 16 * md + 4 * grp) = r;
+  for (int j = 0; j < NR; ++j) {
+    if (!vr[j]) continue;
+    const int r = rr0 + RPI * j;
+    const int64_t qj = qb0 + wave * NE + r / G;
+    float* dst = a.dq + (((int64_t)b * a.Hq + g * G + r % G) * T_ + qj) * D + pr * EPV;
+#pragma unroll
+    for (int e = 0; e < EPV; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(sum[j][e], sum[j][e + 1], sum[j][e + 2], sum[j][e + 3]);
   }
 }
 
