@@ -647,8 +647,9 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
         for (int j = 0; j < U; ++j) {
           const bool in = s + j < a.topk;
           ix[j] = in ? irow[s + j] : -1;
-          u[j] = in ? *reinterpret_cast<const uint4*>(prow + (int64_t)(s + j) * G * D)
-                    : make_uint4(0u, 0u, 0u, 0u);
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};   // read once: streamed past the caches
+          if (in) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(prow + (int64_t)(s + j) * G * D));
+          u[j] = make_uint4(v[0], v[1], v[2], v[3]);
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {

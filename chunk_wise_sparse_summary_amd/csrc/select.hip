@@ -367,8 +367,8 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
       for (int j = 0; j < 4; ++j) {
         const int qq = 4 * j + qr;
         if (qw0 + qq < T_)
-          *reinterpret_cast<uint4*>(keys + off + (int64_t)qq * NCP) =
-              *reinterpret_cast<const uint4*>(kw + qq * KSP + 4 * (lane % 16));
+          __builtin_nontemporal_store(*reinterpret_cast<const u32v<4>*>(kw + qq * KSP + 4 * (lane % 16)),
+                                      reinterpret_cast<u32v<4>*>(keys + off + (int64_t)qq * NCP));
       }
       wave_lds_sync();
     }
@@ -441,7 +441,7 @@ void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       const int c = lane + 64 * j;
-      kv[j] = (j < jn && c < nc) ? rrow[c] : 0u;
+      kv[j] = (j < jn && c < nc) ? __builtin_nontemporal_load(rrow + c) : 0u;
     }
     wave_topk_u32<J>(kv, jn, topk, lane, sbuf[wave], sel[wave]);
     nsel = topk;
@@ -461,7 +461,7 @@ void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
 #pragma unroll
       for (int j = 0; j < JH; ++j) {
         const int c = lane + 64 * j;
-        kv[j] = (j < jn && c < nch) ? rrow[base + c] : 0u;
+        kv[j] = (j < jn && c < nch) ? __builtin_nontemporal_load(rrow + base + c) : 0u;
       }
       int n = nch;
       if (nch > topk) {
