@@ -20,9 +20,10 @@
 // each row's partials with coalesced loads:
 //   out_i = exp(log Z_win - L) o_win + exp(L_sel - L) * sum_slots partial,
 //   L = LSE(L_sel, log Z_win).
-// The (query, slot) lists per chunk are built deterministically: per 64-query
-// tile an LDS bitmap of which queries chose each chunk, a column scan over
-// tiles and a scan over chunks give every entry a fixed position.
+// The (query, slot) lists per chunk are built deterministically: per tile of
+// 1024 queries each chunk's count (from LDS bitmaps of which of 64 queries chose
+// it), a column scan over tiles and a scan over chunks give every entry a fixed
+// position, in query order within its chunk.
 //
 // Score tiles are computed transposed, S^T = K Q^T (tokens x rows), so each lane
 // holds one row's scores for 16 tokens; the same registers, cast to the operand
@@ -52,29 +53,45 @@ struct IdxArgs {
   int64_t T, NCs, ntiles;
 };
 
-// Bitmap of the tile's queries that selected each chunk.
-__device__ void build_bitmap(const IdxArgs& a, uint64_t* bm, int b, int g, int64_t t) {
-  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) bm[c] = 0ull;
-  __syncthreads();
-  const int64_t i0 = t * 64;
-  const int n = 64 * a.topk;
+// Queries per counting tile (the column scan runs over T / kIdxTile tiles) and
+// per ranking sub-tile (one 64-bit LDS bitmap word per chunk).
+constexpr int kIdxTile = 1024;
+constexpr int kIdxSub = 64;
+
+// Sets bit ql of chunk c's word for every entry (query i0 + ql, slot) of the
+// sub-tile of 64 queries at i0 (a chunk listed twice in a row counts once).
+__device__ __forceinline__ void sub_bitmap(const IdxArgs& a, uint64_t* bm, const int32_t* row, int64_t i0) {
+  const int n = kIdxSub * a.topk;
   for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    const int ql = e / a.topk, s = e % a.topk;
-    const int64_t i = i0 + ql;
-    if (i >= a.T) continue;
-    const int32_t c = a.idx[(((int64_t)b * a.Hkv + g) * a.T + i) * a.topk + s];
+    const int ql = e / a.topk;
+    if (i0 + ql >= a.T) break;
+    const int32_t c = row[e];
     if (c >= 0 && c < a.NCs) atomicOr((unsigned long long*)&bm[c], 1ull << ql);
   }
-  __syncthreads();
 }
 
+// Queries of the tile of kIdxTile queries that chose each chunk of (b, g), one
+// sub-tile bitmap at a time.
 __global__ __launch_bounds__(256) void idx_count_kernel(IdxArgs a) {
   extern __shared__ uint64_t bm[];
+  int32_t* cnt = reinterpret_cast<int32_t*>(bm + a.NCs);
   const int64_t t = blockIdx.x;
   const int g = blockIdx.y, b = blockIdx.z;
-  build_bitmap(a, bm, b, g, t);
+  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) {
+    cnt[c] = 0;
+    bm[c] = 0ull;
+  }
+  for (int64_t i0 = t * kIdxTile; i0 < min<int64_t>((t + 1) * kIdxTile, a.T); i0 += kIdxSub) {
+    __syncthreads();
+    sub_bitmap(a, bm, a.idx + (((int64_t)b * a.Hkv + g) * a.T + i0) * a.topk, i0);
+    __syncthreads();
+    for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) {   // each thread its own chunks
+      cnt[c] += __popcll(bm[c]);
+      bm[c] = 0ull;
+    }
+  }
   int32_t* out = a.tile_cnt + (((int64_t)b * a.Hkv + g) * a.ntiles + t) * a.NCs;
-  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) out[c] = __popcll(bm[c]);
+  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) out[c] = cnt[c];
 }
 
 // Column scan over tiles: exclusive offsets in place, totals to bcount.  A block
@@ -128,11 +145,14 @@ __global__ __launch_bounds__(1024) void idx_scan_buckets_kernel(IdxArgs a) {
   }
 }
 
-// Entries at their final positions.  Each chunk's position base for this tile
-// (its bucket's base, relative to the first bucket of (b, g), plus the tile's
-// offset in the bucket) is read once, with coalesced loads, into LDS beside the
-// bitmap, so an entry costs LDS lookups and its one store.  (Relative bases fit
-// 32 bits: a (b, g) has T * topk entries.)
+// Entries at their final positions, in query order within each bucket.  A
+// block takes one tile of kIdxTile queries; each chunk's next position (its
+// bucket's base relative to the first bucket of (b, g), plus the tile's offset
+// in the bucket) sits in LDS, read once with coalesced loads.  The tile's
+// sub-tiles of 64 queries run in order: the bitmap of which of the 64 queries
+// chose each chunk gives an entry its rank among them, then moves the chunk's
+// position on by its count.  (Relative positions fit 32 bits: a (b, g) has
+// T * topk entries.)
 __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
   extern __shared__ uint64_t bm[];
   int32_t* pos = reinterpret_cast<int32_t*>(bm + a.NCs);
@@ -141,21 +161,32 @@ __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
   const int32_t* toff = a.tile_cnt + (((int64_t)b * a.Hkv + g) * a.ntiles + t) * a.NCs;
   const int64_t* bbase = a.bbase + ((int64_t)b * a.Hkv + g) * a.NCs;
   const int64_t base0 = bbase[0];
-  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) pos[c] = (int32_t)(bbase[c] - base0) + toff[c];
-  build_bitmap(a, bm, b, g, t);   // its barriers also publish pos
-  const int64_t i0 = t * 64;
-  const int n = 64 * a.topk;
-  for (int e = threadIdx.x; e < n; e += blockDim.x) {
-    const int ql = e / a.topk, s = e % a.topk;
-    const int64_t i = i0 + ql;
-    if (i >= a.T) continue;
-    const int32_t c = a.idx[(((int64_t)b * a.Hkv + g) * a.T + i) * a.topk + s];
-    if (c < 0 || c >= a.NCs) continue;
-    const int rank = __popcll(bm[c] & ((1ull << ql) - 1ull));
-    a.entries[base0 + pos[c] + rank] = (uint32_t)(i * 64 + s);
+  for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) {
+    pos[c] = (int32_t)(bbase[c] - base0) + toff[c];
+    bm[c] = 0ull;
+  }
+  const int n = kIdxSub * a.topk;
+  for (int64_t i0 = t * kIdxTile; i0 < min<int64_t>((t + 1) * kIdxTile, a.T); i0 += kIdxSub) {
+    const int32_t* row = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i0) * a.topk;
+    __syncthreads();   // pos and bm as the previous sub-tile left them
+    sub_bitmap(a, bm, row, i0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+      const int ql = e / a.topk, sl = e % a.topk;
+      const int64_t i = i0 + ql;
+      if (i >= a.T) break;
+      const int32_t c = row[e];
+      if (c < 0 || c >= a.NCs) continue;
+      const int rank = __popcll(bm[c] & ((1ull << ql) - 1ull));
+      a.entries[base0 + pos[c] + rank] = (uint32_t)(i * 64 + sl);
+    }
+    __syncthreads();
+    for (int64_t c = threadIdx.x; c < a.NCs; c += blockDim.x) {   // each thread its own chunks
+      pos[c] += __popcll(bm[c]);
+      bm[c] = 0ull;
+    }
   }
 }
-
 
 // L_sel = LSE of each head's s_hat over its selected chunks (-inf if none), and
 // each selected chunk's weight exp(s_hat - L_sel) for the G heads of the group,
@@ -740,7 +771,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, bool bf16,
                       size_t* fixed, size_t* per_kv_head) {
   const int64_t NCs = T / S;
-  const int64_t ntiles = (T + 63) / 64;
+  const int64_t ntiles = (T + kIdxTile - 1) / kIdxTile;
   const size_t esz = bf16 ? 2 : 4;
   size_t f = 0;
   f += align256((size_t)B * Hkv * ntiles * NCs * sizeof(int32_t));  // tile_cnt
@@ -756,7 +787,7 @@ void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
 
 size_t entry_lists_bytes(int B, int Hkv, int64_t T, int S, int topk) {
   const int64_t NCs = T / S;
-  const int64_t ntiles = (T + 63) / 64;
+  const int64_t ntiles = (T + kIdxTile - 1) / kIdxTile;
   return align256((size_t)B * Hkv * ntiles * NCs * sizeof(int32_t)) +
          align256((size_t)B * Hkv * NCs * sizeof(int32_t)) + align256((size_t)B * Hkv * NCs * sizeof(int64_t)) +
          align256((size_t)B * Hkv * T * topk * sizeof(uint32_t));
@@ -765,7 +796,7 @@ size_t entry_lists_bytes(int B, int Hkv, int64_t T, int S, int topk) {
 hipError_t launch_entry_lists(const int32_t* idx, int B, int Hq, int Hkv, int64_t T, int S, int topk,
                               void* ws, EntryLists* el, hipStream_t st) {
   const int64_t NCs = T / S;
-  const int64_t ntiles = (T + 63) / 64;
+  const int64_t ntiles = (T + kIdxTile - 1) / kIdxTile;
   char* w = static_cast<char*>(ws);
   IdxArgs ia{};
   ia.idx = idx;
@@ -786,7 +817,8 @@ hipError_t launch_entry_lists(const int32_t* idx, int B, int Hq, int Hkv, int64_
   const size_t lds = (size_t)NCs * sizeof(uint64_t);
   {
     KTimer tm(K_IDX_COUNT, st);
-    hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, Hkv, B), dim3(256), lds, st, ia);
+    hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, Hkv, B), dim3(256),
+                       lds + (size_t)NCs * sizeof(int32_t), st, ia);
   }
   {
     KTimer tm(K_IDX_SCAN_TILES, st);
@@ -808,7 +840,7 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   size_t fixed, per;
   attend_workspace(a.B, a.Hq, a.Hkv, a.T, a.S, a.D, a.topk, a.bf16, &fixed, &per);
   const int64_t NCs = a.T / a.S;
-  const int64_t ntiles = (a.T + 63) / 64;
+  const int64_t ntiles = (a.T + kIdxTile - 1) / kIdxTile;
   const size_t esz = a.bf16 ? 2 : 4;
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(a.ws) + 255) & ~(uintptr_t)255);
   IdxArgs ia{};
@@ -855,7 +887,8 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
     const size_t lds = (size_t)NCs * sizeof(uint64_t);
     {
       KTimer tm(K_IDX_COUNT, st);
-      hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256), lds, st, ia);
+      hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256),
+                         lds + (size_t)NCs * sizeof(int32_t), st, ia);
     }
     {
       KTimer tm(K_IDX_SCAN_TILES, st);
