@@ -188,6 +188,69 @@ __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
   }
 }
 
+// The same as lsel_kernel (below) with four slots per lane: lane (r, hh, q) of
+// a wave takes slots 4q .. 4q+3 of head hh of row r (NQP lanes per head, G NQP
+// per row, 64 / (G NQP) rows per wave), so every score and index load is 16
+// bytes.  The slots' exp terms are added in pairs and then across the NQP
+// lanes by the same butterfly as lsel_kernel's, so the sums are bit for bit
+// the same.  The weights go through a wave-private LDS tile in the record
+// layout [row][slot][G] and leave as contiguous 16-byte stores.
+template <int G, int NQP>
+__global__ __launch_bounds__(256) void lsel4_kernel(IdxArgs a) {
+  constexpr int LPR = G * NQP;       // lanes per row
+  constexpr int RW = kWave / LPR;    // rows per wave
+  __shared__ __align__(16) float wt[4][RW * 4 * NQP * G];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int r = lane / LPR, hh = (lane / NQP) % G, q = lane % NQP;
+  const int64_t nrows = (int64_t)a.B * a.Hkv * a.T;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RW;   // this wave's first row
+  const int64_t row = row0 + r;
+  const bool live = row < nrows;
+  const int64_t rr = live ? row : nrows - 1;
+  const int64_t i = rr % a.T;
+  const int g = (int)((rr / a.T) % a.Hkv);
+  const int b = (int)(rr / (a.T * a.Hkv));
+  const int topk = a.topk;
+  const bool inrow = 4 * q < topk;
+  const int64_t rowq = ((int64_t)b * a.Hq + g * G + hh) * a.T + i;
+  int4 id = make_int4(-1, -1, -1, -1);
+  float4 xs = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+  if (inrow) {
+    id = *reinterpret_cast<const int4*>(a.idx + rr * topk + 4 * q);
+    xs = *reinterpret_cast<const float4*>(a.ssel + rowq * topk + 4 * q);
+  }
+  float x[4] = {id.x >= 0 ? xs.x : kNegInf, id.y >= 0 ? xs.y : kNegInf,
+                id.z >= 0 ? xs.z : kNegInf, id.w >= 0 ? xs.w : kNegInf};
+  float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (NQP > 1) m = fmaxf(m, xor_lane<1>(m));
+  if (NQP > 2) m = fmaxf(m, xor_lane<2>(m));
+  if (NQP > 4) m = fmaxf(m, xor_lane<4>(m));
+  if (NQP > 8) m = fmaxf(m, xor_lane<8>(m));
+  float e[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) e[j] = (x[j] == kNegInf) ? 0.f : __expf(x[j] - m);
+  float z = (e[0] + e[1]) + (e[2] + e[3]);
+  if (NQP > 1) z += xor_lane<1>(z);
+  if (NQP > 2) z += xor_lane<2>(z);
+  if (NQP > 4) z += xor_lane<4>(z);
+  if (NQP > 8) z += xor_lane<8>(z);
+  const float ls = m == kNegInf ? kNegInf : m + __logf(z);
+  if (live && q == 0) a.lsel[rowq] = ls;
+  float* tw = wt[wave];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int slot = 4 * q + j;
+    if (slot < topk) tw[(r * topk + slot) * G + hh] = x[j] == kNegInf ? 0.f : __expf(x[j] - ls);
+  }
+  wave_lds_sync();
+  // the wave's rows are consecutive records: RW * topk * G floats from row0
+  const int nf = RW * topk * G;
+  float* dst = a.wq + row0 * topk * G;
+  const int64_t lim = (nrows - row0) * topk * G;   // floats of live rows
+  for (int f = 4 * lane; f < nf; f += 4 * kWave)
+    if (f < lim) *reinterpret_cast<float4*>(dst + f) = *reinterpret_cast<const float4*>(tw + f);
+}
+
 // L_sel = LSE of each head's s_hat over its selected chunks (-inf if none), and
 // each selected chunk's weight exp(s_hat - L_sel) for the G heads of the group,
 // stored together ([B, Hkv, T, topk, G]) so the chunk-major pass reads one
@@ -873,12 +936,41 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
     while (L < a.topk) L <<= 1;
     const int64_t nl = (int64_t)a.B * a.Hkv * a.T * L;
     const dim3 grid((unsigned)((nl + 255) / 256));
+    const int G = a.Hq / a.Hkv;
+    const int nqp = L / 4;   // lanes per head with four slots each
+    const int64_t nrows = (int64_t)a.B * a.Hkv * a.T;
     KTimer tm(K_LSEL, st);
-    switch (a.Hq / a.Hkv) {
-      case 1: hipLaunchKernelGGL(lsel_kernel<1>, grid, dim3(256), 0, st, ia, L); break;
-      case 2: hipLaunchKernelGGL(lsel_kernel<2>, grid, dim3(256), 0, st, ia, L); break;
-      case 4: hipLaunchKernelGGL(lsel_kernel<4>, grid, dim3(256), 0, st, ia, L); break;
-      default: hipLaunchKernelGGL(lsel_kernel<8>, grid, dim3(256), 0, st, ia, L); break;
+    if (a.topk % 4 == 0 && nqp >= 1 && G * nqp <= kWave) {
+      const int rpb = 4 * (kWave / (G * nqp));   // rows per block of four waves
+      const dim3 g4((unsigned)((nrows + rpb - 1) / rpb));
+      switch (G * 100 + nqp) {
+        case 101: hipLaunchKernelGGL((lsel4_kernel<1, 1>), g4, dim3(256), 0, st, ia); break;
+        case 102: hipLaunchKernelGGL((lsel4_kernel<1, 2>), g4, dim3(256), 0, st, ia); break;
+        case 104: hipLaunchKernelGGL((lsel4_kernel<1, 4>), g4, dim3(256), 0, st, ia); break;
+        case 108: hipLaunchKernelGGL((lsel4_kernel<1, 8>), g4, dim3(256), 0, st, ia); break;
+        case 116: hipLaunchKernelGGL((lsel4_kernel<1, 16>), g4, dim3(256), 0, st, ia); break;
+        case 201: hipLaunchKernelGGL((lsel4_kernel<2, 1>), g4, dim3(256), 0, st, ia); break;
+        case 202: hipLaunchKernelGGL((lsel4_kernel<2, 2>), g4, dim3(256), 0, st, ia); break;
+        case 204: hipLaunchKernelGGL((lsel4_kernel<2, 4>), g4, dim3(256), 0, st, ia); break;
+        case 208: hipLaunchKernelGGL((lsel4_kernel<2, 8>), g4, dim3(256), 0, st, ia); break;
+        case 216: hipLaunchKernelGGL((lsel4_kernel<2, 16>), g4, dim3(256), 0, st, ia); break;
+        case 401: hipLaunchKernelGGL((lsel4_kernel<4, 1>), g4, dim3(256), 0, st, ia); break;
+        case 402: hipLaunchKernelGGL((lsel4_kernel<4, 2>), g4, dim3(256), 0, st, ia); break;
+        case 404: hipLaunchKernelGGL((lsel4_kernel<4, 4>), g4, dim3(256), 0, st, ia); break;
+        case 408: hipLaunchKernelGGL((lsel4_kernel<4, 8>), g4, dim3(256), 0, st, ia); break;
+        case 416: hipLaunchKernelGGL((lsel4_kernel<4, 16>), g4, dim3(256), 0, st, ia); break;
+        case 801: hipLaunchKernelGGL((lsel4_kernel<8, 1>), g4, dim3(256), 0, st, ia); break;
+        case 802: hipLaunchKernelGGL((lsel4_kernel<8, 2>), g4, dim3(256), 0, st, ia); break;
+        case 804: hipLaunchKernelGGL((lsel4_kernel<8, 4>), g4, dim3(256), 0, st, ia); break;
+        default: hipLaunchKernelGGL((lsel4_kernel<8, 8>), g4, dim3(256), 0, st, ia); break;
+      }
+    } else {
+      switch (G) {
+        case 1: hipLaunchKernelGGL(lsel_kernel<1>, grid, dim3(256), 0, st, ia, L); break;
+        case 2: hipLaunchKernelGGL(lsel_kernel<2>, grid, dim3(256), 0, st, ia, L); break;
+        case 4: hipLaunchKernelGGL(lsel_kernel<4>, grid, dim3(256), 0, st, ia, L); break;
+        default: hipLaunchKernelGGL(lsel_kernel<8>, grid, dim3(256), 0, st, ia, L); break;
+      }
     }
   } else {
     ia.lsel = nullptr;  // no selection: the window is the whole normaliser
