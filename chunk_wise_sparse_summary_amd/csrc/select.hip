@@ -439,10 +439,12 @@ void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
     const int jn = (nc + 63) / 64;
     uint32_t kv[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int c = lane + 64 * j;
-      kv[j] = (j < jn && c < nc) ? __builtin_nontemporal_load(rrow + c) : 0u;
-    }
+    // the row holds 64 J keys: the loads need no guard, only their values do
+    // (masked once every load is out)
+    for (int j = 0; j < J; ++j) kv[j] = j < jn ? __builtin_nontemporal_load(rrow + lane + 64 * j) : 0u;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (lane + 64 * j >= nc) kv[j] = 0u;
     wave_topk_u32<J>(kv, jn, topk, lane, sbuf[wave], sel[wave]);
     nsel = topk;
   } else {
@@ -492,29 +494,47 @@ void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
   wave_lds_sync();
   if (lane < topk) a.idx[(((int64_t)b * a.Hkv + g) * T_ + i) * topk + lane] = sel[wave][lane];
   if (a.ssel == nullptr) return;   // selection only (naive BSA)
-  // 64 rows per batch: lane (grp, p) loads piece p of rows r0 + grp + RPI t
+  // 64 rows per batch: lane (grp, p) loads piece p of rows r0 + grp + RPI t.
+  // Every row's chunk id first; then the row loads go out NB at a time with no
+  // condition (a padding row reads row 0 of its head and is dropped by a
+  // select), so they are in flight together rather than one after another.
+  constexpr int NB = 4;
+  const T* kbase = static_cast<const T*>(a.ksum) + ((int64_t)b * Hq + g * G) * NCs * D + p * EPP;
   for (int r0 = 0; r0 < topk * G; r0 += kWave) {
-    float part[PPR];
+    int cs[PPR];
 #pragma unroll
     for (int t = 0; t < PPR; ++t) {
-      const int r = r0 + grp + RPI * t, slot = r / G, hh = r % G;
-      float acc = 0.f;
-      if (slot < nsel) {
-        const int c = sel[wave][slot];
-        const uint4 ku = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.ksum) +
-                                                        (((int64_t)b * Hq + g * G + hh) * NCs + c) * D + p * EPP);
-        const uint32_t kw[4] = {ku.x, ku.y, ku.z, ku.w};
-        const int u = NQ > 1 ? t % NQ : 0;
+      const int slot = (r0 + grp + RPI * t) / G;
+      cs[t] = slot < nsel ? sel[wave][min(slot, kWave - 1)] : -1;
+    }
+    float part[PPR];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (sizeof(T) == 2)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[u][e]),
-                                                  __builtin_bit_cast(bf16x2_t, kw[e]), acc, false);
-          else
-            acc = fmaf(__uint_as_float(qp[u][e]), __uint_as_float(kw[e]), acc);
+    for (int t = 0; t < PPR; ++t) part[t] = 0.f;
+    if (nsel > 0) {   // uniform: with no chunk k' may be empty
+#pragma unroll
+      for (int t0 = 0; t0 < PPR; t0 += NB) {
+        uint4 ku[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int hh = (r0 + grp + RPI * (t0 + u)) % G;
+          ku[u] = *reinterpret_cast<const uint4*>(kbase + ((int64_t)hh * NCs + max(cs[t0 + u], 0)) * D);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const uint32_t kw[4] = {ku[u].x, ku[u].y, ku[u].z, ku[u].w};
+          const int q = NQ > 1 ? (t0 + u) % NQ : 0;
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (sizeof(T) == 2)
+              acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[q][e]),
+                                                    __builtin_bit_cast(bf16x2_t, kw[e]), acc, false);
+            else
+              acc = fmaf(__uint_as_float(qp[q][e]), __uint_as_float(kw[e]), acc);
+          }
+          part[t0 + u] = cs[t0 + u] >= 0 ? acc : 0.f;
         }
       }
-      part[t] = acc;
     }
     rs_rows<PPR / 2, PPR, PPR>(part, lane);
     const int r = r0 + grp + RPI * p, slot = r / G, hh = r % G;   // the row this lane now holds
