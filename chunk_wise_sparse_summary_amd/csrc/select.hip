@@ -268,45 +268,49 @@ __global__ __launch_bounds__(256) void score_lse_kernel(const T* __restrict__ qh
   }
 }
 
-// Queries per workgroup: 64 (4 waves; with 8 waves, 128, the 139 VGPRs leave one
-// workgroup per compute unit, and fewer registers spill).
-template <typename T> constexpr int rank_q() { return 64; }
+// Workgroup of the rank pass: 4 waves, each with two 16-query tiles, so every
+// k' fragment read from LDS feeds two MFMAs (with one tile per wave the LDS
+// reads of the fragments bounded the kernel).
+// (two tiles when their q fragments fit half the registers: bf16 and G d <= 512)
+constexpr int kRankWaves = 4;
+template <typename T, int D, int G> constexpr int rank_tq() { return sizeof(T) == 2 && G * D <= 512 ? 2 : 1; }
+template <typename T, int D, int G> constexpr int rank_q() { return kRankWaves * 16 * rank_tq<T, D, G>(); }
 
 // The prefill selection runs as two kernels over every (b, group) of a pass
 // (the grids' second dimension), each group's rank keys in its own [T][64 J]
 // scratch:
-//   rank_keys  per 64-query tile and 16-chunk k' tile (k' of all G heads staged
-//              once in LDS): wave w owns queries 16 w .. 16 w + 15 of the tile and
-//              every head of the group, so the rank key r = max over heads of
-//              s_hat - L_h (r = s_hat for one head) forms in registers
-//              (transposed score tiles: a lane holds four chunks of one query)
-//              and goes straight to the scratch.
+//   rank_keys  per 64- or 128-query tile and 16-chunk k' tile (k' of all G heads
+//              staged once in LDS): wave w owns one or two 16-query MFMA column
+//              tiles and every head of the group, so the rank
+//              key r = max over heads of s_hat - L_h (r = s_hat for one head)
+//              forms in registers (transposed score tiles: a lane holds four
+//              chunks of one query) and goes straight to the scratch.
 //   topk_scores one wave per query: the exact top-k of its rank keys (below)
 //              and each head's s_hat on the chosen chunks.
-template <typename T, int D, int G, int RQ_ = rank_q<T>()>
+template <typename T, int D, int G, int RQ_ = rank_q<T, D, G>()>
 struct RankTiles {
   static constexpr int KS = D / 32;
-  static constexpr int RQ = RQ_, NT = RQ * 4;   // 16 queries per wave
+  static constexpr int RQ = RQ_, NT = kRankWaves * kWave;
   using Tile = KTile<T, D, G, NT>;
 };
 
 template <typename T, int D, int G, int NCP>
-__global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, int bg0,
-                                                                    uint32_t* __restrict__ keys) {
+__global__ __launch_bounds__(kRankWaves * kWave) void rank_keys_kernel(SelArgs a, int bg0,
+                                                                       uint32_t* __restrict__ keys) {
   // (b, group) bg0 + blockIdx.y of this launch's groups, each with its own keys
   const int b = (bg0 + (int)blockIdx.y) / a.Hkv, g = (bg0 + (int)blockIdx.y) % a.Hkv;
   keys += (int64_t)blockIdx.y * a.group_words;
   using R = RankTiles<T, D, G>;
   constexpr int KS = R::KS, RQ = R::RQ, NT = R::NT;
   using Tile = typename R::Tile;
-  constexpr int NW = RQ / 16;        // waves: 16 queries each
+  constexpr int NW = kRankWaves, TQ = rank_tq<T, D, G>();
   constexpr int KSP = 64 + 4;        // padded staging row (words)
   __shared__ __align__(16) T kt[G * 16 * Tile::KP];
   __shared__ float bt[G * 16];
-  // each wave's rank keys of 64 candidates x 16 queries, written back to HBM as
+  // each wave's rank keys of 64 candidates x 16 TQ queries, written back to HBM as
   // row-contiguous 256-byte runs (one lane per query row and 16-byte piece, as
   // the score tiles leave them, costs a cache line per lane)
-  __shared__ __align__(16) uint32_t kst[NW][16 * KSP];
+  __shared__ __align__(16) uint32_t kst[NW][16 * TQ * KSP];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
@@ -314,21 +318,25 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
   const int64_t T_ = a.T, NCs = a.NCs;
   const int Hq = a.Hq;
   const int64_t qb = (int64_t)(gridDim.x - 1 - blockIdx.x) * RQ;   // longest rows first
-  const int64_t qi = qb + 16 * wave + r16;   // this lane's query (column r16 of the tiles)
+  const int64_t qw0 = qb + 16 * TQ * wave;   // the wave's first query
   const T* kg = static_cast<const T*>(a.ksum) + ((int64_t)b * Hq + g * G) * NCs * D;
   const float* bg = a.bsum + ((int64_t)b * Hq + g * G) * NCs;
-  Frag<T> qf[G][KS];
-  float Lq[G];
+  Frag<T> qf[TQ][G][KS];   // column r16 of tile t: query qw0 + 16 t + r16
+  float Lq[TQ][G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
+  for (int t = 0; t < TQ; ++t) {
+    const int64_t qi = qw0 + 16 * t + r16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load_frag(qf[hh][ks], qrow + 32 * ks);
-    Lq[hh] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = g * G + hh;
+      const T* qrow = qh + (((int64_t)b * Hq + h) * T_ + min(qi, T_ - 1)) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) load_frag(qf[t][hh][ks], qrow + 32 * ks);
+      Lq[t][hh] = (G > 1 && qi < T_) ? a.L[((int64_t)b * Hq + h) * T_ + qi] : 0.f;
+    }
   }
   const int nc_block = (int)num_candidates(min(qb + RQ - 1, T_ - 1), a.S, a.W);
-  const int nc_wave = (int)num_candidates(min(qb + 16 * wave + 15, T_ - 1), a.S, a.W);
+  const int nc_wave = (int)num_candidates(min(qw0 + 16 * TQ - 1, T_ - 1), a.S, a.W);
   const int cl_last = nc_block > 0 ? nc_block - 1 : 0;
   u32v<4 * Tile::NPT> kreg;
   float breg = 0.f;
@@ -339,7 +347,11 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
     __syncthreads();
     if (c0 + 16 < nc_block) tile_fetch<T, D, G, NT>(kreg, breg, kg, bg, NCs, c0 + 16, cl_last);
     if (c0 >= nc_wave) continue;   // no query of this wave has these candidates
-    float r[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+    float r[TQ][4];
+#pragma unroll
+    for (int t = 0; t < TQ; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[t][i] = kNegInf;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       Frag<T> kf[KS];   // row r16 = chunk c0 + r16
@@ -347,24 +359,28 @@ __global__ __launch_bounds__(rank_q<T>() * 4) void rank_keys_kernel(SelArgs a, i
       for (int ks = 0; ks < KS; ++ks)
         load_frag(kf[ks], kt + (hh * 16 + r16) * Tile::KP + 8 * grp + 32 * ks);
       const float4 bk = *reinterpret_cast<const float4*>(bt + hh * 16 + 4 * grp);
-      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma(acc, kf[ks], qf[hh][ks]);
-      r[0] = fmaxf(r[0], fmaf(acc[0], a.scale, bk.x) - Lq[hh]);
-      r[1] = fmaxf(r[1], fmaf(acc[1], a.scale, bk.y) - Lq[hh]);
-      r[2] = fmaxf(r[2], fmaf(acc[2], a.scale, bk.z) - Lq[hh]);
-      r[3] = fmaxf(r[3], fmaf(acc[3], a.scale, bk.w) - Lq[hh]);
+      for (int t = 0; t < TQ; ++t) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mma(acc, kf[ks], qf[t][hh][ks]);
+        r[t][0] = fmaxf(r[t][0], fmaf(acc[0], a.scale, bk.x) - Lq[t][hh]);
+        r[t][1] = fmaxf(r[t][1], fmaf(acc[1], a.scale, bk.y) - Lq[t][hh]);
+        r[t][2] = fmaxf(r[t][2], fmaf(acc[2], a.scale, bk.z) - Lq[t][hh]);
+        r[t][3] = fmaxf(r[t][3], fmaf(acc[3], a.scale, bk.w) - Lq[t][hh]);
+      }
     }
     uint32_t* kw = kst[wave];
-    *reinterpret_cast<uint4*>(kw + r16 * KSP + c0 % 64 + 4 * grp) =
-        make_uint4(order_key(r[0]), order_key(r[1]), order_key(r[2]), order_key(r[3]));
+#pragma unroll
+    for (int t = 0; t < TQ; ++t)
+      *reinterpret_cast<uint4*>(kw + (16 * t + r16) * KSP + c0 % 64 + 4 * grp) =
+          make_uint4(order_key(r[t][0]), order_key(r[t][1]), order_key(r[t][2]), order_key(r[t][3]));
     if (c0 % 64 == 48 || c0 + 16 >= nc_wave) {   // a run of 64 candidates, or the wave's last
       wave_lds_sync();
-      const int64_t qw0 = qb + 16 * wave;
       const int64_t off = qw0 * NCP + (c0 - c0 % 64) + 4 * (lane % 16);
       const int qr = lane / 16;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4 * TQ; ++j) {
         const int qq = 4 * j + qr;
         if (qw0 + qq < T_)
           __builtin_nontemporal_store(*reinterpret_cast<const u32v<4>*>(kw + qq * KSP + 4 * (lane % 16)),
@@ -549,7 +565,7 @@ void topk_scores_kernel(SelArgs a, int bg0, const uint32_t* __restrict__ keys) {
 
 template <typename T, int D, int G, int J>
 hipError_t launch_rank_j(const SelArgs& a, hipStream_t st) {
-  constexpr int RQ = rank_q<T>();
+  constexpr int RQ = rank_q<T, D, G>();
   const dim3 tiles((unsigned)((a.T + RQ - 1) / RQ)), rows((unsigned)((a.T + 3) / 4));
   uint32_t* keys = reinterpret_cast<uint32_t*>(a.scratch);
   // as many (b, group) pairs per launch as the workspace holds rank keys for
@@ -558,7 +574,7 @@ hipError_t launch_rank_j(const SelArgs& a, hipStream_t st) {
     const int n = min(a.gpass, nbg - bg0);
     {
       KTimer tm(K_RANK_KEYS, st);
-      hipLaunchKernelGGL((rank_keys_kernel<T, D, G, 64 * J>), dim3(tiles.x, (unsigned)n), dim3(RQ * 4), 0, st,
+      hipLaunchKernelGGL((rank_keys_kernel<T, D, G, 64 * J>), dim3(tiles.x, (unsigned)n), dim3(kRankWaves * kWave), 0, st,
                          a, bg0, keys);
     }
     KTimer tm(K_TOPK_SCORES, st);
