@@ -8,8 +8,9 @@
 //   L = LSE({s_hat_c} + {log Z_win}),
 // where o_gamma is ordinary softmax attention of q_i over the group's tokens.
 //
-// The pages batch adjacent queries over the union of their selected chunks
-// (paper-body page, implementation, kernel design).  That reuse depends on
+// The pages' kernel takes adjacent queries together and visits every chunk any
+// of them selected once for all of them (paper-body page, implementation,
+// kernel design).  That reuse depends on
 // adjacent queries picking overlapping chunks; when they do not, every
 // (query, chunk) visit re-reads 32 KiB of K/V.  This file instead runs the
 // selected part chunk-major: each selected chunk's K/V is staged once in LDS and

@@ -1,8 +1,9 @@
 // select.hip -- retrieval scores and GQA-aware top-k chunk selection (prefill).
 //
-// Paper-body page, RQ1: each query scores every chunk summary with the linear
-// surrogate of Eq. 7 and keeps the top-k; this scoring is the one part of the
-// method whose cost grows with T^2.  Summary page, Eq. 10: s_hat = q_hat . k' /
+// Paper-body page, RQ1: a query's score for a chunk is the linear (Eq. 7)
+// estimate of its log-mass from the chunk's summary, computed for every complete
+// chunk before the k highest are chosen; this is the one part of the method
+// whose cost grows with T^2.  Summary page, Eq. 10: s_hat = q_hat . k' /
 // sqrt(d) + b'.
 // Paper-body page, GQA-aware chunk selection: per-head normalised chunk weights,
 // max over the heads of a group, top-k per group.  The normalised weight is

@@ -160,10 +160,10 @@ hils_status hils_qcal(const hils_shape* shape, const void* q, const void* hs, co
                       hipStream_t stream);
 
 /*
- * Retrieval scores and top-k selection (paper-body page, RQ1: each query scores
- * every chunk summary by the linear surrogate of Eq. 7 and keeps the top-k;
- * summary page, Eq. 10: s_hat = q_hat . k' / sqrt(d) + b'; paper-body page,
- * GQA-aware chunk selection).  For every b, position i < T and group g:
+ * Retrieval scores and top-k selection (paper-body page, RQ1: every complete
+ * chunk's summary is scored with the linear estimate of Eq. 7 and the k highest
+ * are chosen; summary page, Eq. 10: s_hat = q_hat . k' / sqrt(d) + b';
+ * paper-body page, GQA-aware chunk selection).  For every b, position i < T and group g:
  *     s_hat_{h,i,c} = scale * q_hat_{h,i} . k'_{h,c} + b'_{h,c},   c in C_i
  *     rank key r_c  = s_hat_{h,i,c}                              (G == 1)
  *                   = max_{h in g} (s_hat_{h,i,c} - LSE_{c' in C_i} s_hat_{h,i,c'})   (G > 1)
