@@ -403,9 +403,9 @@ __device__ __forceinline__ void chunk_attend_body(const ChunkArgs& a) {
   const int ntile = (n + NE - 1) / NE;
   const int hh = r16 % G, h = g * G + hh;
 
-  // three-stage pipeline: the entry word of tile t+8 (two of this wave's tiles
-  // ahead), the q rows and weight of tile t+4 (using the word loaded an
-  // iteration earlier), the computation of tile t
+  // pipeline over this wave's tiles t, t+NW, ...: the entry word of tile t+3NW,
+  // the q rows and weight of tile t+2NW (using the word loaded earlier), the
+  // computation of tile t
   auto load_word = [&](int nt) -> uint32_t {
     const int e = nt * NE + r16 / G;
     return (nt < ntile && e < n) ? a.entries[base + e] : 0xffffffffu;
@@ -442,26 +442,27 @@ __device__ __forceinline__ void chunk_attend_body(const ChunkArgs& a) {
   };
 
   constexpr int PKs = D / (16 / (int)sizeof(T));
-  Frag<T> kf[4][KS];   // K rows 16 mt + r16, dims 32 kq + 8 grp .. + 7
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int kq = 0; kq < KS; ++kq) load_frag_swz<PKs>(kf[mt][kq], ks, 16 * mt + r16, 8 * grp + 32 * kq);
+  // q rows two of this wave's tiles ahead: the tile after next goes out while
+  // this one computes (rb holds the next tile's rows, already in flight)
   Frag<T> bq[KS];
-  uint4 raw[NI];
-  uint32_t word = load_word(wave), wordn = load_word(wave + NW);
-  float wt, wtn;
-  load_q(word, raw, wt);
-  to_frags(raw, bq);
+  uint4 ra[NI], rb[NI];
+  uint32_t word = load_word(wave), wordn = load_word(wave + NW), wordnn = load_word(wave + 2 * NW);
+  float wt, wtn, wtnn;
+  load_q(word, ra, wt);
+  load_q(wordn, rb, wtn);
+  to_frags(ra, bq);
   for (int nt = wave; nt < ntile; nt += NW) {
-    load_q(wordn, raw, wtn);               // the next tile's rows, in flight meanwhile
-    const uint32_t wordnn = load_word(nt + 2 * NW);
+    load_q(wordnn, ra, wtnn);              // the tile after next, in flight meanwhile
+    const uint32_t word3 = load_word(nt + 3 * NW);
     f32x4_t acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+      Frag<T> kf[KS];   // K rows 16 mt + r16, dims 32 kq + 8 grp .. + 7
+#pragma unroll
+      for (int kq = 0; kq < KS; ++kq) load_frag_swz<PKs>(kf[kq], ks, 16 * mt + r16, 8 * grp + 32 * kq);
       acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kq = 0; kq < KS; ++kq) mma(acc[mt], kf[mt][kq], bq[kq]);
+      for (int kq = 0; kq < KS; ++kq) mma(acc[mt], kf[kq], bq[kq]);
     }
     float mx = kNegInf;   // sl2 > 0: the max of the raw logits, scaled once
 #pragma unroll
@@ -506,10 +507,14 @@ __device__ __forceinline__ void chunk_attend_body(const ChunkArgs& a) {
       }
     }
     wave_lds_sync();
-    to_frags(raw, bq);
+    to_frags(rb, bq);
+#pragma unroll
+    for (int j = 0; j < NI; ++j) rb[j] = ra[j];
     word = wordn;
     wordn = wordnn;
+    wordnn = word3;
     wt = wtn;
+    wtn = wtnn;
   }
 }
 
