@@ -50,8 +50,12 @@ struct IdxArgs {
   uint32_t* entries;   // i * 64 + slot
   float* wq;           // [B, Hkv, T, topk, G] chunk weights exp(s_hat - L_sel) per head
   float* lsel;         // [B, Hq, T]
+  int32_t* smap;       // [B, Hkv, sbound]: chunk c | range r << 13 of each chunk-pass workgroup
+  int32_t* stot;       // [B, Hkv]: workgroups of (b, g)
   int B, Hq, Hkv, topk;
   int64_t T, NCs, ntiles;
+  int E;               // entries per chunk-pass workgroup (a chunk's list in ranges of E)
+  int64_t sbound;      // workgroups per (b, g), an upper bound
 };
 
 // Queries per counting tile (the column scan runs over T / kIdxTile tiles) and
@@ -144,6 +148,35 @@ __global__ __launch_bounds__(1024) void idx_scan_buckets_kernel(IdxArgs a) {
     a.bbase[j] = run;
     run += a.bcount[j];
   }
+}
+
+// The chunk pass's workgroups of (b, g): chunk c's list in ceil(n_c / E) ranges
+// of E entries, numbered in chunk order (the early chunks, the longest lists,
+// first).  One block per (b, g): per-thread runs of chunks, a block scan of
+// their range counts, then each range's (chunk, range) word.
+__global__ __launch_bounds__(1024) void split_map_kernel(IdxArgs a) {
+  __shared__ int32_t part[1024];
+  const int64_t bg = blockIdx.x;
+  const int32_t* cnt = a.bcount + bg * a.NCs;
+  const int64_t per = (a.NCs + 1023) / 1024;
+  const int64_t lo = threadIdx.x * per, hi = min(lo + per, a.NCs);
+  int32_t sum = 0;
+  for (int64_t c = lo; c < hi; ++c) sum += (cnt[c] + a.E - 1) / a.E;
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t pos = part[threadIdx.x] - sum;
+  int32_t* map = a.smap + bg * a.sbound;
+  for (int64_t c = lo; c < hi; ++c) {
+    const int32_t nr = (cnt[c] + a.E - 1) / a.E;
+    for (int32_t r = 0; r < nr; ++r) map[pos++] = (int32_t)c | (r << 13);
+  }
+  if (threadIdx.x == 1023) a.stot[bg] = part[1023];
 }
 
 // Entries at their final positions, in query order within each bucket.  A
@@ -355,9 +388,13 @@ struct ChunkArgs {
   const int64_t* bbase;
   const uint32_t* entries;
   void* part;   // [B, Hkv_pass, T, topk, G, D]
+  const int32_t* smap;   // the workgroups' (chunk, range) words, sbound per (b, g)
+  const int32_t* stot;
   int B, Hq, Hkv, topk, g0, gpass;
   int64_t T, NCs, NCf;
   float scale;
+  int E;
+  int64_t sbound;
 };
 
 // Selected chunks, chunk-major: one workgroup per (b, g, c).  The chunk's K and V
@@ -383,12 +420,19 @@ __device__ __forceinline__ void chunk_attend_body(const ChunkArgs& a) {
   // group by group (one group's q, G rows of every query, fits the last-level
   // cache while its chunks gather them), and within a group the early chunks,
   // candidates of almost every query and so the longest lists, first
-  const int64_t c = blockIdx.x % a.NCs;
-  const int g = a.g0 + (int)(blockIdx.x / a.NCs), b = blockIdx.z;
-  const int64_t bucket = ((int64_t)b * a.Hkv + g) * a.NCs + c;
-  const int n = a.bcount[bucket];
-  if (n == 0) return;
-  const int64_t base = a.bbase[bucket];
+  // workgroup = one range of E entries of one chunk's list (long lists split, so
+  // that a few of them do not outlast the rest of the grid)
+  const int g = a.g0 + (int)(blockIdx.x / a.sbound), b = blockIdx.z;
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  const int64_t rr = blockIdx.x % a.sbound;
+  if (rr >= a.stot[bg]) return;
+  const int32_t word0 = a.smap[bg * a.sbound + rr];
+  const int64_t c = word0 & 8191;
+  const int e0 = (word0 >> 13) * a.E;
+  const int64_t bucket = bg * a.NCs + c;
+  const int n = min(a.bcount[bucket] - e0, a.E);
+  if (n <= 0) return;
+  const int64_t base = a.bbase[bucket] + e0;
   const T* kc = static_cast<const T*>(a.k) + (((int64_t)b * a.Hkv + g) * a.T + c * kS) * D;
   const T* vtc = static_cast<const T*>(a.vt) + (((int64_t)b * a.Hkv + g) * a.NCf + c) * D * kS;
   stage_chunk<T, D, NW * kWave>(kc, vtc, ks, vt, kS);
@@ -796,10 +840,10 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
   for (int g0 = 0; g0 < a.Hkv; g0 += gpp) {
     const int gp = min(gpp, a.Hkv - g0);
     if (chunks) {
-      ChunkArgs ca{a.q, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part,
-                   a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, NCf, a.scale};
+      ChunkArgs ca{a.q, a.k, vt, ia.wq, ia.bcount, ia.bbase, ia.entries, part, ia.smap, ia.stot,
+                   a.B, a.Hq, a.Hkv, a.topk, g0, gpp, a.T, ia.NCs, NCf, a.scale, ia.E, ia.sbound};
       KTimer tm(K_CHUNK_ATTEND, st);
-      const dim3 grid((unsigned)(ia.NCs * gp), 1, a.B);
+      const dim3 grid((unsigned)(ia.sbound * gp), 1, a.B);
       if constexpr (sizeof(T) == 2)
         hipLaunchKernelGGL((chunk_attend_kernel<T, D, G>), grid, dim3(chunk_waves<T>() * kWave), 0, st, ca);
       else
@@ -837,6 +881,20 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// The chunk pass's workgroups: each takes one range of E entries of a chunk's
+// list, E a multiple of 64, at least 256 and large enough that all (b, g) make
+// about 6144 ranges of the T * topk entries each (so long lists cannot outlast
+// the grid, and short sequences still fill the chip).  Per (b, g) at most
+// sum_c ceil(n_c / E) <= NC + T * topk / E workgroups.
+void chunk_split(int B, int Hkv, int64_t T, int64_t NCs, int topk, int* E, int64_t* bound) {
+  const int64_t total = (int64_t)B * Hkv * T * topk;
+  int64_t e = (total + 6143) / 6144;
+  e = (e + 63) / 64 * 64;
+  if (e < 256) e = 256;
+  *E = (int)e;
+  *bound = NCs + (T * topk + e - 1) / e;
+}
+
 void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, bool bf16,
                       size_t* fixed, size_t* per_kv_head) {
   const int64_t NCs = T / S;
@@ -850,6 +908,11 @@ void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
   f += align256((size_t)B * Hq * T * topk * sizeof(float));         // chunk weights
   f += align256((size_t)B * Hq * T * sizeof(float));                // lsel
   f += align256((size_t)B * Hkv * ((T + kS - 1) / kS) * kS * D * esz);  // V^T per chunk
+  int E;
+  int64_t sbound;
+  chunk_split(B, Hkv, T, NCs, topk > 0 ? topk : 1, &E, &sbound);
+  f += align256((size_t)B * Hkv * sbound * sizeof(int32_t));         // chunk-pass workgroup map
+  f += align256((size_t)B * Hkv * sizeof(int32_t));                  // its counts
   *fixed = f + 256;
   *per_kv_head = align256((size_t)B * (Hq / Hkv) * T * topk * D * esz);
 }
@@ -929,6 +992,11 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
   void* vt = w;
   w += align256((size_t)a.B * a.Hkv * ((a.T + kS - 1) / kS) * kS * a.D * esz);
+  chunk_split(a.B, a.Hkv, a.T, NCs, a.topk > 0 ? a.topk : 1, &ia.E, &ia.sbound);
+  ia.smap = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)a.B * a.Hkv * ia.sbound * sizeof(int32_t));
+  ia.stot = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)a.B * a.Hkv * sizeof(int32_t));
   ia.B = a.B; ia.Hq = a.Hq; ia.Hkv = a.Hkv; ia.topk = a.topk;
   ia.T = a.T; ia.NCs = NCs; ia.ntiles = ntiles;
   void* part = w;
@@ -997,9 +1065,13 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
       KTimer tm(K_IDX_SCAN_BUCKETS, st);
       hipLaunchKernelGGL(idx_scan_buckets_kernel, dim3(1), dim3(1024), 0, st, ia);
     }
-    KTimer tm(K_IDX_FILL, st);
-    hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256),
-                       lds + (size_t)NCs * sizeof(int32_t), st, ia);
+    {
+      KTimer tm(K_IDX_FILL, st);
+      hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256),
+                         lds + (size_t)NCs * sizeof(int32_t), st, ia);
+    }
+    KTimer tm(K_IDX_SCAN_BUCKETS, st);
+    hipLaunchKernelGGL(split_map_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(1024), 0, st, ia);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
