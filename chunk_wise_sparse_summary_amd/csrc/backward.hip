@@ -183,8 +183,10 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
   constexpr int LPH = kWave / G;             // lanes per head for dk'
   constexpr int DPLH = DPW > LPH ? DPW / LPH : 1;
   __shared__ __align__(16) SM sm;
-  const int64_t c = blockIdx.x;
-  const int g = k.g0 + blockIdx.y, b = blockIdx.z;
+  // the group index fastest: every group's early chunks (the longest entry
+  // lists) are dispatched first, so none of them starts late and sets the tail
+  const int64_t c = blockIdx.y;
+  const int g = k.g0 + blockIdx.x, b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int r16 = lane % 16, grp = lane / 16;
@@ -458,7 +460,7 @@ __global__ __launch_bounds__(kBT) void bwd_kv_kernel(BwdKArgs k) {
         }
         if (vrow)
           store4<T>(static_cast<T*>(k.dqp) +
-                        (((((int64_t)blockIdx.y * a.B + b) * T_ + ir) * a.topk + slot) * G + r16 % G) * D +
+                        (((((int64_t)(g - k.g0) * a.B + b) * T_ + ir) * a.topk + slot) * G + r16 % G) * D +
                         16 * md + 4 * grp,
                     o, a.scale);
       }
@@ -768,7 +770,7 @@ hipError_t launch_bwd_tg(BwdKArgs k, int gpp, hipStream_t st) {
     const int ng = min(gpp, a.Hkv - g0);
     {
       KTimer tm(K_BWD_KV, st);
-      hipLaunchKernelGGL((bwd_kv_kernel<T, D, G>), dim3((unsigned)NCf, ng, a.B), dim3(kBT), 0, st, k);
+      hipLaunchKernelGGL((bwd_kv_kernel<T, D, G>), dim3((unsigned)ng, (unsigned)NCf, a.B), dim3(kBT), 0, st, k);
     }
     {
       KTimer tm(K_BWD_DQ, st);
