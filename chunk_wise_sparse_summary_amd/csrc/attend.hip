@@ -50,6 +50,7 @@ struct IdxArgs {
   uint32_t* entries;   // i * 64 + slot
   float* wq;           // [B, Hkv, T, topk, G] chunk weights exp(s_hat - L_sel) per head
   float* lsel;         // [B, Hq, T]
+  int32_t* nvalid;     // [B, Hkv, T]: selected slots of each row (a prefix of its k)
   int32_t* smap;       // [B, Hkv, sbound]: chunk c | range r << 13 of each chunk-pass workgroup
   int32_t* stot;       // [B, Hkv]: workgroups of (b, g)
   int B, Hq, Hkv, topk;
@@ -270,6 +271,13 @@ __global__ __launch_bounds__(256) void lsel4_kernel(IdxArgs a) {
   if (NQP > 8) z += xor_lane<8>(z);
   const float ls = m == kNegInf ? kNegInf : m + __logf(z);
   if (live && q == 0) a.lsel[rowq] = ls;
+  // the row's selected slots (the same for every head), counted over its quarters
+  float nsel = (float)((id.x >= 0) + (id.y >= 0) + (id.z >= 0) + (id.w >= 0));
+  if (NQP > 1) nsel += xor_lane<1>(nsel);
+  if (NQP > 2) nsel += xor_lane<2>(nsel);
+  if (NQP > 4) nsel += xor_lane<4>(nsel);
+  if (NQP > 8) nsel += xor_lane<8>(nsel);
+  if (live && q == 0 && hh == 0) a.nvalid[rr] = (int32_t)nsel;
   float* tw = wt[wave];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -312,6 +320,16 @@ __global__ __launch_bounds__(256) void lsel_kernel(IdxArgs a, int L) {
     xs[hh] = inrow ? a.ssel[rowq * a.topk + l] : kNegInf;
   }
   const bool sel = id >= 0;
+  {
+    float nsel = sel ? 1.f : 0.f;
+    if (L > 1) nsel += xor_lane<1>(nsel);
+    if (L > 2) nsel += xor_lane<2>(nsel);
+    if (L > 4) nsel += xor_lane<4>(nsel);
+    if (L > 8) nsel += xor_lane<8>(nsel);
+    if (L > 16) nsel += xor_lane<16>(nsel);
+    if (L > 32) nsel += xor_lane<32>(nsel);
+    if (live && l == 0) a.nvalid[rr] = (int32_t)nsel;
+  }
   float w[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
@@ -578,7 +596,7 @@ struct WinArgs {
   const void* k;
   const void* vt;        // V^T per chunk, [B, Hkv, NCf, D, S]
   const float* lsel;     // [B, Hq, T] L_sel (null: no selection)
-  const int32_t* idx;    // [B, Hkv, T, topk]
+  const int32_t* nvalid;  // [B, Hkv, T] selected slots of each row (a prefix)
   const void* part;      // this pass's weighted partials, [B, gpass, T, topk, G, D]
   void* out;             // [B, Hq, T, D]
   float* lse;            // [B, Hq, T] or null
@@ -777,20 +795,19 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
       for (int e = 0; e < EPV; ++e) { ows[e] = to_f<T>(t[e]); acc[e] = 0.f; }
     }
     if (wsel > 0.f) {
-      const int32_t* irow = a.idx + (((int64_t)b * a.Hkv + g) * T_ + iq) * a.topk;
+      // the row's selected slots are its first nv (padding only at the end)
+      const int nv = a.nvalid[((int64_t)b * a.Hkv + g) * T_ + iq];
       const T* prow = static_cast<const T*>(a.part) +
                       ((((int64_t)b * a.gpass + (g - a.g0)) * T_ + iq) * a.topk * G + hq) * D + pc * EPV;
-      // U slots' idx and partial loads in flight together, with no load waiting
-      // on another: a padding slot's partial row lies inside the buffer but holds
-      // no value, so it is loaded and then dropped by a select
+      // U slots' partial loads in flight together, with no load waiting on
+      // another: a padding slot's partial row lies inside the buffer but holds no
+      // value, so it is loaded and then dropped by a select
       constexpr int U = 16;
       for (int s = 0; s < a.topk; s += U) {
         uint4 u[U];
-        int32_t ix[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
           const bool in = s + j < a.topk;
-          ix[j] = in ? irow[s + j] : -1;
           u32x4 v = u32x4{0u, 0u, 0u, 0u};   // read once: streamed past the caches
           if (in) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(prow + (int64_t)(s + j) * G * D));
           u[j] = make_uint4(v[0], v[1], v[2], v[3]);
@@ -801,7 +818,7 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
 #pragma unroll
           for (int e = 0; e < EPV; ++e) {
             const float f = to_f<T>(t[e]);
-            acc[e] += ix[j] >= 0 ? f : 0.f;
+            acc[e] += s + j < nv ? f : 0.f;
           }
         }
       }
@@ -851,7 +868,7 @@ hipError_t launch_attend_tg(const AttArgs& a, const IdxArgs& ia, void* part, voi
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    WinArgs wa{a.q, a.k, vt, chunks ? ia.lsel : nullptr, a.idx, part, a.out, a.lse,
+    WinArgs wa{a.q, a.k, vt, chunks ? ia.lsel : nullptr, ia.nvalid, part, a.out, a.lse,
                a.B, a.Hq, a.Hkv, a.S, a.W, a.topk, g0, gpp, a.T, NCf, a.scale};
     const int QB = kWinWaves * (16 / G);
     const dim3 grid((unsigned)((a.T + QB - 1) / QB), (unsigned)gp, a.B);
@@ -907,6 +924,7 @@ void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
   f += align256((size_t)B * Hkv * T * topk * sizeof(uint32_t));     // entries
   f += align256((size_t)B * Hq * T * topk * sizeof(float));         // chunk weights
   f += align256((size_t)B * Hq * T * sizeof(float));                // lsel
+  f += align256((size_t)B * Hkv * T * sizeof(int32_t));             // selected slots per row
   f += align256((size_t)B * Hkv * ((T + kS - 1) / kS) * kS * D * esz);  // V^T per chunk
   int E;
   int64_t sbound;
@@ -990,6 +1008,8 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   w += align256((size_t)a.B * a.Hq * a.T * a.topk * sizeof(float));
   ia.lsel = reinterpret_cast<float*>(w);
   w += align256((size_t)a.B * a.Hq * a.T * sizeof(float));
+  ia.nvalid = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)a.B * a.Hkv * a.T * sizeof(int32_t));
   void* vt = w;
   w += align256((size_t)a.B * a.Hkv * ((a.T + kS - 1) / kS) * kS * a.D * esz);
   chunk_split(a.B, a.Hkv, a.T, NCs, a.topk > 0 ? a.topk : 1, &ia.E, &ia.sbound);
