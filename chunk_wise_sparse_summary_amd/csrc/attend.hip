@@ -630,6 +630,8 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
   // outputs (NR rows of D) for the fusion epilogue
   __shared__ __align__(16) T tiles[2 * kS * D];
   __shared__ float lzs[NR];
+  __shared__ float lss[NR];       // each row's L_sel
+  __shared__ int32_t nvs[NR];     // each row's selected slots
   T* ks = tiles;
   T* vt = tiles + kS * D;
   const int g = a.g0 + (int)blockIdx.y, b = blockIdx.z;
@@ -775,6 +777,12 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
     }
     if (grp == 0) lzs[rho] = (m + hw_log2(lsum)) * kLn2;
   }
+  if (threadIdx.x < NR) {   // the rows' L_sel and selected slots, once per row
+    const int rr = threadIdx.x;
+    const int64_t iq = min<int64_t>(qb0 + rr / G, T_ - 1);
+    lss[rr] = a.lsel ? a.lsel[((int64_t)b * a.Hq + g * G + rr % G) * T_ + iq] : kNegInf;
+    nvs[rr] = a.lsel ? a.nvalid[((int64_t)b * a.Hkv + g) * T_ + iq] : 0;
+  }
   __syncthreads();
   for (int it = threadIdx.x; it < NR * PK; it += kWinThreads) {
     const int rr = it / PK, pc = it % PK;
@@ -783,7 +791,7 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
     const int hq = rr % G;
     const int64_t rowq = ((int64_t)b * a.Hq + g * G + hq) * T_ + iq;
     const float lz = lzs[rr];
-    const float lsl = a.lsel ? a.lsel[rowq] : kNegInf;
+    const float lsl = lss[rr];
     const float L = lsl == kNegInf ? lz : fmaxf(lsl, lz) + __logf(1.f + __expf(-fabsf(lsl - lz)));
     const float ww = __expf(lz - L);
     const float wsel = lsl == kNegInf ? 0.f : __expf(lsl - L);
@@ -796,7 +804,7 @@ __device__ __forceinline__ void window_body(const WinArgs& a) {
     }
     if (wsel > 0.f) {
       // the row's selected slots are its first nv (padding only at the end)
-      const int nv = a.nvalid[((int64_t)b * a.Hkv + g) * T_ + iq];
+      const int nv = nvs[rr];
       const T* prow = static_cast<const T*>(a.part) +
                       ((((int64_t)b * a.gpass + (g - a.g0)) * T_ + iq) * a.topk * G + hq) * D + pc * EPV;
       // U slots' partial loads in flight together, with no load waiting on
