@@ -22,9 +22,9 @@
 //   out_i = exp(log Z_win - L) o_win + exp(L_sel - L) * sum_slots partial,
 //   L = LSE(L_sel, log Z_win).
 // The (query, slot) lists per chunk are built deterministically: per tile of
-// 1024 queries each chunk's count (from LDS bitmaps of which of 64 queries chose
-// it), a column scan over tiles and a scan over chunks give every entry a fixed
-// position, in query order within its chunk.
+// 256 to 1024 queries each chunk's count (from LDS bitmaps of which of 64
+// queries chose it), a column scan over tiles and a scan over chunks give every
+// entry a fixed position, in query order within its chunk.
 //
 // Score tiles are computed transposed, S^T = K Q^T (tokens x rows), so each lane
 // holds one row's scores for 16 tokens; the same registers, cast to the operand
@@ -55,14 +55,24 @@ struct IdxArgs {
   int32_t* stot;       // [B, Hkv]: workgroups of (b, g)
   int B, Hq, Hkv, topk;
   int64_t T, NCs, ntiles;
+  int tile;            // queries per counting tile (idx_tile)
   int E;               // entries per chunk-pass workgroup (a chunk's list in ranges of E)
   int64_t sbound;      // workgroups per (b, g), an upper bound
 };
 
-// Queries per counting tile (the column scan runs over T / kIdxTile tiles) and
-// per ranking sub-tile (one 64-bit LDS bitmap word per chunk).
-constexpr int kIdxTile = 1024;
+// Queries per ranking sub-tile (one 64-bit LDS bitmap word per chunk).  A
+// counting tile is a multiple of it (idx_tile).
 constexpr int kIdxSub = 64;
+
+// Queries per counting tile: 1024, halved down to 256 while the (b, g, tile)
+// grid would have fewer than 1024 workgroups.  A workgroup runs its tile's
+// sub-tiles one after another, so short sequences want shorter tiles; long ones
+// want longer tiles, for fewer per-tile counts to scan and load.
+int idx_tile(int B, int Hkv, int64_t T) {
+  int tile = 1024;
+  while (tile > 256 && (int64_t)B * Hkv * ((T + tile - 1) / tile) < 1024) tile /= 2;
+  return tile;
+}
 
 // Sets bit ql of chunk c's word for every entry (query i0 + ql, slot) of the
 // sub-tile of 64 queries at i0 (a chunk listed twice in a row counts once).
@@ -76,7 +86,7 @@ __device__ __forceinline__ void sub_bitmap(const IdxArgs& a, uint64_t* bm, const
   }
 }
 
-// Queries of the tile of kIdxTile queries that chose each chunk of (b, g), one
+// Queries of the counting tile that chose each chunk of (b, g), one
 // sub-tile bitmap at a time.
 __global__ __launch_bounds__(256) void idx_count_kernel(IdxArgs a) {
   extern __shared__ uint64_t bm[];
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(256) void idx_count_kernel(IdxArgs a) {
     cnt[c] = 0;
     bm[c] = 0ull;
   }
-  for (int64_t i0 = t * kIdxTile; i0 < min<int64_t>((t + 1) * kIdxTile, a.T); i0 += kIdxSub) {
+  for (int64_t i0 = t * a.tile; i0 < min<int64_t>((t + 1) * a.tile, a.T); i0 += kIdxSub) {
     __syncthreads();
     sub_bitmap(a, bm, a.idx + (((int64_t)b * a.Hkv + g) * a.T + i0) * a.topk, i0);
     __syncthreads();
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(1024) void split_map_kernel(IdxArgs a) {
 }
 
 // Entries at their final positions, in query order within each bucket.  A
-// block takes one tile of kIdxTile queries; each chunk's next position (its
+// block takes one counting tile of queries; each chunk's next position (its
 // bucket's base relative to the first bucket of (b, g), plus the tile's offset
 // in the bucket) sits in LDS, read once with coalesced loads.  The tile's
 // sub-tiles of 64 queries run in order: the bitmap of which of the 64 queries
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
     bm[c] = 0ull;
   }
   const int n = kIdxSub * a.topk;
-  for (int64_t i0 = t * kIdxTile; i0 < min<int64_t>((t + 1) * kIdxTile, a.T); i0 += kIdxSub) {
+  for (int64_t i0 = t * a.tile; i0 < min<int64_t>((t + 1) * a.tile, a.T); i0 += kIdxSub) {
     const int32_t* row = a.idx + (((int64_t)b * a.Hkv + g) * a.T + i0) * a.topk;
     __syncthreads();   // pos and bm as the previous sub-tile left them
     sub_bitmap(a, bm, row, i0);
@@ -923,7 +933,8 @@ void chunk_split(int B, int Hkv, int64_t T, int64_t NCs, int topk, int* E, int64
 void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk, bool bf16,
                       size_t* fixed, size_t* per_kv_head) {
   const int64_t NCs = T / S;
-  const int64_t ntiles = (T + kIdxTile - 1) / kIdxTile;
+  const int tile = idx_tile(B, Hkv, T);
+  const int64_t ntiles = (T + tile - 1) / tile;
   const size_t esz = bf16 ? 2 : 4;
   size_t f = 0;
   f += align256((size_t)B * Hkv * ntiles * NCs * sizeof(int32_t));  // tile_cnt
@@ -945,7 +956,8 @@ void attend_workspace(int B, int Hq, int Hkv, int64_t T, int S, int D, int topk,
 
 size_t entry_lists_bytes(int B, int Hkv, int64_t T, int S, int topk) {
   const int64_t NCs = T / S;
-  const int64_t ntiles = (T + kIdxTile - 1) / kIdxTile;
+  const int tile = idx_tile(B, Hkv, T);
+  const int64_t ntiles = (T + tile - 1) / tile;
   return align256((size_t)B * Hkv * ntiles * NCs * sizeof(int32_t)) +
          align256((size_t)B * Hkv * NCs * sizeof(int32_t)) + align256((size_t)B * Hkv * NCs * sizeof(int64_t)) +
          align256((size_t)B * Hkv * T * topk * sizeof(uint32_t));
@@ -954,7 +966,8 @@ size_t entry_lists_bytes(int B, int Hkv, int64_t T, int S, int topk) {
 hipError_t launch_entry_lists(const int32_t* idx, int B, int Hq, int Hkv, int64_t T, int S, int topk,
                               void* ws, EntryLists* el, hipStream_t st) {
   const int64_t NCs = T / S;
-  const int64_t ntiles = (T + kIdxTile - 1) / kIdxTile;
+  const int tile = idx_tile(B, Hkv, T);
+  const int64_t ntiles = (T + tile - 1) / tile;
   char* w = static_cast<char*>(ws);
   IdxArgs ia{};
   ia.idx = idx;
@@ -966,7 +979,7 @@ hipError_t launch_entry_lists(const int32_t* idx, int B, int Hq, int Hkv, int64_
   w += align256((size_t)B * Hkv * NCs * sizeof(int64_t));
   ia.entries = reinterpret_cast<uint32_t*>(w);
   ia.B = B; ia.Hq = Hq; ia.Hkv = Hkv; ia.topk = topk;
-  ia.T = T; ia.NCs = NCs; ia.ntiles = ntiles;
+  ia.T = T; ia.NCs = NCs; ia.ntiles = ntiles; ia.tile = tile;
   el->bcount = ia.bcount;
   el->bbase = ia.bbase;
   el->entries = ia.entries;
@@ -998,7 +1011,8 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   size_t fixed, per;
   attend_workspace(a.B, a.Hq, a.Hkv, a.T, a.S, a.D, a.topk, a.bf16, &fixed, &per);
   const int64_t NCs = a.T / a.S;
-  const int64_t ntiles = (a.T + kIdxTile - 1) / kIdxTile;
+  const int tile = idx_tile(a.B, a.Hkv, a.T);
+  const int64_t ntiles = (a.T + tile - 1) / tile;
   const size_t esz = a.bf16 ? 2 : 4;
   char* w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(a.ws) + 255) & ~(uintptr_t)255);
   IdxArgs ia{};
@@ -1026,7 +1040,7 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
   ia.stot = reinterpret_cast<int32_t*>(w);
   w += align256((size_t)a.B * a.Hkv * sizeof(int32_t));
   ia.B = a.B; ia.Hq = a.Hq; ia.Hkv = a.Hkv; ia.topk = a.topk;
-  ia.T = a.T; ia.NCs = NCs; ia.ntiles = ntiles;
+  ia.T = a.T; ia.NCs = NCs; ia.ntiles = ntiles; ia.tile = tile;
   void* part = w;
   const size_t avail = a.ws_bytes - fixed;
   int gpp = per > 0 ? (int)(avail / per) : a.Hkv;  // k = 0 needs no partial outputs
