@@ -64,6 +64,8 @@ struct IdxArgs {
 // counting tile is a multiple of it (idx_tile).
 constexpr int kIdxSub = 64;
 
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup
+
 // Queries per counting tile: 1024, halved down to 256 while the (b, g, tile)
 // grid would have fewer than 1024 workgroups.  A workgroup runs its tile's
 // sub-tiles one after another, so short sequences want shorter tiles; long ones
@@ -230,6 +232,79 @@ __global__ __launch_bounds__(256) void idx_fill_kernel(IdxArgs a) {
       pos[c] += __popcll(bm[c]);
       bm[c] = 0ull;
     }
+  }
+}
+
+// idx_fill_kernel's result, with the tile's entries staged in LDS in chunk
+// order and each chunk's run then written with contiguous stores (direct
+// 4-byte scatters cost several times their bytes in partial-line writes).  The
+// tile's per-chunk counts (the next tile's offsets minus this tile's, or the
+// chunk's total after the last tile) are scanned to each chunk's start in the
+// stage; the sub-tiles then place their entries there as idx_fill_kernel places
+// them in HBM, and run[c] ends as the end of chunk c's run.  LDS: NCs * 12
+// bytes + tile * topk * 4 bytes (the host checks that they fit).
+__global__ __launch_bounds__(1024) void idx_fill_staged_kernel(IdxArgs a) {
+  extern __shared__ uint64_t bm[];
+  int32_t* run = reinterpret_cast<int32_t*>(bm + a.NCs);
+  uint32_t* stage = reinterpret_cast<uint32_t*>(run + a.NCs);
+  __shared__ int32_t wtot[16];
+  const int64_t t = blockIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int64_t bg = (int64_t)b * a.Hkv + g;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int32_t* toff = a.tile_cnt + (bg * a.ntiles + t) * a.NCs;
+  const int32_t* tnext = t + 1 < a.ntiles ? toff + a.NCs : a.bcount + bg * a.NCs;
+  // each thread a contiguous run of chunks: counts, then an exclusive block scan
+  const int64_t per = (a.NCs + blockDim.x - 1) / blockDim.x;
+  const int64_t c0 = tid * per, c1 = min<int64_t>(c0 + per, a.NCs);
+  int32_t sum = 0;
+  for (int64_t c = c0; c < c1; ++c) sum += tnext[c] - toff[c];
+  int32_t inc = sum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t v = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += v;
+  }
+  if (lane == kWave - 1) wtot[wave] = inc;
+  __syncthreads();
+  int32_t base = inc - sum;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  for (int64_t c = c0; c < c1; ++c) {
+    run[c] = base;
+    base += tnext[c] - toff[c];
+    bm[c] = 0ull;
+  }
+  const int n = kIdxSub * a.topk;
+  for (int64_t i0 = t * a.tile; i0 < min<int64_t>((t + 1) * a.tile, a.T); i0 += kIdxSub) {
+    const int32_t* row = a.idx + (bg * a.T + i0) * a.topk;
+    __syncthreads();   // run and bm as the previous sub-tile left them
+    sub_bitmap(a, bm, row, i0);
+    __syncthreads();
+    for (int e = tid; e < n; e += blockDim.x) {
+      const int ql = e / a.topk, sl = e % a.topk;
+      const int64_t i = i0 + ql;
+      if (i >= a.T) break;
+      const int32_t c = row[e];
+      if (c < 0 || c >= a.NCs) continue;
+      const int rank = __popcll(bm[c] & ((1ull << ql) - 1ull));
+      stage[run[c] + rank] = (uint32_t)(i * 64 + sl);
+    }
+    __syncthreads();
+    for (int64_t c = tid; c < a.NCs; c += blockDim.x) {   // each thread its own chunks
+      run[c] += __popcll(bm[c]);
+      bm[c] = 0ull;
+    }
+  }
+  __syncthreads();
+  // chunk c's run is stage[run[c-1], run[c]) (from 0 for chunk 0); it goes to
+  // its bucket at the tile's offset
+  const int64_t* bbase = a.bbase + bg * a.NCs;
+  for (int64_t c = wave; c < a.NCs; c += nwaves) {
+    const int32_t e1 = run[c], e0 = c > 0 ? run[c - 1] : 0;
+    if (e1 == e0) continue;
+    uint32_t* dst = a.entries + bbase[c] + toff[c];
+    for (int32_t j = lane; j < e1 - e0; j += kWave) dst[j] = stage[e0 + j];
   }
 }
 
@@ -912,6 +987,20 @@ hipError_t launch_attend_t(const AttArgs& a, const IdxArgs& ia, void* part, void
   }
 }
 
+// The fill: staged in LDS when a tile's entries and the per-chunk state fit
+// (for example up to 2048 chunks with tiles of 1024 queries and k = 32), else
+// with direct scatters.
+void launch_idx_fill(const IdxArgs& ia, hipStream_t st) {
+  const size_t lds = (size_t)ia.NCs * (sizeof(uint64_t) + sizeof(int32_t));
+  const size_t staged = lds + (size_t)ia.tile * ia.topk * sizeof(uint32_t);
+  KTimer tm(K_IDX_FILL, st);
+  if (staged + 256 <= kMaxLds)   // + the kernel's static LDS
+    hipLaunchKernelGGL(idx_fill_staged_kernel, dim3((unsigned)ia.ntiles, ia.Hkv, ia.B), dim3(1024), staged, st,
+                       ia);
+  else
+    hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ia.ntiles, ia.Hkv, ia.B), dim3(256), lds, st, ia);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -999,11 +1088,7 @@ hipError_t launch_entry_lists(const int32_t* idx, int B, int Hq, int Hkv, int64_
     KTimer tm(K_IDX_SCAN_BUCKETS, st);
     hipLaunchKernelGGL(idx_scan_buckets_kernel, dim3(1), dim3(1024), 0, st, ia);
   }
-  {
-    KTimer tm(K_IDX_FILL, st);
-    hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, Hkv, B), dim3(256),
-                       lds + (size_t)NCs * sizeof(int32_t), st, ia);
-  }
+  launch_idx_fill(ia, st);
   return hipGetLastError();
 }
 
@@ -1107,11 +1192,7 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
       KTimer tm(K_IDX_SCAN_BUCKETS, st);
       hipLaunchKernelGGL(idx_scan_buckets_kernel, dim3(1), dim3(1024), 0, st, ia);
     }
-    {
-      KTimer tm(K_IDX_FILL, st);
-      hipLaunchKernelGGL(idx_fill_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256),
-                         lds + (size_t)NCs * sizeof(int32_t), st, ia);
-    }
+    launch_idx_fill(ia, st);
     KTimer tm(K_IDX_SCAN_BUCKETS, st);
     hipLaunchKernelGGL(split_map_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(1024), 0, st, ia);
   }
