@@ -89,8 +89,9 @@ __device__ __forceinline__ void sub_bitmap(const IdxArgs& a, uint64_t* bm, const
 }
 
 // Queries of the counting tile that chose each chunk of (b, g), one
-// sub-tile bitmap at a time.
-__global__ __launch_bounds__(256) void idx_count_kernel(IdxArgs a) {
+// sub-tile bitmap at a time (eight waves: the sub-tiles form a chain of
+// barriers, so more waves per chain beat more workgroups per compute unit).
+__global__ __launch_bounds__(512) void idx_count_kernel(IdxArgs a) {
   extern __shared__ uint64_t bm[];
   int32_t* cnt = reinterpret_cast<int32_t*>(bm + a.NCs);
   const int64_t t = blockIdx.x;
@@ -1077,7 +1078,7 @@ hipError_t launch_entry_lists(const int32_t* idx, int B, int Hq, int Hkv, int64_
   const size_t lds = (size_t)NCs * sizeof(uint64_t);
   {
     KTimer tm(K_IDX_COUNT, st);
-    hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, Hkv, B), dim3(256),
+    hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, Hkv, B), dim3(512),
                        lds + (size_t)NCs * sizeof(int32_t), st, ia);
   }
   {
@@ -1180,7 +1181,7 @@ hipError_t launch_attend(const AttArgs& a, hipStream_t st) {
     const size_t lds = (size_t)NCs * sizeof(uint64_t);
     {
       KTimer tm(K_IDX_COUNT, st);
-      hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(256),
+      hipLaunchKernelGGL(idx_count_kernel, dim3((unsigned)ntiles, a.Hkv, a.B), dim3(512),
                          lds + (size_t)NCs * sizeof(int32_t), st, ia);
     }
     {
